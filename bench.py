@@ -1,0 +1,277 @@
+"""Benchmark of the chunkwise gated delta rule forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|headline]
+                    [--no-cpu-baseline]
+
+One step = one gdr_chunk_fwd call over the headline workload (Gated
+DeltaNet, bf16 q/k/v/o, fp32 gates and state, B=8 H=16 T=4096 d=128, C=64):
+every per-chunk operation of the chunk algorithm runs inside that one kernel.
+Inputs are generated on the CPU (seeded) and copied to HBM before timing.
+K steps are timed between torch.cuda.synchronize() calls; each launch is
+also bracketed by HIP events on the launch stream to get the kernel's own
+average duration, from which the roofline fraction is computed against the
+algorithmic bytes (every input read once, every output written once).
+
+The other workloads (KDA, Q-Delta, Gated DeltaNet-2, and the decode step)
+are timed the same way and reported under "workloads"; the float64 oracle
+is timed on a bounded sample of the headline workload under "cpu_baseline".
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import resource
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunked gated-delta fwd tokens/s and % bf16 MFMA peak, d=128, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["common.hpp", "chunk_kernel.hpp", "step_kernel.hpp", "chunk_bf16.hip", "step.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_17_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def flops_per_token_head(dk, dv, C=64):
+    """Algorithmic flops of the chunk algorithm per token and head; the
+    triangular products count only their non-zero half."""
+    f = (C * (C - 1) * dk          # T = tril(E_bar K_bar^T, -1)
+         + C * (C + 1) * dk        # A_qk = tril(Q_gamma K_bar^T, 0)
+         + C * (C - 1) * (C - 2) / 3  # (I + T)^{-1}
+         + C * (C - 1) * dk        # Y = A E_bar
+         + C * (C - 1) * dv        # U = A Z
+         + 6 * C * dk * dv         # Y S, Q_gamma S, K_tail^T W
+         + C * (C + 1) * dv)       # A_qk W
+    return f / C
+
+
+def algorithmic_bytes(cfg, inp, op="chunk"):
+    B, T, H = cfg["B"], cfg["T"], cfg["H"]
+    dk = inp["k"].shape[3]
+    dv = inp["v"].shape[3]
+    io = inp["q"].element_size()
+    n = B * T * H
+    by = n * (2 * dk + 2 * dv) * io   # q, k, v read; o written
+    if inp["g"] is not None:
+        by += inp["g"].numel() * 4
+    for key in ("beta", "b", "w", "lam"):
+        if inp[key] is not None:
+            by += inp[key].numel() * 4
+    st = B * H * dk * dv * 4
+    by += st * (2 if inp["state"] is not None else 1)
+    return by
+
+
+def traffic_from_profile(kernel_tag, workload):
+    """HBM bytes per launch measured by rocprofv3 counters, if the profile was
+    taken with the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_tag, {}).get(workload)
+    if not ent or ent.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, stream, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [s.elapsed_time(e) for s, e in evs]  # ms
+    return wall / steps * 1e3, sum(kern) / len(kern), min(kern)
+
+
+def bench_workload(name, steps, warmup, op="chunk"):
+    import ctypes
+
+    import torch
+
+    import gated_delta_rule_17_amd as gdr
+    from gated_delta_rule_17_amd import _lib
+    from synth import config, make_inputs
+
+    cfg = config(name)
+    inp = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    B, T, H = cfg["B"], cfg["T"], cfg["H"]
+    dk, dv = d["k"].shape[3], d["v"].shape[3]
+    o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
+    so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    kinds = dict(decay=d["decay"], erase=d["erase"], write=d["write"], qmix=d["qmix"])
+    args = gdr.build_args(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
+                          lam=d["lam"], state=d["state"], o=o, state_out=so, **kinds)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    entry = "gdr_chunk_fwd" if op == "chunk" else "gdr_recurrent_step"
+    plan = gdr.plan(d["q"], d["k"], d["v"], op=op, g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
+                    lam=d["lam"], state=d["state"], **kinds)
+
+    def fn():
+        _lib.call(entry, args, sp)
+
+    ms_step, ms_kern, ms_min = time_launches(fn, stream, steps, warmup)
+    byts = algorithmic_bytes(cfg, inp, op)
+    tokens = B * T
+    res = dict(workload=name, variant=cfg["variant"], B=B, T=T, H=H, dk=dk, dv=dv, io=cfg["io"],
+               ms_per_step=ms_step, kernel_ms_avg=ms_kern, kernel_ms_min=ms_min,
+               tokens_per_s=tokens / (ms_step * 1e-3), algorithmic_bytes=byts,
+               hbm_gbs=byts / (ms_kern * 1e-3) / 1e9, plan=plan)
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    if op == "chunk":
+        fl = flops_per_token_head(dk, dv) * B * T * H
+        res["algorithmic_flops"] = fl
+        res["tflops"] = fl / (ms_kern * 1e-3) / 1e12
+        res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
+    del d, o, so
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def cpu_baseline(name, inp, budget_s=15.0):
+    """The float64 oracle as it stands, on a bounded prefix of the workload's
+    sequences (all batch rows and heads), scaled to tokens/s."""
+    from oracle import gdr_recurrence
+    from synth import oracle_kwargs
+
+    def run(Ts):
+        sub = {}
+        for key, val in inp.items():
+            if hasattr(val, "dim") and key not in ("lam", "state"):
+                sub[key] = val[:, :Ts]
+            else:
+                sub[key] = val
+        r0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        gdr_recurrence(sub["q"], sub["k"], sub["v"], **oracle_kwargs(sub))
+        wall = time.perf_counter() - t0
+        r1 = resource.getrusage(resource.RUSAGE_SELF)
+        cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+        return wall, cpu
+
+    B, T = inp["q"].shape[0], inp["q"].shape[1]
+    w64, _ = run(64)
+    Ts = int(min(T, max(64, budget_s / max(w64, 1e-6) * 64)))
+    wall, cpu = run(Ts)
+    cores = max(1, round(cpu / wall))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=B * Ts / wall, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{name}: all {B} batch rows x {inp['q'].shape[2]} heads, first {Ts} of {T} "
+                       f"tokens, float64 numpy token loop, {wall:.1f} s wall, {cpu:.1f} s cpu",
+                cpu_model=model, host_threads_available=len(os.sched_getaffinity(0)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", choices=["all", "headline"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the chunked forward shards over (batch, head) with no "
+              "exchange, so a multi-GPU figure is not produced here; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth import CONFIGS, DECODE, HEADLINE
+
+    torch.cuda.init()
+    head, head_inp = bench_workload(HEADLINE, args.steps, args.warmup)
+    print(f"# headline {HEADLINE}: {head['kernel_ms_avg'] * 1e3:.1f} us/launch, "
+          f"{head['hbm_gbs']:.0f} GB/s ({head['hbm_frac'] * 100:.1f}% HBM), "
+          f"{head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    workloads = {}
+    if args.workloads == "all":
+        for name in CONFIGS:
+            if name == HEADLINE:
+                continue
+            op = "step" if name == DECODE else "chunk"
+            r, _ = bench_workload(name, max(5, args.steps // 2), args.warmup, op=op)
+            keep = ("tokens_per_s", "kernel_ms_avg", "hbm_gbs", "hbm_frac", "tflops", "mfma_frac", "plan",
+                    "algorithmic_bytes")
+            workloads[name] = {k: r[k] for k in keep if k in r}
+            print(f"# {name}: {r['kernel_ms_avg'] * 1e3:.1f} us/launch, {r['hbm_gbs']:.0f} GB/s "
+                  f"({r['hbm_frac'] * 100:.1f}% HBM)", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(HEADLINE, head_inp)
+        print(f"# cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores", file=sys.stderr,
+              flush=True)
+
+    traffic = traffic_from_profile("chunk_fwd_kernel", HEADLINE)
+    roof = dict(bound="hbm", achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=head["hbm_frac"], traffic=traffic,
+                algorithmic_bytes_per_launch=head["algorithmic_bytes"],
+                kernel_ms_avg=head["kernel_ms_avg"], kernel="chunk_fwd_kernel<bf16,bf16,128,%d,false>"
+                % head["plan"]["dv_slice"])
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "variant": "gated_deltanet", "B": head["B"], "T": head["T"],
+                   "H": head["H"], "dk": head["dk"], "dv": head["dv"], "chunk": 64,
+                   "io": "bf16 q/k/v/o, fp32 gates and state", "dv_slice": head["plan"]["dv_slice"],
+                   "grid": head["plan"]["grid"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "tflops": head["tflops"],
+        "mfma_frac": head["mfma_frac"],
+        "workloads": workloads,
+        "kernel_src_sha": kernel_source_hash(),
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

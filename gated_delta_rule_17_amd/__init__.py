@@ -1,0 +1,169 @@
+"""Python binding of libgdr: the chunkwise gated delta rule forward and its
+decode step on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/gdr.h``.  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if the shared
+library is missing, importing the functions raises.
+
+    o, state = chunk_fwd(q, k, v, g=g, beta=beta, state=S0)          # GDN
+    o, state = chunk_fwd(q, k, v, g=g_channel, beta=beta)            # KDA
+    o, state = chunk_fwd(q, k, v, g=g, beta=beta, lam=lam)           # Q-Delta
+    o, state = chunk_fwd(q, k, v, g=g_channel, b=b, w=w)             # Gated DeltaNet-2
+    o, state = recurrent_step(q1, k1, v1, ..., state=state)          # one token
+
+Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g [B,T,H] (scalar decay) or
+[B,T,H,dk] (per-channel decay); beta [B,T,H]; b [B,T,H,dk]; w [B,T,H,dv];
+lam [H]; state [B,H,dk,dv] fp32.  Returns o [B,T,H,dv] in q's dtype and the
+final state [B,H,dk,dv] fp32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _lib
+from ._lib import GdrArgs, GdrPlanInfo, GdrError  # noqa: F401
+
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+DECAY = {"none": 0, "scalar": 1, "channel": 2}
+GATE = {"beta": 0, "channel": 1}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _fptr(t):
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float)) if t is not None \
+        else ctypes.POINTER(ctypes.c_float)()
+
+
+def _check(t, name, dtype=None, ndim=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def build_args(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
+               o=None, state_out=None, decay=None, erase=None, write=None, qmix=None,
+               dv_split=0, T=None):
+    """Fill a ``gdr_args`` struct from tensors (no device work).  Kinds are
+    inferred from which gates are given unless passed explicitly."""
+    B, Tq, H, dk = q.shape
+    dv = v.shape[3]
+    if decay is None:
+        decay = "none" if g is None else ("scalar" if g.dim() == 3 else "channel")
+    if erase is None:
+        erase = "channel" if b is not None else "beta"
+    if write is None:
+        write = "channel" if w is not None else "beta"
+    if qmix is None:
+        qmix = lam is not None
+    a = GdrArgs()
+    a.struct_size = ctypes.sizeof(GdrArgs)
+    a.B, a.T, a.H, a.dk, a.dv = B, Tq if T is None else T, H, dk, dv
+    a.chunk = 64
+    a.io = DTYPES[q.dtype]
+    a.decay, a.erase, a.write, a.qmix = DECAY[decay], GATE[erase], GATE[write], int(bool(qmix))
+    a.dv_split = int(dv_split)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.g, a.beta, a.b, a.w, a.lambda_ = _fptr(g), _fptr(beta), _fptr(b), _fptr(w), _fptr(lam)
+    a.state_in = _fptr(state)
+    a.state_out = _fptr(state_out)
+    a.o = _ptr(o)
+    return a
+
+
+def _prepare(q, k, v, g, beta, b, w, lam, state, T1=False):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    if q.dtype not in DTYPES:
+        raise TypeError(f"q must be bf16 or fp32, got {q.dtype}")
+    _check(q, "q", ndim=4, device=dev)
+    _check(k, "k", dtype=q.dtype, ndim=4, device=dev)
+    _check(v, "v", dtype=q.dtype, ndim=4, device=dev)
+    for name, t in (("g", g), ("beta", beta), ("b", b), ("w", w), ("lam", lam), ("state", state)):
+        _check(t, name, dtype=torch.float32, device=dev)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if g is not None and tuple(g.shape) not in ((B, T, H), (B, T, H, dk)):
+        raise ValueError(f"g must be [B,T,H] or [B,T,H,dk], got {tuple(g.shape)}")
+    if beta is not None and tuple(beta.shape) != (B, T, H):
+        raise ValueError(f"beta must be [B,T,H], got {tuple(beta.shape)}")
+    if b is not None and tuple(b.shape) != (B, T, H, dk):
+        raise ValueError(f"b must be [B,T,H,dk], got {tuple(b.shape)}")
+    if w is not None and tuple(w.shape) != (B, T, H, dv):
+        raise ValueError(f"w must be [B,T,H,dv], got {tuple(w.shape)}")
+    if lam is not None and tuple(lam.shape) != (H,):
+        raise ValueError(f"lam must be [H], got {tuple(lam.shape)}")
+    if state is not None and tuple(state.shape) != (B, H, dk, dv):
+        raise ValueError(f"state must be [B,H,dk,dv], got {tuple(state.shape)}")
+    return B, T, H, dk, dv
+
+
+def _stream_ptr(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
+              decay=None, erase=None, write=None, qmix=None, dv_split=0,
+              out=None, state_out=None):
+    """Chunkwise forward (C = 64) of the generalized gated delta rule.
+    Enqueued on the current stream; no synchronisation."""
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
+                                                             device=q.device)
+    a = build_args(q, k, v, g=g, beta=beta, b=b, w=w, lam=lam, state=state, o=o, state_out=so,
+                   decay=decay, erase=erase, write=write, qmix=qmix, dv_split=dv_split)
+    _lib.call("gdr_chunk_fwd", a, _stream_ptr(q.device))
+    return o, so
+
+
+def recurrent_step(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
+                   decay=None, erase=None, write=None, qmix=None, out=None, state_out=None):
+    """One decode token (T == 1).  ``state_out`` may be ``state`` itself for
+    an in-place update."""
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state)
+    if T != 1:
+        raise ValueError("recurrent_step takes exactly one token (T == 1)")
+    o = out if out is not None else torch.empty((B, 1, H, dv), dtype=q.dtype, device=q.device)
+    so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
+                                                             device=q.device)
+    a = build_args(q, k, v, g=g, beta=beta, b=b, w=w, lam=lam, state=state, o=o, state_out=so,
+                   decay=decay, erase=erase, write=write, qmix=qmix)
+    _lib.call("gdr_recurrent_step", a, _stream_ptr(q.device))
+    return o, so
+
+
+def plan(q, k, v, op="chunk", **kw):
+    """Launch plan (grid, block, value-slice width, LDS bytes, chunks) that a
+    call with these tensors would use; host-only."""
+    a = build_args(q, k, v, **kw)
+    info = GdrPlanInfo()
+    _lib.call("gdr_plan", a, 0 if op == "chunk" else 1, ctypes.byref(info))
+    return dict(grid=info.grid, block=info.block, dv_slice=info.dv_slice, lds_bytes=info.lds_bytes,
+                n_chunks=info.n_chunks)
+
+
+def library_path() -> str:
+    return _lib.path()
+
+
+__all__ = ["chunk_fwd", "recurrent_step", "plan", "build_args", "library_path", "GdrError"]

@@ -1,0 +1,183 @@
+// Shared device helpers for the gfx950 kernels: vector types, MFMA tile
+// products over LDS views, fragment loads and accumulator stores.
+//
+// MFMA lane layouts used throughout (16x16 output tiles, wave64):
+//   v_mfma_f32_16x16x32_bf16: A/B fragment of lane l = 8 consecutive k values
+//       (k = 8*(l>>4) .. +7) of row/column (l & 15).
+//   v_mfma_f32_16x16x4_f32:   A/B fragment of lane l = 1 value, k = l>>4.
+//   accumulator (both):       lane l holds D[4*(l>>4) + r][l & 15], r = 0..3.
+// A tile product D = X * Y therefore reads X with k contiguous (row-major X)
+// and Y^T with k contiguous, and its accumulator stores 4 consecutive rows of
+// one column, i.e. a contiguous vector of D^T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float fexp(float x) { return __expf(x); }
+
+// A matrix in LDS: element (r, c) at p[r * rs + c * cs].
+template <class T>
+struct View {
+  T* p;
+  int rs, cs;
+};
+
+template <class T>
+__device__ __forceinline__ View<T> view(T* p, int rs, int cs) {
+  return View<T>{p, rs, cs};
+}
+
+// ---- MFMA traits ---------------------------------------------------------
+template <class T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int KS = 32;
+  typedef bf16x8 frag;
+  // rows r0..r0+15, k in [k0, k0+32); lanes whose k range starts at or past
+  // klim supply zeros.  The view must have cs == 1.
+  __device__ static __forceinline__ frag load(View<bf16> v, int r0, int k0, int klim, int lane) {
+    const int kk = k0 + ((lane >> 4) << 3);
+    frag z = {};
+    if (kk >= klim) return z;
+    return *reinterpret_cast<const frag*>(v.p + (r0 + (lane & 15)) * v.rs + kk);
+  }
+  __device__ static __forceinline__ f32x4 mma(f32x4 c, frag a, frag b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int KS = 4;
+  typedef float frag;
+  __device__ static __forceinline__ frag load(View<float> v, int r0, int k0, int klim, int lane) {
+    const int kk = k0 + (lane >> 4);
+    if (kk >= klim) return 0.f;
+    return v.p[(r0 + (lane & 15)) * v.rs + kk * v.cs];
+  }
+  __device__ static __forceinline__ f32x4 mma(f32x4 c, frag a, frag b) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// acc += A[i0:i0+16, ak0:ak0+K] * B[bk0:bk0+K, j0:j0+16], with B given as its
+// transpose BT (BT[j][k] = B[k][j]).  K is a multiple of 16.
+template <class T>
+__device__ __forceinline__ f32x4 tmm(f32x4 acc, View<T> A, int i0, int ak0, View<T> BT, int j0,
+                                     int bk0, int K, int lane) {
+  constexpr int KS = Mma<T>::KS;
+#pragma unroll 4
+  for (int kk = 0; kk < K; kk += KS) {
+    acc = Mma<T>::mma(acc, Mma<T>::load(A, i0, ak0 + kk, ak0 + K, lane),
+                      Mma<T>::load(BT, j0, bk0 + kk, bk0 + K, lane));
+  }
+  return acc;
+}
+
+// Store an accumulator tile into out(i, j) for i = i0 + 4*(lane>>4) + r,
+// j = j0 + (lane & 15).  tst_vec requires out.rs == 1 (the four rows of one
+// lane are contiguous); tst_sca works for any strides.
+__device__ __forceinline__ void tst_vec(View<bf16> out, int i0, int j0, f32x4 d, int lane) {
+  const int i = i0 + ((lane >> 4) << 2), j = j0 + (lane & 15);
+  *reinterpret_cast<bf16x4*>(out.p + i + j * out.cs) = __builtin_convertvector(d, bf16x4);
+}
+__device__ __forceinline__ void tst_vec(View<float> out, int i0, int j0, f32x4 d, int lane) {
+  const int i = i0 + ((lane >> 4) << 2), j = j0 + (lane & 15);
+  *reinterpret_cast<f32x4*>(out.p + i + j * out.cs) = d;
+}
+template <class T>
+__device__ __forceinline__ void tst_sca(View<T> out, int i0, int j0, f32x4 d, int lane) {
+  const int i = i0 + ((lane >> 4) << 2), j = j0 + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out.p[(i + r) * out.rs + j * out.cs] = (T)d[r];
+}
+
+// ---- 8-wide vectors for global loads and LDS stores ----------------------
+template <class T>
+struct V8;
+template <>
+struct V8<bf16> {
+  bf16x8 x;
+  __device__ __forceinline__ float operator[](int i) const { return (float)x[i]; }
+};
+template <>
+struct V8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
+__device__ __forceinline__ V8<bf16> ld8(const bf16* p) {
+  return V8<bf16>{*reinterpret_cast<const bf16x8*>(p)};
+}
+__device__ __forceinline__ V8<float> ld8(const float* p) {
+  return V8<float>{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+}
+template <class T>
+__device__ __forceinline__ V8<T> zero8() {
+  V8<T> z;
+  if constexpr (sizeof(T) == 2) {
+    z.x = bf16x8{};
+  } else {
+    z.a = f32x4{};
+    z.b = f32x4{};
+  }
+  return z;
+}
+template <class T>
+__device__ __forceinline__ V8<T> sel8(bool keep, V8<T> v) {
+  return keep ? v : zero8<T>();
+}
+
+// 8 floats -> 8 elements of T at p (16-byte aligned for bf16, 32 for fp32)
+__device__ __forceinline__ void st8(bf16* p, const float* f) {
+  f32x4 a = {f[0], f[1], f[2], f[3]}, b = {f[4], f[5], f[6], f[7]};
+  bf16x4 x = __builtin_convertvector(a, bf16x4), y = __builtin_convertvector(b, bf16x4);
+  bf16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  *reinterpret_cast<bf16x8*>(p) = z;
+}
+__device__ __forceinline__ void st8(float* p, const float* f) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
+// N consecutive elements (N = 1, 2, 4) from floats
+template <int N>
+__device__ __forceinline__ void stn(bf16* p, const float* f) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector((f32x4{f[0], f[1], f[2], f[3]}), bf16x4);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<bf16x2*>(p) = __builtin_convertvector((f32x2{f[0], f[1]}), bf16x2);
+  } else {
+    p[0] = (bf16)f[0];
+  }
+}
+template <int N>
+__device__ __forceinline__ void stn(float* p, const float* f) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<f32x2*>(p) = f32x2{f[0], f[1]};
+  } else {
+    p[0] = f[0];
+  }
+}
+
+// store 4 consecutive outputs to global memory
+__device__ __forceinline__ void gst4(bf16* p, f32x4 d) {
+  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(d, bf16x4);
+}
+__device__ __forceinline__ void gst4(float* p, f32x4 d) { *reinterpret_cast<f32x4*>(p) = d; }
+
+}  // namespace gdr

@@ -1,0 +1,253 @@
+// libgdr host side: argument validation, launch planning and dispatch for
+// the C ABI declared in include/gdr.h.  Validation is pure host code and runs
+// before any HIP call, so every error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/gdr.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+gdr_status fail(gdr_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const char* name, const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+constexpr int kOpChunk = 0, kOpStep = 1;
+
+int dvs_candidates(int io, int* out) {
+  if (io == GDR_BF16) {
+    out[0] = 64; out[1] = 32; out[2] = 16;
+    return 3;
+  }
+  out[0] = 32; out[1] = 16;
+  return 2;
+}
+
+int chunk_lds(int io, int dk, int dvs, bool chan) {
+  return io == GDR_BF16 ? gdr::chunk_lds_bf16(dk, dvs, chan) : gdr::chunk_lds_f32(dk, dvs, chan);
+}
+
+gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
+  if (!a) return fail(GDR_E_NULL, "gdr_args pointer is NULL");
+  if (a->struct_size < sizeof(gdr_args))
+    return fail(GDR_E_ARGS, "struct_size %u is smaller than sizeof(gdr_args) = %zu", a->struct_size,
+                sizeof(gdr_args));
+  if (op != kOpChunk && op != kOpStep) return fail(GDR_E_ARGS, "unknown op %d", op);
+  if (a->B < 1 || a->H < 1 || a->T < 0)
+    return fail(GDR_E_SHAPE, "need B >= 1, H >= 1, T >= 0 (got B=%d H=%d T=%d)", a->B, a->H, a->T);
+  if (op == kOpStep && a->T != 1) return fail(GDR_E_SHAPE, "the recurrent step needs T == 1 (got %d)", a->T);
+  const int chunk = a->chunk ? a->chunk : GDR_CHUNK;
+  if (chunk != GDR_CHUNK) return fail(GDR_E_SHAPE, "chunk must be 64 (got %d)", a->chunk);
+  if (a->dk < 1 || a->dv < 1) return fail(GDR_E_SHAPE, "need dk, dv >= 1 (got %d, %d)", a->dk, a->dv);
+  if (a->io != GDR_F32 && a->io != GDR_BF16) return fail(GDR_E_DTYPE, "unknown io dtype %d", a->io);
+  if (a->decay < GDR_DECAY_NONE || a->decay > GDR_DECAY_CHANNEL)
+    return fail(GDR_E_ARGS, "unknown decay kind %d", a->decay);
+  if (a->erase < GDR_GATE_BETA || a->erase > GDR_GATE_CHANNEL)
+    return fail(GDR_E_ARGS, "unknown erase kind %d", a->erase);
+  if (a->write < GDR_GATE_BETA || a->write > GDR_GATE_CHANNEL)
+    return fail(GDR_E_ARGS, "unknown write kind %d", a->write);
+  if (a->qmix != 0 && a->qmix != 1) return fail(GDR_E_ARGS, "qmix must be 0 or 1 (got %d)", a->qmix);
+  if (a->qmix && a->erase != GDR_GATE_BETA)
+    return fail(GDR_E_ARGS, "qmix mixes the query into the beta-gated erase direction; erase must be BETA");
+  const int64_t BH = int64_t(a->B) * a->H;
+  const int64_t tokens = BH * a->T;
+  if (BH > (int64_t(1) << 30) || tokens * (a->dk > a->dv ? a->dk : a->dv) > (int64_t(1) << 46))
+    return fail(GDR_E_SHAPE, "problem too large");
+
+  const bool has_tok = a->T > 0;
+  const bool need_beta = a->erase == GDR_GATE_BETA || a->write == GDR_GATE_BETA;
+  if (check_ptrs && has_tok) {
+    if (!a->q || !a->k || !a->v || !a->o) return fail(GDR_E_NULL, "q, k, v and o are required when T > 0");
+    if (a->decay != GDR_DECAY_NONE && !a->g) return fail(GDR_E_NULL, "g is required for decay kind %d", a->decay);
+    if (need_beta && !a->beta) return fail(GDR_E_NULL, "beta is required by a BETA gate");
+    if (a->erase == GDR_GATE_CHANNEL && !a->b) return fail(GDR_E_NULL, "b is required by erase CHANNEL");
+    if (a->write == GDR_GATE_CHANNEL && !a->w) return fail(GDR_E_NULL, "w is required by write CHANNEL");
+    if (a->qmix && !a->lambda) return fail(GDR_E_NULL, "lambda is required by qmix");
+  }
+  if (a->decay == GDR_DECAY_NONE && a->g) return fail(GDR_E_ARGS, "g given with decay NONE");
+
+  if (check_ptrs) {
+    // alignment
+    const void* al16[] = {a->q, a->k, a->v, a->o, a->state_in, a->state_out, a->b, a->w,
+                          a->decay == GDR_DECAY_CHANNEL ? a->g : nullptr};
+    for (const void* p : al16)
+      if (p && !aligned(p, 16)) return fail(GDR_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+    const void* al4[] = {a->beta, a->lambda, a->g};
+    for (const void* p : al4)
+      if (p && !aligned(p, 4)) return fail(GDR_E_ALIGN, "a gate pointer is not 4-byte aligned");
+
+    // aliasing
+    const int64_t ioe = a->io == GDR_BF16 ? 2 : 4;
+    const int64_t gsz = a->decay == GDR_DECAY_CHANNEL ? tokens * a->dk * 4 : tokens * 4;
+    const Range ins[] = {rng("q", a->q, tokens * a->dk * ioe),     rng("k", a->k, tokens * a->dk * ioe),
+                         rng("v", a->v, tokens * a->dv * ioe),     rng("g", a->g, gsz),
+                         rng("beta", a->beta, tokens * 4),         rng("b", a->b, tokens * a->dk * 4),
+                         rng("w", a->w, tokens * a->dv * 4),       rng("lambda", a->lambda, int64_t(a->H) * 4),
+                         rng("state_in", a->state_in, BH * a->dk * a->dv * 4)};
+    const Range ro = rng("o", a->o, tokens * a->dv * ioe);
+    const Range rs = rng("state_out", a->state_out, BH * a->dk * a->dv * 4);
+    for (const Range& r : ins) {
+      if (overlap(ro, r)) return fail(GDR_E_ARGS, "o overlaps input %s", r.name);
+      const bool same_state = (r.name[0] == 's') && r.lo == rs.lo;
+      if (!same_state && overlap(rs, r)) return fail(GDR_E_ARGS, "state_out overlaps input %s", r.name);
+    }
+    if (overlap(ro, rs)) return fail(GDR_E_ARGS, "o overlaps state_out");
+  }
+
+  // what this build implements
+  if (op == kOpChunk) {
+    if (a->io == GDR_BF16 && a->dk != 64 && a->dk != 128)
+      return fail(GDR_E_UNSUPPORTED, "bf16 chunk path supports dk in {64, 128} (got %d)", a->dk);
+    if (a->io == GDR_F32 && a->dk != 64)
+      return fail(GDR_E_UNSUPPORTED, "fp32 chunk path supports dk == 64 (got %d)", a->dk);
+    if (a->dv % 16 != 0 || a->dv > 256)
+      return fail(GDR_E_UNSUPPORTED, "dv must be a multiple of 16 up to 256 (got %d)", a->dv);
+    int cand[3];
+    const int nc = dvs_candidates(a->io, cand);
+    if (a->dv_split) {
+      bool ok = false;
+      for (int i = 0; i < nc; ++i) ok |= cand[i] == a->dv_split;
+      if (!ok || a->dv % a->dv_split != 0)
+        return fail(GDR_E_UNSUPPORTED, "dv_split %d is not an available slice width dividing dv=%d",
+                    a->dv_split, a->dv);
+    } else {
+      bool ok = false;
+      for (int i = 0; i < nc; ++i) ok |= (a->dv % cand[i] == 0);
+      if (!ok) return fail(GDR_E_UNSUPPORTED, "no slice width divides dv=%d", a->dv);
+    }
+  } else {
+    if (!gdr::step_supported(a->dk, a->dv))
+      return fail(GDR_E_UNSUPPORTED, "recurrent step supports dk, dv in {64, 128} (got %d, %d)", a->dk, a->dv);
+  }
+  return GDR_OK;
+}
+
+gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
+  const int64_t BH = int64_t(a->B) * a->H;
+  gdr_plan_info pi{};
+  pi.block = 256;
+  if (op == kOpStep) {
+    pi.grid = static_cast<int32_t>(BH);
+    pi.dv_slice = a->dv;
+    pi.lds_bytes = 0;
+    pi.n_chunks = 1;
+  } else {
+    int cand[3];
+    const int nc = dvs_candidates(a->io, cand);
+    int dvs = a->dv_split;
+    if (!dvs) {
+      for (int i = 0; i < nc && !dvs; ++i)
+        if (a->dv % cand[i] == 0 && BH * (a->dv / cand[i]) >= 256) dvs = cand[i];
+      for (int i = nc - 1; i >= 0 && !dvs; --i)
+        if (a->dv % cand[i] == 0) dvs = cand[i];
+    }
+    const bool chan = a->decay == GDR_DECAY_CHANNEL;
+    pi.dv_slice = dvs;
+    pi.grid = static_cast<int32_t>(BH * (a->dv / dvs));
+    pi.lds_bytes = chunk_lds(a->io, a->dk, dvs, chan);
+    pi.n_chunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
+    if (pi.lds_bytes < 0)
+      return fail(GDR_E_UNSUPPORTED, "no kernel instance for io=%d dk=%d slice=%d", a->io, a->dk, dvs);
+  }
+  if (out) *out = pi;
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_validate(const gdr_args* a, int op) { return validate_impl(a, op); }
+
+gdr_status gdr_plan(const gdr_args* a, int op, gdr_plan_info* out) {
+  gdr_status s = validate_impl(a, op, /*check_ptrs=*/false);
+  if (s != GDR_OK) return s;
+  return plan_impl(a, op, out);
+}
+
+gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
+  gdr_status s = validate_impl(a, kOpChunk);
+  if (s != GDR_OK) return s;
+  gdr_plan_info pi;
+  s = plan_impl(a, kOpChunk, &pi);
+  if (s != GDR_OK) return s;
+  if (a->T == 0 && !a->state_out) return GDR_OK;
+  gdr::ChunkParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.g = a->g; p.beta = a->beta; p.b = a->b; p.w = a->w; p.lam = a->lambda;
+  p.state_in = a->state_in; p.state_out = a->state_out; p.o = a->o;
+  p.B = a->B; p.T = a->T; p.H = a->H; p.DV = a->dv;
+  p.decay = a->decay; p.erase = a->erase; p.write = a->write; p.qmix = a->qmix;
+  p.nslices = a->dv / pi.dv_slice;
+  const bool chan = a->decay == GDR_DECAY_CHANNEL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = a->io == GDR_BF16 ? gdr::launch_chunk_bf16(p, a->dk, pi.dv_slice, chan, pi.grid, st)
+                                   : gdr::launch_chunk_f32(p, a->dk, pi.dv_slice, chan, pi.grid, st);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_recurrent_step(const gdr_args* a, void* stream) {
+  gdr_status s = validate_impl(a, kOpStep);
+  if (s != GDR_OK) return s;
+  gdr::StepParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.g = a->g; p.beta = a->beta; p.b = a->b; p.w = a->w; p.lam = a->lambda;
+  p.state_in = a->state_in; p.state_out = a->state_out; p.o = a->o;
+  p.B = a->B; p.H = a->H;
+  p.decay = a->decay; p.erase = a->erase; p.write = a->write; p.qmix = a->qmix;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_step(p, a->io == GDR_BF16, a->dk, a->dv, a->B * a->H, st);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "step kernel launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+const char* gdr_status_str(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_E_NULL: return "GDR_E_NULL";
+    case GDR_E_SHAPE: return "GDR_E_SHAPE";
+    case GDR_E_DTYPE: return "GDR_E_DTYPE";
+    case GDR_E_ALIGN: return "GDR_E_ALIGN";
+    case GDR_E_UNSUPPORTED: return "GDR_E_UNSUPPORTED";
+    case GDR_E_HIP: return "GDR_E_HIP";
+    case GDR_E_ARGS: return "GDR_E_ARGS";
+  }
+  return "GDR_E_UNKNOWN";
+}
+
+const char* gdr_last_error(void) { return g_err.c_str(); }
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+/*
+ * gdr.h -- C ABI of libgdr: the chunkwise-parallel forward pass of the
+ * generalized gated delta rule, and its single-token decode step, on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [QD]   "Q-Delta: Beyond Key-Value Associative State Evolution"
+ *   [GDN2] "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"
+ *   [KDA]  "You could have come up with Kimi Delta Attention"
+ *   [CH11] "Chapter 11  Gated DeltaNet: understanding the recurrence from a
+ *          matrix state"
+ *
+ * The operation.  For each (batch b, head h) an independent state
+ * S in R^{dk x dv} (rows = key channels, [GDN2] key design 1, [CH11] 11.1)
+ * evolves over tokens t = 0..T-1 as
+ *
+ *     S_bar = Diag(exp(g_t)) S          forget    ([KDA] 3-4)
+ *     r     = S_bar^T e_t               predict along the erase direction
+ *     S     = S_bar + k_t (z_t - r)^T   write along the key
+ *     o_t   = S^T q_t                   read the post-update state ([CH11] 11.2)
+ *
+ * with the erase direction e_t and written value z_t chosen by the gate kinds:
+ *     erase BETA:    e = beta_t * k_t    (qmix: e = beta_t * (k_t + lambda_h q_t), [QD] key design 3)
+ *     erase CHANNEL: e = b_t (.) k_t     ([GDN2] key design 1; b is not clamped)
+ *     write BETA:    z = beta_t * v_t
+ *     write CHANNEL: z = w_t (.) v_t     ([GDN2] key design 1)
+ * DeltaNet = (NONE, BETA, BETA); Gated DeltaNet = (SCALAR, BETA, BETA);
+ * KDA = (CHANNEL, BETA, BETA); Q-Delta = (SCALAR, BETA, BETA, qmix);
+ * Gated DeltaNet-2 = (CHANNEL, CHANNEL, CHANNEL).
+ *
+ * gdr_chunk_fwd evaluates this with the chunk WY algorithm of [GDN2] key
+ * design 2 (chunks of C = 64 tokens; intra-chunk matrices plus an
+ * inter-chunk state recurrence), which reaches the token recurrence's result
+ * up to rounding.  gdr_recurrent_step applies one token.
+ *
+ * Caller-side preparation ([GDN2] training strategy, [CH11] 11.3): q and k
+ * arrive already L2-normalised (q scaled as the model wants); gates are fp32
+ * activations; g = log(alpha) <= 0 is finite.  The library never rescales.
+ *
+ * Conventions for every entry point:
+ *  - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *    frees nothing and keeps no pointer after the call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    with no host synchronisation.  Pointers are device pointers.
+ *  - Inputs are read-only.  `o` must not overlap any input.  `state_out` may
+ *    be exactly `state_in` (in-place update) but must not partially overlap it.
+ *  - Errors: GDR_OK (0) or a non-zero gdr_status.  On a validation error
+ *    nothing is launched and no output is written; gdr_last_error() gives a
+ *    thread-local message.  GDR_E_HIP reports a HIP launch error.
+ *  - Reentrant: no global mutable state besides the thread-local message.
+ *  - Deterministic: no atomics; the same inputs give bitwise-identical output.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+#define GDR_CHUNK 64
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_E_NULL = 1,        /* a required pointer (or the args struct) is NULL      */
+  GDR_E_SHAPE = 2,       /* B, T, H, dk, dv, chunk out of range                  */
+  GDR_E_DTYPE = 3,       /* unknown io dtype                                      */
+  GDR_E_ALIGN = 4,       /* a pointer is not aligned as documented                */
+  GDR_E_UNSUPPORTED = 5, /* a valid combination this build does not implement     */
+  GDR_E_HIP = 6,         /* the HIP runtime reported an error                     */
+  GDR_E_ARGS = 7         /* inconsistent arguments (kinds, aliasing, struct size) */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+typedef enum gdr_decay { GDR_DECAY_NONE = 0, GDR_DECAY_SCALAR = 1, GDR_DECAY_CHANNEL = 2 } gdr_decay;
+typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
+
+/*
+ * Arguments.  Every per-token tensor is [B, T, H, ...], contiguous, row-major
+ * (the last index fastest).
+ *
+ *   q, k     [B,T,H,dk]   io dtype                         16-byte aligned
+ *   v        [B,T,H,dv]   io dtype                         16-byte aligned
+ *   o        [B,T,H,dv]   io dtype, written                16-byte aligned
+ *   g        decay SCALAR: [B,T,H] fp32; CHANNEL: [B,T,H,dk] fp32 (16-byte
+ *            aligned); NONE: must be NULL.  Log of the retention gate.
+ *   beta     [B,T,H] fp32; required iff erase or write is BETA (or qmix)
+ *   b        [B,T,H,dk] fp32, 16-byte aligned; required iff erase CHANNEL
+ *   w        [B,T,H,dv] fp32, 16-byte aligned; required iff write CHANNEL
+ *   lambda   [H] fp32; required iff qmix (then erase must be BETA)
+ *   state_in [B,H,dk,dv] fp32, 16-byte aligned, or NULL for a zero state
+ *   state_out[B,H,dk,dv] fp32, 16-byte aligned, or NULL (not written)
+ *
+ * Fields set to zero select defaults; set struct_size = sizeof(gdr_args).
+ * dv_split: 0 lets the library choose how many workgroups share one head's
+ * value columns; otherwise the column-slice width (16, 32 or 64, dividing dv).
+ * When T == 0, q/k/v/o/gates may be NULL and state_out receives state_in
+ * (or zeros).
+ */
+typedef struct gdr_args {
+  uint32_t struct_size;
+  int32_t B, T, H, dk, dv;
+  int32_t chunk;     /* must be 64 (0 = 64) */
+  int32_t io;        /* gdr_dtype of q, k, v, o */
+  int32_t decay;     /* gdr_decay */
+  int32_t erase;     /* gdr_gate */
+  int32_t write;     /* gdr_gate */
+  int32_t qmix;      /* 0 or 1 */
+  int32_t dv_split;  /* 0 = auto */
+  const void *q, *k, *v;
+  const float *g, *beta, *b, *w, *lambda;
+  const float *state_in;
+  float *state_out;
+  void *o;
+} gdr_args;
+
+/* What a call would launch (filled by gdr_plan). */
+typedef struct gdr_plan_info {
+  int32_t grid;        /* workgroups */
+  int32_t block;       /* threads per workgroup */
+  int32_t dv_slice;    /* value columns per workgroup */
+  int32_t lds_bytes;   /* LDS per workgroup */
+  int32_t n_chunks;    /* chunks per sequence */
+} gdr_plan_info;
+
+/*
+ * Chunkwise forward over any T >= 0 ([GDN2] key design 2, C = 64).
+ * Supported: io BF16 with dk in {64, 128}; io F32 with dk == 64 (fp32 matrix
+ * arithmetic for the tighter fp32 tolerance); dv a multiple of 16, 16..256,
+ * divisible by the slice width.  Other valid combinations return
+ * GDR_E_UNSUPPORTED.
+ */
+gdr_status gdr_chunk_fwd(const gdr_args *a, void *stream);
+
+/*
+ * One decode step ([CH11] 11.3: the streaming caller passes the previous
+ * final state back in).  Requires T == 1.  io BF16 or F32, dk and dv in
+ * {64, 128}.  state_out may equal state_in for an in-place update.
+ */
+gdr_status gdr_recurrent_step(const gdr_args *a, void *stream);
+
+/* Host-only validation of `a` for op 0 (chunk) or 1 (step); launches nothing
+ * and touches no device memory, so it runs without a GPU. */
+gdr_status gdr_validate(const gdr_args *a, int op);
+
+/* Host-only launch plan for op 0 / 1.  Checks shapes, kinds and the support
+ * matrix like gdr_validate but not the pointers (they may be NULL). */
+gdr_status gdr_plan(const gdr_args *a, int op, gdr_plan_info *out);
+
+const char *gdr_status_str(gdr_status s);
+const char *gdr_last_error(void);
+int gdr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,166 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+function ``include/gdr.h`` declares, and rejects bad arguments in host
+validation (before any HIP call; the pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_17_amd import _lib
+from gated_delta_rule_17_amd._lib import GdrArgs, GdrPlanInfo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_HIP, E_ARGS = range(8)
+CHUNK, STEP = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", src)))
+
+
+def test_header_functions_are_exported(lib):
+    declared = _declared_functions()
+    assert set(declared) >= {"gdr_chunk_fwd", "gdr_recurrent_step", "gdr_status_str",
+                             "gdr_last_error", "gdr_abi_version", "gdr_validate", "gdr_plan"}
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.path()], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = set(re.findall(r" T (gdr_\w+)", nm.stdout))
+        assert set(declared) <= exported
+    assert sorted(_lib.EXPORTS) == declared
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.gdr_abi_version() == 1
+    for code, name in _lib.STATUS.items():
+        assert lib.gdr_status_str(code).decode() == name
+    assert lib.gdr_status_str(99).decode() == "GDR_E_UNKNOWN"
+
+
+# fake, aligned, non-overlapping addresses (validation never dereferences them)
+_BASE = 0x7F0000000000
+_STEP = 1 << 32
+
+
+def _addr(i, off=0):
+    return _BASE + i * _STEP + off
+
+
+def good_args(**kw):
+    a = GdrArgs()
+    a.struct_size = ctypes.sizeof(GdrArgs)
+    a.B, a.T, a.H, a.dk, a.dv = 2, 200, 4, 128, 128
+    a.chunk, a.io, a.decay, a.erase, a.write, a.qmix, a.dv_split = 64, 1, 1, 0, 0, 0, 0
+    fp = ctypes.POINTER(ctypes.c_float)
+    a.q, a.k, a.v, a.o = _addr(0), _addr(1), _addr(2), _addr(3)
+    a.g = ctypes.cast(ctypes.c_void_p(_addr(4)), fp)
+    a.beta = ctypes.cast(ctypes.c_void_p(_addr(5)), fp)
+    a.state_in = ctypes.cast(ctypes.c_void_p(_addr(6)), fp)
+    a.state_out = ctypes.cast(ctypes.c_void_p(_addr(7)), fp)
+    for key, val in kw.items():
+        if key in ("g", "beta", "b", "w", "lambda_", "state_in", "state_out"):
+            val = ctypes.cast(ctypes.c_void_p(val), fp) if val else fp()
+        setattr(a, key, val)
+    return a
+
+
+def _validate(lib, a, op=CHUNK):
+    return lib.gdr_validate(ctypes.byref(a), op)
+
+
+def test_good_args_validate(lib):
+    assert _validate(lib, good_args()) == OK
+    assert _validate(lib, good_args(T=1), STEP) == OK
+
+
+def test_null_struct(lib):
+    assert lib.gdr_validate(None, CHUNK) == E_NULL
+    assert lib.gdr_chunk_fwd(None, None) == E_NULL
+    assert b"NULL" in lib.gdr_last_error()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 8, E_ARGS),
+    ("B", 0, E_SHAPE), ("H", 0, E_SHAPE), ("T", -1, E_SHAPE),
+    ("chunk", 32, E_SHAPE), ("dk", 0, E_SHAPE),
+    ("io", 7, E_DTYPE),
+    ("decay", 3, E_ARGS), ("erase", 2, E_ARGS), ("write", -1, E_ARGS), ("qmix", 2, E_ARGS),
+    ("q", 0, E_NULL), ("o", 0, E_NULL), ("g", 0, E_NULL), ("beta", 0, E_NULL),
+    ("q", _addr(0, 8), E_ALIGN), ("state_out", _addr(7, 4), E_ALIGN), ("beta", _addr(5, 2), E_ALIGN),
+    ("dk", 96, E_UNSUP), ("dv", 40, E_UNSUP), ("dv_split", 48, E_UNSUP),
+])
+def test_single_bad_field(lib, field, value, code):
+    a = good_args(**{field: value})
+    assert _validate(lib, a) == code, lib.gdr_last_error()
+    assert lib.gdr_last_error()  # a message is set
+
+
+def test_error_paths_return_before_launch(lib):
+    # the full entry points give the same codes without touching a device
+    a = good_args(B=0)
+    assert lib.gdr_chunk_fwd(ctypes.byref(a), None) == E_SHAPE
+    a = good_args(T=5)
+    assert lib.gdr_recurrent_step(ctypes.byref(a), None) == E_SHAPE
+    a = good_args(io=1, dk=256, T=1)
+    assert lib.gdr_recurrent_step(ctypes.byref(a), None) == E_UNSUP
+
+
+def test_kind_consistency(lib):
+    assert _validate(lib, good_args(decay=0)) == E_ARGS           # g given with decay NONE
+    assert _validate(lib, good_args(decay=0, g=0)) == OK
+    assert _validate(lib, good_args(qmix=1)) == E_NULL            # lambda missing
+    assert _validate(lib, good_args(qmix=1, lambda_=_addr(8))) == OK
+    assert _validate(lib, good_args(qmix=1, lambda_=_addr(8), erase=1, b=_addr(9))) == E_ARGS
+    assert _validate(lib, good_args(erase=1)) == E_NULL           # b missing
+    assert _validate(lib, good_args(erase=1, b=_addr(9))) == OK
+    assert _validate(lib, good_args(write=1, beta=0)) == E_NULL   # erase still needs beta
+    assert _validate(lib, good_args(write=1, erase=1, beta=0, b=_addr(9), w=_addr(10))) == OK
+    assert _validate(lib, good_args(decay=2, g=_addr(4, 4))) == E_ALIGN  # channel g is vector-loaded
+
+
+def test_aliasing(lib):
+    assert _validate(lib, good_args(o=_addr(0))) == E_ARGS              # o on top of q
+    assert _validate(lib, good_args(state_out=_addr(6))) == OK          # exact in-place state
+    assert _validate(lib, good_args(state_out=_addr(6, 64))) == E_ARGS  # partial overlap
+    assert _validate(lib, good_args(o=_addr(2, 16))) == E_ARGS          # inside v
+
+
+def test_fp32_support_matrix(lib):
+    assert _validate(lib, good_args(io=0, dk=64, dv=64)) == OK
+    assert _validate(lib, good_args(io=0, dk=128)) == E_UNSUP
+    assert _validate(lib, good_args(io=0, dk=64, dv=64, dv_split=64)) == E_UNSUP
+    assert _validate(lib, good_args(io=0, dk=128, T=1), STEP) == OK
+
+
+def test_zero_length_sequence_needs_no_token_pointers(lib):
+    a = good_args(T=0, q=0, k=0, v=0, o=0, g=0, beta=0)
+    assert _validate(lib, a) == OK
+
+
+@pytest.mark.parametrize("B,H,dv,io,expect", [
+    (8, 16, 128, 1, 64),   # 128 heads -> two 64-column slices -> 256 workgroups
+    (8, 8, 128, 1, 32),    # 64 heads -> four slices
+    (1, 32, 128, 1, 16),   # 32 heads -> eight slices
+    (1, 2, 64, 0, 16),     # fp32, tiny: narrowest slice
+])
+def test_plan_slice_choice(lib, B, H, dv, io, expect):
+    a = good_args(B=B, H=H, dv=dv, io=io, dk=64 if io == 0 else 128)
+    info = GdrPlanInfo()
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+    assert info.dv_slice == expect
+    assert info.grid == B * H * (dv // expect) and info.block == 256
+    assert 0 < info.lds_bytes <= 160 * 1024
+    assert info.n_chunks == (a.T + 63) // 64

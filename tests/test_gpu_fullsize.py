@@ -1,0 +1,59 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times: the whole batch runs on the GPU, and sampled (batch, head)
+sequences (every token of each) are compared with the float64 oracle, which
+is run on just those sequences."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_17_amd as gdr
+from synth import CONFIGS, DECODE, config, make_inputs
+from tests.gpu_util import TOL, assert_parity, gpu_kwargs, run_oracle, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["gdn_bf16_b8h16t4096d128", "kda_bf16_b4h32t8192d128", "qdelta_bf16_b8h8t4096d128",
+        "gdn2_bf16_b1h32t65536d128"]
+
+
+def _sample_heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (B - 1, H - 1)}
+    while len(pairs) < n:
+        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_heads(name):
+    cfg = config(name)
+    say(f"[full] {name}: generating")
+    inp = make_inputs(cfg)
+    d = to_dev(inp)
+    say(f"[full] {name}: chunk_fwd {gdr.plan(d['q'], d['k'], d['v'], g=d['g'], beta=d['beta'], b=d['b'], w=d['w'], lam=d['lam'])}")
+    o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], **gpu_kwargs(d))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    heads = _sample_heads(cfg["B"], cfg["H"], 2 if cfg["T"] > 10000 else 3, seed=len(name))
+    say(f"[full] {name}: oracle on heads {heads}")
+    o_ref, S_ref = run_oracle(inp, heads)
+    for (b, h), orf, srf in zip(heads, o_ref, S_ref):
+        assert_parity(f"{name} b={b} h={h}", o[b, :, h].float().cpu().numpy(), S[b, h].cpu().numpy(),
+                      orf, srf, TOL[cfg["io"]])
+    del d, o, S
+    torch.cuda.empty_cache()
+
+
+def test_full_size_decode_step():
+    cfg = config(DECODE)
+    say(f"[full] {DECODE}")
+    inp = make_inputs(cfg)
+    d = to_dev(inp)
+    o, S = gdr.recurrent_step(d["q"], d["k"], d["v"], **gpu_kwargs(d))
+    torch.cuda.synchronize()
+    heads = _sample_heads(cfg["B"], cfg["H"], 16, seed=5)
+    o_ref, S_ref = run_oracle(inp, heads)
+    for (b, h), orf, srf in zip(heads, o_ref, S_ref):
+        assert_parity(f"decode b={b} h={h}", o[b, :, h].float().cpu().numpy(), S[b, h].cpu().numpy(),
+                      orf, srf, TOL[cfg["io"]])
