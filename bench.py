@@ -36,7 +36,7 @@ METRIC = "chunked gated-delta fwd tokens/s and % bf16 MFMA peak, d=128, 1 MI355X
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["common.hpp", "chunk_kernel.hpp", "step_kernel.hpp", "chunk_bf16.hip", "step.hip"]
+KERNEL_SOURCES = ["common.hpp", "chunk_kernel.hpp", "step_kernel.hpp", "chunk_instances.inc", "step.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -197,6 +197,22 @@ def cpu_baseline(name, inp, budget_s=15.0):
                 cpu_model=model, host_threads_available=len(os.sched_getaffinity(0)))
 
 
+def counters_run(name):
+    """Dispatches for HBM counter calibration: a plain device-to-device copy of
+    exactly 1 GiB (reads 1 GiB, writes 1 GiB), then the headline chunk kernel."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    bench_workload(name, 3, 0)
+    torch.cuda.synchronize()
+    print(f"counters run done: copy 1 GiB, then 3 launches of {name}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +220,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc runs: one 1 GiB device copy (calibration) and three "
+                         "launches of the headline chunk kernel, no timing output")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the chunked forward shards over (batch, head) with no "
@@ -215,6 +234,9 @@ def main():
     from synth import CONFIGS, DECODE, HEADLINE
 
     torch.cuda.init()
+    if args.counters:
+        counters_run(HEADLINE)
+        return
     head, head_inp = bench_workload(HEADLINE, args.steps, args.warmup)
     print(f"# headline {HEADLINE}: {head['kernel_ms_avg'] * 1e3:.1f} us/launch, "
           f"{head['hbm_gbs']:.0f} GB/s ({head['hbm_frac'] * 100:.1f}% HBM), "

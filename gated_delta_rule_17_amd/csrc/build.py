@@ -23,12 +23,13 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 
-SOURCES = ["chunk_bf16.hip", "chunk_f32.hip", "step.hip", "gdr_host.cpp"]
+SOURCES = ["chunk_bf16_gm0.hip", "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip", "chunk_bf16_gm3.hip",
+           "chunk_f32.hip", "step.hip", "gdr_host.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 # Device code is built without packed-fp32 instructions.
-CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
+CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result", "-Wno-pass-failed",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -115,7 +115,38 @@ struct Lay {
                 "alignment");
 };
 
-template <class IO, class CT, int DK, int DVS, bool CHAN>
+// Lower block pair p (0..9) of the 4x4 grid of 16x16 blocks, row-major over
+// I >= J: p = I (I + 1) / 2 + J.
+__device__ __forceinline__ int pair_I(int p) { return p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0)); }
+__device__ __forceinline__ int pair_J(int p) { return p - (pair_I(p) * (pair_I(p) + 1)) / 2; }
+
+// "Row tiles": the 4 x NV tiles (I = 16-token block, n = 16-column value
+// block) of U, W and O^T, NV per wave.  With 4 value blocks each wave owns a
+// value block; otherwise waves split the token blocks.
+template <int NV>
+__device__ __forceinline__ int rt_I(int t, int wave) {
+  if constexpr (NV == 4) return t;
+  else if constexpr (NV == 2) return (wave >> 1) + 2 * t;
+  else return wave;
+}
+template <int NV>
+__device__ __forceinline__ int rt_N(int t, int wave) {
+  if constexpr (NV == 4) return wave;
+  else if constexpr (NV == 2) return wave & 1;
+  else return 0;
+}
+
+// Gate modes (erase kind, write kind): 0 = (BETA, BETA), 1 = (CHANNEL, CHANNEL),
+// 2 = (CHANNEL, BETA), 3 = (BETA, CHANNEL).  Compile-time, so that every
+// global load in the chunk loop is unconditional and can be issued a chunk
+// ahead of its use.
+template <int GM> struct Gates {
+  static constexpr bool ERASE_CH = (GM == 1 || GM == 2);
+  static constexpr bool WRITE_CH = (GM == 1 || GM == 3);
+  static constexpr bool NEED_BETA = !ERASE_CH || !WRITE_CH;
+};
+
+template <class IO, class CT, int DK, int DVS, bool CHAN, int GM>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunk_fwd_kernel(ChunkParams p) {
   using L = Lay<CT, DK, DVS, CHAN>;
@@ -145,14 +176,22 @@ void chunk_fwd_kernel(ChunkParams p) {
   const int vbase = slice * DVS;
   const int nchunks = (T + CH - 1) / CH;
   const bool has_decay = p.decay != 0;
-  const bool erase_ch = p.erase == 1, write_ch = p.write == 1, qmix = p.qmix != 0;
-  const bool need_beta = !erase_ch || !write_ch;
+  constexpr bool erase_ch = Gates<GM>::ERASE_CH, write_ch = Gates<GM>::WRITE_CH;
+  constexpr bool need_beta = Gates<GM>::NEED_BETA;
+  const bool qmix = p.qmix != 0;
   const float lam = qmix ? p.lam[hh] : 0.f;
 
-  const IO* qg = reinterpret_cast<const IO*>(p.q);
-  const IO* kg = reinterpret_cast<const IO*>(p.k);
-  const IO* vg_ = reinterpret_cast<const IO*>(p.v);
-  IO* og = reinterpret_cast<IO*>(p.o);
+  // per-sequence base pointers; offsets inside one sequence are 32-bit
+  // (the host checks T * H * max(dk, dv) < 2^31)
+  const size_t seq0 = (size_t)bb * T * H + hh;  // token index of (bb, t = 0, hh)
+  const IO* qg = reinterpret_cast<const IO*>(p.q) + seq0 * DK;
+  const IO* kg = reinterpret_cast<const IO*>(p.k) + seq0 * DK;
+  const IO* vg_ = reinterpret_cast<const IO*>(p.v) + seq0 * DV + vbase;
+  IO* og = reinterpret_cast<IO*>(p.o) + seq0 * DV + vbase;
+  const float* g_seq = p.g ? p.g + seq0 * (CHAN ? DK : 1) : nullptr;
+  const float* beta_seq = p.beta ? p.beta + seq0 : nullptr;
+  const float* b_seq = p.b ? p.b + seq0 * DK : nullptr;
+  const float* w_seq = p.w ? p.w + seq0 * DV + vbase : nullptr;
 
   CT* sQ = reinterpret_cast<CT*>(smem + L::oQ);
   CT* sEbT = reinterpret_cast<CT*>(smem + L::oEbT);
@@ -183,6 +222,15 @@ void chunk_fwd_kernel(ChunkParams p) {
   View<CT> vAT;  // vAT(n, k) = A[k][n]
   if constexpr (L::CM) vAT = view(sAcm, SC, 1); else vAT = view(sArm, 1, SC);
 
+  // A and A_qk are stored whole; their strictly-upper 16x16 blocks stay zero
+  // for the whole kernel (nothing writes them), so triangular products can
+  // run over the full 64-wide k range.
+  for (int e = tid; e < CH * SC; e += NTHR) {
+    sArm[e] = (CT)0.f;
+    sAqk[e] = (CT)0.f;
+    if constexpr (L::CM) sAcm[e] = (CT)0.f;
+  }
+
   // ---- state slice in accumulators: rows c, columns v -------------------
   f32x4 Sacc[MC][NV];
 #pragma unroll
@@ -201,55 +249,67 @@ void chunk_fwd_kernel(ChunkParams p) {
   const int c0 = cg * 8, tq0 = tg * TPT;       // 8 channels x TPT tokens
   const int myI = tq0 >> 4;                    // 16-token block of my tokens
   const int vgi = tid % VG, vt = tid / VG;
-  const int vv0 = vgi * 8, vtq0 = vt * VPT;    // 8 value columns x VPT tokens
+  const int vv0 = vgi * 8, vtq0 = vt * VPT;    // 8 value columns x VPT tokens (vtq0 may pass 63: idle)
   const bool vact = vtq0 < CH;
 
   struct Raw {
     V8<IO> k[TPT], q[TPT];
     V8<float> g[TPT], bg[TPT];
     float beta[TPT];
+    float gt[TPT];  // scalar log-decay of my tokens
     float gs, bs;  // lane-indexed scalar log-decay and beta (token = lane)
     V8<IO> v[VPT];
     V8<float> w[VPT];
     float vb[VPT];
   };
 
-  auto tok_off = [&](int t) -> size_t { return ((size_t)bb * T + t) * H + hh; };
-
+  // Loads are unconditional, at token indices clamped to T - 1, so that none
+  // of them waits; rows past the end are zeroed where they are consumed.
+  // With no decay the scalar log-decay is read from a stand-in address (any
+  // readable buffer of >= B*T*H floats) and discarded.
+  const float* gsrc = has_decay ? g_seq : reinterpret_cast<const float*>(p.q) + seq0;
   auto load_raw = [&](int n, Raw& R) {
     const int t0 = n * CH;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-      const int t = t0 + tq0 + u;
-      const bool ok = t < T;
-      const size_t to = tok_off(ok ? t : T - 1);
-      R.k[u] = sel8(ok, ld8(kg + to * DK + c0));
-      R.q[u] = sel8(ok, ld8(qg + to * DK + c0));
-      if constexpr (CHAN) R.g[u] = sel8(ok, ld8(p.g + to * DK + c0));
-      if (erase_ch) R.bg[u] = sel8(ok, ld8(p.b + to * DK + c0));
-      R.beta[u] = (need_beta && ok) ? p.beta[to] : 0.f;
+      const int to = min(t0 + tq0 + u, T - 1) * H;
+      R.k[u] = ld8(kg + to * DK + c0);
+      R.q[u] = ld8(qg + to * DK + c0);
+      if constexpr (CHAN) R.g[u] = ld8(g_seq + to * DK + c0);
+      else R.gt[u] = gsrc[to];
+      if constexpr (erase_ch) R.bg[u] = ld8(b_seq + to * DK + c0);
+      if constexpr (need_beta) R.beta[u] = beta_seq[to];
     }
     {
-      const int t = t0 + lane;
-      const bool ok = t < T;
-      const size_t to = tok_off(ok ? t : T - 1);
-      R.gs = (!CHAN && has_decay && ok) ? p.g[to] : 0.f;
-      R.bs = (need_beta && ok) ? p.beta[to] : 0.f;
+      const int to = min(t0 + lane, T - 1) * H;
+      if constexpr (!CHAN) R.gs = gsrc[to];
+      if constexpr (need_beta) R.bs = beta_seq[to];
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int t = t0 + vtq0 + u;
-      const bool ok = vact && t < T;
-      const size_t to = tok_off(ok ? t : T - 1);
-      const size_t vo = to * DV + vbase + (vact ? vv0 : 0);
-      R.v[u] = sel8(ok, ld8(vg_ + vo));
-      if (write_ch) R.w[u] = sel8(ok, ld8(p.w + vo));
-      R.vb[u] = (!write_ch && ok) ? p.beta[to] : 0.f;
+      const int to = min(t0 + vtq0 + u, T - 1) * H;
+      R.v[u] = ld8(vg_ + to * DV + vv0);
+      if constexpr (write_ch) R.w[u] = ld8(w_seq + to * DV + vv0);
+      else R.vb[u] = beta_seq[to];
     }
   };
 
   Raw R;
   if (nchunks > 0) load_raw(0, R);
+
+  // Output tiles of the previous chunk, stored one chunk late: vector memory
+  // stores share the load counter, so storing right before the prefetch
+  // would make the next chunk's wait for its inputs also wait for them.
+  f32x4 pendO[NV];
+  int pend_t0 = -1;
+  auto store_out = [&](int ct0) {
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const int I = rt_I<NV>(t, wave), nt = rt_N<NV>(t, wave);
+      const int tt = ct0 + 16 * I + (lane & 15);
+      if (tt < T) gst4(og + tt * H * DV + 16 * nt + ((lane >> 4) << 2), pendO[t]);
+    }
+  };
 
   for (int n = 0; n < nchunks; ++n) {
     const int t0 = n * CH;
@@ -261,48 +321,63 @@ void chunk_fwd_kernel(ChunkParams p) {
     float gsI[8];                      // channel: G at the start of my block
     if constexpr (!CHAN) {
       // chunk-local inclusive scan of the scalar log-decay, one token per lane
-      float G = R.gs;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(G, d);
-        if (lane >= d) G += y;
-      }
-      const float GC = __shfl(G, 63);
-      const float gam = fexp(G);
-      const float tail = fexp(GC - G);
+      const float G = wave_incl_scan((has_decay && t0 + lane < T) ? R.gs : 0.f);
+      const float GC = lane_value(G, 63);
       expGC = fexp(GC);
       if (wave == 0) {
         sG[lane] = G;
-        sGam[lane] = gam;
-        sBeta[lane] = R.bs;
+        sGam[lane] = fexp(G);
+        sBeta[lane] = need_beta ? R.bs : 0.f;
+      }
+      // my tokens' cumulative decay: the scan value before my first token,
+      // plus my own tokens' log-decays
+      float Gt[TPT];
+      {
+        float run = __shfl(G, (tq0 + 63) & 63);
+        if (tq0 == 0) run = 0.f;
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+          run += (has_decay && t0 + tq0 + u < T) ? R.gt[u] : 0.f;
+          Gt[u] = run;
+        }
       }
       const bool eb_is_k = !erase_ch && !qmix;
+      float ebar[TPT][8], kt[TPT][8];
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
         const int t = tq0 + u;
-        const float gam_t = __shfl(gam, t), tail_t = __shfl(tail, t);
-        float kf[8], qv[8], eb[8], ebar[8], kt[8];
+        const float gam_t = fexp(Gt[u]), tail_t = fexp(GC - Gt[u]);
+        const bool ok = t0 + t < T;
+        float kf[8], qv[8], eb[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          kf[i] = R.k[u][i];
-          qv[i] = R.q[u][i];
-          eb[i] = erase_ch ? R.bg[u][i] * kf[i] : (qmix ? kf[i] + lam * qv[i] : kf[i]);
+          kf[i] = ok ? R.k[u][i] : 0.f;
+          qv[i] = ok ? R.q[u][i] : 0.f;
+          if constexpr (erase_ch) eb[i] = R.bg[u][i] * kf[i];
+          else eb[i] = qmix ? kf[i] + lam * qv[i] : kf[i];
         }
         st8(sK + t * SK + c0, kf);
         st8(sQ + t * SK + c0, qv);
         if (!eb_is_k) st8(sEb + t * SK + c0, eb);
-        const float es = (erase_ch ? 1.f : R.beta[u]) * gam_t;
+        float es = gam_t;
+        if constexpr (!erase_ch) es *= R.beta[u];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          ebar[i] = es * eb[i];
-          kt[i] = tail_t * kf[i];
+          ebar[u][i] = es * eb[i];
+          kt[u][i] = tail_t * kf[i];
         }
-        // transposed writes, one token at a time (TPT tokens are contiguous)
+      }
+      // transposed writes: my TPT tokens are contiguous in each row c
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          sEbT[(c0 + i) * SC + t] = (CT)ebar[i];
-          sKtT[(c0 + i) * SC + t] = (CT)kt[i];
+      for (int i = 0; i < 8; ++i) {
+        float a[TPT], c[TPT];
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+          a[u] = ebar[u][i];
+          c[u] = kt[u][i];
         }
+        stn<TPT>(sEbT + (c0 + i) * SC + tq0, a);
+        stn<TPT>(sKtT + (c0 + i) * SC + tq0, c);
       }
     } else {
       // chunk-local inclusive cumsum per key channel: local over my TPT
@@ -313,7 +388,7 @@ void chunk_fwd_kernel(ChunkParams p) {
         float s = 0.f;
 #pragma unroll
         for (int u = 0; u < TPT; ++u) {
-          s += R.g[u][i];
+          s += (t0 + tq0 + u < T) ? R.g[u][i] : 0.f;
           Gl[u][i] = s;
         }
       }
@@ -359,46 +434,61 @@ void chunk_fwd_kernel(ChunkParams p) {
       float egs[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) egs[i] = fexp(gsI[i]);
+      float ebar[TPT][8], kt[TPT][8];
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
         const int t = tq0 + u;
-        float ebar[8], kt[8], qg2[8];
+        const bool ok = t0 + t < T;
+        float qg2[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float kv = R.k[u][i], qv = R.q[u][i];
-          const float e = erase_ch ? R.bg[u][i] * kv : R.beta[u] * (qmix ? kv + lam * qv : kv);
+          const float kv = ok ? R.k[u][i] : 0.f, qv = ok ? R.q[u][i] : 0.f;
+          float e;
+          if constexpr (erase_ch) e = R.bg[u][i] * kv;
+          else e = R.beta[u] * (qmix ? kv + lam * qv : kv);
           const float f = fexp(G[u][i] - gsI[i]);    // <= 1
           const float rf = fexp(gsI[i] - G[u][i]);   // >= 1, <= exp(window)
           const float tl = fexp(tot[i] - G[u][i]);   // gamma_C / gamma_t <= 1
           const float gm = f * egs[i];                // gamma_t
-          ebar[i] = gm * e;
-          kt[i] = tl * kv;
+          ebar[u][i] = gm * e;
+          kt[u][i] = tl * kv;
           qg2[i] = gm * qv;
           kr[u][i] = rf * kv;
           ef[u][i] = f * e;
           qf[u][i] = f * qv;
         }
         st8(sQ + t * SK + c0, qg2);
+      }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          sEbT[(c0 + i) * SC + t] = (CT)ebar[i];
-          sKtT[(c0 + i) * SC + t] = (CT)kt[i];
+      for (int i = 0; i < 8; ++i) {
+        float a[TPT], c[TPT];
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+          a[u] = ebar[u][i];
+          c[u] = kt[u][i];
         }
+        stn<TPT>(sEbT + (c0 + i) * SC + tq0, a);
+        stn<TPT>(sKtT + (c0 + i) * SC + tq0, c);
       }
     }
-    // value side: Z^T
+    // value side: Z^T (my VPT tokens are contiguous in each row v)
     if (vact) {
 #pragma unroll
-      for (int u = 0; u < VPT; ++u) {
+      for (int i = 0; i < 8; ++i) {
+        float z[VPT];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float z = (write_ch ? R.w[u][i] : R.vb[u]) * R.v[u][i];
-          sZT[(vv0 + i) * SC + vtq0 + u] = (CT)z;
+        for (int u = 0; u < VPT; ++u) {
+          float gate;
+          if constexpr (write_ch) gate = R.w[u][i];
+          else gate = R.vb[u];
+          z[u] = (t0 + vtq0 + u < T) ? gate * R.v[u][i] : 0.f;
         }
+        stn<VPT>(sZT + (vv0 + i) * SC + vtq0, z);
       }
     }
     __syncthreads();
 
+    if (pend_t0 >= 0) store_out(pend_t0);
     // prefetch the next chunk while this one is processed
     if (n + 1 < nchunks) load_raw(n + 1, R);
 
@@ -408,29 +498,52 @@ void chunk_fwd_kernel(ChunkParams p) {
       const View<CT> vK = view(sK, SK, 1);
       const View<CT> vE = view(eb_is_k ? sK : sEb, SK, 1);
       const View<CT> vQ = view(sQ, SK, 1);
-      // 10 lower block pairs (I >= J) x {T, A_qk}
-      for (int task = wave; task < 20; task += 4) {
-        const int pr = task >> 1, kind = task & 1;
-        const int I = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-        const int J = pr - (I * (I + 1)) / 2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tmm(acc, vK, 16 * J, 0, kind ? vQ : vE, 16 * I, 0, DK, lane);
-        // acc[r] = (T^T or A_qk^T)[j][i] before decay and gate
+      // 10 lower block pairs (I >= J) x {T, A_qk}: wave w takes tasks
+      // w, w + 4, ..., i.e. kind = w & 1 and pairs (w >> 1) + 2 m
+      const int kind = wave & 1;
+      const View<CT> vB = kind ? vQ : vE;
+      const float* gsrc_lds = sG;
+      f32x4 acc[5];
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        const int pr = (wave >> 1) + 2 * m;
+        acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[m] = tmm<DK>(acc[m], vK, 16 * pair_J(pr), 0, vB, 16 * pair_I(pr), 0, lane);
+      }
+      // decay, gate and mask; all LDS reads first, then the stores
+      float Gi[5], gi[5];
+      f32x4 Gj[5];
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        const int pr = (wave >> 1) + 2 * m;
+        const int i = 16 * pair_I(pr) + (lane & 15);
+        Gi[m] = gsrc_lds[i];
+        gi[m] = sBeta[i];
+        Gj[m] = *reinterpret_cast<const f32x4*>(gsrc_lds + 16 * pair_J(pr) + ((lane >> 4) << 2));
+      }
+      CT* dst = kind ? sAqk : sTb;
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        const int pr = (wave >> 1) + 2 * m;
+        const int I = pair_I(pr), J = pair_J(pr);
         const int i = 16 * I + (lane & 15);
-        const float Gi = sG[i];
-        const float gi = kind ? 1.f : (erase_ch ? 1.f : sBeta[i]);
-        f32x4 val;
+        const int j0 = 16 * J + ((lane >> 4) << 2);
+        const float gate = (kind || erase_ch) ? 1.f : gi[m];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = 16 * J + ((lane >> 4) << 2) + r;
-          const float x = gi * acc[r] * fexp(Gi - sG[j]);
-          val[r] = (kind ? (j <= i) : (j < i)) ? x : 0.f;
+          const float x = gate * acc[m][r] * fexp(Gi[m] - Gj[m][r]);
+          acc[m][r] = (j0 + r < i + kind) ? x : 0.f;  // T: j < i; A_qk: j <= i
         }
-        if (kind) {
-          tst_vec(view(sAqk, 1, SC), 16 * J, 16 * I, val, lane);
-        } else {
-          tst_vec(view(sTb, 1, SC), 16 * J, 16 * I, val, lane);
-          if (I == J) tst_vec(view(sTd + I * 16 * TDS, 1, TDS), 0, 0, val, lane);
+        tst_vec(view(dst, 1, SC), 16 * J, 16 * I, acc[m], lane);
+      }
+      // the fp32 diagonal blocks of T for the substitution (waves 0 and 2
+      // hold T tiles; their diagonal pairs are m = 0, 2 (wave 0) and 1, 4 (wave 2))
+      if (!kind) {
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          const int pr = (wave >> 1) + 2 * m;
+          const int I = pair_I(pr), J = pair_J(pr);
+          if (I == J) tst_sca(view(sTd + I * 16 * TDS, TDS, 1), 0, 0, acc[m], lane);
         }
       }
       __syncthreads();
@@ -465,22 +578,33 @@ void chunk_fwd_kernel(ChunkParams p) {
           }
         }
         __syncthreads();
-        for (int task = wave; task < 2 * (I + 1); task += 4) {
-          const int J = task >> 1, kind = task & 1;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = tmm(acc, view(sK, SK, 1), 16 * J, 0, view(kind ? sXq : sXe, SK, 1), 0, 0, DK, lane);
-          const int i = 16 * I + (lane & 15);
-          f32x4 val;
+        f32x4 acc[2];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * J + ((lane >> 4) << 2) + r;
-            val[r] = (kind ? (j <= i) : (j < i)) ? acc[r] : 0.f;
-          }
-          if (kind) {
-            tst_vec(view(sAqk, 1, SC), 16 * J, 16 * I, val, lane);
-          } else {
-            tst_vec(view(sTb, 1, SC), 16 * J, 16 * I, val, lane);
-            if (I == J) tst_vec(view(sTd + I * 16 * TDS, 1, TDS), 0, 0, val, lane);
+        for (int m = 0; m < 2; ++m) {
+          const int task = wave + 4 * m;
+          acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (task < 2 * (I + 1))
+            acc[m] = tmm<DK>(acc[m], view(sK, SK, 1), 16 * (task >> 1), 0, view((task & 1) ? sXq : sXe, SK, 1), 0,
+                             0, lane);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int task = wave + 4 * m;
+          if (task < 2 * (I + 1)) {
+            const int J = task >> 1, kind = task & 1;
+            const int i = 16 * I + (lane & 15);
+            f32x4 val;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = 16 * J + ((lane >> 4) << 2) + r;
+              val[r] = (kind ? (j <= i) : (j < i)) ? acc[m][r] : 0.f;
+            }
+            if (kind) {
+              tst_vec(view(sAqk, 1, SC), 16 * J, 16 * I, val, lane);
+            } else {
+              tst_vec(view(sTb, 1, SC), 16 * J, 16 * I, val, lane);
+              if (I == J) tst_sca(view(sTd + I * 16 * TDS, TDS, 1), 0, 0, val, lane);
+            }
           }
         }
         __syncthreads();
@@ -506,13 +630,13 @@ void chunk_fwd_kernel(ChunkParams p) {
           for (int e = tid; e < CH * FBC; e += NTHR) {
             const int t = e / FBC, ch = e % FBC, c = cs + ch;
             const bool ok = t0 + t < T;
-            const size_t to = tok_off(ok ? t0 + t : T - 1);
+            const int to = min(t0 + t, T - 1) * H;
             const float kv = ok ? (float)kg[to * DK + c] : 0.f;
             const float qv = ok ? (float)qg[to * DK + c] : 0.f;
-            const float gv = ok ? p.g[to * DK + c] : 0.f;
+            const float gv = ok ? g_seq[to * DK + c] : 0.f;
             float ev;
-            if (erase_ch) ev = (ok ? p.b[to * DK + c] : 0.f) * kv;
-            else ev = (ok ? p.beta[to] : 0.f) * (qmix ? kv + lam * qv : kv);
+            if constexpr (erase_ch) ev = (ok ? b_seq[to * DK + c] : 0.f) * kv;
+            else ev = (ok ? beta_seq[to] : 0.f) * (qmix ? kv + lam * qv : kv);
             fG[t * FBS + ch] = gv;
             fE[t * FBS + ch] = ev;
             fK[t * FBS + ch] = kv;
@@ -558,7 +682,7 @@ void chunk_fwd_kernel(ChunkParams p) {
             const int j = pp - i * (i + 1) / 2;
             const float tv = (j < i) ? accT[m] : 0.f;
             sTb[i * SC + j] = (CT)tv;
-            if ((i >> 4) == (j >> 4)) sTd[(i >> 4) * 16 * TDS + (i & 15) * TDS + (j & 15)] = tv;
+            if ((i >> 4) == (j >> 4)) sTd[(i >> 4) * 16 * TDS + (j & 15) * TDS + (i & 15)] = tv;
             sAqk[i * SC + j] = (CT)accA[m];
           }
         }
@@ -567,18 +691,25 @@ void chunk_fwd_kernel(ChunkParams p) {
     }
 
     // =================== solve: A = (I + T)^{-1} ============================
-    // level 0: wave w inverts diagonal block w; lane c (< 16) owns column c
+    // level 0: wave w inverts diagonal block w by column-sweep substitution;
+    // lane c (< 16) owns column c of A_ww.  sTd holds each block as T^T
+    // (row j of sTd = column j of T), read with uniform (broadcast) loads.
     {
       const float* Td = sTd + wave * 16 * TDS;
       const int c = lane & 15;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == c) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+      // column j needs rows j+1..15: the aligned float4 groups from (j+1)/4
+      f32x4 col[15][4];
 #pragma unroll
-        for (int j = 0; j < i; ++j) s -= Td[i * TDS + j] * x[j];
-        x[i] = s;
-      }
+      for (int j = 0; j < 15; ++j)
+#pragma unroll
+        for (int q4 = (j + 1) / 4; q4 < 4; ++q4) col[j][q4] = *reinterpret_cast<const f32x4*>(Td + j * TDS + 4 * q4);
+#pragma unroll
+      for (int j = 0; j < 15; ++j)
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] -= col[j][i >> 2][i & 3] * x[j];
       if (lane < 16) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sArm[(16 * wave + i) * SC + 16 * wave + c] = (CT)x[i];
@@ -599,25 +730,27 @@ void chunk_fwd_kernel(ChunkParams p) {
     if (wave < 2) {
       const int I = 2 * wave + 1, J = 2 * wave;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tmm(acc, view(sTb, SC, 1), 16 * I, 16 * J, vAT, 16 * J, 16 * J, 16, lane);
+      acc = tmm_exact<16>(acc, view(sTb, SC, 1), 16 * I, 16 * J, vAT, 16 * J, 16 * J, lane);
       tst_vec(view(sP + wave * 16 * SP, 1, SP), 0, 0, acc, lane);  // P^T row-major
     }
     __syncthreads();
     if (wave < 2) {
       const int I = 2 * wave + 1, J = 2 * wave;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tmm(acc, vArm, 16 * I, 16 * I, view(sP + wave * 16 * SP, SP, 1), 0, 0, 16, lane);
+      acc = tmm_exact<16>(acc, vArm, 16 * I, 16 * I, view(sP + wave * 16 * SP, SP, 1), 0, 0, lane);
       acc = -acc;
       tst_sca(view(sArm, SC, 1), 16 * I, 16 * J, acc, lane);
       if constexpr (L::CM) tst_vec(view(sAcm, 1, SC), 16 * I, 16 * J, acc, lane);
     }
     __syncthreads();
-    // level 2: rows 32..63 x columns 0..31
+    // level 2: rows 32..63 x columns 0..31:
+    //   P_IJ = T[I, 0:32] A[0:32, J]   (A's upper block (0,1) is zero)
+    //   A_IJ = -A[I, 32:64] P[32:64, J]
     {
       const int I = 2 + (wave >> 1), J = wave & 1;
       CT* P2 = sP + J * 16 * SP2;  // P tiles (2,J) and (3,J), stacked along k
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tmm(acc, view(sTb, SC, 1), 16 * I, 16 * J, vAT, 16 * J, 16 * J, 32 - 16 * J, lane);
+      acc = tmm<32>(acc, view(sTb, SC, 1), 16 * I, 0, vAT, 16 * J, 0, lane);
       tst_vec(view(P2 + (I - 2) * 16, 1, SP2), 0, 0, acc, lane);
     }
     __syncthreads();
@@ -625,7 +758,7 @@ void chunk_fwd_kernel(ChunkParams p) {
       const int I = 2 + (wave >> 1), J = wave & 1;
       CT* P2 = sP + J * 16 * SP2;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tmm(acc, vArm, 16 * I, 32, view(P2, SP2, 1), 0, 0, 16 * (I - 1), lane);
+      acc = tmm<32>(acc, vArm, 16 * I, 32, view(P2, SP2, 1), 0, 0, lane);
       acc = -acc;
       tst_sca(view(sArm, SC, 1), 16 * I, 16 * J, acc, lane);
       if constexpr (L::CM) tst_vec(view(sAcm, 1, SC), 16 * I, 16 * J, acc, lane);
@@ -633,65 +766,71 @@ void chunk_fwd_kernel(ChunkParams p) {
     __syncthreads();
 
     // =================== wy: Y^T = E_bar^T A^T, U = A Z; S^T to LDS ==========
+    f32x4 accY[DK / 64][4];
+#pragma unroll
+    for (int cbi = 0; cbi < DK / 64; ++cbi)
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        accY[cbi][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accY[cbi][I] = tmm<CH>(accY[cbi][I], view(sEbT, SC, 1), 16 * (wave + 4 * cbi), 0, vArm, 16 * I, 0, lane);
+      }
+    f32x4 accW[NV];
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      accW[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accW[t] = tmm<CH>(accW[t], vArm, 16 * rt_I<NV>(t, wave), 0, view(sZT, SC, 1), 16 * rt_N<NV>(t, wave), 0,
+                        lane);
+    }
+#pragma unroll
+    for (int cbi = 0; cbi < DK / 64; ++cbi)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        tst_vec(view(sY, 1, SK), 16 * (wave + 4 * cbi), 16 * I, -accY[cbi][I], lane);  // -Y, row-major [i][c]
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NV; ++nt)
         tst_vec(view(sST, 1, SK), (wave * MC + mt) * 16, nt * 16, Sacc[mt][nt], lane);
-#pragma unroll
-    for (int cbi = 0; cbi < DK / 64; ++cbi) {
-      const int cb = wave + 4 * cbi;
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tmm(acc, view(sEbT, SC, 1), 16 * cb, 0, vArm, 16 * I, 0, 16 * (I + 1), lane);
-        tst_vec(view(sY, 1, SK), 16 * cb, 16 * I, -acc, lane);  // store -Y (row-major [i][c])
-      }
-    }
-    f32x4 accW[NV];
-#pragma unroll
-    for (int nt = 0; nt < NV; ++nt) {
-      accW[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accW[nt] = tmm(accW[nt], vArm, 16 * wave, 0, view(sZT, SC, 1), 16 * nt, 0, 16 * (wave + 1), lane);
-    }
     __syncthreads();
 
-    // =================== state: W, O, S ======================================
+    // =================== state: W = U - Y S, O^T = S^T Q^T + W^T A_qk^T ======
     f32x4 accO[NV];
 #pragma unroll
-    for (int nt = 0; nt < NV; ++nt) {
-      accW[nt] = tmm(accW[nt], view(sY, SK, 1), 16 * wave, 0, view(sST, SK, 1), 16 * nt, 0, DK, lane);
-      tst_vec(view(sWT, 1, SC), 16 * wave, 16 * nt, accW[nt], lane);
-      accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accO[nt] = tmm(accO[nt], view(sST, SK, 1), 16 * nt, 0, view(sQ, SK, 1), 16 * wave, 0, DK, lane);
-      if constexpr (!CHAN) accO[nt] *= sGam[16 * wave + (lane & 15)];
+    for (int t = 0; t < NV; ++t) {
+      const int I = rt_I<NV>(t, wave), nt = rt_N<NV>(t, wave);
+      accW[t] = tmm<DK>(accW[t], view(sY, SK, 1), 16 * I, 0, view(sST, SK, 1), 16 * nt, 0, lane);
+      accO[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accO[t] = tmm<DK>(accO[t], view(sST, SK, 1), 16 * nt, 0, view(sQ, SK, 1), 16 * I, 0, lane);
+    }
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const int I = rt_I<NV>(t, wave), nt = rt_N<NV>(t, wave);
+      tst_vec(view(sWT, 1, SC), 16 * I, 16 * nt, accW[t], lane);
+      if constexpr (!CHAN) accO[t] *= sGam[16 * I + (lane & 15)];
     }
     __syncthreads();
 #pragma unroll
-    for (int nt = 0; nt < NV; ++nt) {
-      accO[nt] = tmm(accO[nt], view(sWT, SC, 1), 16 * nt, 0, view(sAqk, SC, 1), 16 * wave, 0,
-                     16 * (wave + 1), lane);
-      const int t = t0 + 16 * wave + (lane & 15);
-      if (t < T) {
-        const int v = vbase + 16 * nt + ((lane >> 4) << 2);
-        gst4(og + tok_off(t) * DV + v, accO[nt]);
-      }
+    for (int t = 0; t < NV; ++t) {
+      const int I = rt_I<NV>(t, wave), nt = rt_N<NV>(t, wave);
+      pendO[t] = tmm<CH>(accO[t], view(sWT, SC, 1), 16 * nt, 0, view(sAqk, SC, 1), 16 * I, 0, lane);
     }
+    pend_t0 = t0;
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt) {
       const int cb = wave * MC + mt;
       f32x4 gc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gc[r] = CHAN ? sGamC[cb * 16 + ((lane >> 4) << 2) + r] : expGC;
+      if constexpr (CHAN) gc = *reinterpret_cast<const f32x4*>(sGamC + cb * 16 + ((lane >> 4) << 2));
+      else gc = f32x4{expGC, expGC, expGC, expGC};
 #pragma unroll
       for (int nt = 0; nt < NV; ++nt) {
         Sacc[mt][nt] *= gc;
-        Sacc[mt][nt] = tmm(Sacc[mt][nt], view(sKtT, SC, 1), cb * 16, 0, view(sWT, SC, 1), 16 * nt, 0, CH, lane);
+        Sacc[mt][nt] = tmm<CH>(Sacc[mt][nt], view(sKtT, SC, 1), cb * 16, 0, view(sWT, SC, 1), 16 * nt, 0, lane);
       }
     }
     __syncthreads();
   }
 
+  if (pend_t0 >= 0) store_out(pend_t0);
   if (p.state_out) {
 #pragma unroll
     for (int mt = 0; mt < MC; ++mt)

@@ -25,6 +25,26 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float fexp(float x) { return __expf(x); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts of 1, 2,
+// 4, 8 within each 16-lane row, then row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+#define GDR_DPP_ADD(ctrl, rmask)                                                                    \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rmask, \
+                                                              0xf, false))
+  GDR_DPP_ADD(0x111, 0xf);  // row_shr:1
+  GDR_DPP_ADD(0x112, 0xf);  // row_shr:2
+  GDR_DPP_ADD(0x114, 0xf);  // row_shr:4
+  GDR_DPP_ADD(0x118, 0xf);  // row_shr:8
+  GDR_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  GDR_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef GDR_DPP_ADD
+  return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 // A matrix in LDS: element (r, c) at p[r * rs + c * cs].
 template <class T>
 struct View {
@@ -45,13 +65,15 @@ template <>
 struct Mma<bf16> {
   static constexpr int KS = 32;
   typedef bf16x8 frag;
-  // rows r0..r0+15, k in [k0, k0+32); lanes whose k range starts at or past
-  // klim supply zeros.  The view must have cs == 1.
-  __device__ static __forceinline__ frag load(View<bf16> v, int r0, int k0, int klim, int lane) {
-    const int kk = k0 + ((lane >> 4) << 3);
-    frag z = {};
-    if (kk >= klim) return z;
-    return *reinterpret_cast<const frag*>(v.p + (r0 + (lane & 15)) * v.rs + kk);
+  // rows r0..r0+15, k in [k0, k0+32).  The view must have cs == 1.
+  __device__ static __forceinline__ frag load(View<bf16> v, int r0, int k0, int lane) {
+    return *reinterpret_cast<const frag*>(v.p + (r0 + (lane & 15)) * v.rs + k0 + ((lane >> 4) << 3));
+  }
+  // as load(), with zeros for k >= klim (klim - k0 a multiple of 8); branch-free
+  __device__ static __forceinline__ frag loadm(View<bf16> v, int r0, int k0, int klim, int lane) {
+    const frag f = load(v, r0, k0, lane);
+    const frag z = {};
+    return (k0 + ((lane >> 4) << 3) < klim) ? f : z;
   }
   __device__ static __forceinline__ f32x4 mma(f32x4 c, frag a, frag b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -62,10 +84,12 @@ template <>
 struct Mma<float> {
   static constexpr int KS = 4;
   typedef float frag;
-  __device__ static __forceinline__ frag load(View<float> v, int r0, int k0, int klim, int lane) {
-    const int kk = k0 + (lane >> 4);
-    if (kk >= klim) return 0.f;
-    return v.p[(r0 + (lane & 15)) * v.rs + kk * v.cs];
+  __device__ static __forceinline__ frag load(View<float> v, int r0, int k0, int lane) {
+    return v.p[(r0 + (lane & 15)) * v.rs + (k0 + (lane >> 4)) * v.cs];
+  }
+  __device__ static __forceinline__ frag loadm(View<float> v, int r0, int k0, int klim, int lane) {
+    const float f = load(v, r0, k0, lane);
+    return (k0 + (lane >> 4) < klim) ? f : 0.f;
   }
   __device__ static __forceinline__ f32x4 mma(f32x4 c, frag a, frag b) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -73,16 +97,38 @@ struct Mma<float> {
 };
 
 // acc += A[i0:i0+16, ak0:ak0+K] * B[bk0:bk0+K, j0:j0+16], with B given as its
-// transpose BT (BT[j][k] = B[k][j]).  K is a multiple of 16.
-template <class T>
-__device__ __forceinline__ f32x4 tmm(f32x4 acc, View<T> A, int i0, int ak0, View<T> BT, int j0,
-                                     int bk0, int K, int lane) {
-  constexpr int KS = Mma<T>::KS;
-#pragma unroll 4
-  for (int kk = 0; kk < K; kk += KS) {
-    acc = Mma<T>::mma(acc, Mma<T>::load(A, i0, ak0 + kk, ak0 + K, lane),
-                      Mma<T>::load(BT, j0, bk0 + kk, bk0 + K, lane));
+// transpose BT (BT[j][k] = B[k][j]).  K is a compile-time multiple of the
+// MFMA k-step; all fragments are loaded before the MFMA chain.
+template <int K, class T>
+__device__ __forceinline__ f32x4 tmm(f32x4 acc, View<T> A, int i0, int ak0, View<T> BT, int j0, int bk0,
+                                     int lane) {
+  constexpr int KS = Mma<T>::KS, NK = K / KS;
+  static_assert(K % KS == 0, "K must be a multiple of the k-step");
+  typename Mma<T>::frag a[NK], b[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    a[s] = Mma<T>::load(A, i0, ak0 + s * KS, lane);
+    b[s] = Mma<T>::load(BT, j0, bk0 + s * KS, lane);
   }
+#pragma unroll
+  for (int s = 0; s < NK; ++s) acc = Mma<T>::mma(acc, a[s], b[s]);
+  return acc;
+}
+
+// As tmm over an exact range of K16 (a multiple of 16) k values, masking the
+// lanes past the range in the last k-step.
+template <int K16, class T>
+__device__ __forceinline__ f32x4 tmm_exact(f32x4 acc, View<T> A, int i0, int ak0, View<T> BT, int j0,
+                                           int bk0, int lane) {
+  constexpr int KS = Mma<T>::KS, NK = (K16 + KS - 1) / KS;
+  typename Mma<T>::frag a[NK], b[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    a[s] = Mma<T>::loadm(A, i0, ak0 + s * KS, ak0 + K16, lane);
+    b[s] = Mma<T>::loadm(BT, j0, bk0 + s * KS, bk0 + K16, lane);
+  }
+#pragma unroll
+  for (int s = 0; s < NK; ++s) acc = Mma<T>::mma(acc, a[s], b[s]);
   return acc;
 }
 

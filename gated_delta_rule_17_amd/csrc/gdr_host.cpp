@@ -53,8 +53,9 @@ int dvs_candidates(int io, int* out) {
   return 2;
 }
 
-int chunk_lds(int io, int dk, int dvs, bool chan) {
-  return io == GDR_BF16 ? gdr::chunk_lds_bf16(dk, dvs, chan) : gdr::chunk_lds_f32(dk, dvs, chan);
+int chunk_lds(const gdr_args* a, int dvs) {
+  return gdr::chunk_lds(a->io == GDR_BF16, gdr::gate_mode(a->erase, a->write), a->dk, dvs,
+                        a->decay == GDR_DECAY_CHANNEL);
 }
 
 gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
@@ -81,8 +82,10 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
     return fail(GDR_E_ARGS, "qmix mixes the query into the beta-gated erase direction; erase must be BETA");
   const int64_t BH = int64_t(a->B) * a->H;
   const int64_t tokens = BH * a->T;
-  if (BH > (int64_t(1) << 30) || tokens * (a->dk > a->dv ? a->dk : a->dv) > (int64_t(1) << 46))
-    return fail(GDR_E_SHAPE, "problem too large");
+  const int64_t dmax = a->dk > a->dv ? a->dk : a->dv;
+  if (BH > (int64_t(1) << 30) || tokens * dmax > (int64_t(1) << 46) ||
+      int64_t(a->T) * a->H * dmax >= (int64_t(1) << 31))
+    return fail(GDR_E_SHAPE, "problem too large (need T * H * max(dk, dv) < 2^31)");
 
   const bool has_tok = a->T > 0;
   const bool need_beta = a->erase == GDR_GATE_BETA || a->write == GDR_GATE_BETA;
@@ -171,10 +174,9 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
       for (int i = nc - 1; i >= 0 && !dvs; --i)
         if (a->dv % cand[i] == 0) dvs = cand[i];
     }
-    const bool chan = a->decay == GDR_DECAY_CHANNEL;
     pi.dv_slice = dvs;
     pi.grid = static_cast<int32_t>(BH * (a->dv / dvs));
-    pi.lds_bytes = chunk_lds(a->io, a->dk, dvs, chan);
+    pi.lds_bytes = chunk_lds(a, dvs);
     pi.n_chunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
     if (pi.lds_bytes < 0)
       return fail(GDR_E_UNSUPPORTED, "no kernel instance for io=%d dk=%d slice=%d", a->io, a->dk, dvs);
@@ -211,8 +213,8 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   p.nslices = a->dv / pi.dv_slice;
   const bool chan = a->decay == GDR_DECAY_CHANNEL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = a->io == GDR_BF16 ? gdr::launch_chunk_bf16(p, a->dk, pi.dv_slice, chan, pi.grid, st)
-                                   : gdr::launch_chunk_f32(p, a->dk, pi.dv_slice, chan, pi.grid, st);
+  hipError_t e = gdr::launch_chunk(a->io == GDR_BF16, gdr::gate_mode(a->erase, a->write), p, a->dk,
+                                   pi.dv_slice, chan, pi.grid, st);
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
   return GDR_OK;
 }
