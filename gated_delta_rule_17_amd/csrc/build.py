@@ -23,7 +23,7 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 
-SOURCES = ["chunk_bf16_gm0.hip", "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip", "chunk_bf16_gm3.hip",
+SOURCES = ["pipe_gm0.hip", "pipe_gm3.hip", "chunk_bf16_gm0.hip", "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip", "chunk_bf16_gm3.hip",
            "chunk_f32.hip", "step.hip", "gdr_host.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

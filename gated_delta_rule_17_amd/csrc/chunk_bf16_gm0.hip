@@ -5,9 +5,6 @@
 #define GDR_CT bf16
 #define GDR_GM 0
 #define GDR_NAME(x) chunk_bf16_gm0_##x
-#define GDR_CASES(X) \
-  X(128, 64, false) X(128, 32, false) X(128, 16, false) \
-  X(128, 64, true)  X(128, 32, true)  X(128, 16, true)  \
-  X(64, 64, false)  X(64, 32, false)  X(64, 16, false)  \
-  X(64, 64, true)   X(64, 32, true)   X(64, 16, true)
+// no and scalar decay go to the pipelined kernel
+#define GDR_CASES(X) X(128, 64, true) X(128, 32, true) X(128, 16, true) X(64, 64, true) X(64, 32, true) X(64, 16, true)
 #include "chunk_instances.inc"

@@ -53,10 +53,15 @@ int dvs_candidates(int io, int* out) {
   return 2;
 }
 
+bool use_pipe(const gdr_args* a) { return gdr::pipe_covers(a->io == GDR_BF16, a->decay, a->erase); }
+
 int chunk_lds(const gdr_args* a, int dvs) {
+  if (use_pipe(a)) return gdr::pipe_lds(gdr::gate_mode(a->erase, a->write), a->dk, dvs);
   return gdr::chunk_lds(a->io == GDR_BF16, gdr::gate_mode(a->erase, a->write), a->dk, dvs,
                         a->decay == GDR_DECAY_CHANNEL);
 }
+
+int chunk_block(const gdr_args* a, int dvs) { return use_pipe(a) ? 64 * (dvs / 16 + 4) : 256; }
 
 gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (!a) return fail(GDR_E_NULL, "gdr_args pointer is NULL");
@@ -177,6 +182,7 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
     pi.dv_slice = dvs;
     pi.grid = static_cast<int32_t>(BH * (a->dv / dvs));
     pi.lds_bytes = chunk_lds(a, dvs);
+    pi.block = chunk_block(a, dvs);
     pi.n_chunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
     if (pi.lds_bytes < 0)
       return fail(GDR_E_UNSUPPORTED, "no kernel instance for io=%d dk=%d slice=%d", a->io, a->dk, dvs);
@@ -213,8 +219,9 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   p.nslices = a->dv / pi.dv_slice;
   const bool chan = a->decay == GDR_DECAY_CHANNEL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = gdr::launch_chunk(a->io == GDR_BF16, gdr::gate_mode(a->erase, a->write), p, a->dk,
-                                   pi.dv_slice, chan, pi.grid, st);
+  const int gm = gdr::gate_mode(a->erase, a->write);
+  hipError_t e = use_pipe(a) ? gdr::launch_pipe(gm, p, a->dk, pi.dv_slice, pi.grid, st)
+                             : gdr::launch_chunk(a->io == GDR_BF16, gm, p, a->dk, pi.dv_slice, chan, pi.grid, st);
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
   return GDR_OK;
 }

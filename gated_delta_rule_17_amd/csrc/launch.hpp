@@ -25,6 +25,24 @@ GDR_DECLARE(chunk_f32_gm2)
 GDR_DECLARE(chunk_f32_gm3)
 #undef GDR_DECLARE
 
+// Pipelined kernel (bf16 I/O, no or scalar decay, beta erase gate), one pair
+// per write-gate mode (0 = beta, 3 = per value channel).
+#define GDR_DECLARE(name)                  \
+  int name##_lds(int dk, int dvs);        \
+  hipError_t name##_launch(const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s);
+GDR_DECLARE(pipe_gm0)
+GDR_DECLARE(pipe_gm3)
+#undef GDR_DECLARE
+
+// true when the pipelined kernel covers (io, decay kind, erase kind)
+inline bool pipe_covers(bool bf16io, int decay, int erase) { return bf16io && decay != 2 && erase == 0; }
+
+inline int pipe_lds(int gm, int dk, int dvs) { return gm == 0 ? pipe_gm0_lds(dk, dvs) : pipe_gm3_lds(dk, dvs); }
+
+inline hipError_t launch_pipe(int gm, const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s) {
+  return gm == 0 ? pipe_gm0_launch(p, dk, dvs, grid, s) : pipe_gm3_launch(p, dk, dvs, grid, s);
+}
+
 // gate mode of (erase, write): 0 = (BETA, BETA), 1 = (CHANNEL, CHANNEL),
 // 2 = (CHANNEL, BETA), 3 = (BETA, CHANNEL)
 inline int gate_mode(int erase, int write) {

@@ -1,0 +1,543 @@
+// Pipelined chunkwise forward of the generalized gated delta rule on gfx950,
+// for bf16 inputs with no decay or a per-head scalar decay and the scalar
+// (beta) erase gate; the write gate may be beta or per value channel, and the
+// Q-Delta mix x = k + lambda q is supported.
+//
+// Same chunk algebra as chunk_kernel.hpp (the chunk WY form with absorbed
+// decay of "Gated DeltaNet-2: Decoupling Erase and Write in Linear
+// Attention", key design 2), regrouped so that only three small products
+// depend on the state:
+//   T   = tril(diag(beta gamma) E K^T diag(1/gamma), -1),  A = (I + T)^{-1}
+//   A_qk = tril(diag(gamma) Q K^T diag(1/gamma), 0)
+//   W   = A (Z - diag(beta gamma) E S)          (= U - Y S of the page)
+//   O   = diag(gamma) Q S + A_qk W
+//   S'  = gamma_C S + K^T diag(tail) W,          tail_j = gamma_C / gamma_j
+// with E = K, or K + lambda Q under the Q-Delta mix.  The per-token scalars
+// scale accumulator rows, so K and Q enter the MFMAs as the raw bf16 inputs
+// and the decay ratios are formed as exp(G_i - G_j) <= 1.
+//
+// Workgroup = NCW = DVS / 16 consumer waves + 4 producer waves.  At step i
+// the producers turn chunk i into LDS operands (inputs, Gram, A = (I+T)^-1)
+// while the consumers apply chunk i - 1 to the state.  Every per-chunk LDS
+// buffer is double-buffered; each step has three workgroup barriers:
+//   phase 1  producers: prefix sum of the log-decay, rows of k, q, z to LDS,
+//                       prefetch of chunk i + 1            | consumers: K S, Q S
+//   phase 2  producers: T and A_qk tiles (MFMA)            | consumers: W, O
+//   phase 3  producer wave 0: A = (I + T)^{-1}             | consumers: S update, O stores
+//
+// Consumer wave c owns value columns [16 c, 16 c + 16) of the slice and all
+// DK rows of the state, in MFMA accumulators.  Products whose contraction
+// index is the accumulator row index take the accumulator (converted to
+// bf16) directly as an MFMA operand; the k order that this imposes is
+// matched on the LDS side, by the choice of rows in row reads and of rows and
+// column groups in transposing reads (ds_read_b64_tr_b16).  State tile 2m+h,
+// accumulator row 4g+r (g = lane / 16) holds channel 32m + 8g + 4h + r.
+#pragma once
+
+#include "chunk_kernel.hpp"
+#include "common.hpp"
+
+namespace gdr {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16.  In each group of 16 lanes, lane s gives the address of
+// row s / 4, columns 4 (s % 4) .. +3 of a 4 x 16 block of 16-bit values; lane
+// i receives column i of the block (rows 0..3).  Each group has its own block.
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x4 cvt4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+__device__ __forceinline__ f32x4 cvtf4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x16: A/B fragment of lane l = 4 consecutive k (k = 4 (l / 16) .. +3)
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                  0, 0, 0);
+}
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
+// ---- LDS layout (byte offsets) -------------------------------------------
+template <int DK, int DVS>
+struct PipeLay {
+  static constexpr int SK = DK + 8;          // bf16 row stride of the [64][DK] arrays
+  static constexpr int SC = CH + 8;          // bf16 row stride of the [64][64] arrays
+  static constexpr int SZ = DVS + 8;         // bf16 row stride of Z
+  static constexpr int TDS = 20;             // fp32 row stride inside a diagonal T block
+  static constexpr int TDB = 16 * TDS + 4;   // fp32 stride between the four diagonal blocks
+  // per-chunk scalars (float offsets): G = chunk cumsum of the log-decay,
+  // beta, c_e = beta gamma, gamma, tail = gamma_C / gamma, gamma_C
+  static constexpr int sG = 0, sBeta = 64, sCE = 128, sGam = 192, sTail = 256, sGC = 320, NSC = 336;
+  static constexpr int szK = CH * SK * 2, szZ = CH * SZ * 2, szA = CH * SC * 2, szS = NSC * 4;
+  static constexpr int oK = 0;                 // 2 x [64][SK]  k rows (zero past the end)
+  static constexpr int oQ = oK + 2 * szK;      // 2 x [64][SK]  q rows
+  static constexpr int oZ = oQ + 2 * szK;      // 2 x [64][SZ]  z = gate * v rows
+  static constexpr int oAcm = oZ + 2 * szZ;    // 2 x [64][SC]  A column-major: Acm[j][i] = A[i][j]
+  static constexpr int oAqk = oAcm + 2 * szA;  // 2 x [64][SC]  A_qk row-major
+  static constexpr int oSc = oAqk + 2 * szA;   // 2 x scalars
+  static constexpr int oT = oSc + 2 * szS;     // [64][SC] T row-major, blocks below the diagonal (producers)
+  static constexpr int oTd = oT + szA;         // 4 x [16][TDS] fp32: Td[b][j][i] = T[16b+i][16b+j] (producers)
+  static constexpr int TOTAL = oTd + 4 * TDB * 4;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+  static_assert(oQ % 16 == 0 && oZ % 16 == 0 && oAcm % 16 == 0 && oAqk % 16 == 0 && oSc % 16 == 0 &&
+                    oT % 16 == 0 && oTd % 16 == 0,
+                "alignment");
+};
+
+template <int DK, int NCW, int GM>
+__global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p) {
+  constexpr int DVS = 16 * NCW;
+  using L = PipeLay<DK, DVS>;
+  constexpr int SK = L::SK, SC = L::SC, SZ = L::SZ, TDS = L::TDS, TDB = L::TDB, NSC = L::NSC;
+  constexpr int NKS = DK / 32;  // 32-channel k-steps
+  constexpr bool write_ch = (GM == 3);
+  static_assert(GM == 0 || GM == 3, "the pipelined kernel takes the beta erase gate");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  bf16* sK = reinterpret_cast<bf16*>(smem + L::oK);
+  bf16* sQ = reinterpret_cast<bf16*>(smem + L::oQ);
+  bf16* sZ = reinterpret_cast<bf16*>(smem + L::oZ);
+  bf16* sAcm = reinterpret_cast<bf16*>(smem + L::oAcm);
+  bf16* sAqk = reinterpret_cast<bf16*>(smem + L::oAqk);
+  float* sSc = reinterpret_cast<float*>(smem + L::oSc);
+  bf16* sT = reinterpret_cast<bf16*>(smem + L::oT);
+  float* sTd = reinterpret_cast<float*>(smem + L::oTd);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // workgroup -> (batch, head, value slice); blockIdx values that share a
+  // residue mod 8 run on one XCD, so the slices of a head share its L2
+  int wid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
+  const int NS = p.nslices;
+  const int bh = wid / NS, slice = wid - bh * NS;
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const int T = p.T, H = p.H, DV = p.DV;
+  const int vbase = slice * DVS;
+  const int nchunks = (T + CH - 1) / CH;
+  const bool qmix = p.qmix != 0;
+  const float lam = qmix ? p.lam[hh] : 0.f;
+  const size_t seq0 = (size_t)bb * T * H + hh;  // token row of (bb, t = 0, hh)
+
+  // A and A_qk: blocks above the diagonal are never written and stay zero,
+  // so triangular products can run over whole 32-wide k-steps
+  {
+    uint4* z = reinterpret_cast<uint4*>(smem + L::oAcm);
+    for (int e = tid; e < (4 * L::szA) / 16; e += 64 * (NCW + 4)) z[e] = uint4{0u, 0u, 0u, 0u};
+  }
+
+  if (wave < NCW) {
+    // =================== consumer ============================================
+    const int vcol = vbase + 16 * wave + l16;  // my value column
+    f32x4 S[2 * NKS];
+#pragma unroll
+    for (int m = 0; m < NKS; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 32 * m + 8 * g + 4 * h + r;
+          S[2 * m + h][r] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + vcol] : 0.f;
+        }
+    bf16* og = reinterpret_cast<bf16*>(p.o) + seq0 * DV + vcol;
+
+    // step 0: the producers build chunk 0
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
+    for (int n = 0; n < nchunks; ++n) {
+      const int buf = n & 1;
+      const bf16* Kb = sK + buf * CH * SK;
+      const bf16* Qb = sQ + buf * CH * SK;
+      const bf16* Zb = sZ + buf * CH * SZ;
+      const bf16* Ab = sAcm + buf * CH * SC;
+      const bf16* Aqb = sAqk + buf * CH * SC;
+      const float* sc = sSc + buf * NSC;
+
+      // ---- phase 1: K S and Q S (rows = tokens) ----------------------------
+      f32x4 KS[4], QS[4];
+      {
+        bf16x8 Sb[NKS];  // k slots of lane group g: channels 32 m + 8 g + e
+#pragma unroll
+        for (int m = 0; m < NKS; ++m) Sb[m] = cat8(cvt4(S[2 * m]), cvt4(S[2 * m + 1]));
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          bf16x8 kf[NKS], qf[NKS];
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) {
+            kf[m] = *reinterpret_cast<const bf16x8*>(Kb + (16 * I + l16) * SK + 32 * m + 8 * g);
+            qf[m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SK + 32 * m + 8 * g);
+          }
+          KS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+          QS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) {
+            KS[I] = mma32(kf[m], Sb[m], KS[I]);
+            QS[I] = mma32(qf[m], Sb[m], QS[I]);
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- phase 2: W = A (Z - c_e E S), O = gamma Q S + A_qk W -------------
+      // W tile 2p+h, accumulator row 4g+r holds token 32p + 8g + 4h + r
+      f32x4 Wt[4], O[4];
+      {
+        bf16x8 Rb[2];  // k slots of group g: tokens 32p + 4g + e, 32p + 16 + 4g + (e - 4)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          f32x4 R2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int I = 2 * pp + h;
+            const f32x4 z = cvtf4(lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + 16 * wave + 4 * (l16 & 3)));
+            const f32x4 ce = *reinterpret_cast<const f32x4*>(sc + L::sCE + 16 * I + 4 * g);
+            const f32x4 es = qmix ? KS[I] + lam * QS[I] : KS[I];
+            R2[h] = z - ce * es;
+          }
+          Rb[pp] = cat8(cvt4(R2[0]), cvt4(R2[1]));
+        }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m2 = 0; m2 <= pp; ++m2) {
+              const int col = 32 * pp + 8 * (l16 & 3) + 4 * h;
+              const bf16x4 a1 = lds_tr4(Ab + (32 * m2 + 4 * g + (l16 >> 2)) * SC + col);
+              const bf16x4 a2 = lds_tr4(Ab + (32 * m2 + 16 + 4 * g + (l16 >> 2)) * SC + col);
+              acc = mma32(cat8(a1, a2), Rb[m2], acc);
+            }
+            Wt[2 * pp + h] = acc;
+          }
+        bf16x8 Wb[2];  // k slots of group g: tokens 32p + 8g + e
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) Wb[pp] = cat8(cvt4(Wt[2 * pp]), cvt4(Wt[2 * pp + 1]));
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(sc + L::sGam + 16 * I + 4 * g);
+          f32x4 acc = gm * QS[I];
+#pragma unroll
+          for (int pp = 0; pp <= I / 2; ++pp) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(Aqb + (16 * I + l16) * SC + 32 * pp + 8 * g);
+            acc = mma32(af, Wb[pp], acc);
+          }
+          O[I] = acc;
+        }
+      }
+      __syncthreads();
+
+      // ---- phase 3: S = gamma_C S + K^T diag(tail) W; outputs ---------------
+      {
+        const float gC = sc[L::sGC];
+        bf16x8 Wtb[2];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const f32x4 t0 = *reinterpret_cast<const f32x4*>(sc + L::sTail + 32 * pp + 8 * g);
+          const f32x4 t1 = *reinterpret_cast<const f32x4*>(sc + L::sTail + 32 * pp + 8 * g + 4);
+          Wtb[pp] = cat8(cvt4(t0 * Wt[2 * pp]), cvt4(t1 * Wt[2 * pp + 1]));
+        }
+#pragma unroll
+        for (int m = 0; m < NKS; ++m)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            f32x4 acc = S[2 * m + h] * gC;
+            const int col = 32 * m + 8 * (l16 & 3) + 4 * h;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const bf16x4 a1 = lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col);
+              const bf16x4 a2 = lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col);
+              acc = mma32(cat8(a1, a2), Wtb[pp], acc);
+            }
+            S[2 * m + h] = acc;
+          }
+        const int t0 = n * CH;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * I + 4 * g + r;
+            if (t < T) og[t * H * DV] = (bf16)O[I][r];
+          }
+      }
+      __syncthreads();
+    }
+    if (p.state_out) {
+#pragma unroll
+      for (int m = 0; m < NKS; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 32 * m + 8 * g + 4 * h + r;
+            p.state_out[((size_t)bh * DK + c) * DV + vcol] = S[2 * m + h][r];
+          }
+    }
+  } else {
+    // =================== producers ===========================================
+    const int pw = wave - NCW, pt = tid - 64 * NCW;
+    constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;        // k, q: 8 channels x TPT tokens
+    constexpr int VG = DVS / 8, VTG = 256 / VG, VPT = (CH + VTG - 1) / VTG;  // v: 8 columns x VPT tokens
+    const int c0 = (pt % CG) * 8, tq0 = (pt / CG) * TPT;
+    const int vv0 = (pt % VG) * 8, vtq0 = (pt / VG) * VPT;
+    const bool vact = vtq0 < CH;  // wave-uniform
+    const bf16* qg = reinterpret_cast<const bf16*>(p.q) + seq0 * DK;
+    const bf16* kg = reinterpret_cast<const bf16*>(p.k) + seq0 * DK;
+    const bf16* vg = reinterpret_cast<const bf16*>(p.v) + seq0 * DV + vbase;
+    const bool has_decay = p.decay != 0;
+    // with no decay the log-decay is read from a stand-in buffer of at least
+    // B*T*H floats (q) and discarded
+    const float* gsrc = has_decay ? p.g + seq0 : reinterpret_cast<const float*>(p.q) + seq0;
+    const float* beta_seq = p.beta + seq0;
+    const float* w_seq = write_ch ? p.w + seq0 * DV + vbase : nullptr;
+
+    struct Raw {
+      bf16x8 k[TPT], q[TPT];
+      float gs, bs;  // log-decay and beta of token t0 + lane
+      bf16x8 v[VPT];
+      f32x4 w[VPT][2];
+      float vb[VPT];
+    };
+    // unconditional loads at token indices clamped to T - 1; rows past the
+    // end are zeroed where they are written to LDS
+    auto load_raw = [&](int n, Raw& R) {
+      const int t0 = n * CH;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int to = min(t0 + tq0 + u, T - 1) * H;
+        R.k[u] = *reinterpret_cast<const bf16x8*>(kg + to * DK + c0);
+        R.q[u] = *reinterpret_cast<const bf16x8*>(qg + to * DK + c0);
+      }
+      {
+        const int to = min(t0 + lane, T - 1) * H;
+        R.gs = gsrc[to];
+        R.bs = beta_seq[to];
+      }
+      if (vact) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+          const int to = min(t0 + vtq0 + u, T - 1) * H;
+          R.v[u] = *reinterpret_cast<const bf16x8*>(vg + to * DV + vv0);
+          if constexpr (write_ch) {
+            R.w[u][0] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0);
+            R.w[u][1] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0 + 4);
+          } else {
+            R.vb[u] = beta_seq[to];
+          }
+        }
+      }
+    };
+
+    // ---- phase 1: chunk scalars, k / q / z rows ------------------------------
+    auto prep = [&](int n, int buf, const Raw& R) {
+      const int t0 = n * CH;
+      const float G = wave_incl_scan((has_decay && t0 + lane < T) ? R.gs : 0.f);
+      if (pw == 0) {
+        float* sc = sSc + buf * NSC;
+        const float GC = lane_value(G, 63);
+        const float gam = fexp(G);
+        sc[L::sG + lane] = G;
+        sc[L::sBeta + lane] = R.bs;
+        sc[L::sCE + lane] = R.bs * gam;
+        sc[L::sGam + lane] = gam;
+        sc[L::sTail + lane] = fexp(GC - G);
+        if (lane == 0) sc[L::sGC] = fexp(GC);
+      }
+      bf16* Kb = sK + buf * CH * SK;
+      bf16* Qb = sQ + buf * CH * SK;
+      bf16* Zb = sZ + buf * CH * SZ;
+      const bf16x8 zero = {};
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int t = tq0 + u;
+        const bool ok = t0 + t < T;
+        *reinterpret_cast<bf16x8*>(Kb + t * SK + c0) = ok ? R.k[u] : zero;
+        *reinterpret_cast<bf16x8*>(Qb + t * SK + c0) = ok ? R.q[u] : zero;
+      }
+      if (vact) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+          const int t = vtq0 + u;
+          const bool ok = t0 + t < T;
+          float z[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float gate;
+            if constexpr (write_ch) gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
+            else gate = R.vb[u];
+            z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
+          }
+          st8(Zb + t * SZ + vv0, z);
+        }
+      }
+    };
+
+    // ---- phase 2: T (waves 0, 1) and A_qk (waves 2, 3) ----------------------
+    // Wave rows {A0, B0} = {0, 3} or {1, 2}: five 16x16 tiles each.  Tiles are
+    // computed transposed, D^T = K_J X_I^T, so that each lane holds four
+    // consecutive columns j of one row i.
+    auto gram = [&](auto a0c, auto b0c, int buf) {
+      constexpr int A0 = decltype(a0c)::value, B0 = decltype(b0c)::value;
+      const int kind = pw >> 1;  // 0: T, 1: A_qk
+      const bf16* Kb = sK + buf * CH * SK;
+      const bf16* Qb = sQ + buf * CH * SK;
+      const bf16* Xb = kind ? Qb : Kb;
+      const float* sc = sSc + buf * NSC;
+      auto xfrag = [&](int I, int s) -> bf16x8 {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(Xb + (16 * I + l16) * SK + 32 * s + 8 * g);
+        if (kind || !qmix) return x;
+        const bf16x8 q = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SK + 32 * s + 8 * g);
+        bf16x8 e;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) e[c] = (bf16)((float)x[c] + lam * (float)q[c]);
+        return e;
+      };
+      bf16x8 xa[NKS], xb[NKS];
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        xa[s] = xfrag(A0, s);
+        xb[s] = xfrag(B0, s);
+      }
+      f32x4 acca[A0 + 1], accb[B0 + 1];
+#pragma unroll
+      for (int J = 0; J <= B0; ++J) {
+        bf16x8 kf[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+          kf[s] = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + l16) * SK + 32 * s + 8 * g);
+        accb[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) accb[J] = mma32(kf[s], xb[s], accb[J]);
+        if (J <= A0) {
+          acca[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) acca[J] = mma32(kf[s], xa[s], acca[J]);
+        }
+      }
+      // decay, beta and mask; i = row (lane), j = 4 columns
+      auto post = [&](int I, int J, f32x4 acc) {
+        const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
+        const float Gi = sc[L::sG + i];
+        const f32x4 Gj = *reinterpret_cast<const f32x4*>(sc + L::sG + j0);
+        const float bi = kind ? 1.f : sc[L::sBeta + i];
+        f32x4 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float val = bi * acc[r] * fexp(Gi - Gj[r]);
+          x[r] = (j0 + r < i + kind) ? val : 0.f;  // T: j < i; A_qk: j <= i
+        }
+        if (kind) {
+          *reinterpret_cast<bf16x4*>(sAqk + buf * CH * SC + i * SC + j0) = cvt4(x);
+        } else if (J < I) {
+          *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(x);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sTd[I * TDB + (4 * g + r) * TDS + l16] = x[r];
+        }
+      };
+#pragma unroll
+      for (int J = 0; J <= A0; ++J) post(A0, J, acca[J]);
+#pragma unroll
+      for (int J = 0; J <= B0; ++J) post(B0, J, accb[J]);
+    };
+
+    // ---- phase 3: A = (I + T)^{-1}, one wave --------------------------------
+    auto solve = [&](int buf) {
+      bf16* Ab = sAcm + buf * CH * SC;
+      // level 0: lane (block g, column l16) forward-substitutes column l16 of
+      // the inverse of diagonal block g; T entries are read as broadcasts
+      {
+        const float* Td = sTd + g * TDB;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
+        f32x4 col[15][4];
+#pragma unroll
+        for (int j = 0; j < 15; ++j)
+#pragma unroll
+          for (int q4 = (j + 1) / 4; q4 < 4; ++q4) col[j][q4] = *reinterpret_cast<const f32x4*>(Td + j * TDS + 4 * q4);
+#pragma unroll
+        for (int j = 0; j < 15; ++j)
+#pragma unroll
+          for (int i = j + 1; i < 16; ++i) x[i] -= col[j][i >> 2][i & 3] * x[j];
+        st8(Ab + (16 * g + l16) * SC + 16 * g, x);
+        st8(Ab + (16 * g + l16) * SC + 16 * g + 8, x + 8);
+      }
+      // level 1: A_IJ = -A_II (T_IJ A_JJ) for (I, J) = (1, 0), (3, 2)
+      f32x4 P1[2];
+#pragma unroll
+      for (int bp = 0; bp < 2; ++bp) {
+        const int I = 2 * bp + 1, J = 2 * bp;
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(sT + (16 * I + l16) * SC + 16 * J + 4 * g);
+        const bf16x4 b = *reinterpret_cast<const bf16x4*>(Ab + (16 * J + l16) * SC + 16 * J + 4 * g);
+        P1[bp] = mma16(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int bp = 0; bp < 2; ++bp) {
+        const int I = 2 * bp + 1, J = 2 * bp;
+        const bf16x4 a = lds_tr4(Ab + (16 * I + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
+        const f32x4 r = mma16(a, cvt4(P1[bp]), f32x4{0.f, 0.f, 0.f, 0.f});
+        *reinterpret_cast<bf16x4*>(Ab + (16 * J + l16) * SC + 16 * I + 4 * g) = cvt4(-r);
+      }
+      // level 2: P_IJ = T[I, 0:32] A[0:32, J], A_IJ = -A[I, 32:64] P[32:64, J]
+      f32x4 P2[2][2];
+#pragma unroll
+      for (int I = 2; I < 4; ++I)
+#pragma unroll
+        for (int J = 0; J < 2; ++J) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sT + (16 * I + l16) * SC + 8 * g);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(Ab + (16 * J + l16) * SC + 8 * g);
+          P2[I - 2][J] = mma32(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+#pragma unroll
+      for (int I = 2; I < 4; ++I)
+#pragma unroll
+        for (int J = 0; J < 2; ++J) {
+          const bf16x4 a1 = lds_tr4(Ab + (32 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
+          const bf16x4 a2 = lds_tr4(Ab + (48 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
+          const f32x4 r = mma32(cat8(a1, a2), cat8(cvt4(P2[0][J]), cvt4(P2[1][J])), f32x4{0.f, 0.f, 0.f, 0.f});
+          *reinterpret_cast<bf16x4*>(Ab + (16 * J + l16) * SC + 16 * I + 4 * g) = cvt4(-r);
+        }
+    };
+
+    Raw R;
+    if (nchunks > 0) load_raw(0, R);
+    for (int n = 0; n < nchunks; ++n) {
+      const int buf = n & 1;
+      prep(n, buf, R);
+      if (n + 1 < nchunks) load_raw(n + 1, R);
+      __syncthreads();
+      if (pw & 1) gram(IC<1>{}, IC<2>{}, buf);
+      else gram(IC<0>{}, IC<3>{}, buf);
+      __syncthreads();
+      if (pw == 0) solve(buf);
+      __syncthreads();
+    }
+    // last step: the consumers apply the last chunk
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
+  }
+}
+
+template <int DK, int NCW>
+constexpr int pipe_lds_bytes() {
+  return PipeLay<DK, 16 * NCW>::TOTAL;
+}
+
+}  // namespace gdr
