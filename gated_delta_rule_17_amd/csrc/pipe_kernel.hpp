@@ -20,9 +20,9 @@
 // the producers turn chunk i into LDS operands (inputs, Gram, A = (I+T)^-1)
 // while the consumers apply chunk i - 1 to the state.  Every per-chunk LDS
 // buffer is double-buffered; each step has three workgroup barriers:
-//   phase 1  producers: prefix sum of the log-decay, rows of k, q, z to LDS,
-//                       prefetch of chunk i + 1            | consumers: K S, Q S
-//   phase 2  producers: T and A_qk tiles (MFMA)            | consumers: W, O
+//   phase 1  producers: rows of k, q, v and the chunk     | consumers: K S, Q S
+//            scalars to LDS
+//   phase 2  producers: T and A_qk tiles (MFMA)            | consumers: W, O to LDS
 //   phase 3  producer wave 0: A = (I + T)^{-1}             | consumers: S update, O stores
 //
 // Consumer wave c owns value columns [16 c, 16 c + 16) of the slice and all
@@ -63,35 +63,72 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                   0, 0, 0);
 }
 
-template <int N>
-struct IC {
-  static constexpr int value = N;
+// The (I, J) 16x16 tiles of T and A_qk that one producer wave computes.
+template <int N_, int I0, int J0, int I1, int J1, int I2 = 0, int J2 = 0>
+struct Tiles {
+  static constexpr int n = N_;
+  static constexpr int I(int t) { return t == 0 ? I0 : (t == 1 ? I1 : I2); }
+  static constexpr int J(int t) { return t == 0 ? J0 : (t == 1 ? J1 : J2); }
 };
+
+// Forward substitution x <- (I + T)^{-1} x for a 16 x 16 strictly lower T
+// whose row i sits in lane i of each 16-lane row (tr = its 16 floats): for
+// j = 0..14 and i > j, x[i] += T[i][j] (-x[j]), with T[i][j] broadcast from
+// lane i by the DPP row_newbcast:i operand of one v_fmac_f32.  The s_nop
+// before the first use of a column gives the two wait states that a DPP
+// source needs after a VALU write.
+template <int J, int I>
+__device__ __forceinline__ void subst_col(float (&x)[16], float tj, float nxj) {
+  if constexpr (I < 16) {
+    if constexpr (I == J + 1)
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(x[I])
+                   : "v"(tj), "v"(nxj), "n"(I));
+    else
+      asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(x[I])
+                   : "v"(tj), "v"(nxj), "n"(I));
+    subst_col<J, I + 1>(x, tj, nxj);
+  }
+}
+template <int J>
+__device__ __forceinline__ void subst(float (&x)[16], const float (&tr)[16]) {
+  if constexpr (J < 15) {
+    subst_col<J, J + 1>(x, tr[J], -x[J]);
+    subst<J + 1>(x, tr);
+  }
+}
 
 // ---- LDS layout (byte offsets) -------------------------------------------
 template <int DK, int DVS>
 struct PipeLay {
-  static constexpr int SK = DK + 8;          // bf16 row stride of the [64][DK] arrays
+  // Row strides (bf16 elements).  K rows are read both as MFMA row fragments
+  // and by transposing reads (4 rows x 4 column groups per 16 lanes); the
+  // strides below keep both free of LDS bank conflicts on gfx950.
+  static constexpr int SK = DK + (DK == 128 ? 32 : 24);  // k rows: 320 B (dk 128) / 176 B (dk 64)
+  static constexpr int SQ = DK + 8;          // q rows
   static constexpr int SC = CH + 8;          // bf16 row stride of the [64][64] arrays
   static constexpr int SZ = DVS + 8;         // bf16 row stride of Z
   static constexpr int TDS = 20;             // fp32 row stride inside a diagonal T block
-  static constexpr int TDB = 16 * TDS + 4;   // fp32 stride between the four diagonal blocks
+  static constexpr int TDB = 16 * TDS;       // fp32 stride between the four diagonal blocks
   // per-chunk scalars (float offsets): G = chunk cumsum of the log-decay,
   // beta, c_e = beta gamma, gamma, tail = gamma_C / gamma, gamma_C
   static constexpr int sG = 0, sBeta = 64, sCE = 128, sGam = 192, sTail = 256, sGC = 320, NSC = 336;
-  static constexpr int szK = CH * SK * 2, szZ = CH * SZ * 2, szA = CH * SC * 2, szS = NSC * 4;
+  static constexpr int SO = CH + 8;          // O staging: [DVS][64] (value column, token)
+  static constexpr int szK = CH * SK * 2, szQ = CH * SQ * 2, szZ = CH * SZ * 2, szA = CH * SC * 2, szS = NSC * 4;
   static constexpr int oK = 0;                 // 2 x [64][SK]  k rows (zero past the end)
-  static constexpr int oQ = oK + 2 * szK;      // 2 x [64][SK]  q rows
-  static constexpr int oZ = oQ + 2 * szK;      // 2 x [64][SZ]  z = gate * v rows
+  static constexpr int oQ = oK + 2 * szK;      // 2 x [64][SQ]  q rows
+  static constexpr int oZ = oQ + 2 * szQ;      // 2 x [64][SZ]  v rows (beta write gate) or w * v
   static constexpr int oAcm = oZ + 2 * szZ;    // 2 x [64][SC]  A column-major: Acm[j][i] = A[i][j]
   static constexpr int oAqk = oAcm + 2 * szA;  // 2 x [64][SC]  A_qk row-major
   static constexpr int oSc = oAqk + 2 * szA;   // 2 x scalars
   static constexpr int oT = oSc + 2 * szS;     // [64][SC] T row-major, blocks below the diagonal (producers)
-  static constexpr int oTd = oT + szA;         // 4 x [16][TDS] fp32: Td[b][j][i] = T[16b+i][16b+j] (producers)
-  static constexpr int TOTAL = oTd + 4 * TDB * 4;
+  static constexpr int oTd = oT + szA;         // 4 x [16][TDS] fp32: Td[b][i][j] = T[16b+i][16b+j] (producers)
+  static constexpr int oO = oTd + 4 * TDB * 4;  // [DVS][SO] output staging (consumers)
+  static constexpr int TOTAL = oO + DVS * SO * 2;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
   static_assert(oQ % 16 == 0 && oZ % 16 == 0 && oAcm % 16 == 0 && oAqk % 16 == 0 && oSc % 16 == 0 &&
-                    oT % 16 == 0 && oTd % 16 == 0,
+                    oT % 16 == 0 && oTd % 16 == 0 && oO % 16 == 0 && (SK * 2) % 16 == 0,
                 "alignment");
 };
 
@@ -99,7 +136,8 @@ template <int DK, int NCW, int GM>
 __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p) {
   constexpr int DVS = 16 * NCW;
   using L = PipeLay<DK, DVS>;
-  constexpr int SK = L::SK, SC = L::SC, SZ = L::SZ, TDS = L::TDS, TDB = L::TDB, NSC = L::NSC;
+  constexpr int SK = L::SK, SQ = L::SQ, SC = L::SC, SZ = L::SZ, SO = L::SO, TDS = L::TDS, TDB = L::TDB,
+                NSC = L::NSC;
   constexpr int NKS = DK / 32;  // 32-channel k-steps
   constexpr bool write_ch = (GM == 3);
   static_assert(GM == 0 || GM == 3, "the pipelined kernel takes the beta erase gate");
@@ -113,6 +151,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
   float* sSc = reinterpret_cast<float*>(smem + L::oSc);
   bf16* sT = reinterpret_cast<bf16*>(smem + L::oT);
   float* sTd = reinterpret_cast<float*>(smem + L::oTd);
+  bf16* sO = reinterpret_cast<bf16*>(smem + L::oO);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -142,7 +181,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
 
   if (wave < NCW) {
     // =================== consumer ============================================
-    const int vcol = vbase + 16 * wave + l16;  // my value column
+    const int vcol = vbase + 16 * wave + l16;  // my value column (state)
     f32x4 S[2 * NKS];
 #pragma unroll
     for (int m = 0; m < NKS; ++m)
@@ -153,7 +192,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
           const int c = 32 * m + 8 * g + 4 * h + r;
           S[2 * m + h][r] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + vcol] : 0.f;
         }
-    bf16* og = reinterpret_cast<bf16*>(p.o) + seq0 * DV + vcol;
+    bf16* og = reinterpret_cast<bf16*>(p.o) + seq0 * DV + vbase;
 
     // step 0: the producers build chunk 0
     __syncthreads();
@@ -162,7 +201,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     for (int n = 0; n < nchunks; ++n) {
       const int buf = n & 1;
       const bf16* Kb = sK + buf * CH * SK;
-      const bf16* Qb = sQ + buf * CH * SK;
+      const bf16* Qb = sQ + buf * CH * SQ;
       const bf16* Zb = sZ + buf * CH * SZ;
       const bf16* Ab = sAcm + buf * CH * SC;
       const bf16* Aqb = sAqk + buf * CH * SC;
@@ -180,7 +219,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
             kf[m] = *reinterpret_cast<const bf16x8*>(Kb + (16 * I + l16) * SK + 32 * m + 8 * g);
-            qf[m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SK + 32 * m + 8 * g);
+            qf[m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SQ + 32 * m + 8 * g);
           }
           KS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
           QS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -193,9 +232,9 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
       }
       __syncthreads();
 
-      // ---- phase 2: W = A (Z - c_e E S), O = gamma Q S + A_qk W -------------
+      // ---- phase 2: W = A (Z - c_e E S), O = gamma Q S + A_qk W; O to LDS ----
       // W tile 2p+h, accumulator row 4g+r holds token 32p + 8g + 4h + r
-      f32x4 Wt[4], O[4];
+      f32x4 Wt[4];
       {
         bf16x8 Rb[2];  // k slots of group g: tokens 32p + 4g + e, 32p + 16 + 4g + (e - 4)
 #pragma unroll
@@ -204,7 +243,8 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int I = 2 * pp + h;
-            const f32x4 z = cvtf4(lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + 16 * wave + 4 * (l16 & 3)));
+            f32x4 z = cvtf4(lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + 16 * wave + 4 * (l16 & 3)));
+            if constexpr (!write_ch) z *= *reinterpret_cast<const f32x4*>(sc + L::sBeta + 16 * I + 4 * g);
             const f32x4 ce = *reinterpret_cast<const f32x4*>(sc + L::sCE + 16 * I + 4 * g);
             const f32x4 es = qmix ? KS[I] + lam * QS[I] : KS[I];
             R2[h] = z - ce * es;
@@ -237,7 +277,8 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
             const bf16x8 af = *reinterpret_cast<const bf16x8*>(Aqb + (16 * I + l16) * SC + 32 * pp + 8 * g);
             acc = mma32(af, Wb[pp], acc);
           }
-          O[I] = acc;
+          // staging is [value column][token]: 4 consecutive tokens per lane
+          *reinterpret_cast<bf16x4*>(sO + (16 * wave + l16) * SO + 16 * I + 4 * g) = cvt4(acc);
         }
       }
       __syncthreads();
@@ -266,14 +307,18 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
             }
             S[2 * m + h] = acc;
           }
-        const int t0 = n * CH;
+        // outputs of the whole slice from the staging: each lane stores two
+        // runs of 8 value columns of one token; wave w covers 64 / NCW tokens
+        constexpr int TW = CH / NCW;
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 16 * I + 4 * g + r;
-            if (t < T) og[t * H * DV] = (bf16)O[I][r];
-          }
+        for (int k = 0; k < 2; ++k) {
+          const int q = 16 * (g + 4 * k);
+          const int tb = TW * wave + q % TW, cgp = q / TW;  // token base, 8-column group
+          const bf16* src = sO + (8 * cgp + (l16 >> 2)) * SO + tb + 4 * (l16 & 3);
+          const bf16x8 v = cat8(lds_tr4(src), lds_tr4(src + 4 * SO));
+          const int t = n * CH + tb + l16;
+          if (t < T) *reinterpret_cast<bf16x8*>(og + t * H * DV + 8 * cgp) = v;
+        }
       }
       __syncthreads();
     }
@@ -290,6 +335,11 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     }
   } else {
     // =================== producers ===========================================
+    // All four producer waves write the rows of chunk n to LDS (phase 1) and
+    // compute the Gram tiles (phase 2); wave 0 then computes A = (I + T)^-1
+    // (phase 3).  The loads of chunk n + 1 are spread over the three phases
+    // (k, q, then v, g, beta) so that a chunk's requests do not leave in one
+    // burst; wave 0 issues all of its share in phase 1.
     const int pw = wave - NCW, pt = tid - 64 * NCW;
     constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;        // k, q: 8 channels x TPT tokens
     constexpr int VG = DVS / 8, VTG = 256 / VG, VPT = (CH + VTG - 1) / VTG;  // v: 8 columns x VPT tokens
@@ -306,24 +356,32 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     const float* beta_seq = p.beta + seq0;
     const float* w_seq = write_ch ? p.w + seq0 * DV + vbase : nullptr;
 
+    // next chunk's inputs, prefetched into registers.  Loads are
+    // unconditional, at token indices clamped to T - 1; rows past the end are
+    // zeroed when they are written to LDS.
     struct Raw {
       bf16x8 k[TPT], q[TPT];
-      float gs, bs;  // log-decay and beta of token t0 + lane
+      float gs, bs;  // wave 3: log-decay and beta of token t0 + lane
       bf16x8 v[VPT];
-      f32x4 w[VPT][2];
-      float vb[VPT];
+      f32x4 w[write_ch ? VPT : 1][2];
     };
-    // unconditional loads at token indices clamped to T - 1; rows past the
-    // end are zeroed where they are written to LDS
-    auto load_raw = [&](int n, Raw& R) {
-      const int t0 = n * CH;
+    auto load_k = [&](int n, Raw& R) {
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
-        const int to = min(t0 + tq0 + u, T - 1) * H;
+        const int to = min(n * CH + tq0 + u, T - 1) * H;
         R.k[u] = *reinterpret_cast<const bf16x8*>(kg + to * DK + c0);
+      }
+    };
+    auto load_q = [&](int n, Raw& R) {
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int to = min(n * CH + tq0 + u, T - 1) * H;
         R.q[u] = *reinterpret_cast<const bf16x8*>(qg + to * DK + c0);
       }
-      {
+    };
+    auto load_v = [&](int n, Raw& R) {
+      const int t0 = n * CH;
+      if (pw == 3) {
         const int to = min(t0 + lane, T - 1) * H;
         R.gs = gsrc[to];
         R.bs = beta_seq[to];
@@ -336,18 +394,16 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
           if constexpr (write_ch) {
             R.w[u][0] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0);
             R.w[u][1] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0 + 4);
-          } else {
-            R.vb[u] = beta_seq[to];
           }
         }
       }
     };
 
-    // ---- phase 1: chunk scalars, k / q / z rows ------------------------------
+    // ---- phase 1: chunk scalars (wave 3), k / q / v rows --------------------
     auto prep = [&](int n, int buf, const Raw& R) {
       const int t0 = n * CH;
-      const float G = wave_incl_scan((has_decay && t0 + lane < T) ? R.gs : 0.f);
-      if (pw == 0) {
+      if (pw == 3) {
+        const float G = wave_incl_scan((has_decay && t0 + lane < T) ? R.gs : 0.f);
         float* sc = sSc + buf * NSC;
         const float GC = lane_value(G, 63);
         const float gam = fexp(G);
@@ -359,7 +415,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
         if (lane == 0) sc[L::sGC] = fexp(GC);
       }
       bf16* Kb = sK + buf * CH * SK;
-      bf16* Qb = sQ + buf * CH * SK;
+      bf16* Qb = sQ + buf * CH * SQ;
       bf16* Zb = sZ + buf * CH * SZ;
       const bf16x8 zero = {};
 #pragma unroll
@@ -367,117 +423,110 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
         const int t = tq0 + u;
         const bool ok = t0 + t < T;
         *reinterpret_cast<bf16x8*>(Kb + t * SK + c0) = ok ? R.k[u] : zero;
-        *reinterpret_cast<bf16x8*>(Qb + t * SK + c0) = ok ? R.q[u] : zero;
+        *reinterpret_cast<bf16x8*>(Qb + t * SQ + c0) = ok ? R.q[u] : zero;
       }
       if (vact) {
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
           const int t = vtq0 + u;
           const bool ok = t0 + t < T;
-          float z[8];
+          if constexpr (write_ch) {
+            float z[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float gate;
-            if constexpr (write_ch) gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
-            else gate = R.vb[u];
-            z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
+            for (int e = 0; e < 8; ++e) {
+              const float gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
+              z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
+            }
+            st8(Zb + t * SZ + vv0, z);
+          } else {
+            // beta is applied by the consumers
+            *reinterpret_cast<bf16x8*>(Zb + t * SZ + vv0) = ok ? R.v[u] : zero;
           }
-          st8(Zb + t * SZ + vv0, z);
         }
       }
     };
 
-    // ---- phase 2: T (waves 0, 1) and A_qk (waves 2, 3) ----------------------
-    // Wave rows {A0, B0} = {0, 3} or {1, 2}: five 16x16 tiles each.  Tiles are
-    // computed transposed, D^T = K_J X_I^T, so that each lane holds four
-    // consecutive columns j of one row i.
-    auto gram = [&](auto a0c, auto b0c, int buf) {
-      constexpr int A0 = decltype(a0c)::value, B0 = decltype(b0c)::value;
-      const int kind = pw >> 1;  // 0: T, 1: A_qk
+    // ---- phase 2: T and A_qk tiles ------------------------------------------
+    // Each producer wave computes both T and A_qk on its (I, J) tiles, so the
+    // K_J fragments and the decay factors exp(G_i - G_j) serve both:
+    //   wave 0: (3,0) (3,1) (0,0)   wave 1: (2,0) (2,1) (2,2)
+    //   wave 2: (1,0) (1,1)         wave 3: (3,2) (3,3)
+    // Tiles are computed transposed, D^T = K_J X_I^T, so that each lane holds
+    // four consecutive columns j of one row i.  Diagonal blocks of T go to
+    // fp32 rows for level 0 of the solve, the others to bf16 rows.
+    auto gram = [&](auto tiles, int buf) {
+      using TL = decltype(tiles);
+      constexpr int NT = TL::n;
       const bf16* Kb = sK + buf * CH * SK;
-      const bf16* Qb = sQ + buf * CH * SK;
-      const bf16* Xb = kind ? Qb : Kb;
+      const bf16* Qb = sQ + buf * CH * SQ;
       const float* sc = sSc + buf * NSC;
-      auto xfrag = [&](int I, int s) -> bf16x8 {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(Xb + (16 * I + l16) * SK + 32 * s + 8 * g);
-        if (kind || !qmix) return x;
-        const bf16x8 q = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SK + 32 * s + 8 * g);
-        bf16x8 e;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) e[c] = (bf16)((float)x[c] + lam * (float)q[c]);
-        return e;
+      // fragments of 16 rows (identical loads are merged by the compiler)
+      auto kfr = [&](int blk, int s) {
+        return *reinterpret_cast<const bf16x8*>(Kb + (16 * blk + l16) * SK + 32 * s + 8 * g);
       };
-      bf16x8 xa[NKS], xb[NKS];
+      auto qfr = [&](int blk, int s) {
+        return *reinterpret_cast<const bf16x8*>(Qb + (16 * blk + l16) * SQ + 32 * s + 8 * g);
+      };
+      f32x4 accT[NT], accA[NT];
+      float Gi[NT], bi[NT];
+      f32x4 Gj[NT];
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        xa[s] = xfrag(A0, s);
-        xb[s] = xfrag(B0, s);
-      }
-      f32x4 acca[A0 + 1], accb[B0 + 1];
+      for (int t = 0; t < NT; ++t) {
+        const int I = TL::I(t), J = TL::J(t);
+        Gi[t] = sc[L::sG + 16 * I + l16];
+        bi[t] = sc[L::sBeta + 16 * I + l16];
+        Gj[t] = *reinterpret_cast<const f32x4*>(sc + L::sG + 16 * J + 4 * g);
+        accT[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = 0; J <= B0; ++J) {
-        bf16x8 kf[NKS];
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 kj = kfr(J, s), ki = kfr(I, s), qi = qfr(I, s);
+          bf16x8 xi = ki;
+          if (qmix) {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-          kf[s] = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + l16) * SK + 32 * s + 8 * g);
-        accb[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) accb[J] = mma32(kf[s], xb[s], accb[J]);
-        if (J <= A0) {
-          acca[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) acca[J] = mma32(kf[s], xa[s], acca[J]);
+            for (int c = 0; c < 8; ++c) xi[c] = (bf16)((float)ki[c] + lam * (float)qi[c]);
+          }
+          accT[t] = mma32(kj, xi, accT[t]);
+          accA[t] = mma32(kj, qi, accA[t]);
         }
       }
-      // decay, beta and mask; i = row (lane), j = 4 columns
-      auto post = [&](int I, int J, f32x4 acc) {
+      // decay, beta and masks; i = row (lane), j = 4 columns
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int I = TL::I(t), J = TL::J(t);
         const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
-        const float Gi = sc[L::sG + i];
-        const f32x4 Gj = *reinterpret_cast<const f32x4*>(sc + L::sG + j0);
-        const float bi = kind ? 1.f : sc[L::sBeta + i];
-        f32x4 x;
+        f32x4 xT, xA;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float val = bi * acc[r] * fexp(Gi - Gj[r]);
-          x[r] = (j0 + r < i + kind) ? val : 0.f;  // T: j < i; A_qk: j <= i
+          const float e = fexp(Gi[t] - Gj[t][r]);
+          xT[r] = (j0 + r < i) ? bi[t] * accT[t][r] * e : 0.f;   // T: j < i
+          xA[r] = (j0 + r <= i) ? accA[t][r] * e : 0.f;          // A_qk: j <= i
         }
-        if (kind) {
-          *reinterpret_cast<bf16x4*>(sAqk + buf * CH * SC + i * SC + j0) = cvt4(x);
-        } else if (J < I) {
-          *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(x);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sTd[I * TDB + (4 * g + r) * TDS + l16] = x[r];
-        }
-      };
-#pragma unroll
-      for (int J = 0; J <= A0; ++J) post(A0, J, acca[J]);
-#pragma unroll
-      for (int J = 0; J <= B0; ++J) post(B0, J, accb[J]);
+        *reinterpret_cast<bf16x4*>(sAqk + buf * CH * SC + i * SC + j0) = cvt4(xA);
+        if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
+        else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
+      }
     };
 
-    // ---- phase 3: A = (I + T)^{-1}, one wave --------------------------------
+    // ---- phase 3 (wave 0): A = (I + T)^{-1} ----------------------------------
+    // level 0: lane (block g, column l16) forward-substitutes column l16 of
+    // (I + T_gg)^{-1}; lane i of each 16-lane row holds row i of T_gg.
     auto solve = [&](int buf) {
-      bf16* Ab = sAcm + buf * CH * SC;
-      // level 0: lane (block g, column l16) forward-substitutes column l16 of
-      // the inverse of diagonal block g; T entries are read as broadcasts
-      {
-        const float* Td = sTd + g * TDB;
-        float x[16];
+      float tr[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
-        f32x4 col[15][4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sTd + g * TDB + l16 * TDS + 4 * q4);
 #pragma unroll
-        for (int j = 0; j < 15; ++j)
-#pragma unroll
-          for (int q4 = (j + 1) / 4; q4 < 4; ++q4) col[j][q4] = *reinterpret_cast<const f32x4*>(Td + j * TDS + 4 * q4);
-#pragma unroll
-        for (int j = 0; j < 15; ++j)
-#pragma unroll
-          for (int i = j + 1; i < 16; ++i) x[i] -= col[j][i >> 2][i & 3] * x[j];
-        st8(Ab + (16 * g + l16) * SC + 16 * g, x);
-        st8(Ab + (16 * g + l16) * SC + 16 * g + 8, x + 8);
+        for (int e = 0; e < 4; ++e) tr[4 * q4 + e] = v[e];
       }
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
+      subst<0>(x, tr);
+      bf16* Ab = sAcm + buf * CH * SC;
+      st8(Ab + (16 * g + l16) * SC + 16 * g, x);
+      st8(Ab + (16 * g + l16) * SC + 16 * g + 8, x + 8);
+
       // level 1: A_IJ = -A_II (T_IJ A_JJ) for (I, J) = (1, 0), (3, 2)
       f32x4 P1[2];
 #pragma unroll
@@ -516,16 +565,30 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     };
 
     Raw R;
-    if (nchunks > 0) load_raw(0, R);
+    if (nchunks > 0) {
+      load_k(0, R);
+      load_q(0, R);
+      load_v(0, R);
+    }
     for (int n = 0; n < nchunks; ++n) {
       const int buf = n & 1;
+      const bool more = n + 1 < nchunks;
       prep(n, buf, R);
-      if (n + 1 < nchunks) load_raw(n + 1, R);
+      if (more) {
+        load_k(n + 1, R);
+        if (pw == 0) load_v(n + 1, R);
+      }
       __syncthreads();
-      if (pw & 1) gram(IC<1>{}, IC<2>{}, buf);
-      else gram(IC<0>{}, IC<3>{}, buf);
+      if (more) load_q(n + 1, R);
+      switch (pw) {
+        case 0: gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf); break;
+        case 1: gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf); break;
+        case 2: gram(Tiles<2, 1, 0, 1, 1>{}, buf); break;
+        default: gram(Tiles<2, 3, 2, 3, 3>{}, buf); break;
+      }
       __syncthreads();
       if (pw == 0) solve(buf);
+      else if (more) load_v(n + 1, R);
       __syncthreads();
     }
     // last step: the consumers apply the last chunk
