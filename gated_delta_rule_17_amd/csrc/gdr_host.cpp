@@ -61,7 +61,9 @@ int chunk_lds(const gdr_args* a, int dvs) {
                         a->decay == GDR_DECAY_CHANNEL);
 }
 
-int chunk_block(const gdr_args* a, int dvs) { return use_pipe(a) ? 64 * (dvs / 16 + 4) : 256; }
+// pipelined kernel: four producer waves plus two consumer waves (one for a
+// 16-column slice)
+int chunk_block(const gdr_args* a, int dvs) { return use_pipe(a) ? 64 * ((dvs >= 32 ? 2 : 1) + 4) : 256; }
 
 gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (!a) return fail(GDR_E_NULL, "gdr_args pointer is NULL");

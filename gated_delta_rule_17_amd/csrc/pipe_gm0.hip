@@ -5,5 +5,5 @@
 
 #define GDR_GM 0
 #define GDR_NAME(x) pipe_gm0_##x
-#define GDR_PIPE_CASES(X) X(128, 4) X(128, 2) X(128, 1) X(64, 4) X(64, 2) X(64, 1)
+#define GDR_PIPE_CASES(X) X(128, 64) X(128, 32) X(128, 16) X(64, 64) X(64, 32) X(64, 16)
 #include "pipe_instances.inc"

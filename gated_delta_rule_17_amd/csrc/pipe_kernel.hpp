@@ -16,7 +16,8 @@
 // scale accumulator rows, so K and Q enter the MFMAs as the raw bf16 inputs
 // and the decay ratios are formed as exp(G_i - G_j) <= 1.
 //
-// Workgroup = NCW = DVS / 16 consumer waves + 4 producer waves.  At step i
+// Workgroup = NCW consumer waves (two, or one for a 16-column slice) + 4
+// producer waves.  At step i
 // the producers turn chunk i into LDS operands (inputs, Gram, A = (I+T)^-1)
 // while the consumers apply chunk i - 1 to the state.  Every per-chunk LDS
 // buffer is double-buffered; each step has three workgroup barriers:
@@ -25,8 +26,8 @@
 //   phase 2  producers: T and A_qk tiles (MFMA)            | consumers: W, O to LDS
 //   phase 3  producer wave 0: A = (I + T)^{-1}             | consumers: S update, O stores
 //
-// Consumer wave c owns value columns [16 c, 16 c + 16) of the slice and all
-// DK rows of the state, in MFMA accumulators.  Products whose contraction
+// Consumer wave c owns 32 value columns of a 64-column slice (16 of a
+// narrower one) and all DK rows of the state, in MFMA accumulators.  Products whose contraction
 // index is the accumulator row index take the accumulator (converted to
 // bf16) directly as an MFMA operand; the k order that this imposes is
 // matched on the LDS side, by the choice of rows in row reads and of rows and
@@ -62,6 +63,11 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
                                                   0, 0, 0);
 }
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
 
 // The (I, J) 16x16 tiles of T and A_qk that one producer wave computes.
 template <int N_, int I0, int J0, int I1, int J1, int I2 = 0, int J2 = 0>
@@ -132,9 +138,17 @@ struct PipeLay {
                 "alignment");
 };
 
-template <int DK, int NCW, int GM>
-__global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p) {
-  constexpr int DVS = 16 * NCW;
+// consumer waves for a value slice of DVS columns: two 32-column waves for
+// 64, two 16-column waves for 32, one for 16
+template <int DVS>
+constexpr int pipe_ncw() {
+  return DVS >= 32 ? 2 : 1;
+}
+
+template <int DK, int DVS, int GM>
+__global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(ChunkParams p) {
+  constexpr int NCW = pipe_ncw<DVS>();
+  constexpr int NB = DVS / (16 * NCW);  // 16-column blocks per consumer wave
   using L = PipeLay<DK, DVS>;
   constexpr int SK = L::SK, SQ = L::SQ, SC = L::SC, SZ = L::SZ, SO = L::SO, TDS = L::TDS, TDB = L::TDB,
                 NSC = L::NSC;
@@ -180,18 +194,23 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
   }
 
   if (wave < NCW) {
-    // =================== consumer ============================================
-    const int vcol = vbase + 16 * wave + l16;  // my value column (state)
-    f32x4 S[2 * NKS];
+    // =================== consumers ===========================================
+    // wave c owns value columns [16 NB c, 16 NB (c + 1)) of the slice as NB
+    // blocks of 16; every LDS fragment serves the NB blocks.
+    const int cw0 = 16 * NB * wave;  // first slice column of this wave
+    f32x4 S[2 * NKS][NB];
 #pragma unroll
     for (int m = 0; m < NKS; ++m)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 32 * m + 8 * g + 4 * h + r;
-          S[2 * m + h][r] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + vcol] : 0.f;
-        }
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 32 * m + 8 * g + 4 * h + r;
+            const int v = vbase + cw0 + 16 * nb + l16;
+            S[2 * m + h][nb][r] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + v] : 0.f;
+          }
     bf16* og = reinterpret_cast<bf16*>(p.o) + seq0 * DV + vbase;
 
     // step 0: the producers build chunk 0
@@ -208,11 +227,13 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
       const float* sc = sSc + buf * NSC;
 
       // ---- phase 1: K S and Q S (rows = tokens) ----------------------------
-      f32x4 KS[4], QS[4];
+      f32x4 KS[4][NB], QS[4][NB];
       {
-        bf16x8 Sb[NKS];  // k slots of lane group g: channels 32 m + 8 g + e
+        bf16x8 Sb[NKS][NB];  // k slots of lane group g: channels 32 m + 8 g + e
 #pragma unroll
-        for (int m = 0; m < NKS; ++m) Sb[m] = cat8(cvt4(S[2 * m]), cvt4(S[2 * m + 1]));
+        for (int m = 0; m < NKS; ++m)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) Sb[m][nb] = cat8(cvt4(S[2 * m][nb]), cvt4(S[2 * m + 1][nb]));
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           bf16x8 kf[NKS], qf[NKS];
@@ -221,12 +242,15 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
             kf[m] = *reinterpret_cast<const bf16x8*>(Kb + (16 * I + l16) * SK + 32 * m + 8 * g);
             qf[m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SQ + 32 * m + 8 * g);
           }
-          KS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-          QS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < NKS; ++m) {
-            KS[I] = mma32(kf[m], Sb[m], KS[I]);
-            QS[I] = mma32(qf[m], Sb[m], QS[I]);
+          for (int nb = 0; nb < NB; ++nb) {
+            KS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            QS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) {
+              KS[I][nb] = mma32(kf[m], Sb[m][nb], KS[I][nb]);
+              QS[I][nb] = mma32(qf[m], Sb[m][nb], QS[I][nb]);
+            }
           }
         }
       }
@@ -234,51 +258,66 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
 
       // ---- phase 2: W = A (Z - c_e E S), O = gamma Q S + A_qk W; O to LDS ----
       // W tile 2p+h, accumulator row 4g+r holds token 32p + 8g + 4h + r
-      f32x4 Wt[4];
+      f32x4 Wt[4][NB];
       {
-        bf16x8 Rb[2];  // k slots of group g: tokens 32p + 4g + e, 32p + 16 + 4g + (e - 4)
+        bf16x8 Rb[2][NB];  // k slots of group g: tokens 32p + 4g + e, 32p + 16 + 4g + (e - 4)
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          f32x4 R2[2];
+        for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int I = 2 * pp + h;
-            f32x4 z = cvtf4(lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + 16 * wave + 4 * (l16 & 3)));
-            if constexpr (!write_ch) z *= *reinterpret_cast<const f32x4*>(sc + L::sBeta + 16 * I + 4 * g);
-            const f32x4 ce = *reinterpret_cast<const f32x4*>(sc + L::sCE + 16 * I + 4 * g);
-            const f32x4 es = qmix ? KS[I] + lam * QS[I] : KS[I];
-            R2[h] = z - ce * es;
+          for (int nb = 0; nb < NB; ++nb) {
+            f32x4 R2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int I = 2 * pp + h;
+              f32x4 z = cvtf4(
+                  lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + cw0 + 16 * nb + 4 * (l16 & 3)));
+              if constexpr (!write_ch) z *= *reinterpret_cast<const f32x4*>(sc + L::sBeta + 16 * I + 4 * g);
+              const f32x4 ce = *reinterpret_cast<const f32x4*>(sc + L::sCE + 16 * I + 4 * g);
+              const f32x4 es = qmix ? KS[I][nb] + lam * QS[I][nb] : KS[I][nb];
+              R2[h] = z - ce * es;
+            }
+            Rb[pp][nb] = cat8(cvt4(R2[0]), cvt4(R2[1]));
           }
-          Rb[pp] = cat8(cvt4(R2[0]), cvt4(R2[1]));
-        }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m2 = 0; m2 <= pp; ++m2) {
               const int col = 32 * pp + 8 * (l16 & 3) + 4 * h;
               const bf16x4 a1 = lds_tr4(Ab + (32 * m2 + 4 * g + (l16 >> 2)) * SC + col);
               const bf16x4 a2 = lds_tr4(Ab + (32 * m2 + 16 + 4 * g + (l16 >> 2)) * SC + col);
-              acc = mma32(cat8(a1, a2), Rb[m2], acc);
-            }
-            Wt[2 * pp + h] = acc;
-          }
-        bf16x8 Wb[2];  // k slots of group g: tokens 32p + 8g + e
+              const bf16x8 af = cat8(a1, a2);
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) Wb[pp] = cat8(cvt4(Wt[2 * pp]), cvt4(Wt[2 * pp + 1]));
+              for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Rb[m2][nb], acc[nb]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Wt[2 * pp + h][nb] = acc[nb];
+          }
+        bf16x8 Wb[2][NB];  // k slots of group g: tokens 32p + 8g + e
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) Wb[pp][nb] = cat8(cvt4(Wt[2 * pp][nb]), cvt4(Wt[2 * pp + 1][nb]));
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           const f32x4 gm = *reinterpret_cast<const f32x4*>(sc + L::sGam + 16 * I + 4 * g);
-          f32x4 acc = gm * QS[I];
+          f32x4 acc[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb] = gm * QS[I][nb];
 #pragma unroll
           for (int pp = 0; pp <= I / 2; ++pp) {
             const bf16x8 af = *reinterpret_cast<const bf16x8*>(Aqb + (16 * I + l16) * SC + 32 * pp + 8 * g);
-            acc = mma32(af, Wb[pp], acc);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Wb[pp][nb], acc[nb]);
           }
           // staging is [value column][token]: 4 consecutive tokens per lane
-          *reinterpret_cast<bf16x4*>(sO + (16 * wave + l16) * SO + 16 * I + 4 * g) = cvt4(acc);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<bf16x4*>(sO + (cw0 + 16 * nb + l16) * SO + 16 * I + 4 * g) = cvt4(acc[nb]);
         }
       }
       __syncthreads();
@@ -286,32 +325,39 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
       // ---- phase 3: S = gamma_C S + K^T diag(tail) W; outputs ---------------
       {
         const float gC = sc[L::sGC];
-        bf16x8 Wtb[2];
+        bf16x8 Wtb[2][NB];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const f32x4 t0 = *reinterpret_cast<const f32x4*>(sc + L::sTail + 32 * pp + 8 * g);
           const f32x4 t1 = *reinterpret_cast<const f32x4*>(sc + L::sTail + 32 * pp + 8 * g + 4);
-          Wtb[pp] = cat8(cvt4(t0 * Wt[2 * pp]), cvt4(t1 * Wt[2 * pp + 1]));
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            Wtb[pp][nb] = cat8(cvt4(t0 * Wt[2 * pp][nb]), cvt4(t1 * Wt[2 * pp + 1][nb]));
         }
 #pragma unroll
         for (int m = 0; m < NKS; ++m)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            f32x4 acc = S[2 * m + h] * gC;
+            f32x4 acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = S[2 * m + h][nb] * gC;
             const int col = 32 * m + 8 * (l16 & 3) + 4 * h;
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
               const bf16x4 a1 = lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col);
               const bf16x4 a2 = lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col);
-              acc = mma32(cat8(a1, a2), Wtb[pp], acc);
+              const bf16x8 af = cat8(a1, a2);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Wtb[pp][nb], acc[nb]);
             }
-            S[2 * m + h] = acc;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) S[2 * m + h][nb] = acc[nb];
           }
-        // outputs of the whole slice from the staging: each lane stores two
-        // runs of 8 value columns of one token; wave w covers 64 / NCW tokens
+        // outputs of the whole slice from the staging: each lane stores 2 NB
+        // runs of 8 value columns of one token; wave c covers 64 / NCW tokens
         constexpr int TW = CH / NCW;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < 2 * NB; ++k) {
           const int q = 16 * (g + 4 * k);
           const int tb = TW * wave + q % TW, cgp = q / TW;  // token base, 8-column group
           const bf16* src = sO + (8 * cgp + (l16 >> 2)) * SO + tb + 4 * (l16 & 3);
@@ -328,10 +374,13 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int c = 32 * m + 8 * g + 4 * h + r;
-            p.state_out[((size_t)bh * DK + c) * DV + vcol] = S[2 * m + h][r];
-          }
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int c = 32 * m + 8 * g + 4 * h + r;
+              const int v = vbase + cw0 + 16 * nb + l16;
+              p.state_out[((size_t)bh * DK + c) * DV + v] = S[2 * m + h][nb][r];
+            }
     }
   } else {
     // =================== producers ===========================================
@@ -340,7 +389,13 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     // (phase 3).  The loads of chunk n + 1 are spread over the three phases
     // (k, q, then v, g, beta) so that a chunk's requests do not leave in one
     // burst; wave 0 issues all of its share in phase 1.
-    const int pw = wave - NCW, pt = tid - 64 * NCW;
+    // One loop per producer wave, with the wave's role fixed at compile time:
+    // a single loop with run-time role branches makes the register allocator
+    // move prefetched registers at the branch joins, which waits for loads
+    // still in flight.
+    auto producer = [&](auto pwc) {
+    constexpr int pw = decltype(pwc)::value;
+    const int pt = tid - 64 * NCW;
     constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;        // k, q: 8 channels x TPT tokens
     constexpr int VG = DVS / 8, VTG = 256 / VG, VPT = (CH + VTG - 1) / VTG;  // v: 8 columns x VPT tokens
     const int c0 = (pt % CG) * 8, tq0 = (pt / CG) * TPT;
@@ -381,7 +436,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     };
     auto load_v = [&](int n, Raw& R) {
       const int t0 = n * CH;
-      if (pw == 3) {
+      if constexpr (pw == 3) {
         const int to = min(t0 + lane, T - 1) * H;
         R.gs = gsrc[to];
         R.bs = beta_seq[to];
@@ -402,7 +457,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
     // ---- phase 1: chunk scalars (wave 3), k / q / v rows --------------------
     auto prep = [&](int n, int buf, const Raw& R) {
       const int t0 = n * CH;
-      if (pw == 3) {
+      if constexpr (pw == 3) {
         const float G = wave_incl_scan((has_decay && t0 + lane < T) ? R.gs : 0.f);
         float* sc = sSc + buf * NSC;
         const float GC = lane_value(G, 63);
@@ -576,31 +631,44 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void pipe_fwd_kernel(ChunkParams p)
       prep(n, buf, R);
       if (more) {
         load_k(n + 1, R);
-        if (pw == 0) load_v(n + 1, R);
+        if constexpr (pw == 0) load_v(n + 1, R);
       }
       __syncthreads();
       if (more) load_q(n + 1, R);
-      switch (pw) {
-        case 0: gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf); break;
-        case 1: gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf); break;
-        case 2: gram(Tiles<2, 1, 0, 1, 1>{}, buf); break;
-        default: gram(Tiles<2, 3, 2, 3, 3>{}, buf); break;
+      if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf);
+      else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf);
+      else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf);
+      else gram(Tiles<2, 3, 2, 3, 3>{}, buf);
+      // wave 3 (fewest Gram tiles) loads v, g and beta here, early, since its
+      // prefix sum waits for g at the start of the next step
+      if constexpr (pw == 3) {
+        if (more) load_v(n + 1, R);
       }
       __syncthreads();
-      if (pw == 0) solve(buf);
-      else if (more) load_v(n + 1, R);
+      if constexpr (pw == 0) {
+        solve(buf);
+      } else if constexpr (pw != 3) {
+        if (more) load_v(n + 1, R);
+      }
       __syncthreads();
     }
     // last step: the consumers apply the last chunk
     __syncthreads();
     __syncthreads();
     __syncthreads();
+    };
+    switch (wave - NCW) {
+      case 0: producer(IC<0>{}); break;
+      case 1: producer(IC<1>{}); break;
+      case 2: producer(IC<2>{}); break;
+      default: producer(IC<3>{}); break;
+    }
   }
 }
 
-template <int DK, int NCW>
+template <int DK, int DVS>
 constexpr int pipe_lds_bytes() {
-  return PipeLay<DK, 16 * NCW>::TOTAL;
+  return PipeLay<DK, DVS>::TOTAL;
 }
 
 }  // namespace gdr
