@@ -234,22 +234,27 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         for (int m = 0; m < NKS; ++m)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) Sb[m][nb] = cat8(cvt4(S[2 * m][nb]), cvt4(S[2 * m + 1][nb]));
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          bf16x8 kf[NKS], qf[NKS];
+        // fragments of row block I + 1 are loaded while block I multiplies
+        bf16x8 kf[2][NKS], qf[2][NKS];
+        auto load_kq = [&](int I, int slot) {
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
-            kf[m] = *reinterpret_cast<const bf16x8*>(Kb + (16 * I + l16) * SK + 32 * m + 8 * g);
-            qf[m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SQ + 32 * m + 8 * g);
+            kf[slot][m] = *reinterpret_cast<const bf16x8*>(Kb + (16 * I + l16) * SK + 32 * m + 8 * g);
+            qf[slot][m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SQ + 32 * m + 8 * g);
           }
+        };
+        load_kq(0, 0);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (I < 3) load_kq(I + 1, (I + 1) & 1);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             KS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
             QS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-              KS[I][nb] = mma32(kf[m], Sb[m][nb], KS[I][nb]);
-              QS[I][nb] = mma32(qf[m], Sb[m][nb], QS[I][nb]);
+              KS[I][nb] = mma32(kf[I & 1][m], Sb[m][nb], KS[I][nb]);
+              QS[I][nb] = mma32(qf[I & 1][m], Sb[m][nb], QS[I][nb]);
             }
           }
         }
@@ -334,25 +339,28 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
           for (int nb = 0; nb < NB; ++nb)
             Wtb[pp][nb] = cat8(cvt4(t0 * Wt[2 * pp][nb]), cvt4(t1 * Wt[2 * pp + 1][nb]));
         }
+        // transposed K fragments of state tile j + 1 are loaded while tile j
+        // multiplies
+        bf16x8 kt[2][2];
+        auto load_kt = [&](int j, int slot) {
+          const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
 #pragma unroll
-        for (int m = 0; m < NKS; ++m)
+          for (int pp = 0; pp < 2; ++pp)
+            kt[slot][pp] = cat8(lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col),
+                                lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col));
+        };
+        load_kt(0, 0);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            f32x4 acc[NB];
+        for (int j = 0; j < 2 * NKS; ++j) {
+          if (j + 1 < 2 * NKS) load_kt(j + 1, (j + 1) & 1);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb] = S[2 * m + h][nb] * gC;
-            const int col = 32 * m + 8 * (l16 & 3) + 4 * h;
+          for (int nb = 0; nb < NB; ++nb) {
+            f32x4 acc = S[j][nb] * gC;
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-              const bf16x4 a1 = lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col);
-              const bf16x4 a2 = lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col);
-              const bf16x8 af = cat8(a1, a2);
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Wtb[pp][nb], acc[nb]);
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) S[2 * m + h][nb] = acc[nb];
+            for (int pp = 0; pp < 2; ++pp) acc = mma32(kt[j & 1][pp], Wtb[pp][nb], acc);
+            S[j][nb] = acc;
           }
+        }
         // outputs of the whole slice from the staging: each lane stores 2 NB
         // runs of 8 value columns of one token; wave c covers 64 / NCW tokens
         constexpr int TW = CH / NCW;
