@@ -36,7 +36,8 @@ METRIC = "chunked gated-delta fwd tokens/s and % bf16 MFMA peak, d=128, 1 MI355X
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["common.hpp", "chunk_kernel.hpp", "step_kernel.hpp", "chunk_instances.inc", "step.hip"]
+KERNEL_SOURCES = ["common.hpp", "chunk_kernel.hpp", "pipe_kernel.hpp", "pipe_instances.inc", "pipe_gm0.hip",
+                  "step_kernel.hpp", "chunk_instances.inc", "step.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -261,12 +262,11 @@ def main():
         print(f"# cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores", file=sys.stderr,
               flush=True)
 
-    traffic = traffic_from_profile("chunk_fwd_kernel", HEADLINE)
+    traffic = traffic_from_profile("pipe_fwd_kernel", HEADLINE)
     roof = dict(bound="hbm", achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=head["hbm_frac"], traffic=traffic,
                 algorithmic_bytes_per_launch=head["algorithmic_bytes"],
-                kernel_ms_avg=head["kernel_ms_avg"], kernel="chunk_fwd_kernel<bf16,bf16,128,%d,false>"
-                % head["plan"]["dv_slice"])
+                kernel_ms_avg=head["kernel_ms_avg"], kernel="pipe_fwd_kernel<128,%d,0>" % head["plan"]["dv_slice"])
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
