@@ -403,6 +403,10 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // still in flight.
     auto producer = [&](auto pwc) {
     constexpr int pw = decltype(pwc)::value;
+    // the chunk scalars (prefix sum of the log-decay) come from wave 1, which
+    // has a SIMD of its own (with two consumer waves, producer waves 2 and 3
+    // share their SIMDs with them)
+    constexpr int kScanWave = 1;
     const int pt = tid - 64 * NCW;
     constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;        // k, q: 8 channels x TPT tokens
     constexpr int VG = DVS / 8, VTG = 256 / VG, VPT = (CH + VTG - 1) / VTG;  // v: 8 columns x VPT tokens
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // zeroed when they are written to LDS.
     struct Raw {
       bf16x8 k[TPT], q[TPT];
-      float gs, bs;  // wave 3: log-decay and beta of token t0 + lane
+      float gs, bs;  // scan wave: log-decay and beta of token t0 + lane
       bf16x8 v[VPT];
       f32x4 w[write_ch ? VPT : 1][2];
     };
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     };
     auto load_v = [&](int n, Raw& R) {
       const int t0 = n * CH;
-      if constexpr (pw == 3) {
+      if constexpr (pw == kScanWave) {
         const int to = min(t0 + lane, T - 1) * H;
         R.gs = gsrc[to];
         R.bs = beta_seq[to];
@@ -462,10 +466,10 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       }
     };
 
-    // ---- phase 1: chunk scalars (wave 3), k / q / v rows --------------------
+    // ---- phase 1: chunk scalars (scan wave), k / q / v rows ----------------
     auto prep = [&](int n, int buf, const Raw& R) {
       const int t0 = n * CH;
-      if constexpr (pw == 3) {
+      if constexpr (pw == kScanWave) {
         const float G = wave_incl_scan((has_decay && t0 + lane < T) ? R.gs : 0.f);
         float* sc = sSc + buf * NSC;
         const float GC = lane_value(G, 63);
@@ -647,15 +651,15 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf);
       else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf);
       else gram(Tiles<2, 3, 2, 3, 3>{}, buf);
-      // wave 3 (fewest Gram tiles) loads v, g and beta here, early, since its
-      // prefix sum waits for g at the start of the next step
-      if constexpr (pw == 3) {
+      // the scan wave loads v, g and beta here, early, since its prefix sum
+      // waits for g at the start of the next step
+      if constexpr (pw == kScanWave) {
         if (more) load_v(n + 1, R);
       }
       __syncthreads();
       if constexpr (pw == 0) {
         solve(buf);
-      } else if constexpr (pw != 3) {
+      } else if constexpr (pw != kScanWave) {
         if (more) load_v(n + 1, R);
       }
       __syncthreads();

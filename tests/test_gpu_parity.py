@@ -223,3 +223,39 @@ def test_step_qdelta_contraction_on_gpu():
     after = (v - torch.einsum("bhcv,bhc->bhv", S1.cpu().double(), x)).norm(dim=-1)
     expect = (1 - beta * a).abs() * before
     assert torch.allclose(after, expect, rtol=1e-4, atol=1e-5)
+
+
+def _yu_chunk_form(inp):
+    """The chunk WY form with Y = A E_bar and U = A Z ([GDN2] key design 2), in
+    float64 through the oracle's literal mirror, on every (b, h)."""
+    from oracle.chunk_mirror import chunk_forward_one
+    q, k, v = (inp[x].double().numpy() for x in ("q", "k", "v"))
+    B, T, H, dk = k.shape
+    dv = v.shape[3]
+    beta = inp["beta"].double().numpy()
+    g = inp["g"].double().numpy() if inp["g"] is not None else np.zeros((B, T, H))
+    lam = inp["lam"].double().numpy() if inp["lam"] is not None else np.zeros(H)
+    S0 = inp["state"].double().numpy() if inp["state"] is not None else np.zeros((B, H, dk, dv))
+    o = np.zeros((B, T, H, dv))
+    S = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            x = k[b, :, h] + (lam[h] * q[b, :, h] if inp["qmix"] else 0.0)
+            e = beta[b, :, h, None] * x
+            z = beta[b, :, h, None] * v[b, :, h]
+            gg = np.repeat(g[b, :, h, None], dk, axis=1)
+            o[b, :, h], S[b, h] = chunk_forward_one(q[b, :, h], k[b, :, h], e, z, gg, S0[b, h])
+    return o, S
+
+
+@pytest.mark.parametrize("name", ["gdn_bf16_small", "qdelta_bf16_small", "deltanet_bf16", "gdn_tail300"])
+def test_pipelined_kernel_matches_the_yu_chunk_form(name):
+    """The pipelined kernel evaluates W = A (Z - E_bar S) instead of the page's
+    U - Y S; checked here directly against the Y / U form."""
+    cfg = CASES[name]
+    inp = make_inputs(cfg)
+    assert inp["decay"] != "channel" and inp["erase"] == "beta" and cfg["io"] == "bf16"
+    say(f"[Y/U form] {name}")
+    o, S = run_chunk(inp)
+    o_ref, S_ref = _yu_chunk_form(inp)
+    assert_parity(name, o, S, o_ref, S_ref, TOL[cfg["io"]])
