@@ -23,7 +23,8 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 
-SOURCES = ["pipe_gm0.hip", "pipe_gm3.hip", "chunk_bf16_gm0.hip", "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip", "chunk_bf16_gm3.hip",
+SOURCES = ["chan_gm0.hip", "chan_gm1.hip", "chan_gm2.hip", "chan_gm3.hip", "pipe_gm0.hip", "pipe_gm3.hip",
+           "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip",
            "chunk_f32.hip", "step.hip", "gdr_host.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -53,17 +53,24 @@ int dvs_candidates(int io, int* out) {
   return 2;
 }
 
-bool use_pipe(const gdr_args* a) { return gdr::pipe_covers(a->io == GDR_BF16, a->decay, a->erase); }
-
-int chunk_lds(const gdr_args* a, int dvs) {
-  if (use_pipe(a)) return gdr::pipe_lds(gdr::gate_mode(a->erase, a->write), a->dk, dvs);
-  return gdr::chunk_lds(a->io == GDR_BF16, gdr::gate_mode(a->erase, a->write), a->dk, dvs,
-                        a->decay == GDR_DECAY_CHANNEL);
+gdr::ChunkKernel kernel_for(const gdr_args* a) {
+  return gdr::chunk_kernel_for(a->io == GDR_BF16, a->decay, a->erase);
 }
 
-// pipelined kernel: four producer waves plus two consumer waves (one for a
-// 16-column slice)
-int chunk_block(const gdr_args* a, int dvs) { return use_pipe(a) ? 64 * ((dvs >= 32 ? 2 : 1) + 4) : 256; }
+int chunk_lds(const gdr_args* a, int dvs) {
+  const int gm = gdr::gate_mode(a->erase, a->write);
+  switch (kernel_for(a)) {
+    case gdr::kPipe: return gdr::pipe_lds(gm, a->dk, dvs);
+    case gdr::kChan: return gdr::chan_lds(gm, a->dk, dvs);
+    default: return gdr::chunk_lds(a->io == GDR_BF16, gm, a->dk, dvs, a->decay == GDR_DECAY_CHANNEL);
+  }
+}
+
+// pipelined kernels: four producer waves plus two consumer waves (one for a
+// 16-column slice); one-pass kernel: four waves
+int chunk_block(const gdr_args* a, int dvs) {
+  return kernel_for(a) != gdr::kOnePass ? 64 * ((dvs >= 32 ? 2 : 1) + 4) : 256;
+}
 
 gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (!a) return fail(GDR_E_NULL, "gdr_args pointer is NULL");
@@ -222,8 +229,12 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   const bool chan = a->decay == GDR_DECAY_CHANNEL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int gm = gdr::gate_mode(a->erase, a->write);
-  hipError_t e = use_pipe(a) ? gdr::launch_pipe(gm, p, a->dk, pi.dv_slice, pi.grid, st)
-                             : gdr::launch_chunk(a->io == GDR_BF16, gm, p, a->dk, pi.dv_slice, chan, pi.grid, st);
+  hipError_t e;
+  switch (kernel_for(a)) {
+    case gdr::kPipe: e = gdr::launch_pipe(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;
+    case gdr::kChan: e = gdr::launch_chan(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;
+    default: e = gdr::launch_chunk(a->io == GDR_BF16, gm, p, a->dk, pi.dv_slice, chan, pi.grid, st); break;
+  }
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
   return GDR_OK;
 }

@@ -9,16 +9,15 @@
 
 namespace gdr {
 
-// Chunk kernel instances, one pair of functions per (precision, gate mode):
-// *_lds returns the LDS bytes of an instance or -1 if there is none; *_launch
-// launches it (hipErrorInvalidValue if there is none).
+// One-pass chunk kernel instances, one pair of functions per (precision, gate
+// mode): *_lds returns the LDS bytes of an instance or -1 if there is none;
+// *_launch launches it (hipErrorInvalidValue if there is none).  With bf16
+// I/O only the per-channel erase gate under no or a scalar decay runs here.
 #define GDR_DECLARE(name)                                                                      \
   int name##_lds(int dk, int dvs, bool chan);                                                  \
   hipError_t name##_launch(const ChunkParams& p, int dk, int dvs, bool chan, int grid, hipStream_t s);
-GDR_DECLARE(chunk_bf16_gm0)
 GDR_DECLARE(chunk_bf16_gm1)
 GDR_DECLARE(chunk_bf16_gm2)
-GDR_DECLARE(chunk_bf16_gm3)
 GDR_DECLARE(chunk_f32_gm0)
 GDR_DECLARE(chunk_f32_gm1)
 GDR_DECLARE(chunk_f32_gm2)
@@ -34,8 +33,44 @@ GDR_DECLARE(pipe_gm0)
 GDR_DECLARE(pipe_gm3)
 #undef GDR_DECLARE
 
-// true when the pipelined kernel covers (io, decay kind, erase kind)
-inline bool pipe_covers(bool bf16io, int decay, int erase) { return bf16io && decay != 2 && erase == 0; }
+// Pipelined kernel for a per-key-channel decay (bf16 I/O), one pair per gate
+// mode.
+#define GDR_DECLARE(name)                  \
+  int name##_lds(int dk, int dvs);        \
+  hipError_t name##_launch(const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s);
+GDR_DECLARE(chan_gm0)
+GDR_DECLARE(chan_gm1)
+GDR_DECLARE(chan_gm2)
+GDR_DECLARE(chan_gm3)
+#undef GDR_DECLARE
+
+// Chunk kernel chosen for (io, decay kind, erase kind): the pipelined kernels
+// take bf16 I/O, the scalar-decay one the beta erase gate only; the rest go to
+// the one-pass kernel.
+enum ChunkKernel { kOnePass = 0, kPipe = 1, kChan = 2 };
+inline ChunkKernel chunk_kernel_for(bool bf16io, int decay, int erase) {
+  if (!bf16io) return kOnePass;
+  if (decay == 2) return kChan;
+  return erase == 0 ? kPipe : kOnePass;
+}
+
+inline int chan_lds(int gm, int dk, int dvs) {
+  switch (gm) {
+    case 0: return chan_gm0_lds(dk, dvs);
+    case 1: return chan_gm1_lds(dk, dvs);
+    case 2: return chan_gm2_lds(dk, dvs);
+    default: return chan_gm3_lds(dk, dvs);
+  }
+}
+
+inline hipError_t launch_chan(int gm, const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s) {
+  switch (gm) {
+    case 0: return chan_gm0_launch(p, dk, dvs, grid, s);
+    case 1: return chan_gm1_launch(p, dk, dvs, grid, s);
+    case 2: return chan_gm2_launch(p, dk, dvs, grid, s);
+    default: return chan_gm3_launch(p, dk, dvs, grid, s);
+  }
+}
 
 inline int pipe_lds(int gm, int dk, int dvs) { return gm == 0 ? pipe_gm0_lds(dk, dvs) : pipe_gm3_lds(dk, dvs); }
 
@@ -55,10 +90,9 @@ inline int chunk_lds(bool bf16io, int gm, int dk, int dvs, bool chan) {
     case 1: return chunk_f32_gm1_lds(dk, dvs, chan);
     case 2: return chunk_f32_gm2_lds(dk, dvs, chan);
     case 3: return chunk_f32_gm3_lds(dk, dvs, chan);
-    case 4: return chunk_bf16_gm0_lds(dk, dvs, chan);
     case 5: return chunk_bf16_gm1_lds(dk, dvs, chan);
     case 6: return chunk_bf16_gm2_lds(dk, dvs, chan);
-    default: return chunk_bf16_gm3_lds(dk, dvs, chan);
+    default: return -1;
   }
 }
 
@@ -69,10 +103,9 @@ inline hipError_t launch_chunk(bool bf16io, int gm, const ChunkParams& p, int dk
     case 1: return chunk_f32_gm1_launch(p, dk, dvs, chan, grid, s);
     case 2: return chunk_f32_gm2_launch(p, dk, dvs, chan, grid, s);
     case 3: return chunk_f32_gm3_launch(p, dk, dvs, chan, grid, s);
-    case 4: return chunk_bf16_gm0_launch(p, dk, dvs, chan, grid, s);
     case 5: return chunk_bf16_gm1_launch(p, dk, dvs, chan, grid, s);
     case 6: return chunk_bf16_gm2_launch(p, dk, dvs, chan, grid, s);
-    default: return chunk_bf16_gm3_launch(p, dk, dvs, chan, grid, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

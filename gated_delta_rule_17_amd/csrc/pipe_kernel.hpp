@@ -105,6 +105,68 @@ __device__ __forceinline__ void subst(float (&x)[16], const float (&tr)[16]) {
   }
 }
 
+// A = (I + T)^{-1} for the 64 x 64 strictly lower T of a chunk, on one wave.
+// T's four diagonal 16x16 blocks come as fp32 rows (block b, row i at
+// Td + b TDB + i TDS), the blocks below the diagonal as bf16 rows of Tm (row
+// stride SC); A goes to Ab column-major (Ab[j SC + i] = A[i][j]), whose blocks
+// above the diagonal must already be zero.
+//   level 0: lane (block g, column l16) forward-substitutes column l16 of
+//            (I + T_gg)^{-1}; lane i of each 16-lane row holds row i of T_gg
+//   level 1: A_IJ = -A_II (T_IJ A_JJ) for (I, J) = (1, 0), (3, 2)
+//   level 2: P_IJ = T[I, 0:32] A[0:32, J], A_IJ = -A[I, 32:64] P[32:64, J]
+template <int SC, int TDS, int TDB>
+__device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, bf16* Ab, int g, int l16) {
+  float tr[16];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(Td + g * TDB + l16 * TDS + 4 * q4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tr[4 * q4 + e] = v[e];
+  }
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
+  subst<0>(x, tr);
+  st8(Ab + (16 * g + l16) * SC + 16 * g, x);
+  st8(Ab + (16 * g + l16) * SC + 16 * g + 8, x + 8);
+
+  // level 1: A_IJ = -A_II (T_IJ A_JJ) for (I, J) = (1, 0), (3, 2)
+  f32x4 P1[2];
+#pragma unroll
+  for (int bp = 0; bp < 2; ++bp) {
+    const int I = 2 * bp + 1, J = 2 * bp;
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(Tm + (16 * I + l16) * SC + 16 * J + 4 * g);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(Ab + (16 * J + l16) * SC + 16 * J + 4 * g);
+    P1[bp] = mma16(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+#pragma unroll
+  for (int bp = 0; bp < 2; ++bp) {
+    const int I = 2 * bp + 1, J = 2 * bp;
+    const bf16x4 a = lds_tr4(Ab + (16 * I + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
+    const f32x4 r = mma16(a, cvt4(P1[bp]), f32x4{0.f, 0.f, 0.f, 0.f});
+    *reinterpret_cast<bf16x4*>(Ab + (16 * J + l16) * SC + 16 * I + 4 * g) = cvt4(-r);
+  }
+  // level 2: P_IJ = T[I, 0:32] A[0:32, J], A_IJ = -A[I, 32:64] P[32:64, J]
+  f32x4 P2[2][2];
+#pragma unroll
+  for (int I = 2; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Tm + (16 * I + l16) * SC + 8 * g);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Ab + (16 * J + l16) * SC + 8 * g);
+      P2[I - 2][J] = mma32(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+#pragma unroll
+  for (int I = 2; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) {
+      const bf16x4 a1 = lds_tr4(Ab + (32 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
+      const bf16x4 a2 = lds_tr4(Ab + (48 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
+      const f32x4 r = mma32(cat8(a1, a2), cat8(cvt4(P2[0][J]), cvt4(P2[1][J])), f32x4{0.f, 0.f, 0.f, 0.f});
+      *reinterpret_cast<bf16x4*>(Ab + (16 * J + l16) * SC + 16 * I + 4 * g) = cvt4(-r);
+    }
+}
+
 // ---- LDS layout (byte offsets) -------------------------------------------
 template <int DK, int DVS>
 struct PipeLay {
@@ -576,60 +638,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     };
 
     // ---- phase 3 (wave 0): A = (I + T)^{-1} ----------------------------------
-    // level 0: lane (block g, column l16) forward-substitutes column l16 of
-    // (I + T_gg)^{-1}; lane i of each 16-lane row holds row i of T_gg.
-    auto solve = [&](int buf) {
-      float tr[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(sTd + g * TDB + l16 * TDS + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) tr[4 * q4 + e] = v[e];
-      }
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
-      subst<0>(x, tr);
-      bf16* Ab = sAcm + buf * CH * SC;
-      st8(Ab + (16 * g + l16) * SC + 16 * g, x);
-      st8(Ab + (16 * g + l16) * SC + 16 * g + 8, x + 8);
-
-      // level 1: A_IJ = -A_II (T_IJ A_JJ) for (I, J) = (1, 0), (3, 2)
-      f32x4 P1[2];
-#pragma unroll
-      for (int bp = 0; bp < 2; ++bp) {
-        const int I = 2 * bp + 1, J = 2 * bp;
-        const bf16x4 a = *reinterpret_cast<const bf16x4*>(sT + (16 * I + l16) * SC + 16 * J + 4 * g);
-        const bf16x4 b = *reinterpret_cast<const bf16x4*>(Ab + (16 * J + l16) * SC + 16 * J + 4 * g);
-        P1[bp] = mma16(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
-      }
-#pragma unroll
-      for (int bp = 0; bp < 2; ++bp) {
-        const int I = 2 * bp + 1, J = 2 * bp;
-        const bf16x4 a = lds_tr4(Ab + (16 * I + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
-        const f32x4 r = mma16(a, cvt4(P1[bp]), f32x4{0.f, 0.f, 0.f, 0.f});
-        *reinterpret_cast<bf16x4*>(Ab + (16 * J + l16) * SC + 16 * I + 4 * g) = cvt4(-r);
-      }
-      // level 2: P_IJ = T[I, 0:32] A[0:32, J], A_IJ = -A[I, 32:64] P[32:64, J]
-      f32x4 P2[2][2];
-#pragma unroll
-      for (int I = 2; I < 4; ++I)
-#pragma unroll
-        for (int J = 0; J < 2; ++J) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sT + (16 * I + l16) * SC + 8 * g);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(Ab + (16 * J + l16) * SC + 8 * g);
-          P2[I - 2][J] = mma32(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
-        }
-#pragma unroll
-      for (int I = 2; I < 4; ++I)
-#pragma unroll
-        for (int J = 0; J < 2; ++J) {
-          const bf16x4 a1 = lds_tr4(Ab + (32 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
-          const bf16x4 a2 = lds_tr4(Ab + (48 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
-          const f32x4 r = mma32(cat8(a1, a2), cat8(cvt4(P2[0][J]), cvt4(P2[1][J])), f32x4{0.f, 0.f, 0.f, 0.f});
-          *reinterpret_cast<bf16x4*>(Ab + (16 * J + l16) * SC + 16 * I + 4 * g) = cvt4(-r);
-        }
-    };
+    auto solve = [&](int buf) { solve_inverse<SC, TDS, TDB>(sTd, sT, sAcm + buf * CH * SC, g, l16); };
 
     Raw R;
     if (nchunks > 0) {

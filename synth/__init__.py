@@ -68,6 +68,8 @@ def make_inputs(cfg: dict) -> dict:
     ``cfg`` keys: variant, B, H, T, d (or dk, dv), io ("bf16"|"f32"),
     q_scale, decay_shift, state_std, seed, and optional stress knobs:
       decay      override the variant's decay kind ("none"|"scalar"|"channel")
+      erase, write  override the gate kinds ("beta"|"channel")
+      qmix       override the Q-Delta mix (True|False)
       g_const    use this constant log-decay instead of -softplus(N + c)
       b_scale    erase gate b = b_scale * sigmoid(N)  (e.g. 2 for b in [0, 2])
       lam_const  use this lambda for every head instead of U[0, 1]
@@ -77,6 +79,9 @@ def make_inputs(cfg: dict) -> dict:
     """
     decay, erase, write, qmix = KINDS[cfg["variant"]]
     decay = cfg.get("decay", decay)
+    erase = cfg.get("erase", erase)
+    write = cfg.get("write", write)
+    qmix = bool(cfg.get("qmix", qmix))
     B, H, T = cfg["B"], cfg["H"], cfg["T"]
     dk = cfg.get("dk", cfg.get("d"))
     dv = cfg.get("dv", cfg.get("d"))

@@ -169,10 +169,12 @@ def test_plan_slice_choice(lib, B, H, dv, io, expect):
     assert info.n_chunks == (a.T + 63) // 64
 
 
-@pytest.mark.parametrize("decay,erase,block", [(2, 0, 256), (1, 1, 256), (0, 0, 384), (1, 0, 384)])
+@pytest.mark.parametrize("decay,erase,block", [(2, 0, 384), (2, 1, 384), (1, 1, 256), (0, 1, 256), (0, 0, 384),
+                                               (1, 0, 384)])
 def test_plan_kernel_choice(lib, decay, erase, block):
-    """Per-channel decay or the per-channel erase gate use the one-pass kernel
-    (one 256-thread workgroup); the rest of the bf16 cases the pipelined one."""
+    """bf16 I/O runs a pipelined kernel (four producer and two consumer waves)
+    except with the per-channel erase gate under no or a scalar decay, which
+    runs the one-pass kernel (one 256-thread workgroup)."""
     a = good_args(B=8, H=16, dv=128, decay=decay, erase=erase, **({"g": 0} if decay == 0 else {}))
     if erase == 1:
         a.b = a.beta

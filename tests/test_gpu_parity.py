@@ -58,6 +58,13 @@ CASES = {
     "gdn_dk128_dv64": config(H, B=1, H=2, T=256, dk=128, dv=64, decay_shift=-2.0),
     "kda_dk64_dv128": config(K, B=1, H=2, T=256, dk=64, dv=128, decay_shift=-3.0),
     "gdn2_f32_dv32": config(F, variant="gdn2", B=1, H=2, T=200, dk=64, dv=32, decay_shift=-4.0),
+    # gate kinds beyond the variants' own: one gate per key or value channel
+    # with the other beta, and the Q-Delta mix, under both decay kinds
+    "kda_erase_ch": config(K, B=1, H=2, T=320, erase="channel", decay_shift=-3.0),
+    "kda_write_ch": config(K, B=1, H=2, T=200, write="channel", decay_shift=-3.0),
+    "kda_qmix": config(K, B=1, H=2, T=256, qmix=True, decay_shift=-3.0),
+    "gdn_erase_ch": config(H, B=1, H=2, T=200, erase="channel", decay_shift=-3.0),
+    "gdn_write_ch": config(H, B=1, H=2, T=320, write="channel", decay_shift=-3.0),
     # nonzero initial state with per-channel decay
     "kda_state": config(K, B=1, H=2, T=192, decay_shift=-4.0, state_std=0.05),
 }

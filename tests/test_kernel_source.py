@@ -1,16 +1,20 @@
-"""Static checks on the pipelined kernel source (CPU only).
+"""Static checks on the pipelined kernel sources (CPU only).
 
 The consumer and producer waves of one workgroup run different code paths
 that must execute the same number of workgroup barriers, or the workgroup
 never finishes.  This counts __syncthreads() in each path, inside and outside
-its chunk loop, straight from the source text.
+its chunk loop, straight from the source text, as a function a N + b of the
+number of chunks N.
 """
 
 import os
 import re
 
-SRC = os.path.join(os.path.dirname(__file__), "..", "gated_delta_rule_17_amd", "csrc", "pipe_kernel.hpp")
-LOOP = "for (int n = 0; n < nchunks; ++n)"
+import pytest
+
+CSRC = os.path.join(os.path.dirname(__file__), "..", "gated_delta_rule_17_amd", "csrc")
+SOURCES = ["pipe_kernel.hpp", "chan_kernel.hpp"]
+LOOP_RE = re.compile(r"for \(int n = 0; n (<|<=) nchunks; \+\+n\)")
 
 
 def _block(text, start):
@@ -37,22 +41,28 @@ def barrier_counts(src):
     prod, _ = _block(src[start + len("if (wave < NCW) ") + len(cons):], "else {")
     out = {}
     for name, path in (("consumer", cons), ("producer", prod)):
-        loop, rest = _block(path, LOOP)
-        out[name] = (loop.count("__syncthreads()"), rest.count("__syncthreads()"))
+        m = LOOP_RE.search(path)
+        assert m, name
+        loop, rest = _block(path, m.group(0))
+        a = loop.count("__syncthreads()")
+        extra = 1 if m.group(1) == "<=" else 0  # iterations: N or N + 1
+        out[name] = (a, a * extra + rest.count("__syncthreads()"))
     return out
 
 
-def test_consumer_and_producer_paths_have_equal_barrier_counts():
-    counts = barrier_counts(open(SRC).read())
+@pytest.mark.parametrize("name", SOURCES)
+def test_consumer_and_producer_paths_have_equal_barrier_counts(name):
+    counts = barrier_counts(open(os.path.join(CSRC, name)).read())
     assert counts["consumer"] == counts["producer"], counts
     assert counts["consumer"][0] >= 1
 
 
-def test_count_detects_an_extra_producer_barrier():
-    src = open(SRC).read()
+@pytest.mark.parametrize("name", SOURCES)
+def test_count_detects_an_extra_producer_barrier(name):
+    src = open(os.path.join(CSRC, name)).read()
     i = src.index("=================== producers")
-    j = src.index(LOOP, i)
-    k = src.index("{", j) + 1
+    m = LOOP_RE.search(src, i)
+    k = src.index("{", m.start()) + 1
     planted = src[:k] + "\n__syncthreads();\n" + src[k:]
     counts = barrier_counts(planted)
     assert counts["consumer"] != counts["producer"], counts
