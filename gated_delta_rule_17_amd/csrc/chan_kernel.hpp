@@ -20,9 +20,13 @@
 // chunk with a window above WINDOW_LIMIT computes its tiles exactly in fp32
 // instead (see gram_exact).
 //
-// Workgroup: consumer waves as in pipe_kernel.hpp plus 4 producer waves, one
-// chunk step = three barriers.  The per-chunk operands do not fit twice in
-// LDS, so each has one buffer, written in the phase after its last reader:
+// Workgroup: the consumer waves of pipe_kernel.hpp, four elementwise waves
+// (wave w owns the 16-token block w: log-decay prefix sums, bounded factors,
+// E_bar, Q_gamma, K_tail, its diagonal Gram tile) and two Gram waves (the six
+// tiles below the diagonal blocks; wave 0 inverts I + T, wave 1 forms the
+// per-(block, channel) constants of the next chunk).  One chunk step = three
+// barriers.  The per-chunk operands do not fit twice in LDS, so each has one
+// buffer, written in the phase after its last reader:
 //   region   written by producers      read by consumers
 //   E        phase 3 (E_bar, Q_gamma)  phase 1 (K S, Q S)
 //   P        phase 1 (kb, xe, xq)      -           (producer Gram, phase 2;
@@ -31,6 +35,9 @@
 //   K        phase 1 of the next step  phase 3 (state update)
 //            (K_tail)
 // Region E is free in phase 2 and holds the exact-Gram staging when needed.
+// Inside the step loops every prefetch is unconditional (indices clamped to
+// the last chunk): registers written under a condition that the compiler
+// cannot tie to their use stay live across the whole loop.
 #pragma once
 
 #include "chunk_kernel.hpp"
@@ -38,13 +45,22 @@
 
 namespace gdr {
 
+// A list of (I, J) 16x16 tiles of T and A_qk: TileList<I0, J0, I1, J1, ...>
+template <int... P>
+struct TileList {
+  static constexpr int n = sizeof...(P) / 2;
+  static constexpr int v[sizeof...(P)] = {P...};
+  static constexpr int I(int t) { return v[2 * t]; }
+  static constexpr int J(int t) { return v[2 * t + 1]; }
+};
+
 template <int DK, int DVS>
 struct ChanLay {
   static constexpr int SE = DK + 8;                       // rows of E_bar, Q_gamma, kb, xe, xq
   static constexpr int SKT = DK + (DK == 128 ? 32 : 24);  // K_tail rows (transposing reads)
   static constexpr int SC = CH + 8, SZ = DVS + 8, SO = CH + 8;
   static constexpr int TDS = 20, TDB = 16 * TDS;
-  static constexpr int SW = DK / 16;  // channels per slab of the exact Gram
+  static constexpr int SW = DK / 32;  // channels per slab of the exact Gram
   static constexpr int szE = CH * SE * 2;
   static constexpr int oEb = 0, oQg = oEb + szE;                            // region E
   static constexpr int oKb = oQg + szE, oXe = oKb + szE, oXq = oXe + szE;  // region P
@@ -52,23 +68,31 @@ struct ChanLay {
   static constexpr int oAcm = oZ + CH * SZ * 2;
   static constexpr int oAqk = oAcm + CH * SC * 2;
   static constexpr int oKt = oAqk + CH * SC * 2;  // region K
-  static constexpr int oSc = oKt + CH * SKT * 2;  // 2 x gamma_C [DK] fp32 (chunk parity)
-  static constexpr int oD = oSc + 2 * DK * 4;     // d_IJ [6][DK] fp32
-  static constexpr int oEs = oD + 6 * DK * 4;     // exp(G at block starts) [4][DK] fp32
-  static constexpr int oT = oEs + 4 * DK * 4;     // T below the diagonal, bf16 rows
-  static constexpr int oTd = oT + CH * SC * 2;    // diagonal blocks of T, fp32 rows
-  static constexpr int oFlag = oTd + 4 * TDB * 4;
-  static constexpr int TOTAL = oFlag + 16;
-  static_assert(4 * CH * 4 * SW * 4 <= 2 * szE, "exact-Gram staging does not fit region E");
+  // per-(block, key channel) constants of a chunk, rows of DK floats:
+  //   0-3   exp(G_sJ), even chunks          E_bar = xe * row, Q_gamma = xq * row
+  //   4-7   exp(G_C - G_sJ)                 K_tail = kb * row
+  //   8-13  d_IJ = exp(G_sI - G_sJ), row 8 + I (I - 1) / 2 + J
+  //   14-15 gamma_C = exp(G_C), by chunk parity
+  //   16-19 exp(G_sJ), odd chunks
+  static constexpr int oCst = oKt + CH * SKT * 2;
+  // in-block prefix sums of the log-decay of the next chunk, rows of DK
+  // floats: 0-3 at the first token of block J, 4-7 at its last token
+  static constexpr int oBt = oCst + 20 * DK * 4;
+  static constexpr int oT = oBt + 8 * DK * 4;     // T below the diagonal, bf16 rows
+  // diagonal blocks of T, fp32 rows of TDS floats (columns 16-19 unused: row
+  // 0 holds the two exact-Gram flags, by chunk parity, in columns 16-17)
+  static constexpr int oTd = oT + CH * SC * 2;
+  static constexpr int TOTAL = oTd + 4 * TDB * 4;
+  static_assert(6 * CH * 4 * SW * 4 <= 2 * szE, "exact-Gram staging does not fit region E");
   static_assert(2 * 32 * SO * 2 <= szE, "output staging does not fit the kb buffer");
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
   static_assert(oQg % 16 == 0 && oKb % 16 == 0 && oZ % 16 == 0 && oAcm % 16 == 0 && oKt % 16 == 0 &&
-                    oSc % 16 == 0 && oD % 16 == 0 && oT % 16 == 0 && oTd % 16 == 0,
+                    oCst % 16 == 0 && oBt % 16 == 0 && oT % 16 == 0 && oTd % 16 == 0,
                 "alignment");
 };
 
 template <int DK, int DVS, int GM>
-__global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(ChunkParams p) {
+__global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 6)) void chan_fwd_kernel(ChunkParams p) {
   constexpr int NCW = pipe_ncw<DVS>();
   constexpr int NB = DVS / (16 * NCW);
   using L = ChanLay<DK, DVS>;
@@ -87,12 +111,15 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
   bf16* sAcm = reinterpret_cast<bf16*>(smem + L::oAcm);
   bf16* sAqk = reinterpret_cast<bf16*>(smem + L::oAqk);
   bf16* sKt = reinterpret_cast<bf16*>(smem + L::oKt);
-  float* sSc = reinterpret_cast<float*>(smem + L::oSc);
-  float* sD = reinterpret_cast<float*>(smem + L::oD);
-  float* sEs = reinterpret_cast<float*>(smem + L::oEs);
+  float* sCst = reinterpret_cast<float*>(smem + L::oCst);
+  auto sEs = [&](int n) { return sCst + ((n & 1) ? 16 * DK : 0); };  // exp(G_sJ)
+  float* sF = sCst + 4 * DK;    // exp(G_C - G_sJ)
+  float* sD = sCst + 8 * DK;    // d_IJ
+  float* sSc = sCst + 14 * DK;  // gamma_C, by chunk parity
+  float* sBt = reinterpret_cast<float*>(smem + L::oBt);
   bf16* sT = reinterpret_cast<bf16*>(smem + L::oT);
   float* sTd = reinterpret_cast<float*>(smem + L::oTd);
-  int* sFlag = reinterpret_cast<int*>(smem + L::oFlag);
+  int* sFlag = reinterpret_cast<int*>(sTd + 16);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -114,10 +141,121 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
   // A and A_qk: blocks above the diagonal are never written and stay zero
   {
     uint4* z = reinterpret_cast<uint4*>(smem + L::oAcm);
-    for (int e = tid; e < (2 * CH * SC * 2) / 16; e += 64 * (NCW + 4)) z[e] = uint4{0u, 0u, 0u, 0u};
-    if (tid == 0) *sFlag = 0;
+    for (int e = tid; e < (2 * CH * SC * 2) / 16; e += 64 * (NCW + 6)) z[e] = uint4{0u, 0u, 0u, 0u};
+    if (tid < 2) sFlag[tid] = 0;
   }
   __syncthreads();
+
+  // ---- T and A_qk tiles (phase 2), shared by the producer waves ------------
+  // Both kinds per tile, computed transposed (D^T = kb_J X_I^T), so that each
+  // lane holds four consecutive columns j of one row i.  Diagonal blocks of T
+  // go to fp32 rows for the solve, the others to bf16 rows; A_qk is held
+  // until phase 3.
+  //
+  // Exact T and A_qk entries for chunks whose block windows exceed the
+  // limit: every lane accumulates its four entries (i, j) of each tile as
+  // sum_c x_i[c] k_j[c] exp(G_i[c] - G_j[c]) in fp32, over slabs of SW
+  // channels staged by this wave alone (region E, free in phase 2).
+  const bf16* qg = reinterpret_cast<const bf16*>(p.q) + seq0 * DK;
+  const bf16* kg = reinterpret_cast<const bf16*>(p.k) + seq0 * DK;
+  const float* g_seq = p.g + seq0 * DK;
+  const float* beta_seq = p.beta ? p.beta + seq0 : nullptr;
+  const float* b_seq = erase_ch ? p.b + seq0 * DK : nullptr;
+  auto gram_exact = [&](auto tl, int n, f32x4* accT, f32x4* accA) __attribute__((always_inline)) {
+    using TL = decltype(tl);
+    float* st = reinterpret_cast<float*>(smem + L::oEb) + (wave - NCW) * (CH * 4 * SW);  // [t][4][SW]
+    const int t0 = n * CH;
+    const int t = lane;  // staging: one token per lane
+    const bool ok = t0 + t < T;
+    const int to = min(t0 + t, T - 1) * H;
+#pragma unroll 1
+    for (int cs = 0; cs < DK; cs += SW) {
+#pragma unroll 1
+      for (int c = 0; c < SW; ++c) {
+        const int a = to * DK + cs + c;
+        const float kv = ok ? (float)kg[a] : 0.f;
+        const float qv = ok ? (float)qg[a] : 0.f;
+        float ev;
+        if constexpr (erase_ch) ev = (ok ? b_seq[a] : 0.f) * kv;
+        else ev = (ok ? beta_seq[to] : 0.f) * (qmix ? kv + lam * qv : kv);
+        st[t * 4 * SW + c] = wave_incl_scan(ok ? g_seq[a] : 0.f);
+        st[t * 4 * SW + SW + c] = ev;
+        st[t * 4 * SW + 2 * SW + c] = kv;
+        st[t * 4 * SW + 3 * SW + c] = qv;
+      }
+      // (one wave: its staging writes complete before these reads)
+#pragma unroll 1
+      for (int c = 0; c < SW; ++c) {
+#pragma unroll
+        for (int tt = 0; tt < TL::n; ++tt) {
+          const int i = 16 * TL::I(tt) + l16, j0 = 16 * TL::J(tt) + 4 * g;
+          const float Gi = st[i * 4 * SW + c], ei = st[i * 4 * SW + SW + c], qi = st[i * 4 * SW + 3 * SW + c];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            const float Gj = st[j * 4 * SW + c], kj = st[j * 4 * SW + 2 * SW + c];
+            const float ex = (j <= i) ? fexp(Gi - Gj) : 0.f;
+            accT[tt][r] += ei * kj * ex;
+            accA[tt][r] += qi * kj * ex;
+          }
+        }
+      }
+    }
+  };
+
+  auto gram = [&](auto tiles, int n, f32x4* aqk_hold) __attribute__((always_inline)) {
+    using TL = decltype(tiles);
+    constexpr int NT = TL::n;
+    f32x4 accT[NT], accA[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) accT[t] = accA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (sFlag[n & 1] != n + 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int I = TL::I(t), J = TL::J(t);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          bf16x8 kj = *reinterpret_cast<const bf16x8*>(sKb + (16 * J + l16) * SE + 32 * s + 8 * g);
+          if (J < I) {
+            const float* d = sD + (I * (I - 1) / 2 + J) * DK + 32 * s + 8 * g;
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(d), d1 = *reinterpret_cast<const f32x4*>(d + 4);
+            f32x4 lo = {(float)kj[0], (float)kj[1], (float)kj[2], (float)kj[3]};
+            f32x4 hi = {(float)kj[4], (float)kj[5], (float)kj[6], (float)kj[7]};
+            kj = cat8(cvt4(lo * d0), cvt4(hi * d1));
+          }
+          const bf16x8 xe = *reinterpret_cast<const bf16x8*>(sXe + (16 * I + l16) * SE + 32 * s + 8 * g);
+          const bf16x8 xq = *reinterpret_cast<const bf16x8*>(sXq + (16 * I + l16) * SE + 32 * s + 8 * g);
+          accT[t] = mma32(kj, xe, accT[t]);
+          accA[t] = mma32(kj, xq, accA[t]);
+        }
+      }
+    } else {
+      gram_exact(tiles, n, accT, accA);
+    }
+    // masks; i = row (lane), j = 4 columns
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int I = TL::I(t), J = TL::J(t);
+      const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
+      f32x4 xT, xA;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        xT[r] = (j0 + r < i) ? accT[t][r] : 0.f;   // T: j < i
+        xA[r] = (j0 + r <= i) ? accA[t][r] : 0.f;  // A_qk: j <= i
+      }
+      aqk_hold[t] = xA;
+      if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
+      else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
+    }
+  };
+  auto store_aqk = [&](auto tiles, const f32x4* aqk_hold) __attribute__((always_inline)) {
+    using TL = decltype(tiles);
+#pragma unroll
+    for (int t = 0; t < TL::n; ++t) {
+      const int i = 16 * TL::I(t) + l16, j0 = 16 * TL::J(t) + 4 * g;
+      *reinterpret_cast<bf16x4*>(sAqk + i * SC + j0) = cvt4(aqk_hold[t]);
+    }
+  };
 
   if (wave < NCW) {
     // =================== consumers ===========================================
@@ -138,6 +276,9 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
     bf16* og = reinterpret_cast<bf16*>(p.o) + seq0 * DV + vbase;
     bf16* stage = sKb + wave * (16 * NB) * SO;  // O staging (phase 3), this wave's columns
 
+    // the producers' prologue (block sums and constants of chunk 0) and step 0
+    __syncthreads();
+    __syncthreads();
     __syncthreads();
     __syncthreads();
     __syncthreads();
@@ -293,55 +434,42 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
               p.state_out[((size_t)bh * DK + c) * DV + v] = S[2 * m + h][nb][r];
             }
     }
-  } else {
-    // =================== producers ===========================================
-    // Phase 1: cumulative log-decay per key channel and the bounded factors
-    // kb, xe, xq (rows to LDS), d_IJ and exp(G) at the block starts, gamma_C;
-    // K_tail of the previous chunk to LDS.  Phase 2: T and A_qk tiles.
-    // Phase 3: wave 0 inverts I + T; every wave stores its A_qk tiles and its
-    // rows of E_bar, Q_gamma and Z.
-    const int pw = wave - NCW, pt = tid - 64 * NCW;
-    // factor layout: thread = 8 key channels x TT tokens; the SEG token groups
-    // of a channel group are consecutive lanes of one wave, so the per-channel
-    // prefix sum runs across lanes without a barrier
-    constexpr int CGN = DK / 8, SEG = 256 / CGN, TT = CH / SEG;
-    static_assert(SEG == 16 || SEG == 32, "prefix-sum segment");
-    const int tg = lane % SEG, cg = pw * (64 / SEG) + lane / SEG;
-    const int c0 = 8 * cg, tq0 = TT * tg;
-    const int segbase = lane - tg;
-    // x at lane SRC of this lane's segment: a DPP row broadcast when the
-    // segment is one 16-lane row, else a lane permute
-    auto seg_lane = [&](auto src, float x) __attribute__((always_inline)) -> float {
-      constexpr int SRC = decltype(src)::value;
-      if constexpr (SEG == 16)
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + SRC,
-                                                                      0xf, 0xf, false));
-      else
-        return __shfl(x, segbase + SRC);
-    };
-    const int myJ = tq0 / 16;  // 16-token block of my tokens
+  } else if (wave < NCW + 4) {
+    // =================== elementwise waves ===================================
+    // Wave w owns the 16-token block w of every chunk: thread = 8 key channels
+    // x TT tokens, lanes along the channels (coalesced rows).
+    //   phase 1  the bounded factors kb, xe, xq of its rows to LDS, K_tail
+    //            in registers; K_tail of the previous chunk to LDS
+    //   phase 2  prefix sums of the next chunk's log-decay inside block w; the
+    //            diagonal tile (w, w) of T and A_qk
+    //   phase 3  E_bar = xe Es_w, Q_gamma = xq Es_w and Z of its rows to LDS;
+    //            erase vectors of the next chunk
+    // Log-decays are carried in base-2 units (times log2 e), so that every
+    // exponential is one exp2.
+    const int w = wave - NCW, pt = tid - 64 * NCW;
+    constexpr int CG = DK / 8, TG = 256 / CG, TT = CH / TG, NQ = 64 / CG;
+    static_assert(TT * NQ == 16, "one 16-token block per elementwise wave");
+    const int c0 = (pt % CG) * 8, tq0 = (pt / CG) * TT;  // tokens of block w
+    const int qg_ = lane / CG;                            // token group inside the block
     // v layout (as the scalar-decay kernel)
     constexpr int VG = DVS / 8, VTG = 256 / VG, VPT = (CH + VTG - 1) / VTG;
     const int vv0 = (pt % VG) * 8, vtq0 = (pt / VG) * VPT;
     const bool vact = vtq0 < CH;
+    constexpr float LOG2E = 1.4426950408889634f;
 
-    const bf16* qg = reinterpret_cast<const bf16*>(p.q) + seq0 * DK;
-    const bf16* kg = reinterpret_cast<const bf16*>(p.k) + seq0 * DK;
     const bf16* vg = reinterpret_cast<const bf16*>(p.v) + seq0 * DV + vbase;
-    const float* g_seq = p.g + seq0 * DK;
-    const float* beta_seq = p.beta ? p.beta + seq0 : nullptr;
-    const float* b_seq = erase_ch ? p.b + seq0 * DK : nullptr;
     const float* w_seq = write_ch ? p.w + seq0 * DV + vbase : nullptr;
 
-    // prefetched inputs of the next chunk (k, q, g: phase 1; b or beta:
-    // phase 2; v and w or beta: phase 3), at token indices clamped to T - 1
+    // prefetched inputs of the next chunk (v and the write gate: of the
+    // current one), at token indices clamped to T - 1
     bf16x8 rk[TT], rq[TT];
     f32x4 rg[TT][2], rb[erase_ch ? TT : 1][2];
     float rbeta[erase_ch ? 1 : TT];
     bf16x8 rv[VPT];
     f32x4 rw[write_ch ? VPT : 1][2];
     float rvb[write_ch ? 1 : VPT];
-    bf16x8 ktail[TT];  // K_tail rows of the current chunk, stored one step later
+    bf16x8 re[TT];          // erase vectors e of the next chunk (bf16)
+    bf16x8 ktail[TT];       // K_tail rows of the current chunk, stored one step later
     // Loads address the chunk from a uniform base with 32-bit per-lane byte
     // offsets (row of the token within the chunk), so that they take the
     // scalar-base form and keep no 64-bit addresses in vector registers.
@@ -353,26 +481,25 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
     auto row = [&](int n, int t) __attribute__((always_inline)) -> unsigned {
       return (unsigned)(min(n * CH + t, T - 1) - n * CH) * H;
     };
-    auto load_kqg = [&](int n) __attribute__((always_inline)) {
+    auto load_g = [&](int n) __attribute__((always_inline)) {
       const size_t cb = (size_t)n * CH * H * DK;
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         const unsigned o = row(n, tq0 + u) * DK + c0;
-        rk[u] = ldg(bf16x8{}, kg + cb, 2 * o);
-        rq[u] = ldg(bf16x8{}, qg + cb, 2 * o);
         rg[u][0] = ldg(f32x4{}, g_seq + cb, 4 * o);
         rg[u][1] = ldg(f32x4{}, g_seq + cb, 4 * o + 16);
       }
     };
-    auto load_b = [&](int n) __attribute__((always_inline)) {
+    auto load_kqb = [&](int n) __attribute__((always_inline)) {
+      const size_t cb = (size_t)n * CH * H * DK;
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
-        const unsigned r = row(n, tq0 + u);
+        const unsigned r = row(n, tq0 + u), o = r * DK + c0;
+        rk[u] = ldg(bf16x8{}, kg + cb, 2 * o);
+        rq[u] = ldg(bf16x8{}, qg + cb, 2 * o);
         if constexpr (erase_ch) {
-          const unsigned o = r * DK + c0;
-          const float* bc = b_seq + (size_t)n * CH * H * DK;
-          rb[u][0] = ldg(f32x4{}, bc, 4 * o);
-          rb[u][1] = ldg(f32x4{}, bc, 4 * o + 16);
+          rb[u][0] = ldg(f32x4{}, b_seq + cb, 4 * o);
+          rb[u][1] = ldg(f32x4{}, b_seq + cb, 4 * o + 16);
         } else {
           rbeta[u] = ldg(float{}, beta_seq + (size_t)n * CH * H, 4 * r);
         }
@@ -395,110 +522,133 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
       }
     };
 
-    // erase vector of my token u, channel i (fp32)
-    auto erase_of = [&](int u, int i, float kv, float qv) -> float __attribute__((always_inline)) {
-      if constexpr (erase_ch) return (i < 4 ? rb[u][0][i] : rb[u][1][i - 4]) * kv;
-      else return rbeta[u] * (qmix ? kv + lam * qv : kv);
+    // ---- phase 2 of the previous step: in-block prefix sums ------------------
+    // Hl = prefix sums over my TT tokens; Hsx = (sum at the block's first
+    // token) - (sum over the token groups before mine), so that the decay of
+    // token u relative to the block start is dl = Hsx - Hl[u] >= 0.
+    float Hl[TT][8], Hsx[8];
+    auto scan = [&](int n) __attribute__((always_inline)) {
+      if (n * CH + CH > T) {
+        // last chunk: g = 0 past the end
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+          if (n * CH + tq0 + u >= T) rg[u][0] = rg[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float excl[8], tot[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < TT; ++u) {
+          sum += (i < 4 ? rg[u][0][i] : rg[u][1][i - 4]) * LOG2E;
+          Hl[u][i] = sum;
+        }
+        tot[i] = sum;
+        // exclusive prefix over the token groups (lanes CG apart)
+        float x = sum;
+#pragma unroll
+        for (int d = CG; d < 64; d *= 2) {
+          const float y = __shfl_up(x, d);
+          x += lane >= d ? y : 0.f;
+        }
+        excl[i] = x - sum;
+      }
+      if (qg_ == 0) st8(sBt + w * DK + c0, Hl[0]);
+      if (qg_ == NQ - 1) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = excl[i] + tot[i];
+        st8(sBt + (4 + w) * DK + c0, e);
+      }
+      // (one wave: its row is complete before this read)
+      const V8<float> hs = ld8(sBt + w * DK + c0);
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        Hsx[i] = hs[i] - excl[i];
+        bad |= !(Hsx[i] - Hl[TT - 1][i] <= WINDOW_LIMIT * LOG2E);
+      }
+      // a block window above the limit switches the chunk to the exact Gram
+      if (bad) sFlag[n & 1] = n + 1;
+    };
+
+    // erase vectors of the next chunk once its loads have landed: e = b k or
+    // beta (k + lam q) (lam = 0 without the Q-Delta mix); k = q = 0 past the
+    // end
+    auto erase_rows = [&](int n) __attribute__((always_inline)) {
+      if (n * CH + CH > T) {
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+          if (n * CH + tq0 + u >= T) rk[u] = rq[u] = bf16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < TT; ++u) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (erase_ch) {
+            lo[i] = rb[u][0][i] * (float)rk[u][i];
+            hi[i] = rb[u][1][i] * (float)rk[u][i + 4];
+          } else {
+            lo[i] = rbeta[u] * __builtin_fmaf(lam, (float)rq[u][i], (float)rk[u][i]);
+            hi[i] = rbeta[u] * __builtin_fmaf(lam, (float)rq[u][i + 4], (float)rk[u][i + 4]);
+          }
+        }
+        re[u] = cat8(cvt4(lo), cvt4(hi));
+      }
     };
 
     // ---- phase 1 ---------------------------------------------------------------
-    auto prep = [&](int n) __attribute__((always_inline)) {
-      const int t0 = n * CH;
-      float G[TT][8];
-      float tot[8];
+    // gamma_C = 2^G_C (wave 0; G_C = sum of the block totals), then the
+    // bounded factors of my rows and K_tail = kb f_w (f_w from the Gram wave
+    // 1, one phase earlier).
+    constexpr int CPL = DK / 64;
+    auto prep = [&](auto wc, int n) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      if constexpr (W == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float s = 0.f;
+        for (int e = 0; e < CPL; ++e) {
+          const int c = CPL * lane + e;
+          float gc = 0.f;
 #pragma unroll
-        for (int u = 0; u < TT; ++u) {
-          const float gv = (t0 + tq0 + u < T) ? (i < 4 ? rg[u][0][i] : rg[u][1][i - 4]) : 0.f;
-          s += gv;
-          G[u][i] = s;
+          for (int J = 0; J < 4; ++J) gc += sBt[(4 + J) * DK + c];
+          sSc[(n & 1) * DK + c] = __builtin_amdgcn_exp2f(gc);
         }
-        tot[i] = s;
       }
-      // exclusive prefix of the per-thread totals over the segment
-      float GC[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = tot[i];
-#define GDR_SEG_ADD(ctrl, rmask)                                                                    \
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rmask, \
-                                                              0xf, false))
-        GDR_SEG_ADD(0x111, 0xf);  // row_shr:1
-        GDR_SEG_ADD(0x112, 0xf);  // row_shr:2
-        GDR_SEG_ADD(0x114, 0xf);  // row_shr:4
-        GDR_SEG_ADD(0x118, 0xf);  // row_shr:8
-        if constexpr (SEG == 32) GDR_SEG_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-#undef GDR_SEG_ADD
-        const float excl = x - tot[i];
-#pragma unroll
-        for (int u = 0; u < TT; ++u) G[u][i] += excl;
-        GC[i] = seg_lane(IC<SEG - 1>{}, x);
-      }
-      // G at the start of my block; d_IJ = exp(G_{s_I} - G_{s_J}) for the
-      // blocks J before mine (stored by the lanes that hold a block start)
-      const bool bstart = tq0 % 16 == 0;
-      float Gm[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float g0 = seg_lane(IC<0>{}, G[0][i]), g1 = seg_lane(IC<16 / TT>{}, G[0][i]),
-                    g2 = seg_lane(IC<32 / TT>{}, G[0][i]), g3 = seg_lane(IC<48 / TT>{}, G[0][i]);
-        Gm[i] = myJ == 0 ? g0 : (myJ == 1 ? g1 : (myJ == 2 ? g2 : g3));
-      }
-      auto dblock = [&](auto Jc) __attribute__((always_inline)) {
-        constexpr int J = decltype(Jc)::value;
-        float d[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d[i] = fexp(Gm[i] - seg_lane(IC<16 * J / TT>{}, G[0][i]));
-        if (bstart && J < myJ) st8(sD + (myJ * (myJ - 1) / 2 + J) * DK + c0, d);
-      };
-      dblock(IC<0>{});
-      dblock(IC<1>{});
-      dblock(IC<2>{});
-      // block windows above the limit switch this chunk to the exact Gram
-      bool bad = false;
-#pragma unroll
-      for (int u = 0; u < TT; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bad |= !(Gm[i] - G[u][i] <= WINDOW_LIMIT);
-      if (bad) *sFlag = n + 1;
-      if (bstart) {
-        float es[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) es[i] = fexp(Gm[i]);
-        st8(sEs + myJ * DK + c0, es);
-      }
-      if (tg == 0) {
-        float gc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gc[i] = fexp(GC[i]);
-        st8(sSc + (n & 1) * DK + c0, gc);
-      }
-      // bounded factors, and K_tail (kept in registers for one step)
+      const V8<float> fk = ld8(sF + W * DK + c0);
+      const bool bad = sFlag[n & 1] == n + 1;
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         const int t = tq0 + u;
-        const bool ok = t0 + t < T;
         float kb[8], xe[8], xq[8], kt[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float kv = ok ? (float)rk[u][i] : 0.f;
-          const float qv = ok ? (float)rq[u][i] : 0.f;
-          const float ev = erase_of(u, i, kv, qv);
-          const float dl = Gm[i] - G[u][i];  // >= 0
-          const float ir = fexp(-dl);
-          kb[i] = kv * fexp(dl);
+          const float kv = (float)rk[u][i];
+          const float qv = (float)rq[u][i];
+          const float ev = (float)re[u][i];
+          const float dl = Hsx[i] - Hl[u][i];  // >= 0
+          const float ir = __builtin_amdgcn_exp2f(-dl);
+          kb[i] = kv * __builtin_amdgcn_exp2f(dl);
           xe[i] = ev * ir;
           xq[i] = qv * ir;
-          kt[i] = kv * fexp(GC[i] - G[u][i]);  // <= |k|
+          kt[i] = kb[i] * fk[i];  // k exp(G_C - G) <= |k|
+        }
+        if (bad) {
+          // kb may have overflowed (the chunk takes the exact Gram): K_tail
+          // from its own exponent, G_C - G = (G_C - G_sw) + dl
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float lf = -sBt[W * DK + c0 + i];
+#pragma unroll
+            for (int J = W; J < 4; ++J) lf += sBt[(4 + J) * DK + c0 + i];
+            kt[i] = (float)rk[u][i] * __builtin_amdgcn_exp2f(lf + Hsx[i] - Hl[u][i]);
+          }
         }
         st8(sKb + t * SE + c0, kb);
         st8(sXe + t * SE + c0, xe);
         st8(sXq + t * SE + c0, xq);
-        f32x4 lo = {kt[0], kt[1], kt[2], kt[3]}, hi = {kt[4], kt[5], kt[6], kt[7]};
-        ktail[u] = cat8(cvt4(lo), cvt4(hi));
-        __builtin_amdgcn_sched_barrier(0);  // one token's temporaries at a time
+        ktail[u] = cat8(cvt4(f32x4{kt[0], kt[1], kt[2], kt[3]}), cvt4(f32x4{kt[4], kt[5], kt[6], kt[7]}));
+        // (one token at a time: no scheduling barrier needed here)
       }
     };
 
@@ -507,130 +657,25 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
       for (int u = 0; u < TT; ++u) *reinterpret_cast<bf16x8*>(sKt + (tq0 + u) * SKT + c0) = ktail[u];
     };
 
-    // Exact T and A_qk entries for chunks whose block windows exceed the
-    // limit: every lane accumulates its four entries (i, j) of each tile as
-    // sum_c x_i[c] k_j[c] exp(G_i[c] - G_j[c]) in fp32, over slabs of SW
-    // channels staged by this wave alone (region E, free in phase 2).
-    auto gram_exact = [&](auto tl, int n, f32x4* accT, f32x4* accA) __attribute__((always_inline)) {
-      using TL = decltype(tl);
-      float* st = reinterpret_cast<float*>(smem + L::oEb) + pw * (CH * 4 * SW);  // [t][4][SW]
-      const int t0 = n * CH;
-      const int t = lane;  // staging: one token per lane
-      const bool ok = t0 + t < T;
-      const int to = min(t0 + t, T - 1) * H;
-#pragma unroll 1
-      for (int cs = 0; cs < DK; cs += SW) {
-#pragma unroll 1
-        for (int c = 0; c < SW; ++c) {
-          const int a = to * DK + cs + c;
-          const float kv = ok ? (float)kg[a] : 0.f;
-          const float qv = ok ? (float)qg[a] : 0.f;
-          float ev;
-          if constexpr (erase_ch) ev = (ok ? b_seq[a] : 0.f) * kv;
-          else ev = (ok ? beta_seq[to] : 0.f) * (qmix ? kv + lam * qv : kv);
-          st[t * 4 * SW + c] = wave_incl_scan(ok ? g_seq[a] : 0.f);
-          st[t * 4 * SW + SW + c] = ev;
-          st[t * 4 * SW + 2 * SW + c] = kv;
-          st[t * 4 * SW + 3 * SW + c] = qv;
-        }
-        // (one wave: its staging writes complete before these reads)
-#pragma unroll 1
-        for (int c = 0; c < SW; ++c) {
-#pragma unroll
-          for (int tt = 0; tt < TL::n; ++tt) {
-            const int i = 16 * TL::I(tt) + l16, j0 = 16 * TL::J(tt) + 4 * g;
-            const float Gi = st[i * 4 * SW + c], ei = st[i * 4 * SW + SW + c], qi = st[i * 4 * SW + 3 * SW + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = j0 + r;
-              const float Gj = st[j * 4 * SW + c], kj = st[j * 4 * SW + 2 * SW + c];
-              const float ex = (j <= i) ? fexp(Gi - Gj) : 0.f;
-              accT[tt][r] += ei * kj * ex;
-              accA[tt][r] += qi * kj * ex;
-            }
-          }
-        }
-      }
-    };
-
-    // ---- phase 2: T and A_qk tiles --------------------------------------------
-    // Tiles as in the scalar-decay kernel: wave 0: (3,0) (3,1) (0,0); wave 1:
-    // (2,0) (2,1) (2,2); wave 2: (1,0) (1,1); wave 3: (3,2) (3,3), both
-    // kinds, computed transposed (D^T = kb_J X_I^T).
-    f32x4 aqk_hold[3];
-    auto gram = [&](auto tiles, int n) __attribute__((always_inline)) {
-      using TL = decltype(tiles);
-      constexpr int NT = TL::n;
-      f32x4 accT[NT], accA[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) accT[t] = accA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (*sFlag != n + 1) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int I = TL::I(t), J = TL::J(t);
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) {
-            bf16x8 kj = *reinterpret_cast<const bf16x8*>(sKb + (16 * J + l16) * SE + 32 * s + 8 * g);
-            if (J < I) {
-              const float* d = sD + (I * (I - 1) / 2 + J) * DK + 32 * s + 8 * g;
-              const f32x4 d0 = *reinterpret_cast<const f32x4*>(d), d1 = *reinterpret_cast<const f32x4*>(d + 4);
-              f32x4 lo = {(float)kj[0], (float)kj[1], (float)kj[2], (float)kj[3]};
-              f32x4 hi = {(float)kj[4], (float)kj[5], (float)kj[6], (float)kj[7]};
-              kj = cat8(cvt4(lo * d0), cvt4(hi * d1));
-            }
-            const bf16x8 xe = *reinterpret_cast<const bf16x8*>(sXe + (16 * I + l16) * SE + 32 * s + 8 * g);
-            const bf16x8 xq = *reinterpret_cast<const bf16x8*>(sXq + (16 * I + l16) * SE + 32 * s + 8 * g);
-            accT[t] = mma32(kj, xe, accT[t]);
-            accA[t] = mma32(kj, xq, accA[t]);
-          }
-          // one tile's fragments in flight at a time (register budget)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        gram_exact(tiles, n, accT, accA);
-      }
-      // masks; i = row (lane), j = 4 columns
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int I = TL::I(t), J = TL::J(t);
-        const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
-        f32x4 xT, xA;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          xT[r] = (j0 + r < i) ? accT[t][r] : 0.f;   // T: j < i
-          xA[r] = (j0 + r <= i) ? accA[t][r] : 0.f;  // A_qk: j <= i
-        }
-        aqk_hold[t] = xA;
-        if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
-        else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
-      }
-    };
-
-    // ---- phase 3 ---------------------------------------------------------------
-    auto store_aqk = [&](auto tiles) __attribute__((always_inline)) {
-      using TL = decltype(tiles);
-#pragma unroll
-      for (int t = 0; t < TL::n; ++t) {
-        const int i = 16 * TL::I(t) + l16, j0 = 16 * TL::J(t) + 4 * g;
-        *reinterpret_cast<bf16x4*>(sAqk + i * SC + j0) = cvt4(aqk_hold[t]);
-      }
-    };
-    // E_bar = xe exp(G_s), Q_gamma = xq exp(G_s) for my rows; Z = gate * v
+    // ---- phase 3: E_bar = xe Es_w, Q_gamma = xq Es_w of my rows; Z = gate * v --
     auto finish = [&](int n) __attribute__((always_inline)) {
       const int t0 = n * CH;
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(sEs + myJ * DK + c0);
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(sEs + myJ * DK + c0 + 4);
+      const V8<float> es = ld8(sEs(n) + w * DK + c0);
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         const int t = tq0 + u;
         const bf16x8 xe = *reinterpret_cast<const bf16x8*>(sXe + t * SE + c0);
         const bf16x8 xq = *reinterpret_cast<const bf16x8*>(sXq + t * SE + c0);
-        f32x4 a0 = {(float)xe[0], (float)xe[1], (float)xe[2], (float)xe[3]};
-        f32x4 a1 = {(float)xe[4], (float)xe[5], (float)xe[6], (float)xe[7]};
-        f32x4 b0 = {(float)xq[0], (float)xq[1], (float)xq[2], (float)xq[3]};
-        f32x4 b1 = {(float)xq[4], (float)xq[5], (float)xq[6], (float)xq[7]};
-        *reinterpret_cast<bf16x8*>(sEb + t * SE + c0) = cat8(cvt4(a0 * e0), cvt4(a1 * e1));
-        *reinterpret_cast<bf16x8*>(sQg + t * SE + c0) = cat8(cvt4(b0 * e0), cvt4(b1 * e1));
+        f32x4 a0, a1, b0, b1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a0[i] = (float)xe[i] * es[i];
+          a1[i] = (float)xe[i + 4] * es[i + 4];
+          b0[i] = (float)xq[i] * es[i];
+          b1[i] = (float)xq[i + 4] * es[i + 4];
+        }
+        *reinterpret_cast<bf16x8*>(sEb + t * SE + c0) = cat8(cvt4(a0), cvt4(a1));
+        *reinterpret_cast<bf16x8*>(sQg + t * SE + c0) = cat8(cvt4(b0), cvt4(b1));
       }
       if (vact) {
 #pragma unroll
@@ -650,46 +695,121 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_fwd_kernel(Ch
       }
     };
 
-
-    auto producer_loop = [&](auto tiles) __attribute__((always_inline)) {
-      // inputs of chunk n + 1 are requested a step ahead (k, q, g in phase 1,
-      // the erase gate in phase 2); v and the write gate of chunk n, which
-      // are used in phase 3, only after the prefix sum of chunk n, to keep
-      // them out of its registers
+    auto elementwise_loop = [&](auto wc) __attribute__((always_inline)) {
       if (nchunks > 0) {
-        load_kqg(0);
-        load_b(0);
+        load_g(0);
+        load_kqb(0);
+        scan(0);
+        erase_rows(0);
+        load_g(min(1, nchunks - 1));
       }
-      for (int n = 0; n <= nchunks; ++n) {
-        const bool cur = n < nchunks, more = n + 1 < nchunks;
+      __syncthreads();  // block sums of chunk 0 to the Gram wave 1
+      __syncthreads();  // its constants of chunk 0 to every wave
+      // Every step runs the same code: the next chunk's index is clamped, so
+      // the last step repeats harmless work on the last chunk, and every
+      // prefetched register is written in the step that reads it (with
+      // conditional loads the compiler keeps them all live across steps).
+      // Loads are spread over the phases (v in phase 1, k, q and the erase
+      // gate in phase 2, the log-decay in phase 3), so that a step's requests
+      // do not leave in one burst that stalls the issuing waves.
+      constexpr int W = decltype(wc)::value;
+      f32x4 aqk_hold[1];
+      for (int n = 0; n < nchunks; ++n) {
+        const int nn = min(n + 1, nchunks - 1), nn2 = min(n + 2, nchunks - 1);
         // phase 1
         if (n > 0) store_ktail();
-        if (cur) prep(n);
-        // the next chunk's loads stay behind the prefix sum: hoisted into
-        // it they would double the registers it holds
+        prep(wc, n);
+        // the loads stay behind the factors: hoisted into them they would
+        // add to the registers held
         __builtin_amdgcn_sched_barrier(0);
-        if (more) load_kqg(n + 1);
-        if (cur) load_v(n);
+        load_v(n);
         __syncthreads();
         // phase 2
-        if (more) load_b(n + 1);
-        if (cur) gram(tiles, n);
+        load_kqb(nn);
+        scan(nn);
+        gram(TileList<W, W>{}, n, aqk_hold);
         __syncthreads();
         // phase 3
-        if (cur) {
-          if (pw == 0) solve_inverse<SC, TDS, TDB>(sTd, sT, sAcm, g, l16);
-          store_aqk(tiles);
-          finish(n);
+        store_aqk(TileList<W, W>{}, aqk_hold);
+        finish(n);
+        load_g(nn2);
+        erase_rows(nn);
+        __syncthreads();
+      }
+      // last step: the consumers apply the last chunk
+      if (nchunks > 0) store_ktail();
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    };
+    switch (w) {
+      case 0: elementwise_loop(IC<0>{}); break;
+      case 1: elementwise_loop(IC<1>{}); break;
+      case 2: elementwise_loop(IC<2>{}); break;
+      default: elementwise_loop(IC<3>{}); break;
+    }
+  } else {
+    // =================== Gram waves ==========================================
+    // phase 2: the T and A_qk tiles below the diagonal blocks; phase 3: wave
+    // 0 inverts I + T, wave 1 forms the per-(block, channel) constants of the
+    // next chunk, both store A_qk.
+    const int gw = wave - NCW - 4;
+
+    // Constants of chunk n from its block sums, for the DK / 64 channels of
+    // each lane (base 2): P_J = G before block J, G_sJ = P_J + Bt[J],
+    // G_C = P_4; Es_J = 2^G_sJ, f_J = 2^(G_C - G_sJ), d_IJ = 2^(G_sI - G_sJ).
+    constexpr int CPL = DK / 64;
+    auto table = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int c = CPL * lane + e;
+        float P[5], gs[4];
+        P[0] = 0.f;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          gs[J] = P[J] + sBt[J * DK + c];
+          P[J + 1] = P[J] + sBt[(4 + J) * DK + c];
+        }
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          sEs(n)[J * DK + c] = __builtin_amdgcn_exp2f(gs[J]);
+          sF[J * DK + c] = __builtin_amdgcn_exp2f(P[4] - gs[J]);
+        }
+#pragma unroll
+        for (int I = 1; I < 4; ++I)
+#pragma unroll
+          for (int J = 0; J < I; ++J) sD[(I * (I - 1) / 2 + J) * DK + c] = __builtin_amdgcn_exp2f(gs[I] - gs[J]);
+      }
+    };
+
+    f32x4 aqk_hold[3];
+    auto gram_loop = [&](auto gc, auto tiles) __attribute__((always_inline)) {
+      constexpr int G = decltype(gc)::value;
+      __syncthreads();  // (the elementwise waves' block sums of chunk 0)
+      if constexpr (G == 1) {
+        if (nchunks > 0) table(0);
+      }
+      __syncthreads();
+      for (int n = 0; n < nchunks; ++n) {
+        __syncthreads();
+        gram(tiles, n, aqk_hold);
+        __syncthreads();
+        if constexpr (G == 0) solve_inverse<SC, TDS, TDB>(sTd, sT, sAcm, g, l16);
+        store_aqk(tiles, aqk_hold);
+        // constants of the next chunk (its block sums came in phase 2)
+        if constexpr (G == 1) {
+          if (n + 1 < nchunks) table(n + 1);
         }
         __syncthreads();
       }
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
     };
-    switch (pw) {
-      case 0: producer_loop(Tiles<3, 3, 0, 3, 1, 0, 0>{}); break;
-      case 1: producer_loop(Tiles<3, 2, 0, 2, 1, 2, 2>{}); break;
-      case 2: producer_loop(Tiles<2, 1, 0, 1, 1>{}); break;
-      default: producer_loop(Tiles<2, 3, 2, 3, 3>{}); break;
-    }
+    // the six tiles below the diagonal (the decay-scaled ones), three each;
+    // tiles sharing a row block I share its xe and xq fragments
+    if (gw == 0) gram_loop(IC<0>{}, TileList<1, 0, 3, 0, 3, 1>{});
+    else gram_loop(IC<1>{}, TileList<2, 0, 2, 1, 3, 2>{});
   }
 }
 

@@ -66,10 +66,16 @@ int chunk_lds(const gdr_args* a, int dvs) {
   }
 }
 
-// pipelined kernels: four producer waves plus two consumer waves (one for a
-// 16-column slice); one-pass kernel: four waves
+// pipelined kernels: two consumer waves (one for a 16-column slice) plus four
+// producer waves (scalar decay) or four elementwise and two Gram waves
+// (per-channel decay); one-pass kernel: four waves
 int chunk_block(const gdr_args* a, int dvs) {
-  return kernel_for(a) != gdr::kOnePass ? 64 * ((dvs >= 32 ? 2 : 1) + 4) : 256;
+  const int ncw = dvs >= 32 ? 2 : 1;
+  switch (kernel_for(a)) {
+    case gdr::kPipe: return 64 * (ncw + 4);
+    case gdr::kChan: return 64 * (ncw + 6);
+    default: return 256;
+  }
 }
 
 gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {

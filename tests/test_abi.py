@@ -169,12 +169,13 @@ def test_plan_slice_choice(lib, B, H, dv, io, expect):
     assert info.n_chunks == (a.T + 63) // 64
 
 
-@pytest.mark.parametrize("decay,erase,block", [(2, 0, 384), (2, 1, 384), (1, 1, 256), (0, 1, 256), (0, 0, 384),
+@pytest.mark.parametrize("decay,erase,block", [(2, 0, 512), (2, 1, 512), (1, 1, 256), (0, 1, 256), (0, 0, 384),
                                                (1, 0, 384)])
 def test_plan_kernel_choice(lib, decay, erase, block):
-    """bf16 I/O runs a pipelined kernel (four producer and two consumer waves)
-    except with the per-channel erase gate under no or a scalar decay, which
-    runs the one-pass kernel (one 256-thread workgroup)."""
+    """bf16 I/O runs a pipelined kernel (two consumer waves plus four producer
+    waves, or six under a per-channel decay) except with the per-channel erase
+    gate under no or a scalar decay, which runs the one-pass kernel (one
+    256-thread workgroup)."""
     a = good_args(B=8, H=16, dv=128, decay=decay, erase=erase, **({"g": 0} if decay == 0 else {}))
     if erase == 1:
         a.b = a.beta
