@@ -123,22 +123,30 @@ def bench_workload(name, steps, warmup, op="chunk"):
     cfg = config(name)
     inp = make_inputs(cfg)
     dev = torch.device("cuda:0")
-    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     B, T, H = cfg["B"], cfg["T"], cfg["H"]
-    dk, dv = d["k"].shape[3], d["v"].shape[3]
-    o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
-    so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    kinds = dict(decay=d["decay"], erase=d["erase"], write=d["write"], qmix=d["qmix"])
-    args = gdr.build_args(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
-                          lam=d["lam"], state=d["state"], o=o, state_out=so, **kinds)
+    # Two copies of every buffer, used alternately, so that a launch finds
+    # none of its inputs in the 256 MB last-level cache from the launch before.
+    copies = []
+    for _ in range(2):
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        dk, dv = d["k"].shape[3], d["v"].shape[3]
+        o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
+        so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        kinds = dict(decay=d["decay"], erase=d["erase"], write=d["write"], qmix=d["qmix"])
+        args = gdr.build_args(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
+                              lam=d["lam"], state=d["state"], o=o, state_out=so, **kinds)
+        copies.append((d, o, so, args))
+    d = copies[0][0]
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     entry = "gdr_chunk_fwd" if op == "chunk" else "gdr_recurrent_step"
     plan = gdr.plan(d["q"], d["k"], d["v"], op=op, g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
                     lam=d["lam"], state=d["state"], **kinds)
+    turn = [0]
 
     def fn():
-        _lib.call(entry, args, sp)
+        _lib.call(entry, copies[turn[0] & 1][3], sp)
+        turn[0] += 1
 
     ms_step, ms_kern, ms_min = time_launches(fn, stream, steps, warmup)
     byts = algorithmic_bytes(cfg, inp, op)
@@ -153,7 +161,7 @@ def bench_workload(name, steps, warmup, op="chunk"):
         res["algorithmic_flops"] = fl
         res["tflops"] = fl / (ms_kern * 1e-3) / 1e12
         res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
-    del d, o, so
+    del d, copies
     torch.cuda.empty_cache()
     return res, inp
 
@@ -198,6 +206,56 @@ def cpu_baseline(name, inp, budget_s=15.0):
                 cpu_model=model, host_threads_available=len(os.sched_getaffinity(0)))
 
 
+def ingest_counters(fetch_csv, write_csv, kernel_tag="pipe_fwd_kernel", workload=None):
+    """Write the headline kernel's HBM bytes per launch to profiles/traffic.json
+    from the counter CSVs of two `rocprofv3 --pmc` passes over `bench.py
+    --counters` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter
+    is scaled by what it reads for the 1 GiB device copy that the run makes
+    first (the copy reads and writes exactly 1 GiB)."""
+    import csv
+    from collections import defaultdict
+
+    from synth import HEADLINE
+
+    workload = workload or HEADLINE
+
+    def per_dispatch(path, counter):
+        vals, names = defaultdict(float), {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            vals[d] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+        copy = [vals[d] for d in sorted(vals) if "copy" in names[d].lower()]
+        kern = [vals[d] for d in sorted(vals) if kernel_tag in names[d]]
+        if not copy or not kern:
+            raise SystemExit(f"{path}: no copy or no {kernel_tag} dispatch with {counter}")
+        return copy[0], sum(kern) / len(kern)
+
+    gib_kib = float(1 << 20)
+    fcopy, fkern = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wcopy, wkern = per_dispatch(write_csv, "WRITE_SIZE")
+    ff, wf = gib_kib / fcopy, gib_kib / wcopy
+    fetch_b, write_b = fkern * ff * 1024, wkern * wf * 1024
+    path = os.path.join(PROFILES, "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data.setdefault(kernel_tag, {})[workload] = {
+        "kernel_src_sha": kernel_source_hash(),
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "fetch_kib_raw": fkern,
+        "write_kib_raw": wkern,
+        "copy_calibration": {"bytes": 1 << 30, "fetch_kib_raw": fcopy, "write_kib_raw": wcopy,
+                             "fetch_factor": ff, "write_factor": wf},
+    }
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+    print(f"{kernel_tag} {workload}: read {fetch_b / 1e6:.1f} MB, write {write_b / 1e6:.1f} MB per launch "
+          f"(factors {ff:.3f}, {wf:.3f}) -> {path}")
+
+
 def counters_run(name):
     """Dispatches for HBM counter calibration: a plain device-to-device copy of
     exactly 1 GiB (reads 1 GiB, writes 1 GiB), then the headline chunk kernel."""
@@ -224,7 +282,13 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc runs: one 1 GiB device copy (calibration) and three "
                          "launches of the headline chunk kernel, no timing output")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: turn the counter CSVs of the FETCH_SIZE and WRITE_SIZE passes over "
+                         "--counters into profiles/traffic.json")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the chunked forward shards over (batch, head) with no "
               "exchange, so a multi-GPU figure is not produced here; run with --gpus 1.", file=sys.stderr)

@@ -646,30 +646,29 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       load_q(0, R);
       load_v(0, R);
     }
+    // Prefetches are unconditional, the next chunk's index clamped to the
+    // last one: registers loaded under a condition that the compiler cannot
+    // tie to their use stay live across the whole loop.
     for (int n = 0; n < nchunks; ++n) {
       const int buf = n & 1;
-      const bool more = n + 1 < nchunks;
+      const int nn = min(n + 1, nchunks - 1);
       prep(n, buf, R);
-      if (more) {
-        load_k(n + 1, R);
-        if constexpr (pw == 0) load_v(n + 1, R);
-      }
+      load_k(nn, R);
+      if constexpr (pw == 0) load_v(nn, R);
       __syncthreads();
-      if (more) load_q(n + 1, R);
+      load_q(nn, R);
       if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf);
       else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf);
       else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf);
       else gram(Tiles<2, 3, 2, 3, 3>{}, buf);
       // the scan wave loads v, g and beta here, early, since its prefix sum
       // waits for g at the start of the next step
-      if constexpr (pw == kScanWave) {
-        if (more) load_v(n + 1, R);
-      }
+      if constexpr (pw == kScanWave) load_v(nn, R);
       __syncthreads();
       if constexpr (pw == 0) {
         solve(buf);
       } else if constexpr (pw != kScanWave) {
-        if (more) load_v(n + 1, R);
+        load_v(nn, R);
       }
       __syncthreads();
     }
