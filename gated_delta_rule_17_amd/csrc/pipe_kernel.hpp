@@ -186,7 +186,7 @@ struct PipeLay {
   static constexpr int szK = CH * SK * 2, szQ = CH * SQ * 2, szZ = CH * SZ * 2, szA = CH * SC * 2, szS = NSC * 4;
   static constexpr int oK = 0;                 // 2 x [64][SK]  k rows (zero past the end)
   static constexpr int oQ = oK + 2 * szK;      // 2 x [64][SQ]  q rows
-  static constexpr int oZ = oQ + 2 * szQ;      // 2 x [64][SZ]  v rows (beta write gate) or w * v
+  static constexpr int oZ = oQ + 2 * szQ;      // 2 x [64][SZ]  gated v rows: beta * v or w * v
   static constexpr int oAcm = oZ + 2 * szZ;    // 2 x [64][SC]  A column-major: Acm[j][i] = A[i][j]
   static constexpr int oAqk = oAcm + 2 * szA;  // 2 x [64][SC]  A_qk row-major
   static constexpr int oSc = oAqk + 2 * szA;   // 2 x scalars
@@ -328,23 +328,28 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       f32x4 Wt[4][NB];
       {
         bf16x8 Rb[2][NB];  // k slots of group g: tokens 32p + 4g + e, 32p + 16 + 4g + (e - 4)
+        // Z rows carry the write gate already (beta or w, applied by the producers)
+        auto residual = [&](auto qm) {
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+          for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            f32x4 R2[2];
+            for (int nb = 0; nb < NB; ++nb) {
+              f32x4 R2[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int I = 2 * pp + h;
-              f32x4 z = cvtf4(
-                  lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + cw0 + 16 * nb + 4 * (l16 & 3)));
-              if constexpr (!write_ch) z *= *reinterpret_cast<const f32x4*>(sc + L::sBeta + 16 * I + 4 * g);
-              const f32x4 ce = *reinterpret_cast<const f32x4*>(sc + L::sCE + 16 * I + 4 * g);
-              const f32x4 es = qmix ? KS[I][nb] + lam * QS[I][nb] : KS[I][nb];
-              R2[h] = z - ce * es;
+              for (int h = 0; h < 2; ++h) {
+                const int I = 2 * pp + h;
+                const f32x4 z = cvtf4(
+                    lds_tr4(Zb + (16 * I + 4 * g + (l16 >> 2)) * SZ + cw0 + 16 * nb + 4 * (l16 & 3)));
+                const f32x4 ce = *reinterpret_cast<const f32x4*>(sc + L::sCE + 16 * I + 4 * g);
+                f32x4 es = KS[I][nb];
+                if constexpr (decltype(qm)::value) es += lam * QS[I][nb];
+                R2[h] = z - ce * es;
+              }
+              Rb[pp][nb] = cat8(cvt4(R2[0]), cvt4(R2[1]));
             }
-            Rb[pp][nb] = cat8(cvt4(R2[0]), cvt4(R2[1]));
-          }
+        };
+        if (qmix) residual(IC<1>{});
+        else residual(IC<0>{});
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
@@ -493,6 +498,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       float gs, bs;  // scan wave: log-decay and beta of token t0 + lane
       bf16x8 v[VPT];
       f32x4 w[write_ch ? VPT : 1][2];
+      float vb[write_ch ? 1 : VPT];  // beta of the v rows (the beta write gate)
     };
     auto load_k = [&](int n, Raw& R) {
 #pragma unroll
@@ -523,6 +529,8 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
           if constexpr (write_ch) {
             R.w[u][0] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0);
             R.w[u][1] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0 + 4);
+          } else {
+            R.vb[u] = beta_seq[to];
           }
         }
       }
@@ -559,18 +567,15 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         for (int u = 0; u < VPT; ++u) {
           const int t = vtq0 + u;
           const bool ok = t0 + t < T;
-          if constexpr (write_ch) {
-            float z[8];
+          float z[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
-              z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
-            }
-            st8(Zb + t * SZ + vv0, z);
-          } else {
-            // beta is applied by the consumers
-            *reinterpret_cast<bf16x8*>(Zb + t * SZ + vv0) = ok ? R.v[u] : zero;
+          for (int e = 0; e < 8; ++e) {
+            float gate;
+            if constexpr (write_ch) gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
+            else gate = R.vb[u];
+            z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
           }
+          st8(Zb + t * SZ + vv0, z);
         }
       }
     };
