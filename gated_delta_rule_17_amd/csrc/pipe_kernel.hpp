@@ -24,7 +24,7 @@
 //   phase 1  producers: rows of k, q, v and the chunk     | consumers: K S, Q S
 //            scalars to LDS
 //   phase 2  producers: T and A_qk tiles (MFMA)            | consumers: W, O to LDS
-//   phase 3  producer wave 0: A = (I + T)^{-1}             | consumers: S update, O stores
+//   phase 3  producer waves 0, 1: A = (I + T)^{-1}         | consumers: S update, O stores
 //
 // Consumer wave c owns 32 value columns of a 64-column slice (16 of a
 // narrower one) and all DK rows of the state, in MFMA accumulators.  Products whose contraction
@@ -114,7 +114,11 @@ __device__ __forceinline__ void subst(float (&x)[16], const float (&tr)[16]) {
 //            (I + T_gg)^{-1}; lane i of each 16-lane row holds row i of T_gg
 //   level 1: A_IJ = -A_II (T_IJ A_JJ) for (I, J) = (1, 0), (3, 2)
 //   level 2: P_IJ = T[I, 0:32] A[0:32, J], A_IJ = -A[I, 32:64] P[32:64, J]
-template <int SC, int TDS, int TDB>
+// JM selects the level-2 column blocks J (bit J) that this call forms: two
+// waves can split level 2, each redoing levels 0 and 1 (their identical
+// writes of those blocks are harmless, and each wave reads them only after
+// writing them itself).
+template <int SC, int TDS, int TDB, int JM = 3>
 __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, bf16* Ab, int g, int l16) {
   float tr[16];
 #pragma unroll
@@ -152,6 +156,7 @@ __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, b
   for (int I = 2; I < 4; ++I)
 #pragma unroll
     for (int J = 0; J < 2; ++J) {
+      if (!((JM >> J) & 1)) continue;
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(Tm + (16 * I + l16) * SC + 8 * g);
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(Ab + (16 * J + l16) * SC + 8 * g);
       P2[I - 2][J] = mma32(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -160,6 +165,7 @@ __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, b
   for (int I = 2; I < 4; ++I)
 #pragma unroll
     for (int J = 0; J < 2; ++J) {
+      if (!((JM >> J) & 1)) continue;
       const bf16x4 a1 = lds_tr4(Ab + (32 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
       const bf16x4 a2 = lds_tr4(Ab + (48 + 4 * g + (l16 >> 2)) * SC + 16 * I + 4 * (l16 & 3));
       const f32x4 r = mma32(cat8(a1, a2), cat8(cvt4(P2[0][J]), cvt4(P2[1][J])), f32x4{0.f, 0.f, 0.f, 0.f});
@@ -460,10 +466,10 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
   } else {
     // =================== producers ===========================================
     // All four producer waves write the rows of chunk n to LDS (phase 1) and
-    // compute the Gram tiles (phase 2); wave 0 then computes A = (I + T)^-1
-    // (phase 3).  The loads of chunk n + 1 are spread over the three phases
-    // (k, q, then v, g, beta) so that a chunk's requests do not leave in one
-    // burst; wave 0 issues all of its share in phase 1.
+    // compute the Gram tiles (phase 2); waves 0 and 1 then compute
+    // A = (I + T)^-1 (phase 3), splitting its last level.  The loads of chunk
+    // n + 1 are spread over the three phases (k, q, then v, g, beta) so that
+    // a chunk's requests do not leave in one burst.
     // One loop per producer wave, with the wave's role fixed at compile time:
     // a single loop with run-time role branches makes the register allocator
     // move prefetched registers at the branch joins, which waits for loads
@@ -514,13 +520,13 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         R.q[u] = *reinterpret_cast<const bf16x8*>(qg + to * DK + c0);
       }
     };
+    auto load_gb = [&](int n, Raw& R) {
+      const int to = min(n * CH + lane, T - 1) * H;
+      R.gs = gsrc[to];
+      R.bs = beta_seq[to];
+    };
     auto load_v = [&](int n, Raw& R) {
       const int t0 = n * CH;
-      if constexpr (pw == kScanWave) {
-        const int to = min(t0 + lane, T - 1) * H;
-        R.gs = gsrc[to];
-        R.bs = beta_seq[to];
-      }
       if (vact) {
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
@@ -643,13 +649,17 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     };
 
     // ---- phase 3 (wave 0): A = (I + T)^{-1} ----------------------------------
-    auto solve = [&](int buf) { solve_inverse<SC, TDS, TDB>(sTd, sT, sAcm + buf * CH * SC, g, l16); };
+    // waves 0 and 1 (the scan wave, with a SIMD of its own) split its last level
+    auto solve = [&](auto jm, int buf) {
+      solve_inverse<SC, TDS, TDB, decltype(jm)::value>(sTd, sT, sAcm + buf * CH * SC, g, l16);
+    };
 
     Raw R;
     if (nchunks > 0) {
       load_k(0, R);
       load_q(0, R);
       load_v(0, R);
+      if constexpr (pw == kScanWave) load_gb(0, R);
     }
     // Prefetches are unconditional, the next chunk's index clamped to the
     // last one: registers loaded under a condition that the compiler cannot
@@ -668,13 +678,14 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       else gram(Tiles<2, 3, 2, 3, 3>{}, buf);
       // the scan wave loads v, g and beta here, early, since its prefix sum
       // waits for g at the start of the next step
-      if constexpr (pw == kScanWave) load_v(nn, R);
-      __syncthreads();
-      if constexpr (pw == 0) {
-        solve(buf);
-      } else if constexpr (pw != kScanWave) {
+      if constexpr (pw == kScanWave) {
+        load_gb(nn, R);
         load_v(nn, R);
       }
+      __syncthreads();
+      if constexpr (pw == 0) solve(IC<1>{}, buf);
+      if constexpr (pw == kScanWave) solve(IC<2>{}, buf);
+      if constexpr (pw >= 2) load_v(nn, R);
       __syncthreads();
     }
     // last step: the consumers apply the last chunk
