@@ -176,19 +176,23 @@ __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, b
 // ---- LDS layout (byte offsets) -------------------------------------------
 template <int DK, int DVS>
 struct PipeLay {
-  // Row strides (bf16 elements).  K rows are read both as MFMA row fragments
-  // and by transposing reads (4 rows x 4 column groups per 16 lanes); the
-  // strides below keep both free of LDS bank conflicts on gfx950.
+  // Row strides (bf16 elements), chosen from measured LDS bank conflicts
+  // on gfx950 (64 four-byte banks) for each array's own access patterns:
+  //   k: 16-row b128 fragment reads and transposing reads of rows 8g + l/4
+  //      pull in opposite directions; 320 B rows give the least in total
+  //   q: b128 fragment reads only; 288 B (dk 128) and 160 B rows are free
+  //   Z: transposing reads of rows 4g + l/4; 160 B rows (64 columns) are free
+  //   O staging: b64 writes of 16 rows x 4 groups; 136 B rows are free
   static constexpr int SK = DK + (DK == 128 ? 32 : 24);  // k rows: 320 B (dk 128) / 176 B (dk 64)
-  static constexpr int SQ = DK + 8;          // q rows
+  static constexpr int SQ = DK + 16;         // q rows
   static constexpr int SC = CH + 8;          // bf16 row stride of the [64][64] arrays
-  static constexpr int SZ = DVS + 8;         // bf16 row stride of Z
+  static constexpr int SZ = DVS == 64 ? 80 : DVS + 8;  // bf16 row stride of Z
   static constexpr int TDS = 20;             // fp32 row stride inside a diagonal T block
   static constexpr int TDB = 16 * TDS;       // fp32 stride between the four diagonal blocks
   // per-chunk scalars (float offsets): G = chunk cumsum of the log-decay,
   // beta, c_e = beta gamma, gamma, tail = gamma_C / gamma, gamma_C
   static constexpr int sG = 0, sBeta = 64, sCE = 128, sGam = 192, sTail = 256, sGC = 320, NSC = 336;
-  static constexpr int SO = CH + 8;          // O staging: [DVS][64] (value column, token)
+  static constexpr int SO = CH + 4;          // O staging: [DVS][64] (value column, token)
   static constexpr int szK = CH * SK * 2, szQ = CH * SQ * 2, szZ = CH * SZ * 2, szA = CH * SC * 2, szS = NSC * 4;
   static constexpr int oK = 0;                 // 2 x [64][SK]  k rows (zero past the end)
   static constexpr int oQ = oK + 2 * szK;      // 2 x [64][SQ]  q rows
@@ -465,11 +469,13 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     }
   } else {
     // =================== producers ===========================================
-    // All four producer waves write the rows of chunk n to LDS (phase 1) and
-    // compute the Gram tiles (phase 2); waves 0 and 1 then compute
-    // A = (I + T)^-1 (phase 3), splitting its last level.  The loads of chunk
-    // n + 1 are spread over the three phases (k, q, then v, g, beta) so that
-    // a chunk's requests do not leave in one burst.
+    // All four producer waves write the k rows of chunk n and the gated v
+    // rows of chunk n - 1 to LDS (phase 1: the consumers read Z of chunk
+    // n - 1 in phase 2 of this step) and compute the Gram tiles (phase 2);
+    // waves 0 and 1 then compute A = (I + T)^-1 (phase 3), splitting its last
+    // level, while waves 2 and 3 write the q rows of chunk n + 1 (phase 3: the
+    // consumers read q in phase 1 only, so the buffer of the chunk that they
+    // apply is free by then) and load those of chunk n + 2.
     // One loop per producer wave, with the wave's role fixed at compile time:
     // a single loop with run-time role branches makes the register allocator
     // move prefetched registers at the branch joins, which waits for loads
@@ -480,10 +486,14 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // has a SIMD of its own (with two consumer waves, producer waves 2 and 3
     // share their SIMDs with them)
     constexpr int kScanWave = 1;
+    constexpr bool kRowWave = pw >= 2;  // writes the q rows
     const int pt = tid - 64 * NCW;
-    constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;        // k, q: 8 channels x TPT tokens
+    constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;      // k: 8 channels x TPT tokens
+    constexpr int QTG = 128 / CG, QPT = CH / QTG;                 // q: over waves 2, 3
     constexpr int VG = DVS / 8, VTG = 256 / VG, VPT = (CH + VTG - 1) / VTG;  // v: 8 columns x VPT tokens
-    const int c0 = (pt % CG) * 8, tq0 = (pt / CG) * TPT;
+    const int c0 = (pt % CG) * 8, tk0 = (pt / CG) * TPT;
+    const int rt = pt - 128;  // lane index over waves 2 and 3
+    const int qc0 = (rt % CG) * 8, tq0 = (rt / CG) * QPT;
     const int vv0 = (pt % VG) * 8, vtq0 = (pt / VG) * VPT;
     const bool vact = vtq0 < CH;  // wave-uniform
     const bf16* qg = reinterpret_cast<const bf16*>(p.q) + seq0 * DK;
@@ -496,53 +506,67 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     const float* beta_seq = p.beta + seq0;
     const float* w_seq = write_ch ? p.w + seq0 * DV + vbase : nullptr;
 
-    // next chunk's inputs, prefetched into registers.  Loads are
+    // inputs of coming chunks, prefetched into registers.  Loads are
     // unconditional, at token indices clamped to T - 1; rows past the end are
     // zeroed when they are written to LDS.
     struct Raw {
-      bf16x8 k[TPT], q[TPT];
+      bf16x8 k[TPT];
       float gs, bs;  // scan wave: log-decay and beta of token t0 + lane
+      bf16x8 q[kRowWave ? QPT : 1];
       bf16x8 v[VPT];
       f32x4 w[write_ch ? VPT : 1][2];
       float vb[write_ch ? 1 : VPT];  // beta of the v rows (the beta write gate)
     };
-    auto load_k = [&](int n, Raw& R) {
-#pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const int to = min(n * CH + tq0 + u, T - 1) * H;
-        R.k[u] = *reinterpret_cast<const bf16x8*>(kg + to * DK + c0);
-      }
+    // Loads address the chunk from a uniform base with 32-bit per-lane byte
+    // offsets (row of the token within the chunk), so that they take the
+    // scalar-base form and keep no 64-bit addresses in vector registers.
+    auto ldg = [&](auto vt, const void* base, unsigned byteoff) __attribute__((always_inline)) {
+      using V = decltype(vt);
+      return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + byteoff);
     };
-    auto load_q = [&](int n, Raw& R) {
+    // token row (t * H) of token t of chunk n relative to the chunk start
+    auto row = [&](int n, int t) __attribute__((always_inline)) -> unsigned {
+      return (unsigned)(min(n * CH + t, T - 1) - n * CH) * H;
+    };
+    auto load_k = [&](int n, Raw& R) {
+      const bf16* kc = kg + (size_t)n * CH * H * DK;
 #pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const int to = min(n * CH + tq0 + u, T - 1) * H;
-        R.q[u] = *reinterpret_cast<const bf16x8*>(qg + to * DK + c0);
-      }
+      for (int u = 0; u < TPT; ++u) R.k[u] = ldg(bf16x8{}, kc, 2 * (row(n, tk0 + u) * DK + c0));
     };
     auto load_gb = [&](int n, Raw& R) {
-      const int to = min(n * CH + lane, T - 1) * H;
-      R.gs = gsrc[to];
-      R.bs = beta_seq[to];
+      const unsigned r = row(n, lane);
+      R.gs = ldg(float{}, gsrc + (size_t)n * CH * H, 4 * r);
+      R.bs = ldg(float{}, beta_seq + (size_t)n * CH * H, 4 * r);
+    };
+    auto load_q = [&](int n, Raw& R) {
+      const bf16* qc = qg + (size_t)n * CH * H * DK;
+#pragma unroll
+      for (int u = 0; u < QPT; ++u) R.q[u] = ldg(bf16x8{}, qc, 2 * (row(n, tq0 + u) * DK + qc0));
     };
     auto load_v = [&](int n, Raw& R) {
-      const int t0 = n * CH;
-      if (vact) {
+      if (!vact) return;
+      const bf16* vc = vg + (size_t)n * CH * H * DV;
 #pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-          const int to = min(t0 + vtq0 + u, T - 1) * H;
-          R.v[u] = *reinterpret_cast<const bf16x8*>(vg + to * DV + vv0);
-          if constexpr (write_ch) {
-            R.w[u][0] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0);
-            R.w[u][1] = *reinterpret_cast<const f32x4*>(w_seq + to * DV + vv0 + 4);
-          } else {
-            R.vb[u] = beta_seq[to];
-          }
-        }
+      for (int u = 0; u < VPT; ++u) {
+        const unsigned r = row(n, vtq0 + u);
+        R.v[u] = ldg(bf16x8{}, vc, 2 * (r * DV + vv0));
+        if constexpr (!write_ch) R.vb[u] = ldg(float{}, beta_seq + (size_t)n * CH * H, 4 * r);
+      }
+    };
+    // per-channel write gate: loaded one phase before its use rather than a
+    // step before, so that its registers are not live during the Gram tiles
+    auto load_w = [&](int n, Raw& R) {
+      if (!vact) return;
+      const float* wc = w_seq + (size_t)n * CH * H * DV;
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const unsigned o = row(n, vtq0 + u) * DV + vv0;
+        R.w[u][0] = ldg(f32x4{}, wc, 4 * o);
+        R.w[u][1] = ldg(f32x4{}, wc, 4 * o + 16);
       }
     };
 
-    // ---- phase 1: chunk scalars (scan wave), k / q / v rows ----------------
+    // ---- phase 1: chunk scalars (scan wave), k rows ------------------------
     auto prep = [&](int n, int buf, const Raw& R) {
       const int t0 = n * CH;
       if constexpr (pw == kScanWave) {
@@ -558,34 +582,44 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         if (lane == 0) sc[L::sGC] = fexp(GC);
       }
       bf16* Kb = sK + buf * CH * SK;
-      bf16* Qb = sQ + buf * CH * SQ;
-      bf16* Zb = sZ + buf * CH * SZ;
       const bf16x8 zero = {};
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
-        const int t = tq0 + u;
-        const bool ok = t0 + t < T;
-        *reinterpret_cast<bf16x8*>(Kb + t * SK + c0) = ok ? R.k[u] : zero;
-        *reinterpret_cast<bf16x8*>(Qb + t * SQ + c0) = ok ? R.q[u] : zero;
-      }
-      if (vact) {
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-          const int t = vtq0 + u;
-          const bool ok = t0 + t < T;
-          float z[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float gate;
-            if constexpr (write_ch) gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
-            else gate = R.vb[u];
-            z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
-          }
-          st8(Zb + t * SZ + vv0, z);
-        }
+        const int t = tk0 + u;
+        *reinterpret_cast<bf16x8*>(Kb + t * SK + c0) = (t0 + t < T) ? R.k[u] : zero;
       }
     };
-
+    // ---- phase 3 (waves 2, 3): q rows of chunk n -----------------------------
+    auto rows_q = [&](int n, int buf, const Raw& R) {
+      const int t0 = n * CH;
+      bf16* Qb = sQ + buf * CH * SQ;
+      const bf16x8 zero = {};
+#pragma unroll
+      for (int u = 0; u < QPT; ++u) {
+        const int t = tq0 + u;
+        *reinterpret_cast<bf16x8*>(Qb + t * SQ + qc0) = (t0 + t < T) ? R.q[u] : zero;
+      }
+    };
+    // ---- phase 1 of the next step: Z = gate * v rows of chunk n --------------
+    auto rows_z = [&](int n, int buf, const Raw& R) {
+      if (!vact) return;
+      const int t0 = n * CH;
+      bf16* Zb = sZ + buf * CH * SZ;
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int t = vtq0 + u;
+        const bool ok = t0 + t < T;
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float gate;
+          if constexpr (write_ch) gate = e < 4 ? R.w[u][0][e] : R.w[u][1][e - 4];
+          else gate = R.vb[u];
+          z[e] = ok ? gate * (float)R.v[u][e] : 0.f;
+        }
+        st8(Zb + t * SZ + vv0, z);
+      }
+    };
     // ---- phase 2: T and A_qk tiles ------------------------------------------
     // Each producer wave computes both T and A_qk on its (I, J) tiles, so the
     // K_J fragments and the decay factors exp(G_i - G_j) serve both:
@@ -657,37 +691,43 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     Raw R;
     if (nchunks > 0) {
       load_k(0, R);
-      load_q(0, R);
-      load_v(0, R);
       if constexpr (pw == kScanWave) load_gb(0, R);
+      if constexpr (kRowWave) {
+        load_q(0, R);
+        rows_q(0, 0, R);
+        load_q(min(1, nchunks - 1), R);
+      }
     }
-    // Prefetches are unconditional, the next chunk's index clamped to the
-    // last one: registers loaded under a condition that the compiler cannot
-    // tie to their use stay live across the whole loop.
+    // Prefetches are unconditional, the chunk index clamped to the last one:
+    // registers loaded under a condition that the compiler cannot tie to
+    // their use stay live across the whole loop.
     for (int n = 0; n < nchunks; ++n) {
       const int buf = n & 1;
       const int nn = min(n + 1, nchunks - 1);
       prep(n, buf, R);
+      if (n > 0) rows_z(n - 1, buf ^ 1, R);
       load_k(nn, R);
-      if constexpr (pw == 0) load_v(nn, R);
+      load_v(n, R);
       __syncthreads();
-      load_q(nn, R);
       if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf);
       else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf);
       else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf);
       else gram(Tiles<2, 3, 2, 3, 3>{}, buf);
-      // the scan wave loads v, g and beta here, early, since its prefix sum
-      // waits for g at the start of the next step
-      if constexpr (pw == kScanWave) {
-        load_gb(nn, R);
-        load_v(nn, R);
-      }
+      // g and beta are loaded here rather than in phase 3, so that they have
+      // arrived when the next step's prefix sum starts
+      if constexpr (pw == kScanWave) load_gb(nn, R);
       __syncthreads();
       if constexpr (pw == 0) solve(IC<1>{}, buf);
       if constexpr (pw == kScanWave) solve(IC<2>{}, buf);
-      if constexpr (pw >= 2) load_v(nn, R);
+      if constexpr (kRowWave) {
+        if (n + 1 < nchunks) rows_q(n + 1, buf ^ 1, R);
+        load_q(min(n + 2, nchunks - 1), R);
+      }
+      if constexpr (write_ch) load_w(n, R);
       __syncthreads();
     }
+    // Z rows of the last chunk, before the consumers' phase 2 applies it
+    if (nchunks > 0) rows_z(nchunks - 1, (nchunks - 1) & 1, R);
     // last step: the consumers apply the last chunk
     __syncthreads();
     __syncthreads();
