@@ -628,8 +628,11 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // Tiles are computed transposed, D^T = K_J X_I^T, so that each lane holds
     // four consecutive columns j of one row i.  Diagonal blocks of T go to
     // fp32 rows for level 0 of the solve, the others to bf16 rows.
-    auto gram = [&](auto tiles, int buf) {
+    // (the Q-Delta mix is a template argument: a run-time test inside the
+    // k-step loop branches around every fragment)
+    auto gram = [&](auto tiles, int buf, auto qm) {
       using TL = decltype(tiles);
+      constexpr bool mix = decltype(qm)::value;
       constexpr int NT = TL::n;
       const bf16* Kb = sK + buf * CH * SK;
       const bf16* Qb = sQ + buf * CH * SQ;
@@ -656,7 +659,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         for (int s = 0; s < NKS; ++s) {
           const bf16x8 kj = kfr(J, s), ki = kfr(I, s), qi = qfr(I, s);
           bf16x8 xi = ki;
-          if (qmix) {
+          if constexpr (mix) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) xi[c] = (bf16)((float)ki[c] + lam * (float)qi[c]);
           }
@@ -709,10 +712,14 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       load_k(nn, R);
       load_v(n, R);
       __syncthreads();
-      if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf);
-      else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf);
-      else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf);
-      else gram(Tiles<2, 3, 2, 3, 3>{}, buf);
+      auto tiles = [&](auto qm) {
+        if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf, qm);
+        else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf, qm);
+        else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf, qm);
+        else gram(Tiles<2, 3, 2, 3, 3>{}, buf, qm);
+      };
+      if (qmix) tiles(IC<1>{});
+      else tiles(IC<0>{});
       // g and beta are loaded here rather than in phase 3, so that they have
       // arrived when the next step's prefix sum starts
       if constexpr (pw == kScanWave) load_gb(nn, R);
