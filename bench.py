@@ -139,15 +139,19 @@ def bench_workload(name, steps, warmup, op="chunk"):
         o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
         so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
         kinds = dict(decay=d["decay"], erase=d["erase"], write=d["write"], qmix=d["qmix"])
-        args = gdr.build_args(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
-                              lam=d["lam"], state=d["state"], o=o, state_out=so, **kinds)
-        copies.append((d, o, so, args))
+        gates = dict(g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], lam=d["lam"], state=d["state"])
+        # the two-pass per-channel form, where the library offers one, with
+        # its workspace (one per copy, like every other buffer)
+        ws = gdr.new_workspace(d["q"], d["k"], d["v"], **gates, **kinds) if op == "chunk" else None
+        args = gdr.build_args(d["q"], d["k"], d["v"], o=o, state_out=so, workspace=ws, **gates, **kinds)
+        copies.append((d, o, so, args, ws))
     d = copies[0][0]
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     entry = "gdr_chunk_fwd" if op == "chunk" else "gdr_recurrent_step"
     plan = gdr.plan(d["q"], d["k"], d["v"], op=op, g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
-                    lam=d["lam"], state=d["state"], **kinds)
+                    lam=d["lam"], state=d["state"], workspace=copies[0][4], **kinds)
+    plan["workspace_bytes"] = copies[0][4].numel() if copies[0][4] is not None else 0
     turn = [0]
 
     def fn():

@@ -59,9 +59,10 @@ def _check(t, name, dtype=None, ndim=None, device=None):
 
 def build_args(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
                o=None, state_out=None, decay=None, erase=None, write=None, qmix=None,
-               dv_split=0, T=None):
+               dv_split=0, T=None, workspace=None):
     """Fill a ``gdr_args`` struct from tensors (no device work).  Kinds are
-    inferred from which gates are given unless passed explicitly."""
+    inferred from which gates are given unless passed explicitly.
+    ``workspace``: an optional uint8 device tensor for the two-pass form."""
     B, Tq, H, dk = q.shape
     dv = v.shape[3]
     if decay is None:
@@ -84,7 +85,24 @@ def build_args(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=No
     a.state_in = _fptr(state)
     a.state_out = _fptr(state_out)
     a.o = _ptr(o)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
     return a
+
+
+def workspace_size(q, k, v, **kw) -> int:
+    """Bytes of workspace that ``chunk_fwd`` with these tensors can use for
+    its two-pass form (0 when the shape takes the single pass); host-only."""
+    a = build_args(q, k, v, **kw)
+    n = ctypes.c_uint64(0)
+    _lib.call("gdr_workspace_size", a, ctypes.byref(n))
+    return int(n.value)
+
+
+def new_workspace(q, k, v, **kw):
+    """A uint8 device tensor of ``workspace_size`` bytes, or None."""
+    n = workspace_size(q, k, v, **kw)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
 
 
 def _prepare(q, k, v, g, beta, b, w, lam, state, T1=False):
@@ -123,15 +141,29 @@ def _stream_ptr(device):
 
 def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
               decay=None, erase=None, write=None, qmix=None, dv_split=0,
-              out=None, state_out=None):
+              out=None, state_out=None, workspace=None, two_pass=None):
     """Chunkwise forward (C = 64) of the generalized gated delta rule.
-    Enqueued on the current stream; no synchronisation."""
+    Enqueued on the current stream; no synchronisation.
+
+    ``two_pass``: None uses the two-pass form where the library offers one
+    (allocating a workspace unless ``workspace`` is given), False never, True
+    requires it.  ``workspace``: a uint8 device tensor (see ``new_workspace``)."""
     B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
                                                              device=q.device)
-    a = build_args(q, k, v, g=g, beta=beta, b=b, w=w, lam=lam, state=state, o=o, state_out=so,
-                   decay=decay, erase=erase, write=write, qmix=qmix, dv_split=dv_split)
+    kw = dict(g=g, beta=beta, b=b, w=w, lam=lam, state=state, decay=decay, erase=erase, write=write,
+              qmix=qmix, dv_split=dv_split)
+    ws = None
+    if two_pass is not False:
+        need = workspace_size(q, k, v, **kw)
+        if two_pass and not need:
+            raise ValueError("this shape has no two-pass form")
+        if need:
+            _check(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
+            ws = workspace if workspace is not None and workspace.numel() >= need else \
+                torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = build_args(q, k, v, o=o, state_out=so, workspace=ws, **kw)
     _lib.call("gdr_chunk_fwd", a, _stream_ptr(q.device))
     return o, so
 
@@ -159,11 +191,12 @@ def plan(q, k, v, op="chunk", **kw):
     info = GdrPlanInfo()
     _lib.call("gdr_plan", a, 0 if op == "chunk" else 1, ctypes.byref(info))
     return dict(grid=info.grid, block=info.block, dv_slice=info.dv_slice, lds_bytes=info.lds_bytes,
-                n_chunks=info.n_chunks)
+                n_chunks=info.n_chunks, passes=info.passes)
 
 
 def library_path() -> str:
     return _lib.path()
 
 
-__all__ = ["chunk_fwd", "recurrent_step", "plan", "build_args", "library_path", "GdrError"]
+__all__ = ["chunk_fwd", "recurrent_step", "plan", "build_args", "workspace_size", "new_workspace",
+           "library_path", "GdrError"]

@@ -8,8 +8,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-EXPORTS = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr_validate", "gdr_plan", "gdr_status_str",
-           "gdr_last_error", "gdr_abi_version"]
+EXPORTS = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr_validate", "gdr_plan", "gdr_workspace_size",
+           "gdr_status_str", "gdr_last_error", "gdr_abi_version"]
 
 STATUS = {0: "GDR_OK", 1: "GDR_E_NULL", 2: "GDR_E_SHAPE", 3: "GDR_E_DTYPE", 4: "GDR_E_ALIGN",
           5: "GDR_E_UNSUPPORTED", 6: "GDR_E_HIP", 7: "GDR_E_ARGS"}
@@ -29,12 +29,13 @@ class GdrArgs(ctypes.Structure):
         ("g", _FP), ("beta", _FP), ("b", _FP), ("w", _FP), ("lambda_", _FP),
         ("state_in", _FP), ("state_out", _FP),
         ("o", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
 class GdrPlanInfo(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("block", ctypes.c_int32), ("dv_slice", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32), ("n_chunks", ctypes.c_int32)]
+                ("lds_bytes", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("passes", ctypes.c_int32)]
 
 
 class GdrError(RuntimeError):
@@ -68,6 +69,8 @@ def load():
     lib.gdr_validate.restype = ctypes.c_int
     lib.gdr_plan.argtypes = [ctypes.POINTER(GdrArgs), ctypes.c_int, ctypes.POINTER(GdrPlanInfo)]
     lib.gdr_plan.restype = ctypes.c_int
+    lib.gdr_workspace_size.argtypes = [ctypes.POINTER(GdrArgs), ctypes.POINTER(ctypes.c_uint64)]
+    lib.gdr_workspace_size.restype = ctypes.c_int
     lib.gdr_status_str.argtypes = [ctypes.c_int]
     lib.gdr_status_str.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []

@@ -24,6 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 
 SOURCES = ["chan_gm0.hip", "chan_gm1.hip", "chan_gm2.hip", "chan_gm3.hip", "pipe_gm0.hip", "pipe_gm3.hip",
+           "chan_split_gm0.hip", "chan_split_gm1.hip", "chan_split_gm2.hip", "chan_split_gm3.hip",
            "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip",
            "chunk_f32.hip", "step.hip", "gdr_host.cpp"]
 

@@ -54,6 +54,108 @@ struct TileList {
   static constexpr int J(int t) { return v[2 * t + 1]; }
 };
 
+// ---- T and A_qk tiles of one chunk, shared by the kernels of this file and
+// chan_split_kernel.hpp ------------------------------------------------------
+// Both kinds per tile, computed transposed (D^T = kb_J X_I^T), so that each
+// lane holds four consecutive columns j of one row i (lane l: row 16 I + l %
+// 16, columns 16 J + 4 (l / 16) + r).
+
+// Bounded-factor products: kb, xe, xq rows of stride SE, d_IJ rows of DK.
+template <int DK, int SE, class TL>
+__device__ __forceinline__ void gram_bounded_tiles(TL, const bf16* sKb, const bf16* sXe, const bf16* sXq,
+                                                   const float* sD, f32x4* accT, f32x4* accA, int g, int l16) {
+  constexpr int NKS = DK / 32;
+#pragma unroll
+  for (int t = 0; t < TL::n; ++t) {
+    const int I = TL::I(t), J = TL::J(t);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      bf16x8 kj = *reinterpret_cast<const bf16x8*>(sKb + (16 * J + l16) * SE + 32 * s + 8 * g);
+      if (J < I) {
+        const float* d = sD + (I * (I - 1) / 2 + J) * DK + 32 * s + 8 * g;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(d), d1 = *reinterpret_cast<const f32x4*>(d + 4);
+        f32x4 lo = {(float)kj[0], (float)kj[1], (float)kj[2], (float)kj[3]};
+        f32x4 hi = {(float)kj[4], (float)kj[5], (float)kj[6], (float)kj[7]};
+        kj = cat8(cvt4(lo * d0), cvt4(hi * d1));
+      }
+      const bf16x8 xe = *reinterpret_cast<const bf16x8*>(sXe + (16 * I + l16) * SE + 32 * s + 8 * g);
+      const bf16x8 xq = *reinterpret_cast<const bf16x8*>(sXq + (16 * I + l16) * SE + 32 * s + 8 * g);
+      accT[t] = mma32(kj, xe, accT[t]);
+      accA[t] = mma32(kj, xq, accA[t]);
+    }
+  }
+}
+
+// Exact entries sum_c x_i[c] k_j[c] exp(G_i[c] - G_j[c]) in fp32, for chunks
+// whose block windows exceed the limit: over slabs of SW channels staged by
+// this wave alone in st ([64 tokens][4][SW] floats; one token per lane).
+// The log-decay cumsum here is in natural units.
+template <int DK, int SW, bool ERASE_CH, class TL>
+__device__ __forceinline__ void gram_exact_tiles(TL, float* st, const bf16* kg, const bf16* qg, const float* g_seq,
+                                                 const float* b_seq, const float* beta_seq, bool qmix, float lam,
+                                                 int n, int T, int H, f32x4* accT, f32x4* accA, int lane, int g,
+                                                 int l16) {
+  const int t0 = n * CH;
+  const int t = lane;
+  const bool ok = t0 + t < T;
+  const int to = min(t0 + t, T - 1) * H;
+#pragma unroll 1
+  for (int cs = 0; cs < DK; cs += SW) {
+#pragma unroll 1
+    for (int c = 0; c < SW; ++c) {
+      const int a = to * DK + cs + c;
+      const float kv = ok ? (float)kg[a] : 0.f;
+      const float qv = ok ? (float)qg[a] : 0.f;
+      float ev;
+      if constexpr (ERASE_CH) ev = (ok ? b_seq[a] : 0.f) * kv;
+      else ev = (ok ? beta_seq[to] : 0.f) * (qmix ? kv + lam * qv : kv);
+      st[t * 4 * SW + c] = wave_incl_scan(ok ? g_seq[a] : 0.f);
+      st[t * 4 * SW + SW + c] = ev;
+      st[t * 4 * SW + 2 * SW + c] = kv;
+      st[t * 4 * SW + 3 * SW + c] = qv;
+    }
+    // (one wave: its staging writes complete before these reads)
+#pragma unroll 1
+    for (int c = 0; c < SW; ++c) {
+#pragma unroll
+      for (int tt = 0; tt < TL::n; ++tt) {
+        const int i = 16 * TL::I(tt) + l16, j0 = 16 * TL::J(tt) + 4 * g;
+        const float Gi = st[i * 4 * SW + c], ei = st[i * 4 * SW + SW + c], qi = st[i * 4 * SW + 3 * SW + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          const float Gj = st[j * 4 * SW + c], kj = st[j * 4 * SW + 2 * SW + c];
+          const float ex = (j <= i) ? fexp(Gi - Gj) : 0.f;
+          accT[tt][r] += ei * kj * ex;
+          accA[tt][r] += qi * kj * ex;
+        }
+      }
+    }
+  }
+}
+
+// Masks (T: j < i, A_qk: j <= i); T below the diagonal blocks to bf16 rows
+// of stride SC, its diagonal blocks to fp32 rows (block stride TDB, row
+// stride TDS); A_qk returned in aqk.
+template <int SC, int TDS, int TDB, class TL>
+__device__ __forceinline__ void gram_mask_tiles(TL, const f32x4* accT, const f32x4* accA, f32x4* aqk, bf16* sT,
+                                                float* sTd, int g, int l16) {
+#pragma unroll
+  for (int t = 0; t < TL::n; ++t) {
+    const int I = TL::I(t), J = TL::J(t);
+    const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
+    f32x4 xT, xA;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      xT[r] = (j0 + r < i) ? accT[t][r] : 0.f;
+      xA[r] = (j0 + r <= i) ? accA[t][r] : 0.f;
+    }
+    aqk[t] = xA;
+    if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
+    else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
+  }
+}
+
 template <int DK, int DVS>
 struct ChanLay {
   static constexpr int SE = DK + 8;                       // rows of E_bar, Q_gamma, kb, xe, xq
@@ -147,62 +249,14 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 6)) void chan_fwd_kernel(Ch
   __syncthreads();
 
   // ---- T and A_qk tiles (phase 2), shared by the producer waves ------------
-  // Both kinds per tile, computed transposed (D^T = kb_J X_I^T), so that each
-  // lane holds four consecutive columns j of one row i.  Diagonal blocks of T
-  // go to fp32 rows for the solve, the others to bf16 rows; A_qk is held
-  // until phase 3.
-  //
-  // Exact T and A_qk entries for chunks whose block windows exceed the
-  // limit: every lane accumulates its four entries (i, j) of each tile as
-  // sum_c x_i[c] k_j[c] exp(G_i[c] - G_j[c]) in fp32, over slabs of SW
-  // channels staged by this wave alone (region E, free in phase 2).
+  // Diagonal blocks of T go to fp32 rows for the solve, the others to bf16
+  // rows; A_qk is held until phase 3.  Chunks whose block windows exceed the
+  // limit take the exact tiles, staged in region E (free in phase 2).
   const bf16* qg = reinterpret_cast<const bf16*>(p.q) + seq0 * DK;
   const bf16* kg = reinterpret_cast<const bf16*>(p.k) + seq0 * DK;
   const float* g_seq = p.g + seq0 * DK;
   const float* beta_seq = p.beta ? p.beta + seq0 : nullptr;
   const float* b_seq = erase_ch ? p.b + seq0 * DK : nullptr;
-  auto gram_exact = [&](auto tl, int n, f32x4* accT, f32x4* accA) __attribute__((always_inline)) {
-    using TL = decltype(tl);
-    float* st = reinterpret_cast<float*>(smem + L::oEb) + (wave - NCW) * (CH * 4 * SW);  // [t][4][SW]
-    const int t0 = n * CH;
-    const int t = lane;  // staging: one token per lane
-    const bool ok = t0 + t < T;
-    const int to = min(t0 + t, T - 1) * H;
-#pragma unroll 1
-    for (int cs = 0; cs < DK; cs += SW) {
-#pragma unroll 1
-      for (int c = 0; c < SW; ++c) {
-        const int a = to * DK + cs + c;
-        const float kv = ok ? (float)kg[a] : 0.f;
-        const float qv = ok ? (float)qg[a] : 0.f;
-        float ev;
-        if constexpr (erase_ch) ev = (ok ? b_seq[a] : 0.f) * kv;
-        else ev = (ok ? beta_seq[to] : 0.f) * (qmix ? kv + lam * qv : kv);
-        st[t * 4 * SW + c] = wave_incl_scan(ok ? g_seq[a] : 0.f);
-        st[t * 4 * SW + SW + c] = ev;
-        st[t * 4 * SW + 2 * SW + c] = kv;
-        st[t * 4 * SW + 3 * SW + c] = qv;
-      }
-      // (one wave: its staging writes complete before these reads)
-#pragma unroll 1
-      for (int c = 0; c < SW; ++c) {
-#pragma unroll
-        for (int tt = 0; tt < TL::n; ++tt) {
-          const int i = 16 * TL::I(tt) + l16, j0 = 16 * TL::J(tt) + 4 * g;
-          const float Gi = st[i * 4 * SW + c], ei = st[i * 4 * SW + SW + c], qi = st[i * 4 * SW + 3 * SW + c];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            const float Gj = st[j * 4 * SW + c], kj = st[j * 4 * SW + 2 * SW + c];
-            const float ex = (j <= i) ? fexp(Gi - Gj) : 0.f;
-            accT[tt][r] += ei * kj * ex;
-            accA[tt][r] += qi * kj * ex;
-          }
-        }
-      }
-    }
-  };
-
   auto gram = [&](auto tiles, int n, f32x4* aqk_hold) __attribute__((always_inline)) {
     using TL = decltype(tiles);
     constexpr int NT = TL::n;
@@ -210,43 +264,13 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 6)) void chan_fwd_kernel(Ch
 #pragma unroll
     for (int t = 0; t < NT; ++t) accT[t] = accA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (sFlag[n & 1] != n + 1) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int I = TL::I(t), J = TL::J(t);
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          bf16x8 kj = *reinterpret_cast<const bf16x8*>(sKb + (16 * J + l16) * SE + 32 * s + 8 * g);
-          if (J < I) {
-            const float* d = sD + (I * (I - 1) / 2 + J) * DK + 32 * s + 8 * g;
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(d), d1 = *reinterpret_cast<const f32x4*>(d + 4);
-            f32x4 lo = {(float)kj[0], (float)kj[1], (float)kj[2], (float)kj[3]};
-            f32x4 hi = {(float)kj[4], (float)kj[5], (float)kj[6], (float)kj[7]};
-            kj = cat8(cvt4(lo * d0), cvt4(hi * d1));
-          }
-          const bf16x8 xe = *reinterpret_cast<const bf16x8*>(sXe + (16 * I + l16) * SE + 32 * s + 8 * g);
-          const bf16x8 xq = *reinterpret_cast<const bf16x8*>(sXq + (16 * I + l16) * SE + 32 * s + 8 * g);
-          accT[t] = mma32(kj, xe, accT[t]);
-          accA[t] = mma32(kj, xq, accA[t]);
-        }
-      }
+      gram_bounded_tiles<DK, SE>(tiles, sKb, sXe, sXq, sD, accT, accA, g, l16);
     } else {
-      gram_exact(tiles, n, accT, accA);
+      float* st = reinterpret_cast<float*>(smem + L::oEb) + (wave - NCW) * (CH * 4 * SW);  // [t][4][SW]
+      gram_exact_tiles<DK, SW, erase_ch>(tiles, st, kg, qg, g_seq, b_seq, beta_seq, qmix, lam, n, T, H, accT, accA,
+                                         lane, g, l16);
     }
-    // masks; i = row (lane), j = 4 columns
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int I = TL::I(t), J = TL::J(t);
-      const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
-      f32x4 xT, xA;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xT[r] = (j0 + r < i) ? accT[t][r] : 0.f;   // T: j < i
-        xA[r] = (j0 + r <= i) ? accA[t][r] : 0.f;  // A_qk: j <= i
-      }
-      aqk_hold[t] = xA;
-      if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
-      else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
-    }
+    gram_mask_tiles<SC, TDS, TDB>(tiles, accT, accA, aqk_hold, sT, sTd, g, l16);
   };
   auto store_aqk = [&](auto tiles, const f32x4* aqk_hold) __attribute__((always_inline)) {
     using TL = decltype(tiles);

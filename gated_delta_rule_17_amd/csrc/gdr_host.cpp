@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -44,6 +45,30 @@ bool overlap(const Range& a, const Range& b) {
 
 constexpr int kOpChunk = 0, kOpStep = 1;
 
+// a struct of ABI version 1 ends before the workspace fields
+constexpr size_t kArgsV1Size = offsetof(gdr_args, workspace);
+
+struct Workspace {
+  void* ptr;
+  uint64_t bytes;
+};
+Workspace workspace_of(const gdr_args* a) {
+  if (a->struct_size < sizeof(gdr_args)) return Workspace{nullptr, 0};
+  return Workspace{a->workspace, a->workspace ? a->workspace_bytes : 0};
+}
+
+// Workspace bytes of the two-pass per-channel form for slice width dvs, or 0
+// when that form does not apply: it serves bf16 I/O, dk 128 and slices of 16
+// or 32 columns (few heads), where the single-pass kernel would repeat every
+// chunk's state-independent work in many slices.
+int64_t split_bytes(const gdr_args* a, int dvs) {
+  if (gdr::chunk_kernel_for(a->io == GDR_BF16, a->decay, a->erase) != gdr::kChan || a->dk != 128 ||
+      (dvs != 16 && dvs != 32) || a->T < 1)
+    return 0;
+  const int64_t nchunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
+  return int64_t(a->B) * a->H * nchunks * gdr::kSplitRecBytes;
+}
+
 int dvs_candidates(int io, int* out) {
   if (io == GDR_BF16) {
     out[0] = 64; out[1] = 32; out[2] = 16;
@@ -80,9 +105,9 @@ int chunk_block(const gdr_args* a, int dvs) {
 
 gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (!a) return fail(GDR_E_NULL, "gdr_args pointer is NULL");
-  if (a->struct_size < sizeof(gdr_args))
-    return fail(GDR_E_ARGS, "struct_size %u is smaller than sizeof(gdr_args) = %zu", a->struct_size,
-                sizeof(gdr_args));
+  if (a->struct_size < kArgsV1Size)
+    return fail(GDR_E_ARGS, "struct_size %u is smaller than the version-1 gdr_args (%zu bytes)", a->struct_size,
+                kArgsV1Size);
   if (op != kOpChunk && op != kOpStep) return fail(GDR_E_ARGS, "unknown op %d", op);
   if (a->B < 1 || a->H < 1 || a->T < 0)
     return fail(GDR_E_SHAPE, "need B >= 1, H >= 1, T >= 0 (got B=%d H=%d T=%d)", a->B, a->H, a->T);
@@ -179,6 +204,7 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
   const int64_t BH = int64_t(a->B) * a->H;
   gdr_plan_info pi{};
   pi.block = 256;
+  pi.passes = 1;
   if (op == kOpStep) {
     pi.grid = static_cast<int32_t>(BH);
     pi.dv_slice = a->dv;
@@ -196,9 +222,18 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
     }
     pi.dv_slice = dvs;
     pi.grid = static_cast<int32_t>(BH * (a->dv / dvs));
-    pi.lds_bytes = chunk_lds(a, dvs);
-    pi.block = chunk_block(a, dvs);
     pi.n_chunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
+    const int64_t need = split_bytes(a, dvs);
+    const Workspace ws = workspace_of(a);
+    if (need > 0 && ws.ptr && ws.bytes >= static_cast<uint64_t>(need)) {
+      pi.passes = 2;
+      pi.lds_bytes = gdr::chan_split_lds(gdr::gate_mode(a->erase, a->write), a->dk, dvs);
+      pi.block = 64 * ((dvs >= 32 ? 2 : 1) + 4);
+    } else {
+      pi.passes = 1;
+      pi.lds_bytes = chunk_lds(a, dvs);
+      pi.block = chunk_block(a, dvs);
+    }
     if (pi.lds_bytes < 0)
       return fail(GDR_E_UNSUPPORTED, "no kernel instance for io=%d dk=%d slice=%d", a->io, a->dk, dvs);
   }
@@ -218,6 +253,18 @@ gdr_status gdr_plan(const gdr_args* a, int op, gdr_plan_info* out) {
   return plan_impl(a, op, out);
 }
 
+gdr_status gdr_workspace_size(const gdr_args* a, uint64_t* bytes) {
+  if (!bytes) return fail(GDR_E_NULL, "bytes pointer is NULL");
+  *bytes = 0;
+  gdr_status s = validate_impl(a, kOpChunk, /*check_ptrs=*/false);
+  if (s != GDR_OK) return s;
+  gdr_plan_info pi;
+  s = plan_impl(a, kOpChunk, &pi);
+  if (s != GDR_OK) return s;
+  *bytes = static_cast<uint64_t>(split_bytes(a, pi.dv_slice));
+  return GDR_OK;
+}
+
 gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   gdr_status s = validate_impl(a, kOpChunk);
   if (s != GDR_OK) return s;
@@ -225,6 +272,25 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   s = plan_impl(a, kOpChunk, &pi);
   if (s != GDR_OK) return s;
   if (a->T == 0 && !a->state_out) return GDR_OK;
+  const Workspace ws = workspace_of(a);
+  if (pi.passes == 2) {
+    // the workspace of the two-pass form: aligned, and apart from every
+    // other buffer of the call
+    if (!aligned(ws.ptr, 256)) return fail(GDR_E_ALIGN, "workspace is not 256-byte aligned");
+    const int64_t tokens = int64_t(a->B) * a->H * a->T;
+    const int64_t BH = int64_t(a->B) * a->H;
+    const int64_t ioe = a->io == GDR_BF16 ? 2 : 4;
+    const Range rw = rng("workspace", ws.ptr, static_cast<int64_t>(ws.bytes));
+    const Range others[] = {rng("q", a->q, tokens * a->dk * ioe),    rng("k", a->k, tokens * a->dk * ioe),
+                            rng("v", a->v, tokens * a->dv * ioe),    rng("o", a->o, tokens * a->dv * ioe),
+                            rng("g", a->g, tokens * a->dk * 4),      rng("beta", a->beta, tokens * 4),
+                            rng("b", a->b, tokens * a->dk * 4),      rng("w", a->w, tokens * a->dv * 4),
+                            rng("lambda", a->lambda, int64_t(a->H) * 4),
+                            rng("state_in", a->state_in, BH * a->dk * a->dv * 4),
+                            rng("state_out", a->state_out, BH * a->dk * a->dv * 4)};
+    for (const Range& r : others)
+      if (overlap(rw, r)) return fail(GDR_E_ARGS, "workspace overlaps %s", r.name);
+  }
   gdr::ChunkParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.g = a->g; p.beta = a->beta; p.b = a->b; p.w = a->w; p.lam = a->lambda;
@@ -236,6 +302,12 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int gm = gdr::gate_mode(a->erase, a->write);
   hipError_t e;
+  if (pi.passes == 2) {
+    const int prep_grid = static_cast<int>(int64_t(a->B) * a->H * pi.n_chunks);
+    e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
+    if (e != hipSuccess) return fail(GDR_E_HIP, "two-pass chunk kernels failed to launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+  }
   switch (kernel_for(a)) {
     case gdr::kPipe: e = gdr::launch_pipe(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;
     case gdr::kChan: e = gdr::launch_chan(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;

@@ -44,6 +44,42 @@ GDR_DECLARE(chan_gm2)
 GDR_DECLARE(chan_gm3)
 #undef GDR_DECLARE
 
+// Two-pass kernels for a per-key-channel decay (bf16 I/O, dk 128, value
+// slices of 16 or 32), one pair per gate mode: *_lds gives the second pass's
+// LDS bytes (-1: no instance); *_launch enqueues both passes (prep_grid
+// chunk workgroups, then grid slice workgroups) with workspace ws.
+#define GDR_DECLARE(name)                 \
+  int name##_lds(int dk, int dvs);       \
+  hipError_t name##_launch(const ChunkParams& p, void* ws, int dk, int dvs, int grid, int prep_grid, hipStream_t s);
+GDR_DECLARE(chan_split_gm0)
+GDR_DECLARE(chan_split_gm1)
+GDR_DECLARE(chan_split_gm2)
+GDR_DECLARE(chan_split_gm3)
+#undef GDR_DECLARE
+
+inline int chan_split_lds(int gm, int dk, int dvs) {
+  switch (gm) {
+    case 0: return chan_split_gm0_lds(dk, dvs);
+    case 1: return chan_split_gm1_lds(dk, dvs);
+    case 2: return chan_split_gm2_lds(dk, dvs);
+    default: return chan_split_gm3_lds(dk, dvs);
+  }
+}
+
+inline hipError_t launch_chan_split(int gm, const ChunkParams& p, void* ws, int dk, int dvs, int grid,
+                                    int prep_grid, hipStream_t s) {
+  switch (gm) {
+    case 0: return chan_split_gm0_launch(p, ws, dk, dvs, grid, prep_grid, s);
+    case 1: return chan_split_gm1_launch(p, ws, dk, dvs, grid, prep_grid, s);
+    case 2: return chan_split_gm2_launch(p, ws, dk, dvs, grid, prep_grid, s);
+    default: return chan_split_gm3_launch(p, ws, dk, dvs, grid, prep_grid, s);
+  }
+}
+
+// bytes of one chunk's workspace record (dk 128): E_bar, Q_gamma, K_tail
+// rows, A, A_qk, gamma_C (matches SplitRec in chan_split_kernel.hpp)
+constexpr int64_t kSplitRecBytes = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4;
+
 // Chunk kernel chosen for (io, decay kind, erase kind): the pipelined kernels
 // take bf16 I/O, the scalar-decay one the beta erase gate only; the rest go to
 // the one-pass kernel.

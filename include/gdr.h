@@ -38,8 +38,9 @@
  * activations; g = log(alpha) <= 0 is finite.  The library never rescales.
  *
  * Conventions for every entry point:
- *  - Ownership: the caller owns every buffer.  The library allocates nothing,
- *    frees nothing and keeps no pointer after the call returns.
+ *  - Ownership: the caller owns every buffer, the optional workspace
+ *    included.  The library allocates nothing, frees nothing and keeps no
+ *    pointer after the call returns.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    with no host synchronisation.  Pointers are device pointers.
  *  - Inputs are read-only.  `o` must not overlap any input.  `state_out` may
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 #define GDR_CHUNK 64
 
 typedef enum gdr_status {
@@ -94,10 +95,24 @@ typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
  *   state_out[B,H,dk,dv] fp32, 16-byte aligned, or NULL (not written)
  *
  * Fields set to zero select defaults; set struct_size = sizeof(gdr_args).
+ * A struct of ABI version 1 (ending at `o`, struct_size = offsetof(gdr_args,
+ * workspace)) is accepted and runs without a workspace.
  * dv_split: 0 lets the library choose how many workgroups share one head's
  * value columns; otherwise the column-slice width (16, 32 or 64, dividing dv).
  * When T == 0, q/k/v/o/gates may be NULL and state_out receives state_in
  * (or zeros).
+ *
+ * workspace, workspace_bytes: optional device scratch, 256-byte aligned, for
+ * the two-pass form of the per-channel-decay forward (bf16 I/O, dk = 128).
+ * When a head's value columns are split into slices of 16 or 32 (few heads:
+ * B * H * dv / 64 < 256), the single-pass kernel repeats every chunk's state-independent work
+ * (decay factors, Gram, inverse) in each slice; with a workspace of at least
+ * gdr_workspace_size() bytes that work runs once per chunk, in a separate
+ * parallel pass that writes one 64.5 KiB record per (batch, head, chunk) to
+ * the workspace, and a second pass applies the records to the state.  NULL
+ * (or too small) keeps the single pass.  The workspace must not overlap any
+ * other argument; its contents are undefined after the call, and concurrent
+ * calls need separate workspaces.
  */
 typedef struct gdr_args {
   uint32_t struct_size;
@@ -114,6 +129,8 @@ typedef struct gdr_args {
   const float *state_in;
   float *state_out;
   void *o;
+  void *workspace;          /* optional, see above; NULL = none */
+  uint64_t workspace_bytes; /* bytes available at workspace */
 } gdr_args;
 
 /* What a call would launch (filled by gdr_plan). */
@@ -123,6 +140,8 @@ typedef struct gdr_plan_info {
   int32_t dv_slice;    /* value columns per workgroup */
   int32_t lds_bytes;   /* LDS per workgroup */
   int32_t n_chunks;    /* chunks per sequence */
+  int32_t passes;      /* 1, or 2 for the workspace form (grid, block and
+                          lds_bytes then describe the second pass) */
 } gdr_plan_info;
 
 /*
@@ -140,6 +159,10 @@ gdr_status gdr_chunk_fwd(const gdr_args *a, void *stream);
  * {64, 128}.  state_out may equal state_in for an in-place update.
  */
 gdr_status gdr_recurrent_step(const gdr_args *a, void *stream);
+
+/* Host-only: the workspace bytes that gdr_chunk_fwd can use for `a` (0 when
+ * the shape takes no workspace).  Checks `a` like gdr_plan. */
+gdr_status gdr_workspace_size(const gdr_args *a, uint64_t *bytes);
 
 /* Host-only validation of `a` for op 0 (chunk) or 1 (step); launches nothing
  * and touches no device memory, so it runs without a GPU. */

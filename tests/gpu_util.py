@@ -29,9 +29,9 @@ def gpu_kwargs(d):
                 decay=d["decay"], erase=d["erase"], write=d["write"], qmix=d["qmix"])
 
 
-def run_chunk(inp, dv_split=0):
+def run_chunk(inp, dv_split=0, two_pass=None):
     d = to_dev(inp)
-    o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], dv_split=dv_split, **gpu_kwargs(d))
+    o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], dv_split=dv_split, two_pass=two_pass, **gpu_kwargs(d))
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), S.cpu().numpy()
 

@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_functions_are_exported(lib):
     declared = _declared_functions()
     assert set(declared) >= {"gdr_chunk_fwd", "gdr_recurrent_step", "gdr_status_str",
-                             "gdr_last_error", "gdr_abi_version", "gdr_validate", "gdr_plan"}
+                             "gdr_last_error", "gdr_abi_version", "gdr_validate", "gdr_plan",
+                             "gdr_workspace_size"}
     for name in declared:
         assert hasattr(lib, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.path()], capture_output=True, text=True)
@@ -44,7 +45,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_abi_version() == 2
     for code, name in _lib.STATUS.items():
         assert lib.gdr_status_str(code).decode() == name
     assert lib.gdr_status_str(99).decode() == "GDR_E_UNKNOWN"
@@ -182,3 +183,76 @@ def test_plan_kernel_choice(lib, decay, erase, block):
     info = GdrPlanInfo()
     assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
     assert info.block == block and info.dv_slice == 64
+
+
+# ---- the workspace of the two-pass per-channel form ---------------------------
+
+REC = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4  # bytes of one chunk's record
+
+
+def _chan_args(**kw):
+    """Gated DeltaNet-2 kinds (per-channel decay, erase and write gates)."""
+    base = dict(decay=2, erase=1, write=1, beta=0, b=_addr(9), w=_addr(10))
+    base.update(kw)
+    return good_args(**base)
+
+
+def _ws_size(lib, a):
+    n = ctypes.c_uint64(123)
+    st = lib.gdr_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("B,H,T,dk,decay,io,expect_chunks", [
+    (1, 32, 200, 128, 2, 1, 4),   # 32 heads -> 16-column slices: two-pass form, 4 chunks each
+    (2, 16, 65, 128, 2, 1, 2),    # 32 heads, ragged tail
+    (2, 32, 200, 128, 2, 1, 4),   # 64 heads -> 32-column slices
+    (8, 16, 200, 128, 2, 1, 0),   # 128 heads -> 64-column slices: single pass
+    (1, 32, 200, 64, 2, 1, 0),    # dk 64: single pass
+    (1, 32, 200, 128, 1, 1, 0),   # scalar decay: the scalar-decay kernel
+    (1, 32, 0, 128, 2, 1, 0),     # nothing to do
+])
+def test_workspace_size(lib, B, H, T, dk, decay, io, expect_chunks):
+    kw = {} if decay == 2 else dict(erase=0, write=0, beta=_addr(5), b=0, w=0)
+    a = _chan_args(B=B, H=H, T=T, dk=dk, decay=decay, io=io, **kw)
+    st, n = _ws_size(lib, a)
+    assert st == OK, lib.gdr_last_error()
+    assert n == B * H * expect_chunks * REC
+
+
+def test_workspace_switches_the_plan(lib):
+    a = _chan_args(B=1, H=32, T=200)
+    st, need = _ws_size(lib, a)
+    assert st == OK and need == 32 * 4 * REC
+    info = GdrPlanInfo()
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+    assert info.passes == 1 and info.block == 64 * 7   # single pass: 1 consumer + 6 producer waves
+    a.workspace, a.workspace_bytes = _addr(11), need - 1  # too small: still one pass
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK and info.passes == 1
+    a.workspace_bytes = need
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+    assert info.passes == 2 and info.dv_slice == 16 and info.grid == 32 * 8
+    assert info.block == 64 * 5 and 0 < info.lds_bytes <= 160 * 1024   # 1 consumer + 4 loader waves
+
+
+def test_version_one_struct_runs_without_workspace(lib):
+    v1 = GdrArgs.workspace.offset
+    a = _chan_args(B=1, H=32, T=200, workspace=_addr(11), workspace_bytes=1 << 40)
+    a.struct_size = v1
+    info = GdrPlanInfo()
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK and info.passes == 1
+    a.struct_size = v1 - 8
+    assert _validate(lib, a) == E_ARGS
+
+
+def test_workspace_errors_return_before_launch(lib):
+    a = _chan_args(B=1, H=32, T=200)
+    _, need = _ws_size(lib, a)
+    a.workspace, a.workspace_bytes = _addr(11, 128), need      # not 256-byte aligned
+    assert lib.gdr_chunk_fwd(ctypes.byref(a), None) == E_ALIGN
+    a.workspace = _addr(0)                                      # on top of q
+    assert lib.gdr_chunk_fwd(ctypes.byref(a), None) == E_ARGS
+    assert b"workspace" in lib.gdr_last_error()
+    n = ctypes.c_uint64(0)
+    assert lib.gdr_workspace_size(None, ctypes.byref(n)) == E_NULL
+    assert lib.gdr_workspace_size(ctypes.byref(a), None) == E_NULL

@@ -31,17 +31,27 @@ def test_full_size_sampled_heads(name):
     say(f"[full] {name}: generating")
     inp = make_inputs(cfg)
     d = to_dev(inp)
-    say(f"[full] {name}: chunk_fwd {gdr.plan(d['q'], d['k'], d['v'], g=d['g'], beta=d['beta'], b=d['b'], w=d['w'], lam=d['lam'])}")
-    o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], **gpu_kwargs(d))
-    torch.cuda.synchronize()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    # the form bench.py times (two passes where the library offers them), and
+    # the single pass too where that differs
+    forms = [None] + ([False] if gdr.workspace_size(d["q"], d["k"], d["v"], **gpu_kwargs(d)) else [])
+    results = []
+    for two_pass in forms:
+        ws = None if two_pass is False else gdr.new_workspace(d["q"], d["k"], d["v"], **gpu_kwargs(d))
+        plan = gdr.plan(d["q"], d["k"], d["v"], workspace=ws, **gpu_kwargs(d))
+        say(f"[full] {name}: chunk_fwd two_pass={two_pass} {plan}")
+        o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], two_pass=two_pass, workspace=ws, **gpu_kwargs(d))
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+        results.append((two_pass, o.float().cpu(), S.cpu()))
+        del o, S, ws
     heads = _sample_heads(cfg["B"], cfg["H"], 2 if cfg["T"] > 10000 else 3, seed=len(name))
     say(f"[full] {name}: oracle on heads {heads}")
     o_ref, S_ref = run_oracle(inp, heads)
-    for (b, h), orf, srf in zip(heads, o_ref, S_ref):
-        assert_parity(f"{name} b={b} h={h}", o[b, :, h].float().cpu().numpy(), S[b, h].cpu().numpy(),
-                      orf, srf, TOL[cfg["io"]])
-    del d, o, S
+    for two_pass, o, S in results:
+        for (b, h), orf, srf in zip(heads, o_ref, S_ref):
+            assert_parity(f"{name} two_pass={two_pass} b={b} h={h}", o[b, :, h].numpy(), S[b, h].numpy(),
+                          orf, srf, TOL[cfg["io"]])
+    del d, results
     torch.cuda.empty_cache()
 
 

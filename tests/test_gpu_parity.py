@@ -70,14 +70,45 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
-def test_chunk_parity(name):
+def _two_pass_form(cfg):
+    """Shapes on which chunk_fwd takes the two-pass per-channel form by
+    default (bf16, dk 128, per-channel decay, few heads)."""
+    dk, dv = cfg.get("dk", cfg["d"]), cfg.get("dv", cfg["d"])
+    decay = cfg.get("decay") or ("channel" if cfg["variant"] in ("kda", "gdn2") else "scalar")
+    return cfg["io"] == "bf16" and dk == 128 and decay == "channel" and cfg["B"] * cfg["H"] * dv // 64 < 256
+
+
+# every case as chunk_fwd runs it by default, and the two-pass cases once more
+# on the single-pass kernel
+PARITY = [(n, None) for n in sorted(CASES)] + [(n, False) for n in sorted(CASES) if _two_pass_form(CASES[n])]
+
+
+@pytest.mark.parametrize("name,two_pass", PARITY)
+def test_chunk_parity(name, two_pass):
     cfg = CASES[name]
-    say(f"[chunk parity] {name}: {cfg}")
+    say(f"[chunk parity] {name} two_pass={two_pass}: {cfg}")
     inp = make_inputs(cfg)
-    o, S = run_chunk(inp)
+    o, S = run_chunk(inp, two_pass=two_pass)
     o_ref, S_ref = run_oracle(inp)
     assert_parity(name, o, S, o_ref, S_ref, TOL[cfg["io"]])
+
+
+@pytest.mark.parametrize("name", ["gdn2_bf16_small", "kda_bf16_small", "gdn2_extreme"])
+def test_two_pass_form(name):
+    """The two-pass form is what the plan reports with a workspace, and its
+    16- and 32-column slices give bitwise-identical results."""
+    cfg = CASES[name]
+    inp = make_inputs(cfg)
+    d = to_dev(inp)
+    ws = gdr.new_workspace(d["q"], d["k"], d["v"], **gpu_kwargs(d))
+    assert ws is not None
+    assert gdr.plan(d["q"], d["k"], d["v"], workspace=ws, **gpu_kwargs(d))["passes"] == 2
+    assert gdr.plan(d["q"], d["k"], d["v"], **gpu_kwargs(d))["passes"] == 1
+    outs = []
+    for wdt in (16, 32):
+        say(f"[two-pass] {name} dv_split={wdt}")
+        outs.append(run_chunk(inp, dv_split=wdt, two_pass=True))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
 @pytest.mark.parametrize("name", ["gdn_bf16_small", "gdn2_bf16_small", "kda_f32_mild"])
@@ -90,7 +121,7 @@ def test_slice_width_does_not_change_results(name):
     ref = None
     for wdt in widths:
         say(f"[slice] {name} dv_split={wdt}")
-        o, S = run_chunk(inp, dv_split=wdt)
+        o, S = run_chunk(inp, dv_split=wdt, two_pass=False)
         if ref is None:
             ref = (o, S)
         else:

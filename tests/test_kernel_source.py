@@ -13,7 +13,7 @@ import re
 import pytest
 
 CSRC = os.path.join(os.path.dirname(__file__), "..", "gated_delta_rule_17_amd", "csrc")
-SOURCES = ["pipe_kernel.hpp", "chan_kernel.hpp"]
+SOURCES = ["pipe_kernel.hpp", "chan_kernel.hpp", "chan_split_kernel.hpp"]
 LOOP_RE = re.compile(r"for \(int n = 0; n (<|<=) nchunks; \+\+n\)")
 
 
