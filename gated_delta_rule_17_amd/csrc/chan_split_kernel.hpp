@@ -368,6 +368,18 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
         const bf16* sZ = reinterpret_cast<const bf16*>(smem + L::oZ + buf * L::szZ);
         const float* gC = reinterpret_cast<const float*>(smem + L::oGc) + buf * DK;
 
+        // The three phases of a chunk run back to back in this wave, so each
+        // requests the next one's LDS fragments before its own products:
+        // A (transposing reads) and A_qk rows for W and O, K_tail^T and
+        // gamma_C for the state update.
+        auto afrag = [&](int pp, int h, int m2) __attribute__((always_inline)) {
+          const int col = 32 * pp + 8 * (l16 & 3) + 4 * h;
+          return cat8(lds_tr4(sAcm + (32 * m2 + 4 * g + (l16 >> 2)) * SC + col),
+                      lds_tr4(sAcm + (32 * m2 + 16 + 4 * g + (l16 >> 2)) * SC + col));
+        };
+        bf16x8 Af[2][2][2], Aq[4][2], Kt[2 * NKS][2];
+        f32x4 Gc[2 * NKS];
+
         // E_bar S and Q_gamma S
         f32x4 ES[4][NB], QS[4][NB];
         {
@@ -376,7 +388,8 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
           for (int m = 0; m < NKS; ++m)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) Sb[m][nb] = cat8(cvt4(S[2 * m][nb]), cvt4(S[2 * m + 1][nb]));
-          bf16x8 ef[2][NKS], qf[2][NKS];
+          // fragments of row block I + 2 are requested while block I multiplies
+          bf16x8 ef[3][NKS], qf[3][NKS];
           auto load_eq = [&](int I, int slot) __attribute__((always_inline)) {
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
@@ -385,17 +398,31 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
             }
           };
           load_eq(0, 0);
+          load_eq(1, 1);
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
-            if (I < 3) load_eq(I + 1, (I + 1) & 1);
+            if (I + 2 < 4) load_eq(I + 2, (I + 2) % 3);
+            if (I == 2) {
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                  for (int m2 = 0; m2 <= pp; ++m2) Af[pp][h][m2] = afrag(pp, h, m2);
+#pragma unroll
+              for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int pp = 0; pp <= J / 2; ++pp)
+                  Aq[J][pp] = *reinterpret_cast<const bf16x8*>(sAqk + (16 * J + l16) * SC + 32 * pp + 8 * g);
+            }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
               ES[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
               QS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int m = 0; m < NKS; ++m) {
-                ES[I][nb] = mma32(ef[I & 1][m], Sb[m][nb], ES[I][nb]);
-                QS[I][nb] = mma32(qf[I & 1][m], Sb[m][nb], QS[I][nb]);
+                ES[I][nb] = mma32(ef[I % 3][m], Sb[m][nb], ES[I][nb]);
+                QS[I][nb] = mma32(qf[I % 3][m], Sb[m][nb], QS[I][nb]);
               }
             }
           }
@@ -427,16 +454,23 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int m2 = 0; m2 <= pp; ++m2) {
-                const int col = 32 * pp + 8 * (l16 & 3) + 4 * h;
-                const bf16x8 af = cat8(lds_tr4(sAcm + (32 * m2 + 4 * g + (l16 >> 2)) * SC + col),
-                                       lds_tr4(sAcm + (32 * m2 + 16 + 4 * g + (l16 >> 2)) * SC + col));
+              for (int m2 = 0; m2 <= pp; ++m2)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Rb[m2][nb], acc[nb]);
-              }
+                for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(Af[pp][h][m2], Rb[m2][nb], acc[nb]);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) Wt[2 * pp + h][nb] = acc[nb];
             }
+          // the state update's fragments, requested behind W's products
+#pragma unroll
+          for (int j = 0; j < 2 * NKS; ++j) {
+            const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+              Kt[j][pp] = cat8(lds_tr4(sKt + (32 * pp + 8 * g + (l16 >> 2)) * SKT + col),
+                               lds_tr4(sKt + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SKT + col));
+            // rows of state tile j: channels 32 (j/2) + 8 g + 4 (j%2) + r
+            Gc[j] = *reinterpret_cast<const f32x4*>(gC + 32 * (j >> 1) + 8 * g + 4 * (j & 1));
+          }
           bf16x8 Wb[2][NB];
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp)
@@ -447,11 +481,9 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) Oh[I][nb] = QS[I][nb];
 #pragma unroll
-            for (int pp = 0; pp <= I / 2; ++pp) {
-              const bf16x8 af = *reinterpret_cast<const bf16x8*>(sAqk + (16 * I + l16) * SC + 32 * pp + 8 * g);
+            for (int pp = 0; pp <= I / 2; ++pp)
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) Oh[I][nb] = mma32(af, Wb[pp][nb], Oh[I][nb]);
-            }
+              for (int nb = 0; nb < NB; ++nb) Oh[I][nb] = mma32(Aq[I][pp], Wb[pp][nb], Oh[I][nb]);
           }
         }
 
@@ -462,25 +494,13 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
           for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) Wtb[pp][nb] = cat8(cvt4(Wt[2 * pp][nb]), cvt4(Wt[2 * pp + 1][nb]));
-          bf16x8 kt[2][2];
-          auto load_kt = [&](int j, int slot) __attribute__((always_inline)) {
-            const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
-              kt[slot][pp] = cat8(lds_tr4(sKt + (32 * pp + 8 * g + (l16 >> 2)) * SKT + col),
-                                  lds_tr4(sKt + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SKT + col));
-          };
-          load_kt(0, 0);
 #pragma unroll
           for (int j = 0; j < 2 * NKS; ++j) {
-            if (j + 1 < 2 * NKS) load_kt(j + 1, (j + 1) & 1);
-            // rows of state tile j: channels 32 (j/2) + 8 g + 4 (j%2) + r
-            const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 32 * (j >> 1) + 8 * g + 4 * (j & 1));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              f32x4 acc = S[j][nb] * gc;
+              f32x4 acc = S[j][nb] * Gc[j];
 #pragma unroll
-              for (int pp = 0; pp < 2; ++pp) acc = mma32(kt[j & 1][pp], Wtb[pp][nb], acc);
+              for (int pp = 0; pp < 2; ++pp) acc = mma32(Kt[j][pp], Wtb[pp][nb], acc);
               S[j][nb] = acc;
             }
           }

@@ -54,6 +54,7 @@ struct ChunkParams {
   int write;  // 0 beta, 1 channel
   int qmix;
   int nslices;
+  const void* ws;  // workspace records of the two-pass forms (else unused)
 };
 
 // largest 16-token log-decay window for which the bounded-factor Gram is

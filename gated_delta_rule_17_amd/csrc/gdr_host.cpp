@@ -57,16 +57,16 @@ Workspace workspace_of(const gdr_args* a) {
   return Workspace{a->workspace, a->workspace ? a->workspace_bytes : 0};
 }
 
-// Workspace bytes of the two-pass per-channel form for slice width dvs, or 0
-// when that form does not apply: it serves bf16 I/O, dk 128 and slices of 16
-// or 32 columns (few heads), where the single-pass kernel would repeat every
-// chunk's state-independent work in many slices.
+// Workspace bytes of the two-pass form for slice width dvs, or 0 when that
+// form does not apply: it serves the two pipelined kernels (bf16 I/O) at dk
+// 128 with slices of 16 or 32 columns (few heads), where a single pass would
+// repeat every chunk's state-independent work in many slices.
 int64_t split_bytes(const gdr_args* a, int dvs) {
-  if (gdr::chunk_kernel_for(a->io == GDR_BF16, a->decay, a->erase) != gdr::kChan || a->dk != 128 ||
-      (dvs != 16 && dvs != 32) || a->T < 1)
+  const gdr::ChunkKernel kern = gdr::chunk_kernel_for(a->io == GDR_BF16, a->decay, a->erase);
+  if ((kern != gdr::kChan && kern != gdr::kPipe) || a->dk != 128 || (dvs != 16 && dvs != 32) || a->T < 1)
     return 0;
   const int64_t nchunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
-  return int64_t(a->B) * a->H * nchunks * gdr::kSplitRecBytes;
+  return int64_t(a->B) * a->H * nchunks * (kern == gdr::kChan ? gdr::kSplitRecBytes : gdr::kPipeRecBytes);
 }
 
 int dvs_candidates(int io, int* out) {
@@ -227,7 +227,8 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
     const Workspace ws = workspace_of(a);
     if (need > 0 && ws.ptr && ws.bytes >= static_cast<uint64_t>(need)) {
       pi.passes = 2;
-      pi.lds_bytes = gdr::chan_split_lds(gdr::gate_mode(a->erase, a->write), a->dk, dvs);
+      const bool chan = kernel_for(a) == gdr::kChan;
+      pi.lds_bytes = chan ? gdr::chan_split_lds(gdr::gate_mode(a->erase, a->write), a->dk, dvs) : chunk_lds(a, dvs);
       pi.block = 64 * ((dvs >= 32 ? 2 : 1) + 4);
     } else {
       pi.passes = 1;
@@ -283,7 +284,8 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
     const Range rw = rng("workspace", ws.ptr, static_cast<int64_t>(ws.bytes));
     const Range others[] = {rng("q", a->q, tokens * a->dk * ioe),    rng("k", a->k, tokens * a->dk * ioe),
                             rng("v", a->v, tokens * a->dv * ioe),    rng("o", a->o, tokens * a->dv * ioe),
-                            rng("g", a->g, tokens * a->dk * 4),      rng("beta", a->beta, tokens * 4),
+                            rng("g", a->g, a->decay == GDR_DECAY_CHANNEL ? tokens * a->dk * 4 : tokens * 4),
+                            rng("beta", a->beta, tokens * 4),
                             rng("b", a->b, tokens * a->dk * 4),      rng("w", a->w, tokens * a->dv * 4),
                             rng("lambda", a->lambda, int64_t(a->H) * 4),
                             rng("state_in", a->state_in, BH * a->dk * a->dv * 4),
@@ -304,7 +306,9 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   hipError_t e;
   if (pi.passes == 2) {
     const int prep_grid = static_cast<int>(int64_t(a->B) * a->H * pi.n_chunks);
-    e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
+    p.ws = ws.ptr;
+    if (kernel_for(a) == gdr::kChan) e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
+    else e = gdr::launch_pipe_split(gm, p, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
     if (e != hipSuccess) return fail(GDR_E_HIP, "two-pass chunk kernels failed to launch: %s", hipGetErrorString(e));
     return GDR_OK;
   }

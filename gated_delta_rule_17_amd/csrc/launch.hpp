@@ -26,12 +26,26 @@ GDR_DECLARE(chunk_f32_gm3)
 
 // Pipelined kernel (bf16 I/O, no or scalar decay, beta erase gate), one pair
 // per write-gate mode (0 = beta, 3 = per value channel).
+// *_split_launch enqueues the two-pass form (dk 128, slices of 16 or 32):
+// prep_grid chunk workgroups writing records to p.ws, then the pipelined
+// kernel reading them.
 #define GDR_DECLARE(name)                  \
   int name##_lds(int dk, int dvs);        \
-  hipError_t name##_launch(const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s);
+  hipError_t name##_launch(const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s); \
+  hipError_t name##_split_launch(const ChunkParams& p, int dk, int dvs, int grid, int prep_grid, hipStream_t s);
 GDR_DECLARE(pipe_gm0)
 GDR_DECLARE(pipe_gm3)
 #undef GDR_DECLARE
+
+// bytes of one chunk's record in the scalar-decay two-pass form: A, A_qk,
+// 336 chunk scalars (matches PipeRec in pipe_kernel.hpp)
+constexpr int64_t kPipeRecBytes = 17920;
+
+inline hipError_t launch_pipe_split(int gm, const ChunkParams& p, int dk, int dvs, int grid, int prep_grid,
+                                    hipStream_t s) {
+  return gm == 0 ? pipe_gm0_split_launch(p, dk, dvs, grid, prep_grid, s)
+                 : pipe_gm3_split_launch(p, dk, dvs, grid, prep_grid, s);
+}
 
 // Pipelined kernel for a per-key-channel decay (bf16 I/O), one pair per gate
 // mode.

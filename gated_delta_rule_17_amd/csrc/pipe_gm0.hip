@@ -1,7 +1,7 @@
 // Pipelined chunk kernel, bf16 I/O, beta erase gate, write gate mode 0
 // (beta).
 #include "launch.hpp"
-#include "pipe_kernel.hpp"
+#include "pipe_split_kernel.hpp"
 
 #define GDR_GM 0
 #define GDR_NAME(x) pipe_gm0_##x

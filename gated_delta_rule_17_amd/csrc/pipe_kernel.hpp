@@ -173,6 +173,67 @@ __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, b
     }
 }
 
+// T and A_qk tiles (list TL) of one chunk under no or a scalar decay, as
+// D^T = K_J X_I^T (X = K, or K + lam Q under the Q-Delta mix, for T; Q for
+// A_qk), so that each lane holds four consecutive columns j of one row i;
+// then the decay exp(G_i - G_j) <= 1, beta_i on T, and the masks (T: j < i,
+// A_qk: j <= i).  K, Q rows of strides SK, SQ; G and beta per token.  T below
+// the diagonal blocks goes to bf16 rows of sT (stride SC), its diagonal
+// blocks to fp32 rows of sTd (block stride TDB, row stride TDS); A_qk to bf16
+// rows of aqk with row stride AS.
+template <int DK, int SK, int SQ, int SC, int TDS, int TDB, bool MIX, class TL>
+__device__ __forceinline__ void scalar_gram_tiles(TL, const bf16* Kb, const bf16* Qb, const float* sG,
+                                                  const float* sBeta, float lam, bf16* sT, float* sTd, bf16* aqk,
+                                                  int AS, int g, int l16) {
+  constexpr int NT = TL::n, NKS = DK / 32;
+  // fragments of 16 rows (identical loads are merged by the compiler)
+  auto kfr = [&](int blk, int s) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(Kb + (16 * blk + l16) * SK + 32 * s + 8 * g);
+  };
+  auto qfr = [&](int blk, int s) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(Qb + (16 * blk + l16) * SQ + 32 * s + 8 * g);
+  };
+  f32x4 accT[NT], accA[NT];
+  float Gi[NT], bi[NT];
+  f32x4 Gj[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int I = TL::I(t), J = TL::J(t);
+    Gi[t] = sG[16 * I + l16];
+    bi[t] = sBeta[16 * I + l16];
+    Gj[t] = *reinterpret_cast<const f32x4*>(sG + 16 * J + 4 * g);
+    accT[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const bf16x8 kj = kfr(J, s), ki = kfr(I, s), qi = qfr(I, s);
+      bf16x8 xi = ki;
+      if constexpr (MIX) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xi[c] = (bf16)((float)ki[c] + lam * (float)qi[c]);
+      }
+      accT[t] = mma32(kj, xi, accT[t]);
+      accA[t] = mma32(kj, qi, accA[t]);
+    }
+  }
+  // decay, beta and masks; i = row (lane), j = 4 columns
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int I = TL::I(t), J = TL::J(t);
+    const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
+    f32x4 xT, xA;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = fexp(Gi[t] - Gj[t][r]);
+      xT[r] = (j0 + r < i) ? bi[t] * accT[t][r] * e : 0.f;  // T: j < i
+      xA[r] = (j0 + r <= i) ? accA[t][r] * e : 0.f;         // A_qk: j <= i
+    }
+    *reinterpret_cast<bf16x4*>(aqk + i * AS + j0) = cvt4(xA);
+    if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
+    else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
+  }
+}
+
 // ---- LDS layout (byte offsets) -------------------------------------------
 template <int DK, int DVS>
 struct PipeLay {
@@ -205,9 +266,20 @@ struct PipeLay {
   static constexpr int oO = oTd + 4 * TDB * 4;  // [DVS][SO] output staging (consumers)
   static constexpr int TOTAL = oO + DVS * SO * 2;
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+  static_assert(NSC == 336 && NSC % 4 == 0, "the two-pass record holds NSC scalars");
   static_assert(oQ % 16 == 0 && oZ % 16 == 0 && oAcm % 16 == 0 && oAqk % 16 == 0 && oSc % 16 == 0 &&
                     oT % 16 == 0 && oTd % 16 == 0 && oO % 16 == 0 && (SK * 2) % 16 == 0,
                 "alignment");
+};
+
+// Workspace record of one chunk for the two-pass form (pipe_split_kernel.hpp
+// writes it, pipe_fwd_kernel<..., PRE = true> reads it): A column-major and
+// A_qk row-major, [64][64] bf16 each, then the NSC chunk scalars.
+struct PipeRec {
+  static constexpr int NSC = 336;  // PipeLay::NSC
+  static constexpr int oAcm = 0, oAqk = CH * CH * 2, oSc = 2 * CH * CH * 2;
+  static constexpr int NPIECE = (oSc + NSC * 4) / 16;  // 16-byte pieces
+  static constexpr int BYTES = (oSc + NSC * 4 + 255) / 256 * 256;
 };
 
 // consumer waves for a value slice of DVS columns: two 32-column waves for
@@ -217,7 +289,10 @@ constexpr int pipe_ncw() {
   return DVS >= 32 ? 2 : 1;
 }
 
-template <int DK, int DVS, int GM>
+// PRE: the second pass of the two-pass form, whose producer waves copy each
+// chunk's record (A, A_qk, scalars; pipe_split_kernel.hpp) from p.ws into LDS
+// instead of forming it.
+template <int DK, int DVS, int GM, bool PRE = false>
 __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(ChunkParams p) {
   constexpr int NCW = pipe_ncw<DVS>();
   constexpr int NB = DVS / (16 * NCW);  // 16-column blocks per consumer wave
@@ -298,6 +373,28 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       const bf16* Aqb = sAqk + buf * CH * SC;
       const float* sc = sSc + buf * NSC;
 
+      // LDS fragments of the later phases: A (transposing reads: A^T rows as
+      // the k slots of W's products), A_qk rows, K^T (state update).  Waves
+      // of one 16-column block have registers to spare and few products to
+      // hide a read behind, so they request each phase's fragments at the
+      // end of the phase before (the buffers of chunk n - 1 are complete
+      // since the last step and are not rewritten in this one).
+      auto afrag = [&](int pp, int h, int m2) __attribute__((always_inline)) {
+        const int col = 32 * pp + 8 * (l16 & 3) + 4 * h;
+        return cat8(lds_tr4(Ab + (32 * m2 + 4 * g + (l16 >> 2)) * SC + col),
+                    lds_tr4(Ab + (32 * m2 + 16 + 4 * g + (l16 >> 2)) * SC + col));
+      };
+      auto aqfrag = [&](int I, int pp) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(Aqb + (16 * I + l16) * SC + 32 * pp + 8 * g);
+      };
+      auto ktfrag = [&](int j, int pp) __attribute__((always_inline)) {
+        const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
+        return cat8(lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col),
+                    lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col));
+      };
+      constexpr bool kAhead = NB == 1;
+      bf16x8 Af[kAhead ? 2 : 1][2][2], Aq[kAhead ? 4 : 1][2], Kt[kAhead ? 2 * NKS : 1][2];
+
       // ---- phase 1: K S and Q S (rows = tokens) ----------------------------
       f32x4 KS[4][NB], QS[4][NB];
       {
@@ -307,7 +404,11 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) Sb[m][nb] = cat8(cvt4(S[2 * m][nb]), cvt4(S[2 * m + 1][nb]));
         // fragments of row block I + 1 are loaded while block I multiplies
-        bf16x8 kf[2][NKS], qf[2][NKS];
+        // fragments of row block I + AHEAD are requested while block I
+        // multiplies; a one-block wave has fewer products to cover a read,
+        // so it looks two blocks ahead
+        constexpr int AHEAD = NB == 1 ? 2 : 1, RING = AHEAD + 1;
+        bf16x8 kf[RING][NKS], qf[RING][NKS];
         auto load_kq = [&](int I, int slot) {
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
@@ -315,20 +416,33 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
             qf[slot][m] = *reinterpret_cast<const bf16x8*>(Qb + (16 * I + l16) * SQ + 32 * m + 8 * g);
           }
         };
-        load_kq(0, 0);
+#pragma unroll
+        for (int I = 0; I < AHEAD; ++I) load_kq(I, I);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          if (I < 3) load_kq(I + 1, (I + 1) & 1);
+          if (I + AHEAD < 4) load_kq(I + AHEAD, (I + AHEAD) % RING);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             KS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
             QS[I][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-              KS[I][nb] = mma32(kf[I & 1][m], Sb[m][nb], KS[I][nb]);
-              QS[I][nb] = mma32(qf[I & 1][m], Sb[m][nb], QS[I][nb]);
+              KS[I][nb] = mma32(kf[I % RING][m], Sb[m][nb], KS[I][nb]);
+              QS[I][nb] = mma32(qf[I % RING][m], Sb[m][nb], QS[I][nb]);
             }
           }
+        }
+        if constexpr (kAhead) {
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int m2 = 0; m2 <= pp; ++m2) Af[pp][h][m2] = afrag(pp, h, m2);
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int pp = 0; pp <= I / 2; ++pp) Aq[I][pp] = aqfrag(I, pp);
         }
       }
       __syncthreads();
@@ -369,10 +483,9 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
             for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m2 = 0; m2 <= pp; ++m2) {
-              const int col = 32 * pp + 8 * (l16 & 3) + 4 * h;
-              const bf16x4 a1 = lds_tr4(Ab + (32 * m2 + 4 * g + (l16 >> 2)) * SC + col);
-              const bf16x4 a2 = lds_tr4(Ab + (32 * m2 + 16 + 4 * g + (l16 >> 2)) * SC + col);
-              const bf16x8 af = cat8(a1, a2);
+              bf16x8 af;
+              if constexpr (kAhead) af = Af[pp][h][m2];
+              else af = afrag(pp, h, m2);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Rb[m2][nb], acc[nb]);
             }
@@ -392,7 +505,9 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
           for (int nb = 0; nb < NB; ++nb) acc[nb] = gm * QS[I][nb];
 #pragma unroll
           for (int pp = 0; pp <= I / 2; ++pp) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(Aqb + (16 * I + l16) * SC + 32 * pp + 8 * g);
+            bf16x8 af;
+            if constexpr (kAhead) af = Aq[I][pp];
+            else af = aqfrag(I, pp);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Wb[pp][nb], acc[nb]);
           }
@@ -400,6 +515,12 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
             *reinterpret_cast<bf16x4*>(sO + (cw0 + 16 * nb + l16) * SO + 16 * I + 4 * g) = cvt4(acc[nb]);
+        }
+        if constexpr (kAhead) {
+#pragma unroll
+          for (int j = 0; j < 2 * NKS; ++j)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) Kt[j][pp] = ktfrag(j, pp);
         }
       }
       __syncthreads();
@@ -417,24 +538,22 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
             Wtb[pp][nb] = cat8(cvt4(t0 * Wt[2 * pp][nb]), cvt4(t1 * Wt[2 * pp + 1][nb]));
         }
         // transposed K fragments of state tile j + 1 are loaded while tile j
-        // multiplies
+        // multiplies (one-block waves have all of them already)
         bf16x8 kt[2][2];
         auto load_kt = [&](int j, int slot) {
-          const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp)
-            kt[slot][pp] = cat8(lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col),
-                                lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col));
+          for (int pp = 0; pp < 2; ++pp) kt[slot][pp] = ktfrag(j, pp);
         };
-        load_kt(0, 0);
+        if constexpr (!kAhead) load_kt(0, 0);
 #pragma unroll
         for (int j = 0; j < 2 * NKS; ++j) {
-          if (j + 1 < 2 * NKS) load_kt(j + 1, (j + 1) & 1);
+          if constexpr (!kAhead)
+            if (j + 1 < 2 * NKS) load_kt(j + 1, (j + 1) & 1);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             f32x4 acc = S[j][nb] * gC;
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) acc = mma32(kt[j & 1][pp], Wtb[pp][nb], acc);
+            for (int pp = 0; pp < 2; ++pp) acc = mma32(kAhead ? Kt[j][pp] : kt[j & 1][pp], Wtb[pp][nb], acc);
             S[j][nb] = acc;
           }
         }
@@ -516,6 +635,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       bf16x8 v[VPT];
       f32x4 w[write_ch ? VPT : 1][2];
       float vb[write_ch ? 1 : VPT];  // beta of the v rows (the beta write gate)
+      u32x4 rc[PRE ? 5 : 1];         // record pieces pt + 256 k of the chunk
     };
     // Loads address the chunk from a uniform base with 32-bit per-lane byte
     // offsets (row of the token within the chunk), so that they take the
@@ -566,7 +686,39 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       }
     };
 
+    // PRE: pieces 0-511 of a record are A, 512-1023 A_qk (rows of 8 pieces),
+    // 1024-1107 the scalars
+    static_assert(PipeRec::NPIECE == 1024 + NSC / 4, "record pieces");
+    auto load_rec = [&](int n, Raw& R) __attribute__((always_inline)) {
+      const u32x4* rp = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.ws) +
+                                                       ((size_t)bh * nchunks + n) * PipeRec::BYTES) + pt;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) R.rc[k] = rp[256 * k];
+      R.rc[4] = rp[1024 + min(pt, NSC / 4 - 1) - pt];
+    };
+    auto write_rec = [&](int buf, const Raw& R) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = pt + 256 * (k & 1), row = q >> 3, col = q & 7;
+        bf16* dst = (k < 2 ? sAcm : sAqk) + buf * CH * SC + row * SC + col * 8;
+        *reinterpret_cast<u32x4*>(dst) = R.rc[k];
+      }
+      if (pt < NSC / 4) *reinterpret_cast<u32x4*>(sSc + buf * NSC + 4 * pt) = R.rc[4];
+    };
+
     // ---- phase 1: chunk scalars (scan wave), k rows ------------------------
+    // (PRE: the scalars come with the record, and the k rows, which nothing
+    // reads before the next step, move to phase 2)
+    auto rows_k = [&](int n, int buf, const Raw& R) {
+      const int t0 = n * CH;
+      bf16* Kb = sK + buf * CH * SK;
+      const bf16x8 zero = {};
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int t = tk0 + u;
+        *reinterpret_cast<bf16x8*>(Kb + t * SK + c0) = (t0 + t < T) ? R.k[u] : zero;
+      }
+    };
     auto prep = [&](int n, int buf, const Raw& R) {
       const int t0 = n * CH;
       if constexpr (pw == kScanWave) {
@@ -581,13 +733,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         sc[L::sTail + lane] = fexp(GC - G);
         if (lane == 0) sc[L::sGC] = fexp(GC);
       }
-      bf16* Kb = sK + buf * CH * SK;
-      const bf16x8 zero = {};
-#pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const int t = tk0 + u;
-        *reinterpret_cast<bf16x8*>(Kb + t * SK + c0) = (t0 + t < T) ? R.k[u] : zero;
-      }
+      rows_k(n, buf, R);
     };
     // ---- phase 3 (waves 2, 3): q rows of chunk n -----------------------------
     auto rows_q = [&](int n, int buf, const Raw& R) {
@@ -631,58 +777,10 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // (the Q-Delta mix is a template argument: a run-time test inside the
     // k-step loop branches around every fragment)
     auto gram = [&](auto tiles, int buf, auto qm) {
-      using TL = decltype(tiles);
-      constexpr bool mix = decltype(qm)::value;
-      constexpr int NT = TL::n;
-      const bf16* Kb = sK + buf * CH * SK;
-      const bf16* Qb = sQ + buf * CH * SQ;
       const float* sc = sSc + buf * NSC;
-      // fragments of 16 rows (identical loads are merged by the compiler)
-      auto kfr = [&](int blk, int s) {
-        return *reinterpret_cast<const bf16x8*>(Kb + (16 * blk + l16) * SK + 32 * s + 8 * g);
-      };
-      auto qfr = [&](int blk, int s) {
-        return *reinterpret_cast<const bf16x8*>(Qb + (16 * blk + l16) * SQ + 32 * s + 8 * g);
-      };
-      f32x4 accT[NT], accA[NT];
-      float Gi[NT], bi[NT];
-      f32x4 Gj[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int I = TL::I(t), J = TL::J(t);
-        Gi[t] = sc[L::sG + 16 * I + l16];
-        bi[t] = sc[L::sBeta + 16 * I + l16];
-        Gj[t] = *reinterpret_cast<const f32x4*>(sc + L::sG + 16 * J + 4 * g);
-        accT[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const bf16x8 kj = kfr(J, s), ki = kfr(I, s), qi = qfr(I, s);
-          bf16x8 xi = ki;
-          if constexpr (mix) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) xi[c] = (bf16)((float)ki[c] + lam * (float)qi[c]);
-          }
-          accT[t] = mma32(kj, xi, accT[t]);
-          accA[t] = mma32(kj, qi, accA[t]);
-        }
-      }
-      // decay, beta and masks; i = row (lane), j = 4 columns
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int I = TL::I(t), J = TL::J(t);
-        const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
-        f32x4 xT, xA;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = fexp(Gi[t] - Gj[t][r]);
-          xT[r] = (j0 + r < i) ? bi[t] * accT[t][r] * e : 0.f;   // T: j < i
-          xA[r] = (j0 + r <= i) ? accA[t][r] * e : 0.f;          // A_qk: j <= i
-        }
-        *reinterpret_cast<bf16x4*>(sAqk + buf * CH * SC + i * SC + j0) = cvt4(xA);
-        if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
-        else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
-      }
+      scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, decltype(qm)::value>(
+          tiles, sK + buf * CH * SK, sQ + buf * CH * SQ, sc + L::sG, sc + L::sBeta, lam, sT, sTd,
+          sAqk + buf * CH * SC, SC, g, l16);
     };
 
     // ---- phase 3 (wave 0): A = (I + T)^{-1} ----------------------------------
@@ -694,7 +792,8 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     Raw R;
     if (nchunks > 0) {
       load_k(0, R);
-      if constexpr (pw == kScanWave) load_gb(0, R);
+      if constexpr (PRE) load_rec(0, R);
+      else if constexpr (pw == kScanWave) load_gb(0, R);
       if constexpr (kRowWave) {
         load_q(0, R);
         rows_q(0, 0, R);
@@ -707,25 +806,34 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     for (int n = 0; n < nchunks; ++n) {
       const int buf = n & 1;
       const int nn = min(n + 1, nchunks - 1);
-      prep(n, buf, R);
+      if constexpr (!PRE) prep(n, buf, R);
       if (n > 0) rows_z(n - 1, buf ^ 1, R);
-      load_k(nn, R);
+      if constexpr (!PRE) load_k(nn, R);
       load_v(n, R);
       __syncthreads();
-      auto tiles = [&](auto qm) {
-        if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf, qm);
-        else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf, qm);
-        else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf, qm);
-        else gram(Tiles<2, 3, 2, 3, 3>{}, buf, qm);
-      };
-      if (qmix) tiles(IC<1>{});
-      else tiles(IC<0>{});
-      // g and beta are loaded here rather than in phase 3, so that they have
-      // arrived when the next step's prefix sum starts
-      if constexpr (pw == kScanWave) load_gb(nn, R);
+      if constexpr (PRE) {
+        rows_k(n, buf, R);
+        load_k(nn, R);
+        write_rec(buf, R);
+        load_rec(nn, R);
+      } else {
+        auto tiles = [&](auto qm) {
+          if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf, qm);
+          else if constexpr (pw == 1) gram(Tiles<3, 2, 0, 2, 1, 2, 2>{}, buf, qm);
+          else if constexpr (pw == 2) gram(Tiles<2, 1, 0, 1, 1>{}, buf, qm);
+          else gram(Tiles<2, 3, 2, 3, 3>{}, buf, qm);
+        };
+        if (qmix) tiles(IC<1>{});
+        else tiles(IC<0>{});
+        // g and beta are loaded here rather than in phase 3, so that they
+        // have arrived when the next step's prefix sum starts
+        if constexpr (pw == kScanWave) load_gb(nn, R);
+      }
       __syncthreads();
-      if constexpr (pw == 0) solve(IC<1>{}, buf);
-      if constexpr (pw == kScanWave) solve(IC<2>{}, buf);
+      if constexpr (!PRE) {
+        if constexpr (pw == 0) solve(IC<1>{}, buf);
+        if constexpr (pw == kScanWave) solve(IC<2>{}, buf);
+      }
       if constexpr (kRowWave) {
         if (n + 1 < nchunks) rows_q(n + 1, buf ^ 1, R);
         load_q(min(n + 2, nchunks - 1), R);

@@ -103,14 +103,16 @@ typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
  * (or zeros).
  *
  * workspace, workspace_bytes: optional device scratch, 256-byte aligned, for
- * the two-pass form of the per-channel-decay forward (bf16 I/O, dk = 128).
- * When a head's value columns are split into slices of 16 or 32 (few heads:
- * B * H * dv / 64 < 256), the single-pass kernel repeats every chunk's state-independent work
- * (decay factors, Gram, inverse) in each slice; with a workspace of at least
- * gdr_workspace_size() bytes that work runs once per chunk, in a separate
- * parallel pass that writes one 64.5 KiB record per (batch, head, chunk) to
- * the workspace, and a second pass applies the records to the state.  NULL
- * (or too small) keeps the single pass.  The workspace must not overlap any
+ * the two-pass form of the bf16, dk = 128 forward under a per-channel decay,
+ * or under no or a scalar decay with the beta erase gate.  When a head's
+ * value columns are split into slices of 16 or 32 (few heads: B * H * dv / 64
+ * < 256), the single-pass kernels repeat every chunk's state-independent work
+ * (decay factors, Gram tiles, inverse) in each slice; with a workspace of at
+ * least gdr_workspace_size() bytes that work runs once per chunk, in a
+ * separate parallel pass that writes one record per (batch, head, chunk) to
+ * the workspace (64.5 KiB under a per-channel decay, 17.5 KiB otherwise), and
+ * a second pass applies the records to the state.  NULL (or too small) keeps
+ * the single pass.  The workspace must not overlap any
  * other argument; its contents are undefined after the call, and concurrent
  * calls need separate workspaces.
  */

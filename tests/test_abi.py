@@ -187,7 +187,8 @@ def test_plan_kernel_choice(lib, decay, erase, block):
 
 # ---- the workspace of the two-pass per-channel form ---------------------------
 
-REC = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4  # bytes of one chunk's record
+REC = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4  # bytes of one chunk's record (per-channel decay)
+REC_SCALAR = 17920                                   # A, A_qk, 336 scalars, rounded to 256 (scalar decay)
 
 
 def _chan_args(**kw):
@@ -203,21 +204,24 @@ def _ws_size(lib, a):
     return st, n.value
 
 
-@pytest.mark.parametrize("B,H,T,dk,decay,io,expect_chunks", [
+@pytest.mark.parametrize("B,H,T,dk,decay,erase,expect_chunks", [
     (1, 32, 200, 128, 2, 1, 4),   # 32 heads -> 16-column slices: two-pass form, 4 chunks each
     (2, 16, 65, 128, 2, 1, 2),    # 32 heads, ragged tail
     (2, 32, 200, 128, 2, 1, 4),   # 64 heads -> 32-column slices
     (8, 16, 200, 128, 2, 1, 0),   # 128 heads -> 64-column slices: single pass
     (1, 32, 200, 64, 2, 1, 0),    # dk 64: single pass
-    (1, 32, 200, 128, 1, 1, 0),   # scalar decay: the scalar-decay kernel
+    (1, 32, 200, 128, 1, 0, 4),   # scalar decay: the scalar-decay form's smaller records
+    (8, 8, 4096, 128, 1, 0, 64),  # the Q-Delta workload's shape
+    (8, 16, 4096, 128, 1, 0, 0),  # the headline workload's shape: single pass
+    (1, 32, 200, 128, 1, 1, 0),   # scalar decay, per-channel erase: the one-pass kernel
     (1, 32, 0, 128, 2, 1, 0),     # nothing to do
 ])
-def test_workspace_size(lib, B, H, T, dk, decay, io, expect_chunks):
-    kw = {} if decay == 2 else dict(erase=0, write=0, beta=_addr(5), b=0, w=0)
-    a = _chan_args(B=B, H=H, T=T, dk=dk, decay=decay, io=io, **kw)
+def test_workspace_size(lib, B, H, T, dk, decay, erase, expect_chunks):
+    kw = {} if decay == 2 else dict(erase=erase, write=0, beta=_addr(5), b=_addr(9) if erase else 0, w=0)
+    a = _chan_args(B=B, H=H, T=T, dk=dk, decay=decay, **kw)
     st, n = _ws_size(lib, a)
     assert st == OK, lib.gdr_last_error()
-    assert n == B * H * expect_chunks * REC
+    assert n == B * H * expect_chunks * (REC if decay == 2 else REC_SCALAR)
 
 
 def test_workspace_switches_the_plan(lib):

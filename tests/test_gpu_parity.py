@@ -71,15 +71,18 @@ CASES = {
 
 
 def _two_pass_form(cfg):
-    """Shapes on which chunk_fwd takes the two-pass per-channel form by
-    default (bf16, dk 128, per-channel decay, few heads)."""
+    """Shapes on which chunk_fwd takes a two-pass form by default: bf16, dk
+    128, few heads (slices of 16 or 32 columns), and either kernel that has
+    one (per-channel decay; or no or a scalar decay with the beta erase gate)."""
     dk, dv = cfg.get("dk", cfg["d"]), cfg.get("dv", cfg["d"])
     decay = cfg.get("decay") or ("channel" if cfg["variant"] in ("kda", "gdn2") else "scalar")
-    return cfg["io"] == "bf16" and dk == 128 and decay == "channel" and cfg["B"] * cfg["H"] * dv // 64 < 256
+    erase = cfg.get("erase") or ("channel" if cfg["variant"] == "gdn2" else "beta")
+    kernel = decay == "channel" or erase == "beta"
+    return cfg["io"] == "bf16" and dk == 128 and kernel and cfg["B"] * cfg["H"] * dv // 64 < 256
 
 
 # every case as chunk_fwd runs it by default, and the two-pass cases once more
-# on the single-pass kernel
+# on the single-pass kernels
 PARITY = [(n, None) for n in sorted(CASES)] + [(n, False) for n in sorted(CASES) if _two_pass_form(CASES[n])]
 
 
@@ -93,7 +96,8 @@ def test_chunk_parity(name, two_pass):
     assert_parity(name, o, S, o_ref, S_ref, TOL[cfg["io"]])
 
 
-@pytest.mark.parametrize("name", ["gdn2_bf16_small", "kda_bf16_small", "gdn2_extreme"])
+@pytest.mark.parametrize("name", ["gdn2_bf16_small", "kda_bf16_small", "gdn2_extreme", "gdn_bf16_small",
+                                  "qdelta_lam1", "deltanet_bf16"])
 def test_two_pass_form(name):
     """The two-pass form is what the plan reports with a workspace, and its
     16- and 32-column slices give bitwise-identical results."""
@@ -293,7 +297,8 @@ def test_pipelined_kernel_matches_the_yu_chunk_form(name):
     cfg = CASES[name]
     inp = make_inputs(cfg)
     assert inp["decay"] != "channel" and inp["erase"] == "beta" and cfg["io"] == "bf16"
-    say(f"[Y/U form] {name}")
-    o, S = run_chunk(inp)
     o_ref, S_ref = _yu_chunk_form(inp)
-    assert_parity(name, o, S, o_ref, S_ref, TOL[cfg["io"]])
+    for two_pass in (False, None):
+        say(f"[Y/U form] {name} two_pass={two_pass}")
+        o, S = run_chunk(inp, two_pass=two_pass)
+        assert_parity(name, o, S, o_ref, S_ref, TOL[cfg["io"]])
