@@ -340,7 +340,7 @@ def main():
     roof = dict(bound="hbm", achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=head["hbm_frac"], traffic=traffic,
                 algorithmic_bytes_per_launch=head["algorithmic_bytes"],
-                kernel_ms_avg=head["kernel_ms_avg"], kernel="pipe_fwd_kernel<128,%d,0>" % head["plan"]["dv_slice"])
+                kernel_ms_avg=head["kernel_ms_avg"], kernel="pipe_fwd_kernel<128,%d,0,false>" % head["plan"]["dv_slice"])
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
