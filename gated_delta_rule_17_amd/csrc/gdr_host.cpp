@@ -228,7 +228,8 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
     if (need > 0 && ws.ptr && ws.bytes >= static_cast<uint64_t>(need)) {
       pi.passes = 2;
       const bool chan = kernel_for(a) == gdr::kChan;
-      pi.lds_bytes = chan ? gdr::chan_split_lds(gdr::gate_mode(a->erase, a->write), a->dk, dvs) : chunk_lds(a, dvs);
+      const int gm = gdr::gate_mode(a->erase, a->write);
+      pi.lds_bytes = chan ? gdr::chan_split_lds(gm, a->dk, dvs) : gdr::pipe_split_lds(gm, a->dk, dvs);
       pi.block = 64 * ((dvs >= 32 ? 2 : 1) + 4);
     } else {
       pi.passes = 1;

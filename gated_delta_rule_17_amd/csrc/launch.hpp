@@ -32,7 +32,8 @@ GDR_DECLARE(chunk_f32_gm3)
 #define GDR_DECLARE(name)                  \
   int name##_lds(int dk, int dvs);        \
   hipError_t name##_launch(const ChunkParams& p, int dk, int dvs, int grid, hipStream_t s); \
-  hipError_t name##_split_launch(const ChunkParams& p, int dk, int dvs, int grid, int prep_grid, hipStream_t s);
+  hipError_t name##_split_launch(const ChunkParams& p, int dk, int dvs, int grid, int prep_grid, hipStream_t s); \
+  int name##_split_lds(int dk, int dvs);
 GDR_DECLARE(pipe_gm0)
 GDR_DECLARE(pipe_gm3)
 #undef GDR_DECLARE
@@ -40,6 +41,11 @@ GDR_DECLARE(pipe_gm3)
 // bytes of one chunk's record in the scalar-decay two-pass form: A, A_qk,
 // 336 chunk scalars (matches PipeRec in pipe_kernel.hpp)
 constexpr int64_t kPipeRecBytes = 17920;
+
+// LDS bytes of the second pass of the scalar-decay two-pass form (-1: none)
+inline int pipe_split_lds(int gm, int dk, int dvs) {
+  return gm == 0 ? pipe_gm0_split_lds(dk, dvs) : pipe_gm3_split_lds(dk, dvs);
+}
 
 inline hipError_t launch_pipe_split(int gm, const ChunkParams& p, int dk, int dvs, int grid, int prep_grid,
                                     hipStream_t s) {

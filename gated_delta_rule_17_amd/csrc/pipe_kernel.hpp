@@ -235,7 +235,7 @@ __device__ __forceinline__ void scalar_gram_tiles(TL, const bf16* Kb, const bf16
 }
 
 // ---- LDS layout (byte offsets) -------------------------------------------
-template <int DK, int DVS>
+template <int DK, int DVS, bool KT = false>
 struct PipeLay {
   // Row strides (bf16 elements), chosen from measured LDS bank conflicts
   // on gfx950 (64 four-byte banks) for each array's own access patterns:
@@ -244,6 +244,9 @@ struct PipeLay {
   //   q: b128 fragment reads only; 288 B (dk 128) and 160 B rows are free
   //   Z: transposing reads of rows 4g + l/4; 160 B rows (64 columns) are free
   //   O staging: b64 writes of 16 rows x 4 groups; 136 B rows are free
+  //   K^T (record mode): b128 reads of channels 8a + b (a, b < 4) of one
+  //      16-token run; 144 B rows with the run index XORed with 4 in
+  //      channels 16..31 of every 32 are free (see kt_off)
   static constexpr int SK = DK + (DK == 128 ? 32 : 24);  // k rows: 320 B (dk 128) / 176 B (dk 64)
   static constexpr int SQ = DK + 16;         // q rows
   static constexpr int SC = CH + 8;          // bf16 row stride of the [64][64] arrays
@@ -257,20 +260,30 @@ struct PipeLay {
   static constexpr int szK = CH * SK * 2, szQ = CH * SQ * 2, szZ = CH * SZ * 2, szA = CH * SC * 2, szS = NSC * 4;
   static constexpr int oK = 0;                 // 2 x [64][SK]  k rows (zero past the end)
   static constexpr int oQ = oK + 2 * szK;      // 2 x [64][SQ]  q rows
-  static constexpr int oZ = oQ + 2 * szQ;      // 2 x [64][SZ]  gated v rows: beta * v or w * v
-  static constexpr int oAcm = oZ + 2 * szZ;    // 2 x [64][SC]  A column-major: Acm[j][i] = A[i][j]
+  static constexpr int oZ = oQ + 2 * szQ;      // [64][SZ]  gated v rows: beta * v or w * v (written
+                                               // and read in the same step)
+  static constexpr int oAcm = oZ + szZ;        // 2 x [64][SC]  A column-major: Acm[j][i] = A[i][j]
   static constexpr int oAqk = oAcm + 2 * szA;  // 2 x [64][SC]  A_qk row-major
   static constexpr int oSc = oAqk + 2 * szA;   // 2 x scalars
   static constexpr int oT = oSc + 2 * szS;     // [64][SC] T row-major, blocks below the diagonal (producers)
   static constexpr int oTd = oT + szA;         // 4 x [16][TDS] fp32: Td[b][i][j] = T[16b+i][16b+j] (producers)
   static constexpr int oO = oTd + 4 * TDB * 4;  // [DVS][SO] output staging (consumers)
-  static constexpr int TOTAL = oO + DVS * SO * 2;
+  static constexpr int oKT = oO + DVS * SO * 2;  // record mode: [DK][SKT] K^T (channel, token)
+  static constexpr int SKT = CH + 8;
+  static constexpr int TOTAL = oKT + (KT ? DK * SKT * 2 : 0);
   static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
   static_assert(NSC == 336 && NSC % 4 == 0, "the two-pass record holds NSC scalars");
   static_assert(oQ % 16 == 0 && oZ % 16 == 0 && oAcm % 16 == 0 && oAqk % 16 == 0 && oSc % 16 == 0 &&
-                    oT % 16 == 0 && oTd % 16 == 0 && oO % 16 == 0 && (SK * 2) % 16 == 0,
+                    oT % 16 == 0 && oTd % 16 == 0 && oO % 16 == 0 && oKT % 16 == 0 && (SK * 2) % 16 == 0,
                 "alignment");
 };
+
+// Byte offset in the K^T array (rows of SKT = 72 bf16) of the 16-byte run r
+// (tokens 8r .. 8r + 7) of channel c.  A consumer fragment read takes
+// channels 32m + 8a + 4h + b (a, b < 4) of one run; with 144-byte rows
+// those pairs a, a + 2 hit the same banks, so the run index is XORed with 4
+// in channels 16..31 of every 32.
+__device__ __forceinline__ int kt_off(int c, int r) { return c * ((CH + 8) * 2) + 16 * (r ^ (((c >> 4) & 1) << 2)); }
 
 // Workspace record of one chunk for the two-pass form (pipe_split_kernel.hpp
 // writes it, pipe_fwd_kernel<..., PRE = true> reads it): A column-major and
@@ -296,7 +309,7 @@ template <int DK, int DVS, int GM, bool PRE = false>
 __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(ChunkParams p) {
   constexpr int NCW = pipe_ncw<DVS>();
   constexpr int NB = DVS / (16 * NCW);  // 16-column blocks per consumer wave
-  using L = PipeLay<DK, DVS>;
+  using L = PipeLay<DK, DVS, PRE>;
   constexpr int SK = L::SK, SQ = L::SQ, SC = L::SC, SZ = L::SZ, SO = L::SO, TDS = L::TDS, TDB = L::TDB,
                 NSC = L::NSC;
   constexpr int NKS = DK / 32;  // 32-channel k-steps
@@ -313,6 +326,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
   bf16* sT = reinterpret_cast<bf16*>(smem + L::oT);
   float* sTd = reinterpret_cast<float*>(smem + L::oTd);
   bf16* sO = reinterpret_cast<bf16*>(smem + L::oO);
+  char* sKT = smem + L::oKT;  // record mode only
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -368,7 +382,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       const int buf = n & 1;
       const bf16* Kb = sK + buf * CH * SK;
       const bf16* Qb = sQ + buf * CH * SQ;
-      const bf16* Zb = sZ + buf * CH * SZ;
+      const bf16* Zb = sZ;
       const bf16* Ab = sAcm + buf * CH * SC;
       const bf16* Aqb = sAqk + buf * CH * SC;
       const float* sc = sSc + buf * NSC;
@@ -388,9 +402,15 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         return *reinterpret_cast<const bf16x8*>(Aqb + (16 * I + l16) * SC + 32 * pp + 8 * g);
       };
       auto ktfrag = [&](int j, int pp) __attribute__((always_inline)) {
-        const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
-        return cat8(lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col),
-                    lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col));
+        if constexpr (PRE) {
+          // channel 32 (j / 2) + 8 (l16 / 4) + 4 (j % 2) + l16 % 4, tokens 32 pp + 8 g ..
+          const int c = 32 * (j >> 1) + 8 * (l16 >> 2) + 4 * (j & 1) + (l16 & 3);
+          return *reinterpret_cast<const bf16x8*>(sKT + kt_off(c, 4 * pp + g));
+        } else {
+          const int col = 32 * (j >> 1) + 8 * (l16 & 3) + 4 * (j & 1);
+          return cat8(lds_tr4(Kb + (32 * pp + 8 * g + (l16 >> 2)) * SK + col),
+                      lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col));
+        }
       };
       constexpr bool kAhead = NB == 1;
       bf16x8 Af[kAhead ? 2 : 1][2][2], Aq[kAhead ? 4 : 1][2], Kt[kAhead ? 2 * NKS : 1][2];
@@ -606,6 +626,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // share their SIMDs with them)
     constexpr int kScanWave = 1;
     constexpr bool kRowWave = pw >= 2;  // writes the q rows
+    constexpr bool kRecWave = PRE && pw < 2;  // record mode: copies the record
     const int pt = tid - 64 * NCW;
     constexpr int CG = DK / 8, TG = 256 / CG, TPT = CH / TG;      // k: 8 channels x TPT tokens
     constexpr int QTG = 128 / CG, QPT = CH / QTG;                 // q: over waves 2, 3
@@ -635,7 +656,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       bf16x8 v[VPT];
       f32x4 w[write_ch ? VPT : 1][2];
       float vb[write_ch ? 1 : VPT];  // beta of the v rows (the beta write gate)
-      u32x4 rc[PRE ? 5 : 1];         // record pieces pt + 256 k of the chunk
+      u32x4 rc[kRecWave ? 9 : 1];    // record mode: pieces pt + 128 k of the chunk
     };
     // Loads address the chunk from a uniform base with 32-bit per-lane byte
     // offsets (row of the token within the chunk), so that they take the
@@ -687,28 +708,48 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     };
 
     // PRE: pieces 0-511 of a record are A, 512-1023 A_qk (rows of 8 pieces),
-    // 1024-1107 the scalars
-    static_assert(PipeRec::NPIECE == 1024 + NSC / 4, "record pieces");
+    // 1024-1107 the scalars; waves 0 and 1 copy them (lane pt: pieces
+    // pt + 128 k), waves 2 and 3 the q rows
+    static_assert(PipeRec::NPIECE == 1024 + NSC / 4 && NSC / 4 <= 128, "record pieces");
     auto load_rec = [&](int n, Raw& R) __attribute__((always_inline)) {
-      const u32x4* rp = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.ws) +
-                                                       ((size_t)bh * nchunks + n) * PipeRec::BYTES) + pt;
+      if constexpr (kRecWave) {
+        const u32x4* rp = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.ws) +
+                                                         ((size_t)bh * nchunks + n) * PipeRec::BYTES) + pt;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) R.rc[k] = rp[256 * k];
-      R.rc[4] = rp[1024 + min(pt, NSC / 4 - 1) - pt];
+        for (int k = 0; k < 8; ++k) R.rc[k] = rp[128 * k];
+        R.rc[8] = rp[1024 + min(pt, NSC / 4 - 1) - pt];
+      }
     };
     auto write_rec = [&](int buf, const Raw& R) __attribute__((always_inline)) {
+      if constexpr (kRecWave) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int q = pt + 128 * (k & 3), row = q >> 3, col = q & 7;
+          bf16* dst = (k < 4 ? sAcm : sAqk) + buf * CH * SC + row * SC + col * 8;
+          *reinterpret_cast<u32x4*>(dst) = R.rc[k];
+        }
+        if (pt < NSC / 4) *reinterpret_cast<u32x4*>(sSc + buf * NSC + 4 * pt) = R.rc[8];
+      }
+    };
+    // PRE, phase 3: K^T of chunk n (channel-major runs of 8 tokens) from its
+    // k rows, for the consumers' b128 fragment reads.  Lane pt, k: 16-lane
+    // group 4 (pt / 64) + g + 16 k takes channels 16 (group / 8) + l16, run
+    // group % 8 (two transposing reads of 4 tokens x 16 channels).
+    auto rows_kt = [&](int buf) __attribute__((always_inline)) {
+      const bf16* Kb = sK + buf * CH * SK;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int q = pt + 256 * (k & 1), row = q >> 3, col = q & 7;
-        bf16* dst = (k < 2 ? sAcm : sAqk) + buf * CH * SC + row * SC + col * 8;
-        *reinterpret_cast<u32x4*>(dst) = R.rc[k];
+        const int grp = 4 * pw + g + 16 * k, r = grp & 7, cb = 16 * (grp >> 3);
+        const bf16* src = Kb + (8 * r + (l16 >> 2)) * SK + cb + 4 * (l16 & 3);
+        const bf16x8 v = cat8(lds_tr4(src), lds_tr4(src + 4 * SK));
+        *reinterpret_cast<bf16x8*>(sKT + kt_off(cb + l16, r)) = v;
       }
-      if (pt < NSC / 4) *reinterpret_cast<u32x4*>(sSc + buf * NSC + 4 * pt) = R.rc[4];
     };
 
     // ---- phase 1: chunk scalars (scan wave), k rows ------------------------
-    // (PRE: the scalars come with the record, and the k rows, which nothing
-    // reads before the next step, move to phase 2)
+    // (PRE: the scalars come with the record in phase 2, which also takes the
+    // q rows of the next chunk: with no Gram tiles or inverse to form, the
+    // producers' work of a step fits in the consumers' first two phases)
     auto rows_k = [&](int n, int buf, const Raw& R) {
       const int t0 = n * CH;
       bf16* Kb = sK + buf * CH * SK;
@@ -750,7 +791,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     auto rows_z = [&](int n, int buf, const Raw& R) {
       if (!vact) return;
       const int t0 = n * CH;
-      bf16* Zb = sZ + buf * CH * SZ;
+      bf16* Zb = sZ;
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
         const int t = vtq0 + u;
@@ -806,16 +847,20 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     for (int n = 0; n < nchunks; ++n) {
       const int buf = n & 1;
       const int nn = min(n + 1, nchunks - 1);
-      if constexpr (!PRE) prep(n, buf, R);
+      if constexpr (PRE) rows_k(n, buf, R);
+      else prep(n, buf, R);
       if (n > 0) rows_z(n - 1, buf ^ 1, R);
-      if constexpr (!PRE) load_k(nn, R);
+      load_k(nn, R);
       load_v(n, R);
       __syncthreads();
       if constexpr (PRE) {
-        rows_k(n, buf, R);
-        load_k(nn, R);
+        // (the consumers have read the q rows of chunk n - 1 in phase 1)
         write_rec(buf, R);
         load_rec(nn, R);
+        if constexpr (kRowWave) {
+          if (n + 1 < nchunks) rows_q(n + 1, buf ^ 1, R);
+          load_q(min(n + 2, nchunks - 1), R);
+        }
       } else {
         auto tiles = [&](auto qm) {
           if constexpr (pw == 0) gram(Tiles<3, 3, 0, 3, 1, 0, 0>{}, buf, qm);
@@ -830,13 +875,16 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         if constexpr (pw == kScanWave) load_gb(nn, R);
       }
       __syncthreads();
-      if constexpr (!PRE) {
+      if constexpr (PRE) {
+        // (the consumers have read K^T of chunk n - 1 in phase 2)
+        rows_kt(buf);
+      } else {
         if constexpr (pw == 0) solve(IC<1>{}, buf);
         if constexpr (pw == kScanWave) solve(IC<2>{}, buf);
-      }
-      if constexpr (kRowWave) {
-        if (n + 1 < nchunks) rows_q(n + 1, buf ^ 1, R);
-        load_q(min(n + 2, nchunks - 1), R);
+        if constexpr (kRowWave) {
+          if (n + 1 < nchunks) rows_q(n + 1, buf ^ 1, R);
+          load_q(min(n + 2, nchunks - 1), R);
+        }
       }
       if constexpr (write_ch) load_w(n, R);
       __syncthreads();
