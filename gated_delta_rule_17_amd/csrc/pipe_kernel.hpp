@@ -412,8 +412,8 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
                       lds_tr4(Kb + (32 * pp + 8 * g + 4 + (l16 >> 2)) * SK + col));
         }
       };
-      constexpr bool kAhead = NB == 1;
-      bf16x8 Af[kAhead ? 2 : 1][2][2], Aq[kAhead ? 4 : 1][2], Kt[kAhead ? 2 * NKS : 1][2];
+      constexpr bool kAhead = NB == 1, kAheadA = true;
+      bf16x8 Af[kAheadA ? 2 : 1][2][2], Aq[kAheadA ? 4 : 1][2], Kt[kAhead ? 2 * NKS : 1][2];
 
       // ---- phase 1: K S and Q S (rows = tokens) ----------------------------
       f32x4 KS[4][NB], QS[4][NB];
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
             }
           }
         }
-        if constexpr (kAhead) {
+        if constexpr (kAheadA) {
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
 #pragma unroll
             for (int m2 = 0; m2 <= pp; ++m2) {
               bf16x8 af;
-              if constexpr (kAhead) af = Af[pp][h][m2];
+              if constexpr (kAheadA) af = Af[pp][h][m2];
               else af = afrag(pp, h, m2);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Rb[m2][nb], acc[nb]);
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
 #pragma unroll
           for (int pp = 0; pp <= I / 2; ++pp) {
             bf16x8 af;
-            if constexpr (kAhead) af = Aq[I][pp];
+            if constexpr (kAheadA) af = Aq[I][pp];
             else af = aqfrag(I, pp);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = mma32(af, Wb[pp][nb], acc[nb]);
@@ -850,8 +850,12 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       if constexpr (PRE) rows_k(n, buf, R);
       else prep(n, buf, R);
       if (n > 0) rows_z(n - 1, buf ^ 1, R);
-      load_k(nn, R);
-      load_v(n, R);
+      // (waves 2 and 3 share their SIMDs with the consumers and bound phase
+      // 1: their loads go behind their Gram tiles in phase 2)
+      if constexpr (PRE || !kRowWave) {
+        load_k(nn, R);
+        load_v(n, R);
+      }
       __syncthreads();
       if constexpr (PRE) {
         // (the consumers have read the q rows of chunk n - 1 in phase 1)
@@ -870,6 +874,10 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
         };
         if (qmix) tiles(IC<1>{});
         else tiles(IC<0>{});
+        if constexpr (kRowWave) {
+          load_k(nn, R);
+          load_v(n, R);
+        }
         // g and beta are loaded here rather than in phase 3, so that they
         // have arrived when the next step's prefix sum starts
         if constexpr (pw == kScanWave) load_gb(nn, R);
