@@ -541,19 +541,21 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
     // Regions start at multiples of 256 pieces, so piece k of every lane lies
     // in one region: E_bar k = 0-3, Q_gamma 4-7, K_tail 8-11, A 12-13,
     // A_qk 14-15, gamma_C 16 (lanes 0-31).  Z = gate * v of the slice is
-    // formed from its own loads.
+    // formed from its own loads, ZC columns of one token per lane, so that
+    // every loader lane takes an equal share of it.
     const int lt = tid - 64 * NCW;
-    constexpr int VG = DVS / 8;                 // 16-byte groups of a v row
-    const int tz = lt / VG, vv0 = (lt % VG) * 8;
-    const bool vact = lt < 64 * VG;             // wave-uniform
+    constexpr int ZC = DVS / 4;                 // Z columns per lane (64 DVS values over 256 lanes)
+    constexpr int VG = DVS / ZC;                // lanes per v row
+    const int tz = lt / VG, vv0 = (lt % VG) * ZC;
+    typedef bf16 bfz __attribute__((ext_vector_type(ZC)));
     const bf16* vg = reinterpret_cast<const bf16*>(p.v) + seq0 * DV + vbase;
     const float* beta_seq = p.beta ? p.beta + seq0 : nullptr;
     const float* w_seq = write_ch ? p.w + seq0 * DV + vbase : nullptr;
     // (clang vector elements: arrays of HIP's uint4 struct stay in scratch
     // memory instead of registers)
     u32x4 rE[4], rQ[4], rK[4], rAc[2], rAq[2], rG;
-    bf16x8 rv = {};
-    f32x4 rw0 = {}, rw1 = {};
+    bfz rv = {};
+    f32x4 rw[write_ch ? ZC / 4 : 1] = {};
     float rvb = 0.f;
     // Loads are unconditional, at chunk indices clamped to the last one.
 #define GDR_SPLIT_LOAD(nl)                                                                  \
@@ -570,13 +572,13 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
         rAq[k] = rec[3584 + 256 * k];                                                       \
       }                                                                                     \
       rG = rec[4096 + min(lt, 31) - lt];                                                    \
-      if (vact) {                                                                           \
+      {                                                                                     \
         const unsigned r = (unsigned)(min(n_ * CH + tz, T - 1) - n_ * CH) * H;              \
-        rv = *reinterpret_cast<const bf16x8*>(vg + (size_t)n_ * CH * H * DV + r * DV + vv0); \
+        rv = *reinterpret_cast<const bfz*>(vg + (size_t)n_ * CH * H * DV + r * DV + vv0);   \
         if constexpr (write_ch) {                                                           \
           const float* wc = w_seq + (size_t)n_ * CH * H * DV + r * DV + vv0;               \
-          rw0 = *reinterpret_cast<const f32x4*>(wc);                                        \
-          rw1 = *reinterpret_cast<const f32x4*>(wc + 4);                                    \
+          _Pragma("unroll") for (int i = 0; i < ZC / 4; ++i)                               \
+            rw[i] = *reinterpret_cast<const f32x4*>(wc + 4 * i);                            \
         } else {                                                                            \
           rvb = beta_seq[(size_t)n_ * CH * H + r];                                          \
         }                                                                                   \
@@ -603,17 +605,19 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
           *reinterpret_cast<u32x4*>(smem + L::oAqk + buf * L::szA + row * SC * 2 + col * 16) = rAq[k];
         }
         if (lt < 32) *reinterpret_cast<u32x4*>(smem + L::oGc + buf * DK * 4 + lt * 16) = rG;
-        if (vact) {
+        {
           const bool ok = nw * CH + tz < T;
-          float z[8];
+          float z[ZC];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < ZC; ++e) {
             float gate;
-            if constexpr (write_ch) gate = e < 4 ? rw0[e] : rw1[e - 4];
+            if constexpr (write_ch) gate = rw[e / 4][e % 4];
             else gate = rvb;
             z[e] = ok ? gate * (float)rv[e] : 0.f;
           }
-          st8(reinterpret_cast<bf16*>(smem + L::oZ + buf * L::szZ) + tz * SZ + vv0, z);
+          bf16* zd = reinterpret_cast<bf16*>(smem + L::oZ + buf * L::szZ) + tz * SZ + vv0;
+          if constexpr (ZC == 8) st8(zd, z);
+          else *reinterpret_cast<bf16x4*>(zd) = cvt4(f32x4{z[0], z[1], z[2], z[3]});
         }
         GDR_SPLIT_LOAD(min(n + 1, nchunks - 1))
       }
