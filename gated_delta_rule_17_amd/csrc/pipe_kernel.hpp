@@ -614,7 +614,9 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
     // waves 0 and 1 then compute A = (I + T)^-1 (phase 3), splitting its last
     // level, while waves 2 and 3 write the q rows of chunk n + 1 (phase 3: the
     // consumers read q in phase 1 only, so the buffer of the chunk that they
-    // apply is free by then) and load those of chunk n + 2.
+    // apply is free by then) and load those of chunk n + 2.  Waves 2 and 3
+    // share their SIMDs with the consumers and bound phase 1, so they issue
+    // their k and v loads behind their Gram tiles instead.
     // One loop per producer wave, with the wave's role fixed at compile time:
     // a single loop with run-time role branches makes the register allocator
     // move prefetched registers at the branch joins, which waits for loads
