@@ -22,13 +22,19 @@
 
 namespace gdr {
 
+// Three workgroups share a CU: the k rows take the q rows' stride (this
+// kernel reads both only as b128 fragments, which that stride serves without
+// bank conflicts) and A takes the place of the k rows once the Gram tiles
+// have read them.
 template <int DK>
 struct PrepPipeLay {
-  using P = PipeLay<DK, 64>;  // row strides and scalar layout of the pipelined kernel
-  static constexpr int SK = P::SK, SQ = P::SQ, SC = P::SC, TDS = P::TDS, TDB = P::TDB, NSC = P::NSC;
+  using P = PipeLay<DK, 64>;  // q stride, [64][64] stride and scalar layout of the pipelined kernel
+  static constexpr int SK = P::SQ, SQ = P::SQ, SC = P::SC, TDS = P::TDS, TDB = P::TDB, NSC = P::NSC;
   static constexpr int oK = 0, oQ = CH * SK * 2, oSc = oQ + CH * SQ * 2, oT = oSc + NSC * 4;
-  static constexpr int oTd = oT + CH * SC * 2, oA = oTd + 4 * TDB * 4, TOTAL = oA + CH * SC * 2;
-  static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
+  static constexpr int oTd = oT + CH * SC * 2, TOTAL = oTd + 4 * TDB * 4;
+  static constexpr int oA = oK;  // after the Gram tiles
+  static_assert(CH * SC * 2 <= CH * SK * 2, "A fits in the k rows");
+  static_assert(3 * TOTAL <= 160 * 1024, "three workgroups per CU");
   static_assert(oQ % 16 == 0 && oSc % 16 == 0 && oT % 16 == 0 && oTd % 16 == 0 && oA % 16 == 0, "alignment");
 };
 
@@ -62,8 +68,6 @@ __global__ __launch_bounds__(256) void pipe_prep_kernel(ChunkParams p, char* __r
   char* rec = ws + (size_t)job * R::BYTES;
   const int t0 = n * CH;
 
-  // A starts at zero above the diagonal blocks
-  for (int e = tid; e < CH * SC * 2 / 16; e += 256) reinterpret_cast<uint4*>(sA)[e] = uint4{0u, 0u, 0u, 0u};
   // k and q rows of the chunk (zero past the end)
   {
     const bf16* kg = reinterpret_cast<const bf16*>(p.k) + seq0 * DK;
@@ -128,6 +132,10 @@ __global__ __launch_bounds__(256) void pipe_prep_kernel(ChunkParams p, char* __r
       if (u < 6) *reinterpret_cast<bf16x4*>(aqk_out + (16 * up[u][0] + l16) * CH + 16 * up[u][1] + 4 * g) = zero;
     }
   }
+  __syncthreads();
+  // A (in the k rows, read for the last time above) starts at zero, so that
+  // its blocks above the diagonal stay zero
+  for (int e = tid; e < CH * SC * 2 / 16; e += 256) reinterpret_cast<uint4*>(sA)[e] = uint4{0u, 0u, 0u, 0u};
   __syncthreads();
   // A = (I + T)^{-1}: waves 0 and 1 split its last level
   if (w == 0) solve_inverse<SC, TDS, TDB, 1>(sTd, sT, sA, g, l16);
