@@ -1,15 +1,18 @@
 """Benchmark of the chunkwise gated delta rule forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|headline]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+                    [--workloads all|headline] [--no-cpu-baseline]
 
 One step = one gdr_chunk_fwd call over the headline workload (Gated
 DeltaNet, bf16 q/k/v/o, fp32 gates and state, B=8 H=16 T=4096 d=128, C=64):
 every per-chunk operation of the chunk algorithm runs inside that one kernel.
 Inputs are generated on the CPU (seeded) and copied to HBM before timing.
-K steps are timed between torch.cuda.synchronize() calls; each launch is
-also bracketed by HIP events on the launch stream to get the kernel's own
-average duration, from which the roofline fraction is computed against the
+Each workload's step first runs back to back for --settle-ms milliseconds
+(untimed; from idle the shader clock takes tens of milliseconds of load to
+reach its sustained value), then W untimed warm-up steps; then K steps are
+timed between torch.cuda.synchronize() calls, and a pair of HIP events on
+the launch stream around them gives the kernel's own average duration, from
+which the roofline fraction is computed against the
 algorithmic bytes (every input read once, every output written once).
 
 The other workloads (KDA, Q-Delta, Gated DeltaNet-2, and the decode step)
@@ -94,8 +97,14 @@ def traffic_from_profile(kernel_tag, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, stream, steps, warmup):
+def time_launches(fn, stream, steps, warmup, settle_ms=0.0):
     """Wall time per step and the kernel's average duration per launch.
+
+    Untimed first: the step back to back for ``settle_ms`` milliseconds,
+    then ``warmup`` steps.  From idle the GPU raises its shader clock over
+    some tens of milliseconds of load, so steps timed right after a few
+    warm-up launches measure the ramp rather than the clock that sustained
+    load runs at.
 
     One pair of HIP events on the launch stream brackets the whole timed
     region: the launches queue back to back, so the average is the kernel's
@@ -103,6 +112,11 @@ def time_launches(fn, stream, steps, warmup):
     pair around every launch would add the event packets' own gaps to each.)
     """
     import torch
+    t_end = time.perf_counter() + settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -117,7 +131,7 @@ def time_launches(fn, stream, steps, warmup):
     return wall / steps * 1e3, e0.elapsed_time(e1) / steps
 
 
-def bench_workload(name, steps, warmup, op="chunk"):
+def bench_workload(name, steps, warmup, op="chunk", settle_ms=0.0):
     import ctypes
 
     import torch
@@ -158,7 +172,7 @@ def bench_workload(name, steps, warmup, op="chunk"):
         _lib.call(entry, copies[turn[0] & 1][3], sp)
         turn[0] += 1
 
-    ms_step, ms_kern = time_launches(fn, stream, steps, warmup)
+    ms_step, ms_kern = time_launches(fn, stream, steps, warmup, settle_ms)
     byts = algorithmic_bytes(cfg, inp, op)
     tokens = B * T
     res = dict(workload=name, variant=cfg["variant"], B=B, T=T, H=H, dk=dk, dv=dv, io=cfg["io"],
@@ -285,8 +299,11 @@ def counters_run(name):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back steps before the warm-up steps of each workload, in "
+                         "milliseconds, so that the timed steps run at the sustained clock")
     ap.add_argument("--workloads", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -312,7 +329,7 @@ def main():
     if args.counters:
         counters_run(HEADLINE)
         return
-    head, head_inp = bench_workload(HEADLINE, args.steps, args.warmup)
+    head, head_inp = bench_workload(HEADLINE, args.steps, args.warmup, settle_ms=args.settle_ms)
     print(f"# headline {HEADLINE}: {head['kernel_ms_avg'] * 1e3:.1f} us/launch, "
           f"{head['hbm_gbs']:.0f} GB/s ({head['hbm_frac'] * 100:.1f}% HBM), "
           f"{head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -323,7 +340,7 @@ def main():
             if name == HEADLINE:
                 continue
             op = "step" if name == DECODE else "chunk"
-            r, _ = bench_workload(name, max(5, args.steps // 2), args.warmup, op=op)
+            r, _ = bench_workload(name, max(5, args.steps // 2), args.warmup, op=op, settle_ms=args.settle_ms)
             keep = ("tokens_per_s", "kernel_ms_avg", "hbm_gbs", "hbm_frac", "tflops", "mfma_frac", "plan",
                     "algorithmic_bytes")
             workloads[name] = {k: r[k] for k in keep if k in r}
@@ -348,6 +365,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
