@@ -15,12 +15,15 @@
 //   pass 2 (chan_rec_kernel, one workgroup per (head, value slice)): the
 //     state recurrence, with loader waves copying record n + 1 into LDS
 //     while the consumer waves apply record n; one barrier per chunk.
-// Workspace record of a chunk (bytes; dense rows, n = chunk within its
-// sequence; records ordered by (batch, head, chunk)):
+// Workspace record of a chunk (bytes; n = chunk within its sequence; records
+// ordered by (batch, head, chunk)):
 //   E_bar [64][dk] bf16 | Q_gamma [64][dk] bf16 | K_tail [64][dk] bf16 |
-//   A column-major [64][64] bf16 (Acm[j][i] = A[i][j]) |
-//   A_qk row-major [64][64] bf16 | gamma_C [dk] fp32
-// with the 16 x 16 blocks above the diagonal of A and A_qk zero.
+//   A column-major (Acm[j][i] = A[i][j]), its ten non-zero 16 x 16 blocks |
+//   A_qk row-major, its ten non-zero blocks | gamma_C [dk] fp32
+// The six blocks above the diagonal of A and A_qk are zero and not stored:
+// A_qk keeps, for row block I, the blocks J <= I of its 16 rows (rows of
+// 32 (I + 1) bytes, row blocks in order); Acm keeps, for row block J, the
+// blocks I >= J (rows of 32 (4 - J) bytes).  Each takes 320 pieces of 16 bytes.
 #pragma once
 
 #include "chan_kernel.hpp"
@@ -29,10 +32,35 @@ namespace gdr {
 
 template <int DK>
 struct SplitRec {
+  static constexpr int PIECES_A = 320;  // 16-byte pieces of the ten stored blocks
   static constexpr int oEb = 0, oQg = CH * DK * 2, oKt = 2 * CH * DK * 2;
-  static constexpr int oAcm = 3 * CH * DK * 2, oAqk = oAcm + CH * CH * 2, oGc = oAqk + CH * CH * 2;
+  static constexpr int oAcm = 3 * CH * DK * 2, oAqk = oAcm + PIECES_A * 16, oGc = oAqk + PIECES_A * 16;
   static constexpr int BYTES = (oGc + DK * 4 + 255) / 256 * 256;
 };
+
+// Piece q (< 320) of a stored triangle -> (row, 16-byte column) of the dense
+// [64][64] bf16 matrix.  Lower (A_qk): row block I holds 2 (I + 1) pieces per
+// row; upper (Acm): row block J holds 2 (4 - J) pieces per row, starting at
+// column piece 2 J.
+struct TriPiece {
+  int row, col;
+};
+__device__ __forceinline__ TriPiece tri_lower_piece(int q) {
+  const int I = q < 32 ? 0 : q < 96 ? 1 : q < 192 ? 2 : 3;
+  const int w = 2 * (I + 1), l = q - 16 * I * (I + 1);
+  return {16 * I + l / w, l % w};
+}
+__device__ __forceinline__ TriPiece tri_upper_piece(int q) {
+  const int J = q < 128 ? 0 : q < 224 ? 1 : q < 288 ? 2 : 3;
+  const int w = 2 * (4 - J), l = q - (J == 0 ? 0 : J == 1 ? 128 : J == 2 ? 224 : 288);
+  return {16 * J + l / w, 2 * J + l % w};
+}
+// Byte offset, within a stored lower triangle, of row r of the dense matrix at
+// bf16 column c (c in a block J <= r / 16).
+__device__ __forceinline__ int tri_lower_byte(int r, int c) {
+  const int I = r >> 4;
+  return 512 * (I * (I + 1) / 2) + 32 * (I + 1) * (r & 15) + 2 * c;
+}
 
 // ---- pass 1 ------------------------------------------------------------------
 template <int DK>
@@ -257,21 +285,14 @@ __global__ __launch_bounds__(256) void chan_prep_kernel(ChunkParams p, char* __r
       gram_mask_tiles<SC, TDS, TDB>(tl, accT, accA, aqk, sT, sTd, g, l16);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        *reinterpret_cast<bf16x4*>(aqk_out + (16 * TL::I(t) + l16) * CH + 16 * TL::J(t) + 4 * g) = cvt4(aqk[t]);
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(aqk_out) +
+                                   tri_lower_byte(16 * TL::I(t) + l16, 16 * TL::J(t) + 4 * g)) = cvt4(aqk[t]);
     };
     switch (w) {
       case 0: tiles(TileList<0, 0, 3, 0, 3, 1>{}); break;
       case 1: tiles(TileList<1, 1, 1, 0>{}); break;
       case 2: tiles(TileList<2, 2, 2, 0, 2, 1>{}); break;
       default: tiles(TileList<3, 3, 3, 2>{}); break;
-    }
-    // the six blocks above the diagonal of A_qk are zero
-    constexpr int up[6][2] = {{0, 1}, {1, 3}, {0, 2}, {2, 3}, {0, 3}, {1, 2}};
-    const bf16x4 zero = {};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int u = 2 * w + k;
-      if (u < 6) *reinterpret_cast<bf16x4*>(aqk_out + (16 * up[u][0] + l16) * CH + 16 * up[u][1] + 4 * g) = zero;
     }
   }
   __syncthreads();
@@ -283,9 +304,10 @@ __global__ __launch_bounds__(256) void chan_prep_kernel(ChunkParams p, char* __r
   if (w == 0) solve_inverse<SC, TDS, TDB, 1>(sTd, sT, sA, g, l16);
   else if (w == 1) solve_inverse<SC, TDS, TDB, 2>(sTd, sT, sA, g, l16);
   __syncthreads();
-  for (int e = tid; e < CH * CH / 8; e += 256) {
-    const int r = e >> 3, c = e & 7;
-    reinterpret_cast<uint4*>(rec + R::oAcm)[e] = *reinterpret_cast<const uint4*>(sA + r * SC + 8 * c);
+  // the ten stored blocks of A (column-major)
+  for (int q = tid; q < R::PIECES_A; q += 256) {
+    const TriPiece pc = tri_upper_piece(q);
+    reinterpret_cast<uint4*>(rec + R::oAcm)[q] = *reinterpret_cast<const uint4*>(sA + pc.row * SC + 8 * pc.col);
   }
 }
 
@@ -336,6 +358,12 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
   const int nchunks = (T + CH - 1) / CH;
   const size_t seq0 = (size_t)bb * T * H + hh;
   const char* recs = ws + (size_t)bh * nchunks * R::BYTES;
+
+  // the blocks above the diagonal of A and A_qk (not in the record) stay zero
+  static_assert(L::oAqk == L::oAcm + 2 * L::szA, "A and A_qk buffers adjacent");
+  for (int e = tid; e < 4 * L::szA / 16; e += 64 * (NCW + 4))
+    reinterpret_cast<uint4*>(smem + L::oAcm)[e] = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
 
   if (wave < NCW) {
     // =================== consumers (as in chan_kernel.hpp) ====================
@@ -537,13 +565,30 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
     }
   } else {
     // =================== loaders ===============================================
-    // Record pieces of 16 bytes: piece lt + 256 k of the record goes to LDS.
-    // Regions start at multiples of 256 pieces, so piece k of every lane lies
-    // in one region: E_bar k = 0-3, Q_gamma 4-7, K_tail 8-11, A 12-13,
-    // A_qk 14-15, gamma_C 16 (lanes 0-31).  Z = gate * v of the slice is
-    // formed from its own loads, ZC columns of one token per lane, so that
-    // every loader lane takes an equal share of it.
+    // Record pieces of 16 bytes: lane lt copies piece lt + 256 k of E_bar,
+    // Q_gamma and K_tail (k < 4 each; 1,024 pieces per region) and piece lt
+    // of the stored A and A_qk triangles (320 pieces each); the remaining 64
+    // pieces of A go to loader wave 1, those of A_qk to wave 2 and gamma_C
+    // (32 pieces) to wave 3.  Z = gate * v of the slice is formed from its
+    // own loads, ZC columns of one token per lane, so that every loader lane
+    // takes an equal share of it.
     const int lt = tid - 64 * NCW;
+    const int lw = wave - NCW, l64 = lt & 63;  // loader wave (uniform), lane in it
+    constexpr int qA = R::oAcm / 16, qAqk = R::oAqk / 16, qGc = R::oGc / 16;  // region starts, in pieces
+    // LDS destinations (bytes, buffer 0) of the triangle pieces
+    const TriPiece pa = tri_upper_piece(lt), pq = tri_lower_piece(lt);
+    const int dA = L::oAcm + pa.row * SC * 2 + pa.col * 16, dAq = L::oAqk + pq.row * SC * 2 + pq.col * 16;
+    int xsrc = 0, xdst = 0, xstride = 0;  // the extra piece of waves 1-3
+    if (lw == 1) {
+      const TriPiece t = tri_upper_piece(256 + l64);
+      xsrc = qA + 256 + l64, xdst = L::oAcm + t.row * SC * 2 + t.col * 16, xstride = L::szA;
+    } else if (lw == 2) {
+      const TriPiece t = tri_lower_piece(256 + l64);
+      xsrc = qAqk + 256 + l64, xdst = L::oAqk + t.row * SC * 2 + t.col * 16, xstride = L::szA;
+    } else if (lw == 3) {
+      xsrc = qGc + min(l64, 31), xdst = L::oGc + l64 * 16, xstride = DK * 4;
+    }
+    const bool xwrite = lw == 1 || lw == 2 || (lw == 3 && l64 < 32);
     constexpr int ZC = DVS / 4;                 // Z columns per lane (64 DVS values over 256 lanes)
     constexpr int VG = DVS / ZC;                // lanes per v row
     const int tz = lt / VG, vv0 = (lt % VG) * ZC;
@@ -553,7 +598,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
     const float* w_seq = write_ch ? p.w + seq0 * DV + vbase : nullptr;
     // (clang vector elements: arrays of HIP's uint4 struct stay in scratch
     // memory instead of registers)
-    u32x4 rE[4], rQ[4], rK[4], rAc[2], rAq[2], rG;
+    u32x4 rE[4], rQ[4], rK[4], rAc, rAq, rX = {};
     bfz rv = {};
     f32x4 rw[write_ch ? ZC / 4 : 1] = {};
     float rvb = 0.f;
@@ -561,17 +606,16 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
 #define GDR_SPLIT_LOAD(nl)                                                                  \
     {                                                                                       \
       const int n_ = (nl);                                                                  \
-      const u32x4* rec = reinterpret_cast<const u32x4*>(recs + (size_t)n_ * R::BYTES) + lt; \
+      const u32x4* rec0 = reinterpret_cast<const u32x4*>(recs + (size_t)n_ * R::BYTES);     \
+      const u32x4* rec = rec0 + lt;                                                         \
       _Pragma("unroll") for (int k = 0; k < 4; ++k) {                                       \
         rE[k] = rec[256 * k];                                                               \
         rQ[k] = rec[1024 + 256 * k];                                                        \
         rK[k] = rec[2048 + 256 * k];                                                        \
       }                                                                                     \
-      _Pragma("unroll") for (int k = 0; k < 2; ++k) {                                       \
-        rAc[k] = rec[3072 + 256 * k];                                                       \
-        rAq[k] = rec[3584 + 256 * k];                                                       \
-      }                                                                                     \
-      rG = rec[4096 + min(lt, 31) - lt];                                                    \
+      rAc = rec[qA];                                                                        \
+      rAq = rec[qAqk];                                                                      \
+      if (lw != 0) rX = rec0[xsrc];                                                         \
       {                                                                                     \
         const unsigned r = (unsigned)(min(n_ * CH + tz, T - 1) - n_ * CH) * H;              \
         rv = *reinterpret_cast<const bfz*>(vg + (size_t)n_ * CH * H * DV + r * DV + vv0);   \
@@ -590,7 +634,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
       // that no one reads any more)
       if (nchunks > 0) {
         const int nw = min(n, nchunks - 1), buf = n & 1;
-        // rows of 16 pieces (E_bar, Q_gamma, K_tail), then of 8 (A, A_qk)
+        // rows of 16 pieces (E_bar, Q_gamma, K_tail), then the triangles
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int q = lt + 256 * k, row = q >> 4, col = q & 15;
@@ -598,13 +642,9 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
           *reinterpret_cast<u32x4*>(smem + L::oQg + buf * L::szE + row * SE * 2 + col * 16) = rQ[k];
           *reinterpret_cast<u32x4*>(smem + L::oKt + buf * L::szK + row * SKT * 2 + col * 16) = rK[k];
         }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int q = lt + 256 * k, row = q >> 3, col = q & 7;
-          *reinterpret_cast<u32x4*>(smem + L::oAcm + buf * L::szA + row * SC * 2 + col * 16) = rAc[k];
-          *reinterpret_cast<u32x4*>(smem + L::oAqk + buf * L::szA + row * SC * 2 + col * 16) = rAq[k];
-        }
-        if (lt < 32) *reinterpret_cast<u32x4*>(smem + L::oGc + buf * DK * 4 + lt * 16) = rG;
+        *reinterpret_cast<u32x4*>(smem + dA + buf * L::szA) = rAc;
+        *reinterpret_cast<u32x4*>(smem + dAq + buf * L::szA) = rAq;
+        if (xwrite) *reinterpret_cast<u32x4*>(smem + xdst + buf * xstride) = rX;
         {
           const bool ok = nw * CH + tz < T;
           float z[ZC];

@@ -97,8 +97,9 @@ inline hipError_t launch_chan_split(int gm, const ChunkParams& p, void* ws, int 
 }
 
 // bytes of one chunk's workspace record (dk 128): E_bar, Q_gamma, K_tail
-// rows, A, A_qk, gamma_C (matches SplitRec in chan_split_kernel.hpp)
-constexpr int64_t kSplitRecBytes = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4;
+// rows, the ten non-zero 16 x 16 blocks of A and of A_qk, gamma_C (matches
+// SplitRec in chan_split_kernel.hpp)
+constexpr int64_t kSplitRecBytes = 3 * 64 * 128 * 2 + 2 * 10 * 16 * 16 * 2 + 128 * 4;
 
 // Chunk kernel chosen for (io, decay kind, erase kind): the pipelined kernels
 // take bf16 I/O, the scalar-decay one the beta erase gate only; the rest go to
