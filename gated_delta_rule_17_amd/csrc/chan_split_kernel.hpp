@@ -38,30 +38,6 @@ struct SplitRec {
   static constexpr int BYTES = (oGc + DK * 4 + 255) / 256 * 256;
 };
 
-// Piece q (< 320) of a stored triangle -> (row, 16-byte column) of the dense
-// [64][64] bf16 matrix.  Lower (A_qk): row block I holds 2 (I + 1) pieces per
-// row; upper (Acm): row block J holds 2 (4 - J) pieces per row, starting at
-// column piece 2 J.
-struct TriPiece {
-  int row, col;
-};
-__device__ __forceinline__ TriPiece tri_lower_piece(int q) {
-  const int I = q < 32 ? 0 : q < 96 ? 1 : q < 192 ? 2 : 3;
-  const int w = 2 * (I + 1), l = q - 16 * I * (I + 1);
-  return {16 * I + l / w, l % w};
-}
-__device__ __forceinline__ TriPiece tri_upper_piece(int q) {
-  const int J = q < 128 ? 0 : q < 224 ? 1 : q < 288 ? 2 : 3;
-  const int w = 2 * (4 - J), l = q - (J == 0 ? 0 : J == 1 ? 128 : J == 2 ? 224 : 288);
-  return {16 * J + l / w, 2 * J + l % w};
-}
-// Byte offset, within a stored lower triangle, of row r of the dense matrix at
-// bf16 column c (c in a block J <= r / 16).
-__device__ __forceinline__ int tri_lower_byte(int r, int c) {
-  const int I = r >> 4;
-  return 512 * (I * (I + 1) / 2) + 32 * (I + 1) * (r & 15) + 2 * c;
-}
-
 // ---- pass 1 ------------------------------------------------------------------
 template <int DK>
 struct PrepLay {

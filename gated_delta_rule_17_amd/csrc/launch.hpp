@@ -38,9 +38,10 @@ GDR_DECLARE(pipe_gm0)
 GDR_DECLARE(pipe_gm3)
 #undef GDR_DECLARE
 
-// bytes of one chunk's record in the scalar-decay two-pass form: A, A_qk,
-// 336 chunk scalars (matches PipeRec in pipe_kernel.hpp)
-constexpr int64_t kPipeRecBytes = 17920;
+// bytes of one chunk's record in the scalar-decay two-pass form: the ten
+// non-zero 16 x 16 blocks of A and of A_qk, 336 chunk scalars, rounded up to
+// 256 (matches PipeRec in pipe_kernel.hpp)
+constexpr int64_t kPipeRecBytes = 11776;
 
 // LDS bytes of the second pass of the scalar-decay two-pass form (-1: none)
 inline int pipe_split_lds(int gm, int dk, int dvs) {

@@ -173,6 +173,33 @@ __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, b
     }
 }
 
+// Stored triangles: a [64][64] bf16 matrix whose six 16 x 16 blocks above
+// (or below) the diagonal are zero keeps only its ten other blocks, as 320
+// pieces of 16 bytes.  Lower: row block I holds its blocks J <= I, rows of
+// 32 (I + 1) bytes, row blocks in order.  Upper: row block J holds its
+// blocks I >= J, rows of 32 (4 - J) bytes.
+// Piece q (< 320) of a stored triangle -> (row, 16-byte column) of the dense
+// matrix.
+struct TriPiece {
+  int row, col;
+};
+__device__ __forceinline__ TriPiece tri_lower_piece(int q) {
+  const int I = q < 32 ? 0 : q < 96 ? 1 : q < 192 ? 2 : 3;
+  const int w = 2 * (I + 1), l = q - 16 * I * (I + 1);
+  return {16 * I + l / w, l % w};
+}
+__device__ __forceinline__ TriPiece tri_upper_piece(int q) {
+  const int J = q < 128 ? 0 : q < 224 ? 1 : q < 288 ? 2 : 3;
+  const int w = 2 * (4 - J), l = q - (J == 0 ? 0 : J == 1 ? 128 : J == 2 ? 224 : 288);
+  return {16 * J + l / w, 2 * J + l % w};
+}
+// Byte offset, within a stored lower triangle, of row r of the dense matrix at
+// bf16 column c (c in a block J <= r / 16).
+__device__ __forceinline__ int tri_lower_byte(int r, int c) {
+  const int I = r >> 4;
+  return 512 * (I * (I + 1) / 2) + 32 * (I + 1) * (r & 15) + 2 * c;
+}
+
 // T and A_qk tiles (list TL) of one chunk under no or a scalar decay, as
 // D^T = K_J X_I^T (X = K, or K + lam Q under the Q-Delta mix, for T; Q for
 // A_qk), so that each lane holds four consecutive columns j of one row i;
@@ -180,8 +207,8 @@ __device__ __forceinline__ void solve_inverse(const float* Td, const bf16* Tm, b
 // A_qk: j <= i).  K, Q rows of strides SK, SQ; G and beta per token.  T below
 // the diagonal blocks goes to bf16 rows of sT (stride SC), its diagonal
 // blocks to fp32 rows of sTd (block stride TDB, row stride TDS); A_qk to bf16
-// rows of aqk with row stride AS.
-template <int DK, int SK, int SQ, int SC, int TDS, int TDB, bool MIX, class TL>
+// rows of aqk with row stride AS, or (TRI) to aqk as a stored lower triangle.
+template <int DK, int SK, int SQ, int SC, int TDS, int TDB, bool MIX, bool TRI = false, class TL>
 __device__ __forceinline__ void scalar_gram_tiles(TL, const bf16* Kb, const bf16* Qb, const float* sG,
                                                   const float* sBeta, float lam, bf16* sT, float* sTd, bf16* aqk,
                                                   int AS, int g, int l16) {
@@ -228,7 +255,8 @@ __device__ __forceinline__ void scalar_gram_tiles(TL, const bf16* Kb, const bf16
       xT[r] = (j0 + r < i) ? bi[t] * accT[t][r] * e : 0.f;  // T: j < i
       xA[r] = (j0 + r <= i) ? accA[t][r] * e : 0.f;         // A_qk: j <= i
     }
-    *reinterpret_cast<bf16x4*>(aqk + i * AS + j0) = cvt4(xA);
+    if constexpr (TRI) *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(aqk) + tri_lower_byte(i, j0)) = cvt4(xA);
+    else *reinterpret_cast<bf16x4*>(aqk + i * AS + j0) = cvt4(xA);
     if (J < I) *reinterpret_cast<bf16x4*>(sT + i * SC + j0) = cvt4(xT);
     else *reinterpret_cast<f32x4*>(sTd + I * TDB + l16 * TDS + 4 * g) = xT;
   }
@@ -290,7 +318,8 @@ __device__ __forceinline__ int kt_off(int c, int r) { return c * ((CH + 8) * 2) 
 // A_qk row-major, [64][64] bf16 each, then the NSC chunk scalars.
 struct PipeRec {
   static constexpr int NSC = 336;  // PipeLay::NSC
-  static constexpr int oAcm = 0, oAqk = CH * CH * 2, oSc = 2 * CH * CH * 2;
+  static constexpr int PIECES_A = 320;  // A (column-major) and A_qk as stored triangles
+  static constexpr int oAcm = 0, oAqk = PIECES_A * 16, oSc = 2 * PIECES_A * 16;
   static constexpr int NPIECE = (oSc + NSC * 4) / 16;  // 16-byte pieces
   static constexpr int BYTES = (oSc + NSC * 4 + 255) / 256 * 256;
 };
@@ -658,7 +687,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       bf16x8 v[VPT];
       f32x4 w[write_ch ? VPT : 1][2];
       float vb[write_ch ? 1 : VPT];  // beta of the v rows (the beta write gate)
-      u32x4 rc[kRecWave ? 9 : 1];    // record mode: pieces pt + 128 k of the chunk
+      u32x4 rc[kRecWave ? 6 : 1];    // record mode: this lane's pieces of the chunk's record
     };
     // Loads address the chunk from a uniform base with 32-bit per-lane byte
     // offsets (row of the token within the chunk), so that they take the
@@ -709,28 +738,43 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void pipe_fwd_kernel(Ch
       }
     };
 
-    // PRE: pieces 0-511 of a record are A, 512-1023 A_qk (rows of 8 pieces),
-    // 1024-1107 the scalars; waves 0 and 1 copy them (lane pt: pieces
-    // pt + 128 k), waves 2 and 3 the q rows
-    static_assert(PipeRec::NPIECE == 1024 + NSC / 4 && NSC / 4 <= 128, "record pieces");
+    // PRE: pieces 0-319 of a record are the A triangle, 320-639 the A_qk
+    // triangle, 640-723 the scalars; waves 0 and 1 copy them, waves 2 and 3
+    // write the q rows.  Lane pt < 128: pieces pt and pt + 128 of each
+    // triangle; the last 64 pieces of A go to wave 0, those of A_qk to wave
+    // 1; scalar pieces 0-63 to wave 0, 64-83 to wave 1.
+    static_assert(PipeRec::NPIECE == 2 * PipeRec::PIECES_A + NSC / 4 && NSC / 4 > 64 && NSC / 4 <= 128,
+                  "record pieces");
+    constexpr int qAqk = PipeRec::oAqk / 16, qSc = PipeRec::oSc / 16;
+    const int px = pt & 63;
+    const int rxq = pw == 0 ? 256 + px : qAqk + 256 + px;           // extra triangle piece
+    const int rsq = qSc + (pw == 0 ? px : 64 + min(px, NSC / 4 - 65));  // scalar piece
     auto load_rec = [&](int n, Raw& R) __attribute__((always_inline)) {
       if constexpr (kRecWave) {
-        const u32x4* rp = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.ws) +
-                                                         ((size_t)bh * nchunks + n) * PipeRec::BYTES) + pt;
+        const u32x4* r0 = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.ws) +
+                                                         ((size_t)bh * nchunks + n) * PipeRec::BYTES);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) R.rc[k] = rp[128 * k];
-        R.rc[8] = rp[1024 + min(pt, NSC / 4 - 1) - pt];
+        for (int k = 0; k < 2; ++k) {
+          R.rc[k] = r0[pt + 128 * k];
+          R.rc[2 + k] = r0[qAqk + pt + 128 * k];
+        }
+        R.rc[4] = r0[rxq];
+        R.rc[5] = r0[rsq];
       }
     };
     auto write_rec = [&](int buf, const Raw& R) __attribute__((always_inline)) {
       if constexpr (kRecWave) {
+        bf16* A = sAcm + buf * CH * SC;
+        bf16* Aq = sAqk + buf * CH * SC;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int q = pt + 128 * (k & 3), row = q >> 3, col = q & 7;
-          bf16* dst = (k < 4 ? sAcm : sAqk) + buf * CH * SC + row * SC + col * 8;
-          *reinterpret_cast<u32x4*>(dst) = R.rc[k];
+        for (int k = 0; k < 2; ++k) {
+          const TriPiece a = tri_upper_piece(pt + 128 * k), b = tri_lower_piece(pt + 128 * k);
+          *reinterpret_cast<u32x4*>(A + a.row * SC + a.col * 8) = R.rc[k];
+          *reinterpret_cast<u32x4*>(Aq + b.row * SC + b.col * 8) = R.rc[2 + k];
         }
-        if (pt < NSC / 4) *reinterpret_cast<u32x4*>(sSc + buf * NSC + 4 * pt) = R.rc[8];
+        const TriPiece x = pw == 0 ? tri_upper_piece(256 + px) : tri_lower_piece(256 + px);
+        *reinterpret_cast<u32x4*>((pw == 0 ? A : Aq) + x.row * SC + x.col * 8) = R.rc[4];
+        if (pw == 0 || px < NSC / 4 - 64) *reinterpret_cast<u32x4*>(sSc + buf * NSC + 4 * (rsq - qSc)) = R.rc[5];
       }
     };
     // PRE, phase 3: K^T of chunk n (channel-major runs of 8 tokens) from its

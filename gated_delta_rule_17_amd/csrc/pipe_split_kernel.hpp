@@ -12,10 +12,11 @@
 //   pass 2 (pipe_fwd_kernel with PRE = true): the pipelined kernel whose
 //     producer waves copy the record into LDS instead of forming it.
 // Workspace record of a chunk (records ordered by (batch, head, chunk)):
-//   A column-major [64][64] bf16 (Acm[j][i] = A[i][j]) | A_qk row-major
-//   [64][64] bf16 | the 336 chunk scalars in the pipelined kernel's layout
-//   (PipeLay: G, beta, c_e, gamma, tail at 0, 64, 128, 192, 256; gamma_C at 320)
-// with the 16 x 16 blocks above the diagonal of A and A_qk zero.
+//   A column-major (Acm[j][i] = A[i][j]) as a stored upper triangle | A_qk
+//   row-major as a stored lower triangle (pipe_kernel.hpp: the ten non-zero
+//   16 x 16 blocks of each, 320 pieces of 16 bytes) | the 336 chunk scalars
+//   in the pipelined kernel's layout (PipeLay: G, beta, c_e, gamma, tail at
+//   0, 64, 128, 192, 256; gamma_C at 320).
 #pragma once
 
 #include "pipe_kernel.hpp"
@@ -111,26 +112,18 @@ __global__ __launch_bounds__(256) void pipe_prep_kernel(ChunkParams p, char* __r
       const float* sG = sc + PL::sG;
       const float* sB = sc + PL::sBeta;
       switch (w) {
-        case 0: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix>(Tiles<3, 3, 0, 3, 1, 0, 0>{}, sK, sQ, sG, sB, lam, sT,
+        case 0: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix, true>(Tiles<3, 3, 0, 3, 1, 0, 0>{}, sK, sQ, sG, sB, lam, sT,
                                                                  sTd, aqk_out, CH, g, l16); break;
-        case 1: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix>(Tiles<3, 2, 0, 2, 1, 2, 2>{}, sK, sQ, sG, sB, lam, sT,
+        case 1: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix, true>(Tiles<3, 2, 0, 2, 1, 2, 2>{}, sK, sQ, sG, sB, lam, sT,
                                                                  sTd, aqk_out, CH, g, l16); break;
-        case 2: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix>(Tiles<2, 1, 0, 1, 1>{}, sK, sQ, sG, sB, lam, sT, sTd,
+        case 2: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix, true>(Tiles<2, 1, 0, 1, 1>{}, sK, sQ, sG, sB, lam, sT, sTd,
                                                                  aqk_out, CH, g, l16); break;
-        default: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix>(Tiles<2, 3, 2, 3, 3>{}, sK, sQ, sG, sB, lam, sT,
+        default: scalar_gram_tiles<DK, SK, SQ, SC, TDS, TDB, mix, true>(Tiles<2, 3, 2, 3, 3>{}, sK, sQ, sG, sB, lam, sT,
                                                                   sTd, aqk_out, CH, g, l16); break;
       }
     };
     if (p.qmix) tiles(IC<1>{});
     else tiles(IC<0>{});
-    // the six blocks above the diagonal of A_qk are zero
-    constexpr int up[6][2] = {{0, 1}, {1, 3}, {0, 2}, {2, 3}, {0, 3}, {1, 2}};
-    const bf16x4 zero = {};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int u = 2 * w + k;
-      if (u < 6) *reinterpret_cast<bf16x4*>(aqk_out + (16 * up[u][0] + l16) * CH + 16 * up[u][1] + 4 * g) = zero;
-    }
   }
   __syncthreads();
   // A (in the k rows, read for the last time above) starts at zero, so that
@@ -141,9 +134,9 @@ __global__ __launch_bounds__(256) void pipe_prep_kernel(ChunkParams p, char* __r
   if (w == 0) solve_inverse<SC, TDS, TDB, 1>(sTd, sT, sA, g, l16);
   else if (w == 1) solve_inverse<SC, TDS, TDB, 2>(sTd, sT, sA, g, l16);
   __syncthreads();
-  for (int e = tid; e < CH * CH / 8; e += 256) {
-    const int r = e >> 3, c = e & 7;
-    reinterpret_cast<uint4*>(rec + R::oAcm)[e] = *reinterpret_cast<const uint4*>(sA + r * SC + 8 * c);
+  for (int q = tid; q < R::PIECES_A; q += 256) {
+    const TriPiece pc = tri_upper_piece(q);
+    reinterpret_cast<uint4*>(rec + R::oAcm)[q] = *reinterpret_cast<const uint4*>(sA + pc.row * SC + 8 * pc.col);
   }
   if (tid < PL::NSC / 4) reinterpret_cast<uint4*>(rec + R::oSc)[tid] = reinterpret_cast<const uint4*>(sc)[tid];
 }

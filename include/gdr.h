@@ -110,7 +110,7 @@ typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
  * (decay factors, Gram tiles, inverse) in each slice; with a workspace of at
  * least gdr_workspace_size() bytes that work runs once per chunk, in a
  * separate parallel pass that writes one record per (batch, head, chunk) to
- * the workspace (58.5 KiB under a per-channel decay, 17.5 KiB otherwise), and
+ * the workspace (58.5 KiB under a per-channel decay, 11.5 KiB otherwise), and
  * a second pass applies the records to the state.  NULL (or too small) keeps
  * the single pass.  The workspace must not overlap any
  * other argument; its contents are undefined after the call, and concurrent

@@ -188,7 +188,7 @@ def test_plan_kernel_choice(lib, decay, erase, block):
 # ---- the workspace of the two-pass per-channel form ---------------------------
 
 REC = 3 * 64 * 128 * 2 + 2 * 10 * 16 * 16 * 2 + 128 * 4  # one chunk's record (per-channel decay): 10 blocks of A, A_qk
-REC_SCALAR = 17920                                   # A, A_qk, 336 scalars, rounded to 256 (scalar decay)
+REC_SCALAR = 11776                                   # 10 blocks of A, A_qk, 336 scalars, rounded to 256 (scalar decay)
 
 
 def _chan_args(**kw):
