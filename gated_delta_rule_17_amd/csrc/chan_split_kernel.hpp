@@ -545,7 +545,8 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
     // Q_gamma and K_tail (k < 4 each; 1,024 pieces per region) and piece lt
     // of the stored A and A_qk triangles (320 pieces each); the remaining 64
     // pieces of A go to loader wave 1, those of A_qk to wave 2 and gamma_C
-    // (32 pieces) to wave 3.  Z = gate * v of the slice is formed from its
+    // (32 pieces) to wave 0, so that wave 3, which shares its SIMD with the
+    // first consumer wave, issues the fewest loads.  Z = gate * v of the slice is formed from its
     // own loads, ZC columns of one token per lane, so that every loader lane
     // takes an equal share of it.
     const int lt = tid - 64 * NCW;
@@ -561,10 +562,10 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
     } else if (lw == 2) {
       const TriPiece t = tri_lower_piece(256 + l64);
       xsrc = qAqk + 256 + l64, xdst = L::oAqk + t.row * SC * 2 + t.col * 16, xstride = L::szA;
-    } else if (lw == 3) {
+    } else if (lw == 0) {
       xsrc = qGc + min(l64, 31), xdst = L::oGc + l64 * 16, xstride = DK * 4;
     }
-    const bool xwrite = lw == 1 || lw == 2 || (lw == 3 && l64 < 32);
+    const bool xwrite = lw == 1 || lw == 2 || (lw == 0 && l64 < 32);
     constexpr int ZC = DVS / 4;                 // Z columns per lane (64 DVS values over 256 lanes)
     constexpr int VG = DVS / ZC;                // lanes per v row
     const int tz = lt / VG, vv0 = (lt % VG) * ZC;
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(64 * (pipe_ncw<DVS>() + 4)) void chan_rec_kernel(Ch
       }                                                                                     \
       rAc = rec[qA];                                                                        \
       rAq = rec[qAqk];                                                                      \
-      if (lw != 0) rX = rec0[xsrc];                                                         \
+      if (lw != 3) rX = rec0[xsrc];                                                         \
       {                                                                                     \
         const unsigned r = (unsigned)(min(n_ * CH + tz, T - 1) - n_ * CH) * H;              \
         rv = *reinterpret_cast<const bfz*>(vg + (size_t)n_ * CH * H * DV + r * DV + vv0);   \
