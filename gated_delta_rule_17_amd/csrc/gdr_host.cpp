@@ -172,7 +172,7 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
     if (overlap(ro, rs)) return fail(GDR_E_ARGS, "o overlaps state_out");
   }
 
-  // what this build implements
+  // what the library implements
   if (op == kOpChunk) {
     if (a->io == GDR_BF16 && a->dk != 64 && a->dk != 128)
       return fail(GDR_E_UNSUPPORTED, "bf16 chunk path supports dk in {64, 128} (got %d)", a->dk);

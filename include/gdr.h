@@ -69,7 +69,7 @@ typedef enum gdr_status {
   GDR_E_SHAPE = 2,       /* B, T, H, dk, dv, chunk out of range                  */
   GDR_E_DTYPE = 3,       /* unknown io dtype                                      */
   GDR_E_ALIGN = 4,       /* a pointer is not aligned as documented                */
-  GDR_E_UNSUPPORTED = 5, /* a valid combination this build does not implement     */
+  GDR_E_UNSUPPORTED = 5, /* a valid combination the library does not implement   */
   GDR_E_HIP = 6,         /* the HIP runtime reported an error                     */
   GDR_E_ARGS = 7         /* inconsistent arguments (kinds, aliasing, struct size) */
 } gdr_status;
