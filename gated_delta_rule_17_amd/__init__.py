@@ -10,12 +10,15 @@ library is missing, importing the functions raises.
     o, state = chunk_fwd(q, k, v, g=g_channel, beta=beta)            # KDA
     o, state = chunk_fwd(q, k, v, g=g, beta=beta, lam=lam)           # Q-Delta
     o, state = chunk_fwd(q, k, v, g=g_channel, b=b, w=w)             # Gated DeltaNet-2
+    o, state = chunk_fwd(q, k, v, g=g, beta=beta, lam=lam_t)         # Q-Delta, lambda_t [B,T,H]
+    o, state = chunk_fwd(q, k, v, g=g, beta=beta_v)                  # beta per value channel [B,T,H,dv]
     o, state = recurrent_step(q1, k1, v1, ..., state=state)          # one token
 
 Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g [B,T,H] (scalar decay) or
-[B,T,H,dk] (per-channel decay); beta [B,T,H]; b [B,T,H,dk]; w [B,T,H,dv];
-lam [H]; state [B,H,dk,dv] fp32.  Returns o [B,T,H,dv] in q's dtype and the
-final state [B,H,dk,dv] fp32.
+[B,T,H,dk] (per-channel decay); beta [B,T,H] (or [B,T,H,dv]: one beta per
+value channel); b [B,T,H,dk]; w [B,T,H,dv]; lam [H] (or [B,T,H]: lambda_t);
+state [B,H,dk,dv] fp32.  Returns o [B,T,H,dv] in q's dtype and the final
+state [B,H,dk,dv] fp32.
 """
 
 from __future__ import annotations
@@ -30,7 +33,7 @@ from ._lib import GdrArgs, GdrPlanInfo, GdrError  # noqa: F401
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 DECAY = {"none": 0, "scalar": 1, "channel": 2}
-GATE = {"beta": 0, "channel": 1}
+GATE = {"beta": 0, "channel": 1, "value": 2}
 
 
 def _ptr(t):
@@ -65,20 +68,24 @@ def build_args(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=No
     ``workspace``: an optional uint8 device tensor for the two-pass form."""
     B, Tq, H, dk = q.shape
     dv = v.shape[3]
+    vbeta = beta is not None and beta.dim() == 4
     if decay is None:
         decay = "none" if g is None else ("scalar" if g.dim() == 3 else "channel")
     if erase is None:
-        erase = "channel" if b is not None else "beta"
+        erase = "value" if vbeta else ("channel" if b is not None else "beta")
     if write is None:
-        write = "channel" if w is not None else "beta"
+        write = "value" if vbeta else ("channel" if w is not None else "beta")
     if qmix is None:
-        qmix = lam is not None
+        qmix = 0 if lam is None else (2 if lam.dim() == 3 else 1)
     a = GdrArgs()
     a.struct_size = ctypes.sizeof(GdrArgs)
     a.B, a.T, a.H, a.dk, a.dv = B, Tq if T is None else T, H, dk, dv
     a.chunk = 64
     a.io = DTYPES[q.dtype]
-    a.decay, a.erase, a.write, a.qmix = DECAY[decay], GATE[erase], GATE[write], int(bool(qmix))
+    qm = int(qmix)
+    if qm == 1 and lam is not None and lam.dim() == 3:
+        qm = 2
+    a.decay, a.erase, a.write, a.qmix = DECAY[decay], GATE[erase], GATE[write], qm
     a.dv_split = int(dv_split)
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.g, a.beta, a.b, a.w, a.lambda_ = _fptr(g), _fptr(beta), _fptr(b), _fptr(w), _fptr(lam)
@@ -105,7 +112,7 @@ def new_workspace(q, k, v, **kw):
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
 
 
-def _prepare(q, k, v, g, beta, b, w, lam, state, T1=False):
+def _prepare(q, k, v, g, beta, b, w, lam, state, decay=None):
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device")
@@ -122,14 +129,18 @@ def _prepare(q, k, v, g, beta, b, w, lam, state, T1=False):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if g is not None and tuple(g.shape) not in ((B, T, H), (B, T, H, dk)):
         raise ValueError(f"g must be [B,T,H] or [B,T,H,dk], got {tuple(g.shape)}")
-    if beta is not None and tuple(beta.shape) != (B, T, H):
-        raise ValueError(f"beta must be [B,T,H], got {tuple(beta.shape)}")
+    if g is not None and decay is not None:
+        want = {"scalar": 3, "channel": 4}.get(decay)
+        if want != g.dim():
+            raise ValueError(f"decay={decay!r} needs g with {want} dims, got shape {tuple(g.shape)}")
+    if beta is not None and tuple(beta.shape) not in ((B, T, H), (B, T, H, dv)):
+        raise ValueError(f"beta must be [B,T,H] or [B,T,H,dv], got {tuple(beta.shape)}")
     if b is not None and tuple(b.shape) != (B, T, H, dk):
         raise ValueError(f"b must be [B,T,H,dk], got {tuple(b.shape)}")
     if w is not None and tuple(w.shape) != (B, T, H, dv):
         raise ValueError(f"w must be [B,T,H,dv], got {tuple(w.shape)}")
-    if lam is not None and tuple(lam.shape) != (H,):
-        raise ValueError(f"lam must be [H], got {tuple(lam.shape)}")
+    if lam is not None and tuple(lam.shape) not in ((H,), (B, T, H)):
+        raise ValueError(f"lam must be [H] or [B,T,H], got {tuple(lam.shape)}")
     if state is not None and tuple(state.shape) != (B, H, dk, dv):
         raise ValueError(f"state must be [B,H,dk,dv], got {tuple(state.shape)}")
     return B, T, H, dk, dv
@@ -145,24 +156,32 @@ def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=Non
     """Chunkwise forward (C = 64) of the generalized gated delta rule.
     Enqueued on the current stream; no synchronisation.
 
-    ``two_pass``: None uses the two-pass form where the library offers one
-    (allocating a workspace unless ``workspace`` is given), False never, True
-    requires it.  ``workspace``: a uint8 device tensor (see ``new_workspace``)."""
-    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state)
+    ``workspace``: a uint8 device tensor of at least ``workspace_size()``
+    bytes (see ``new_workspace``) selects the two-pass form where the library
+    offers one; a smaller one raises.  Without one the call allocates nothing
+    but its outputs (unless ``out``/``state_out`` are given too).
+    ``two_pass``: None lets the workspace decide; False never uses the
+    two-pass form; True requires it and, when no workspace is passed,
+    allocates one for this call."""
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
                                                              device=q.device)
     kw = dict(g=g, beta=beta, b=b, w=w, lam=lam, state=state, decay=decay, erase=erase, write=write,
               qmix=qmix, dv_split=dv_split)
     ws = None
-    if two_pass is not False:
+    if two_pass is not False and (two_pass or workspace is not None):
         need = workspace_size(q, k, v, **kw)
         if two_pass and not need:
             raise ValueError("this shape has no two-pass form")
         if need:
             _check(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
-            ws = workspace if workspace is not None and workspace.numel() >= need else \
-                torch.empty(need, dtype=torch.uint8, device=q.device)
+            if workspace is None:
+                ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif workspace.numel() < need:
+                raise ValueError(f"workspace has {workspace.numel()} bytes, the two-pass form needs {need}")
+            else:
+                ws = workspace
     a = build_args(q, k, v, o=o, state_out=so, workspace=ws, **kw)
     _lib.call("gdr_chunk_fwd", a, _stream_ptr(q.device))
     return o, so
@@ -172,7 +191,7 @@ def recurrent_step(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, stat
                    decay=None, erase=None, write=None, qmix=None, out=None, state_out=None):
     """One decode token (T == 1).  ``state_out`` may be ``state`` itself for
     an in-place update."""
-    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state)
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
     if T != 1:
         raise ValueError("recurrent_step takes exactly one token (T == 1)")
     o = out if out is not None else torch.empty((B, 1, H, dv), dtype=q.dtype, device=q.device)

@@ -45,6 +45,16 @@ bool overlap(const Range& a, const Range& b) {
 
 constexpr int kOpChunk = 0, kOpStep = 1;
 
+// bytes of beta: [B,T,H], or [B,T,H,dv] under the per-value-channel beta
+int64_t beta_bytes(const gdr_args* a) {
+  const int64_t tokens = int64_t(a->B) * a->H * a->T;
+  return tokens * 4 * (a->erase == GDR_GATE_VALUE ? a->dv : 1);
+}
+// bytes of lambda: [H], or [B,T,H] for a time-varying lambda
+int64_t lambda_bytes(const gdr_args* a) {
+  return 4 * (a->qmix == 2 ? int64_t(a->B) * a->H * a->T : int64_t(a->H));
+}
+
 // a struct of ABI version 1 ends before the workspace fields
 constexpr size_t kArgsV1Size = offsetof(gdr_args, workspace);
 
@@ -62,15 +72,23 @@ Workspace workspace_of(const gdr_args* a) {
 // 128 with slices of 16 or 32 columns (few heads), where a single pass would
 // repeat every chunk's state-independent work in many slices.
 int64_t split_bytes(const gdr_args* a, int dvs) {
-  const gdr::ChunkKernel kern = gdr::chunk_kernel_for(a->io == GDR_BF16, a->decay, a->erase);
+  const gdr::ChunkKernel kern = gdr::chunk_kernel_for(a->io == GDR_BF16, a->dk, a->decay, a->erase, a->qmix);
   if ((kern != gdr::kChan && kern != gdr::kPipe) || a->dk != 128 || (dvs != 16 && dvs != 32) || a->T < 1)
     return 0;
   const int64_t nchunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
   return int64_t(a->B) * a->H * nchunks * (kern == gdr::kChan ? gdr::kSplitRecBytes : gdr::kPipeRecBytes);
 }
 
-int dvs_candidates(int io, int* out) {
-  if (io == GDR_BF16) {
+gdr::ChunkKernel kernel_for(const gdr_args* a) {
+  return gdr::chunk_kernel_for(a->io == GDR_BF16, a->dk, a->decay, a->erase, a->qmix);
+}
+
+int dvs_candidates(const gdr_args* a, int* out) {
+  if (kernel_for(a) == gdr::kPlain) {
+    out[0] = 16;
+    return 1;
+  }
+  if (a->io == GDR_BF16) {
     out[0] = 64; out[1] = 32; out[2] = 16;
     return 3;
   }
@@ -78,22 +96,19 @@ int dvs_candidates(int io, int* out) {
   return 2;
 }
 
-gdr::ChunkKernel kernel_for(const gdr_args* a) {
-  return gdr::chunk_kernel_for(a->io == GDR_BF16, a->decay, a->erase);
-}
-
 int chunk_lds(const gdr_args* a, int dvs) {
   const int gm = gdr::gate_mode(a->erase, a->write);
   switch (kernel_for(a)) {
     case gdr::kPipe: return gdr::pipe_lds(gm, a->dk, dvs);
     case gdr::kChan: return gdr::chan_lds(gm, a->dk, dvs);
+    case gdr::kPlain: return dvs == 16 ? gdr::plain_lds(a->dk) : -1;
     default: return gdr::chunk_lds(a->io == GDR_BF16, gm, a->dk, dvs, a->decay == GDR_DECAY_CHANNEL);
   }
 }
 
 // pipelined kernels: two consumer waves (one for a 16-column slice) plus four
 // producer waves (scalar decay) or four elementwise and two Gram waves
-// (per-channel decay); one-pass kernel: four waves
+// (per-channel decay); one-pass and plain kernels: four waves
 int chunk_block(const gdr_args* a, int dvs) {
   const int ncw = dvs >= 32 ? 2 : 1;
   switch (kernel_for(a)) {
@@ -118,22 +133,26 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (a->io != GDR_F32 && a->io != GDR_BF16) return fail(GDR_E_DTYPE, "unknown io dtype %d", a->io);
   if (a->decay < GDR_DECAY_NONE || a->decay > GDR_DECAY_CHANNEL)
     return fail(GDR_E_ARGS, "unknown decay kind %d", a->decay);
-  if (a->erase < GDR_GATE_BETA || a->erase > GDR_GATE_CHANNEL)
+  if (a->erase < GDR_GATE_BETA || a->erase > GDR_GATE_VALUE)
     return fail(GDR_E_ARGS, "unknown erase kind %d", a->erase);
-  if (a->write < GDR_GATE_BETA || a->write > GDR_GATE_CHANNEL)
+  if (a->write < GDR_GATE_BETA || a->write > GDR_GATE_VALUE)
     return fail(GDR_E_ARGS, "unknown write kind %d", a->write);
-  if (a->qmix != 0 && a->qmix != 1) return fail(GDR_E_ARGS, "qmix must be 0 or 1 (got %d)", a->qmix);
+  if ((a->erase == GDR_GATE_VALUE) != (a->write == GDR_GATE_VALUE))
+    return fail(GDR_E_ARGS, "the per-value-channel beta gates erase and write together: both kinds must be VALUE");
+  if (a->qmix < 0 || a->qmix > 2) return fail(GDR_E_ARGS, "qmix must be 0, 1 or 2 (got %d)", a->qmix);
   if (a->qmix && a->erase != GDR_GATE_BETA)
     return fail(GDR_E_ARGS, "qmix mixes the query into the beta-gated erase direction; erase must be BETA");
   const int64_t BH = int64_t(a->B) * a->H;
   const int64_t tokens = BH * a->T;
   const int64_t dmax = a->dk > a->dv ? a->dk : a->dv;
+  // Kernels address a sequence with 32-bit element offsets (T * H * d) and a
+  // chunk's rows with 32-bit byte offsets (up to 64 rows of H * d fp32).
   if (BH > (int64_t(1) << 30) || tokens * dmax > (int64_t(1) << 46) ||
-      int64_t(a->T) * a->H * dmax >= (int64_t(1) << 31))
-    return fail(GDR_E_SHAPE, "problem too large (need T * H * max(dk, dv) < 2^31)");
+      int64_t(a->T) * a->H * dmax >= (int64_t(1) << 31) || int64_t(a->H) * dmax * 4 * 64 >= (int64_t(1) << 32))
+    return fail(GDR_E_SHAPE, "problem too large (need T * H * max(dk, dv) < 2^31 and H * max(dk, dv) < 2^24)");
 
   const bool has_tok = a->T > 0;
-  const bool need_beta = a->erase == GDR_GATE_BETA || a->write == GDR_GATE_BETA;
+  const bool need_beta = a->erase != GDR_GATE_CHANNEL || a->write != GDR_GATE_CHANNEL;
   if (check_ptrs && has_tok) {
     if (!a->q || !a->k || !a->v || !a->o) return fail(GDR_E_NULL, "q, k, v and o are required when T > 0");
     if (a->decay != GDR_DECAY_NONE && !a->g) return fail(GDR_E_NULL, "g is required for decay kind %d", a->decay);
@@ -159,8 +178,8 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
     const int64_t gsz = a->decay == GDR_DECAY_CHANNEL ? tokens * a->dk * 4 : tokens * 4;
     const Range ins[] = {rng("q", a->q, tokens * a->dk * ioe),     rng("k", a->k, tokens * a->dk * ioe),
                          rng("v", a->v, tokens * a->dv * ioe),     rng("g", a->g, gsz),
-                         rng("beta", a->beta, tokens * 4),         rng("b", a->b, tokens * a->dk * 4),
-                         rng("w", a->w, tokens * a->dv * 4),       rng("lambda", a->lambda, int64_t(a->H) * 4),
+                         rng("beta", a->beta, beta_bytes(a)),      rng("b", a->b, tokens * a->dk * 4),
+                         rng("w", a->w, tokens * a->dv * 4),       rng("lambda", a->lambda, lambda_bytes(a)),
                          rng("state_in", a->state_in, BH * a->dk * a->dv * 4)};
     const Range ro = rng("o", a->o, tokens * a->dv * ioe);
     const Range rs = rng("state_out", a->state_out, BH * a->dk * a->dv * 4);
@@ -176,12 +195,12 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (op == kOpChunk) {
     if (a->io == GDR_BF16 && a->dk != 64 && a->dk != 128)
       return fail(GDR_E_UNSUPPORTED, "bf16 chunk path supports dk in {64, 128} (got %d)", a->dk);
-    if (a->io == GDR_F32 && a->dk != 64)
-      return fail(GDR_E_UNSUPPORTED, "fp32 chunk path supports dk == 64 (got %d)", a->dk);
+    if (a->io == GDR_F32 && a->dk != 64 && a->dk != 128)
+      return fail(GDR_E_UNSUPPORTED, "fp32 chunk path supports dk in {64, 128} (got %d)", a->dk);
     if (a->dv % 16 != 0 || a->dv > 256)
       return fail(GDR_E_UNSUPPORTED, "dv must be a multiple of 16 up to 256 (got %d)", a->dv);
     int cand[3];
-    const int nc = dvs_candidates(a->io, cand);
+    const int nc = dvs_candidates(a, cand);
     if (a->dv_split) {
       bool ok = false;
       for (int i = 0; i < nc; ++i) ok |= cand[i] == a->dv_split;
@@ -212,7 +231,7 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
     pi.n_chunks = 1;
   } else {
     int cand[3];
-    const int nc = dvs_candidates(a->io, cand);
+    const int nc = dvs_candidates(a, cand);
     int dvs = a->dv_split;
     if (!dvs) {
       for (int i = 0; i < nc && !dvs; ++i)
@@ -286,9 +305,9 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
     const Range others[] = {rng("q", a->q, tokens * a->dk * ioe),    rng("k", a->k, tokens * a->dk * ioe),
                             rng("v", a->v, tokens * a->dv * ioe),    rng("o", a->o, tokens * a->dv * ioe),
                             rng("g", a->g, a->decay == GDR_DECAY_CHANNEL ? tokens * a->dk * 4 : tokens * 4),
-                            rng("beta", a->beta, tokens * 4),
+                            rng("beta", a->beta, beta_bytes(a)),
                             rng("b", a->b, tokens * a->dk * 4),      rng("w", a->w, tokens * a->dv * 4),
-                            rng("lambda", a->lambda, int64_t(a->H) * 4),
+                            rng("lambda", a->lambda, lambda_bytes(a)),
                             rng("state_in", a->state_in, BH * a->dk * a->dv * 4),
                             rng("state_out", a->state_out, BH * a->dk * a->dv * 4)};
     for (const Range& r : others)
@@ -316,6 +335,7 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   switch (kernel_for(a)) {
     case gdr::kPipe: e = gdr::launch_pipe(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;
     case gdr::kChan: e = gdr::launch_chan(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;
+    case gdr::kPlain: e = gdr::launch_plain(p, a->io == GDR_BF16, a->dk, pi.grid, st); break;
     default: e = gdr::launch_chunk(a->io == GDR_BF16, gm, p, a->dk, pi.dv_slice, chan, pi.grid, st); break;
   }
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));

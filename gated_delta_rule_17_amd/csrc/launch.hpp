@@ -102,11 +102,19 @@ inline hipError_t launch_chan_split(int gm, const ChunkParams& p, void* ws, int 
 // SplitRec in chan_split_kernel.hpp)
 constexpr int64_t kSplitRecBytes = 3 * 64 * 128 * 2 + 2 * 10 * 16 * 16 * 2 + 128 * 4;
 
-// Chunk kernel chosen for (io, decay kind, erase kind): the pipelined kernels
-// take bf16 I/O, the scalar-decay one the beta erase gate only; the rest go to
-// the one-pass kernel.
-enum ChunkKernel { kOnePass = 0, kPipe = 1, kChan = 2 };
-inline ChunkKernel chunk_kernel_for(bool bf16io, int decay, int erase) {
+// Plain fp32 chunk kernel (plain_kernel.hpp): io fp32 or bf16, dk 64 or 128,
+// value slices of 16 columns.  plain_lds gives the LDS bytes (-1: no instance).
+int plain_lds(int dk);
+hipError_t launch_plain(const ChunkParams& p, bool bf16io, int dk, int grid, hipStream_t s);
+
+// Chunk kernel chosen for (io, dk, decay kind, erase kind, qmix): the plain
+// fp32 kernel takes the per-value-channel beta (erase 2), a time-varying
+// lambda (qmix 2) and fp32 I/O at dk 128; otherwise the pipelined kernels take
+// bf16 I/O, the scalar-decay one the beta erase gate only; the rest go to the
+// one-pass kernel.
+enum ChunkKernel { kOnePass = 0, kPipe = 1, kChan = 2, kPlain = 3 };
+inline ChunkKernel chunk_kernel_for(bool bf16io, int dk, int decay, int erase, int qmix) {
+  if (erase == 2 || qmix == 2 || (!bf16io && dk == 128)) return kPlain;
   if (!bf16io) return kOnePass;
   if (decay == 2) return kChan;
   return erase == 0 ? kPipe : kOnePass;

@@ -4,7 +4,8 @@
 // S = S_bar + k (z - r)^T,  o = S^T q  ("Chapter 11  Gated DeltaNet", 11.2
 // and 11.3: a streaming caller hands the final state back in; the variant
 // gates follow the Gated DeltaNet-2 page, key design 1, and the Q-Delta page,
-// key design 3).
+// key designs 2 and 3; under the per-value-channel beta of "Chapter 11", 11.3,
+// e = k and column v of the correction is scaled by beta[v]).
 //
 // The step is one pass over the fp32 state, so it is bound by HBM: each
 // workgroup streams one head's dk x dv state in (float4 per thread, rows
@@ -38,7 +39,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   constexpr int RG = 256 / VGN;   // row groups
   constexpr int RPT = DK / RG;    // rows per thread
   static_assert(RG * VGN == 256 && RPT * RG == DK, "step layout");
-  __shared__ float sA[DK], sE[DK], sK[DK], sQ[DK], sZ[DV];
+  __shared__ float sA[DK], sE[DK], sK[DK], sQ[DK];
+  __shared__ __attribute__((aligned(16))) float sZ[DV], sM[DV];
   __shared__ __attribute__((aligned(16))) float sR[RG][DV];
 
   const int tid = threadIdx.x;
@@ -68,7 +70,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     else if (p.decay == 2) a = fexp(p.g[to * DK + c]);
     float e;
     if (p.erase == 1) e = p.b[to * DK + c] * kv;
-    else e = beta * (p.qmix ? kv + p.lam[h] * qv : kv);
+    else if (p.erase == 2) e = kv;
+    else e = beta * (p.qmix ? kv + (p.qmix == 2 ? p.lam[to] : p.lam[h]) * qv : kv);
     sA[c] = a;
     sE[c] = e;
     sK[c] = kv;
@@ -76,7 +79,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   }
   if (tid < DV) {
     const float vv = (float)vg[to * DV + tid];
-    sZ[tid] = (p.write == 1 ? p.w[to * DV + tid] : beta) * vv;
+    const float m = p.erase == 2 ? p.beta[to * DV + tid] : 1.f;
+    sZ[tid] = (p.write == 1 ? p.w[to * DV + tid] : (p.erase == 2 ? m : beta)) * vv;
+    sM[tid] = m;
   }
   __syncthreads();
 
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   f32x4 rt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < RG; ++j) rt += *reinterpret_cast<const f32x4*>(&sR[j][v0]);
-  const f32x4 d = *reinterpret_cast<const f32x4*>(&sZ[v0]) - rt;
+  const f32x4 d = *reinterpret_cast<const f32x4*>(&sZ[v0]) - *reinterpret_cast<const f32x4*>(&sM[v0]) * rt;
   __syncthreads();  // sR is reused for the readout partials
 
   // write along k, then read along q

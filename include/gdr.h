@@ -20,10 +20,14 @@
  *     o_t   = S^T q_t                   read the post-update state ([CH11] 11.2)
  *
  * with the erase direction e_t and written value z_t chosen by the gate kinds:
- *     erase BETA:    e = beta_t * k_t    (qmix: e = beta_t * (k_t + lambda_h q_t), [QD] key design 3)
+ *     erase BETA:    e = beta_t * k_t    (qmix: e = beta_t * (k_t + lambda q_t), [QD] key design 3,
+ *                                         lambda fixed per head or time-varying, key design 2)
  *     erase CHANNEL: e = b_t (.) k_t     ([GDN2] key design 1; b is not clamped)
  *     write BETA:    z = beta_t * v_t
  *     write CHANNEL: z = w_t (.) v_t     ([GDN2] key design 1)
+ *     erase = write = VALUE: one beta per value channel gates the prediction
+ *                    error ([CH11] 11.3): S = S_bar + k_t (beta_t (.) (v_t - S_bar^T k_t))^T,
+ *                    i.e. every column of S follows its own scalar-beta rule.
  * DeltaNet = (NONE, BETA, BETA); Gated DeltaNet = (SCALAR, BETA, BETA);
  * KDA = (CHANNEL, BETA, BETA); Q-Delta = (SCALAR, BETA, BETA, qmix);
  * Gated DeltaNet-2 = (CHANNEL, CHANNEL, CHANNEL).
@@ -60,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 #define GDR_CHUNK 64
 
 typedef enum gdr_status {
@@ -76,7 +80,7 @@ typedef enum gdr_status {
 
 typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 typedef enum gdr_decay { GDR_DECAY_NONE = 0, GDR_DECAY_SCALAR = 1, GDR_DECAY_CHANNEL = 2 } gdr_decay;
-typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
+typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1, GDR_GATE_VALUE = 2 } gdr_gate;
 
 /*
  * Arguments.  Every per-token tensor is [B, T, H, ...], contiguous, row-major
@@ -87,10 +91,12 @@ typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
  *   o        [B,T,H,dv]   io dtype, written                16-byte aligned
  *   g        decay SCALAR: [B,T,H] fp32; CHANNEL: [B,T,H,dk] fp32 (16-byte
  *            aligned); NONE: must be NULL.  Log of the retention gate.
- *   beta     [B,T,H] fp32; required iff erase or write is BETA (or qmix)
+ *   beta     [B,T,H] fp32; required iff erase or write is BETA (or qmix);
+ *            [B,T,H,dv] fp32 when erase = write = VALUE
  *   b        [B,T,H,dk] fp32, 16-byte aligned; required iff erase CHANNEL
  *   w        [B,T,H,dv] fp32, 16-byte aligned; required iff write CHANNEL
- *   lambda   [H] fp32; required iff qmix (then erase must be BETA)
+ *   lambda   qmix 1: [H] fp32 (one lambda per head); qmix 2: [B,T,H] fp32
+ *            (time-varying lambda_t); required iff qmix (then erase must be BETA)
  *   state_in [B,H,dk,dv] fp32, 16-byte aligned, or NULL for a zero state
  *   state_out[B,H,dk,dv] fp32, 16-byte aligned, or NULL (not written)
  *
@@ -124,7 +130,7 @@ typedef struct gdr_args {
   int32_t decay;     /* gdr_decay */
   int32_t erase;     /* gdr_gate */
   int32_t write;     /* gdr_gate */
-  int32_t qmix;      /* 0 or 1 */
+  int32_t qmix;      /* 0 none, 1 lambda per head, 2 lambda per token */
   int32_t dv_split;  /* 0 = auto */
   const void *q, *k, *v;
   const float *g, *beta, *b, *w, *lambda;
@@ -148,10 +154,11 @@ typedef struct gdr_plan_info {
 
 /*
  * Chunkwise forward over any T >= 0 ([GDN2] key design 2, C = 64).
- * Supported: io BF16 with dk in {64, 128}; io F32 with dk == 64 (fp32 matrix
- * arithmetic for the tighter fp32 tolerance); dv a multiple of 16, 16..256,
- * divisible by the slice width.  Other valid combinations return
- * GDR_E_UNSUPPORTED.
+ * Supported: io BF16 or F32 with dk in {64, 128}; dv a multiple of 16,
+ * 16..256, divisible by the slice width.  fp32 I/O runs fp32 matrix
+ * arithmetic (the tighter fp32 tolerance); the per-value-channel beta and a
+ * time-varying lambda run on an all-fp32 kernel with 16-column slices.  Other
+ * valid combinations return GDR_E_UNSUPPORTED.
  */
 gdr_status gdr_chunk_fwd(const gdr_args *a, void *stream);
 

@@ -45,7 +45,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdr_abi_version() == 2
+    assert lib.gdr_abi_version() == 3
     for code, name in _lib.STATUS.items():
         assert lib.gdr_status_str(code).decode() == name
     assert lib.gdr_status_str(99).decode() == "GDR_E_UNKNOWN"
@@ -98,7 +98,8 @@ def test_null_struct(lib):
     ("B", 0, E_SHAPE), ("H", 0, E_SHAPE), ("T", -1, E_SHAPE),
     ("chunk", 32, E_SHAPE), ("dk", 0, E_SHAPE),
     ("io", 7, E_DTYPE),
-    ("decay", 3, E_ARGS), ("erase", 2, E_ARGS), ("write", -1, E_ARGS), ("qmix", 2, E_ARGS),
+    ("decay", 3, E_ARGS), ("erase", 3, E_ARGS), ("write", -1, E_ARGS), ("qmix", 3, E_ARGS),
+    ("erase", 2, E_ARGS), ("write", 2, E_ARGS),
     ("q", 0, E_NULL), ("o", 0, E_NULL), ("g", 0, E_NULL), ("beta", 0, E_NULL),
     ("q", _addr(0, 8), E_ALIGN), ("state_out", _addr(7, 4), E_ALIGN), ("beta", _addr(5, 2), E_ALIGN),
     ("dk", 96, E_UNSUP), ("dv", 40, E_UNSUP), ("dv_split", 48, E_UNSUP),
@@ -132,6 +133,42 @@ def test_kind_consistency(lib):
     assert _validate(lib, good_args(decay=2, g=_addr(4, 4))) == E_ALIGN  # channel g is vector-loaded
 
 
+def test_time_varying_lambda_and_value_beta(lib):
+    # lambda_t [B,T,H] and beta per value channel [B,T,H,dv] (erase = write = VALUE)
+    assert _validate(lib, good_args(qmix=2, lambda_=_addr(8))) == OK
+    assert _validate(lib, good_args(qmix=2, lambda_=0)) == E_NULL
+    assert _validate(lib, good_args(erase=2, write=2)) == OK
+    assert _validate(lib, good_args(erase=2, write=2, beta=0)) == E_NULL
+    assert _validate(lib, good_args(erase=2, write=2, qmix=1, lambda_=_addr(8))) == E_ARGS
+    # the aliasing check sizes beta [B,T,H,dv] and lambda [B,T,H]: o placed
+    # just past [B,T,H] floats but inside the larger tensors is rejected
+    tokens = 2 * 4 * 200
+    assert _validate(lib, good_args(erase=2, write=2, o=_addr(5, tokens * 4 + 256))) == E_ARGS
+    assert _validate(lib, good_args(o=_addr(5, tokens * 4 + 256))) == OK
+    assert _validate(lib, good_args(qmix=2, lambda_=_addr(8), o=_addr(8, 4 * 4 + 256))) == E_ARGS
+    assert _validate(lib, good_args(qmix=1, lambda_=_addr(8), o=_addr(8, 4 * 4 + 256))) == OK
+    # both run on the plain fp32 kernel: 16-column slices, four waves
+    for kw in (dict(qmix=2, lambda_=_addr(8)), dict(erase=2, write=2)):
+        a = good_args(B=8, H=16, **kw)
+        info = GdrPlanInfo()
+        assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+        assert info.dv_slice == 16 and info.block == 256 and info.grid == 8 * 16 * 8
+        assert _validate(lib, good_args(dv_split=32, **kw)) == E_UNSUP
+        assert _validate(lib, good_args(T=1, **kw), STEP) == OK
+
+
+def test_byte_offsets_fit_32_bits(lib):
+    # a chunk's 64 rows of H * max(dk, dv) fp32 are addressed with 32-bit byte
+    # offsets: H * max(dk, dv) must stay below 2^24
+    # (gdr_plan: shape checks without the pointer checks, whose fake buffers
+    # are too close together for these sizes)
+    lim = (1 << 24) // 128
+    info = GdrPlanInfo()
+    for H, code in ((lim - 1, OK), (lim, E_SHAPE), (160000, E_SHAPE)):
+        a = good_args(B=1, T=64, H=H)
+        assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == code, H
+
+
 def test_aliasing(lib):
     assert _validate(lib, good_args(o=_addr(0))) == E_ARGS              # o on top of q
     assert _validate(lib, good_args(state_out=_addr(6))) == OK          # exact in-place state
@@ -141,9 +178,17 @@ def test_aliasing(lib):
 
 def test_fp32_support_matrix(lib):
     assert _validate(lib, good_args(io=0, dk=64, dv=64)) == OK
-    assert _validate(lib, good_args(io=0, dk=128)) == E_UNSUP
+    assert _validate(lib, good_args(io=0, dk=128)) == OK
+    assert _validate(lib, good_args(io=0, dk=96)) == E_UNSUP
     assert _validate(lib, good_args(io=0, dk=64, dv=64, dv_split=64)) == E_UNSUP
+    assert _validate(lib, good_args(io=0, dk=128, dv_split=32)) == E_UNSUP   # plain kernel: 16 columns
     assert _validate(lib, good_args(io=0, dk=128, T=1), STEP) == OK
+    # fp32 at dk = 128 runs the plain fp32 kernel (16-column slices, no workspace)
+    a = good_args(io=0, dk=128, B=1, H=2)
+    info = GdrPlanInfo()
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+    assert info.dv_slice == 16 and info.block == 256 and info.passes == 1
+    assert _ws_size(lib, a) == (OK, 0)
 
 
 def test_zero_length_sequence_needs_no_token_pointers(lib):

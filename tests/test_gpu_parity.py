@@ -38,7 +38,15 @@ CASES = {
     "deltanet_bf16": config(H, B=1, H=2, T=512, decay="none"),
     "kda_mild": config(K, B=1, H=2, T=512, decay_shift=-4.0),
     "gdn2_mild": config(G2, B=1, H=2, T=512, decay_shift=-4.0),
-    # stress: per-channel mild decay at fp32 I/O (s3, d = 64: the fp32 path's width)
+    # stress: per-channel mild decay at fp32 I/O (s3), at d = 128 (the plain
+    # fp32 kernel) and at d = 64 (the fp32 MFMA kernel)
+    "kda_f32_mild_d128": config(F, variant="kda", B=1, H=2, T=512, d=128, decay_shift=-4.0),
+    "gdn2_f32_mild_d128": config(F, variant="gdn2", B=1, H=2, T=512, d=128, decay_shift=-4.0, state_std=0.1),
+    "gdn_f32_mild_d128": config(F, B=1, H=2, T=512, d=128, decay_shift=-4.0, state_std=0.05),
+    "qdelta_f32_d128": config(F, variant="qdelta", B=1, H=2, T=320, d=128, q_scale=False, decay_shift=-2.0),
+    "deltanet_f32_d128_tail": config(F, B=2, H=1, T=300, d=128, decay="none"),
+    "kda_extreme_f32_d128": config(F, variant="kda", B=1, H=2, T=130, d=128, g_const=-20.0),
+    "gdn2_f32_d128_dv64": config(F, variant="gdn2", B=1, H=2, T=200, dk=128, dv=64, decay_shift=-4.0),
     "kda_f32_mild": config(F, variant="kda", B=1, H=2, T=512, decay_shift=-4.0),
     "gdn2_f32_mild": config(F, variant="gdn2", B=1, H=2, T=300, decay_shift=-4.0, state_std=0.1),
     "qdelta_f32": config(F, variant="qdelta", B=1, H=2, T=256, q_scale=False),
@@ -57,6 +65,13 @@ CASES = {
     # dk != dv catches transposed operands
     "gdn_dk128_dv64": config(H, B=1, H=2, T=256, dk=128, dv=64, decay_shift=-2.0),
     "kda_dk64_dv128": config(K, B=1, H=2, T=256, dk=64, dv=128, decay_shift=-3.0),
+    # dk = dv = 64 on the bf16 kernels, and dv = 256
+    "gdn_bf16_d64": config(H, B=1, H=2, T=320, d=64, decay_shift=-3.0),
+    "gdn_bf16_d64_wch": config(H, B=2, H=2, T=200, d=64, write="channel", decay_shift=-3.0),
+    "gdn_erase_ch_d64": config(H, B=1, H=2, T=200, d=64, erase="channel", decay_shift=-3.0),
+    "gdn2_bf16_d64": config(G2, B=1, H=2, T=256, d=64, decay_shift=-4.0),
+    "gdn_dv256": config(H, B=1, H=2, T=256, dk=128, dv=256, decay_shift=-3.0),
+    "kda_dv256": config(K, B=1, H=2, T=192, dk=128, dv=256, decay_shift=-3.0),
     "gdn2_f32_dv32": config(F, variant="gdn2", B=1, H=2, T=200, dk=64, dv=32, decay_shift=-4.0),
     # gate kinds beyond the variants' own: one gate per key or value channel
     # with the other beta, and the Q-Delta mix, under both decay kinds
@@ -83,7 +98,7 @@ def _two_pass_form(cfg):
 
 # every case as chunk_fwd runs it by default, and the two-pass cases once more
 # on the single-pass kernels
-PARITY = [(n, None) for n in sorted(CASES)] + [(n, False) for n in sorted(CASES) if _two_pass_form(CASES[n])]
+PARITY = [(n, None) for n in sorted(CASES)] + [(n, True) for n in sorted(CASES) if _two_pass_form(CASES[n])]
 
 
 @pytest.mark.parametrize("name,two_pass", PARITY)
@@ -115,13 +130,15 @@ def test_two_pass_form(name):
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("name", ["gdn_bf16_small", "gdn2_bf16_small", "kda_f32_mild"])
+@pytest.mark.parametrize("name", ["gdn_bf16_small", "gdn2_bf16_small", "kda_f32_mild", "kda_f32_mild_d128"])
 def test_slice_width_does_not_change_results(name):
     """Every value-slice width gives bitwise-identical results (the per-column
     arithmetic does not depend on how columns are split over workgroups)."""
     cfg = CASES[name]
     inp = make_inputs(cfg)
     widths = (16, 32) if cfg["io"] == "f32" else (16, 32, 64)
+    if cfg["io"] == "f32" and cfg.get("d") == 128:
+        widths = (16, 0)   # the plain kernel's one width, chosen or given
     ref = None
     for wdt in widths:
         say(f"[slice] {name} dv_split={wdt}")
@@ -298,7 +315,7 @@ def test_pipelined_kernel_matches_the_yu_chunk_form(name):
     inp = make_inputs(cfg)
     assert inp["decay"] != "channel" and inp["erase"] == "beta" and cfg["io"] == "bf16"
     o_ref, S_ref = _yu_chunk_form(inp)
-    for two_pass in (False, None):
+    for two_pass in (False, True):
         say(f"[Y/U form] {name} two_pass={two_pass}")
         o, S = run_chunk(inp, two_pass=two_pass)
         assert_parity(name, o, S, o_ref, S_ref, TOL[cfg["io"]])
