@@ -32,6 +32,8 @@ from . import _lib
 from ._lib import GdrArgs, GdrPlanInfo, GdrError  # noqa: F401
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+# bytes of the library's own scratch used by chunk_fwd_noalloc (per device)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DECAY = {"none": 0, "scalar": 1, "channel": 2}
 GATE = {"beta": 0, "channel": 1, "value": 2}
 
@@ -187,6 +189,22 @@ def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=Non
     return o, so
 
 
+def chunk_fwd_noalloc(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
+                      decay=None, erase=None, write=None, qmix=None, dv_split=0, out=None, state_out=None):
+    """``gdr_chunk_fwd_noalloc``: the chunkwise forward with the two-pass
+    records in the library's static scratch (NOALLOC_SCRATCH_BYTES per
+    device) instead of a workspace.  With ``out`` and ``state_out`` given,
+    nothing is allocated; calls that overlap on one GPU race on the scratch."""
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
+                                                             device=q.device)
+    a = build_args(q, k, v, g=g, beta=beta, b=b, w=w, lam=lam, state=state, o=o, state_out=so,
+                   decay=decay, erase=erase, write=write, qmix=qmix, dv_split=dv_split)
+    _lib.call("gdr_chunk_fwd_noalloc", a, _stream_ptr(q.device))
+    return o, so
+
+
 def recurrent_step(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
                    decay=None, erase=None, write=None, qmix=None, out=None, state_out=None):
     """One decode token (T == 1).  ``state_out`` may be ``state`` itself for
@@ -217,5 +235,5 @@ def library_path() -> str:
     return _lib.path()
 
 
-__all__ = ["chunk_fwd", "recurrent_step", "plan", "build_args", "workspace_size", "new_workspace",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "recurrent_step", "plan", "build_args", "workspace_size", "new_workspace",
            "library_path", "GdrError"]

@@ -8,8 +8,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-EXPORTS = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr_validate", "gdr_plan", "gdr_workspace_size",
-           "gdr_status_str", "gdr_last_error", "gdr_abi_version"]
+EXPORTS = ["gdr_abi_version", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_plan",
+           "gdr_recurrent_step", "gdr_status_str", "gdr_validate", "gdr_workspace_size"]
 
 STATUS = {0: "GDR_OK", 1: "GDR_E_NULL", 2: "GDR_E_SHAPE", 3: "GDR_E_DTYPE", 4: "GDR_E_ALIGN",
           5: "GDR_E_UNSUPPORTED", 6: "GDR_E_HIP", 7: "GDR_E_ARGS"}
@@ -61,7 +61,7 @@ def load():
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python gated_delta_rule_17_amd/csrc/build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
-    for name in ("gdr_chunk_fwd", "gdr_recurrent_step"):
+    for name in ("gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_recurrent_step"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(GdrArgs), ctypes.c_void_p]
         fn.restype = ctypes.c_int

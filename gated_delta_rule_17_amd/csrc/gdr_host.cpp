@@ -7,6 +7,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/gdr.h"
@@ -219,7 +220,7 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   return GDR_OK;
 }
 
-gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
+gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out, Workspace ws) {
   const int64_t BH = int64_t(a->B) * a->H;
   gdr_plan_info pi{};
   pi.block = 256;
@@ -243,7 +244,6 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
     pi.grid = static_cast<int32_t>(BH * (a->dv / dvs));
     pi.n_chunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
     const int64_t need = split_bytes(a, dvs);
-    const Workspace ws = workspace_of(a);
     if (need > 0 && ws.ptr && ws.bytes >= static_cast<uint64_t>(need)) {
       pi.passes = 2;
       const bool chan = kernel_for(a) == gdr::kChan;
@@ -262,6 +262,44 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
   return GDR_OK;
 }
 
+gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
+  return plan_impl(a, op, out, workspace_of(a));
+}
+
+// The body of the chunk entry points: validation, plan and launch, with the
+// workspace given explicitly (the caller's, or the library's static scratch).
+gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool check_ws);
+
+// ---- scratch of the no-allocation entry point ------------------------------
+// Device memory of the two-pass records for callers that cannot allocate.
+// Every device the library runs on holds its own copy of this array until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address on the current device comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch.
+constexpr uint64_t kScratchBytes = GDR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+gdr_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDR_E_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GDR_E_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -272,6 +310,26 @@ gdr_status gdr_plan(const gdr_args* a, int op, gdr_plan_info* out) {
   gdr_status s = validate_impl(a, op, /*check_ptrs=*/false);
   if (s != GDR_OK) return s;
   return plan_impl(a, op, out);
+}
+
+gdr_status gdr_chunk_fwd_noalloc(const gdr_args* a, void* stream) {
+  gdr_status s = validate_impl(a, kOpChunk);
+  if (s != GDR_OK) return s;
+  // the plan as it would be with a workspace of unlimited size
+  gdr_plan_info pi;
+  s = plan_impl(a, kOpChunk, &pi);
+  if (s != GDR_OK) return s;
+  const int64_t need = split_bytes(a, pi.dv_slice);
+  if (need > static_cast<int64_t>(kScratchBytes))
+    return fail(GDR_E_SHAPE,
+                "the two-pass records of this call need %lld bytes; the no-allocation entry point's scratch "
+                "holds %llu (use gdr_chunk_fwd with a caller workspace)",
+                static_cast<long long>(need), static_cast<unsigned long long>(kScratchBytes));
+  if (need == 0) return chunk_fwd_impl(a, stream, Workspace{nullptr, 0}, false);
+  void* ptr = nullptr;
+  s = scratch_ptr(&ptr);
+  if (s != GDR_OK) return s;
+  return chunk_fwd_impl(a, stream, Workspace{ptr, kScratchBytes}, false);
 }
 
 gdr_status gdr_workspace_size(const gdr_args* a, uint64_t* bytes) {
@@ -289,12 +347,19 @@ gdr_status gdr_workspace_size(const gdr_args* a, uint64_t* bytes) {
 gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   gdr_status s = validate_impl(a, kOpChunk);
   if (s != GDR_OK) return s;
+  return chunk_fwd_impl(a, stream, workspace_of(a), true);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool check_ws) {
   gdr_plan_info pi;
-  s = plan_impl(a, kOpChunk, &pi);
+  gdr_status s = plan_impl(a, kOpChunk, &pi, ws);
   if (s != GDR_OK) return s;
   if (a->T == 0 && !a->state_out) return GDR_OK;
-  const Workspace ws = workspace_of(a);
-  if (pi.passes == 2) {
+  if (pi.passes == 2 && check_ws) {
     // the workspace of the two-pass form: aligned, and apart from every
     // other buffer of the call
     if (!aligned(ws.ptr, 256)) return fail(GDR_E_ALIGN, "workspace is not 256-byte aligned");
@@ -341,6 +406,10 @@ gdr_status gdr_chunk_fwd(const gdr_args* a, void* stream) {
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
   return GDR_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 gdr_status gdr_recurrent_step(const gdr_args* a, void* stream) {
   gdr_status s = validate_impl(a, kOpStep);

@@ -52,7 +52,8 @@
  *  - Errors: GDR_OK (0) or a non-zero gdr_status.  On a validation error
  *    nothing is launched and no output is written; gdr_last_error() gives a
  *    thread-local message.  GDR_E_HIP reports a HIP launch error.
- *  - Reentrant: no global mutable state besides the thread-local message.
+ *  - Reentrant: no global mutable state besides the thread-local message
+ *    (and the per-device scratch of gdr_chunk_fwd_noalloc, see there).
  *  - Deterministic: no atomics; the same inputs give bitwise-identical output.
  */
 #ifndef GDR_H
@@ -161,6 +162,29 @@ typedef struct gdr_plan_info {
  * valid combinations return GDR_E_UNSUPPORTED.
  */
 gdr_status gdr_chunk_fwd(const gdr_args *a, void *stream);
+
+/*
+ * The chunkwise forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and support matrix as gdr_chunk_fwd
+ * with a workspace of gdr_workspace_size() bytes; the two-pass records are
+ * written to a scratch array inside the library instead of a caller
+ * workspace (a->workspace and a->workspace_bytes are ignored).
+ *  - Limit: the scratch holds GDR_NOALLOC_SCRATCH_BYTES (64 MiB) per device;
+ *    a call whose records need more (gdr_workspace_size) returns GDR_E_SHAPE
+ *    before any launch.  Shapes without a two-pass form run the single pass
+ *    and touch no scratch.
+ *  - The call allocates nothing (no hipMalloc, no library allocation).  Each
+ *    GPU the library runs on holds its own copy of the scratch until the
+ *    process ends; its device address is looked up once per device, on the
+ *    first call made with that device current.
+ *  - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *    time on one GPU (concurrent streams, or several host threads) race and
+ *    must be serialised by the caller.  The records are rewritten in full by
+ *    each call; nothing in the scratch needs clearing.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES (64ull << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_args *a, void *stream);
 
 /*
  * One decode step ([CH11] 11.3: the streaming caller passes the previous

@@ -284,6 +284,20 @@ def test_workspace_switches_the_plan(lib):
     assert info.block == 64 * 5 and 0 < info.lds_bytes <= 160 * 1024   # 1 consumer + 4 loader waves
 
 
+def test_noalloc_rejects_records_beyond_its_scratch(lib):
+    # Gated DeltaNet-2 at B1 H32 T65536 needs 1.96 GB of records, far beyond
+    # the 64 MiB scratch: rejected in host code, before any HIP call
+    a = _chan_args(B=1, H=32, T=65536)
+    st, need = _ws_size(lib, a)
+    assert st == OK and need > (64 << 20)
+    assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(a), None) == E_SHAPE
+    assert b"scratch" in lib.gdr_last_error()
+    # validation errors come first, as for gdr_chunk_fwd
+    a = good_args(B=0)
+    assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(a), None) == E_SHAPE
+    assert lib.gdr_chunk_fwd_noalloc(None, None) == E_NULL
+
+
 def test_version_one_struct_runs_without_workspace(lib):
     v1 = GdrArgs.workspace.offset
     a = _chan_args(B=1, H=32, T=200, workspace=_addr(11), workspace_bytes=1 << 40)
