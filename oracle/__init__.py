@@ -25,12 +25,21 @@ Modules
                  order, plus the product expansion and linear-attention brute
                  force; used only to pin ``recurrence``.
 ``chunk_mirror`` the chunkwise WY form with absorbed decay, written literally
-                 in float64; pinned against ``recurrence``.
+                 in float64, and its backward in the chunk form's own terms;
+                 pinned against ``recurrence`` and ``backward``.
+``backward``     reverse mode through the token loop: the gradients of every
+                 input for a given output and final-state cotangent; pinned
+                 by finite differences of ``recurrence``.
+``epilogue``     RMSNorm of each head's readout, then the SiLU output gate;
+                 pinned by torch's rms_norm and silu and by closed forms.
 
 Every function here is pinned by a ``-m "not gpu"`` test in
-``tests/test_oracle_pins.py`` against something other than itself (a worked
+``tests/test_oracle_pins.py`` or ``tests/test_oracle_backward.py`` against
+something other than itself (a worked
 example from [CH11], closed forms, page-form reductions, a stability identity
 from [QD], finite-difference gradients).  No function is parity-unpinned.
 """
 
 from .recurrence import gdr_recurrence, gdr_step, VARIANTS, variant_kinds  # noqa: F401
+from .backward import gdr_recurrence_vjp  # noqa: F401
+from .epilogue import output_norm_gate  # noqa: F401

@@ -71,3 +71,77 @@ def chunk_forward_one(q, k, e, z, g, S0, C=64, return_intermediates=False):
     if return_intermediates:
         return o, S, inter
     return o, S
+
+
+def chunk_backward_one(q, k, e, z, g, S0, do, dS_final, C=64):
+    """Backward of ``chunk_forward_one`` in the chunk form's own terms
+    ([GDN2] key design 3): per chunk, from the last one, with dS the gradient
+    of the state leaving the chunk,
+
+      dW   = A_qk^T dO + K_tail dS              (W = U - Y S)
+      dU   = dW,  dY = -dW S^T
+      dA   = dU Z^T + dY E_bar^T                (the gate-weighted dA products)
+      dT   = -tril(A^T dA A^T, -1)              (adjoint of the triangular inverse)
+      dE_bar = A^T dY + dT K_bar,  dZ = A^T dU,  dK_bar = dT^T E_bar + dA_qk^T Q_gamma
+      dQ_gamma = dO S^T + dA_qk K_bar,  dA_qk = tril(dO W^T, 0)
+      dS_in = Q_gamma^T dO + Diag(gamma_C) dS - Y^T dW
+
+    and the decay factors gamma = exp(cumsum(g)) taken back to g by the chain
+    rule (gamma^{-1} formed literally, so mild decay only, like the forward
+    mirror).  Returns (dq, dk, de, dz, dg, dS0), float64, shaped like the
+    inputs (de, dz: gradients of the erase directions and written values)."""
+    q, k, e, z, g, S0, do, dSf = (_f64(x) for x in (q, k, e, z, g, S0, do, dS_final))
+    T, dk = k.shape
+    dv = z.shape[1]
+    n_chunks = -(-T // C)
+    pad = n_chunks * C - T
+
+    def padrows(x):
+        return np.concatenate([x, np.zeros((pad,) + x.shape[1:])], axis=0) if pad else x
+
+    q, k, e, z, g, do = (padrows(x) for x in (q, k, e, z, g, do))
+    # forward, keeping each chunk's entering state
+    S_in = []
+    S = S0.copy()
+    for n in range(n_chunks):
+        sl = slice(n * C, (n + 1) * C)
+        S_in.append(S.copy())
+        _, S = chunk_forward_one(q[sl], k[sl], e[sl], z[sl], g[sl], S, C=C)
+    dq, dk_, de, dz, dg = (np.zeros_like(x) for x in (q, k, e, z, g))
+    dS = dSf.copy()
+    for n in range(n_chunks - 1, -1, -1):
+        sl = slice(n * C, (n + 1) * C)
+        Q, K, E, Z, dO, S = q[sl], k[sl], e[sl], z[sl], do[sl], S_in[n]
+        G = np.cumsum(g[sl], axis=0)
+        gam = np.exp(G)
+        gC = gam[-1]
+        K_bar, E_bar, Q_gam = K / gam, gam * E, gam * Q
+        Tm = np.tril(E_bar @ K_bar.T, -1)
+        A = np.linalg.inv(np.eye(C) + Tm)
+        Y, U = A @ E_bar, A @ Z
+        A_qk = np.tril(Q_gam @ K_bar.T, 0)
+        K_tail = (gC[None, :] / gam) * K
+        W = U - Y @ S
+        # the chunk's outputs and the leaving state
+        dW = A_qk.T @ dO + K_tail @ dS
+        dA_qk = np.tril(dO @ W.T, 0)
+        dQ_gam = dO @ S.T + dA_qk @ K_bar
+        dK_tail = W @ dS.T
+        dgC = np.einsum("cv,cv->c", S, dS) * gC
+        dS_prev = Q_gam.T @ dO + gC[:, None] * dS - Y.T @ dW
+        dU, dY = dW, -dW @ S.T
+        dA = dU @ Z.T + dY @ E_bar.T
+        dT = -np.tril(A.T @ dA @ A.T, -1)
+        dE_bar = A.T @ dY + dT @ K_bar
+        dZ = A.T @ dU
+        dK_bar = dT.T @ E_bar + dA_qk.T @ Q_gam
+        # back to the raw rows and the cumulative log-decay G
+        dE = gam * dE_bar
+        dQ = gam * dQ_gam
+        dK = dK_bar / gam + dK_tail * gC[None, :] / gam
+        dG = dE_bar * E_bar + dQ_gam * Q_gam - dK_bar * K_bar - dK_tail * K_tail
+        dG[-1] += dgC + np.einsum("jc,jc->c", dK_tail, K_tail)
+        dq[sl], dk_[sl], de[sl], dz[sl] = dQ, dK, dE, dZ
+        dg[sl] = np.cumsum(dG[::-1], axis=0)[::-1]   # G = cumsum(g)
+        dS = dS_prev
+    return dq[:T], dk_[:T], de[:T], dz[:T], dg[:T], dS

@@ -104,10 +104,16 @@ def kda_kda(q, k, v, alpha_vec, beta, S0=None, s=1.0):
     return o, S
 
 
+def _lam_at(lam, t):
+    """lambda of token t: one value per head, or lambda_t ([QD] key design 2)."""
+    return lam[t] if np.ndim(lam) else lam
+
+
 def qdelta_qd(q, k, v, alpha, beta, lam, S0=None):
     """[QD] key design 3 (the rule rewritten with the mixed input):
     x_t = k_t + lam q_t and S_t = alpha_t S_{t-1} (I - beta_t x_t k_t^T)
-    + beta_t v_t k_t^T, state dv x dk; read o_t = S_t q_t."""
+    + beta_t v_t k_t^T, state dv x dk; read o_t = S_t q_t.  ``lam`` is a
+    number, or one lambda_t per token (key design 2)."""
     q, k, v, alpha, beta = _arr(q, k, v, alpha, beta)
     T, dk = k.shape
     dv = v.shape[1]
@@ -115,7 +121,7 @@ def qdelta_qd(q, k, v, alpha, beta, lam, S0=None):
     o = np.zeros((T, dv))
     eye = np.eye(dk)
     for t in range(T):
-        x = k[t] + lam * q[t]
+        x = k[t] + _lam_at(lam, t) * q[t]
         S = alpha[t] * S @ (eye - beta[t] * np.outer(x, k[t])) + beta[t] * np.outer(v[t], k[t])
         o[t] = S @ q[t]
     return o, S
@@ -124,7 +130,8 @@ def qdelta_qd(q, k, v, alpha, beta, lam, S0=None):
 def qdelta_error_form(q, k, v, alpha, beta, lam, S0=None):
     """[QD] overall framework: after forgetting, the state yields the key
     retrieval v^ = S k and the query prediction o^ = S q; the mixed error
-    v - v^ - lam o^ is written back along k with strength beta (dv x dk)."""
+    v - v^ - lam o^ is written back along k with strength beta (dv x dk).
+    ``lam`` is a number, or one lambda_t per token."""
     q, k, v, alpha, beta = _arr(q, k, v, alpha, beta)
     T, dk = k.shape
     dv = v.shape[1]
@@ -134,8 +141,26 @@ def qdelta_error_form(q, k, v, alpha, beta, lam, S0=None):
         S = alpha[t] * S
         vhat = S @ k[t]
         ohat = S @ q[t]
-        S = S + beta[t] * np.outer(v[t] - vhat - lam * ohat, k[t])
+        S = S + beta[t] * np.outer(v[t] - vhat - _lam_at(lam, t) * ohat, k[t])
         o[t] = S @ q[t]
+    return o, S
+
+
+def gdn_value_beta_ch11(q, k, v, alpha, beta_vec, S0=None):
+    """[CH11] §11.3, the module's write gate: one beta per value channel
+    scales that channel's prediction error, the forget gate stays a scalar:
+    S~ = alpha S, v^ = S~^T k, S = S~ + k (beta_t * (v - v^))^T (dk x dv);
+    read y = S^T q."""
+    q, k, v, alpha, beta_vec = _arr(q, k, v, alpha, beta_vec)
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        St = alpha[t] * S
+        vhat = St.T @ k[t]
+        S = St + np.outer(k[t], beta_vec[t] * (v[t] - vhat))
+        o[t] = S.T @ q[t]
     return o, S
 
 

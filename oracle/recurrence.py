@@ -41,6 +41,18 @@ GDN-2: [GDN2] key design 1 gives
 ``S_t = (I - k_t (b_t * k_t)^T) D_t S_{t-1} + k_t (w_t * v_t)^T``, i.e. the
 unified step with ``e = b * k`` and ``z = w * v``.  The erase gate is not
 clamped (the same page's ablation also trains b in [0, 2]).
+
+Two variants of the pages go beyond that table:
+
+* time-varying lambda: [QD] key design 2 writes the feedback coefficient as
+  ``lambda_t in [0, 1]``; ``lam`` of shape [B, T, H] gives one per token
+  (shape [H]: one per head, the reading the workloads use).
+* one beta per value channel: [CH11] §11.3 notes that the module it follows
+  gates the prediction error of each value channel with its own beta (the
+  forget gate stays one scalar per head), ``S_t = S_bar + k_t (beta_t *
+  (v_t - S_bar^T k_t))^T`` with ``beta_t in R^{dv}``; selected by
+  ``erase = write = "value"`` with ``beta`` of shape [B, T, H, dv].  It is
+  not an (e, z) pair of the table: the erase strength differs per column.
 """
 
 from __future__ import annotations
@@ -48,7 +60,7 @@ from __future__ import annotations
 import numpy as np
 
 DECAYS = ("none", "scalar", "channel")
-GATES = ("beta", "channel")
+GATES = ("beta", "channel", "value")
 
 # name -> (decay, erase, write, qmix)
 VARIANTS = {
@@ -92,9 +104,10 @@ def gdr_recurrence(q, k, v, *, decay="none", g=None, erase="beta", write="beta",
       g         [B,T,H] (decay="scalar") or [B,T,H,dk] (decay="channel");
                 log of the retention gate, so alpha = exp(g)
       beta      [B,T,H]          (erase and/or write == "beta", or qmix)
+                [B,T,H,dv]       (erase == write == "value": one per value channel)
       b         [B,T,H,dk]       (erase == "channel")
       w         [B,T,H,dv]       (write == "channel")
-      lam       [H]              (qmix)
+      lam       [H] or [B,T,H]   (qmix; per head, or per token)
       state     [B,H,dk,dv] or None (zeros)
 
     Returns (o [B,T,H,dv], S_final [B,H,dk,dv]), float64 numpy arrays.
@@ -103,6 +116,8 @@ def gdr_recurrence(q, k, v, *, decay="none", g=None, erase="beta", write="beta",
     """
     if decay not in DECAYS or erase not in GATES or write not in GATES:
         raise ValueError("bad variant kinds")
+    if (erase == "value") != (write == "value"):
+        raise ValueError("the per-value-channel beta gates erase and write together")
     if qmix and erase != "beta":
         raise ValueError("qmix mixes the query into a beta-gated erase direction")
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -112,10 +127,16 @@ def gdr_recurrence(q, k, v, *, decay="none", g=None, erase="beta", write="beta",
 
     qf, kf, vf = _heads_first(q), _heads_first(k), _heads_first(v)
     gf = _heads_first(_f64(g)) if decay != "none" else None
-    bef = _heads_first(_f64(beta)) if (erase == "beta" or write == "beta") else None
+    bef = _heads_first(_f64(beta)) if erase != "channel" or write != "channel" else None
     bf = _heads_first(_f64(b)) if erase == "channel" else None
     wf = _heads_first(_f64(w)) if write == "channel" else None
-    lamf = np.repeat(_f64(lam)[None, :], B, axis=0).reshape(B * H) if qmix else None
+    lamf = None
+    if qmix:
+        lam = _f64(lam)
+        if lam.ndim == 1:  # one lambda per head, the same at every token
+            lamf = np.repeat(np.repeat(lam[None, :], B, axis=0).reshape(B * H)[:, None], T, axis=1)
+        else:              # lambda_t, [B, T, H]
+            lamf = _heads_first(lam)
     if state is None:
         S0 = np.zeros((B * H, dk, dv))
     else:
@@ -133,9 +154,15 @@ def gdr_recurrence(q, k, v, *, decay="none", g=None, erase="beta", write="beta",
             elif decay == "channel":
                 S *= np.exp(gf[sl, t])[:, :, None]
             kt = kf[sl, t]
+            if erase == "value":
+                # [CH11] §11.3: predict along k, gate each value channel's error
+                r = np.matmul(kt[:, None, :], S)[:, 0, :]
+                S += kt[:, :, None] * (bef[sl, t] * (vf[sl, t] - r))[:, None, :]
+                o[sl, t] = np.matmul(qf[sl, t][:, None, :], S)[:, 0, :]
+                continue
             # erase direction e and written value z
             if erase == "beta":
-                x = kt + lamf[sl, None] * qf[sl, t] if qmix else kt
+                x = kt + lamf[sl, t, None] * qf[sl, t] if qmix else kt
                 e = bef[sl, t, None] * x
             else:
                 e = bf[sl, t] * kt

@@ -40,9 +40,17 @@ MUTANTS = {
     "decay_on_value_axis": [("S *= np.exp(gf[sl, t])[:, :, None]", "S *= np.exp(gf[sl, t]).mean(axis=1)[:, None, None]")],
     # query mixed into the write direction as well
     "qmix_in_write": [("S += kt[:, :, None] * (z - r)[:, None, :]",
-                       "S += (kt + (lamf[sl, None] * qf[sl, t] if qmix else 0))[:, :, None] * (z - r)[:, None, :]")],
+                       "S += (kt + (lamf[sl, t, None] * qf[sl, t] if qmix else 0))[:, :, None] * (z - r)[:, None, :]")],
     # lambda ignored
-    "lambda_ignored": [("x = kt + lamf[sl, None] * qf[sl, t] if qmix else kt", "x = kt")],
+    "lambda_ignored": [("x = kt + lamf[sl, t, None] * qf[sl, t] if qmix else kt", "x = kt")],
+    # lambda_t read one token late
+    "lambda_t_shifted": [("x = kt + lamf[sl, t, None] * qf[sl, t] if qmix else kt",
+                          "x = kt + lamf[sl, max(t - 1, 0), None] * qf[sl, t] if qmix else kt")],
+    # per-value-channel beta applied to the write only, not to the prediction
+    "value_beta_write_only": [("(bef[sl, t] * (vf[sl, t] - r))", "(bef[sl, t] * vf[sl, t] - r)")],
+    # per-value-channel beta predicting before the decay
+    "value_beta_decay_after_write": [
+        ("            if erase == \"value\":\n", "            if erase == \"value\":\n                S /= np.exp(gf[sl, t])[:, None, None] if decay == \"scalar\" else 1.0\n")],
     # beta applied twice to the written value
     "beta_twice": [("z = bef[sl, t, None] * vf[sl, t]", "z = bef[sl, t, None] ** 2 * vf[sl, t]")],
     # readout along k instead of q

@@ -435,3 +435,113 @@ def test_head_batching_does_not_change_results():
     o1, S1 = gdr_recurrence(q[1:2, :, 2:3], k[1:2, :, 2:3], v[1:2, :, 2:3], decay="channel",
                             g=g[1:2, :, 2:3], beta=beta[1:2, :, 2:3], state=S0[1:2, 2:3])
     assert np.array_equal(o1[0, :, 0], a[0][1, :, 2]) and np.array_equal(S1[0, 0], a[1][1, 2])
+
+
+# ---------------------------------------------------------------------------
+# P10: a time-varying lambda_t ([QD] key design 2 writes lambda_t in [0, 1];
+# key design 3 mixes it into x_t = k_t + lambda_t q_t)
+
+def _qdelta_t(x, lam_t):
+    o, S = gdr_recurrence(_seq(x["q"]), _seq(x["k"]), _seq(x["v"]), decay="scalar",
+                          g=_seq(np.log(x["alpha"])), beta=_seq(x["beta"]), qmix=True,
+                          lam=_seq(lam_t), state=x["S0"][None, None])
+    return o[0, :, 0], S[0, 0]
+
+
+def test_time_varying_lambda_matches_page_forms():
+    x = _one(T, DK, DV, 50)
+    lam_t = np.random.default_rng(51).uniform(0, 1, T)
+    o, S = _qdelta_t(x, lam_t)
+    o1, S1 = pf.qdelta_qd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], lam_t, x["S0"].T)
+    o2, S2 = pf.qdelta_error_form(x["q"], x["k"], x["v"], x["alpha"], x["beta"], lam_t, x["S0"].T)
+    _close(o, o1, 1e-13); _close(S, S1.T, 1e-13)
+    _close(o, o2, 1e-13); _close(S, S2.T, 1e-13)
+
+
+def test_constant_lambda_t_is_the_per_head_lambda():
+    x = _one(T, DK, DV, 52)
+    o, S = _qdelta_t(x, np.full(T, 0.37))
+    o1, S1 = _run(x, "qdelta", lam=0.37)
+    assert np.array_equal(o, o1) and np.array_equal(S, S1)
+
+
+def test_time_varying_lambda_contracts_at_every_step():
+    """Lemma 3.1 of [QD] holds token by token with x_t = k_t + lambda_t q_t:
+    at alpha = 1 the mixed error of each step scales by exactly
+    |1 - beta_t k_t . x_t|."""
+    rng = np.random.default_rng(53)
+    Tn, dk, dv = 30, 8, 6
+    q, k = _unit(rng, Tn, dk), _unit(rng, Tn, dk)
+    v = rng.standard_normal((Tn, dv))
+    beta = rng.uniform(0.05, 0.95, Tn)
+    lam_t = rng.uniform(0, 1, Tn)
+    S = rng.standard_normal((dk, dv))
+    for t in range(Tn):
+        _, S1 = gdr_recurrence(_seq(q[t:t + 1]), _seq(k[t:t + 1]), _seq(v[t:t + 1]), decay="none",
+                               beta=_seq(beta[t:t + 1]), qmix=True, lam=_seq(lam_t[t:t + 1]),
+                               state=S[None, None])
+        S1 = S1[0, 0]
+        xt = k[t] + lam_t[t] * q[t]
+        a = k[t] @ xt
+        before = np.linalg.norm(v[t] - S.T @ xt)
+        after = np.linalg.norm(v[t] - S1.T @ xt)
+        assert abs(after - abs(1 - beta[t] * a) * before) <= 1e-12 * max(1.0, before)
+        S = S1
+
+
+# ---------------------------------------------------------------------------
+# P11: one beta per value channel ([CH11] §11.3: the module gates each value
+# channel's prediction error with its own beta; §11.4: with a vector write
+# gate the affine update is read column by column of the state)
+
+def _value_beta(x, beta_vec, decay="scalar"):
+    g = np.log(x["alpha"]) if decay == "scalar" else np.log(x["alpha_vec"])
+    o, S = gdr_recurrence(_seq(x["q"]), _seq(x["k"]), _seq(x["v"]), decay=decay, g=_seq(g),
+                          erase="value", write="value", beta=_seq(beta_vec), state=x["S0"][None, None])
+    return o[0, :, 0], S[0, 0]
+
+
+def test_value_beta_matches_page_form():
+    x = _one(T, DK, DV, 60)
+    bv = np.random.default_rng(61).uniform(0, 1, (T, DV))
+    o, S = _value_beta(x, bv)
+    o1, S1 = pf.gdn_value_beta_ch11(x["q"], x["k"], x["v"], x["alpha"], bv, x["S0"])
+    _close(o, o1, 1e-13); _close(S, S1, 1e-13)
+
+
+@pytest.mark.parametrize("decay", ["scalar", "channel"])
+def test_value_beta_is_a_scalar_beta_rule_per_column(decay):
+    x = _one(T, DK, DV, 62)
+    bv = np.random.default_rng(63).uniform(0, 1, (T, DV))
+    o, S = _value_beta(x, bv, decay)
+    for c in range(DV):
+        vc, S0c = x["v"][:, c:c + 1], x["S0"][:, c:c + 1]
+        if decay == "scalar":
+            oc, Sc = pf.gdn_ch11(x["q"], x["k"], vc, x["alpha"], bv[:, c], S0c)
+        else:
+            oc, Sc = pf.kda_kda(x["q"], x["k"], vc, x["alpha_vec"], bv[:, c], S0c.T)
+            Sc = Sc.T
+        _close(o[:, c:c + 1], oc, 1e-13)
+        _close(S[:, c:c + 1], Sc, 1e-13)
+
+
+def test_value_beta_uniform_is_gated_deltanet():
+    x = _one(T, DK, DV, 64)
+    o, S = _value_beta(x, np.repeat(x["beta"][:, None], DV, axis=1))
+    o1, S1 = pf.gdn_ch11(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
+    _close(o, o1, 1e-13); _close(S, S1, 1e-13)
+
+
+def test_value_beta_worked_example():
+    """[CH11] §11.2's example with the per-channel write strength: k = e_1,
+    v = [3, 4], alpha = 1, beta = [1, 1/2].  Row 1 becomes
+    [3, (4 + S[0,1]) / 2] exactly (the first channel overwritten, the second
+    halfway to its target); row 2 is unchanged."""
+    S0 = np.array([[0.625, -1.25], [2.5, 0.375]])
+    k = np.array([[1.0, 0.0]])
+    v = np.array([[3.0, 4.0]])
+    _, S = gdr_recurrence(_seq(k), _seq(k), _seq(v), decay="none", erase="value", write="value",
+                          beta=_seq(np.array([[1.0, 0.5]])), state=S0[None, None])
+    S = S[0, 0]
+    assert S[0, 0] == 3.0 and S[0, 1] == (4.0 + S0[0, 1]) / 2
+    assert np.array_equal(S[1], S0[1])
