@@ -13,6 +13,9 @@ library is missing, importing the functions raises.
     o, state = chunk_fwd(q, k, v, g=g, beta=beta, lam=lam_t)         # Q-Delta, lambda_t [B,T,H]
     o, state = chunk_fwd(q, k, v, g=g, beta=beta_v)                  # beta per value channel [B,T,H,dv]
     o, state = recurrent_step(q1, k1, v1, ..., state=state)          # one token
+    o, state = recurrent_fwd(q, k, v, ..., state=state)              # token loop, short T
+    y, state = chunk_fwd(..., gate=gate, norm_weight=wt)             # + RMSNorm, SiLU gate
+    y = output_norm_gate(o, gate, wt)                                # the epilogue alone
 
 Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g [B,T,H] (scalar decay) or
 [B,T,H,dk] (per-channel decay); beta [B,T,H] (or [B,T,H,dv]: one beta per
@@ -29,7 +32,7 @@ import os
 import torch
 
 from . import _lib
-from ._lib import GdrArgs, GdrPlanInfo, GdrError  # noqa: F401
+from ._lib import GdrArgs, GdrNormArgs, GdrPlanInfo, GdrError  # noqa: F401
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 # bytes of the library's own scratch used by chunk_fwd_noalloc (per device)
@@ -64,10 +67,11 @@ def _check(t, name, dtype=None, ndim=None, device=None):
 
 def build_args(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
                o=None, state_out=None, decay=None, erase=None, write=None, qmix=None,
-               dv_split=0, T=None, workspace=None):
+               dv_split=0, T=None, workspace=None, gate=None, norm_weight=None, norm_eps=0.0):
     """Fill a ``gdr_args`` struct from tensors (no device work).  Kinds are
     inferred from which gates are given unless passed explicitly.
-    ``workspace``: an optional uint8 device tensor for the two-pass form."""
+    ``workspace``: an optional uint8 device tensor for the two-pass form.
+    ``gate``, ``norm_weight``, ``norm_eps``: the optional output epilogue."""
     B, Tq, H, dk = q.shape
     dv = v.shape[3]
     vbeta = beta is not None and beta.dim() == 4
@@ -96,6 +100,9 @@ def build_args(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=No
     a.o = _ptr(o)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    a.out_gate = _ptr(gate)
+    a.norm_weight = _fptr(norm_weight)
+    a.norm_eps = float(norm_eps)
     return a
 
 
@@ -112,6 +119,15 @@ def new_workspace(q, k, v, **kw):
     """A uint8 device tensor of ``workspace_size`` bytes, or None."""
     n = workspace_size(q, k, v, **kw)
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def _check_epilogue(q, v, gate, norm_weight):
+    if gate is None:
+        return
+    _check(gate, "gate", dtype=q.dtype, ndim=4, device=q.device)
+    _check(norm_weight, "norm_weight", dtype=torch.float32, ndim=1, device=q.device)
+    if gate.shape != v.shape or norm_weight.shape[0] != v.shape[3]:
+        raise ValueError(f"gate must be shaped like v {tuple(v.shape)} and norm_weight [dv]")
 
 
 def _prepare(q, k, v, g, beta, b, w, lam, state, decay=None):
@@ -154,7 +170,8 @@ def _stream_ptr(device):
 
 def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
               decay=None, erase=None, write=None, qmix=None, dv_split=0,
-              out=None, state_out=None, workspace=None, two_pass=None):
+              out=None, state_out=None, workspace=None, two_pass=None,
+              gate=None, norm_weight=None, norm_eps=0.0):
     """Chunkwise forward (C = 64) of the generalized gated delta rule.
     Enqueued on the current stream; no synchronisation.
 
@@ -164,8 +181,11 @@ def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=Non
     but its outputs (unless ``out``/``state_out`` are given too).
     ``two_pass``: None lets the workspace decide; False never uses the
     two-pass form; True requires it and, when no workspace is passed,
-    allocates one for this call."""
+    allocates one for this call.
+    ``gate``, ``norm_weight``: the output epilogue (RMSNorm, SiLU gate);
+    the returned tensor then holds y instead of the readout."""
     B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
+    _check_epilogue(q, v, gate, norm_weight)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
                                                              device=q.device)
@@ -184,7 +204,8 @@ def chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=Non
                 raise ValueError(f"workspace has {workspace.numel()} bytes, the two-pass form needs {need}")
             else:
                 ws = workspace
-    a = build_args(q, k, v, o=o, state_out=so, workspace=ws, **kw)
+    a = build_args(q, k, v, o=o, state_out=so, workspace=ws, gate=gate, norm_weight=norm_weight,
+                   norm_eps=norm_eps, **kw)
     _lib.call("gdr_chunk_fwd", a, _stream_ptr(q.device))
     return o, so
 
@@ -206,19 +227,62 @@ def chunk_fwd_noalloc(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, s
 
 
 def recurrent_step(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
-                   decay=None, erase=None, write=None, qmix=None, out=None, state_out=None):
+                   decay=None, erase=None, write=None, qmix=None, out=None, state_out=None,
+                   gate=None, norm_weight=None, norm_eps=0.0):
     """One decode token (T == 1).  ``state_out`` may be ``state`` itself for
     an in-place update."""
     B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
+    _check_epilogue(q, v, gate, norm_weight)
     if T != 1:
         raise ValueError("recurrent_step takes exactly one token (T == 1)")
     o = out if out is not None else torch.empty((B, 1, H, dv), dtype=q.dtype, device=q.device)
     so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
                                                              device=q.device)
     a = build_args(q, k, v, g=g, beta=beta, b=b, w=w, lam=lam, state=state, o=o, state_out=so,
-                   decay=decay, erase=erase, write=write, qmix=qmix)
+                   decay=decay, erase=erase, write=write, qmix=qmix, gate=gate, norm_weight=norm_weight,
+                   norm_eps=norm_eps)
     _lib.call("gdr_recurrent_step", a, _stream_ptr(q.device))
     return o, so
+
+
+def recurrent_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state=None,
+                  decay=None, erase=None, write=None, qmix=None, out=None, state_out=None,
+                  gate=None, norm_weight=None, norm_eps=0.0):
+    """``gdr_recurrent_fwd``: the token loop in one kernel over any T (short
+    sequences), the state in registers; same arguments as ``chunk_fwd``."""
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
+    _check_epilogue(q, v, gate, norm_weight)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    so = state_out if state_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32,
+                                                             device=q.device)
+    a = build_args(q, k, v, g=g, beta=beta, b=b, w=w, lam=lam, state=state, o=o, state_out=so,
+                   decay=decay, erase=erase, write=write, qmix=qmix, gate=gate, norm_weight=norm_weight,
+                   norm_eps=norm_eps)
+    _lib.call("gdr_recurrent_fwd", a, _stream_ptr(q.device))
+    return o, so
+
+
+def output_norm_gate(o, gate, weight, *, eps=0.0, out=None):
+    """``gdr_output_norm_gate``: y = RMSNorm(o) * weight * silu(gate) over the
+    last dimension of o (any leading shape); ``out`` may be ``o`` (in place)."""
+    if o.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _check(o, "o", device=o.device)
+    _check(gate, "gate", dtype=o.dtype, device=o.device)
+    _check(weight, "weight", dtype=torch.float32, ndim=1, device=o.device)
+    if gate.shape != o.shape or weight.shape[0] != o.shape[-1]:
+        raise ValueError("gate must be shaped like o and weight [dv]")
+    y = out if out is not None else torch.empty_like(o)
+    a = GdrNormArgs()
+    a.struct_size = ctypes.sizeof(GdrNormArgs)
+    a.dv = o.shape[-1]
+    a.io = DTYPES[o.dtype]
+    a.eps = float(eps)
+    a.rows = o.numel() // o.shape[-1] if o.numel() else 0
+    a.o, a.gate, a.y = _ptr(o), _ptr(gate), _ptr(y)
+    a.weight = _fptr(weight)
+    _lib.call("gdr_output_norm_gate", a, _stream_ptr(o.device))
+    return y
 
 
 def plan(q, k, v, op="chunk", **kw):
@@ -226,7 +290,7 @@ def plan(q, k, v, op="chunk", **kw):
     call with these tensors would use; host-only."""
     a = build_args(q, k, v, **kw)
     info = GdrPlanInfo()
-    _lib.call("gdr_plan", a, 0 if op == "chunk" else 1, ctypes.byref(info))
+    _lib.call("gdr_plan", a, {"chunk": 0, "step": 1, "recurrent": 2}[op], ctypes.byref(info))
     return dict(grid=info.grid, block=info.block, dv_slice=info.dv_slice, lds_bytes=info.lds_bytes,
                 n_chunks=info.n_chunks, passes=info.passes)
 
@@ -235,5 +299,6 @@ def library_path() -> str:
     return _lib.path()
 
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "recurrent_step", "plan", "build_args", "workspace_size", "new_workspace",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "recurrent_step", "recurrent_fwd",
+           "output_norm_gate", "plan", "build_args", "workspace_size", "new_workspace",
            "library_path", "GdrError"]

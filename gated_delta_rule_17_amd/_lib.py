@@ -8,8 +8,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-EXPORTS = ["gdr_abi_version", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_plan",
-           "gdr_recurrent_step", "gdr_status_str", "gdr_validate", "gdr_workspace_size"]
+EXPORTS = ["gdr_abi_version", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_output_norm_gate",
+           "gdr_plan", "gdr_recurrent_fwd", "gdr_recurrent_step", "gdr_status_str", "gdr_validate",
+           "gdr_workspace_size"]
 
 STATUS = {0: "GDR_OK", 1: "GDR_E_NULL", 2: "GDR_E_SHAPE", 3: "GDR_E_DTYPE", 4: "GDR_E_ALIGN",
           5: "GDR_E_UNSUPPORTED", 6: "GDR_E_HIP", 7: "GDR_E_ARGS"}
@@ -30,7 +31,14 @@ class GdrArgs(ctypes.Structure):
         ("state_in", _FP), ("state_out", _FP),
         ("o", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+        ("out_gate", ctypes.c_void_p), ("norm_weight", _FP), ("norm_eps", ctypes.c_float),
     ]
+
+
+class GdrNormArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dv", ctypes.c_int32), ("io", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rows", ctypes.c_int64),
+                ("o", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("weight", _FP), ("y", ctypes.c_void_p)]
 
 
 class GdrPlanInfo(ctypes.Structure):
@@ -61,7 +69,9 @@ def load():
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python gated_delta_rule_17_amd/csrc/build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
-    for name in ("gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_recurrent_step"):
+    lib.gdr_output_norm_gate.argtypes = [ctypes.POINTER(GdrNormArgs), ctypes.c_void_p]
+    lib.gdr_output_norm_gate.restype = ctypes.c_int
+    for name in ("gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_recurrent_step", "gdr_recurrent_fwd"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(GdrArgs), ctypes.c_void_p]
         fn.restype = ctypes.c_int

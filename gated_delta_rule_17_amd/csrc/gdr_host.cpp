@@ -44,7 +44,7 @@ bool overlap(const Range& a, const Range& b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
-constexpr int kOpChunk = 0, kOpStep = 1;
+constexpr int kOpChunk = 0, kOpStep = 1, kOpRecur = 2;
 
 // bytes of beta: [B,T,H], or [B,T,H,dv] under the per-value-channel beta
 int64_t beta_bytes(const gdr_args* a) {
@@ -56,16 +56,30 @@ int64_t lambda_bytes(const gdr_args* a) {
   return 4 * (a->qmix == 2 ? int64_t(a->B) * a->H * a->T : int64_t(a->H));
 }
 
-// a struct of ABI version 1 ends before the workspace fields
+// a struct of ABI version 1 ends before the workspace fields, one of
+// version 2 before the epilogue fields
 constexpr size_t kArgsV1Size = offsetof(gdr_args, workspace);
+constexpr size_t kArgsV2Size = offsetof(gdr_args, out_gate);
 
 struct Workspace {
   void* ptr;
   uint64_t bytes;
 };
 Workspace workspace_of(const gdr_args* a) {
-  if (a->struct_size < sizeof(gdr_args)) return Workspace{nullptr, 0};
+  if (a->struct_size < kArgsV2Size) return Workspace{nullptr, 0};
   return Workspace{a->workspace, a->workspace ? a->workspace_bytes : 0};
+}
+
+// the output epilogue of a call (gate == nullptr: none)
+struct Epilogue {
+  const void* gate;
+  const float* weight;
+  float eps;
+};
+constexpr float kDefaultEps = 1e-6f;
+Epilogue epilogue_of(const gdr_args* a) {
+  if (a->struct_size < sizeof(gdr_args) || !a->out_gate) return Epilogue{nullptr, nullptr, 0.f};
+  return Epilogue{a->out_gate, a->norm_weight, a->norm_eps > 0.f ? a->norm_eps : kDefaultEps};
 }
 
 // Workspace bytes of the two-pass form for slice width dvs, or 0 when that
@@ -124,7 +138,7 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
   if (a->struct_size < kArgsV1Size)
     return fail(GDR_E_ARGS, "struct_size %u is smaller than the version-1 gdr_args (%zu bytes)", a->struct_size,
                 kArgsV1Size);
-  if (op != kOpChunk && op != kOpStep) return fail(GDR_E_ARGS, "unknown op %d", op);
+  if (op != kOpChunk && op != kOpStep && op != kOpRecur) return fail(GDR_E_ARGS, "unknown op %d", op);
   if (a->B < 1 || a->H < 1 || a->T < 0)
     return fail(GDR_E_SHAPE, "need B >= 1, H >= 1, T >= 0 (got B=%d H=%d T=%d)", a->B, a->H, a->T);
   if (op == kOpStep && a->T != 1) return fail(GDR_E_SHAPE, "the recurrent step needs T == 1 (got %d)", a->T);
@@ -163,6 +177,8 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
     if (a->qmix && !a->lambda) return fail(GDR_E_NULL, "lambda is required by qmix");
   }
   if (a->decay == GDR_DECAY_NONE && a->g) return fail(GDR_E_ARGS, "g given with decay NONE");
+  const Epilogue epi = epilogue_of(a);
+  if (check_ptrs && epi.gate && !epi.weight) return fail(GDR_E_NULL, "norm_weight is required with out_gate");
 
   if (check_ptrs) {
     // alignment
@@ -170,7 +186,8 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
                           a->decay == GDR_DECAY_CHANNEL ? a->g : nullptr};
     for (const void* p : al16)
       if (p && !aligned(p, 16)) return fail(GDR_E_ALIGN, "a tensor pointer is not 16-byte aligned");
-    const void* al4[] = {a->beta, a->lambda, a->g};
+    if (epi.gate && !aligned(epi.gate, 16)) return fail(GDR_E_ALIGN, "out_gate is not 16-byte aligned");
+    const void* al4[] = {a->beta, a->lambda, a->g, epi.weight};
     for (const void* p : al4)
       if (p && !aligned(p, 4)) return fail(GDR_E_ALIGN, "a gate pointer is not 4-byte aligned");
 
@@ -181,7 +198,9 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
                          rng("v", a->v, tokens * a->dv * ioe),     rng("g", a->g, gsz),
                          rng("beta", a->beta, beta_bytes(a)),      rng("b", a->b, tokens * a->dk * 4),
                          rng("w", a->w, tokens * a->dv * 4),       rng("lambda", a->lambda, lambda_bytes(a)),
-                         rng("state_in", a->state_in, BH * a->dk * a->dv * 4)};
+                         rng("state_in", a->state_in, BH * a->dk * a->dv * 4),
+                         rng("out_gate", epi.gate, tokens * a->dv * ioe),
+                         rng("norm_weight", epi.weight, int64_t(a->dv) * 4)};
     const Range ro = rng("o", a->o, tokens * a->dv * ioe);
     const Range rs = rng("state_out", a->state_out, BH * a->dk * a->dv * 4);
     for (const Range& r : ins) {
@@ -213,9 +232,14 @@ gdr_status validate_impl(const gdr_args* a, int op, bool check_ptrs = true) {
       for (int i = 0; i < nc; ++i) ok |= (a->dv % cand[i] == 0);
       if (!ok) return fail(GDR_E_UNSUPPORTED, "no slice width divides dv=%d", a->dv);
     }
-  } else {
+    if (epi.gate && !gdr::norm_gate_supported(a->dv))
+      return fail(GDR_E_UNSUPPORTED, "the chunk path's output epilogue needs dv in {64, 128, 256} (got %d)", a->dv);
+  } else if (op == kOpStep) {
     if (!gdr::step_supported(a->dk, a->dv))
       return fail(GDR_E_UNSUPPORTED, "recurrent step supports dk, dv in {64, 128} (got %d, %d)", a->dk, a->dv);
+  } else {
+    if (!gdr::recur_supported(a->dk, a->dv))
+      return fail(GDR_E_UNSUPPORTED, "the recurrent form supports dk, dv in {64, 128} (got %d, %d)", a->dk, a->dv);
   }
   return GDR_OK;
 }
@@ -230,6 +254,13 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out, Workspace ws
     pi.dv_slice = a->dv;
     pi.lds_bytes = 0;
     pi.n_chunks = 1;
+  } else if (op == kOpRecur) {
+    // one workgroup of dv threads per (batch, head); 16 tokens staged in LDS
+    pi.grid = static_cast<int32_t>(BH);
+    pi.block = a->dv;
+    pi.dv_slice = a->dv;
+    pi.lds_bytes = 4 * 16 * a->dk * 4 + 16 * (a->dv / 64) * 4;
+    pi.n_chunks = 0;
   } else {
     int cand[3];
     const int nc = dvs_candidates(a, cand);
@@ -269,6 +300,16 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out) {
 // The body of the chunk entry points: validation, plan and launch, with the
 // workspace given explicitly (the caller's, or the library's static scratch).
 gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool check_ws);
+
+// the output epilogue of a chunk call: a second kernel over o, in place
+gdr_status chunk_epilogue(const gdr_args* a, hipStream_t st) {
+  const Epilogue epi = epilogue_of(a);
+  if (!epi.gate || a->T == 0) return GDR_OK;
+  const hipError_t e = gdr::launch_norm_gate(a->o, epi.gate, epi.weight, a->o, int64_t(a->B) * a->T * a->H, a->dv,
+                                             a->io == GDR_BF16, epi.eps, st);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "output epilogue launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
 
 // ---- scratch of the no-allocation entry point ------------------------------
 // Device memory of the two-pass records for callers that cannot allocate.
@@ -395,7 +436,7 @@ gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool ch
     if (kernel_for(a) == gdr::kChan) e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
     else e = gdr::launch_pipe_split(gm, p, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
     if (e != hipSuccess) return fail(GDR_E_HIP, "two-pass chunk kernels failed to launch: %s", hipGetErrorString(e));
-    return GDR_OK;
+    return chunk_epilogue(a, st);
   }
   switch (kernel_for(a)) {
     case gdr::kPipe: e = gdr::launch_pipe(gm, p, a->dk, pi.dv_slice, pi.grid, st); break;
@@ -404,7 +445,7 @@ gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool ch
     default: e = gdr::launch_chunk(a->io == GDR_BF16, gm, p, a->dk, pi.dv_slice, chan, pi.grid, st); break;
   }
   if (e != hipSuccess) return fail(GDR_E_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
-  return GDR_OK;
+  return chunk_epilogue(a, st);
 }
 
 }  // namespace
@@ -418,11 +459,56 @@ gdr_status gdr_recurrent_step(const gdr_args* a, void* stream) {
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.g = a->g; p.beta = a->beta; p.b = a->b; p.w = a->w; p.lam = a->lambda;
   p.state_in = a->state_in; p.state_out = a->state_out; p.o = a->o;
+  const Epilogue epi = epilogue_of(a);
+  p.gate = epi.gate; p.nw = epi.weight; p.eps = epi.eps;
   p.B = a->B; p.H = a->H;
   p.decay = a->decay; p.erase = a->erase; p.write = a->write; p.qmix = a->qmix;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = gdr::launch_step(p, a->io == GDR_BF16, a->dk, a->dv, a->B * a->H, st);
   if (e != hipSuccess) return fail(GDR_E_HIP, "step kernel launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_recurrent_fwd(const gdr_args* a, void* stream) {
+  gdr_status s = validate_impl(a, kOpRecur);
+  if (s != GDR_OK) return s;
+  if (a->T == 0 && !a->state_out) return GDR_OK;
+  gdr::RecurParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.g = a->g; p.beta = a->beta; p.b = a->b; p.w = a->w; p.lam = a->lambda;
+  p.state_in = a->state_in; p.state_out = a->state_out; p.o = a->o;
+  const Epilogue epi = epilogue_of(a);
+  p.gate = epi.gate; p.nw = epi.weight; p.eps = epi.eps;
+  p.B = a->B; p.T = a->T; p.H = a->H;
+  p.decay = a->decay; p.erase = a->erase; p.write = a->write; p.qmix = a->qmix;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_recur(p, a->io == GDR_BF16, a->dk, a->dv, a->B * a->H, st);
+  if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent kernel launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_output_norm_gate(const gdr_norm_args* a, void* stream) {
+  if (!a) return fail(GDR_E_NULL, "gdr_norm_args pointer is NULL");
+  if (a->struct_size < sizeof(gdr_norm_args))
+    return fail(GDR_E_ARGS, "struct_size %u is smaller than gdr_norm_args (%zu bytes)", a->struct_size,
+                sizeof(gdr_norm_args));
+  if (a->io != GDR_F32 && a->io != GDR_BF16) return fail(GDR_E_DTYPE, "unknown io dtype %d", a->io);
+  if (a->rows < 0 || a->rows > (int64_t(1) << 40)) return fail(GDR_E_SHAPE, "rows out of range (%lld)",
+                                                                static_cast<long long>(a->rows));
+  if (!gdr::norm_gate_supported(a->dv)) return fail(GDR_E_UNSUPPORTED, "dv must be 64, 128 or 256 (got %d)", a->dv);
+  if (a->rows == 0) return GDR_OK;
+  if (!a->o || !a->gate || !a->weight || !a->y) return fail(GDR_E_NULL, "o, gate, weight and y are required");
+  if (!aligned(a->o, 16) || !aligned(a->gate, 16) || !aligned(a->y, 16) || !aligned(a->weight, 4))
+    return fail(GDR_E_ALIGN, "o, gate and y must be 16-byte aligned, weight 4-byte aligned");
+  const int64_t bytes = a->rows * a->dv * (a->io == GDR_BF16 ? 2 : 4);
+  const Range ry = rng("y", a->y, bytes);
+  const Range ro = rng("o", a->o, bytes), rg = rng("gate", a->gate, bytes), rw = rng("weight", a->weight, a->dv * 4);
+  if ((overlap(ry, ro) && ry.lo != ro.lo) || overlap(ry, rg) || overlap(ry, rw))
+    return fail(GDR_E_ARGS, "y overlaps an input (only y == o exactly is allowed)");
+  const float eps = a->eps > 0.f ? a->eps : kDefaultEps;
+  const hipError_t e = gdr::launch_norm_gate(a->o, a->gate, a->weight, a->y, a->rows, a->dv, a->io == GDR_BF16, eps,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_E_HIP, "output epilogue launch failed: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "chunk_kernel.hpp"
+#include "recur_kernel.hpp"
 #include "step_kernel.hpp"
 
 namespace gdr {
@@ -178,5 +179,15 @@ inline hipError_t launch_chunk(bool bf16io, int gm, const ChunkParams& p, int dk
 // returns hipErrorInvalidValue when (io, dk, dv) has no instance
 hipError_t launch_step(const StepParams& p, int io_bf16, int dk, int dv, int grid, hipStream_t s);
 bool step_supported(int dk, int dv);
+
+// multi-token recurrent kernel (recur_kernel.hpp): one workgroup of dv
+// threads per (batch, head)
+bool recur_supported(int dk, int dv);
+hipError_t launch_recur(const RecurParams& p, bool bf16io, int dk, int dv, int grid, hipStream_t s);
+
+// standalone output epilogue over rows of dv values; y may equal o
+bool norm_gate_supported(int dv);
+hipError_t launch_norm_gate(const void* o, const void* gate, const float* nw, void* y, int64_t rows, int dv,
+                            bool bf16io, float eps, hipStream_t s);
 
 }  // namespace gdr

@@ -1,0 +1,240 @@
+// Fused multi-token recurrent kernel and the output epilogue.
+//
+// Recurrent form: the token loop of the generalized gated delta rule, the
+// "fully recurrent" kernel that the Q-Delta page (key design 3) pairs with
+// the chunked one, for short sequences (prefill of a few tokens, speculative
+// decode, a streaming caller handing its state back in, "Chapter 11 Gated
+// DeltaNet" 11.3).  Per token:
+//   S_bar = Diag(alpha_t) S;  r = S_bar^T e_t;  S = S_bar + k_t (z_t - m_t (.) r)^T;  o_t = S^T q_t
+// with m_t = 1, or the per-value-channel beta of 11.3 (e = k, z = beta (.) v).
+//
+// One workgroup per (batch, head), one thread per value column: thread v
+// keeps column v of the state (all dk rows) in registers for the whole call,
+// so both contractions over the key channels (r and o) are thread-local and
+// a token needs no barrier.  The per-token key-side vectors (alpha, e, k, q)
+// of a block of TB tokens are staged in LDS and read as broadcasts.
+//
+// Output epilogue (11.3: RMSNorm of each head's readout, then the SiLU output
+// gate; the Gated DeltaNet-2 page's method flowchart ends with the same step):
+//   y = o / sqrt(mean_v(o^2) + eps) * weight (.) silu(gate),  silu(x) = x / (1 + exp(-x))
+// fused into the recurrent kernel (the workgroup holds a token's whole
+// readout), and as a standalone kernel over rows of o.
+#pragma once
+
+#include "common.hpp"
+
+namespace gdr {
+
+struct RecurParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* b;
+  const float* w;
+  const float* lam;
+  const float* state_in;
+  float* state_out;
+  void* o;
+  const void* gate;  // epilogue: [B,T,H,dv] io dtype, or nullptr (plain readout)
+  const float* nw;   // epilogue: RMSNorm weight [dv]
+  float eps;
+  int B, T, H;
+  int decay, erase, write, qmix;
+};
+
+__device__ __forceinline__ float ldx(const float* p) { return *p; }
+__device__ __forceinline__ float ldx(const bf16* p) { return (float)*p; }
+
+__device__ __forceinline__ float silu(float x) { return x / (1.f + fexp(-x)); }
+
+// sum over the lanes of a wave (every lane gets the total)
+__device__ __forceinline__ float wave_sum(float s) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s += __shfl_xor(s, m, 64);
+  return s;
+}
+
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
+  constexpr int TB = 16;        // tokens staged per block
+  constexpr int NW = DV / 64;   // waves
+  static_assert(DV % 64 == 0 && DK % 4 == 0, "recurrent layout");
+  __shared__ __attribute__((aligned(16))) float sA[TB][DK], sE[TB][DK], sK[TB][DK], sQ[TB][DK];
+  __shared__ float sP[TB][NW];
+
+  const int v = threadIdx.x, wave = v >> 6;
+  const int bh = blockIdx.x;
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const int T = p.T, H = p.H;
+  const int decay = p.decay, erase = p.erase, write = p.write, qmix = p.qmix;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* qg = reinterpret_cast<const IO*>(p.q);
+  const IO* kg = reinterpret_cast<const IO*>(p.k);
+  const IO* vg = reinterpret_cast<const IO*>(p.v);
+  const IO* gateg = reinterpret_cast<const IO*>(p.gate);
+  IO* og = reinterpret_cast<IO*>(p.o);
+  const bool epi = p.gate != nullptr;
+  const float nwv = epi ? p.nw[v] : 0.f;
+
+  float S[DK];
+#pragma unroll
+  for (int c = 0; c < DK; ++c) S[c] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + v] : 0.f;
+
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    const int nt = min(TB, T - t0);
+    // ---- key side of the block: alpha, e, k, q (zeros and alpha = 1 past T)
+    for (int idx = v; idx < TB * DK; idx += DV) {
+      const int tt = idx / DK, c = idx - tt * DK;
+      float a = 1.f, e = 0.f, kv = 0.f, qv = 0.f;
+      if (tt < nt) {
+        const size_t tok = seq0 + (size_t)(t0 + tt) * H;
+        kv = ldx(kg + tok * DK + c);
+        qv = ldx(qg + tok * DK + c);
+        if (decay == 2) a = fexp(p.g[tok * DK + c]);
+        else if (decay == 1) a = fexp(p.g[tok]);
+        if (erase == 1) e = p.b[tok * DK + c] * kv;
+        else if (erase == 2) e = kv;
+        else e = p.beta[tok] * (qmix ? __builtin_fmaf(qmix == 2 ? p.lam[tok] : p.lam[hh], qv, kv) : kv);
+      }
+      sA[tt][c] = a;
+      sE[tt][c] = e;
+      sK[tt][c] = kv;
+      sQ[tt][c] = qv;
+    }
+    // ---- value side of my column: z and the erase multiplier m
+    float z[TB], m[TB], gt[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      z[tt] = 0.f;
+      m[tt] = 1.f;
+      gt[tt] = 0.f;
+      if (tt < nt) {
+        const size_t tok = seq0 + (size_t)(t0 + tt) * H;
+        const float vv = ldx(vg + tok * DV + v);
+        if (erase == 2) {
+          m[tt] = p.beta[tok * DV + v];
+          z[tt] = m[tt] * vv;
+        } else {
+          z[tt] = (write == 1 ? p.w[tok * DV + v] : p.beta[tok]) * vv;
+        }
+        if (epi) gt[tt] = ldx(gateg + tok * DV + v);
+      }
+    }
+    __syncthreads();
+    float ob[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      ob[tt] = 0.f;
+      if (tt < nt) {
+        // forget, then predict along e
+        float r = 0.f;
+#pragma unroll
+        for (int c = 0; c < DK; c += 4) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[tt][c]);
+          const f32x4 e = *reinterpret_cast<const f32x4*>(&sE[tt][c]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            S[c + u] *= a[u];
+            r = __builtin_fmaf(e[u], S[c + u], r);
+          }
+        }
+        const float d = z[tt] - m[tt] * r;
+        // write along k, then read along q
+        float o = 0.f;
+#pragma unroll
+        for (int c = 0; c < DK; c += 4) {
+          const f32x4 kk = *reinterpret_cast<const f32x4*>(&sK[tt][c]);
+          const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[tt][c]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            S[c + u] = __builtin_fmaf(kk[u], d, S[c + u]);
+            o = __builtin_fmaf(qq[u], S[c + u], o);
+          }
+        }
+        ob[tt] = o;
+      }
+    }
+    if (epi) {
+      // mean of o^2 over the dv columns of each token: wave sums, then the waves'
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const float s = wave_sum(ob[tt] * ob[tt]);
+        if ((v & 63) == 0) sP[tt][wave] = s;
+      }
+    }
+    __syncthreads();  // the block's key-side vectors (and partial sums) are read
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      if (tt < nt) {
+        const size_t tok = seq0 + (size_t)(t0 + tt) * H;
+        float y = ob[tt];
+        if (epi) {
+          float ss = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) ss += sP[tt][w2];
+          y = y * rsqrtf(ss * (1.f / DV) + p.eps) * nwv * silu(gt[tt]);
+        }
+        og[tok * DV + v] = (IO)y;
+      }
+    }
+  }
+  if (p.state_out) {
+#pragma unroll
+    for (int c = 0; c < DK; ++c) p.state_out[((size_t)bh * DK + c) * DV + v] = S[c];
+  }
+}
+
+// Standalone epilogue over `rows` rows of dv values (o and gate [rows][dv],
+// io dtype; y may be o itself).  L lanes share one row, each with 16 bytes
+// of it; 64 / L rows per wave, 4 waves per workgroup.
+template <class IO, int DV>
+__global__ __launch_bounds__(256) void norm_gate_kernel(const IO* o, const IO* gate, const float* nw, IO* y,
+                                                        int64_t rows, float eps) {
+  constexpr int EPL = 16 / sizeof(IO);  // elements per lane
+  constexpr int L = DV / EPL;           // lanes per row
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "epilogue layout");
+  constexpr int RPW = 64 / L;           // rows per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / L, li = lane - sub * L;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * RPW + sub;
+  const bool ok = row < rows;
+  const int64_t base = (ok ? row : 0) * DV + li * EPL;
+  float x[EPL], gg[EPL];
+  if constexpr (sizeof(IO) == 2) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + base);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(gate + base);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      x[i] = (float)a[i];
+      gg[i] = (float)b[i];
+    }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(o + base);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(gate + base);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      x[i] = a[i];
+      gg[i] = b[i];
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) s = __builtin_fmaf(x[i], x[i], s);
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) s += __shfl_xor(s, m, L);
+  const float inv = rsqrtf(s * (1.f / DV) + eps);
+  float out[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) out[i] = x[i] * inv * nw[li * EPL + i] * silu(gg[i]);
+  if (ok) {
+    if constexpr (sizeof(IO) == 2) {
+      st8(y + base, out);
+    } else {
+      *reinterpret_cast<f32x4*>(y + base) = f32x4{out[0], out[1], out[2], out[3]};
+    }
+  }
+}
+
+}  // namespace gdr

@@ -29,6 +29,9 @@ struct StepParams {
   const float* state_in;
   float* state_out;
   void* o;
+  const void* gate;  // output epilogue (RMSNorm, SiLU gate), or nullptr
+  const float* nw;
+  float eps;
   int B, H;
   int decay, erase, write, qmix;
 };
@@ -116,6 +119,20 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     f32x4 ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < RG; ++j) ot += *reinterpret_cast<const f32x4*>(&sR[j][v0]);
+    if (p.gate) {
+      // output epilogue ("Chapter 11", 11.3): the VGN threads of row group 0
+      // hold the whole readout; RMSNorm over it, then the SiLU gate
+      float ss = ot[0] * ot[0] + ot[1] * ot[1] + ot[2] * ot[2] + ot[3] * ot[3];
+#pragma unroll
+      for (int m = 1; m < VGN; m <<= 1) ss += __shfl_xor(ss, m, VGN);
+      const float inv = rsqrtf(ss * (1.f / DV) + p.eps);
+      const IO* gg = reinterpret_cast<const IO*>(p.gate) + to * DV + v0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float gv = (float)gg[u];
+        ot[u] = ot[u] * inv * p.nw[v0 + u] * (gv / (1.f + fexp(-gv)));
+      }
+    }
     gst4(reinterpret_cast<IO*>(p.o) + to * DV + v0, ot);
   }
 }

@@ -35,7 +35,14 @@
  * gdr_chunk_fwd evaluates this with the chunk WY algorithm of [GDN2] key
  * design 2 (chunks of C = 64 tokens; intra-chunk matrices plus an
  * inter-chunk state recurrence), which reaches the token recurrence's result
- * up to rounding.  gdr_recurrent_step applies one token.
+ * up to rounding.  gdr_recurrent_step applies one token; gdr_recurrent_fwd
+ * runs the token loop itself over any T (the fully recurrent form that [QD]
+ * key design 3 pairs with the chunked one), for short sequences.
+ *
+ * Optional output epilogue ([CH11] 11.3; [GDN2] method flowchart): with
+ * out_gate set, every entry point writes, instead of the readout o_t,
+ *     y_t = o_t / sqrt(mean(o_t^2) + eps) (.) norm_weight (.) silu(gate_t)
+ * per (batch, token, head) over the dv channels, silu(x) = x / (1 + e^-x).
  *
  * Caller-side preparation ([GDN2] training strategy, [CH11] 11.3): q and k
  * arrive already L2-normalised (q scaled as the model wants); gates are fp32
@@ -100,10 +107,14 @@ typedef enum gdr_gate { GDR_GATE_BETA = 0, GDR_GATE_CHANNEL = 1, GDR_GATE_VALUE 
  *            (time-varying lambda_t); required iff qmix (then erase must be BETA)
  *   state_in [B,H,dk,dv] fp32, 16-byte aligned, or NULL for a zero state
  *   state_out[B,H,dk,dv] fp32, 16-byte aligned, or NULL (not written)
+ *   out_gate [B,T,H,dv] io dtype, 16-byte aligned, or NULL (no epilogue)
+ *   norm_weight [dv] fp32; required iff out_gate
+ *   norm_eps  RMSNorm epsilon; <= 0 selects 1e-6
  *
  * Fields set to zero select defaults; set struct_size = sizeof(gdr_args).
- * A struct of ABI version 1 (ending at `o`, struct_size = offsetof(gdr_args,
- * workspace)) is accepted and runs without a workspace.
+ * Older structs are accepted: ABI version 1 (ending at `o`, struct_size =
+ * offsetof(gdr_args, workspace)) runs without a workspace, version 2 (ending
+ * at workspace_bytes) without the epilogue.
  * dv_split: 0 lets the library choose how many workgroups share one head's
  * value columns; otherwise the column-slice width (16, 32 or 64, dividing dv).
  * When T == 0, q/k/v/o/gates may be NULL and state_out receives state_in
@@ -140,6 +151,9 @@ typedef struct gdr_args {
   void *o;
   void *workspace;          /* optional, see above; NULL = none */
   uint64_t workspace_bytes; /* bytes available at workspace */
+  const void *out_gate;     /* ABI version 3: output epilogue gate, NULL = none */
+  const float *norm_weight;
+  float norm_eps;
 } gdr_args;
 
 /* What a call would launch (filled by gdr_plan). */
@@ -159,7 +173,9 @@ typedef struct gdr_plan_info {
  * 16..256, divisible by the slice width.  fp32 I/O runs fp32 matrix
  * arithmetic (the tighter fp32 tolerance); the per-value-channel beta and a
  * time-varying lambda run on an all-fp32 kernel with 16-column slices.  Other
- * valid combinations return GDR_E_UNSUPPORTED.
+ * valid combinations return GDR_E_UNSUPPORTED.  The epilogue (out_gate)
+ * needs dv in {64, 128, 256}; it runs as a second kernel over o in place,
+ * because the chunk kernels split a head's value columns over workgroups.
  */
 gdr_status gdr_chunk_fwd(const gdr_args *a, void *stream);
 
@@ -189,19 +205,51 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_args *a, void *stream);
 /*
  * One decode step ([CH11] 11.3: the streaming caller passes the previous
  * final state back in).  Requires T == 1.  io BF16 or F32, dk and dv in
- * {64, 128}.  state_out may equal state_in for an in-place update.
+ * {64, 128}.  state_out may equal state_in for an in-place update.  The
+ * epilogue is fused.
  */
 gdr_status gdr_recurrent_step(const gdr_args *a, void *stream);
+
+/*
+ * The fully recurrent form over any T >= 0 ([QD] key design 3 provides it
+ * beside the chunked kernel; [CH11] 11.3's streaming caller): the token loop
+ * in one kernel, one workgroup per (batch, head), the state in registers for
+ * the whole call.  For short sequences (prefill of a few tokens, speculative
+ * decode); the chunk form is the one for long ones.  Every gate kind and
+ * qmix; io BF16 or F32; dk and dv in {64, 128}.  state_out may equal
+ * state_in.  The epilogue is fused.
+ */
+gdr_status gdr_recurrent_fwd(const gdr_args *a, void *stream);
+
+/*
+ * The output epilogue on its own ([CH11] 11.3): y = o / sqrt(mean(o^2) +
+ * eps) (.) weight (.) silu(gate) over each row of dv values.  o, gate and y
+ * are [rows][dv] in the io dtype, 16-byte aligned; y may be exactly o (in
+ * place) but must not partially overlap o, gate or weight.  dv in {64, 128,
+ * 256}; eps <= 0 selects 1e-6.
+ */
+typedef struct gdr_norm_args {
+  uint32_t struct_size; /* sizeof(gdr_norm_args) */
+  int32_t dv;
+  int32_t io;           /* gdr_dtype */
+  float eps;
+  int64_t rows;         /* >= 0, e.g. B * T * H */
+  const void *o;
+  const void *gate;
+  const float *weight;  /* [dv] fp32 */
+  void *y;
+} gdr_norm_args;
+gdr_status gdr_output_norm_gate(const gdr_norm_args *a, void *stream);
 
 /* Host-only: the workspace bytes that gdr_chunk_fwd can use for `a` (0 when
  * the shape takes no workspace).  Checks `a` like gdr_plan. */
 gdr_status gdr_workspace_size(const gdr_args *a, uint64_t *bytes);
 
-/* Host-only validation of `a` for op 0 (chunk) or 1 (step); launches nothing
- * and touches no device memory, so it runs without a GPU. */
+/* Host-only validation of `a` for op 0 (chunk), 1 (step) or 2 (recurrent);
+ * launches nothing and touches no device memory, so it runs without a GPU. */
 gdr_status gdr_validate(const gdr_args *a, int op);
 
-/* Host-only launch plan for op 0 / 1.  Checks shapes, kinds and the support
+/* Host-only launch plan for op 0 / 1 / 2.  Checks shapes, kinds and the support
  * matrix like gdr_validate but not the pointers (they may be NULL). */
 gdr_status gdr_plan(const gdr_args *a, int op, gdr_plan_info *out);
 

@@ -73,6 +73,11 @@ def make_inputs(cfg: dict) -> dict:
       g_const    use this constant log-decay instead of -softplus(N + c)
       b_scale    erase gate b = b_scale * sigmoid(N)  (e.g. 2 for b in [0, 2])
       lam_const  use this lambda for every head instead of U[0, 1]
+      lam_t      draw one lambda per token, [B, T, H] ~ U[0, 1] (time-varying)
+      value_beta one beta per value channel, [B, T, H, dv] = sigmoid(N)
+                 (erase = write = "value"; replaces beta, b, w)
+      epilogue   also draw the output gate [B, T, H, dv] ~ N(0, 1) (I/O
+                 dtype) and the RMSNorm weight [dv] = 1 + 0.1 N(0, 1) (fp32)
 
     Returns a dict of CPU tensors (q, k, v in the I/O dtype; gates and state in
     fp32; unused gates are None) plus the kind fields.
@@ -81,6 +86,8 @@ def make_inputs(cfg: dict) -> dict:
     decay = cfg.get("decay", decay)
     erase = cfg.get("erase", erase)
     write = cfg.get("write", write)
+    if cfg.get("value_beta"):
+        erase = write = "value"
     qmix = bool(cfg.get("qmix", qmix))
     B, H, T = cfg["B"], cfg["H"], cfg["T"]
     dk = cfg.get("dk", cfg.get("d"))
@@ -100,7 +107,9 @@ def make_inputs(cfg: dict) -> dict:
         q = q * (1.0 / math.sqrt(dk))
 
     beta = b = w = None
-    if erase == "beta" or write == "beta":
+    if erase == "value":
+        beta = torch.sigmoid(randn(B, T, H, dv))
+    elif erase == "beta" or write == "beta":
         beta = torch.sigmoid(randn(B, T, H))
     if erase == "channel":
         b = torch.sigmoid(randn(B, T, H, dk)) * float(cfg.get("b_scale", 1.0))
@@ -119,15 +128,21 @@ def make_inputs(cfg: dict) -> dict:
     if qmix:
         if "lam_const" in cfg:
             lam = torch.full((H,), float(cfg["lam_const"]), dtype=torch.float32)
+        elif cfg.get("lam_t"):
+            lam = torch.rand(B, T, H, generator=gen, dtype=torch.float32)
         else:
             lam = torch.rand(H, generator=gen, dtype=torch.float32)
 
     std = float(cfg.get("state_std", 0.0))
     state = randn(B, H, dk, dv) * std if std > 0 else None
 
-    return dict(q=q.to(io).contiguous(), k=k.to(io).contiguous(), v=v.to(io).contiguous(),
-                g=g, beta=beta, b=b, w=w, lam=lam, state=state,
-                decay=decay, erase=erase, write=write, qmix=qmix)
+    out = dict(q=q.to(io).contiguous(), k=k.to(io).contiguous(), v=v.to(io).contiguous(),
+               g=g, beta=beta, b=b, w=w, lam=lam, state=state,
+               decay=decay, erase=erase, write=write, qmix=qmix)
+    if cfg.get("epilogue"):
+        out["gate"] = randn(B, T, H, dv).to(io).contiguous()
+        out["norm_weight"] = 1.0 + 0.1 * randn(dv)
+    return out
 
 
 def oracle_kwargs(inp: dict) -> dict:

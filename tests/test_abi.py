@@ -10,13 +10,13 @@ import subprocess
 import pytest
 
 from gated_delta_rule_17_amd import _lib
-from gated_delta_rule_17_amd._lib import GdrArgs, GdrPlanInfo
+from gated_delta_rule_17_amd._lib import GdrArgs, GdrNormArgs, GdrPlanInfo
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_HIP, E_ARGS = range(8)
-CHUNK, STEP = 0, 1
+CHUNK, STEP, RECUR = 0, 1, 2
 
 
 @pytest.fixture(scope="module")
@@ -319,3 +319,70 @@ def test_workspace_errors_return_before_launch(lib):
     n = ctypes.c_uint64(0)
     assert lib.gdr_workspace_size(None, ctypes.byref(n)) == E_NULL
     assert lib.gdr_workspace_size(ctypes.byref(a), None) == E_NULL
+
+
+# ---- the recurrent form and the output epilogue -------------------------------
+
+def test_recurrent_form_validation_and_plan(lib):
+    assert _validate(lib, good_args(), RECUR) == OK
+    assert _validate(lib, good_args(T=0, q=0, k=0, v=0, o=0, g=0, beta=0), RECUR) == OK
+    assert _validate(lib, good_args(dk=96), RECUR) == E_UNSUP
+    assert _validate(lib, good_args(dv=256), RECUR) == E_UNSUP
+    assert _validate(lib, good_args(), 3) == E_ARGS
+    info = GdrPlanInfo()
+    a = good_args(B=4, H=8, dv=64)
+    assert lib.gdr_plan(ctypes.byref(a), RECUR, ctypes.byref(info)) == OK
+    assert info.grid == 32 and info.block == 64 and info.dv_slice == 64
+    a = good_args(B=0)
+    assert lib.gdr_recurrent_fwd(ctypes.byref(a), None) == E_SHAPE
+
+
+def test_epilogue_fields(lib):
+    fp = ctypes.POINTER(ctypes.c_float)
+    def epi(**kw):
+        a = good_args(**kw)
+        a.out_gate = _addr(12)
+        a.norm_weight = ctypes.cast(ctypes.c_void_p(_addr(13)), fp)
+        return a
+    for op in (CHUNK, STEP, RECUR):
+        a = epi(T=1 if op == STEP else 200)
+        assert _validate(lib, a, op) == OK, lib.gdr_last_error()
+        a.norm_weight = fp()
+        assert _validate(lib, a, op) == E_NULL
+        a = epi(T=1 if op == STEP else 200)
+        a.out_gate = _addr(12, 8)
+        assert _validate(lib, a, op) == E_ALIGN
+        a = epi(T=1 if op == STEP else 200, o=_addr(12, 64))       # o inside the gate
+        assert _validate(lib, a, op) == E_ARGS
+    assert _validate(lib, epi(dv=192, dv_split=64), CHUNK) == E_UNSUP   # the chunk epilogue: dv 64, 128, 256
+    assert _validate(lib, good_args(dv=192, dv_split=64), CHUNK) == OK
+    # a version-2 struct has no epilogue fields: they are not read
+    a = epi()
+    a.struct_size = GdrArgs.out_gate.offset
+    a.norm_weight = fp()
+    assert _validate(lib, a, CHUNK) == OK
+
+
+def _norm(**kw):
+    a = GdrNormArgs()
+    a.struct_size = ctypes.sizeof(GdrNormArgs)
+    a.dv, a.io, a.eps, a.rows = 128, 1, 0.0, 1000
+    a.o, a.gate, a.y = _addr(0), _addr(1), _addr(2)
+    a.weight = ctypes.cast(ctypes.c_void_p(_addr(3)), ctypes.POINTER(ctypes.c_float))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+def test_output_norm_gate_errors_return_before_launch(lib):
+    f = lib.gdr_output_norm_gate
+    assert f(None, None) == E_NULL
+    assert f(ctypes.byref(_norm(struct_size=8)), None) == E_ARGS
+    assert f(ctypes.byref(_norm(io=5)), None) == E_DTYPE
+    assert f(ctypes.byref(_norm(dv=96)), None) == E_UNSUP
+    assert f(ctypes.byref(_norm(rows=-1)), None) == E_SHAPE
+    assert f(ctypes.byref(_norm(rows=0, o=0, gate=0, y=0)), None) == OK
+    assert f(ctypes.byref(_norm(gate=0)), None) == E_NULL
+    assert f(ctypes.byref(_norm(y=_addr(2, 8))), None) == E_ALIGN
+    assert f(ctypes.byref(_norm(y=_addr(0, 256))), None) == E_ARGS      # partial overlap with o
+    assert f(ctypes.byref(_norm(y=_addr(1))), None) == E_ARGS           # y on the gate
