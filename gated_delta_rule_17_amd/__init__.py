@@ -16,6 +16,7 @@ library is missing, importing the functions raises.
     o, state = recurrent_fwd(q, k, v, ..., state=state)              # token loop, short T
     y, state = chunk_fwd(..., gate=gate, norm_weight=wt)             # + RMSNorm, SiLU gate
     y = output_norm_gate(o, gate, wt)                                # the epilogue alone
+    grads = chunk_bwd(q, k, v, do, g=g, beta=beta, state=S0, dstate=dS)  # backward
 
 Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g [B,T,H] (scalar decay) or
 [B,T,H,dk] (per-channel decay); beta [B,T,H] (or [B,T,H,dv]: one beta per
@@ -32,7 +33,7 @@ import os
 import torch
 
 from . import _lib
-from ._lib import GdrArgs, GdrNormArgs, GdrPlanInfo, GdrError  # noqa: F401
+from ._lib import GdrArgs, GdrBwdArgs, GdrNormArgs, GdrPlanInfo, GdrError  # noqa: F401
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 # bytes of the library's own scratch used by chunk_fwd_noalloc (per device)
@@ -262,6 +263,67 @@ def recurrent_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, lam=None, state
     return o, so
 
 
+def build_bwd_args(fwd_args, do, *, dstate=None, grads=None, workspace=None):
+    """Fill a ``gdr_bwd_args`` struct (no device work).  ``fwd_args`` is a
+    ``GdrArgs`` from ``build_args`` (kept alive by the caller); ``grads`` a
+    dict of fp32 output tensors (dq, dk, dv, dg, dbeta, db, dw, dlam, dstate)."""
+    grads = grads or {}
+    a = GdrBwdArgs()
+    a.struct_size = ctypes.sizeof(GdrBwdArgs)
+    a.fwd = ctypes.pointer(fwd_args)
+    a.d_o = _ptr(do)
+    a.d_state = _fptr(dstate)
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "db", "dw", "dlam", "dstate"):
+        setattr(a, name, _fptr(grads.get(name)))
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    return a
+
+
+def bwd_workspace_size(q, k, v, do, **kw) -> int:
+    """Bytes of workspace ``chunk_bwd`` needs with these tensors (host-only)."""
+    fa = build_args(q, k, v, o=do, **kw)
+    a = build_bwd_args(fa, do)
+    n = ctypes.c_uint64(0)
+    _lib.call("gdr_bwd_workspace_size", a, ctypes.byref(n))
+    return int(n.value)
+
+
+def chunk_bwd(q, k, v, do, *, g=None, beta=None, b=None, w=None, lam=None, state=None, dstate=None,
+              decay=None, erase=None, write=None, qmix=None, grads=None, workspace=None):
+    """``gdr_chunk_bwd``: gradients of every input of ``chunk_fwd`` for the
+    cotangents ``do`` (of o, shaped like v, q's dtype) and ``dstate`` (of the
+    final state, or None).  Returns a dict of fp32 tensors dq, dk, dv and,
+    where the forward uses them, dg, dbeta, db, dw, dlam, and dstate (the
+    gradient of ``state``).  ``grads``: preallocated outputs by name;
+    ``workspace``: a uint8 device tensor of ``bwd_workspace_size()`` bytes
+    (allocated for this call when not given)."""
+    B, T, H, dk, dv = _prepare(q, k, v, g, beta, b, w, lam, state, decay)
+    _check(do, "do", dtype=q.dtype, ndim=4, device=q.device)
+    _check(dstate, "dstate", dtype=torch.float32, device=q.device)
+    if do.shape != v.shape:
+        raise ValueError(f"do must be shaped like v {tuple(v.shape)}")
+    kw = dict(g=g, beta=beta, b=b, w=w, lam=lam, state=state, decay=decay, erase=erase, write=write, qmix=qmix)
+    fa = build_args(q, k, v, o=do, **kw)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = dict(grads or {})
+    out.setdefault("dq", torch.empty((B, T, H, dk), **f32))
+    out.setdefault("dk", torch.empty((B, T, H, dk), **f32))
+    out.setdefault("dv", torch.empty((B, T, H, dv), **f32))
+    out.setdefault("dstate", torch.empty((B, H, dk, dv), **f32))
+    for name, src in (("dg", g), ("db", b), ("dw", w), ("dlam", lam)):
+        if src is not None:
+            out.setdefault(name, torch.empty(src.shape, **f32))
+    if fa.erase == 0 or fa.write == 0:
+        out.setdefault("dbeta", torch.empty((B, T, H), **f32))
+    need = bwd_workspace_size(q, k, v, do, **kw)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = build_bwd_args(fa, do, dstate=dstate, grads=out, workspace=workspace)
+    _lib.call("gdr_chunk_bwd", a, _stream_ptr(q.device))
+    return out
+
+
 def output_norm_gate(o, gate, weight, *, eps=0.0, out=None):
     """``gdr_output_norm_gate``: y = RMSNorm(o) * weight * silu(gate) over the
     last dimension of o (any leading shape); ``out`` may be ``o`` (in place)."""
@@ -300,5 +362,5 @@ def library_path() -> str:
 
 
 __all__ = ["chunk_fwd", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "recurrent_step", "recurrent_fwd",
-           "output_norm_gate", "plan", "build_args", "workspace_size", "new_workspace",
+           "output_norm_gate", "chunk_bwd", "bwd_workspace_size", "build_bwd_args", "plan", "build_args", "workspace_size", "new_workspace",
            "library_path", "GdrError"]

@@ -8,7 +8,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-EXPORTS = ["gdr_abi_version", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_output_norm_gate",
+EXPORTS = ["gdr_abi_version", "gdr_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_output_norm_gate",
            "gdr_plan", "gdr_recurrent_fwd", "gdr_recurrent_step", "gdr_status_str", "gdr_validate",
            "gdr_workspace_size"]
 
@@ -33,6 +33,14 @@ class GdrArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
         ("out_gate", ctypes.c_void_p), ("norm_weight", _FP), ("norm_eps", ctypes.c_float),
     ]
+
+
+class GdrBwdArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("fwd", ctypes.POINTER(GdrArgs)),
+                ("d_o", ctypes.c_void_p), ("d_state", _FP),
+                ("dq", _FP), ("dk", _FP), ("dv", _FP), ("dg", _FP), ("dbeta", _FP), ("db", _FP), ("dw", _FP),
+                ("dlam", _FP), ("dstate", _FP),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class GdrNormArgs(ctypes.Structure):
@@ -69,6 +77,10 @@ def load():
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python gated_delta_rule_17_amd/csrc/build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
+    lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(GdrBwdArgs), ctypes.c_void_p]
+    lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_bwd_workspace_size.argtypes = [ctypes.POINTER(GdrBwdArgs), ctypes.POINTER(ctypes.c_uint64)]
+    lib.gdr_bwd_workspace_size.restype = ctypes.c_int
     lib.gdr_output_norm_gate.argtypes = [ctypes.POINTER(GdrNormArgs), ctypes.c_void_p]
     lib.gdr_output_norm_gate.restype = ctypes.c_int
     for name in ("gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_recurrent_step", "gdr_recurrent_fwd"):

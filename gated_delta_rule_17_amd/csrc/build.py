@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libgdr.so")
 SOURCES = ["chan_gm0.hip", "chan_gm1.hip", "chan_gm2.hip", "chan_gm3.hip", "pipe_gm0.hip", "pipe_gm3.hip",
            "chan_split_gm0.hip", "chan_split_gm1.hip", "chan_split_gm2.hip", "chan_split_gm3.hip",
            "chunk_bf16_gm1.hip", "chunk_bf16_gm2.hip",
-           "chunk_f32.hip", "plain.hip", "recur.hip", "step.hip", "gdr_host.cpp"]
+           "chunk_f32.hip", "plain.hip", "recur.hip", "bwd.hip", "step.hip", "gdr_host.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")

@@ -1,0 +1,41 @@
+// Instances and launch sequence of the backward (bwd_kernel.hpp): io {fp32,
+// bf16} x dk {64, 128} x dv {64, 128}.
+#include "bwd_kernel.hpp"
+#include "launch.hpp"
+
+namespace gdr {
+
+#define GDR_BWD_CASES(X) X(128, 128) X(128, 64) X(64, 128) X(64, 64)
+
+bool bwd_supported(int dk, int dv) {
+#define X(DK, DV) if (dk == DK && dv == DV) return true;
+  GDR_BWD_CASES(X)
+#undef X
+  return false;
+}
+
+template <class IO, int DK, int DV>
+hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
+  const int ns = p.f.nslices, N = p.nchunks;
+  if (N > 0)
+    hipLaunchKernelGGL((plain_fwd_kernel<IO, DK, 16, true>), dim3(BH * ns), dim3(NTHR), 0, s, p.f, p.ws);
+  hipLaunchKernelGGL((bwd_state_kernel<IO, DK, 16>), dim3(BH * ns), dim3(NTHR), 0, s, p);
+  if (N > 0) {
+    hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
+    hipLaunchKernelGGL((bwd_key_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
+  }
+  if (p.f.qmix == 1)
+    hipLaunchKernelGGL(bwd_lam_reduce_kernel, dim3(p.f.H), dim3(256), 0, s, p.ws.dlam, p.dlam, p.f.B, p.f.T, p.f.H);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, bool bf16io, int dk, int dv, int BH, hipStream_t s) {
+#define X(DK, DV)                                                             \
+  if (dk == DK && dv == DV)                                                   \
+    return bf16io ? bwd_sequence<bf16, DK, DV>(p, BH, s) : bwd_sequence<float, DK, DV>(p, BH, s);
+  GDR_BWD_CASES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -1,0 +1,500 @@
+// Backward of the chunkwise forward: gradients of every input for given
+// cotangents dO of the outputs and dS of the final state.
+//
+// The chunk form's backward of "Gated DeltaNet-2: Decoupling Erase and
+// Write in Linear Attention" (key design 3): per chunk, the gradient of the
+// triangular inverse is dT = -tril(A^T dA A^T, -1), and with the per-channel
+// gates the gate weights stay inside the dA products (no scalar can be
+// pulled out of them).  Evaluated here on the regrouped forward of the plain
+// kernel (W = A R, R = Z - E_bar S), where dA = dW R^T and therefore
+//   dR = A^T dW,   dT = -tril(dR W^T, -1),   dZ = dR,   dE_bar = -dR S^T.
+// All arithmetic is fp32.  Four passes, each a kernel on the caller's stream:
+//
+//  0  record  the plain forward in record mode (plain_kernel.hpp): per chunk
+//             the entering state S, W, and T, A_qk, E_bar, Q_gamma, K_tail,
+//             gamma_C to the workspace.
+//  A  state   per (batch, head, 16-column slice), chunks in reverse, the
+//             gradient of the state dS (leaving the chunk) carried in LDS:
+//               dW = A_qk^T dO + K_tail dS
+//               dR = (I + T)^{-T} dW          (backward substitution)
+//               dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR
+//             writes dR and each chunk's incoming dS; the last dS is the
+//             gradient of the initial state.
+//  B1 prod    per (batch, head, chunk): the products over the value channels
+//               dT = -tril(dR W^T, -1), dA_qk = tril(dO W^T),
+//               dE_bar = -dR S^T, dQ_gamma = dO S^T, dK_tail = W dS^T,
+//               sC = rowsum(S (.) dS)
+//  B2 key     per (batch, head, chunk): the decay-weighted sums back to the
+//             rows, with d_ij[c] = exp(G_i[c] - G_j[c]) <= 1,
+//               de_i  = gamma_i dE_bar_i + sum_{j<i}  dT[i][j]  k_j d_ij
+//               dq_i  = gamma_i dQ_gamma_i + sum_{j<=i} dA_qk[i][j] k_j d_ij
+//               dk_j  = tail_j dK_tail_j + sum_{i>j} dT[i][j] e_i d_ij + sum_{i>=j} dA_qk[i][j] q_i d_ij
+//               dG_i  = e_i gamma_i dE_bar_i + q_i gamma_i dQ_gamma_i + e_i P_i + q_i Pq_i - k_i (R_i + Rq_i)
+//             then dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC:
+//             K_tail_j depends on g_t for j < t <= 63 and gamma_C on every
+//             g_t of the chunk, so these enter as a prefix sum and a constant
+//             instead of as pairs of O(1) terms at rows j and 63 that cancel
+//             (in a ragged tail the last valid row has tail = 1); the
+//             diagonal of A_qk (d_ii = 1) likewise stays out of dG.  Then the
+//             gate chain (e = beta (k + lambda q) or b (.) k; z = beta v or w (.) v).
+// A lambda shared by a head's tokens sums its per-token gradients in a
+// final reduction.
+#pragma once
+
+#include "plain_kernel.hpp"
+
+namespace gdr {
+
+
+
+// ---- pass A: the reverse state recurrence ---------------------------------
+template <class IO, int DK, int DVS>
+struct BwdALay {
+  static constexpr int DKP = DK + 1, DVP = DVS + 1, TP = CH + 1;
+  static constexpr int oEb = 0, oQg = oEb + CH * DKP, oKt = oQg + CH * DKP;
+  static constexpr int oT = oKt + CH * DKP, oA = oT + CH * TP;
+  static constexpr int oS = oA + CH * TP;          // [DK][DVP] dS
+  static constexpr int oO = oS + DK * DVP;         // [64][DVP] dO
+  static constexpr int oW = oO + CH * DVP;         // [64][DVP] dW
+  static constexpr int oR = oW + CH * DVP;         // [64][DVP] dR
+  static constexpr int oC = oR + CH * DVP;         // [DK] gamma_C
+  static constexpr int TOTAL = oC + DK;
+  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <class IO, int DK, int DVS>
+__global__ __launch_bounds__(NTHR) void bwd_state_kernel(BwdParams p) {
+  using L = BwdALay<IO, DK, DVS>;
+  constexpr int DKP = L::DKP, DVP = L::DVP, TP = L::TP;
+  static_assert(DVS == 16, "16 columns x 16 lanes in the substitution");
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  float *sEb = lds + L::oEb, *sQg = lds + L::oQg, *sKt = lds + L::oKt, *sT = lds + L::oT, *sA = lds + L::oA;
+  float *sdS = lds + L::oS, *sdO = lds + L::oO, *sdW = lds + L::oW, *sdR = lds + L::oR, *sgC = lds + L::oC;
+
+  const int tid = threadIdx.x;
+  const int NS = p.f.nslices;
+  const int bh = blockIdx.x / NS, slice = blockIdx.x - bh * NS;
+  const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
+  const int T = p.f.T, H = p.f.H, DV = p.f.DV, N = p.nchunks;
+  const int vbase = slice * DVS;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* dog = reinterpret_cast<const IO*>(p.d_o);
+  const BwdWs& ws = p.ws;
+
+  for (int e = tid; e < DK * DVS; e += NTHR) {
+    const int c = e / DVS, v = e - c * DVS;
+    sdS[c * DVP + v] = p.d_st ? p.d_st[((size_t)bh * DK + c) * DV + vbase + v] : 0.f;
+  }
+  for (int n = N - 1; n >= 0; --n) {
+    const size_t ch = (size_t)bh * N + n;
+    const int t0 = n * CH;
+    for (int e = tid; e < CH * DK; e += NTHR) {
+      const int r = e / DK, c = e - r * DK;
+      sEb[r * DKP + c] = ws.Eb[(ch * CH + r) * DK + c];
+      sQg[r * DKP + c] = ws.Qg[(ch * CH + r) * DK + c];
+      sKt[r * DKP + c] = ws.Kt[(ch * CH + r) * DK + c];
+    }
+    for (int e = tid; e < CH * CH; e += NTHR) {
+      const int i = e >> 6, j = e & 63;
+      sT[i * TP + j] = ws.T[ch * CH * CH + e];
+      sA[i * TP + j] = ws.A[ch * CH * CH + e];
+    }
+    for (int e = tid; e < DK; e += NTHR) sgC[e] = ws.gC[ch * DK + e];
+    for (int e = tid; e < CH * DVS; e += NTHR) {
+      const int r = e / DVS, v = e - r * DVS;
+      const int t = t0 + r;
+      sdO[r * DVP + v] = t < T ? ldf(dog + (seq0 + (size_t)t * H) * DV + vbase + v) : 0.f;
+    }
+    // the gradient of the state leaving this chunk, for the product pass
+    for (int e = tid; e < DK * DVS; e += NTHR) {
+      const int c = e / DVS, v = e - c * DVS;
+      ws.dS[(ch * DK + c) * DV + vbase + v] = sdS[c * DVP + v];
+    }
+    __syncthreads();
+    // dW = A_qk^T dO + K_tail dS: row j, 4 columns per thread
+    {
+      const int j = tid >> 2, vq = (tid & 3) * 4;
+      float s[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = j; i < CH; ++i) {
+        const float a = sA[i * TP + j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] = __builtin_fmaf(a, sdO[i * DVP + vq + u], s[u]);
+      }
+      for (int c = 0; c < DK; ++c) {
+        const float kt = sKt[j * DKP + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] = __builtin_fmaf(kt, sdS[c * DVP + vq + u], s[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sdW[j * DVP + vq + u] = s[u];
+    }
+    __syncthreads();
+    // dR solves (I + T)^T dR = dW: backward substitution, column v = tid / 16
+    {
+      const int v = tid >> 4, part = tid & 15;
+      float rreg[4] = {0.f, 0.f, 0.f, 0.f};  // dR[part + 16 m][v]
+      for (int j = CH - 1; j >= 0; --j) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int i = part + 16 * m;
+          if (i > j) s = __builtin_fmaf(sT[i * TP + j], rreg[m], s);
+        }
+        s = sum16(s);
+        const float r = sdW[j * DVP + v] - s;
+        if ((j & 15) == part) rreg[j >> 4] = r;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = part + 16 * m;
+        sdR[i * DVP + v] = rreg[m];
+        ws.dR[(ch * CH + i) * DV + vbase + v] = rreg[m];
+      }
+    }
+    __syncthreads();
+    // dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR: 8 entries of row c per thread
+    {
+      const int c = tid >> 1, v0 = (tid & 1) * 8;
+      if (c < DK) {
+        float s[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] = sgC[c] * sdS[c * DVP + v0 + u];
+        for (int i = 0; i < CH; ++i) {
+          const float qg = sQg[i * DKP + c], eb = sEb[i * DKP + c];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            s[u] = __builtin_fmaf(qg, sdO[i * DVP + v0 + u], s[u]);
+            s[u] = __builtin_fmaf(-eb, sdR[i * DVP + v0 + u], s[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sdS[c * DVP + v0 + u] = s[u];
+      }
+    }
+    __syncthreads();
+  }
+  if (p.dstate) {
+    for (int e = tid; e < DK * DVS; e += NTHR) {
+      const int c = e / DVS, v = e - c * DVS;
+      p.dstate[((size_t)bh * DK + c) * DV + vbase + v] = sdS[c * DVP + v];
+    }
+  }
+}
+
+// ---- pass B1: products over the value channels ----------------------------
+// P[x][y] = sgn * sum_v X[x][v] Y[y][v] for x < 64, y < NY; thread t owns
+// rows 4 (t >> 4) .. +3 and columns (t & 15) * NY/16 .. +NY/16-1.  MASK: 0
+// none, 1 keep y < x (strictly lower), 2 keep y <= x.
+template <int DV, int NY, int MASK>
+__device__ __forceinline__ void prod_rows(const float* X, const float* Y, float sgn, float* out, int ldo) {
+  constexpr int LD = DV + 4, NB = NY / 16;
+  const int tid = threadIdx.x, xb = tid >> 4, yb = tid & 15;
+  float acc[4][NB];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[a][b] = 0.f;
+#pragma unroll 2
+  for (int v = 0; v < DV; v += 4) {
+    f32x4 xr[4], yr[NB];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) xr[a] = *reinterpret_cast<const f32x4*>(X + (4 * xb + a) * LD + v);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) yr[b] = *reinterpret_cast<const f32x4*>(Y + (yb * NB + b) * LD + v);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[a][b] = __builtin_fmaf(xr[a][u], yr[b][u], acc[a][b]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int x = 4 * xb + a, y = yb * NB + b;
+      const bool keep = MASK == 0 || (MASK == 1 ? y < x : y <= x);
+      out[(size_t)x * ldo + y] = keep ? sgn * acc[a][b] : 0.f;
+    }
+}
+
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(NTHR) void bwd_prod_kernel(BwdParams p) {
+  constexpr int LD = DV + 4;
+  constexpr int R2 = (DK > CH ? DK : CH);
+  __shared__ __attribute__((aligned(16))) float lds[(2 * CH + R2) * LD];
+  float* s0 = lds;
+  float* s1 = lds + CH * LD;
+  float* s2 = lds + 2 * CH * LD;
+  const int tid = threadIdx.x;
+  const int N = p.nchunks;
+  const size_t ch = blockIdx.x;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
+  const int T = p.f.T, H = p.f.H;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* dog = reinterpret_cast<const IO*>(p.d_o);
+  const BwdWs& ws = p.ws;
+  auto load = [&](float* dst, const float* src, int rows) {
+    for (int e = tid; e < rows * DV; e += NTHR) {
+      const int r = e / DV, v = e - r * DV;
+      dst[r * LD + v] = src[(size_t)r * DV + v];
+    }
+  };
+  // phase 1: dT = -tril(dR W^T, -1), dA_qk = tril(dO W^T)
+  load(s0, ws.dR + ch * CH * DV, CH);
+  for (int e = tid; e < CH * DV; e += NTHR) {
+    const int r = e / DV, v = e - r * DV;
+    const int t = n * CH + r;
+    s1[r * LD + v] = t < T ? ldf(dog + (seq0 + (size_t)t * H) * DV + v) : 0.f;
+  }
+  load(s2, ws.W + ch * CH * DV, CH);
+  __syncthreads();
+  prod_rows<DV, CH, 1>(s0, s2, -1.f, ws.T + ch * CH * CH, CH);
+  prod_rows<DV, CH, 2>(s1, s2, 1.f, ws.A + ch * CH * CH, CH);
+  __syncthreads();
+  // phase 2: dE_bar = -dR S^T, dQ_gamma = dO S^T
+  load(s2, ws.S + ch * DK * DV, DK);
+  __syncthreads();
+  prod_rows<DV, DK, 0>(s0, s2, -1.f, ws.Eb + ch * CH * DK, DK);
+  prod_rows<DV, DK, 0>(s1, s2, 1.f, ws.Qg + ch * CH * DK, DK);
+  __syncthreads();
+  // phase 3: dK_tail = W dS^T and sum_v S (.) dS
+  load(s0, ws.W + ch * CH * DV, CH);
+  load(s2, ws.dS + ch * DK * DV, DK);
+  __syncthreads();
+  prod_rows<DV, DK, 0>(s0, s2, 1.f, ws.Kt + ch * CH * DK, DK);
+  for (int c = tid; c < DK; c += NTHR) {
+    const float* srow = ws.S + (ch * DK + c) * DV;
+    float s = 0.f;
+    for (int v = 0; v < DV; ++v) s = __builtin_fmaf(srow[v], s2[c * LD + v], s);
+    ws.gC[ch * DK + c] = s;
+  }
+}
+
+// ---- pass B2: back to the rows, the cumulative decay and the gates -----------
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
+  constexpr int NP = NTHR / DK;          // row partitions
+  constexpr int RPP = CH / NP;           // rows per partition
+  constexpr int WPP = DK / 64;           // waves per partition
+  constexpr int VW = DV / 64;            // waves per row of the value side
+  __shared__ __attribute__((aligned(16))) float sK[CH * DK], sE[CH * DK], sQ[CH * DK], sG[CH * DK];
+  __shared__ float sGC[DK], sRb[CH][WPP], sRl[CH][WPP], sRz[CH][VW > 0 ? VW : 1];
+  __shared__ float sBeta[CH], sLam[CH];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int N = p.nchunks;
+  const size_t ch = blockIdx.x;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
+  const int T = p.f.T, H = p.f.H;
+  const int t0 = n * CH;
+  const int decay = p.f.decay, erase = p.f.erase, write = p.f.write, qmix = p.f.qmix;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* qg = reinterpret_cast<const IO*>(p.f.q);
+  const IO* kg = reinterpret_cast<const IO*>(p.f.k);
+  const IO* vg = reinterpret_cast<const IO*>(p.f.v);
+  const BwdWs& ws = p.ws;
+
+  // ---- rows of the chunk (zero past T), gates per token
+  for (int e = tid; e < CH * DK; e += NTHR) {
+    const int r = e / DK, c = e - r * DK;
+    const int t = t0 + r;
+    float kv = 0.f, qv = 0.f, ev = 0.f, gv = 0.f;
+    if (t < T) {
+      const size_t tok = seq0 + (size_t)t * H;
+      kv = ldf(kg + tok * DK + c);
+      qv = ldf(qg + tok * DK + c);
+      if (erase == 1) {
+        ev = p.f.b[tok * DK + c] * kv;
+      } else {
+        float x = kv;
+        if (qmix) x = __builtin_fmaf(qmix == 2 ? p.f.lam[tok] : p.f.lam[hh], qv, kv);
+        ev = p.f.beta[tok] * x;
+      }
+      if (decay == 2) gv = p.f.g[tok * DK + c];
+      else if (decay == 1) gv = p.f.g[tok];
+    }
+    sK[e] = kv;
+    sQ[e] = qv;
+    sE[e] = ev;
+    sG[e] = gv;
+  }
+  for (int r = tid; r < CH; r += NTHR) {
+    const int t = t0 + r;
+    const size_t tok = seq0 + (size_t)t * H;
+    sBeta[r] = (t < T && (erase == 0 || write == 0)) ? p.f.beta[tok] : 0.f;
+    sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
+  }
+  __syncthreads();
+  if (tid < DK) {
+    float run = 0.f;
+    for (int r = 0; r < CH; ++r) {
+      run += sG[r * DK + tid];
+      sG[r * DK + tid] = run;
+    }
+    sGC[tid] = run;
+  }
+  __syncthreads();
+
+  // ---- key side: thread (row partition par, channel c)
+  const int c = tid % DK;
+  const int par = __builtin_amdgcn_readfirstlane(tid / DK);
+  const int wpp = (tid % DK) >> 6;  // my wave within the partition
+  const float* dT = ws.T + ch * CH * CH;
+  const float* dA = ws.A + ch * CH * CH;
+  const float GC = sGC[c];
+  float dGr[RPP], xkt[RPP];
+  for (int m = 0; m < RPP; ++m) {
+    const int i = par + NP * m;  // wave-uniform
+    const float gi = sG[i * DK + c];
+    const float gam = fexp(gi), tl = fexp(GC - gi);
+    const float ki = sK[i * DK + c], ei = sE[i * DK + c], qi = sQ[i * DK + c];
+    const float dEb = ws.Eb[(ch * CH + i) * DK + c];
+    const float dQg = ws.Qg[(ch * CH + i) * DK + c];
+    const float dKt = ws.Kt[(ch * CH + i) * DK + c];
+    // off-diagonal sums (the diagonal of A_qk has d_ii = 1 and does not
+    // depend on G: its two contributions to dG cancel exactly, so it is
+    // kept out of dG rather than added and cancelled in fp32)
+    float P = 0.f, Pq = 0.f, Rm = 0.f, Rq = 0.f;
+    for (int j = 0; j < i; ++j) {
+      const float d = fexp(gi - sG[j * DK + c]);
+      const float kd = sK[j * DK + c] * d;
+      P = __builtin_fmaf(dT[i * CH + j], kd, P);
+      Pq = __builtin_fmaf(dA[i * CH + j], kd, Pq);
+    }
+    for (int i2 = i + 1; i2 < CH; ++i2) {
+      const float d = fexp(sG[i2 * DK + c] - gi);
+      Rm = __builtin_fmaf(dT[i2 * CH + i], sE[i2 * DK + c] * d, Rm);
+      Rq = __builtin_fmaf(dA[i2 * CH + i], sQ[i2 * DK + c] * d, Rq);
+    }
+    const float diag = dA[i * CH + i];
+    const float de = __builtin_fmaf(gam, dEb, P);
+    float dqd = __builtin_fmaf(gam, dQg, __builtin_fmaf(diag, ki, Pq));
+    float dkd = tl * dKt + Rm + __builtin_fmaf(diag, qi, Rq);
+    dGr[m] = ei * gam * dEb + qi * gam * dQg + ei * P + qi * Pq - ki * (Rm + Rq);
+    xkt[m] = ki * tl * dKt;  // K_tail_i dK_tail_i
+    // the erase gate
+    float rb = 0.f, rl = 0.f;
+    const int t = t0 + i;
+    const size_t tok = seq0 + (size_t)(t < T ? t : 0) * H;
+    if (erase == 1) {
+      if (t < T) p.db[tok * DK + c] = de * ki;
+      dkd = __builtin_fmaf(t < T ? p.f.b[tok * DK + c] : 0.f, de, dkd);
+    } else {
+      const float bt = sBeta[i], lt = sLam[i];
+      rb = de * __builtin_fmaf(lt, qi, ki);
+      dkd = __builtin_fmaf(bt, de, dkd);
+      if (qmix) {
+        dqd = __builtin_fmaf(bt * lt, de, dqd);
+        rl = bt * de * qi;
+      }
+    }
+    if (t < T) {
+      p.dq[tok * DK + c] = dqd;
+      p.dk[tok * DK + c] = dkd;
+    }
+    rb = wave_sum(rb);
+    rl = wave_sum(rl);
+    if (lane == 0) {
+      sRb[i][wpp] = rb;
+      sRl[i][wpp] = rl;
+    }
+  }
+  __syncthreads();  // the rows of G, k, e, q are no longer read: sG takes dG, sE the K_tail terms
+#pragma unroll
+  for (int m = 0; m < RPP; ++m) {
+    const int i = par + NP * m;
+    sG[i * DK + c] = dGr[m];
+    sE[i * DK + c] = xkt[m];
+  }
+  __syncthreads();
+  // dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC
+  if (decay != 0 && tid < DK) {
+    float pre = 0.f;
+    for (int r = 0; r < CH; ++r) {  // exclusive prefix of the K_tail terms
+      const float x = sE[r * DK + tid];
+      sE[r * DK + tid] = pre;
+      pre += x;
+    }
+    const float base = fexp(sGC[tid]) * ws.gC[ch * DK + tid];
+    float run = 0.f;
+    for (int r = CH - 1; r >= 0; --r) {
+      run += sG[r * DK + tid];
+      const float dgv = run + sE[r * DK + tid] + base;
+      if (decay == 2) {
+        if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + tid] = dgv;
+      } else {
+        sG[r * DK + tid] = dgv;
+      }
+    }
+  }
+  // ---- value side: dZ = dR
+  {
+    const float* dz = ws.dR + ch * CH * DV;
+    const IO* vrow = vg;
+    for (int e = tid; e < CH * DV; e += NTHR) {
+      const int r = e / DV, v = e - r * DV;
+      const int t = t0 + r;
+      float zb = 0.f;
+      if (t < T) {
+        const size_t tok = seq0 + (size_t)t * H;
+        const float z = dz[e], vv = ldf(vrow + tok * DV + v);
+        if (write == 1) {
+          p.dw[tok * DV + v] = z * vv;
+          p.dv[tok * DV + v] = p.f.w[tok * DV + v] * z;
+        } else {
+          zb = z * vv;
+          p.dv[tok * DV + v] = sBeta[r] * z;
+        }
+      }
+      zb = wave_sum(zb);
+      if (lane == 0 && VW > 0) sRz[r][(v >> 6)] = zb;
+    }
+  }
+  __syncthreads();
+  // ---- per-token sums: the scalar-decay dg, dbeta, dlambda
+  for (int r = tid; r < CH; r += NTHR) {
+    const int t = t0 + r;
+    if (t >= T) continue;
+    const size_t tok = seq0 + (size_t)t * H;
+    if (decay == 1) {
+      float s = 0.f;
+      for (int c2 = 0; c2 < DK; ++c2) s += sG[r * DK + c2];
+      p.dg[tok] = s;
+    }
+    float sb = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < WPP; ++w2) {
+      sb += sRb[r][w2];
+      sl += sRl[r][w2];
+    }
+    if (write == 0) {
+#pragma unroll
+      for (int w2 = 0; w2 < VW; ++w2) sb += sRz[r][w2];
+    }
+    if (erase == 0 || write == 0) p.dbeta[tok] = sb;
+    if (qmix == 2) p.dlam[tok] = sl;
+    else if (qmix == 1) ws.dlam[tok] = sl;
+  }
+}
+
+// ---- a per-head lambda: the sum of its per-token gradients ------------------
+__global__ __launch_bounds__(256) void bwd_lam_reduce_kernel(const float* dlam_t, float* dlam, int B, int T,
+                                                             int H) {
+  __shared__ float part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = (int64_t)B * T;
+  float s = 0.f;
+  for (int64_t i = tid; i < n; i += 256) s += dlam_t[i * H + h];
+  part[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) dlam[h] = part[0];
+}
+
+}  // namespace gdr

@@ -42,6 +42,13 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   return x;
 }
 
+// sum over the lanes of a wave (every lane gets the total)
+__device__ __forceinline__ float wave_sum(float s) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s += __shfl_xor(s, m, 64);
+  return s;
+}
+
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }

@@ -7,10 +7,12 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 
 #include "../../include/gdr.h"
+#include "bwd_params.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -484,6 +486,153 @@ gdr_status gdr_recurrent_fwd(const gdr_args* a, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = gdr::launch_recur(p, a->io == GDR_BF16, a->dk, a->dv, a->B * a->H, st);
   if (e != hipSuccess) return fail(GDR_E_HIP, "recurrent kernel launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// the backward's workspace: fp32 arrays at 256-byte aligned offsets
+struct BwdLayout {
+  int64_t S, W, dR, dS, T, A, Eb, Qg, Kt, gC, dlam, total;
+};
+BwdLayout bwd_layout(const gdr_args* f) {
+  const int64_t BH = int64_t(f->B) * f->H, N = (f->T + GDR_CHUNK - 1) / GDR_CHUNK, NC = BH * N;
+  const int64_t dk = f->dk, dv = f->dv, C = GDR_CHUNK;
+  BwdLayout l{};
+  int64_t off = 0;
+  auto take = [&](int64_t floats) {
+    const int64_t o = off;
+    off += (floats * 4 + 255) / 256 * 256;
+    return o;
+  };
+  l.S = take(NC * dk * dv);
+  l.W = take(NC * C * dv);
+  l.dR = take(NC * C * dv);
+  l.dS = take(NC * dk * dv);
+  l.T = take(NC * C * C);
+  l.A = take(NC * C * C);
+  l.Eb = take(NC * C * dk);
+  l.Qg = take(NC * C * dk);
+  l.Kt = take(NC * C * dk);
+  l.gC = take(NC * dk);
+  l.dlam = take(f->qmix == 1 ? BH * f->T : 0);
+  l.total = off;
+  return l;
+}
+
+gdr_status bwd_validate(const gdr_bwd_args* a, bool check_ptrs, gdr_args* fcopy) {
+  if (!a) return fail(GDR_E_NULL, "gdr_bwd_args pointer is NULL");
+  if (a->struct_size < sizeof(gdr_bwd_args))
+    return fail(GDR_E_ARGS, "struct_size %u is smaller than gdr_bwd_args (%zu bytes)", a->struct_size,
+                sizeof(gdr_bwd_args));
+  if (!a->fwd) return fail(GDR_E_NULL, "fwd (the forward's arguments) is NULL");
+  if (a->fwd->struct_size < kArgsV1Size) return fail(GDR_E_ARGS, "fwd: struct_size too small");
+  // the forward's checks, with d_o in the place of o; no state_out, workspace or epilogue
+  gdr_args f{};
+  std::memcpy(&f, a->fwd, a->fwd->struct_size < sizeof(gdr_args) ? a->fwd->struct_size : sizeof(gdr_args));
+  f.struct_size = sizeof(gdr_args);
+  f.o = const_cast<void*>(a->d_o);
+  f.state_out = nullptr;
+  f.workspace = nullptr;
+  f.workspace_bytes = 0;
+  f.out_gate = nullptr;
+  f.norm_weight = nullptr;
+  f.dv_split = 0;
+  gdr_status s = validate_impl(&f, kOpChunk, check_ptrs);
+  if (s != GDR_OK) return s;
+  if (!gdr::bwd_supported(f.dk, f.dv))
+    return fail(GDR_E_UNSUPPORTED, "the backward supports dk, dv in {64, 128} (got %d, %d)", f.dk, f.dv);
+  if (f.erase == GDR_GATE_VALUE)
+    return fail(GDR_E_UNSUPPORTED, "the backward does not implement the per-value-channel beta");
+  *fcopy = f;
+  if (!check_ptrs) return GDR_OK;
+  const int64_t tokens = int64_t(f.B) * f.H * f.T, BH = int64_t(f.B) * f.H;
+  const bool has_tok = f.T > 0;
+  const bool need_beta = f.erase == GDR_GATE_BETA || f.write == GDR_GATE_BETA;
+  if (has_tok) {
+    if (!a->dq || !a->dk || !a->dv) return fail(GDR_E_NULL, "dq, dk and dv are required when T > 0");
+    if (f.decay != GDR_DECAY_NONE && !a->dg) return fail(GDR_E_NULL, "dg is required with a decay");
+    if (need_beta && !a->dbeta) return fail(GDR_E_NULL, "dbeta is required by a BETA gate");
+    if (f.erase == GDR_GATE_CHANNEL && !a->db) return fail(GDR_E_NULL, "db is required by erase CHANNEL");
+    if (f.write == GDR_GATE_CHANNEL && !a->dw) return fail(GDR_E_NULL, "dw is required by write CHANNEL");
+  }
+  if (f.qmix && !a->dlam) return fail(GDR_E_NULL, "dlam is required by qmix");
+  const void* al4[] = {a->dq, a->dk, a->dv, a->dg, a->dbeta, a->db, a->dw, a->dlam, a->dstate, a->d_state};
+  for (const void* p : al4)
+    if (p && !aligned(p, 4)) return fail(GDR_E_ALIGN, "a gradient pointer is not 4-byte aligned");
+  if (a->d_state && !aligned(a->d_state, 16)) return fail(GDR_E_ALIGN, "d_state is not 16-byte aligned");
+  const BwdLayout l = bwd_layout(&f);
+  if (has_tok) {
+    if (!a->workspace || a->workspace_bytes < static_cast<uint64_t>(l.total))
+      return fail(GDR_E_ARGS, "the backward needs a workspace of %lld bytes", static_cast<long long>(l.total));
+    if (!aligned(a->workspace, 256)) return fail(GDR_E_ALIGN, "workspace is not 256-byte aligned");
+  }
+  const int64_t ioe = f.io == GDR_BF16 ? 2 : 4;
+  const int64_t gsz = f.decay == GDR_DECAY_CHANNEL ? tokens * f.dk * 4 : tokens * 4;
+  const Range ins[] = {rng("q", f.q, tokens * f.dk * ioe),      rng("k", f.k, tokens * f.dk * ioe),
+                       rng("v", f.v, tokens * f.dv * ioe),      rng("g", f.g, gsz),
+                       rng("beta", f.beta, beta_bytes(&f)),     rng("b", f.b, tokens * f.dk * 4),
+                       rng("w", f.w, tokens * f.dv * 4),        rng("lambda", f.lambda, lambda_bytes(&f)),
+                       rng("state_in", f.state_in, BH * f.dk * f.dv * 4),
+                       rng("d_o", a->d_o, tokens * f.dv * ioe), rng("d_state", a->d_state, BH * f.dk * f.dv * 4)};
+  const Range outs[] = {rng("dq", a->dq, tokens * f.dk * 4),    rng("dk", a->dk, tokens * f.dk * 4),
+                        rng("dv", a->dv, tokens * f.dv * 4),    rng("dg", a->dg, gsz),
+                        rng("dbeta", a->dbeta, tokens * 4),     rng("db", a->db, tokens * f.dk * 4),
+                        rng("dw", a->dw, tokens * f.dv * 4),    rng("dlam", a->dlam, lambda_bytes(&f)),
+                        rng("dstate", a->dstate, BH * f.dk * f.dv * 4),
+                        rng("workspace", a->workspace, has_tok ? l.total : 0)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(GDR_E_ARGS, "%s overlaps input %s", outs[i].name, r.name);
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDR_E_ARGS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_bwd_workspace_size(const gdr_bwd_args* a, uint64_t* bytes) {
+  if (!bytes) return fail(GDR_E_NULL, "bytes pointer is NULL");
+  *bytes = 0;
+  gdr_args f;
+  gdr_status s = bwd_validate(a, false, &f);
+  if (s != GDR_OK) return s;
+  *bytes = f.T > 0 ? static_cast<uint64_t>(bwd_layout(&f).total) : 0;
+  return GDR_OK;
+}
+
+gdr_status gdr_chunk_bwd(const gdr_bwd_args* a, void* stream) {
+  gdr_args f;
+  gdr_status s = bwd_validate(a, true, &f);
+  if (s != GDR_OK) return s;
+  gdr::BwdParams p{};
+  p.f.q = f.q; p.f.k = f.k; p.f.v = f.v;
+  p.f.g = f.g; p.f.beta = f.beta; p.f.b = f.b; p.f.w = f.w; p.f.lam = f.lambda;
+  p.f.state_in = f.state_in; p.f.state_out = nullptr; p.f.o = nullptr;
+  p.f.B = f.B; p.f.T = f.T; p.f.H = f.H; p.f.DV = f.dv;
+  p.f.decay = f.decay; p.f.erase = f.erase; p.f.write = f.write; p.f.qmix = f.qmix;
+  p.f.nslices = f.dv / 16;
+  p.d_o = a->d_o;
+  p.d_st = a->d_state;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv; p.dg = a->dg; p.dbeta = a->dbeta; p.db = a->db; p.dw = a->dw;
+  p.dlam = a->dlam; p.dstate = a->dstate;
+  p.nchunks = (f.T + GDR_CHUNK - 1) / GDR_CHUNK;
+  if (f.T > 0) {
+    const BwdLayout l = bwd_layout(&f);
+    char* base = static_cast<char*>(a->workspace);
+    auto at = [&](int64_t off) { return reinterpret_cast<float*>(base + off); };
+    p.ws = gdr::BwdWs{at(l.S), at(l.W), at(l.dR), at(l.dS), at(l.T), at(l.A), at(l.Eb), at(l.Qg), at(l.Kt),
+                      at(l.gC), at(l.dlam)};
+  }
+  if (!a->dstate && p.nchunks == 0 && f.qmix != 1) return GDR_OK;
+  const hipError_t e = gdr::launch_bwd(p, f.io == GDR_BF16, f.dk, f.dv, f.B * f.H,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_E_HIP, "backward kernels failed to launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 

@@ -185,6 +185,12 @@ bool step_supported(int dk, int dv);
 bool recur_supported(int dk, int dv);
 hipError_t launch_recur(const RecurParams& p, bool bf16io, int dk, int dv, int grid, hipStream_t s);
 
+// backward (bwd_kernel.hpp): record pass, reverse state pass, product and
+// key passes, and the per-head lambda reduction, on one stream
+struct BwdParams;
+bool bwd_supported(int dk, int dv);
+hipError_t launch_bwd(const BwdParams& p, bool bf16io, int dk, int dv, int BH, hipStream_t s);
+
 // standalone output epilogue over rows of dv values; y may equal o
 bool norm_gate_supported(int dv);
 hipError_t launch_norm_gate(const void* o, const void* gate, const float* nw, void* y, int64_t rows, int dv,

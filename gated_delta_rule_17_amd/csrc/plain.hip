@@ -17,8 +17,8 @@ int plain_lds(int dk) {
 hipError_t launch_plain(const ChunkParams& p, bool bf16io, int dk, int grid, hipStream_t s) {
 #define X(DK)                                                                                   \
   if (dk == DK) {                                                                               \
-    if (bf16io) hipLaunchKernelGGL((plain_fwd_kernel<bf16, DK, 16>), dim3(grid), dim3(NTHR), 0, s, p); \
-    else hipLaunchKernelGGL((plain_fwd_kernel<float, DK, 16>), dim3(grid), dim3(NTHR), 0, s, p);   \
+    if (bf16io) hipLaunchKernelGGL((plain_fwd_kernel<bf16, DK, 16>), dim3(grid), dim3(NTHR), 0, s, p, BwdWs{}); \
+    else hipLaunchKernelGGL((plain_fwd_kernel<float, DK, 16>), dim3(grid), dim3(NTHR), 0, s, p, BwdWs{});   \
     return hipGetLastError();                                                                   \
   }
   GDR_PLAIN_CASES(X)

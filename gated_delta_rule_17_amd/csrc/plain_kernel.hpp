@@ -32,11 +32,18 @@
 // One workgroup (4 waves) owns one (batch, head) and a slice of DVS = 16
 // value columns; chunks are walked in order, the slice of the state stays in
 // LDS.  q, k, e, G rows of the chunk are staged in LDS as fp32.
+//
+// Record mode (REC) is the first pass of the backward: instead of o it
+// writes, per chunk, what the reverse passes read back (see bwd_kernel.hpp):
+// the entering state and W (each slice its columns), and, from slice 0, T,
+// A_qk, E_bar, Q_gamma, K_tail and gamma_C.
 #pragma once
 
+#include "bwd_params.hpp"
 #include "chunk_kernel.hpp"
 
 namespace gdr {
+
 
 template <int DK, int DVS>
 struct PlainLay {
@@ -82,8 +89,8 @@ __device__ __forceinline__ float sum16(float s) {
   return s;
 }
 
-template <class IO, int DK, int DVS>
-__global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p) {
+template <class IO, int DK, int DVS, bool REC = false>
+__global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p, BwdWs ws) {
   using L = PlainLay<DK, DVS>;
   constexpr int DKP = L::DKP, DVP = L::DVP, TP = L::TP;
   static_assert(DVS == 16, "the substitution maps 16 columns x 16 lanes onto the workgroup");
@@ -125,6 +132,13 @@ __global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p) {
 
   for (int n = 0; n < nchunks; ++n) {
     const int t0 = n * CH;
+    const size_t ch = (size_t)bh * nchunks + n;
+    if constexpr (REC) {
+      for (int e = tid; e < DK * DVS; e += NTHR) {
+        const int c = e / DVS, v = e - c * DVS;
+        ws.S[(ch * DK + c) * DV + vbase + v] = sS[c * DVP + v];
+      }
+    }
     // ---- rows of the chunk: k, q, e and the log-decay (zero past T) -------
     for (int e = tid; e < CH * DK; e += NTHR) {
       const int r = e / DK, c = e - r * DK;
@@ -181,6 +195,18 @@ __global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p) {
       }
     }
     __syncthreads();
+    if constexpr (REC) {
+      if (slice == 0) {
+        for (int e = tid; e < CH * DK; e += NTHR) {
+          const int r = e / DK, c = e - r * DK;
+          const float G = sG[r * DKP + c], GC = sG[(CH - 1) * DKP + c], gam = fexp(G);
+          ws.Eb[(ch * CH + r) * DK + c] = sX[r * DKP + c] * gam;
+          ws.Qg[(ch * CH + r) * DK + c] = sQ[r * DKP + c] * gam;
+          ws.Kt[(ch * CH + r) * DK + c] = sK[r * DKP + c] * fexp(GC - G);
+          if (r == 0) ws.gC[ch * DK + c] = fexp(GC);
+        }
+      }
+    }
 
     // ---- Gram: T and A_qk, 4 x 4 (i, j) blocks per thread ----------------
     float accT[4][4], accA[4][4];
@@ -240,6 +266,15 @@ __global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p) {
       sQS[ri * DVP + vq + u] = qs[u];
     }
     __syncthreads();
+    if constexpr (REC) {
+      if (slice == 0) {
+        for (int e = tid; e < CH * CH; e += NTHR) {
+          const int i = e >> 6, j = e & 63;
+          ws.T[ch * CH * CH + e] = sT[i * TP + j];
+          ws.A[ch * CH * CH + e] = sAqk[i * TP + j];
+        }
+      }
+    }
 
     // ---- W: forward substitution, column v = tid / 16, lanes split j ------
     {
@@ -257,7 +292,10 @@ __global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p) {
         if ((i & 15) == part) wreg[i >> 4] = w;
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) sW[(part + 16 * m) * DVP + v] = wreg[m];
+      for (int m = 0; m < 4; ++m) {
+        sW[(part + 16 * m) * DVP + v] = wreg[m];
+        if constexpr (REC) ws.W[(ch * CH + part + 16 * m) * DV + vbase + v] = wreg[m];
+      }
     }
     __syncthreads();
 
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p) {
         for (int u = 0; u < 4; ++u) o[u] = __builtin_fmaf(a, sW[j * DVP + vq + u], o[u]);
       }
       const int t = t0 + ri;
-      if (t < T) {
+      if (!REC && t < T) {
         IO* op = og + (seq0 + (size_t)t * H) * DV + vbase + vq;
 #pragma unroll
         for (int u = 0; u < 4; ++u) op[u] = (IO)o[u];

@@ -49,13 +49,6 @@ __device__ __forceinline__ float ldx(const bf16* p) { return (float)*p; }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + fexp(-x)); }
 
-// sum over the lanes of a wave (every lane gets the total)
-__device__ __forceinline__ float wave_sum(float s) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) s += __shfl_xor(s, m, 64);
-  return s;
-}
-
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
   constexpr int TB = 16;        // tokens staged per block

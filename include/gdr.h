@@ -241,6 +241,45 @@ typedef struct gdr_norm_args {
 } gdr_norm_args;
 gdr_status gdr_output_norm_gate(const gdr_norm_args *a, void *stream);
 
+/*
+ * Backward of the chunkwise forward ([GDN2] key design 3: the chunk form's
+ * backward, with dT = -tril(A^T dA A^T, -1) and the gate weights inside the
+ * dA products): for a loss L with dL/do = d_o and dL/dS_final = d_state,
+ * the gradients of every input of the forward call `fwd`.
+ *
+ *   fwd       the forward's arguments (q, k, v, gates, kinds, state_in);
+ *             its o, state_out, workspace and epilogue fields are not read
+ *             (the gradient is the one of the readout o, before any epilogue)
+ *   d_o       [B,T,H,dv] io dtype, 16-byte aligned
+ *   d_state   [B,H,dk,dv] fp32, or NULL (zero)
+ *   dq, dk    [B,T,H,dk] fp32, written        dv  [B,T,H,dv] fp32, written
+ *   dg        like g (SCALAR [B,T,H], CHANNEL [B,T,H,dk]); iff a decay
+ *   dbeta     [B,T,H]; iff beta is used       db  [B,T,H,dk]; iff erase CHANNEL
+ *   dw        [B,T,H,dv]; iff write CHANNEL   dlam [H] (qmix 1) or [B,T,H] (qmix 2)
+ *   dstate    [B,H,dk,dv] fp32 or NULL: the gradient of state_in
+ *   workspace >= gdr_bwd_workspace_size() bytes, 256-byte aligned (required
+ *             when T > 0): the per-chunk states and factors the reverse
+ *             passes read back (about 320 KiB per (batch, head, chunk) at
+ *             dk = dv = 128)
+ * Outputs are fp32 and must overlap neither the inputs nor each other.
+ * Supported: io BF16 or F32, dk and dv in {64, 128}, every decay, the BETA
+ * and CHANNEL gates and qmix; the per-value-channel beta returns
+ * GDR_E_UNSUPPORTED.  All arithmetic is fp32.  Deterministic (no atomics).
+ */
+typedef struct gdr_bwd_args {
+  uint32_t struct_size;     /* sizeof(gdr_bwd_args) */
+  const gdr_args *fwd;
+  const void *d_o;
+  const float *d_state;
+  float *dq, *dk, *dv, *dg, *dbeta, *db, *dw, *dlam, *dstate;
+  void *workspace;
+  uint64_t workspace_bytes;
+} gdr_bwd_args;
+gdr_status gdr_chunk_bwd(const gdr_bwd_args *a, void *stream);
+
+/* Host-only: the workspace bytes gdr_chunk_bwd needs for `a`. */
+gdr_status gdr_bwd_workspace_size(const gdr_bwd_args *a, uint64_t *bytes);
+
 /* Host-only: the workspace bytes that gdr_chunk_fwd can use for `a` (0 when
  * the shape takes no workspace).  Checks `a` like gdr_plan. */
 gdr_status gdr_workspace_size(const gdr_args *a, uint64_t *bytes);

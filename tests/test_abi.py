@@ -386,3 +386,48 @@ def test_output_norm_gate_errors_return_before_launch(lib):
     assert f(ctypes.byref(_norm(y=_addr(2, 8))), None) == E_ALIGN
     assert f(ctypes.byref(_norm(y=_addr(0, 256))), None) == E_ARGS      # partial overlap with o
     assert f(ctypes.byref(_norm(y=_addr(1))), None) == E_ARGS           # y on the gate
+
+
+# ---- the backward ---------------------------------------------------------------
+
+def _bwd(lib, fwd, **kw):
+    from gated_delta_rule_17_amd._lib import GdrBwdArgs
+    fp = ctypes.POINTER(ctypes.c_float)
+    a = GdrBwdArgs()
+    a.struct_size = ctypes.sizeof(GdrBwdArgs)
+    a.fwd = ctypes.pointer(fwd)
+    a.d_o = _addr(20)
+    for i, name in enumerate(("dq", "dk", "dv", "dg", "dbeta", "dstate")):
+        setattr(a, name, ctypes.cast(ctypes.c_void_p(_addr(21 + i)), fp))
+    a.workspace, a.workspace_bytes = _addr(40), 1 << 40
+    for key, val in kw.items():
+        if key in ("dq", "dk", "dv", "dg", "dbeta", "db", "dw", "dlam", "dstate", "d_state"):
+            val = ctypes.cast(ctypes.c_void_p(val), fp) if val else fp()
+        setattr(a, key, val)
+    return a
+
+
+def test_backward_workspace_and_validation(lib):
+    from gated_delta_rule_17_amd._lib import GdrBwdArgs  # noqa: F401
+    f = good_args(B=2, H=4, T=200, o=0)
+    a = _bwd(lib, f)
+    n = ctypes.c_uint64(0)
+    assert lib.gdr_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == OK, lib.gdr_last_error()
+    # per chunk-head: S, dS (dk dv), W, dR (64 dv), T, A (64 x 64), E_bar, Q_gamma, K_tail (64 dk), gamma_C (dk)
+    per = (2 * 128 * 128 + 2 * 64 * 128 + 2 * 64 * 64 + 3 * 64 * 128 + 128) * 4
+    assert n.value == 2 * 4 * 4 * per
+    f.erase = f.write = 2                       # per-value-channel beta: no backward
+    assert lib.gdr_bwd_workspace_size(ctypes.byref(_bwd(lib, f)), ctypes.byref(n)) == E_UNSUP
+    f = good_args(B=2, H=4, T=200, o=0, dk=96)
+    assert lib.gdr_bwd_workspace_size(ctypes.byref(_bwd(lib, f)), ctypes.byref(n)) == E_UNSUP
+    # error paths of gdr_chunk_bwd, all before any launch
+    f = good_args(B=2, H=4, T=200, o=0)
+    assert lib.gdr_chunk_bwd(None, None) == E_NULL
+    assert lib.gdr_chunk_bwd(ctypes.byref(_bwd(lib, f, dg=0)), None) == E_NULL
+    assert lib.gdr_chunk_bwd(ctypes.byref(_bwd(lib, f, workspace_bytes=16)), None) == E_ARGS
+    assert lib.gdr_chunk_bwd(ctypes.byref(_bwd(lib, f, workspace=_addr(40, 64))), None) == E_ALIGN
+    assert lib.gdr_chunk_bwd(ctypes.byref(_bwd(lib, f, dq=_addr(0))), None) == E_ARGS      # dq on q
+    assert lib.gdr_chunk_bwd(ctypes.byref(_bwd(lib, f, dk=_addr(21, 128))), None) == E_ARGS  # dk inside dq
+    f.qmix = 1
+    f.lambda_ = ctypes.cast(ctypes.c_void_p(_addr(8)), ctypes.POINTER(ctypes.c_float))
+    assert lib.gdr_chunk_bwd(ctypes.byref(_bwd(lib, f)), None) == E_NULL                   # dlam missing
