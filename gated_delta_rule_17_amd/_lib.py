@@ -6,7 +6,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libgdr.so")
+# GDR_LIBRARY selects another build of the library (e.g. the sanitized one)
+_LIB_PATH = os.environ.get("GDR_LIBRARY") or os.path.join(_HERE, "libgdr.so")
 
 EXPORTS = ["gdr_abi_version", "gdr_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_output_norm_gate",
            "gdr_plan", "gdr_recurrent_fwd", "gdr_recurrent_step", "gdr_status_str", "gdr_validate",

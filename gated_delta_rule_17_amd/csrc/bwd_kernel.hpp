@@ -47,6 +47,26 @@ namespace gdr {
 
 
 
+// rows x COLS fp32 from global memory (row stride COLS) to LDS (row stride
+// LD), four floats per load, the loads of up to 8 quads per thread issued
+// together
+template <int ROWS, int COLS, int LD>
+__device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid) {
+  constexpr int QPR = COLS / 4, NQ = ROWS * QPR / NTHR, UB = NQ < 8 ? NQ : 8;
+  static_assert(NQ * NTHR == ROWS * QPR && NQ % UB == 0, "copy layout");
+  for (int u0 = 0; u0 < NQ; u0 += UB) {
+    f32x4 x[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) x[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(tid + NTHR * (u0 + u)) * 4);
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int e = tid + NTHR * (u0 + u), r = e / QPR, c4 = (e - r * QPR) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[r * LD + c4 + i] = x[u][i];
+    }
+  }
+}
+
 // ---- pass A: the reverse state recurrence ---------------------------------
 template <class IO, int DK, int DVS>
 struct BwdALay {
@@ -88,22 +108,27 @@ __global__ __launch_bounds__(NTHR) void bwd_state_kernel(BwdParams p) {
   for (int n = N - 1; n >= 0; --n) {
     const size_t ch = (size_t)bh * N + n;
     const int t0 = n * CH;
-    for (int e = tid; e < CH * DK; e += NTHR) {
-      const int r = e / DK, c = e - r * DK;
-      sEb[r * DKP + c] = ws.Eb[(ch * CH + r) * DK + c];
-      sQg[r * DKP + c] = ws.Qg[(ch * CH + r) * DK + c];
-      sKt[r * DKP + c] = ws.Kt[(ch * CH + r) * DK + c];
-    }
-    for (int e = tid; e < CH * CH; e += NTHR) {
-      const int i = e >> 6, j = e & 63;
-      sT[i * TP + j] = ws.T[ch * CH * CH + e];
-      sA[i * TP + j] = ws.A[ch * CH * CH + e];
-    }
+    // the chunk's factors from the record pass: four floats per load, every
+    // load of a loop issued before its LDS stores
+    copy_rows<CH, DK, DKP>(sEb, ws.Eb + ch * CH * DK, tid);
+    copy_rows<CH, DK, DKP>(sQg, ws.Qg + ch * CH * DK, tid);
+    copy_rows<CH, DK, DKP>(sKt, ws.Kt + ch * CH * DK, tid);
+    copy_rows<CH, CH, TP>(sT, ws.T + ch * CH * CH, tid);
+    copy_rows<CH, CH, TP>(sA, ws.A + ch * CH * CH, tid);
     for (int e = tid; e < DK; e += NTHR) sgC[e] = ws.gC[ch * DK + e];
-    for (int e = tid; e < CH * DVS; e += NTHR) {
-      const int r = e / DVS, v = e - r * DVS;
-      const int t = t0 + r;
-      sdO[r * DVP + v] = t < T ? ldf(dog + (seq0 + (size_t)t * H) * DV + vbase + v) : 0.f;
+    {
+      constexpr int NV = CH * DVS / NTHR;
+      float rv[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + NTHR * u, r = e / DVS, v = e - r * DVS;
+        rv[u] = ldf(dog + (seq0 + (size_t)min(t0 + r, T - 1) * H) * DV + vbase + v);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + NTHR * u, r = e / DVS, v = e - r * DVS;
+        sdO[r * DVP + v] = t0 + r < T ? rv[u] : 0.f;
+      }
     }
     // the gradient of the state leaving this chunk, for the product pass
     for (int e = tid; e < DK * DVS; e += NTHR) {
@@ -235,33 +260,38 @@ __global__ __launch_bounds__(NTHR) void bwd_prod_kernel(BwdParams p) {
   const size_t seq0 = (size_t)bb * T * H + hh;
   const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   const BwdWs& ws = p.ws;
-  auto load = [&](float* dst, const float* src, int rows) {
-    for (int e = tid; e < rows * DV; e += NTHR) {
-      const int r = e / DV, v = e - r * DV;
-      dst[r * LD + v] = src[(size_t)r * DV + v];
-    }
-  };
   // phase 1: dT = -tril(dR W^T, -1), dA_qk = tril(dO W^T)
-  load(s0, ws.dR + ch * CH * DV, CH);
-  for (int e = tid; e < CH * DV; e += NTHR) {
-    const int r = e / DV, v = e - r * DV;
-    const int t = n * CH + r;
-    s1[r * LD + v] = t < T ? ldf(dog + (seq0 + (size_t)t * H) * DV + v) : 0.f;
+  copy_rows<CH, DV, LD>(s0, ws.dR + ch * CH * DV, tid);
+  {
+    constexpr int QPR = DV / 4, NQ = CH * QPR / NTHR;
+    f32x4 x[NQ];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = tid + NTHR * u, r = e / QPR, c4 = (e - r * QPR) * 4;
+      x[u] = ldf4(dog + (seq0 + (size_t)min(n * CH + r, T - 1) * H) * DV + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = tid + NTHR * u, r = e / QPR, c4 = (e - r * QPR) * 4;
+      const bool ok = n * CH + r < T;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s1[r * LD + c4 + i] = ok ? x[u][i] : 0.f;
+    }
   }
-  load(s2, ws.W + ch * CH * DV, CH);
+  copy_rows<CH, DV, LD>(s2, ws.W + ch * CH * DV, tid);
   __syncthreads();
   prod_rows<DV, CH, 1>(s0, s2, -1.f, ws.T + ch * CH * CH, CH);
   prod_rows<DV, CH, 2>(s1, s2, 1.f, ws.A + ch * CH * CH, CH);
   __syncthreads();
   // phase 2: dE_bar = -dR S^T, dQ_gamma = dO S^T
-  load(s2, ws.S + ch * DK * DV, DK);
+  copy_rows<DK, DV, LD>(s2, ws.S + ch * DK * DV, tid);
   __syncthreads();
   prod_rows<DV, DK, 0>(s0, s2, -1.f, ws.Eb + ch * CH * DK, DK);
   prod_rows<DV, DK, 0>(s1, s2, 1.f, ws.Qg + ch * CH * DK, DK);
   __syncthreads();
   // phase 3: dK_tail = W dS^T and sum_v S (.) dS
-  load(s0, ws.W + ch * CH * DV, CH);
-  load(s2, ws.dS + ch * DK * DV, DK);
+  copy_rows<CH, DV, LD>(s0, ws.W + ch * CH * DV, tid);
+  copy_rows<DK, DV, LD>(s2, ws.dS + ch * DK * DV, tid);
   __syncthreads();
   prod_rows<DV, DK, 0>(s0, s2, 1.f, ws.Kt + ch * CH * DK, DK);
   for (int c = tid; c < DK; c += NTHR) {
@@ -273,14 +303,22 @@ __global__ __launch_bounds__(NTHR) void bwd_prod_kernel(BwdParams p) {
 }
 
 // ---- pass B2: back to the rows, the cumulative decay and the gates -----------
+// The key channels are taken KC = 64 at a time, so that the chunk's k, e, q
+// and G columns of the pass and the whole dT and dA_qk fit in LDS together;
+// every inner-loop operand is then an LDS read (dT and dA_qk rows as
+// broadcasts).  Thread (wave w, lane c) owns channel c of the pass in rows
+// w, w + 4, ..., so each row of a pass is one wave and its sums over the
+// channels are wave reductions.
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
-  constexpr int NP = NTHR / DK;          // row partitions
-  constexpr int RPP = CH / NP;           // rows per partition
-  constexpr int WPP = DK / 64;           // waves per partition
-  constexpr int VW = DV / 64;            // waves per row of the value side
-  __shared__ __attribute__((aligned(16))) float sK[CH * DK], sE[CH * DK], sQ[CH * DK], sG[CH * DK];
-  __shared__ float sGC[DK], sRb[CH][WPP], sRl[CH][WPP], sRz[CH][VW > 0 ? VW : 1];
+  constexpr int KC = 64, NPASS = DK / KC;
+  constexpr int NP = NTHR / KC, RPP = CH / NP;   // 4 row partitions of 16 rows
+  constexpr int VW = DV / 64;                    // waves per row of the value side
+  constexpr int TP = CH + 1;
+  static_assert(DK % KC == 0, "key channels in passes of 64");
+  __shared__ __attribute__((aligned(16))) float sK[CH * KC], sE[CH * KC], sQ[CH * KC], sG[CH * KC];
+  __shared__ __attribute__((aligned(16))) float sdT[CH * TP], sdA[CH * TP];
+  __shared__ float sGC[KC], sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW], sDg[CH];
   __shared__ float sBeta[CH], sLam[CH];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -297,150 +335,173 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
   const IO* vg = reinterpret_cast<const IO*>(p.f.v);
   const BwdWs& ws = p.ws;
 
-  // ---- rows of the chunk (zero past T), gates per token
-  for (int e = tid; e < CH * DK; e += NTHR) {
-    const int r = e / DK, c = e - r * DK;
-    const int t = t0 + r;
-    float kv = 0.f, qv = 0.f, ev = 0.f, gv = 0.f;
-    if (t < T) {
-      const size_t tok = seq0 + (size_t)t * H;
-      kv = ldf(kg + tok * DK + c);
-      qv = ldf(qg + tok * DK + c);
-      if (erase == 1) {
-        ev = p.f.b[tok * DK + c] * kv;
-      } else {
-        float x = kv;
-        if (qmix) x = __builtin_fmaf(qmix == 2 ? p.f.lam[tok] : p.f.lam[hh], qv, kv);
-        ev = p.f.beta[tok] * x;
-      }
-      if (decay == 2) gv = p.f.g[tok * DK + c];
-      else if (decay == 1) gv = p.f.g[tok];
-    }
-    sK[e] = kv;
-    sQ[e] = qv;
-    sE[e] = ev;
-    sG[e] = gv;
-  }
+  copy_rows<CH, CH, TP>(sdT, ws.T + ch * CH * CH, tid);
+  copy_rows<CH, CH, TP>(sdA, ws.A + ch * CH * CH, tid);
   for (int r = tid; r < CH; r += NTHR) {
     const int t = t0 + r;
-    const size_t tok = seq0 + (size_t)t * H;
+    const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
     sBeta[r] = (t < T && (erase == 0 || write == 0)) ? p.f.beta[tok] : 0.f;
     sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
+    sDg[r] = 0.f;
   }
-  __syncthreads();
-  if (tid < DK) {
-    float run = 0.f;
-    for (int r = 0; r < CH; ++r) {
-      run += sG[r * DK + tid];
-      sG[r * DK + tid] = run;
-    }
-    sGC[tid] = run;
-  }
-  __syncthreads();
+  const int c = lane;
+  const int par = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- key side: thread (row partition par, channel c)
-  const int c = tid % DK;
-  const int par = __builtin_amdgcn_readfirstlane(tid / DK);
-  const int wpp = (tid % DK) >> 6;  // my wave within the partition
-  const float* dT = ws.T + ch * CH * CH;
-  const float* dA = ws.A + ch * CH * CH;
-  const float GC = sGC[c];
-  float dGr[RPP], xkt[RPP];
-  for (int m = 0; m < RPP; ++m) {
-    const int i = par + NP * m;  // wave-uniform
-    const float gi = sG[i * DK + c];
-    const float gam = fexp(gi), tl = fexp(GC - gi);
-    const float ki = sK[i * DK + c], ei = sE[i * DK + c], qi = sQ[i * DK + c];
-    const float dEb = ws.Eb[(ch * CH + i) * DK + c];
-    const float dQg = ws.Qg[(ch * CH + i) * DK + c];
-    const float dKt = ws.Kt[(ch * CH + i) * DK + c];
-    // off-diagonal sums (the diagonal of A_qk has d_ii = 1 and does not
-    // depend on G: its two contributions to dG cancel exactly, so it is
-    // kept out of dG rather than added and cancelled in fp32)
-    float P = 0.f, Pq = 0.f, Rm = 0.f, Rq = 0.f;
-    for (int j = 0; j < i; ++j) {
-      const float d = fexp(gi - sG[j * DK + c]);
-      const float kd = sK[j * DK + c] * d;
-      P = __builtin_fmaf(dT[i * CH + j], kd, P);
-      Pq = __builtin_fmaf(dA[i * CH + j], kd, Pq);
-    }
-    for (int i2 = i + 1; i2 < CH; ++i2) {
-      const float d = fexp(sG[i2 * DK + c] - gi);
-      Rm = __builtin_fmaf(dT[i2 * CH + i], sE[i2 * DK + c] * d, Rm);
-      Rq = __builtin_fmaf(dA[i2 * CH + i], sQ[i2 * DK + c] * d, Rq);
-    }
-    const float diag = dA[i * CH + i];
-    const float de = __builtin_fmaf(gam, dEb, P);
-    float dqd = __builtin_fmaf(gam, dQg, __builtin_fmaf(diag, ki, Pq));
-    float dkd = tl * dKt + Rm + __builtin_fmaf(diag, qi, Rq);
-    dGr[m] = ei * gam * dEb + qi * gam * dQg + ei * P + qi * Pq - ki * (Rm + Rq);
-    xkt[m] = ki * tl * dKt;  // K_tail_i dK_tail_i
-    // the erase gate
-    float rb = 0.f, rl = 0.f;
-    const int t = t0 + i;
-    const size_t tok = seq0 + (size_t)(t < T ? t : 0) * H;
-    if (erase == 1) {
-      if (t < T) p.db[tok * DK + c] = de * ki;
-      dkd = __builtin_fmaf(t < T ? p.f.b[tok * DK + c] : 0.f, de, dkd);
-    } else {
-      const float bt = sBeta[i], lt = sLam[i];
-      rb = de * __builtin_fmaf(lt, qi, ki);
-      dkd = __builtin_fmaf(bt, de, dkd);
-      if (qmix) {
-        dqd = __builtin_fmaf(bt * lt, de, dqd);
-        rl = bt * de * qi;
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int cg = ps * KC + c;  // key channel of this thread
+    __syncthreads();             // the previous pass's columns are no longer read
+    // ---- this pass's columns of the chunk's rows (zero past T)
+    {
+      constexpr int QPR = KC / 4, NQ = CH * QPR / NTHR;
+      f32x4 rk[NQ], rq[NQ], rg[NQ], rb[NQ];
+      float rgs[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, c4 = ps * KC + (e - r * QPR) * 4;
+        const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+        rk[u] = ldf4(kg + tok * DK + c4);
+        rq[u] = ldf4(qg + tok * DK + c4);
+        if (decay == 2) rg[u] = ldf4(p.f.g + tok * DK + c4);
+        rgs[u] = decay == 1 ? p.f.g[tok] : 0.f;
+        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + c4);
+      }
+      __syncthreads();  // sBeta, sLam
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, cl = (e - r * QPR) * 4;
+        const bool ok = t0 + r < T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float kv = ok ? rk[u][i] : 0.f, qv = ok ? rq[u][i] : 0.f;
+          sK[r * KC + cl + i] = kv;
+          sQ[r * KC + cl + i] = qv;
+          sE[r * KC + cl + i] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv
+                                           : sBeta[r] * __builtin_fmaf(sLam[r], qv, kv);
+          sG[r * KC + cl + i] = !ok ? 0.f : (decay == 2 ? rg[u][i] : rgs[u]);
+        }
       }
     }
-    if (t < T) {
-      p.dq[tok * DK + c] = dqd;
-      p.dk[tok * DK + c] = dkd;
+    __syncthreads();
+    if (tid < KC) {
+      float run = 0.f;
+      for (int r = 0; r < CH; ++r) {
+        run += sG[r * KC + tid];
+        sG[r * KC + tid] = run;
+      }
+      sGC[tid] = run;
     }
-    rb = wave_sum(rb);
-    rl = wave_sum(rl);
-    if (lane == 0) {
-      sRb[i][wpp] = rb;
-      sRl[i][wpp] = rl;
-    }
-  }
-  __syncthreads();  // the rows of G, k, e, q are no longer read: sG takes dG, sE the K_tail terms
+    // the product pass's results for my rows
+    float dEb[RPP], dQg[RPP], dKt[RPP];
 #pragma unroll
-  for (int m = 0; m < RPP; ++m) {
-    const int i = par + NP * m;
-    sG[i * DK + c] = dGr[m];
-    sE[i * DK + c] = xkt[m];
-  }
-  __syncthreads();
-  // dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC
-  if (decay != 0 && tid < DK) {
-    float pre = 0.f;
-    for (int r = 0; r < CH; ++r) {  // exclusive prefix of the K_tail terms
-      const float x = sE[r * DK + tid];
-      sE[r * DK + tid] = pre;
-      pre += x;
+    for (int m = 0; m < RPP; ++m) {
+      const size_t at = (ch * CH + par + NP * m) * DK + cg;
+      dEb[m] = ws.Eb[at];
+      dQg[m] = ws.Qg[at];
+      dKt[m] = ws.Kt[at];
     }
-    const float base = fexp(sGC[tid]) * ws.gC[ch * DK + tid];
-    float run = 0.f;
-    for (int r = CH - 1; r >= 0; --r) {
-      run += sG[r * DK + tid];
-      const float dgv = run + sE[r * DK + tid] + base;
-      if (decay == 2) {
-        if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + tid] = dgv;
+    __syncthreads();
+    const float GC = sGC[c];
+    float dGr[RPP], xkt[RPP];
+    for (int m = 0; m < RPP; ++m) {
+      const int i = par + NP * m;  // wave-uniform
+      const float gi = sG[i * KC + c];
+      const float gam = fexp(gi), tl = fexp(GC - gi);
+      const float ki = sK[i * KC + c], ei = sE[i * KC + c], qi = sQ[i * KC + c];
+      // off-diagonal sums (the diagonal of A_qk has d_ii = 1 and does not
+      // depend on G: its two contributions to dG cancel exactly, so it is
+      // kept out of dG rather than added and cancelled in fp32)
+      float P = 0.f, Pq = 0.f, Rm = 0.f, Rq = 0.f;
+      for (int j = 0; j < i; ++j) {
+        const float kd = sK[j * KC + c] * fexp(gi - sG[j * KC + c]);
+        P = __builtin_fmaf(sdT[i * TP + j], kd, P);
+        Pq = __builtin_fmaf(sdA[i * TP + j], kd, Pq);
+      }
+      for (int i2 = i + 1; i2 < CH; ++i2) {
+        const float d = fexp(sG[i2 * KC + c] - gi);
+        Rm = __builtin_fmaf(sdT[i2 * TP + i], sE[i2 * KC + c] * d, Rm);
+        Rq = __builtin_fmaf(sdA[i2 * TP + i], sQ[i2 * KC + c] * d, Rq);
+      }
+      const float diag = sdA[i * TP + i];
+      const float de = __builtin_fmaf(gam, dEb[m], P);
+      float dqd = __builtin_fmaf(gam, dQg[m], __builtin_fmaf(diag, ki, Pq));
+      float dkd = tl * dKt[m] + Rm + __builtin_fmaf(diag, qi, Rq);
+      dGr[m] = ei * gam * dEb[m] + qi * gam * dQg[m] + ei * P + qi * Pq - ki * (Rm + Rq);
+      xkt[m] = ki * tl * dKt[m];  // K_tail_i dK_tail_i
+      // the erase gate
+      float rb = 0.f, rl = 0.f;
+      const int t = t0 + i;
+      const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+      if (erase == 1) {
+        const float bi = t < T ? p.f.b[tok * DK + cg] : 0.f;
+        if (t < T) p.db[tok * DK + cg] = de * ki;
+        dkd = __builtin_fmaf(bi, de, dkd);
       } else {
-        sG[r * DK + tid] = dgv;
+        const float bt = sBeta[i], lt = sLam[i];
+        rb = de * __builtin_fmaf(lt, qi, ki);
+        dkd = __builtin_fmaf(bt, de, dkd);
+        if (qmix) {
+          dqd = __builtin_fmaf(bt * lt, de, dqd);
+          rl = bt * de * qi;
+        }
+      }
+      if (t < T) {
+        p.dq[tok * DK + cg] = dqd;
+        p.dk[tok * DK + cg] = dkd;
+      }
+      rb = wave_sum(rb);
+      rl = wave_sum(rl);
+      if (lane == 0) {
+        sRb[i][ps] = rb;
+        sRl[i][ps] = rl;
+      }
+    }
+    __syncthreads();  // sG takes dG, sE the K_tail terms
+#pragma unroll
+    for (int m = 0; m < RPP; ++m) {
+      const int i = par + NP * m;
+      sG[i * KC + c] = dGr[m];
+      sE[i * KC + c] = xkt[m];
+    }
+    __syncthreads();
+    // dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC
+    if (decay != 0 && tid < KC) {
+      float pre = 0.f;
+      for (int r = 0; r < CH; ++r) {  // exclusive prefix of the K_tail terms
+        const float x = sE[r * KC + tid];
+        sE[r * KC + tid] = pre;
+        pre += x;
+      }
+      const float base = fexp(GC) * ws.gC[ch * DK + ps * KC + tid];
+      float run = 0.f;
+      for (int r = CH - 1; r >= 0; --r) {
+        run += sG[r * KC + tid];
+        const float dgv = run + sE[r * KC + tid] + base;
+        if (decay == 2) {
+          if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + ps * KC + tid] = dgv;
+        } else {
+          sG[r * KC + tid] = dgv;
+        }
+      }
+    }
+    if (decay == 1) {
+      __syncthreads();
+      if (tid < CH) {
+        float s = 0.f;
+        for (int c2 = 0; c2 < KC; ++c2) s += sG[tid * KC + c2];
+        sDg[tid] += s;
       }
     }
   }
   // ---- value side: dZ = dR
   {
     const float* dz = ws.dR + ch * CH * DV;
-    const IO* vrow = vg;
     for (int e = tid; e < CH * DV; e += NTHR) {
       const int r = e / DV, v = e - r * DV;
       const int t = t0 + r;
+      const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+      const float z = dz[e], vv = ldf(vg + tok * DV + v);
       float zb = 0.f;
       if (t < T) {
-        const size_t tok = seq0 + (size_t)t * H;
-        const float z = dz[e], vv = ldf(vrow + tok * DV + v);
         if (write == 1) {
           p.dw[tok * DV + v] = z * vv;
           p.dv[tok * DV + v] = p.f.w[tok * DV + v] * z;
@@ -450,7 +511,7 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
         }
       }
       zb = wave_sum(zb);
-      if (lane == 0 && VW > 0) sRz[r][(v >> 6)] = zb;
+      if (lane == 0) sRz[r][v >> 6] = zb;
     }
   }
   __syncthreads();
@@ -459,16 +520,12 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
     const int t = t0 + r;
     if (t >= T) continue;
     const size_t tok = seq0 + (size_t)t * H;
-    if (decay == 1) {
-      float s = 0.f;
-      for (int c2 = 0; c2 < DK; ++c2) s += sG[r * DK + c2];
-      p.dg[tok] = s;
-    }
+    if (decay == 1) p.dg[tok] = sDg[r];
     float sb = 0.f, sl = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < WPP; ++w2) {
-      sb += sRb[r][w2];
-      sl += sRl[r][w2];
+    for (int q2 = 0; q2 < NPASS; ++q2) {
+      sb += sRb[r][q2];
+      sl += sRl[r][q2];
     }
     if (write == 0) {
 #pragma unroll

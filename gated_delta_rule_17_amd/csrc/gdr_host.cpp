@@ -257,11 +257,11 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out, Workspace ws
     pi.lds_bytes = 0;
     pi.n_chunks = 1;
   } else if (op == kOpRecur) {
-    // one workgroup of dv threads per (batch, head); 16 tokens staged in LDS
+    // one workgroup of dv threads per (batch, head); 8 tokens staged in LDS
     pi.grid = static_cast<int32_t>(BH);
     pi.block = a->dv;
     pi.dv_slice = a->dv;
-    pi.lds_bytes = 4 * 16 * a->dk * 4 + 16 * (a->dv / 64) * 4;
+    pi.lds_bytes = 4 * 8 * a->dk * 4 + 8 * (a->dv / 64) * 4 + 3 * 8 * a->dv * 4;
     pi.n_chunks = 0;
   } else {
     int cand[3];
@@ -662,7 +662,11 @@ gdr_status gdr_output_norm_gate(const gdr_norm_args* a, void* stream) {
 }
 
 const char* gdr_status_str(gdr_status s) {
-  switch (s) {
+  // any int may arrive through the C ABI: read it as an int, not as the enum
+  // (a value outside the enumerators is not a valid gdr_status in C++)
+  int v;
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case GDR_OK: return "GDR_OK";
     case GDR_E_NULL: return "GDR_E_NULL";
     case GDR_E_SHAPE: return "GDR_E_SHAPE";

@@ -79,6 +79,10 @@ constexpr int plain_lds_bytes() {
 
 __device__ __forceinline__ float ldf(const float* p) { return *p; }
 __device__ __forceinline__ float ldf(const bf16* p) { return (float)*p; }
+__device__ __forceinline__ f32x4 ldf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ldf4(const bf16* p) {
+  return __builtin_convertvector(*reinterpret_cast<const bf16x4*>(p), f32x4);
+}
 
 // sum over the 16 lanes of each 16-lane group
 __device__ __forceinline__ float sum16(float s) {
@@ -139,51 +143,61 @@ __global__ __launch_bounds__(NTHR) void plain_fwd_kernel(ChunkParams p, BwdWs ws
         ws.S[(ch * DK + c) * DV + vbase + v] = sS[c * DVP + v];
       }
     }
-    // ---- rows of the chunk: k, q, e and the log-decay (zero past T) -------
-    for (int e = tid; e < CH * DK; e += NTHR) {
-      const int r = e / DK, c = e - r * DK;
-      const int t = t0 + r;
-      float kv = 0.f, qv = 0.f, ev = 0.f, gv = 0.f;
-      if (t < T) {
-        const size_t tok = seq0 + (size_t)t * H;
-        kv = ldf(kg + tok * DK + c);
-        qv = ldf(qg + tok * DK + c);
-        if (erase == 1) {
-          ev = p.b[tok * DK + c] * kv;
-        } else if (erase == 2) {
-          ev = kv;  // per-value-channel beta: the strength sits in M
-        } else {
-          float x = kv;
-          if (qmix) x = __builtin_fmaf(qmix == 2 ? p.lam[tok] : p.lam[hh], qv, kv);
-          ev = p.beta[tok] * x;
-        }
-        if (decay == 2) gv = p.g[tok * DK + c];
-        else if (decay == 1) gv = p.g[tok];
+    // ---- rows of the chunk: k, q, e and the log-decay (zero past T).  Four
+    // channels per load; every load of the chunk is issued first, at a token
+    // index clamped to T - 1, and masked afterwards.
+    {
+      constexpr int QPR = DK / 4, NQ = CH * QPR / NTHR;
+      f32x4 rk[NQ], rq[NQ], rg[NQ], rb[NQ];
+      float rgs[NQ], rbe[NQ], rl[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, c4 = (e - r * QPR) * 4;
+        const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+        rk[u] = ldf4(kg + tok * DK + c4);
+        rq[u] = ldf4(qg + tok * DK + c4);
+        if (decay == 2) rg[u] = ldf4(p.g + tok * DK + c4);
+        rgs[u] = decay == 1 ? p.g[tok] : 0.f;
+        if (erase == 1) rb[u] = ldf4(p.b + tok * DK + c4);
+        rbe[u] = erase == 0 ? p.beta[tok] : 0.f;
+        rl[u] = qmix == 2 ? p.lam[tok] : (qmix ? p.lam[hh] : 0.f);
       }
-      sK[r * DKP + c] = kv;
-      sQ[r * DKP + c] = qv;
-      sX[r * DKP + c] = ev;
-      sG[r * DKP + c] = gv;
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, c4 = (e - r * QPR) * 4;
+        const bool ok = t0 + r < T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float kv = ok ? rk[u][i] : 0.f, qv = ok ? rq[u][i] : 0.f;
+          float ev;
+          if (erase == 1) ev = rb[u][i] * kv;
+          else if (erase == 2) ev = kv;  // per-value-channel beta: the strength sits in M
+          else ev = rbe[u] * __builtin_fmaf(rl[u], qv, kv);
+          sK[r * DKP + c4 + i] = kv;
+          sQ[r * DKP + c4 + i] = qv;
+          sX[r * DKP + c4 + i] = ok ? ev : 0.f;
+          sG[r * DKP + c4 + i] = !ok ? 0.f : (decay == 2 ? rg[u][i] : rgs[u]);
+        }
+      }
     }
     // ---- value side: z and the erase multiplier M -------------------------
-    for (int e = tid; e < CH * DVS; e += NTHR) {
-      const int r = e / DVS, v = e - r * DVS;
-      const int t = t0 + r;
-      float z = 0.f, m = 1.f;
-      if (t < T) {
-        const size_t tok = seq0 + (size_t)t * H;
-        const float vv = ldf(vg + tok * DV + vbase + v);
-        if (erase == 2) {
-          m = p.beta[tok * DV + vbase + v];
-          z = m * vv;
-        } else if (write == 1) {
-          z = p.w[tok * DV + vbase + v] * vv;
-        } else {
-          z = p.beta[tok] * vv;
-        }
+    {
+      constexpr int NV = CH * DVS / NTHR;
+      float rv[NV], rw[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + NTHR * u, r = e / DVS, v = e - r * DVS;
+        const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+        rv[u] = ldf(vg + tok * DV + vbase + v);
+        rw[u] = erase == 2 ? p.beta[tok * DV + vbase + v] : (write == 1 ? p.w[tok * DV + vbase + v] : p.beta[tok]);
       }
-      sZ[r * DVP + v] = z;
-      sM[r * DVP + v] = m;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + NTHR * u, r = e / DVS, v = e - r * DVS;
+        const bool ok = t0 + r < T;
+        sZ[r * DVP + v] = ok ? rw[u] * rv[u] : 0.f;
+        sM[r * DVP + v] = (ok && erase == 2) ? rw[u] : 1.f;
+      }
     }
     __syncthreads();
     // ---- chunk-local inclusive cumsum of the log-decay, one channel per thread

@@ -12,7 +12,7 @@
 // keeps column v of the state (all dk rows) in registers for the whole call,
 // so both contractions over the key channels (r and o) are thread-local and
 // a token needs no barrier.  The per-token key-side vectors (alpha, e, k, q)
-// of a block of TB tokens are staged in LDS and read as broadcasts.
+// of a block of TB = 8 tokens are staged in LDS and read as broadcasts.
 //
 // Output epilogue (11.3: RMSNorm of each head's readout, then the SiLU output
 // gate; the Gated DeltaNet-2 page's method flowchart ends with the same step):
@@ -47,15 +47,22 @@ struct RecurParams {
 __device__ __forceinline__ float ldx(const float* p) { return *p; }
 __device__ __forceinline__ float ldx(const bf16* p) { return (float)*p; }
 
+// four consecutive elements as floats
+__device__ __forceinline__ f32x4 ld4x(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4x(const bf16* p) {
+  return __builtin_convertvector(*reinterpret_cast<const bf16x4*>(p), f32x4);
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.f + fexp(-x)); }
 
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
-  constexpr int TB = 16;        // tokens staged per block
+  constexpr int TB = 8;         // tokens staged per block
   constexpr int NW = DV / 64;   // waves
   static_assert(DV % 64 == 0 && DK % 4 == 0, "recurrent layout");
   __shared__ __attribute__((aligned(16))) float sA[TB][DK], sE[TB][DK], sK[TB][DK], sQ[TB][DK];
   __shared__ float sP[TB][NW];
+  __shared__ float sZ[TB][DV], sM[TB][DV], sGt[TB][DV];  // value side, one column per thread
 
   const int v = threadIdx.x, wave = v >> 6;
   const int bh = blockIdx.x;
@@ -75,44 +82,69 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
 #pragma unroll
   for (int c = 0; c < DK; ++c) S[c] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + v] : 0.f;
 
+  // staging layout: QPR threads cover a row of DK channels four at a time;
+  // the DV / QPR groups of them take every (DV / QPR)-th token of a block
+  constexpr int QPR = DK / 4, NG = DV / QPR, TPG = TB / NG;
+  static_assert(NG * QPR == DV && TPG * NG == TB, "staging layout");
+  const int grp = v / QPR, c4 = (v - grp * QPR) * 4;
+  const float* gsrc = decay ? p.g : reinterpret_cast<const float*>(p.v);  // any readable stand-in
+  const float* bsrc = (erase == 0 || write == 0) ? p.beta : reinterpret_cast<const float*>(p.v);
   for (int t0 = 0; t0 < T; t0 += TB) {
     const int nt = min(TB, T - t0);
-    // ---- key side of the block: alpha, e, k, q (zeros and alpha = 1 past T)
-    for (int idx = v; idx < TB * DK; idx += DV) {
-      const int tt = idx / DK, c = idx - tt * DK;
-      float a = 1.f, e = 0.f, kv = 0.f, qv = 0.f;
-      if (tt < nt) {
-        const size_t tok = seq0 + (size_t)(t0 + tt) * H;
-        kv = ldx(kg + tok * DK + c);
-        qv = ldx(qg + tok * DK + c);
-        if (decay == 2) a = fexp(p.g[tok * DK + c]);
-        else if (decay == 1) a = fexp(p.g[tok]);
-        if (erase == 1) e = p.b[tok * DK + c] * kv;
-        else if (erase == 2) e = kv;
-        else e = p.beta[tok] * (qmix ? __builtin_fmaf(qmix == 2 ? p.lam[tok] : p.lam[hh], qv, kv) : kv);
-      }
-      sA[tt][c] = a;
-      sE[tt][c] = e;
-      sK[tt][c] = kv;
-      sQ[tt][c] = qv;
-    }
-    // ---- value side of my column: z and the erase multiplier m
-    float z[TB], m[TB], gt[TB];
+    // ---- key side of the block: alpha, e, k, q (zeros and alpha = 1 past T).
+    // Every load is issued first, at a token index clamped to T - 1, and
+    // masked afterwards, so that the loads of the block are in flight together.
+    {
+      f32x4 rk[TPG], rq[TPG], rg[TPG], rb[TPG];
+      float rgs[TPG], rbe[TPG], rl[TPG];
 #pragma unroll
-    for (int tt = 0; tt < TB; ++tt) {
-      z[tt] = 0.f;
-      m[tt] = 1.f;
-      gt[tt] = 0.f;
-      if (tt < nt) {
-        const size_t tok = seq0 + (size_t)(t0 + tt) * H;
-        const float vv = ldx(vg + tok * DV + v);
-        if (erase == 2) {
-          m[tt] = p.beta[tok * DV + v];
-          z[tt] = m[tt] * vv;
-        } else {
-          z[tt] = (write == 1 ? p.w[tok * DV + v] : p.beta[tok]) * vv;
+      for (int u = 0; u < TPG; ++u) {
+        const int tt = grp + NG * u;
+        const size_t tok = seq0 + (size_t)min(t0 + tt, T - 1) * H;
+        rk[u] = ld4x(kg + tok * DK + c4);
+        rq[u] = ld4x(qg + tok * DK + c4);
+        if (decay == 2) rg[u] = ld4x(p.g + tok * DK + c4);
+        rgs[u] = gsrc[tok];
+        if (erase == 1) rb[u] = ld4x(p.b + tok * DK + c4);
+        rbe[u] = bsrc[tok];
+        rl[u] = qmix == 2 ? p.lam[tok] : (qmix ? p.lam[hh] : 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < TPG; ++u) {
+        const int tt = grp + NG * u;
+        const bool ok = tt < nt;
+        f32x4 a, e, kk, qq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kk[i] = ok ? rk[u][i] : 0.f;
+          qq[i] = ok ? rq[u][i] : 0.f;
+          a[i] = !ok ? 1.f : (decay == 2 ? fexp(rg[u][i]) : (decay == 1 ? fexp(rgs[u]) : 1.f));
+          if (erase == 1) e[i] = (ok ? rb[u][i] : 0.f) * kk[i];
+          else if (erase == 2) e[i] = kk[i];
+          else e[i] = rbe[u] * __builtin_fmaf(rl[u], qq[i], kk[i]);
         }
-        if (epi) gt[tt] = ldx(gateg + tok * DV + v);
+        *reinterpret_cast<f32x4*>(&sA[tt][c4]) = a;
+        *reinterpret_cast<f32x4*>(&sE[tt][c4]) = e;
+        *reinterpret_cast<f32x4*>(&sK[tt][c4]) = kk;
+        *reinterpret_cast<f32x4*>(&sQ[tt][c4]) = qq;
+      }
+    }
+    // ---- value side of my column: z, the erase multiplier m and the gate
+    {
+      float rv[TB], rw[TB], rgt[TB];
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const size_t tok = seq0 + (size_t)min(t0 + tt, T - 1) * H;
+        rv[tt] = ldx(vg + tok * DV + v);
+        rw[tt] = erase == 2 ? p.beta[tok * DV + v] : (write == 1 ? p.w[tok * DV + v] : bsrc[tok]);
+        rgt[tt] = epi ? ldx(gateg + tok * DV + v) : 0.f;
+      }
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const bool ok = tt < nt;
+        sM[tt][v] = (erase == 2 && ok) ? rw[tt] : 1.f;
+        sZ[tt][v] = ok ? rw[tt] * rv[tt] : 0.f;
+        sGt[tt][v] = ok ? rgt[tt] : 0.f;
       }
     }
     __syncthreads();
@@ -133,7 +165,7 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
             r = __builtin_fmaf(e[u], S[c + u], r);
           }
         }
-        const float d = z[tt] - m[tt] * r;
+        const float d = sZ[tt][v] - sM[tt][v] * r;
         // write along k, then read along q
         float o = 0.f;
 #pragma unroll
@@ -167,7 +199,7 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
           float ss = 0.f;
 #pragma unroll
           for (int w2 = 0; w2 < NW; ++w2) ss += sP[tt][w2];
-          y = y * rsqrtf(ss * (1.f / DV) + p.eps) * nwv * silu(gt[tt]);
+          y = y * rsqrtf(ss * (1.f / DV) + p.eps) * nwv * silu(sGt[tt][v]);
         }
         og[tok * DV + v] = (IO)y;
       }
