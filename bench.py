@@ -278,7 +278,7 @@ def _seq_slice(x, bs, hs, Ts):
     return x[bs, :Ts, hs][:, :, None] if x.ndim == 3 else x[bs, :Ts, hs, :][:, :, None, :]
 
 
-def cpu_baseline_all(items, budget_s=4.0):
+def cpu_baseline_all(items, budget_s=3.0):
     """The float64 oracle as it stands, on every core of this host: each
     workload's (batch, head) pairs are split over one process per core (one
     BLAS thread each) on a prefix of the tokens sized to about ``budget_s``
@@ -333,7 +333,7 @@ def cpu_baseline_all(items, budget_s=4.0):
                 busy = sum(pool.map(_oracle_worker, jobs))
                 return time.perf_counter() - t0, busy
 
-            T0 = min(T, 8)
+            T0 = min(T, 64)
             w0, _ = run(T0)
             Ts = int(min(T, max(T0, budget_s / max(w0, 1e-6) * T0)))
             wall, busy = run(Ts)
@@ -412,9 +412,21 @@ def collect_counters(outdir, only=None):
     ingest_counters(outdir)
 
 
+def _demangle(kname):
+    if not kname.startswith("_Z"):
+        return kname
+    import subprocess
+    try:
+        # this c++filt does not know the bf16 code DF16b: spell it as a vendor type
+        name = kname.replace("DF16b", "u6__bf16")
+        return subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip() or kname
+    except OSError:
+        return kname
+
+
 def _short(kname):
     """Kernel name without namespace and parameter list."""
-    k = kname.split("(")[0].replace("gdr::", "").replace("void ", "")
+    k = _demangle(kname).split("(")[0].replace("gdr::", "").replace("void ", "")
     return k.strip()
 
 
@@ -432,7 +444,11 @@ def ingest_counters(root):
         names = {}
         for r in csv.DictReader(open(path)):
             dsp = int(r["Dispatch_Id"])
+            # summed over the counter's instances (shader engines, XCDs), and the
+            # largest instance (what a cycle count such as GRBM_GUI_ACTIVE needs)
             vals[dsp][r["Counter_Name"]] += float(r["Counter_Value"])
+            mk = r["Counter_Name"] + "_max"
+            vals[dsp][mk] = max(vals[dsp].get(mk, 0.0), float(r["Counter_Value"]))
             names[dsp] = r["Kernel_Name"]
         copies = [d for d in vals if "copy" in names[d].lower()]
         if pas in ("fetch", "write") and copies:
@@ -440,7 +456,7 @@ def ingest_counters(root):
             big = max(copies, key=lambda d: vals[d].get(cnt, 0.0))
             calib[(spec, pas)] = vals[big].get(cnt, 0.0)
         for dsp in sorted(vals):
-            if "gdr::" not in names[dsp]:
+            if "gdr::" not in names[dsp] and not names[dsp].startswith("_ZN3gdr"):
                 continue
             k = _short(names[dsp])
             for cname, v in vals[dsp].items():
@@ -589,7 +605,9 @@ def main():
     if kents:
         for k, e in kents.items():
             if "SQ_VALU_MFMA_BUSY_CYCLES" in e and "GRBM_GUI_ACTIVE" in e:
-                roof["mfma_busy_frac_counter"] = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (e["GRBM_GUI_ACTIVE"] * 1024)
+                # MFMA busy cycles over the 1024 SIMDs' cycles while the kernel
+                # ran; rocprofv3 reports GRBM_GUI_ACTIVE summed over the 8 XCDs
+                roof["mfma_busy_frac_counter"] = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (e["GRBM_GUI_ACTIVE"] / 8 * 1024)
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
