@@ -37,25 +37,37 @@ def run_chunk(inp, dv_split=0, two_pass=None):
 
 
 def run_oracle(inp, heads=None):
-    """Oracle on all heads, or on a list of (b, h) pairs (each a full sequence)."""
+    """Oracle on all heads, or on a list of (b, h) pairs (each a full
+    sequence; run as one batch of single-head sequences)."""
     if heads is None:
         return gdr_recurrence(inp["q"], inp["k"], inp["v"], **oracle_kwargs(inp))
-    outs_o, outs_S = [], []
-    for (b, h) in heads:
-        sub = {}
-        for key, val in inp.items():
-            if not isinstance(val, torch.Tensor):
-                sub[key] = val
-            elif key == "lam":
-                sub[key] = val[h:h + 1]
-            elif key == "state":
-                sub[key] = val[b:b + 1, h:h + 1]
-            else:
-                sub[key] = val[b:b + 1, :, h:h + 1]
-        o, S = gdr_recurrence(sub["q"], sub["k"], sub["v"], **oracle_kwargs(sub))
-        outs_o.append(o[0, :, 0])
-        outs_S.append(S[0, 0])
-    return outs_o, outs_S
+    bs = torch.tensor([b for b, _ in heads])
+    hs = torch.tensor([h for _, h in heads])
+    sub = {}
+    for key, val in inp.items():
+        if not isinstance(val, torch.Tensor):
+            sub[key] = val
+        elif key == "lam":
+            sub[key] = val[hs] if val.dim() == 1 else val[bs, :, hs][:, :, None]
+        elif key == "state":
+            sub[key] = val[bs, hs][:, None]
+        elif key in ("gate", "norm_weight"):
+            continue
+        else:
+            sub[key] = val[bs, :, hs][:, :, None] if val.dim() == 3 else val[bs, :, hs, :][:, :, None, :]
+    kw = oracle_kwargs(sub)
+    if sub["qmix"] and inp["lam"].dim() == 1:
+        # a per-head lambda: every sampled pair is its own batch row of one head
+        kw["lam"] = sub["lam"][:, None].expand(len(heads), sub["q"].shape[1]).unsqueeze(-1).contiguous()
+    o, S = gdr_recurrence(sub["q"], sub["k"], sub["v"], **kw)
+    return [o[i, :, 0] for i in range(len(heads))], [S[i, 0] for i in range(len(heads))]
+
+
+def elementwise_rel(x, ref):
+    """Diagnostic: max |x - ref| / (|ref| + 1e-6), elementwise."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float((np.abs(x - ref) / (np.abs(ref) + 1e-6)).max())
 
 
 def assert_parity(name, o, S, o_ref, S_ref, tol):
