@@ -2,6 +2,7 @@
 // bf16} x dk {64, 128} x dv {64, 128}.
 #include "bwd_kernel.hpp"
 #include "launch.hpp"
+#include "plain_split_kernel.hpp"
 
 namespace gdr {
 
@@ -17,8 +18,12 @@ bool bwd_supported(int dk, int dv) {
 template <class IO, int DK, int DV>
 hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
   const int ns = p.f.nslices, N = p.nchunks;
-  if (N > 0)
-    hipLaunchKernelGGL((plain_fwd_kernel<IO, DK, 16, true>), dim3(BH * ns), dim3(NTHR), 0, s, p.f, p.ws);
+  // record pass: the chunk records once per chunk, then the recurrence of
+  // each slice writing its entering states and W
+  if (N > 0) {
+    hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws);
+    hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, true>), dim3(BH * ns), dim3(NTHR), 0, s, p.f, p.ws);
+  }
   hipLaunchKernelGGL((bwd_state_kernel<IO, DK, 16>), dim3(BH * ns), dim3(NTHR), 0, s, p);
   if (N > 0) {
     hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);

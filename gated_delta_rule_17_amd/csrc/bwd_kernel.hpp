@@ -10,13 +10,14 @@
 //   dR = A^T dW,   dT = -tril(dR W^T, -1),   dZ = dR,   dE_bar = -dR S^T.
 // All arithmetic is fp32.  Four passes, each a kernel on the caller's stream:
 //
-//  0  record  the plain forward in record mode (plain_kernel.hpp): per chunk
-//             the entering state S, W, and T, A_qk, E_bar, Q_gamma, K_tail,
-//             gamma_C to the workspace.
+//  0  record  the two-pass plain forward in record mode
+//             (plain_split_kernel.hpp): per chunk A = (I + T)^{-1} (in the
+//             place of T), A_qk, E_bar, Q_gamma, K_tail, gamma_C, and per slice
+//             the entering state S and W, to the workspace.
 //  A  state   per (batch, head, 16-column slice), chunks in reverse, the
 //             gradient of the state dS (leaving the chunk) carried in LDS:
 //               dW = A_qk^T dO + K_tail dS
-//               dR = (I + T)^{-T} dW          (backward substitution)
+//               dR = A^T dW,  A = (I + T)^{-1} from the record pass
 //               dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR
 //             writes dR and each chunk's incoming dS; the last dS is the
 //             gradient of the initial state.
@@ -154,26 +155,21 @@ __global__ __launch_bounds__(NTHR) void bwd_state_kernel(BwdParams p) {
       for (int u = 0; u < 4; ++u) sdW[j * DVP + vq + u] = s[u];
     }
     __syncthreads();
-    // dR solves (I + T)^T dR = dW: backward substitution, column v = tid / 16
+    // dR = A^T dW with A = (I + T)^{-1} from the record (in the place of T):
+    // row j, 4 columns per thread; A is zero above the diagonal, so the sum
+    // starts at the wave's first row
     {
-      const int v = tid >> 4, part = tid & 15;
-      float rreg[4] = {0.f, 0.f, 0.f, 0.f};  // dR[part + 16 m][v]
-      for (int j = CH - 1; j >= 0; --j) {
-        float s = 0.f;
+      const int j = tid >> 2, vq = (tid & 3) * 4;
+      float r[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = (tid >> 6) * 16; i < CH; ++i) {
+        const float a = sT[i * TP + j];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int i = part + 16 * m;
-          if (i > j) s = __builtin_fmaf(sT[i * TP + j], rreg[m], s);
-        }
-        s = sum16(s);
-        const float r = sdW[j * DVP + v] - s;
-        if ((j & 15) == part) rreg[j >> 4] = r;
+        for (int u = 0; u < 4; ++u) r[u] = __builtin_fmaf(a, sdW[i * DVP + vq + u], r[u]);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i = part + 16 * m;
-        sdR[i * DVP + v] = rreg[m];
-        ws.dR[(ch * CH + i) * DV + vbase + v] = rreg[m];
+      for (int u = 0; u < 4; ++u) {
+        sdR[j * DVP + vq + u] = r[u];
+        ws.dR[(ch * CH + j) * DV + vbase + vq + u] = r[u];
       }
     }
     __syncthreads();

@@ -87,9 +87,16 @@ Epilogue epilogue_of(const gdr_args* a) {
 // Workspace bytes of the two-pass form for slice width dvs, or 0 when that
 // form does not apply: it serves the two pipelined kernels (bf16 I/O) at dk
 // 128 with slices of 16 or 32 columns (few heads), where a single pass would
-// repeat every chunk's state-independent work in many slices.
+// repeat every chunk's state-independent work in many slices, and the plain
+// fp32 kernel (16-column slices) at every shape.
 int64_t split_bytes(const gdr_args* a, int dvs) {
   const gdr::ChunkKernel kern = gdr::chunk_kernel_for(a->io == GDR_BF16, a->dk, a->decay, a->erase, a->qmix);
+  if (kern == gdr::kPlain) {
+    // the plain kernel's two-pass form: one record per chunk for every shape
+    if (a->T < 1) return 0;
+    const int64_t nrec = int64_t(a->B) * a->H * ((a->T + GDR_CHUNK - 1) / GDR_CHUNK);
+    return gdr::plain_split_layout(nrec, a->dk, nullptr, nullptr);
+  }
   if ((kern != gdr::kChan && kern != gdr::kPipe) || a->dk != 128 || (dvs != 16 && dvs != 32) || a->T < 1)
     return 0;
   const int64_t nchunks = (a->T + GDR_CHUNK - 1) / GDR_CHUNK;
@@ -279,10 +286,15 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out, Workspace ws
     const int64_t need = split_bytes(a, dvs);
     if (need > 0 && ws.ptr && ws.bytes >= static_cast<uint64_t>(need)) {
       pi.passes = 2;
-      const bool chan = kernel_for(a) == gdr::kChan;
+      const gdr::ChunkKernel kern = kernel_for(a);
       const int gm = gdr::gate_mode(a->erase, a->write);
-      pi.lds_bytes = chan ? gdr::chan_split_lds(gm, a->dk, dvs) : gdr::pipe_split_lds(gm, a->dk, dvs);
-      pi.block = 64 * ((dvs >= 32 ? 2 : 1) + 4);
+      if (kern == gdr::kPlain) {
+        pi.lds_bytes = dvs == 16 ? gdr::plain_split_lds(a->dk) : -1;
+        pi.block = 256;
+      } else {
+        pi.lds_bytes = kern == gdr::kChan ? gdr::chan_split_lds(gm, a->dk, dvs) : gdr::pipe_split_lds(gm, a->dk, dvs);
+        pi.block = 64 * ((dvs >= 32 ? 2 : 1) + 4);
+      }
     } else {
       pi.passes = 1;
       pi.lds_bytes = chunk_lds(a, dvs);
@@ -362,7 +374,9 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_args* a, void* stream) {
   gdr_plan_info pi;
   s = plan_impl(a, kOpChunk, &pi);
   if (s != GDR_OK) return s;
-  const int64_t need = split_bytes(a, pi.dv_slice);
+  int64_t need = split_bytes(a, pi.dv_slice);
+  // the plain kernel has a single-pass form that needs no records
+  if (need > static_cast<int64_t>(kScratchBytes) && kernel_for(a) == gdr::kPlain) need = 0;
   if (need > static_cast<int64_t>(kScratchBytes))
     return fail(GDR_E_SHAPE,
                 "the two-pass records of this call need %lld bytes; the no-allocation entry point's scratch "
@@ -435,8 +449,16 @@ gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool ch
   if (pi.passes == 2) {
     const int prep_grid = static_cast<int>(int64_t(a->B) * a->H * pi.n_chunks);
     p.ws = ws.ptr;
-    if (kernel_for(a) == gdr::kChan) e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
-    else e = gdr::launch_pipe_split(gm, p, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
+    const gdr::ChunkKernel kern = kernel_for(a);
+    if (kern == gdr::kPlain) {
+      gdr::BwdWs rec;
+      gdr::plain_split_layout(prep_grid, a->dk, static_cast<char*>(ws.ptr), &rec);
+      e = gdr::launch_plain_split(p, rec, a->io == GDR_BF16, a->dk, pi.grid, prep_grid, st);
+    } else if (kern == gdr::kChan) {
+      e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
+    } else {
+      e = gdr::launch_pipe_split(gm, p, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
+    }
     if (e != hipSuccess) return fail(GDR_E_HIP, "two-pass chunk kernels failed to launch: %s", hipGetErrorString(e));
     return chunk_epilogue(a, st);
   }

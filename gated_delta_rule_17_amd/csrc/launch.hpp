@@ -107,6 +107,13 @@ constexpr int64_t kSplitRecBytes = 3 * 64 * 128 * 2 + 2 * 10 * 16 * 16 * 2 + 128
 // value slices of 16 columns.  plain_lds gives the LDS bytes (-1: no instance).
 int plain_lds(int dk);
 hipError_t launch_plain(const ChunkParams& p, bool bf16io, int dk, int grid, hipStream_t s);
+// Its two-pass form (plain_split_kernel.hpp): prep_grid chunk workgroups
+// write the records to the arrays of ws (plain_split_layout in
+// bwd_params.hpp), then grid slice workgroups run the recurrence.
+struct BwdWs;
+int plain_split_lds(int dk);
+hipError_t launch_plain_split(const ChunkParams& p, const BwdWs& ws, bool bf16io, int dk, int grid, int prep_grid,
+                              hipStream_t s);
 
 // Chunk kernel chosen for (io, dk, decay kind, erase kind, qmix): the plain
 // fp32 kernel takes the per-value-channel beta (erase 2), a time-varying

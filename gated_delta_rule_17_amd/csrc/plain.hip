@@ -1,7 +1,8 @@
-// Instances of the plain fp32 chunk kernel: io {fp32, bf16} x dk {64, 128},
-// value slices of 16 columns.
+// Instances of the plain fp32 chunk kernel and of its two-pass form: io
+// {fp32, bf16} x dk {64, 128}, value slices of 16 columns.
 #include "launch.hpp"
 #include "plain_kernel.hpp"
+#include "plain_split_kernel.hpp"
 
 namespace gdr {
 
@@ -21,6 +22,33 @@ hipError_t launch_plain(const ChunkParams& p, bool bf16io, int dk, int grid, hip
     else hipLaunchKernelGGL((plain_fwd_kernel<float, DK, 16>), dim3(grid), dim3(NTHR), 0, s, p, BwdWs{});   \
     return hipGetLastError();                                                                   \
   }
+  GDR_PLAIN_CASES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+int plain_split_lds(int dk) {
+#define X(DK) if (dk == DK) return plain_rec_lds_bytes<DK, 16>();
+  GDR_PLAIN_CASES(X)
+#undef X
+  return -1;
+}
+
+template <class IO, int DK>
+hipError_t plain_split_sequence(const ChunkParams& p, const BwdWs& ws, int grid, int prep_grid, hipStream_t s) {
+  hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_plain_split(const ChunkParams& p, const BwdWs& ws, bool bf16io, int dk, int grid, int prep_grid,
+                              hipStream_t s) {
+#define X(DK)                                                                                          \
+  if (dk == DK)                                                                                        \
+    return bf16io ? plain_split_sequence<bf16, DK>(p, ws, grid, prep_grid, s)                          \
+                  : plain_split_sequence<float, DK>(p, ws, grid, prep_grid, s);
   GDR_PLAIN_CASES(X)
 #undef X
   return hipErrorInvalidValue;

@@ -1,0 +1,558 @@
+// Two-pass form of the plain fp32 chunk kernel (plain_kernel.hpp): the same
+// chunk WY form with absorbed decay ("Gated DeltaNet-2: Decoupling Erase and
+// Write in Linear Attention", key design 2), all arithmetic fp32, with the
+// state-independent work of a chunk done once per (batch, head, chunk)
+// instead of once per value slice:
+//
+//   pass 1  plain_prep_kernel, one workgroup per chunk: the gates, the
+//           chunk-local prefix sums G of the log-decay, the factor rows
+//             E_bar = e (.) exp(G),  Q_gamma = q (.) exp(G),
+//             K_tail = k (.) exp(G_C - G),  gamma_C = exp(G_C)
+//           the Gram matrices
+//             T[i][j]   = sum_c e_i[c] k_j[c] exp(G_i[c] - G_j[c])   j <  i
+//             Aqk[i][j] = sum_c q_i[c] k_j[c] exp(G_i[c] - G_j[c])   j <= i
+//           (zeros elsewhere) and the inverse A = (I + T)^{-1} (diagonal
+//           16 x 16 blocks by forward substitution, then the blocks below
+//           them block row by block row), written to the record arrays of a
+//           BwdWs: A in the place of T, or T itself under the
+//           per-value-channel beta, whose systems differ per column.
+//   pass 2  plain_rec_kernel, one workgroup per (batch, head, 16-column value
+//           slice), chunks in order, the state slice in LDS:
+//             ES = E_bar S, QS = Q_gamma S,
+//             W = A (Z - ES), or under the per-value-channel beta the
+//               solution of (I + M (.) T) W = Z - M (.) ES by forward
+//               substitution, column by column,
+//             O = QS + Aqk W,  S <- Diag(gamma_C) S + K_tail^T W.
+//
+// Every exponent is <= 0 (G is non-increasing along the chunk), so no factor
+// leaves the fp32 range.  Under a scalar decay (or none) exp(G_i - G_j) is
+// the same for every channel and multiplies the channel sums; under a decay
+// per key channel it is formed per term.  The erase direction e is
+// beta (k + lambda q) (lambda = 0 without the Q-Delta mix; per head or per
+// token), b (.) k for the per-channel erase gate, or k under the
+// per-value-channel beta, whose strength M then sits in the substitution.
+//
+// The record pass of the backward (bwd_kernel.hpp) is pass 1 followed by
+// pass 2 in record mode (REC), which writes, per chunk, the entering state
+// and W of its slice instead of o.
+#pragma once
+
+#include "bwd_params.hpp"
+#include "common.hpp"
+#include "plain_kernel.hpp"
+
+namespace gdr {
+
+// ---- pass 1 -----------------------------------------------------------------
+// Channels are processed in halves of 64: [64][65] arrays of k, e, q and the
+// prefix sums G of the half, 67 KB of LDS (two workgroups per CU).
+struct PlainPrepLay {
+  static constexpr int CHH = 64;       // channels per half
+  static constexpr int HP = CHH + 1;   // row stride (floats)
+  static constexpr int oK = 0, oX = oK + CH * HP, oQ = oX + CH * HP, oG = oQ + CH * HP;
+  static constexpr int oGs = oG + CH * HP;  // [64] scalar-decay prefix sums
+  static constexpr int oPart = oGs + CH;    // [16][64] sums of the log-decay over 4-row groups
+  static constexpr int TOTAL = oPart + 16 * CHH;
+  static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
+};
+
+template <class IO, int DK>
+__global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs ws) {
+  using L = PlainPrepLay;
+  constexpr int HP = L::HP, CHH = L::CHH, NH = DK / CHH;
+  static_assert(DK % CHH == 0, "whole halves");
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  float* sK = lds + L::oK;
+  float* sX = lds + L::oX;
+  float* sQ = lds + L::oQ;
+  float* sG = lds + L::oG;
+  float* sGs = lds + L::oGs;
+  float* sPart = lds + L::oPart;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = p.T, H = p.H, N = (T + CH - 1) / CH;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int bb = bh / H, hh = bh - bb * H;
+  const int t0 = n * CH;
+  const size_t ch = blockIdx.x;  // record index (batch * H + head) * N + chunk
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const int decay = p.decay, erase = p.erase, qmix = p.qmix;
+  const IO* qg = reinterpret_cast<const IO*>(p.q);
+  const IO* kg = reinterpret_cast<const IO*>(p.k);
+
+  // scalar decay: prefix sums of the chunk's per-token log-decay (zero past T)
+  if (wave == 0) {
+    const int t = t0 + lane;
+    const float g = (decay == 1 && t < T) ? p.g[seq0 + (size_t)t * H] : 0.f;
+    sGs[lane] = wave_incl_scan(g);
+  }
+
+  // elementwise layout: thread = rows 4 rg .. 4 rg + 3 x channels c4 .. c4 + 3
+  // of the half (16 threads cover a row's 64 channels: coalesced rows)
+  const int rg = tid >> 4, c4 = (tid & 15) * 4;
+  // Gram layout: 4 x 4 blocks (ib, jb) of (i, j), blocks with jb <= ib
+  const int ib = tid >> 4, jb = tid & 15;
+  float accT[4][4], accA[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) accT[a][b] = accA[a][b] = 0.f;
+
+  for (int half = 0; half < NH; ++half) {
+    const int cb = half * CHH;  // first channel of the half
+    if (half > 0) __syncthreads();  // the previous half's Gram reads are done
+    // ---- loads: every load of the thread first, at token indices clamped to
+    // T - 1, masked afterwards
+    f32x4 rk[4], rq[4], rgc[4], rb[4];
+    float rbeta[4], rlam[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * rg + u;
+      const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+      rk[u] = ldf4(kg + tok * DK + cb + c4);
+      rq[u] = ldf4(qg + tok * DK + cb + c4);
+      if (decay == 2) rgc[u] = *reinterpret_cast<const f32x4*>(p.g + tok * DK + cb + c4);
+      if (erase == 1) rb[u] = *reinterpret_cast<const f32x4*>(p.b + tok * DK + cb + c4);
+      rbeta[u] = erase == 0 ? p.beta[tok] : 0.f;
+      rlam[u] = qmix == 2 ? p.lam[tok] : (qmix ? p.lam[hh] : 0.f);
+    }
+    __syncthreads();  // (sGs ready; sPart free)
+    // ---- prefix sums of the log-decay per channel: within the thread's four
+    // rows, then over the 4-row groups through sPart
+    float G[4][4];  // [row u][channel i]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float run = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = t0 + 4 * rg + u < T;
+        run += (decay == 2 && ok) ? rgc[u][i] : 0.f;
+        G[u][i] = run;
+      }
+    }
+    if (decay == 2) {
+      *reinterpret_cast<f32x4*>(sPart + rg * CHH + c4) = f32x4{G[3][0], G[3][1], G[3][2], G[3][3]};
+    }
+    __syncthreads();
+    float GC[4];
+    if (decay == 2) {
+      f32x4 excl = {0.f, 0.f, 0.f, 0.f}, tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const f32x4 s = *reinterpret_cast<const f32x4*>(sPart + q * CHH + c4);
+        if (q < rg) excl += s;
+        tot += s;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) G[u][i] += excl[i];
+        GC[i] = tot[i];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G[u][i] = sGs[4 * rg + u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) GC[i] = sGs[CH - 1];
+    }
+    // ---- erase directions, factor rows to the record, operands to LDS ------
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * rg + u;
+      const bool ok = t0 + r < T;
+      f32x4 kv, qv, ev, eb, qgm, kt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kv[i] = ok ? rk[u][i] : 0.f;
+        qv[i] = ok ? rq[u][i] : 0.f;
+        if (erase == 1) ev[i] = rb[u][i] * kv[i];
+        else if (erase == 2) ev[i] = kv[i];
+        else ev[i] = rbeta[u] * __builtin_fmaf(rlam[u], qv[i], kv[i]);
+        if (!ok) ev[i] = 0.f;
+        const float gam = fexp(G[u][i]);
+        eb[i] = ev[i] * gam;
+        qgm[i] = qv[i] * gam;
+        kt[i] = kv[i] * fexp(GC[i] - G[u][i]);
+      }
+      const size_t ro = (ch * CH + r) * DK + cb + c4;
+      *reinterpret_cast<f32x4*>(ws.Eb + ro) = eb;
+      *reinterpret_cast<f32x4*>(ws.Qg + ro) = qgm;
+      *reinterpret_cast<f32x4*>(ws.Kt + ro) = kt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sK[r * HP + c4 + i] = kv[i];
+        sX[r * HP + c4 + i] = ev[i];
+        sQ[r * HP + c4 + i] = qv[i];
+        sG[r * HP + c4 + i] = G[u][i];
+      }
+    }
+    if (rg == 0) {
+      *reinterpret_cast<f32x4*>(ws.gC + ch * DK + cb + c4) =
+          f32x4{fexp(GC[0]), fexp(GC[1]), fexp(GC[2]), fexp(GC[3])};
+    }
+    __syncthreads();
+    // ---- Gram sums over the half's channels ----------------------------------
+    if (jb <= ib) {
+      for (int c = 0; c < CHH; ++c) {
+        float xi[4], qi[4], kj[4], gi[4], gj[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int i = 4 * ib + a, j = 4 * jb + a;
+          xi[a] = sX[i * HP + c];
+          qi[a] = sQ[i * HP + c];
+          kj[a] = sK[j * HP + c];
+          if (decay == 2) {
+            gi[a] = sG[i * HP + c];
+            gj[a] = sG[j * HP + c];
+          }
+        }
+        if (decay == 2) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              // exponent clamped at 0: entries above the diagonal are discarded
+              const float kd = kj[b] * fexp(fminf(gi[a] - gj[b], 0.f));
+              accT[a][b] = __builtin_fmaf(xi[a], kd, accT[a][b]);
+              accA[a][b] = __builtin_fmaf(qi[a], kd, accA[a][b]);
+            }
+        } else {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              accT[a][b] = __builtin_fmaf(xi[a], kj[b], accT[a][b]);
+              accA[a][b] = __builtin_fmaf(qi[a], kj[b], accA[a][b]);
+            }
+        }
+      }
+    }
+  }
+  // ---- Aqk to the record, T to LDS (dense [64][64], zeros above the masks) -
+  __syncthreads();  // every Gram read of the operand arrays is done
+  float* sT = lds + L::oK;   // [64][HP] T
+  float* sAi = lds + L::oX;  // [64][HP] A = (I + T)^{-1}
+  float* sP = lds + L::oQ;   // [48][HP] block products of the inverse's levels
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = 4 * ib + a;
+    f32x4 tv, av;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = 4 * jb + b;
+      // scalar decay or none: the common factor exp(G_i - G_j) of the channels
+      const float d = decay == 2 ? 1.f : fexp(fminf(sGs[i] - sGs[j], 0.f));
+      tv[b] = (jb <= ib && j < i) ? accT[a][b] * d : 0.f;
+      av[b] = (jb <= ib && j <= i) ? accA[a][b] * d : 0.f;
+      sT[i * HP + j] = tv[b];
+    }
+    *reinterpret_cast<f32x4*>(ws.A + ch * CH * CH + i * CH + 4 * jb) = av;
+    // under the per-value-channel beta every column has its own system: T
+    if (erase == 2) *reinterpret_cast<f32x4*>(ws.T + ch * CH * CH + i * CH + 4 * jb) = tv;
+  }
+  if (erase == 2) return;
+  __syncthreads();
+  // ---- A = (I + T)^{-1} ------------------------------------------------------
+  // level 0: the diagonal blocks (I + T_bb)^{-1}; thread 16 b + l solves for
+  // column l of block b (x = e_l, then x_i -= sum_{m < i} T_im x_m)
+  if (tid < CH) {
+    const int r0 = 16 * (tid >> 4), l = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i == l ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = __builtin_fmaf(sT[(r0 + i) * HP + r0 + m], x[m], s);
+      x[i] -= s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sAi[(r0 + i) * HP + r0 + l] = x[i];
+  }
+  __syncthreads();
+  // levels s = 1, 2, 3: the blocks (I, J) with I - J = s,
+  //   A_IJ = -A_II sum_{K = J}^{I - 1} T_IK A_KJ
+  // (every A_KJ on the right lies closer to the diagonal)
+  for (int sl = 1; sl < 4; ++sl) {
+    const int nel = (4 - sl) * 256;  // elements of the level's blocks
+    for (int e = tid; e < nel; e += NTHR) {
+      const int J = e >> 8, i = (e >> 4) & 15, j = e & 15, I = J + sl;
+      float acc = 0.f;
+      for (int kk = 16 * J; kk < 16 * I; ++kk) acc = __builtin_fmaf(sT[(16 * I + i) * HP + kk], sAi[kk * HP + 16 * J + j], acc);
+      sP[(16 * J + i) * HP + j] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < nel; e += NTHR) {
+      const int J = e >> 8, i = (e >> 4) & 15, j = e & 15, I = J + sl;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(sAi[(16 * I + i) * HP + 16 * I + m], sP[(16 * J + m) * HP + j], acc);
+      sAi[(16 * I + i) * HP + 16 * J + j] = -acc;
+    }
+    __syncthreads();
+  }
+  // A to the record in the place of T (zero above the diagonal)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + NTHR * u, i = e >> 4, j4 = (e & 15) * 4;
+    f32x4 av;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) av[b] = j4 + b <= i ? sAi[i * HP + j4 + b] : 0.f;
+    *reinterpret_cast<f32x4*>(ws.T + ch * CH * CH + i * CH + j4) = av;
+  }
+}
+
+// sum over the four lanes of each quad (DPP quad permutations), every lane
+// gets the total
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));  // lane ^ 1
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, true));  // lane ^ 2
+  return x;
+}
+
+// ---- pass 2 -----------------------------------------------------------------
+template <int DK, int DVS>
+struct PlainRecLay {
+  static constexpr int SP = DVS + 4;  // row stride (floats) of [rows][DVS] arrays: 16-byte rows
+  static constexpr int TP = CH + 1;   // row stride of the [64][64] arrays
+  static constexpr int oS = 0;                // [DK][SP] state slice
+  static constexpr int oA = oS + DK * SP;     // [64][TP] A (T under the per-value-channel beta)
+  static constexpr int oAq = oA + CH * TP;    // [64][TP] Aqk
+  static constexpr int oZ = oAq + CH * TP;    // [64][SP] written values z
+  static constexpr int oM = oZ + CH * SP;     // [64][SP] erase multiplier M
+  static constexpr int oW = oM + CH * SP;     // [64][SP] W
+  static constexpr int oES = oW + CH * SP;    // [64][SP] E_bar S, or R = Z - E_bar S
+  static constexpr int oQS = oES + CH * SP;   // [64][SP] Q_gamma S
+  static constexpr int TOTAL = oQS + CH * SP;
+  static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
+};
+
+template <int DK, int DVS>
+constexpr int plain_rec_lds_bytes() {
+  return PlainRecLay<DK, DVS>::TOTAL * 4;
+}
+
+template <class IO, int DK, int DVS, bool REC = false>
+__global__ __launch_bounds__(NTHR) void plain_rec_kernel(ChunkParams p, BwdWs ws) {
+  using L = PlainRecLay<DK, DVS>;
+  constexpr int SP = L::SP, TP = L::TP;
+  static_assert(DVS == 16, "row ri x 4 columns per thread; 16 columns x 16 lanes in the substitution");
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  float* sS = lds + L::oS;
+  float* sA = lds + L::oA;
+  float* sAq = lds + L::oAq;
+  float* sZ = lds + L::oZ;
+  float* sM = lds + L::oM;
+  float* sW = lds + L::oW;
+  float* sES = lds + L::oES;
+  float* sQS = lds + L::oQS;
+
+  const int tid = threadIdx.x;
+  // workgroup -> (batch, head, slice); blockIdx values that share a residue
+  // mod 8 run on one XCD, so the slices of a head read its records from one L2
+  int wid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
+  const int NS = p.nslices;
+  const int bh = wid / NS, slice = wid - bh * NS;
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const int T = p.T, H = p.H, DV = p.DV;
+  const int vbase = slice * DVS;
+  const int N = (T + CH - 1) / CH;
+  const int erase = p.erase, write = p.write;
+  const bool subst = erase == 2;  // per-value-channel beta: per-column systems
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* vg = reinterpret_cast<const IO*>(p.v);
+  IO* og = reinterpret_cast<IO*>(p.o);
+
+  for (int e = tid; e < DK * DVS; e += NTHR) {
+    const int c = e / DVS, v = e - c * DVS;
+    sS[c * SP + v] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + vbase + v] : 0.f;
+  }
+
+  // row layouts: thread = row ri x columns vq .. vq + 3 (quad member cq) for
+  // the row products; the channel sums of E_bar S and Q_gamma S are split
+  // over the quad (channels DK / 4 cq ..) and summed across it.  Update:
+  // channel cu x VPT columns.
+  const int ri = tid >> 2, cq = tid & 3, vq = 4 * cq;
+  const int jend = ((tid >> 6) + 1) * 16;  // the wave's rows are 16 (tid / 64) .. + 15
+  constexpr int CPQ = DK / 4;              // channels per quad member
+  constexpr int TPC = NTHR / DK, VPT = DVS / TPC;
+  const int cu = tid / TPC, vu = (tid % TPC) * VPT;
+
+  for (int n = 0; n < N; ++n) {
+    const int t0 = n * CH;
+    const size_t ch = (size_t)bh * N + n;
+    __syncthreads();  // the previous chunk's update of S and reads of W are complete
+    if constexpr (REC) {
+      for (int e = tid; e < DK * DVS; e += NTHR) {
+        const int c = e / DVS, v = e - c * DVS;
+        ws.S[(ch * DK + c) * DV + vbase + v] = sS[c * SP + v];
+      }
+    }
+    // ---- every load of the phase first: A (or T), Aqk, this thread's
+    // channels of its E_bar and Q_gamma rows, and z, M of its row and columns
+    f32x4 ra[4], rq[4], e4[CPQ / 4], q4[CPQ / 4];
+    float rv[4], rw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = *reinterpret_cast<const f32x4*>(ws.T + ch * CH * CH + 4 * (tid + NTHR * u));
+      if constexpr (!REC) rq[u] = *reinterpret_cast<const f32x4*>(ws.A + ch * CH * CH + 4 * (tid + NTHR * u));
+    }
+    {
+      const float* ebr = ws.Eb + (ch * CH + ri) * DK + CPQ * cq;
+      const float* qgr = ws.Qg + (ch * CH + ri) * DK + CPQ * cq;
+#pragma unroll
+      for (int u = 0; u < CPQ / 4; ++u) {
+        e4[u] = *reinterpret_cast<const f32x4*>(ebr + 4 * u);
+        q4[u] = *reinterpret_cast<const f32x4*>(qgr + 4 * u);
+      }
+      const size_t tok = seq0 + (size_t)min(t0 + ri, T - 1) * H;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        rv[u] = ldf(vg + tok * DV + vbase + vq + u);
+        rw[u] = subst ? p.beta[tok * DV + vbase + vq + u]
+                      : (write == 1 ? p.w[tok * DV + vbase + vq + u] : p.beta[tok]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * (tid + NTHR * u), r = e / CH, c = e - r * CH;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sA[r * TP + c + i] = ra[u][i];
+        if constexpr (!REC) sAq[r * TP + c + i] = rq[u][i];
+      }
+    }
+    // ---- E_bar S and Q_gamma S of row ri: partial sums over the thread's
+    // channels for all 16 columns, summed across the quad ---------------------
+    {
+      float es[DVS], qs[DVS];
+#pragma unroll
+      for (int v = 0; v < DVS; ++v) es[v] = qs[v] = 0.f;
+#pragma unroll
+      for (int u = 0; u < CPQ / 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* srow = sS + (CPQ * cq + 4 * u + i) * SP;
+#pragma unroll
+          for (int x = 0; x < DVS; x += 4) {
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(srow + x);
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              es[x + y] = __builtin_fmaf(e4[u][i], s4[y], es[x + y]);
+              qs[x + y] = __builtin_fmaf(q4[u][i], s4[y], qs[x + y]);
+            }
+          }
+        }
+#pragma unroll
+      for (int v = 0; v < DVS; ++v) {
+        es[v] = quad_sum(es[v]);
+        qs[v] = quad_sum(qs[v]);
+      }
+      // this thread's four columns (static selects over the quad member)
+      f32x4 e_m, q_m;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        e_m[y] = cq == 0 ? es[y] : cq == 1 ? es[4 + y] : cq == 2 ? es[8 + y] : es[12 + y];
+        q_m[y] = cq == 0 ? qs[y] : cq == 1 ? qs[4 + y] : cq == 2 ? qs[8 + y] : qs[12 + y];
+      }
+      const bool ok = t0 + ri < T;
+      f32x4 z, m;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        z[y] = ok ? rw[y] * rv[y] : 0.f;
+        m[y] = (ok && subst) ? rw[y] : 1.f;
+      }
+      *reinterpret_cast<f32x4*>(sQS + ri * SP + vq) = q_m;
+      if (subst) {
+        *reinterpret_cast<f32x4*>(sES + ri * SP + vq) = e_m;
+        *reinterpret_cast<f32x4*>(sZ + ri * SP + vq) = z;
+        *reinterpret_cast<f32x4*>(sM + ri * SP + vq) = m;
+      } else {
+        *reinterpret_cast<f32x4*>(sES + ri * SP + vq) = z - e_m;  // R = Z - E_bar S
+      }
+    }
+    // K_tail column cu of the chunk for the update, requested here so that it
+    // arrives during W and O
+    float kt[CH];
+    {
+      const float* ktc = ws.Kt + ch * CH * DK + cu;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) kt[j] = ktc[j * DK];
+    }
+    __syncthreads();
+    // ---- W ---------------------------------------------------------------------
+    if (!subst) {
+      // W = A R: row ri, columns vq .. (A is zero above the diagonal, so the
+      // wave runs to its last row)
+      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int j = 0; j < jend; ++j) w += sA[ri * TP + j] * *reinterpret_cast<const f32x4*>(sES + j * SP + vq);
+      *reinterpret_cast<f32x4*>(sW + ri * SP + vq) = w;
+      if constexpr (REC) *reinterpret_cast<f32x4*>(ws.W + (ch * CH + ri) * DV + vbase + vq) = w;
+    } else {
+      // forward substitution, column v = tid / 16, lanes split j
+      const int v = tid >> 4, part = tid & 15;
+      float wreg[4] = {0.f, 0.f, 0.f, 0.f};  // W[part + 16 m][v]
+      for (int i = 0; i < CH; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int j = part + 16 * m;
+          if (j < i) s = __builtin_fmaf(sA[i * TP + j], wreg[m], s);
+        }
+        s = sum16(s);
+        const float w = sZ[i * SP + v] - sM[i * SP + v] * (sES[i * SP + v] + s);
+        if ((i & 15) == part) wreg[i >> 4] = w;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        sW[(part + 16 * m) * SP + v] = wreg[m];
+        if constexpr (REC) ws.W[(ch * CH + part + 16 * m) * DV + vbase + v] = wreg[m];
+      }
+    }
+    __syncthreads();
+    // ---- O = Q_gamma S + Aqk W ---------------------------------------------------
+    if constexpr (!REC) {
+      f32x4 o = *reinterpret_cast<const f32x4*>(sQS + ri * SP + vq);
+#pragma unroll 4
+      for (int j = 0; j < jend; ++j) o += sAq[ri * TP + j] * *reinterpret_cast<const f32x4*>(sW + j * SP + vq);
+      const int t = t0 + ri;
+      if (t < T) {
+        IO* op = og + (seq0 + (size_t)t * H) * DV + vbase + vq;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) op[u] = (IO)o[u];
+      }
+    }
+    // ---- S <- Diag(gamma_C) S + K_tail^T W: channel cu, columns vu .. -------
+    {
+      const float gC = ws.gC[ch * DK + cu];
+      float s[VPT];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) s[u] = gC * sS[cu * SP + vu + u];
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int x = 0; x < VPT; x += 4) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(sW + j * SP + vu + x);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[x + i] = __builtin_fmaf(kt[j], w4[i], s[x + i]);
+        }
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) sS[cu * SP + vu + u] = s[u];
+    }
+  }
+  __syncthreads();
+  if (p.state_out) {
+    for (int e = tid; e < DK * DVS; e += NTHR) {
+      const int c = e / DVS, v = e - c * DVS;
+      p.state_out[((size_t)bh * DK + c) * DV + vbase + v] = sS[c * SP + v];
+    }
+  }
+}
+
+}  // namespace gdr

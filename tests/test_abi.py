@@ -183,12 +183,35 @@ def test_fp32_support_matrix(lib):
     assert _validate(lib, good_args(io=0, dk=64, dv=64, dv_split=64)) == E_UNSUP
     assert _validate(lib, good_args(io=0, dk=128, dv_split=32)) == E_UNSUP   # plain kernel: 16 columns
     assert _validate(lib, good_args(io=0, dk=128, T=1), STEP) == OK
-    # fp32 at dk = 128 runs the plain fp32 kernel (16-column slices, no workspace)
+    # fp32 at dk = 128 runs the plain fp32 kernel (16-column slices): one
+    # pass without a workspace, the two-pass form (records once per chunk)
+    # with one
     a = good_args(io=0, dk=128, B=1, H=2)
     info = GdrPlanInfo()
     assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
     assert info.dv_slice == 16 and info.block == 256 and info.passes == 1
-    assert _ws_size(lib, a) == (OK, 0)
+    st, need = _ws_size(lib, a)
+    assert st == OK and need == plain_record_bytes(1 * 2 * 4, 128)   # T = 200: 4 chunks
+    a.workspace, a.workspace_bytes = _addr(11), need
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+    assert info.passes == 2 and info.dv_slice == 16 and info.block == 256
+    assert info.grid == 2 * 8 and 0 < info.lds_bytes <= 160 * 1024 // 2   # two workgroups per CU
+
+
+def plain_record_bytes(nrec, dk):
+    """Workspace of the plain kernel's two-pass form: T, A_qk [64][64],
+    E_bar, Q_gamma, K_tail [64][dk], gamma_C [dk] fp32 per record, each
+    array 256-byte aligned."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return 2 * up(nrec * 64 * 64 * 4) + 3 * up(nrec * 64 * dk * 4) + up(nrec * dk * 4)
+
+
+@pytest.mark.parametrize("B,H,T,dk,io", [(1, 2, 200, 128, 0), (2, 3, 65, 128, 0), (1, 1, 1, 128, 0)])
+def test_plain_workspace_size(lib, B, H, T, dk, io):
+    a = good_args(io=io, dk=dk, dv=64, B=B, H=H, T=T)
+    st, n = _ws_size(lib, a)
+    assert st == OK, lib.gdr_last_error()
+    assert n == plain_record_bytes(B * H * ((T + 63) // 64), dk)
 
 
 def test_zero_length_sequence_needs_no_token_pointers(lib):
@@ -292,6 +315,14 @@ def test_noalloc_rejects_records_beyond_its_scratch(lib):
     assert st == OK and need > (64 << 20)
     assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(a), None) == E_SHAPE
     assert b"scratch" in lib.gdr_last_error()
+    # the plain fp32 kernel falls back to its single pass instead (it needs
+    # no records): the call gets past the host checks to the launch, which
+    # fails here only for want of a GPU
+    a = good_args(io=0, dk=128, B=8, H=16, T=4096)
+    st, need = _ws_size(lib, a)
+    assert st == OK and need > (64 << 20)
+    assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(a), None) not in (E_SHAPE, OK)
+    assert b"scratch" not in lib.gdr_last_error()
     # validation errors come first, as for gdr_chunk_fwd
     a = good_args(B=0)
     assert lib.gdr_chunk_fwd_noalloc(ctypes.byref(a), None) == E_SHAPE

@@ -86,18 +86,21 @@ CASES = {
 
 
 def _two_pass_form(cfg):
-    """Shapes on which chunk_fwd takes a two-pass form by default: bf16, dk
-    128, few heads (slices of 16 or 32 columns), and either kernel that has
-    one (per-channel decay; or no or a scalar decay with the beta erase gate)."""
+    """Shapes that have a two-pass form (taken with a workspace): bf16, dk
+    128, few heads (slices of 16 or 32 columns), and either pipelined kernel
+    (per-channel decay; or no or a scalar decay with the beta erase gate);
+    and every shape of the plain fp32 kernel (fp32 I/O at dk 128)."""
     dk, dv = cfg.get("dk", cfg["d"]), cfg.get("dv", cfg["d"])
+    if cfg["io"] == "f32":
+        return dk == 128
     decay = cfg.get("decay") or ("channel" if cfg["variant"] in ("kda", "gdn2") else "scalar")
     erase = cfg.get("erase") or ("channel" if cfg["variant"] == "gdn2" else "beta")
     kernel = decay == "channel" or erase == "beta"
-    return cfg["io"] == "bf16" and dk == 128 and kernel and cfg["B"] * cfg["H"] * dv // 64 < 256
+    return dk == 128 and kernel and cfg["B"] * cfg["H"] * dv // 64 < 256
 
 
-# every case as chunk_fwd runs it by default, and the two-pass cases once more
-# on the single-pass kernels
+# every case as chunk_fwd runs it by default (single pass), and the cases
+# with a two-pass form once more in that form
 PARITY = [(n, None) for n in sorted(CASES)] + [(n, True) for n in sorted(CASES) if _two_pass_form(CASES[n])]
 
 

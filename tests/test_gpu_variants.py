@@ -43,13 +43,15 @@ VARIANT_CASES = {
 }
 
 
+@pytest.mark.parametrize("two_pass", [False, True])
 @pytest.mark.parametrize("name", sorted(VARIANT_CASES))
-def test_variant_chunk_parity(name):
+def test_variant_chunk_parity(name, two_pass):
+    """Through the plain kernel's single pass and its two-pass form."""
     cfg = VARIANT_CASES[name]
-    say(f"[variant chunk] {name}: {cfg}")
+    say(f"[variant chunk] {name} two_pass={two_pass}: {cfg}")
     inp = make_inputs(cfg)
     d = to_dev(inp)
-    o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], **gpu_kwargs(d))
+    o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], two_pass=two_pass, **gpu_kwargs(d))
     torch.cuda.synchronize()
     o_ref, S_ref = run_oracle(inp)
     assert_parity(name, o.float().cpu().numpy(), S.cpu().numpy(), o_ref, S_ref, TOL[cfg["io"]])
