@@ -43,6 +43,7 @@
 #pragma once
 
 #include "plain_kernel.hpp"
+#include "plain_split_kernel.hpp"
 
 namespace gdr {
 
@@ -69,32 +70,39 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
 }
 
 // ---- pass A: the reverse state recurrence ---------------------------------
-template <class IO, int DK, int DVS>
+// LDS holds the chunk's two [64][64] matrices, the slice of dS and the rows
+// of dO, dW, dR (59 KB: two workgroups per CU); the factor rows and columns
+// of the record go straight to registers, every load of a phase issued
+// first.
+template <int DK, int DVS>
 struct BwdALay {
-  static constexpr int DKP = DK + 1, DVP = DVS + 1, TP = CH + 1;
-  static constexpr int oEb = 0, oQg = oEb + CH * DKP, oKt = oQg + CH * DKP;
-  static constexpr int oT = oKt + CH * DKP, oA = oT + CH * TP;
-  static constexpr int oS = oA + CH * TP;          // [DK][DVP] dS
-  static constexpr int oO = oS + DK * DVP;         // [64][DVP] dO
-  static constexpr int oW = oO + CH * DVP;         // [64][DVP] dW
-  static constexpr int oR = oW + CH * DVP;         // [64][DVP] dR
-  static constexpr int oC = oR + CH * DVP;         // [DK] gamma_C
-  static constexpr int TOTAL = oC + DK;
-  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+  static constexpr int SP = DVS + 4, TP = CH + 4;
+  static constexpr int oA = 0;             // [64][TP] A = (I + T)^{-1}
+  static constexpr int oAq = oA + CH * TP; // [64][TP] A_qk
+  static constexpr int oS = oAq + CH * TP; // [DK][SP] dS
+  static constexpr int oO = oS + DK * SP;  // [64][SP] dO
+  static constexpr int oW = oO + CH * SP;  // [64][SP] dW
+  static constexpr int oR = oW + CH * SP;  // [64][SP] dR
+  static constexpr int TOTAL = oR + CH * SP;
+  static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
 };
 
 template <class IO, int DK, int DVS>
 __global__ __launch_bounds__(NTHR) void bwd_state_kernel(BwdParams p) {
-  using L = BwdALay<IO, DK, DVS>;
-  constexpr int DKP = L::DKP, DVP = L::DVP, TP = L::TP;
-  static_assert(DVS == 16, "16 columns x 16 lanes in the substitution");
+  using L = BwdALay<DK, DVS>;
+  constexpr int SP = L::SP, TP = L::TP;
+  static_assert(DVS == 16, "row x 4 columns per thread over 16 columns");
   __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
-  float *sEb = lds + L::oEb, *sQg = lds + L::oQg, *sKt = lds + L::oKt, *sT = lds + L::oT, *sA = lds + L::oA;
-  float *sdS = lds + L::oS, *sdO = lds + L::oO, *sdW = lds + L::oW, *sdR = lds + L::oR, *sgC = lds + L::oC;
+  float *sA = lds + L::oA, *sAq = lds + L::oAq, *sdS = lds + L::oS;
+  float *sdO = lds + L::oO, *sdW = lds + L::oW, *sdR = lds + L::oR;
 
   const int tid = threadIdx.x;
+  // the slices of a head on one XCD (blockIdx residues mod 8), as the record pass
+  int wid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
   const int NS = p.f.nslices;
-  const int bh = blockIdx.x / NS, slice = blockIdx.x - bh * NS;
+  const int bh = wid / NS, slice = wid - bh * NS;
   const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
   const int T = p.f.T, H = p.f.H, DV = p.f.DV, N = p.nchunks;
   const int vbase = slice * DVS;
@@ -102,102 +110,126 @@ __global__ __launch_bounds__(NTHR) void bwd_state_kernel(BwdParams p) {
   const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   const BwdWs& ws = p.ws;
 
+  // row j x columns vq .. (quad member cq; the K_tail sums over the channels
+  // are split over the quad, DK / 4 channels each); dS update: channel cu x
+  // VPT columns
+  const int rj = tid >> 2, cq = tid & 3, vq = 4 * cq;
+  const int i0 = (tid >> 6) * 16;  // the wave's first row
+  constexpr int CPQ = DK / 4;
+  constexpr int TPC = NTHR / DK, VPT = DVS / TPC;
+  const int cu = tid / TPC, vu = (tid % TPC) * VPT;
+
   for (int e = tid; e < DK * DVS; e += NTHR) {
     const int c = e / DVS, v = e - c * DVS;
-    sdS[c * DVP + v] = p.d_st ? p.d_st[((size_t)bh * DK + c) * DV + vbase + v] : 0.f;
+    sdS[c * SP + v] = p.d_st ? p.d_st[((size_t)bh * DK + c) * DV + vbase + v] : 0.f;
   }
   for (int n = N - 1; n >= 0; --n) {
     const size_t ch = (size_t)bh * N + n;
     const int t0 = n * CH;
-    // the chunk's factors from the record pass: four floats per load, every
-    // load of a loop issued before its LDS stores
-    copy_rows<CH, DK, DKP>(sEb, ws.Eb + ch * CH * DK, tid);
-    copy_rows<CH, DK, DKP>(sQg, ws.Qg + ch * CH * DK, tid);
-    copy_rows<CH, DK, DKP>(sKt, ws.Kt + ch * CH * DK, tid);
-    copy_rows<CH, CH, TP>(sT, ws.T + ch * CH * CH, tid);
-    copy_rows<CH, CH, TP>(sA, ws.A + ch * CH * CH, tid);
-    for (int e = tid; e < DK; e += NTHR) sgC[e] = ws.gC[ch * DK + e];
-    {
-      constexpr int NV = CH * DVS / NTHR;
-      float rv[NV];
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int e = tid + NTHR * u, r = e / DVS, v = e - r * DVS;
-        rv[u] = ldf(dog + (seq0 + (size_t)min(t0 + r, T - 1) * H) * DV + vbase + v);
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int e = tid + NTHR * u, r = e / DVS, v = e - r * DVS;
-        sdO[r * DVP + v] = t0 + r < T ? rv[u] : 0.f;
-      }
-    }
+    __syncthreads();  // the previous chunk's update of dS and reads of dO, dR are complete
     // the gradient of the state leaving this chunk, for the product pass
     for (int e = tid; e < DK * DVS; e += NTHR) {
       const int c = e / DVS, v = e - c * DVS;
-      ws.dS[(ch * DK + c) * DV + vbase + v] = sdS[c * DVP + v];
+      ws.dS[(ch * DK + c) * DV + vbase + v] = sdS[c * SP + v];
     }
-    __syncthreads();
-    // dW = A_qk^T dO + K_tail dS: row j, 4 columns per thread
-    {
-      const int j = tid >> 2, vq = (tid & 3) * 4;
-      float s[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int i = j; i < CH; ++i) {
-        const float a = sA[i * TP + j];
+    // ---- loads: A and A_qk, dO of row rj, this thread's channels of K_tail row rj
+    f32x4 ra[4], rq[4], k4[CPQ / 4], o4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s[u] = __builtin_fmaf(a, sdO[i * DVP + vq + u], s[u]);
-      }
-      for (int c = 0; c < DK; ++c) {
-        const float kt = sKt[j * DKP + c];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s[u] = __builtin_fmaf(kt, sdS[c * DVP + vq + u], s[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sdW[j * DVP + vq + u] = s[u];
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = *reinterpret_cast<const f32x4*>(ws.T + ch * CH * CH + 4 * (tid + NTHR * u));
+      rq[u] = *reinterpret_cast<const f32x4*>(ws.A + ch * CH * CH + 4 * (tid + NTHR * u));
     }
-    __syncthreads();
-    // dR = A^T dW with A = (I + T)^{-1} from the record (in the place of T):
-    // row j, 4 columns per thread; A is zero above the diagonal, so the sum
-    // starts at the wave's first row
     {
-      const int j = tid >> 2, vq = (tid & 3) * 4;
-      float r[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int i = (tid >> 6) * 16; i < CH; ++i) {
-        const float a = sT[i * TP + j];
+      const float* ktr = ws.Kt + (ch * CH + rj) * DK + CPQ * cq;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = __builtin_fmaf(a, sdW[i * DVP + vq + u], r[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sdR[j * DVP + vq + u] = r[u];
-        ws.dR[(ch * CH + j) * DV + vbase + vq + u] = r[u];
-      }
+      for (int u = 0; u < CPQ / 4; ++u) k4[u] = *reinterpret_cast<const f32x4*>(ktr + 4 * u);
+      o4 = ldf4(dog + (seq0 + (size_t)min(t0 + rj, T - 1) * H) * DV + vbase + vq);
+      if (t0 + rj >= T) o4 = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    // dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR: 8 entries of row c per thread
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * (tid + NTHR * u), r = e / CH, c = e - r * CH;
+      *reinterpret_cast<f32x4*>(sA + r * TP + c) = ra[u];
+      *reinterpret_cast<f32x4*>(sAq + r * TP + c) = rq[u];
+    }
+    *reinterpret_cast<f32x4*>(sdO + rj * SP + vq) = o4;
+    // K_tail dS of row rj: partial sums over the thread's channels, summed
+    // across the quad
+    f32x4 kds;
     {
-      const int c = tid >> 1, v0 = (tid & 1) * 8;
-      if (c < DK) {
-        float s[8];
+      float acc[DVS];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s[u] = sgC[c] * sdS[c * DVP + v0 + u];
-        for (int i = 0; i < CH; ++i) {
-          const float qg = sQg[i * DKP + c], eb = sEb[i * DKP + c];
+      for (int v = 0; v < DVS; ++v) acc[v] = 0.f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            s[u] = __builtin_fmaf(qg, sdO[i * DVP + v0 + u], s[u]);
-            s[u] = __builtin_fmaf(-eb, sdR[i * DVP + v0 + u], s[u]);
+      for (int u = 0; u < CPQ / 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* srow = sdS + (CPQ * cq + 4 * u + i) * SP;
+#pragma unroll
+          for (int x = 0; x < DVS; x += 4) {
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(srow + x);
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[x + y] = __builtin_fmaf(k4[u][i], s4[y], acc[x + y]);
           }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sdS[c * DVP + v0 + u] = s[u];
-      }
+      for (int v = 0; v < DVS; ++v) acc[v] = quad_sum(acc[v]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        kds[y] = cq == 0 ? acc[y] : cq == 1 ? acc[4 + y] : cq == 2 ? acc[8 + y] : acc[12 + y];
+    }
+    // the columns of Q_gamma and E_bar for the update, requested here so that
+    // they arrive during dW and dR
+    float qcol[CH], ecol[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      qcol[i] = ws.Qg[(ch * CH + i) * DK + cu];
+      ecol[i] = ws.Eb[(ch * CH + i) * DK + cu];
     }
     __syncthreads();
+    // ---- dW = A_qk^T dO + K_tail dS: row rj (A_qk is zero above the
+    // diagonal, so the sum starts at the wave's first row)
+    {
+      f32x4 w = kds;
+      for (int i = i0; i < CH; ++i) w += sAq[i * TP + rj] * *reinterpret_cast<const f32x4*>(sdO + i * SP + vq);
+      *reinterpret_cast<f32x4*>(sdW + rj * SP + vq) = w;
+    }
+    __syncthreads();
+    // ---- dR = A^T dW ------------------------------------------------------------
+    {
+      f32x4 r = {0.f, 0.f, 0.f, 0.f};
+      for (int i = i0; i < CH; ++i) r += sA[i * TP + rj] * *reinterpret_cast<const f32x4*>(sdW + i * SP + vq);
+      *reinterpret_cast<f32x4*>(sdR + rj * SP + vq) = r;
+      *reinterpret_cast<f32x4*>(ws.dR + (ch * CH + rj) * DV + vbase + vq) = r;
+    }
+    __syncthreads();
+    // ---- dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR: channel cu -------
+    {
+      const float gC = ws.gC[ch * DK + cu];
+      float s[VPT];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) s[u] = gC * sdS[cu * SP + vu + u];
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+#pragma unroll
+        for (int x = 0; x < VPT; x += 4) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(sdO + i * SP + vu + x);
+          const f32x4 r = *reinterpret_cast<const f32x4*>(sdR + i * SP + vu + x);
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            s[x + y] = __builtin_fmaf(qcol[i], o[y], s[x + y]);
+            s[x + y] = __builtin_fmaf(-ecol[i], r[y], s[x + y]);
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) sdS[cu * SP + vu + u] = s[u];
+    }
   }
+  __syncthreads();
   if (p.dstate) {
     for (int e = tid; e < DK * DVS; e += NTHR) {
       const int c = e / DVS, v = e - c * DVS;
-      p.dstate[((size_t)bh * DK + c) * DV + vbase + v] = sdS[c * DVP + v];
+      p.dstate[((size_t)bh * DK + c) * DV + vbase + v] = sdS[c * SP + v];
     }
   }
 }
@@ -302,20 +334,25 @@ __global__ __launch_bounds__(NTHR) void bwd_prod_kernel(BwdParams p) {
 // The key channels are taken KC = 64 at a time, so that the chunk's k, e, q
 // and G columns of the pass and the whole dT and dA_qk fit in LDS together;
 // every inner-loop operand is then an LDS read (dT and dA_qk rows as
-// broadcasts).  Thread (wave w, lane c) owns channel c of the pass in rows
-// w, w + 4, ..., so each row of a pass is one wave and its sums over the
-// channels are wave reductions.
+// broadcasts).  Thread (wave w, lane c) owns channel c of the pass in 16
+// rows, so each row of a pass is one wave and its sums over the channels are
+// wave reductions.  Under a decay per key channel the weights d_ij[c] are
+// formed per term (rows w, w + 4, ...).  Under a scalar decay (or none)
+// d_ij is one number per token pair: the kernel forms D1 = dT (.) D and
+// D2 = dA_qk (.) D below the diagonal (and their transposes) once per
+// chunk, and the four sums are row products with them (rows 16 w .. + 15,
+// so that each wave's sums stop at its rows' bounds).
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
   constexpr int KC = 64, NPASS = DK / KC;
   constexpr int NP = NTHR / KC, RPP = CH / NP;   // 4 row partitions of 16 rows
   constexpr int VW = DV / 64;                    // waves per row of the value side
-  constexpr int TP = CH + 1;
+  constexpr int TP = CH + 4;  // 16-byte rows for the b128 reads of the scalar-decay products
   static_assert(DK % KC == 0, "key channels in passes of 64");
   __shared__ __attribute__((aligned(16))) float sK[CH * KC], sE[CH * KC], sQ[CH * KC], sG[CH * KC];
-  __shared__ __attribute__((aligned(16))) float sdT[CH * TP], sdA[CH * TP];
+  __shared__ __attribute__((aligned(16))) float sdT[CH * TP], sdA[CH * TP], sD1T[CH * TP], sD2T[CH * TP];
   __shared__ float sGC[KC], sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW], sDg[CH];
-  __shared__ float sBeta[CH], sLam[CH];
+  __shared__ float sBeta[CH], sLam[CH], sGt[CH], sDiag[CH], sRG[CH], sRX[CH];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int N = p.nchunks;
@@ -339,9 +376,36 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
     sBeta[r] = (t < T && (erase == 0 || write == 0)) ? p.f.beta[tok] : 0.f;
     sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
     sDg[r] = 0.f;
+    sRG[r] = 0.f;
+    sRX[r] = 0.f;
   }
   const int c = lane;
   const int par = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chan = decay == 2;
+  // rows of this thread: w, w + 4, ... (per-channel decay) or 16 w .. + 15
+  auto row_of = [&](int m) { return chan ? par + NP * m : 16 * par + m; };
+
+  if (!chan) {
+    // the scalar decay's prefix sums G_t (zero past T), then
+    // D1 = dT (.) D, D2 = dA_qk (.) D strictly below the diagonal (in place;
+    // the diagonal of dA_qk kept apart) and their transposes
+    if (tid < CH) {
+      const int t = t0 + tid;
+      const float g = (decay == 1 && t < T) ? p.f.g[seq0 + (size_t)t * H] : 0.f;
+      sGt[tid] = wave_incl_scan(g);
+    }
+    __syncthreads();
+    for (int e = tid; e < CH * CH; e += NTHR) {
+      const int i = e >> 6, j = e & 63;
+      const float d = j < i ? fexp(sGt[i] - sGt[j]) : 0.f;
+      const float d1 = sdT[i * TP + j] * d, d2 = sdA[i * TP + j] * d;
+      if (i == j) sDiag[i] = sdA[i * TP + j];
+      sdT[i * TP + j] = d1;
+      sdA[i * TP + j] = d2;
+      sD1T[j * TP + i] = d1;
+      sD2T[j * TP + i] = d2;
+    }
+  }
 
   for (int ps = 0; ps < NPASS; ++ps) {
     const int cg = ps * KC + c;  // key channel of this thread
@@ -378,7 +442,7 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    if (tid < KC) {
+    if (chan && tid < KC) {
       float run = 0.f;
       for (int r = 0; r < CH; ++r) {
         run += sG[r * KC + tid];
@@ -387,37 +451,89 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
       sGC[tid] = run;
     }
     // the product pass's results for my rows
-    float dEb[RPP], dQg[RPP], dKt[RPP];
+    float dEb[RPP], dQg[RPP], dKt[RPP], bI[RPP];
 #pragma unroll
     for (int m = 0; m < RPP; ++m) {
-      const size_t at = (ch * CH + par + NP * m) * DK + cg;
+      const size_t at = (ch * CH + row_of(m)) * DK + cg;
       dEb[m] = ws.Eb[at];
       dQg[m] = ws.Qg[at];
       dKt[m] = ws.Kt[at];
+      const int t = t0 + row_of(m);
+      bI[m] = (erase == 1 && t < T) ? p.f.b[(seq0 + (size_t)t * H) * DK + cg] : 0.f;
     }
     __syncthreads();
-    const float GC = sGC[c];
+    const float GC = chan ? sGC[c] : sGt[CH - 1];
+    // scalar decay: the four sums of my 16 rows as row products with D1, D2
+    // (zero at and above the diagonal) and their transposes
+    float sP[RPP], sPq[RPP], sRm[RPP], sRq[RPP];
+    if (!chan) {
+      static_assert(RPP == 16, "16 rows per wave");
+      const int i0 = 16 * par;
+#pragma unroll
+      for (int m = 0; m < RPP; ++m) sP[m] = sPq[m] = sRm[m] = sRq[m] = 0.f;
+      for (int j0 = 0; j0 < i0 + 16; j0 += 4) {  // j < i
+        float kj[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kj[u] = sK[(j0 + u) * KC + c];
+#pragma unroll
+        for (int m = 0; m < RPP; ++m) {
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(sdT + (i0 + m) * TP + j0);
+          const f32x4 d2 = *reinterpret_cast<const f32x4*>(sdA + (i0 + m) * TP + j0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            sP[m] = __builtin_fmaf(d1[u], kj[u], sP[m]);
+            sPq[m] = __builtin_fmaf(d2[u], kj[u], sPq[m]);
+          }
+        }
+      }
+      for (int j0 = i0; j0 < CH; j0 += 4) {  // i2 > i
+        float ej[4], qj[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ej[u] = sE[(j0 + u) * KC + c];
+          qj[u] = sQ[(j0 + u) * KC + c];
+        }
+#pragma unroll
+        for (int m = 0; m < RPP; ++m) {
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(sD1T + (i0 + m) * TP + j0);
+          const f32x4 d2 = *reinterpret_cast<const f32x4*>(sD2T + (i0 + m) * TP + j0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            sRm[m] = __builtin_fmaf(d1[u], ej[u], sRm[m]);
+            sRq[m] = __builtin_fmaf(d2[u], qj[u], sRq[m]);
+          }
+        }
+      }
+    }
     float dGr[RPP], xkt[RPP];
+#pragma unroll
     for (int m = 0; m < RPP; ++m) {
-      const int i = par + NP * m;  // wave-uniform
-      const float gi = sG[i * KC + c];
+      const int i = row_of(m);  // wave-uniform
+      const float gi = chan ? sG[i * KC + c] : sGt[i];
       const float gam = fexp(gi), tl = fexp(GC - gi);
       const float ki = sK[i * KC + c], ei = sE[i * KC + c], qi = sQ[i * KC + c];
       // off-diagonal sums (the diagonal of A_qk has d_ii = 1 and does not
       // depend on G: its two contributions to dG cancel exactly, so it is
       // kept out of dG rather than added and cancelled in fp32)
       float P = 0.f, Pq = 0.f, Rm = 0.f, Rq = 0.f;
-      for (int j = 0; j < i; ++j) {
-        const float kd = sK[j * KC + c] * fexp(gi - sG[j * KC + c]);
-        P = __builtin_fmaf(sdT[i * TP + j], kd, P);
-        Pq = __builtin_fmaf(sdA[i * TP + j], kd, Pq);
+      if (chan) {
+        for (int j = 0; j < i; ++j) {
+          const float kd = sK[j * KC + c] * fexp(gi - sG[j * KC + c]);
+          P = __builtin_fmaf(sdT[i * TP + j], kd, P);
+          Pq = __builtin_fmaf(sdA[i * TP + j], kd, Pq);
+        }
+        for (int i2 = i + 1; i2 < CH; ++i2) {
+          const float d = fexp(sG[i2 * KC + c] - gi);
+          Rm = __builtin_fmaf(sdT[i2 * TP + i], sE[i2 * KC + c] * d, Rm);
+          Rq = __builtin_fmaf(sdA[i2 * TP + i], sQ[i2 * KC + c] * d, Rq);
+        }
+      } else {
+        P = sP[m];
+        Pq = sPq[m];
+        Rm = sRm[m];
+        Rq = sRq[m];
       }
-      for (int i2 = i + 1; i2 < CH; ++i2) {
-        const float d = fexp(sG[i2 * KC + c] - gi);
-        Rm = __builtin_fmaf(sdT[i2 * TP + i], sE[i2 * KC + c] * d, Rm);
-        Rq = __builtin_fmaf(sdA[i2 * TP + i], sQ[i2 * KC + c] * d, Rq);
-      }
-      const float diag = sdA[i * TP + i];
+      const float diag = chan ? sdA[i * TP + i] : sDiag[i];
       const float de = __builtin_fmaf(gam, dEb[m], P);
       float dqd = __builtin_fmaf(gam, dQg[m], __builtin_fmaf(diag, ki, Pq));
       float dkd = tl * dKt[m] + Rm + __builtin_fmaf(diag, qi, Rq);
@@ -428,7 +544,7 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
       const int t = t0 + i;
       const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
       if (erase == 1) {
-        const float bi = t < T ? p.f.b[tok * DK + cg] : 0.f;
+        const float bi = bI[m];
         if (t < T) p.db[tok * DK + cg] = de * ki;
         dkd = __builtin_fmaf(bi, de, dkd);
       } else {
@@ -444,23 +560,33 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
         p.dq[tok * DK + cg] = dqd;
         p.dk[tok * DK + cg] = dkd;
       }
-      rb = wave_sum(rb);
-      rl = wave_sum(rl);
+      rb = wave_total(rb);
+      rl = wave_total(rl);
+      // scalar decay: the row sums over the channels of dG and of the K_tail
+      // terms, from which the per-token dg follows after the passes
+      float rg = 0.f, rx = 0.f;
+      if (decay == 1) {
+        rg = wave_total(dGr[m]);
+        rx = wave_total(xkt[m]);
+      }
       if (lane == 0) {
         sRb[i][ps] = rb;
         sRl[i][ps] = rl;
+        sRG[i] += rg;
+        sRX[i] += rx;
       }
     }
+    if (chan) {
     __syncthreads();  // sG takes dG, sE the K_tail terms
 #pragma unroll
     for (int m = 0; m < RPP; ++m) {
-      const int i = par + NP * m;
+      const int i = row_of(m);
       sG[i * KC + c] = dGr[m];
       sE[i * KC + c] = xkt[m];
     }
     __syncthreads();
     // dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC
-    if (decay != 0 && tid < KC) {
+    if (tid < KC) {
       float pre = 0.f;
       for (int r = 0; r < CH; ++r) {  // exclusive prefix of the K_tail terms
         const float x = sE[r * KC + tid];
@@ -472,41 +598,55 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
       for (int r = CH - 1; r >= 0; --r) {
         run += sG[r * KC + tid];
         const float dgv = run + sE[r * KC + tid] + base;
-        if (decay == 2) {
-          if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + ps * KC + tid] = dgv;
-        } else {
-          sG[r * KC + tid] = dgv;
-        }
+        if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + ps * KC + tid] = dgv;
       }
     }
-    if (decay == 1) {
-      __syncthreads();
-      if (tid < CH) {
-        float s = 0.f;
-        for (int c2 = 0; c2 < KC; ++c2) s += sG[tid * KC + c2];
-        sDg[tid] += s;
-      }
     }
   }
-  // ---- value side: dZ = dR
+  // scalar decay: dg_t = sum_{r>=t} RG_r + sum_{j<t} RX_j + gamma_C sum_c sC[c]
+  // (the per-channel form summed over the channels), by wave prefix sums
+  if (decay == 1) {
+    __syncthreads();
+    if (tid < CH) {
+      float sc = 0.f;
+      for (int c2 = tid; c2 < DK; c2 += CH) sc += ws.gC[ch * DK + c2];
+      const float base = fexp(sGt[CH - 1]) * wave_total(sc);
+      const float rg = sRG[tid], rx = sRX[tid];
+      const float ig = wave_incl_scan(rg), ix = wave_incl_scan(rx);
+      sDg[tid] = (lane_value(ig, 63) - ig + rg) + (ix - rx) + base;
+    }
+  }
+  // ---- value side: dZ = dR (every load of the thread issued first; each
+  // wave covers 64 columns of one row per step)
   {
+    constexpr int NE = CH * DV / NTHR;
     const float* dz = ws.dR + ch * CH * DV;
-    for (int e = tid; e < CH * DV; e += NTHR) {
-      const int r = e / DV, v = e - r * DV;
+    float zr[NE], vr[NE], wr[NE];
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = tid + NTHR * u, r = e / DV, v = e - r * DV;
+      const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+      zr[u] = dz[e];
+      vr[u] = ldf(vg + tok * DV + v);
+      wr[u] = write == 1 ? p.f.w[tok * DV + v] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = tid + NTHR * u, r = e / DV, v = e - r * DV;
       const int t = t0 + r;
       const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
-      const float z = dz[e], vv = ldf(vg + tok * DV + v);
+      const float z = zr[u], vv = vr[u];
       float zb = 0.f;
       if (t < T) {
         if (write == 1) {
           p.dw[tok * DV + v] = z * vv;
-          p.dv[tok * DV + v] = p.f.w[tok * DV + v] * z;
+          p.dv[tok * DV + v] = wr[u] * z;
         } else {
           zb = z * vv;
           p.dv[tok * DV + v] = sBeta[r] * z;
         }
       }
-      zb = wave_sum(zb);
+      zb = wave_total(zb);
       if (lane == 0) sRz[r][v >> 6] = zb;
     }
   }

@@ -53,6 +53,10 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
+// sum over the 64 lanes of a wave as the last lane of its DPP prefix sum
+// (every lane active; the result is wave-uniform)
+__device__ __forceinline__ float wave_total(float x) { return lane_value(wave_incl_scan(x), 63); }
+
 // A matrix in LDS: element (r, c) at p[r * rs + c * cs].
 template <class T>
 struct View {
