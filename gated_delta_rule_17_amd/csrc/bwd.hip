@@ -20,9 +20,13 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
   const int ns = p.f.nslices, N = p.nchunks;
   // record pass: the chunk records once per chunk, then the recurrence of
   // each slice writing its entering states and W
+  // (the recurrence on the matrix cores, slices of 64 columns; the backward
+  // takes no per-value-channel beta)
   if (N > 0) {
     hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws);
-    hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, true>), dim3(BH * ns), dim3(NTHR), 0, s, p.f, p.ws);
+    ChunkParams f64 = p.f;
+    f64.nslices = DV / 64;
+    hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64, p.ws);
   }
   hipLaunchKernelGGL((bwd_state_kernel<IO, DK, 16>), dim3(BH * ns), dim3(NTHR), 0, s, p);
   if (N > 0) {

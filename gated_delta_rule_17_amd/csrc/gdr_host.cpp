@@ -289,7 +289,10 @@ gdr_status plan_impl(const gdr_args* a, int op, gdr_plan_info* out, Workspace ws
       const gdr::ChunkKernel kern = kernel_for(a);
       const int gm = gdr::gate_mode(a->erase, a->write);
       if (kern == gdr::kPlain) {
-        pi.lds_bytes = dvs == 16 ? gdr::plain_split_lds(a->dk) : -1;
+        // the two-pass plain form picks its own slice width
+        pi.dv_slice = gdr::plain_split_slice(a->erase, a->dv, a->dv_split);
+        pi.grid = static_cast<int32_t>(BH * (a->dv / pi.dv_slice));
+        pi.lds_bytes = gdr::plain_split_lds(a->dk, pi.dv_slice);
         pi.block = 256;
       } else {
         pi.lds_bytes = kern == gdr::kChan ? gdr::chan_split_lds(gm, a->dk, dvs) : gdr::pipe_split_lds(gm, a->dk, dvs);
@@ -453,7 +456,7 @@ gdr_status chunk_fwd_impl(const gdr_args* a, void* stream, Workspace ws, bool ch
     if (kern == gdr::kPlain) {
       gdr::BwdWs rec;
       gdr::plain_split_layout(prep_grid, a->dk, static_cast<char*>(ws.ptr), &rec);
-      e = gdr::launch_plain_split(p, rec, a->io == GDR_BF16, a->dk, pi.grid, prep_grid, st);
+      e = gdr::launch_plain_split(p, rec, a->io == GDR_BF16, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
     } else if (kern == gdr::kChan) {
       e = gdr::launch_chan_split(gm, p, ws.ptr, a->dk, pi.dv_slice, pi.grid, prep_grid, st);
     } else {

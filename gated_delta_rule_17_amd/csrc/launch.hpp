@@ -110,10 +110,16 @@ hipError_t launch_plain(const ChunkParams& p, bool bf16io, int dk, int grid, hip
 // Its two-pass form (plain_split_kernel.hpp): prep_grid chunk workgroups
 // write the records to the arrays of ws (plain_split_layout in
 // bwd_params.hpp), then grid slice workgroups run the recurrence.
+// Its recurrence runs on the matrix cores with slices of 64 columns, or on
+// the vector ALUs with slices of 16 (the per-value-channel beta, erase kind
+// 2, whose substitution differs per column; or a caller's 16-column split).
 struct BwdWs;
-int plain_split_lds(int dk);
-hipError_t launch_plain_split(const ChunkParams& p, const BwdWs& ws, bool bf16io, int dk, int grid, int prep_grid,
-                              hipStream_t s);
+inline int plain_split_slice(int erase, int dv, int dv_split) {
+  return (erase == 2 || dv % 64 != 0 || dv_split == 16) ? 16 : 64;
+}
+int plain_split_lds(int dk, int dvs);
+hipError_t launch_plain_split(const ChunkParams& p, const BwdWs& ws, bool bf16io, int dk, int dvs, int grid,
+                              int prep_grid, hipStream_t s);
 
 // Chunk kernel chosen for (io, dk, decay kind, erase kind, qmix): the plain
 // fp32 kernel takes the per-value-channel beta (erase 2), a time-varying

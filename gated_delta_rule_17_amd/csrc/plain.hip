@@ -27,28 +27,37 @@ hipError_t launch_plain(const ChunkParams& p, bool bf16io, int dk, int grid, hip
   return hipErrorInvalidValue;
 }
 
-int plain_split_lds(int dk) {
-#define X(DK) if (dk == DK) return plain_rec_lds_bytes<DK, 16>();
+int plain_split_lds(int dk, int dvs) {
+#define X(DK)                                                                    \
+  if (dk == DK && dvs == 64) return plain_mrec_lds_bytes<DK>();                  \
+  if (dk == DK && dvs == 16) return plain_rec_lds_bytes<DK, 16>();
   GDR_PLAIN_CASES(X)
 #undef X
   return -1;
 }
 
+// the recurrence: on the matrix cores for 64-column slices, on the vector
+// ALUs for 16-column ones (p.nslices follows the slice width)
 template <class IO, int DK>
-hipError_t plain_split_sequence(const ChunkParams& p, const BwdWs& ws, int grid, int prep_grid, hipStream_t s) {
+hipError_t plain_split_sequence(const ChunkParams& p, const BwdWs& ws, int dvs, int grid, int prep_grid,
+                                hipStream_t s) {
+  if (dvs == 64 && p.erase == 2) return hipErrorInvalidValue;  // the substitution needs 16-column slices
   hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+  if (dvs == 64)
+    hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+  else
+    hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
   return hipGetLastError();
 }
 
-hipError_t launch_plain_split(const ChunkParams& p, const BwdWs& ws, bool bf16io, int dk, int grid, int prep_grid,
-                              hipStream_t s) {
+hipError_t launch_plain_split(const ChunkParams& p, const BwdWs& ws, bool bf16io, int dk, int dvs, int grid,
+                              int prep_grid, hipStream_t s) {
 #define X(DK)                                                                                          \
   if (dk == DK)                                                                                        \
-    return bf16io ? plain_split_sequence<bf16, DK>(p, ws, grid, prep_grid, s)                          \
-                  : plain_split_sequence<float, DK>(p, ws, grid, prep_grid, s);
+    return bf16io ? plain_split_sequence<bf16, DK>(p, ws, dvs, grid, prep_grid, s)                     \
+                  : plain_split_sequence<float, DK>(p, ws, dvs, grid, prep_grid, s);
   GDR_PLAIN_CASES(X)
 #undef X
   return hipErrorInvalidValue;

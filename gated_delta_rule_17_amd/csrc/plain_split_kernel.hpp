@@ -556,3 +556,233 @@ __global__ __launch_bounds__(NTHR) void plain_rec_kernel(ChunkParams p, BwdWs ws
 }
 
 }  // namespace gdr
+
+namespace gdr {
+
+// ---- pass 2 on the matrix cores ---------------------------------------------
+// The same recurrence with every product on v_mfma_f32_16x16x4_f32 (fp32
+// operands, fp32 accumulation), for every gate kind but the per-value-channel
+// beta: one workgroup of four waves per (batch, head, 64-column slice), wave
+// w owning columns 16 w .. + 15 and the state S of those columns in
+// accumulators: register r of block b of lane l holds
+// S[16 b + 4 (l / 16) + r][16 w + l % 16].
+//
+// Each product contracts over 4-wide k-steps; k-step (b, r) takes, in lane
+// group g = l / 16, the channel (or token) 16 b + 4 g + r, which is where
+// that lane's accumulators hold it.  So the state, R, W and the other
+// accumulator tiles serve as B operands as they are, and the A operands are
+// 16-byte LDS reads of four consecutive channels (tokens) of one row:
+//   ES, QS  = E_bar S, Q_gamma S          A = E_bar, Q_gamma rows (token x channel)
+//   W       = A (Z - ES)                  A = A rows (token x token), lower blocks only
+//   O       = QS + Aqk W                  A = Aqk rows
+//   S      <- Diag(gamma_C) S + K_tail^T W   A = K_tail^T rows (channel x token)
+// The chunk's records go to LDS once per chunk (K_tail transposed on the
+// way); the next chunk's are loaded into registers while this one computes.
+template <int DK>
+struct PlainMrecLay {
+  static constexpr int SE = DK + 4;  // rows of E_bar, Q_gamma (16-byte rows; 4 banks apart)
+  static constexpr int SA = CH + 4;  // rows of A, Aqk, K_tail^T
+  static constexpr int oEb = 0, oQg = oEb + CH * SE, oKtT = oQg + CH * SE;
+  static constexpr int oA = oKtT + DK * SA, oAq = oA + CH * SA, oGC = oAq + CH * SA;
+  static constexpr int TOTAL = oGC + DK;
+  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <int DK>
+constexpr int plain_mrec_lds_bytes() {
+  return PlainMrecLay<DK>::TOTAL * 4;
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <class IO, int DK, bool REC = false>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
+  using L = PlainMrecLay<DK>;
+  constexpr int SE = L::SE, SA = L::SA, NB = DK / 16;
+  constexpr int DVS = 64;
+  constexpr int NQ_E = CH * DK / 4 / NTHR;  // 16-byte pieces per thread of a [64][DK] record array
+  constexpr int NQ_A = CH * CH / 4 / NTHR;  // of a [64][64] array
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  float* sEb = lds + L::oEb;
+  float* sQg = lds + L::oQg;
+  float* sKtT = lds + L::oKtT;
+  float* sA = lds + L::oA;
+  float* sAq = lds + L::oAq;
+  float* sGC = lds + L::oGC;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  int wid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
+  const int NS = p.nslices;
+  const int bh = wid / NS, slice = wid - bh * NS;
+  const int bb = bh / p.H, hh = bh - bb * p.H;
+  const int T = p.T, H = p.H, DV = p.DV;
+  const int N = (T + CH - 1) / CH;
+  const int write = p.write;
+  const int col = slice * DVS + 16 * wave + l16;  // this lane's value column
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* vg = reinterpret_cast<const IO*>(p.v);
+  IO* og = reinterpret_cast<IO*>(p.o);
+
+  f32x4 S[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[b][r] = p.state_in ? p.state_in[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] : 0.f;
+
+  // registers of a chunk's records and of this lane's z inputs
+  struct Rec {
+    f32x4 eb[NQ_E], qg[NQ_E], kt[NQ_E], a[NQ_A], aq[NQ_A];
+    float gc;
+    float v[16], gt[16];  // rows 16 I + 4 g + r of this lane's column
+  };
+  auto load = [&](int n, Rec& R) __attribute__((always_inline)) {
+    const size_t ch = (size_t)bh * N + n;
+#pragma unroll
+    for (int u = 0; u < NQ_E; ++u) {
+      const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
+      R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
+      R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
+      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + o);
+    }
+#pragma unroll
+    for (int u = 0; u < NQ_A; ++u) {
+      const size_t o = ch * CH * CH + 4 * (tid + NTHR * u);
+      R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
+      if constexpr (!REC) R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
+    }
+    R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = 4 * I + r;
+        const size_t tok = seq0 + (size_t)min(n * CH + 16 * I + 4 * g + r, T - 1) * H;
+        R.v[k] = ldf(vg + tok * DV + col);
+        R.gt[k] = write == 1 ? p.w[tok * DV + col] : p.beta[tok];
+      }
+  };
+  auto stage = [&](const Rec& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NQ_E; ++u) {
+      const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
+      *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
+      *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sKtT[(c + i) * SA + t] = R.kt[u][i];
+    }
+#pragma unroll
+    for (int u = 0; u < NQ_A; ++u) {
+      const int e = 4 * (tid + NTHR * u), t = e / CH, c = e - t * CH;
+      *reinterpret_cast<f32x4*>(sA + t * SA + c) = R.a[u];
+      if constexpr (!REC) *reinterpret_cast<f32x4*>(sAq + t * SA + c) = R.aq[u];
+    }
+    if (tid < DK) sGC[tid] = R.gc;
+  };
+
+  Rec R;
+  if (N > 0) load(0, R);
+  for (int n = 0; n < N; ++n) {
+    const int t0 = n * CH;
+    const size_t ch = (size_t)bh * N + n;
+    __syncthreads();  // every read of the previous chunk's LDS records is done
+    stage(R);
+    float z[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bool ok = t0 + 16 * (k >> 2) + 4 * g + (k & 3) < T;  // row 16 I + 4 g + r, k = 4 I + r
+      z[k] = ok ? R.gt[k] * R.v[k] : 0.f;
+    }
+    __syncthreads();
+    if (n + 1 < N) load(n + 1, R);
+    if constexpr (REC) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ws.S[(ch * DK + 16 * b + 4 * g + r) * DV + col] = S[b][r];
+    }
+    // ---- ES, QS -----------------------------------------------------------------
+    f32x4 W[4], QS[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 es = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const f32x4 ae = *reinterpret_cast<const f32x4*>(sEb + (16 * I + l16) * SE + 16 * b + 4 * g);
+        const f32x4 aq = *reinterpret_cast<const f32x4*>(sQg + (16 * I + l16) * SE + 16 * b + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          es = mfma_f32(ae[r], S[b][r], es);
+          qs = mfma_f32(aq[r], S[b][r], qs);
+        }
+      }
+      QS[I] = qs;
+      // R = Z - E_bar S (rows 16 I + 4 g + r of this lane's column)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) W[I][r] = z[4 * I + r] - es[r];
+    }
+    // ---- W = A R, block rows from the last (each reads R blocks J <= I) --------
+#pragma unroll
+    for (int I = 3; I >= 0; --I) {
+      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * I + l16) * SA + 16 * J + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w = mfma_f32(a[r], W[J][r], w);
+      }
+      W[I] = w;
+    }
+    if constexpr (REC) {
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ws.W[(ch * CH + 16 * I + 4 * g + r) * DV + col] = W[I][r];
+    } else {
+      // ---- O = QS + Aqk W -------------------------------------------------------
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 o = QS[I];
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(sAq + (16 * I + l16) * SA + 16 * J + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o = mfma_f32(a[r], W[J][r], o);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 16 * I + 4 * g + r;
+          if (t < T) og[(seq0 + (size_t)t * H) * DV + col] = (IO)o[r];
+        }
+      }
+    }
+    // ---- S <- Diag(gamma_C) S + K_tail^T W ---------------------------------------
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + 16 * b + 4 * g);
+      f32x4 s = S[b] * gc;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sKtT + (16 * b + l16) * SA + 16 * J + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s = mfma_f32(a[r], W[J][r], s);
+      }
+      S[b] = s;
+    }
+  }
+  if (p.state_out) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.state_out[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] = S[b][r];
+  }
+}
+
+}  // namespace gdr

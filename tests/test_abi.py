@@ -194,8 +194,15 @@ def test_fp32_support_matrix(lib):
     assert st == OK and need == plain_record_bytes(1 * 2 * 4, 128)   # T = 200: 4 chunks
     a.workspace, a.workspace_bytes = _addr(11), need
     assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
-    assert info.passes == 2 and info.dv_slice == 16 and info.block == 256
-    assert info.grid == 2 * 8 and 0 < info.lds_bytes <= 160 * 1024 // 2   # two workgroups per CU
+    # the two-pass recurrence on the matrix cores: 64-column slices
+    assert info.passes == 2 and info.dv_slice == 64 and info.block == 256
+    assert info.grid == 2 * 2 and 0 < info.lds_bytes <= 160 * 1024
+    # a caller's 16-column split, and the per-value-channel beta, keep the
+    # vector-ALU recurrence (16 columns, two workgroups per CU)
+    a.dv_split = 16
+    assert lib.gdr_plan(ctypes.byref(a), CHUNK, ctypes.byref(info)) == OK
+    assert info.passes == 2 and info.dv_slice == 16 and info.grid == 2 * 8
+    assert 0 < info.lds_bytes <= 160 * 1024 // 2
 
 
 def plain_record_bytes(nrec, dk):

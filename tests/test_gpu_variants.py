@@ -194,3 +194,31 @@ def test_epilogue_fused(entry, io):
     o_ref, S_ref = run_oracle(inp)
     y_ref = _epilogue_ref(inp, o_ref)
     assert_parity(f"epilogue {entry} {io}", y.float().cpu().numpy(), S.cpu().numpy(), y_ref, S_ref, TOL[io])
+
+
+# ---- the plain fp32 kernel's two recurrences ----------------------------------
+
+@pytest.mark.parametrize("name,cfg", [
+    ("gdn_f32_d128", config(F, B=2, H=2, T=300, d=128, decay_shift=-3.0, state_std=0.1)),
+    ("kda_f32_d128_dv64", config(F, variant="kda", B=1, H=3, T=200, dk=128, dv=64, decay_shift=-4.0)),
+    ("kda_bf16_lam_t", config(K, B=1, H=2, T=150, qmix=True, lam_t=True, decay_shift=-4.0)),
+    ("gdn2_bf16_value_beta", config(G2, B=1, H=2, T=150, value_beta=True, decay_shift=-4.0)),
+])
+def test_plain_two_pass_recurrences(name, cfg):
+    """The two-pass plain form's recurrence on the matrix cores (64-column
+    slices) and on the vector ALUs (a 16-column split, or the per-value-channel
+    beta's substitution), and the single pass, each against the oracle."""
+    inp = make_inputs(cfg)
+    d = to_dev(inp)
+    o_ref, S_ref = run_oracle(inp)
+    for two_pass, split in ((True, 0), (True, 16), (False, 0)):
+        say(f"[plain recurrences] {name} two_pass={two_pass} dv_split={split}")
+        plan = gdr.plan(d["q"], d["k"], d["v"], dv_split=split, workspace=gdr.new_workspace(
+            d["q"], d["k"], d["v"], **gpu_kwargs(d)) if two_pass else None, **gpu_kwargs(d))
+        assert plan["passes"] == (2 if two_pass else 1)
+        # (the per-value-channel beta keeps 16-column slices: per-column systems)
+        assert plan["dv_slice"] == (64 if two_pass and not split and not cfg.get("value_beta") else 16)
+        o, S = gdr.chunk_fwd(d["q"], d["k"], d["v"], dv_split=split, two_pass=two_pass, **gpu_kwargs(d))
+        torch.cuda.synchronize()
+        assert_parity(f"{name} {two_pass} {split}", o.float().cpu().numpy(), S.cpu().numpy(), o_ref, S_ref,
+                      TOL[cfg["io"]])
