@@ -17,7 +17,7 @@ bool bwd_supported(int dk, int dv) {
 
 template <class IO, int DK, int DV>
 hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
-  const int ns = p.f.nslices, N = p.nchunks;
+  const int N = p.nchunks;
   // record pass: the chunk records once per chunk, then the recurrence of
   // each slice writing its entering states and W
   // (the recurrence on the matrix cores, slices of 64 columns; the backward
@@ -28,7 +28,7 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
     f64.nslices = DV / 64;
     hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64, p.ws);
   }
-  hipLaunchKernelGGL((bwd_state_kernel<IO, DK, 16>), dim3(BH * ns), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK>), dim3(BH * (DV / 64)), dim3(NTHR), 0, s, p);
   if (N > 0) {
     hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
     hipLaunchKernelGGL((bwd_key_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);

@@ -14,8 +14,9 @@
 //             (plain_split_kernel.hpp): per chunk A = (I + T)^{-1} (in the
 //             place of T), A_qk, E_bar, Q_gamma, K_tail, gamma_C, and per slice
 //             the entering state S and W, to the workspace.
-//  A  state   per (batch, head, 16-column slice), chunks in reverse, the
-//             gradient of the state dS (leaving the chunk) carried in LDS:
+//  A  state   per (batch, head, 64-column slice), chunks in reverse, the
+//             gradient of the state dS (leaving the chunk) carried in MFMA
+//             accumulators:
 //               dW = A_qk^T dO + K_tail dS
 //               dR = A^T dW,  A = (I + T)^{-1} from the record pass
 //               dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR
@@ -69,168 +70,186 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
   }
 }
 
-// ---- pass A: the reverse state recurrence ---------------------------------
-// LDS holds the chunk's two [64][64] matrices, the slice of dS and the rows
-// of dO, dW, dR (59 KB: two workgroups per CU); the factor rows and columns
-// of the record go straight to registers, every load of a phase issued
-// first.
-template <int DK, int DVS>
-struct BwdALay {
-  static constexpr int SP = DVS + 4, TP = CH + 4;
-  static constexpr int oA = 0;             // [64][TP] A = (I + T)^{-1}
-  static constexpr int oAq = oA + CH * TP; // [64][TP] A_qk
-  static constexpr int oS = oAq + CH * TP; // [DK][SP] dS
-  static constexpr int oO = oS + DK * SP;  // [64][SP] dO
-  static constexpr int oW = oO + CH * SP;  // [64][SP] dW
-  static constexpr int oR = oW + CH * SP;  // [64][SP] dR
-  static constexpr int TOTAL = oR + CH * SP;
-  static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
+// ---- pass A: the reverse state recurrence, on the matrix cores ----------------
+// Every product on v_mfma_f32_16x16x4_f32: one workgroup of four waves per (batch, head, 64-column slice), wave w
+// owning columns 16 w .. + 15 and dS of those columns in accumulators
+// (register r of block b of lane l: dS[16 b + 4 (l / 16) + r][16 w + l % 16],
+// the forward recurrence's state layout).  k-step (b, r) takes, in lane group
+// g, the channel or token 16 b + 4 g + r, so dS, dO, dW and dR serve as B
+// operands in place and the A operands are 16-byte LDS reads:
+//   dW = A_qk^T dO + K_tail dS        A = A_qk^T rows, K_tail rows
+//   dR = A^T dW                       A = A^T rows (upper blocks only)
+//   dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR   A = Q_gamma^T, E_bar^T rows
+// The chunk's records go to LDS once per chunk (the transposes on the way);
+// the previous chunk's are loaded into registers while this one computes.
+template <int DK>
+struct BwdAMLay {
+  static constexpr int SE = DK + 4, SA = CH + 4;
+  static constexpr int oKt = 0;                  // [64][SE] K_tail rows
+  static constexpr int oQgT = oKt + CH * SE;     // [DK][SA] Q_gamma^T
+  static constexpr int oEbT = oQgT + DK * SA;    // [DK][SA] E_bar^T
+  static constexpr int oAqT = oEbT + DK * SA;    // [64][SA] A_qk^T
+  static constexpr int oAT = oAqT + CH * SA;     // [64][SA] A^T
+  static constexpr int oGC = oAT + CH * SA;      // [DK] gamma_C
+  static constexpr int TOTAL = oGC + DK;
+  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
 };
 
-template <class IO, int DK, int DVS>
-__global__ __launch_bounds__(NTHR) void bwd_state_kernel(BwdParams p) {
-  using L = BwdALay<DK, DVS>;
-  constexpr int SP = L::SP, TP = L::TP;
-  static_assert(DVS == 16, "row x 4 columns per thread over 16 columns");
+template <class IO, int DK>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_state_mfma_kernel(BwdParams p) {
+  using L = BwdAMLay<DK>;
+  constexpr int SE = L::SE, SA = L::SA, NB = DK / 16, DVS = 64;
+  constexpr int NQ_E = CH * DK / 4 / NTHR, NQ_A = CH * CH / 4 / NTHR;
   __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
-  float *sA = lds + L::oA, *sAq = lds + L::oAq, *sdS = lds + L::oS;
-  float *sdO = lds + L::oO, *sdW = lds + L::oW, *sdR = lds + L::oR;
+  float *sKt = lds + L::oKt, *sQgT = lds + L::oQgT, *sEbT = lds + L::oEbT;
+  float *sAqT = lds + L::oAqT, *sAT = lds + L::oAT, *sGC = lds + L::oGC;
 
-  const int tid = threadIdx.x;
-  // the slices of a head on one XCD (blockIdx residues mod 8), as the record pass
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
   int wid = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) wid = (wid & 7) * (nwg >> 3) + (wid >> 3);
-  const int NS = p.f.nslices;
+  const int NS = p.f.DV / DVS;
   const int bh = wid / NS, slice = wid - bh * NS;
   const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
   const int T = p.f.T, H = p.f.H, DV = p.f.DV, N = p.nchunks;
-  const int vbase = slice * DVS;
+  const int col = slice * DVS + 16 * wave + l16;
   const size_t seq0 = (size_t)bb * T * H + hh;
   const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   const BwdWs& ws = p.ws;
 
-  // row j x columns vq .. (quad member cq; the K_tail sums over the channels
-  // are split over the quad, DK / 4 channels each); dS update: channel cu x
-  // VPT columns
-  const int rj = tid >> 2, cq = tid & 3, vq = 4 * cq;
-  const int i0 = (tid >> 6) * 16;  // the wave's first row
-  constexpr int CPQ = DK / 4;
-  constexpr int TPC = NTHR / DK, VPT = DVS / TPC;
-  const int cu = tid / TPC, vu = (tid % TPC) * VPT;
+  f32x4 dS[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dS[b][r] = p.d_st ? p.d_st[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] : 0.f;
 
-  for (int e = tid; e < DK * DVS; e += NTHR) {
-    const int c = e / DVS, v = e - c * DVS;
-    sdS[c * SP + v] = p.d_st ? p.d_st[((size_t)bh * DK + c) * DV + vbase + v] : 0.f;
-  }
+  struct Rec {
+    f32x4 eb[NQ_E], qg[NQ_E], kt[NQ_E], a[NQ_A], aq[NQ_A];
+    float gc;
+    float o[16];  // dO rows 16 I + 4 g + r of this lane's column
+  };
+  auto load = [&](int n, Rec& R) __attribute__((always_inline)) {
+    const size_t ch = (size_t)bh * N + n;
+#pragma unroll
+    for (int u = 0; u < NQ_E; ++u) {
+      const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
+      R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
+      R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
+      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + o);
+    }
+#pragma unroll
+    for (int u = 0; u < NQ_A; ++u) {
+      const size_t o = ch * CH * CH + 4 * (tid + NTHR * u);
+      R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
+      R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
+    }
+    R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int t = n * CH + 16 * (k >> 2) + 4 * g + (k & 3);
+      const float x = ldf(dog + (seq0 + (size_t)min(t, T - 1) * H) * DV + col);
+      R.o[k] = t < T ? x : 0.f;
+    }
+  };
+  auto stage = [&](const Rec& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NQ_E; ++u) {
+      const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
+      *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sQgT[(c + i) * SA + t] = R.qg[u][i];
+        sEbT[(c + i) * SA + t] = R.eb[u][i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NQ_A; ++u) {
+      const int e = 4 * (tid + NTHR * u), t = e / CH, c = e - t * CH;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sAT[(c + i) * SA + t] = R.a[u][i];
+        sAqT[(c + i) * SA + t] = R.aq[u][i];
+      }
+    }
+    if (tid < DK) sGC[tid] = R.gc;
+  };
+
+  Rec R;
+  if (N > 0) load(N - 1, R);
   for (int n = N - 1; n >= 0; --n) {
     const size_t ch = (size_t)bh * N + n;
-    const int t0 = n * CH;
-    __syncthreads();  // the previous chunk's update of dS and reads of dO, dR are complete
+    __syncthreads();  // every read of the later chunk's LDS records is done
+    stage(R);
+    float dO[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dO[k] = R.o[k];
+    __syncthreads();
+    if (n > 0) load(n - 1, R);
     // the gradient of the state leaving this chunk, for the product pass
-    for (int e = tid; e < DK * DVS; e += NTHR) {
-      const int c = e / DVS, v = e - c * DVS;
-      ws.dS[(ch * DK + c) * DV + vbase + v] = sdS[c * SP + v];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ws.dS[(ch * DK + 16 * b + 4 * g + r) * DV + col] = dS[b][r];
+    // ---- dW = A_qk^T dO + K_tail dS (A_qk^T is zero below the diagonal) ---------
+    f32x4 dW[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sKt + (16 * I + l16) * SE + 16 * b + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w = mfma_f32(a[r], dS[b][r], w);
+      }
+#pragma unroll
+      for (int J = I; J < 4; ++J) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sAqT + (16 * I + l16) * SA + 16 * J + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w = mfma_f32(a[r], dO[4 * J + r], w);
+      }
+      dW[I] = w;
     }
-    // ---- loads: A and A_qk, dO of row rj, this thread's channels of K_tail row rj
-    f32x4 ra[4], rq[4], k4[CPQ / 4], o4;
+    // ---- dR = A^T dW, block rows from the first (each reads dW blocks J >= I) ----
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = *reinterpret_cast<const f32x4*>(ws.T + ch * CH * CH + 4 * (tid + NTHR * u));
-      rq[u] = *reinterpret_cast<const f32x4*>(ws.A + ch * CH * CH + 4 * (tid + NTHR * u));
+    for (int I = 0; I < 4; ++I) {
+      f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int J = I; J < 4; ++J) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sAT + (16 * I + l16) * SA + 16 * J + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r4 = mfma_f32(a[r], dW[J][r], r4);
+      }
+      dW[I] = r4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ws.dR[(ch * CH + 16 * I + 4 * g + r) * DV + col] = r4[r];
     }
-    {
-      const float* ktr = ws.Kt + (ch * CH + rj) * DK + CPQ * cq;
+    // ---- dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR -----------------------
 #pragma unroll
-      for (int u = 0; u < CPQ / 4; ++u) k4[u] = *reinterpret_cast<const f32x4*>(ktr + 4 * u);
-      o4 = ldf4(dog + (seq0 + (size_t)min(t0 + rj, T - 1) * H) * DV + vbase + vq);
-      if (t0 + rj >= T) o4 = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int b = 0; b < NB; ++b) {
+      const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + 16 * b + 4 * g);
+      f32x4 s = dS[b] * gc;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = 4 * (tid + NTHR * u), r = e / CH, c = e - r * CH;
-      *reinterpret_cast<f32x4*>(sA + r * TP + c) = ra[u];
-      *reinterpret_cast<f32x4*>(sAq + r * TP + c) = rq[u];
-    }
-    *reinterpret_cast<f32x4*>(sdO + rj * SP + vq) = o4;
-    // K_tail dS of row rj: partial sums over the thread's channels, summed
-    // across the quad
-    f32x4 kds;
-    {
-      float acc[DVS];
+      for (int J = 0; J < 4; ++J) {
+        const f32x4 aq = *reinterpret_cast<const f32x4*>(sQgT + (16 * b + l16) * SA + 16 * J + 4 * g);
+        const f32x4 ae = *reinterpret_cast<const f32x4*>(sEbT + (16 * b + l16) * SA + 16 * J + 4 * g);
 #pragma unroll
-      for (int v = 0; v < DVS; ++v) acc[v] = 0.f;
-#pragma unroll
-      for (int u = 0; u < CPQ / 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float* srow = sdS + (CPQ * cq + 4 * u + i) * SP;
-#pragma unroll
-          for (int x = 0; x < DVS; x += 4) {
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(srow + x);
-#pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x + y] = __builtin_fmaf(k4[u][i], s4[y], acc[x + y]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          s = mfma_f32(aq[r], dO[4 * J + r], s);
+          s = mfma_f32(-ae[r], dW[J][r], s);
         }
-#pragma unroll
-      for (int v = 0; v < DVS; ++v) acc[v] = quad_sum(acc[v]);
-#pragma unroll
-      for (int y = 0; y < 4; ++y)
-        kds[y] = cq == 0 ? acc[y] : cq == 1 ? acc[4 + y] : cq == 2 ? acc[8 + y] : acc[12 + y];
-    }
-    // the columns of Q_gamma and E_bar for the update, requested here so that
-    // they arrive during dW and dR
-    float qcol[CH], ecol[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      qcol[i] = ws.Qg[(ch * CH + i) * DK + cu];
-      ecol[i] = ws.Eb[(ch * CH + i) * DK + cu];
-    }
-    __syncthreads();
-    // ---- dW = A_qk^T dO + K_tail dS: row rj (A_qk is zero above the
-    // diagonal, so the sum starts at the wave's first row)
-    {
-      f32x4 w = kds;
-      for (int i = i0; i < CH; ++i) w += sAq[i * TP + rj] * *reinterpret_cast<const f32x4*>(sdO + i * SP + vq);
-      *reinterpret_cast<f32x4*>(sdW + rj * SP + vq) = w;
-    }
-    __syncthreads();
-    // ---- dR = A^T dW ------------------------------------------------------------
-    {
-      f32x4 r = {0.f, 0.f, 0.f, 0.f};
-      for (int i = i0; i < CH; ++i) r += sA[i * TP + rj] * *reinterpret_cast<const f32x4*>(sdW + i * SP + vq);
-      *reinterpret_cast<f32x4*>(sdR + rj * SP + vq) = r;
-      *reinterpret_cast<f32x4*>(ws.dR + (ch * CH + rj) * DV + vbase + vq) = r;
-    }
-    __syncthreads();
-    // ---- dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR: channel cu -------
-    {
-      const float gC = ws.gC[ch * DK + cu];
-      float s[VPT];
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) s[u] = gC * sdS[cu * SP + vu + u];
-#pragma unroll
-      for (int i = 0; i < CH; ++i)
-#pragma unroll
-        for (int x = 0; x < VPT; x += 4) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(sdO + i * SP + vu + x);
-          const f32x4 r = *reinterpret_cast<const f32x4*>(sdR + i * SP + vu + x);
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            s[x + y] = __builtin_fmaf(qcol[i], o[y], s[x + y]);
-            s[x + y] = __builtin_fmaf(-ecol[i], r[y], s[x + y]);
-          }
-        }
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) sdS[cu * SP + vu + u] = s[u];
+      }
+      dS[b] = s;
     }
   }
-  __syncthreads();
   if (p.dstate) {
-    for (int e = tid; e < DK * DVS; e += NTHR) {
-      const int c = e / DVS, v = e - c * DVS;
-      p.dstate[((size_t)bh * DK + c) * DV + vbase + v] = sdS[c * SP + v];
-    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.dstate[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] = dS[b][r];
   }
 }
 
