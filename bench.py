@@ -96,7 +96,8 @@ def workload_list(which):
         if name != HEADLINE:
             out.append((name, "step" if name == DECODE else "chunk", config(name)))
     out += [
-        # fp32 I/O at d = 128 (the plain fp32 kernel)
+        # fp32 I/O at d = 128 (the plain fp32 kernel's two-pass form: per-chunk prep, then
+        # the recurrence on the matrix cores)
         ("gdn_f32_b8h16t4096d128", "chunk", config(HEADLINE, io="f32")),
         # short sequences: the recurrent form beside the chunk form
         ("gdn_bf16_b64h32t16d128", "recurrent", config(HEADLINE, B=64, H=32, T=16)),
@@ -179,7 +180,8 @@ def bench_workload(name, op, cfg, steps, warmup, settle_ms=0.0):
             args = gdr.build_bwd_args(fa, do, dstate=dS, grads=grads, workspace=ws)
             keep += [do, dS, fa, grads, ws]
             entry = "gdr_chunk_bwd"
-            plan = dict(workspace_bytes=need, passes=4 + (d["qmix"] == 1))
+            # record pass (prep, recurrence), state, product, key (+ a per-head lambda's reduction)
+            plan = dict(workspace_bytes=need, passes=5 + (d["qmix"] == 1))
         else:
             o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
             so = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
