@@ -253,52 +253,35 @@ void bwd_state_mfma_kernel(BwdParams p) {
   }
 }
 
-// ---- pass B1: products over the value channels ----------------------------
-// P[x][y] = sgn * sum_v X[x][v] Y[y][v] for x < 64, y < NY; thread t owns
-// rows 4 (t >> 4) .. +3 and columns (t & 15) * NY/16 .. +NY/16-1.  MASK: 0
-// none, 1 keep y < x (strictly lower), 2 keep y <= x.
-template <int DV, int NY, int MASK>
-__device__ __forceinline__ void prod_rows(const float* X, const float* Y, float sgn, float* out, int ldo) {
-  constexpr int LD = DV + 4, NB = NY / 16;
-  const int tid = threadIdx.x, xb = tid >> 4, yb = tid & 15;
-  float acc[4][NB];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[a][b] = 0.f;
-#pragma unroll 2
-  for (int v = 0; v < DV; v += 4) {
-    f32x4 xr[4], yr[NB];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) xr[a] = *reinterpret_cast<const f32x4*>(X + (4 * xb + a) * LD + v);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) yr[b] = *reinterpret_cast<const f32x4*>(Y + (yb * NB + b) * LD + v);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[a][b] = __builtin_fmaf(xr[a][u], yr[b][u], acc[a][b]);
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int x = 4 * xb + a, y = yb * NB + b;
-      const bool keep = MASK == 0 || (MASK == 1 ? y < x : y <= x);
-      out[(size_t)x * ldo + y] = keep ? sgn * acc[a][b] : 0.f;
-    }
-}
+// ---- pass B1: products over the value channels, on the matrix cores --------
+// One workgroup of four waves per (batch, head, chunk).  The value channels
+// are taken in halves of 64: dR, dO, W [64][64] and S, dS [DK][64] of the
+// half in LDS (123 KB), the products' partial sums carried over the halves
+// in accumulators.  Wave w owns row block w (rows 16 w .. + 15) of every
+// output: dT and dA_qk (blocks J <= w), dE_bar, dQ_gamma, dK_tail (all DK / 16
+// column blocks).  Every product contracts over the value channels with
+// v_mfma_f32_16x16x4_f32; k-step (b, r) takes, in lane group g, the value
+// channel 16 b + 4 g + r of the half, so both operands are 16-byte LDS reads
+// of rows (four k-steps each).  Then sC = sum_v S (.) dS per key channel.
+template <int DK>
+struct BwdB1Lay {
+  static constexpr int VH = 64, SP = VH + 4;
+  static constexpr int oR = 0, oO = oR + CH * SP, oW = oO + CH * SP, oS = oW + CH * SP, odS = oS + DK * SP;
+  static constexpr int TOTAL = odS + DK * SP;
+  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+};
 
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(NTHR) void bwd_prod_kernel(BwdParams p) {
-  constexpr int LD = DV + 4;
-  constexpr int R2 = (DK > CH ? DK : CH);
-  __shared__ __attribute__((aligned(16))) float lds[(2 * CH + R2) * LD];
-  float* s0 = lds;
-  float* s1 = lds + CH * LD;
-  float* s2 = lds + 2 * CH * LD;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_prod_kernel(BwdParams p) {
+  using L = BwdB1Lay<DK>;
+  constexpr int VH = L::VH, SP = L::SP, NC = DK / 16;
+  static_assert(DV % VH == 0, "value channels in halves of 64");
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  float *sR = lds + L::oR, *sO = lds + L::oO, *sW = lds + L::oW, *sS = lds + L::oS, *sdS = lds + L::odS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
   const int N = p.nchunks;
   const size_t ch = blockIdx.x;
   const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
@@ -307,46 +290,119 @@ __global__ __launch_bounds__(NTHR) void bwd_prod_kernel(BwdParams p) {
   const size_t seq0 = (size_t)bb * T * H + hh;
   const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   const BwdWs& ws = p.ws;
-  // phase 1: dT = -tril(dR W^T, -1), dA_qk = tril(dO W^T)
-  copy_rows<CH, DV, LD>(s0, ws.dR + ch * CH * DV, tid);
-  {
-    constexpr int QPR = DV / 4, NQ = CH * QPR / NTHR;
-    f32x4 x[NQ];
+
+  f32x4 aT[4], aA[4], aE[NC], aQ[NC], aK[NC];
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int e = tid + NTHR * u, r = e / QPR, c4 = (e - r * QPR) * 4;
-      x[u] = ldf4(dog + (seq0 + (size_t)min(n * CH + r, T - 1) * H) * DV + c4);
+  for (int J = 0; J < 4; ++J) aT[J] = aA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) aE[c] = aQ[c] = aK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float sc = 0.f;  // sum_v S (.) dS of channel tid >> 1, half of the value channels of each half
+
+  for (int vh = 0; vh < DV; vh += VH) {
+    if (vh > 0) __syncthreads();  // the previous half's reads are done
+    // ---- the half's rows to LDS (every load of the thread issued first)
+    {
+      constexpr int QR = CH * VH / 4 / NTHR, QS = DK * VH / 4 / NTHR;
+      f32x4 xr[QR], xo[QR], xw[QR], xs[QS], xd[QS];
+#pragma unroll
+      for (int u = 0; u < QR; ++u) {
+        const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+        xr[u] = *reinterpret_cast<const f32x4*>(ws.dR + (ch * CH + r) * DV + vh + c4);
+        xw[u] = *reinterpret_cast<const f32x4*>(ws.W + (ch * CH + r) * DV + vh + c4);
+        xo[u] = ldf4(dog + (seq0 + (size_t)min(n * CH + r, T - 1) * H) * DV + vh + c4);
+        if (n * CH + r >= T) xo[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < QS; ++u) {
+        const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+        xs[u] = *reinterpret_cast<const f32x4*>(ws.S + (ch * DK + r) * DV + vh + c4);
+        xd[u] = *reinterpret_cast<const f32x4*>(ws.dS + (ch * DK + r) * DV + vh + c4);
+      }
+#pragma unroll
+      for (int u = 0; u < QR; ++u) {
+        const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+        *reinterpret_cast<f32x4*>(sR + r * SP + c4) = xr[u];
+        *reinterpret_cast<f32x4*>(sO + r * SP + c4) = xo[u];
+        *reinterpret_cast<f32x4*>(sW + r * SP + c4) = xw[u];
+      }
+#pragma unroll
+      for (int u = 0; u < QS; ++u) {
+        const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+        *reinterpret_cast<f32x4*>(sS + r * SP + c4) = xs[u];
+        *reinterpret_cast<f32x4*>(sdS + r * SP + c4) = xd[u];
+      }
     }
+    __syncthreads();
+    // ---- sC: channel tid >> 1 (DK = 128) or tid >> 2 (DK = 64), a run of the half
+    {
+      constexpr int TPC = NTHR / DK, RUN = VH / TPC;
+      const int c = tid / TPC, v0 = (tid % TPC) * RUN;
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int e = tid + NTHR * u, r = e / QPR, c4 = (e - r * QPR) * 4;
-      const bool ok = n * CH + r < T;
+      for (int v = 0; v < RUN; v += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sS + c * SP + v0 + v);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(sdS + c * SP + v0 + v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s1[r * LD + c4 + i] = ok ? x[u][i] : 0.f;
+        for (int i = 0; i < 4; ++i) sc = __builtin_fmaf(a[i], b[i], sc);
+      }
+    }
+    // ---- the products of row block w over the half
+#pragma unroll
+    for (int b = 0; b < VH / 16; ++b) {
+      const int ko = 16 * b + 4 * g;
+      const f32x4 ar = *reinterpret_cast<const f32x4*>(sR + (16 * w + l16) * SP + ko);
+      const f32x4 ao = *reinterpret_cast<const f32x4*>(sO + (16 * w + l16) * SP + ko);
+      const f32x4 aw = *reinterpret_cast<const f32x4*>(sW + (16 * w + l16) * SP + ko);
+      // dT = -dR W^T, dA_qk = dO W^T: column blocks J <= w
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J > w) continue;  // wave-uniform
+        const f32x4 bw = *reinterpret_cast<const f32x4*>(sW + (16 * J + l16) * SP + ko);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          aT[J] = mfma_f32(ar[r], bw[r], aT[J]);
+          aA[J] = mfma_f32(ao[r], bw[r], aA[J]);
+        }
+      }
+      // dE_bar = -dR S^T, dQ_gamma = dO S^T, dK_tail = W dS^T
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x4 bs = *reinterpret_cast<const f32x4*>(sS + (16 * c + l16) * SP + ko);
+        const f32x4 bd = *reinterpret_cast<const f32x4*>(sdS + (16 * c + l16) * SP + ko);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          aE[c] = mfma_f32(ar[r], bs[r], aE[c]);
+          aQ[c] = mfma_f32(ao[r], bs[r], aQ[c]);
+          aK[c] = mfma_f32(aw[r], bd[r], aK[c]);
+        }
+      }
     }
   }
-  copy_rows<CH, DV, LD>(s2, ws.W + ch * CH * DV, tid);
-  __syncthreads();
-  prod_rows<DV, CH, 1>(s0, s2, -1.f, ws.T + ch * CH * CH, CH);
-  prod_rows<DV, CH, 2>(s1, s2, 1.f, ws.A + ch * CH * CH, CH);
-  __syncthreads();
-  // phase 2: dE_bar = -dR S^T, dQ_gamma = dO S^T
-  copy_rows<DK, DV, LD>(s2, ws.S + ch * DK * DV, tid);
-  __syncthreads();
-  prod_rows<DV, DK, 0>(s0, s2, -1.f, ws.Eb + ch * CH * DK, DK);
-  prod_rows<DV, DK, 0>(s1, s2, 1.f, ws.Qg + ch * CH * DK, DK);
-  __syncthreads();
-  // phase 3: dK_tail = W dS^T and sum_v S (.) dS
-  copy_rows<CH, DV, LD>(s0, ws.W + ch * CH * DV, tid);
-  copy_rows<DK, DV, LD>(s2, ws.dS + ch * DK * DV, tid);
-  __syncthreads();
-  prod_rows<DV, DK, 0>(s0, s2, 1.f, ws.Kt + ch * CH * DK, DK);
-  for (int c = tid; c < DK; c += NTHR) {
-    const float* srow = ws.S + (ch * DK + c) * DV;
-    float s = 0.f;
-    for (int v = 0; v < DV; ++v) s = __builtin_fmaf(srow[v], s2[c * LD + v], s);
-    ws.gC[ch * DK + c] = s;
+  // ---- outputs: lane holds rows 16 w + 4 g + r of column l16 of each block
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * w + 4 * g + r;
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      const int j = 16 * J + l16;
+      const float t = J <= w && j < i ? -aT[J][r] : 0.f;   // dT: strictly lower
+      const float a = J <= w && j <= i ? aA[J][r] : 0.f;   // dA_qk: lower
+      ws.T[(ch * CH + i) * CH + j] = t;
+      ws.A[(ch * CH + i) * CH + j] = a;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const size_t o = (ch * CH + i) * DK + 16 * c + l16;
+      ws.Eb[o] = -aE[c][r];
+      ws.Qg[o] = aQ[c][r];
+      ws.Kt[o] = aK[c][r];
+    }
   }
+  // sC: the channel's threads (adjacent lanes) combined
+  constexpr int TPC = NTHR / DK;
+  sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0xB1, 0xf, 0xf, true));
+  if constexpr (TPC == 4)
+    sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0x4E, 0xf, 0xf, true));
+  if (tid % TPC == 0) ws.gC[ch * DK + tid / TPC] = sc;
 }
 
 // ---- pass B2: back to the rows, the cumulative decay and the gates -----------
