@@ -100,6 +100,8 @@ def workload_list(which):
         # the recurrence on the matrix cores)
         ("gdn_f32_b8h16t4096d128", "chunk", config(HEADLINE, io="f32")),
         # short sequences: the recurrent form beside the chunk form
+        ("gdn_bf16_b64h32t4d128", "recurrent", config(HEADLINE, B=64, H=32, T=4)),
+        ("gdn_bf16_b64h32t4d128", "chunk", config(HEADLINE, B=64, H=32, T=4)),
         ("gdn_bf16_b64h32t16d128", "recurrent", config(HEADLINE, B=64, H=32, T=16)),
         ("gdn_bf16_b64h32t16d128", "chunk", config(HEADLINE, B=64, H=32, T=16)),
         ("gdn_bf16_b64h32t64d128", "recurrent", config(HEADLINE, B=64, H=32, T=64)),

@@ -8,11 +8,14 @@
 //   S_bar = Diag(alpha_t) S;  r = S_bar^T e_t;  S = S_bar + k_t (z_t - m_t (.) r)^T;  o_t = S^T q_t
 // with m_t = 1, or the per-value-channel beta of 11.3 (e = k, z = beta (.) v).
 //
-// One workgroup per (batch, head), one thread per value column: thread v
-// keeps column v of the state (all dk rows) in registers for the whole call,
-// so both contractions over the key channels (r and o) are thread-local and
-// a token needs no barrier.  The per-token key-side vectors (alpha, e, k, q)
-// of a block of TB = 8 tokens are staged in LDS and read as broadcasts.
+// One workgroup per (batch, head) with one thread per value column: thread
+// v keeps the columns 2 (v / 2) and 2 (v / 2) + 1 of the state in registers
+// for the whole call, over half of the key channels (v % 2 picks the half),
+// so each broadcast of a key-side value feeds two columns, the contractions
+// over the key channels (r and o) are thread-local up to one exchange with
+// the neighbouring lane (DPP), and a token needs no barrier.  The per-token
+// key-side vectors (alpha, e, k, q) of a block of TB = 8 tokens are staged in
+// LDS and read as broadcasts; thread v stages and writes column v.
 //
 // Output epilogue (11.3: RMSNorm of each head's readout, then the SiLU output
 // gate; the Gated DeltaNet-2 page's method flowchart ends with the same step):
@@ -78,9 +81,19 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
   const bool epi = p.gate != nullptr;
   const float nwv = epi ? p.nw[v] : 0.f;
 
-  float S[DK];
+  // state: columns col0 and col0 + 1, key channels cb .. cb + DK / 2 - 1
+  constexpr int DH = DK / 2;
+  const int col0 = v & ~1, hf = v & 1, cb = hf * DH;
+  float S[2][DH];
 #pragma unroll
-  for (int c = 0; c < DK; ++c) S[c] = p.state_in ? p.state_in[((size_t)bh * DK + c) * DV + v] : 0.f;
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < DH; ++c)
+      S[j][c] = p.state_in ? p.state_in[((size_t)bh * DK + cb + c) * DV + col0 + j] : 0.f;
+  // the neighbouring lane's partial sum added (DPP quad permutation 1 0 3 2)
+  auto pair_sum = [](float x) __attribute__((always_inline)) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
+  };
 
   // staging layout: QPR threads cover a row of DK channels four at a time;
   // the DV / QPR groups of them take every (DV / QPR)-th token of a block
@@ -153,32 +166,49 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
     for (int tt = 0; tt < TB; ++tt) {
       ob[tt] = 0.f;
       if (tt < nt) {
-        // forget, then predict along e
-        float r = 0.f;
+        // forget (no decay: alpha = 1), then predict along e
+        if (decay != 0) {
 #pragma unroll
-        for (int c = 0; c < DK; c += 4) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[tt][c]);
-          const f32x4 e = *reinterpret_cast<const f32x4*>(&sE[tt][c]);
+          for (int c = 0; c < DH; c += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[tt][cb + c]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            S[c + u] *= a[u];
-            r = __builtin_fmaf(e[u], S[c + u], r);
+            for (int u = 0; u < 4; ++u) {
+              S[0][c + u] *= a[u];
+              S[1][c + u] *= a[u];
+            }
           }
         }
-        const float d = sZ[tt][v] - sM[tt][v] * r;
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < DH; c += 4) {
+          const f32x4 e = *reinterpret_cast<const f32x4*>(&sE[tt][cb + c]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            r0 = __builtin_fmaf(e[u], S[0][c + u], r0);
+            r1 = __builtin_fmaf(e[u], S[1][c + u], r1);
+          }
+        }
+        r0 = pair_sum(r0);
+        r1 = pair_sum(r1);
+        const float d0 = sZ[tt][col0] - sM[tt][col0] * r0;
+        const float d1 = sZ[tt][col0 + 1] - sM[tt][col0 + 1] * r1;
         // write along k, then read along q
-        float o = 0.f;
+        float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < DK; c += 4) {
-          const f32x4 kk = *reinterpret_cast<const f32x4*>(&sK[tt][c]);
-          const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[tt][c]);
+        for (int c = 0; c < DH; c += 4) {
+          const f32x4 kk = *reinterpret_cast<const f32x4*>(&sK[tt][cb + c]);
+          const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[tt][cb + c]);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            S[c + u] = __builtin_fmaf(kk[u], d, S[c + u]);
-            o = __builtin_fmaf(qq[u], S[c + u], o);
+            S[0][c + u] = __builtin_fmaf(kk[u], d0, S[0][c + u]);
+            S[1][c + u] = __builtin_fmaf(kk[u], d1, S[1][c + u]);
+            o0 = __builtin_fmaf(qq[u], S[0][c + u], o0);
+            o1 = __builtin_fmaf(qq[u], S[1][c + u], o1);
           }
         }
-        ob[tt] = o;
+        o0 = pair_sum(o0);
+        o1 = pair_sum(o1);
+        ob[tt] = hf ? o1 : o0;  // column v
       }
     }
     if (epi) {
@@ -207,7 +237,9 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
   }
   if (p.state_out) {
 #pragma unroll
-    for (int c = 0; c < DK; ++c) p.state_out[((size_t)bh * DK + c) * DV + v] = S[c];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < DH; ++c) p.state_out[((size_t)bh * DK + cb + c) * DV + col0 + j] = S[j][c];
   }
 }
 
