@@ -42,6 +42,12 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   return x;
 }
 
+// an integer as a type (compile-time roles and levels of lambdas)
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
 // sum over the lanes of a wave (every lane gets the total)
 __device__ __forceinline__ float wave_sum(float s) {
 #pragma unroll

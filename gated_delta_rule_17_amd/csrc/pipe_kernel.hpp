@@ -64,11 +64,6 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                   0, 0, 0);
 }
 
-template <int N>
-struct IC {
-  static constexpr int value = N;
-};
-
 // The (I, J) 16x16 tiles of T and A_qk that one producer wave computes.
 template <int N_, int I0, int J0, int I1, int J1, int I2 = 0, int J2 = 0>
 struct Tiles {

@@ -44,11 +44,17 @@
 namespace gdr {
 
 // ---- pass 1 -----------------------------------------------------------------
-// Channels are processed in halves of 64: [64][65] arrays of k, e, q and the
-// prefix sums G of the half, 67 KB of LDS (two workgroups per CU).
+// Channels are processed in halves of 64: [64][68] arrays of k, e, q and the
+// prefix sums G of the half, 74 KB of LDS (two workgroups per CU).  Under a
+// scalar decay (or none) the Gram sums are fp32 MFMA tiles
+// (v_mfma_f32_16x16x4f32; k-step (b, r) takes, in lane group g, the channel
+// 16 b + 4 g + r, so both operands are 16-byte reads of rows): wave w owns the
+// (I, J) tile pairs w, w + 4, w + 8 of the ten on or below the diagonal.
+// Under a decay per key channel every term carries its own exponential and
+// the sums run on the vector ALUs, 4 x 4 (i, j) blocks per thread.
 struct PlainPrepLay {
   static constexpr int CHH = 64;       // channels per half
-  static constexpr int HP = CHH + 1;   // row stride (floats)
+  static constexpr int HP = CHH + 4;   // row stride (floats): 16-byte rows
   static constexpr int oK = 0, oX = oK + CH * HP, oQ = oX + CH * HP, oG = oQ + CH * HP;
   static constexpr int oGs = oG + CH * HP;  // [64] scalar-decay prefix sums
   static constexpr int oPart = oGs + CH;    // [16][64] sums of the log-decay over 4-row groups
@@ -69,7 +75,8 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
   float* sGs = lds + L::oGs;
   float* sPart = lds + L::oPart;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = p.T, H = p.H, N = (T + CH - 1) / CH;
   const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
   const int bb = bh / H, hh = bh - bb * H;
@@ -97,6 +104,14 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) accT[a][b] = accA[a][b] = 0.f;
+  // matrix-core layout: tile pair pr = wave + 4 t (t < 3, pr < 10) of the
+  // ten (I >= J) in the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ..
+  const int g = lane >> 4, l16 = lane & 15;
+  auto tile_I = [](int pr) { return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3; };
+  auto tile_J = [](int pr) { return pr - (pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 3 : 6); };
+  f32x4 mT[3], mA[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) mT[t] = mA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int half = 0; half < NH; ++half) {
     const int cb = half * CHH;  // first channel of the half
@@ -194,7 +209,26 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
     }
     __syncthreads();
     // ---- Gram sums over the half's channels ----------------------------------
-    if (jb <= ib) {
+    if (decay != 2) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int pr = wave + 4 * t;
+        if (pr >= 10) continue;  // wave-uniform
+        const int I = tile_I(pr), J = tile_J(pr);
+#pragma unroll
+        for (int b = 0; b < CHH / 16; ++b) {
+          const int ko = 16 * b + 4 * g;
+          const f32x4 ax = *reinterpret_cast<const f32x4*>(sX + (16 * I + l16) * HP + ko);
+          const f32x4 aq = *reinterpret_cast<const f32x4*>(sQ + (16 * I + l16) * HP + ko);
+          const f32x4 bk = *reinterpret_cast<const f32x4*>(sK + (16 * J + l16) * HP + ko);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            mT[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax[r], bk[r], mT[t], 0, 0, 0);
+            mA[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[r], bk[r], mA[t], 0, 0, 0);
+          }
+        }
+      }
+    } else if (jb <= ib) {
       for (int c = 0; c < CHH; ++c) {
         float xi[4], qi[4], kj[4], gi[4], gj[4];
 #pragma unroll
@@ -203,30 +237,18 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
           xi[a] = sX[i * HP + c];
           qi[a] = sQ[i * HP + c];
           kj[a] = sK[j * HP + c];
-          if (decay == 2) {
-            gi[a] = sG[i * HP + c];
-            gj[a] = sG[j * HP + c];
+          gi[a] = sG[i * HP + c];
+          gj[a] = sG[j * HP + c];
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            // exponent clamped at 0: entries above the diagonal are discarded
+            const float kd = kj[b] * fexp(fminf(gi[a] - gj[b], 0.f));
+            accT[a][b] = __builtin_fmaf(xi[a], kd, accT[a][b]);
+            accA[a][b] = __builtin_fmaf(qi[a], kd, accA[a][b]);
           }
-        }
-        if (decay == 2) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              // exponent clamped at 0: entries above the diagonal are discarded
-              const float kd = kj[b] * fexp(fminf(gi[a] - gj[b], 0.f));
-              accT[a][b] = __builtin_fmaf(xi[a], kd, accT[a][b]);
-              accA[a][b] = __builtin_fmaf(qi[a], kd, accA[a][b]);
-            }
-        } else {
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              accT[a][b] = __builtin_fmaf(xi[a], kj[b], accT[a][b]);
-              accA[a][b] = __builtin_fmaf(qi[a], kj[b], accA[a][b]);
-            }
-        }
       }
     }
   }
@@ -235,22 +257,54 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
   float* sT = lds + L::oK;   // [64][HP] T
   float* sAi = lds + L::oX;  // [64][HP] A = (I + T)^{-1}
   float* sP = lds + L::oQ;   // [48][HP] block products of the inverse's levels
+  // (under the per-value-channel beta every column has its own system: T
+  // itself goes to the record)
+  if (decay == 2) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = 4 * ib + a;
-    f32x4 tv, av;
+    for (int a = 0; a < 4; ++a) {
+      const int i = 4 * ib + a;
+      f32x4 tv, av;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = 4 * jb + b;
-      // scalar decay or none: the common factor exp(G_i - G_j) of the channels
-      const float d = decay == 2 ? 1.f : fexp(fminf(sGs[i] - sGs[j], 0.f));
-      tv[b] = (jb <= ib && j < i) ? accT[a][b] * d : 0.f;
-      av[b] = (jb <= ib && j <= i) ? accA[a][b] * d : 0.f;
-      sT[i * HP + j] = tv[b];
+      for (int b = 0; b < 4; ++b) {
+        const int j = 4 * jb + b;
+        tv[b] = (jb <= ib && j < i) ? accT[a][b] : 0.f;
+        av[b] = (jb <= ib && j <= i) ? accA[a][b] : 0.f;
+        sT[i * HP + j] = tv[b];
+      }
+      *reinterpret_cast<f32x4*>(ws.A + ch * CH * CH + i * CH + 4 * jb) = av;
+      if (erase == 2) *reinterpret_cast<f32x4*>(ws.T + ch * CH * CH + i * CH + 4 * jb) = tv;
     }
-    *reinterpret_cast<f32x4*>(ws.A + ch * CH * CH + i * CH + 4 * jb) = av;
-    // under the per-value-channel beta every column has its own system: T
-    if (erase == 2) *reinterpret_cast<f32x4*>(ws.T + ch * CH * CH + i * CH + 4 * jb) = tv;
+  } else {
+    // the tiles on and below the diagonal, times the common factor
+    // exp(G_i - G_j) of the channels; lane: rows 16 I + 4 g + r, column 16 J + l16
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int pr = wave + 4 * t;
+      if (pr >= 10) continue;
+      const int I = tile_I(pr), J = tile_J(pr), j = 16 * J + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        const float d = fexp(fminf(sGs[i] - sGs[j], 0.f));
+        const float tv = j < i ? mT[t][r] * d : 0.f, av = j <= i ? mA[t][r] * d : 0.f;
+        sT[i * HP + j] = tv;
+        ws.A[ch * CH * CH + i * CH + j] = av;
+        if (erase == 2) ws.T[ch * CH * CH + i * CH + j] = tv;
+      }
+    }
+    // the six tiles above the diagonal are zero in the record
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int u = wave + 4 * t;
+      if (u >= 6) continue;
+      const int I = u < 3 ? 0 : u < 5 ? 1 : 2, J = u < 3 ? u + 1 : u < 5 ? u - 1 : 3, j = 16 * J + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        ws.A[ch * CH * CH + i * CH + j] = 0.f;
+        if (erase == 2) ws.T[ch * CH * CH + i * CH + j] = 0.f;
+      }
+    }
   }
   if (erase == 2) return;
   __syncthreads();
@@ -276,24 +330,34 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
   // levels s = 1, 2, 3: the blocks (I, J) with I - J = s,
   //   A_IJ = -A_II sum_{K = J}^{I - 1} T_IK A_KJ
   // (every A_KJ on the right lies closer to the diagonal)
-  for (int sl = 1; sl < 4; ++sl) {
-    const int nel = (4 - sl) * 256;  // elements of the level's blocks
-    for (int e = tid; e < nel; e += NTHR) {
-      const int J = e >> 8, i = (e >> 4) & 15, j = e & 15, I = J + sl;
-      float acc = 0.f;
-      for (int kk = 16 * J; kk < 16 * I; ++kk) acc = __builtin_fmaf(sT[(16 * I + i) * HP + kk], sAi[kk * HP + 16 * J + j], acc);
-      sP[(16 * J + i) * HP + j] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < nel; e += NTHR) {
-      const int J = e >> 8, i = (e >> 4) & 15, j = e & 15, I = J + sl;
+  // (thread tid: element (i, j) = (tid / 16, tid % 16) of each block)
+  const int bi = tid >> 4, bj = tid & 15;
+  auto level = [&](auto slc) __attribute__((always_inline)) {
+    constexpr int sl = decltype(slc)::value;
+#pragma unroll
+    for (int J = 0; J + sl < 4; ++J) {
+      const int I = J + sl;
       float acc = 0.f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(sAi[(16 * I + i) * HP + 16 * I + m], sP[(16 * J + m) * HP + j], acc);
-      sAi[(16 * I + i) * HP + 16 * J + j] = -acc;
+      for (int kk = 16 * J; kk < 16 * I; ++kk)
+        acc = __builtin_fmaf(sT[(16 * I + bi) * HP + kk], sAi[kk * HP + 16 * J + bj], acc);
+      sP[(16 * J + bi) * HP + bj] = acc;
     }
     __syncthreads();
-  }
+#pragma unroll
+    for (int J = 0; J + sl < 4; ++J) {
+      const int I = J + sl;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        acc = __builtin_fmaf(sAi[(16 * I + bi) * HP + 16 * I + m], sP[(16 * J + m) * HP + bj], acc);
+      sAi[(16 * I + bi) * HP + 16 * J + bj] = -acc;
+    }
+    __syncthreads();
+  };
+  level(IC<1>{});
+  level(IC<2>{});
+  level(IC<3>{});
   // A to the record in the place of T (zero above the diagonal)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
