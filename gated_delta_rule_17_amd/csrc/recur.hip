@@ -18,8 +18,8 @@ bool recur_supported(int dk, int dv) {
 hipError_t launch_recur(const RecurParams& p, bool bf16io, int dk, int dv, int grid, hipStream_t s) {
 #define X(DK, DV)                                                                                  \
   if (dk == DK && dv == DV) {                                                                      \
-    if (bf16io) hipLaunchKernelGGL((recur_fwd_kernel<bf16, DK, DV>), dim3(grid), dim3(DV), 0, s, p); \
-    else hipLaunchKernelGGL((recur_fwd_kernel<float, DK, DV>), dim3(grid), dim3(DV), 0, s, p);   \
+    if (bf16io) hipLaunchKernelGGL((recur_fwd_kernel<bf16, DK, DV>), dim3(grid), dim3(DK * DV / 64), 0, s, p); \
+    else hipLaunchKernelGGL((recur_fwd_kernel<float, DK, DV>), dim3(grid), dim3(DK * DV / 64), 0, s, p); \
     return hipGetLastError();                                                                      \
   }
   GDR_RECUR_CASES(X)

@@ -8,14 +8,24 @@
 //   S_bar = Diag(alpha_t) S;  r = S_bar^T e_t;  S = S_bar + k_t (z_t - m_t (.) r)^T;  o_t = S^T q_t
 // with m_t = 1, or the per-value-channel beta of 11.3 (e = k, z = beta (.) v).
 //
-// One workgroup per (batch, head) with one thread per value column: thread
-// v keeps the columns 2 (v / 2) and 2 (v / 2) + 1 of the state in registers
-// for the whole call, over half of the key channels (v % 2 picks the half),
-// so each broadcast of a key-side value feeds two columns, the contractions
-// over the key channels (r and o) are thread-local up to one exchange with
-// the neighbouring lane (DPP), and a token needs no barrier.  The per-token
-// key-side vectors (alpha, e, k, q) of a block of TB = 8 tokens are staged in
-// LDS and read as broadcasts; thread v stages and writes column v.
+// One workgroup per (batch, head) with dk threads.  Thread (group, l) keeps
+// the state entries of key channels 16 l .. 16 l + 15 and of the dv / 16
+// value columns of its column group in registers for the whole call; the
+// dk / 16 lanes of a column group are consecutive, so the contractions over
+// the key channels (r and o) end in a DPP sum over 4 or 8 lanes, and every
+// LDS read of a staged key-side vector feeds dv / 16 columns.  The key-side
+// vectors (e, k, q, one fold factor) of a block of TB = 8 tokens are staged
+// in LDS by one thread per key channel, the value side (z, m, gate) by one
+// thread per value column; a token needs no barrier.
+//
+// The decay is applied lazily: per key channel the state is held as
+// s * S~, with s the product of the channel's decays since its last fold,
+// so the staging scales e and q by s and k by 1/s and the token loop does no
+// decay multiply.  A channel whose s would leave [2^-40, 2^40] folds s into
+// its state row at that token (one multiply of the row, flagged per token),
+// and the call ends with a fold of every channel.  The rounding therefore
+// depends on where a sequence is split between calls (within fp32 rounding
+// of the one-call result).
 //
 // Output epilogue (11.3: RMSNorm of each head's readout, then the SiLU output
 // gate; the Gated DeltaNet-2 page's method flowchart ends with the same step):
@@ -58,16 +68,66 @@ __device__ __forceinline__ f32x4 ld4x(const bf16* p) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + fexp(-x)); }
 
-template <class IO, int DK, int DV>
-__global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
-  constexpr int TB = 8;         // tokens staged per block
-  constexpr int NW = DV / 64;   // waves
-  static_assert(DV % 64 == 0 && DK % 4 == 0, "recurrent layout");
-  __shared__ __attribute__((aligned(16))) float sA[TB][DK], sE[TB][DK], sK[TB][DK], sQ[TB][DK];
-  __shared__ float sP[TB][NW];
-  __shared__ float sZ[TB][DV], sM[TB][DV], sGt[TB][DV];  // value side, one column per thread
+// DPP read of a neighbouring lane's value: quad_perm [1,0,3,2] (lane ^ 1),
+// quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (lane i of each 8-lane
+// half-row from lane 7 - i)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppX1 = 0xB1, kDppX2 = 0x4E, kDppHalfMirror = 0x141;
 
-  const int v = threadIdx.x, wave = v >> 6;
+// sum over the G consecutive lanes (G = 4 or 8, aligned) that share a value
+// column group; every lane of the group gets the sum
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f<kDppX1>(x);
+  x += dpp_f<kDppX2>(x);
+  if constexpr (G == 8) x += dpp_f<kDppHalfMirror>(x);
+  return x;
+}
+
+// one halving step of a reduce-scatter over a lane pair: the lane with `up`
+// set keeps the upper half of the first L values, its partner the lower
+// half, and each adds the partner's copy of the half it keeps (L = 1: plain
+// sum)
+template <int L, int CTRL, int N>
+__device__ __forceinline__ void halve(float (&x)[N], bool up) {
+  if constexpr (L == 1) {
+    x[0] += dpp_f<CTRL>(x[0]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < L / 2; ++j) {
+      const float keep = up ? x[j + L / 2] : x[j];
+      const float send = up ? x[j] : x[j + L / 2];
+      x[j] = keep + dpp_f<CTRL>(send);
+    }
+  }
+}
+
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(DK * DV / 64) __attribute__((amdgpu_waves_per_eu(4))) void recur_fwd_kernel(RecurParams p) {
+  constexpr int TB = 8;                  // tokens staged per block
+  constexpr int DC = 16;                 // key channels per thread
+  constexpr int G = DK / DC;             // lanes per value-column group (4 or 8)
+  constexpr int NC = 4;                  // value columns per thread
+  constexpr int NT = DK * DV / 64;       // threads: G lanes per group of NC columns
+  constexpr int NW = NT / 64;            // waves
+  constexpr int GS = DC + 4;             // padded stride of one lane's channels in a key-side row
+  constexpr int RS = G * GS;             // key-side row (floats)
+  constexpr int L0 = G == 8 ? (NC > 1 ? NC / 2 : 1) : NC;  // values left after the half-mirror step
+  constexpr int L1 = L0 > 1 ? L0 / 2 : 1;                  // after the lane ^ 2 step
+  constexpr int NO = L1 > 1 ? L1 / 2 : 1;                  // after the lane ^ 1 step: my outputs
+  static_assert((G == 4 || G == 8) && NT % 64 == 0, "recurrent layout");
+  __shared__ __attribute__((aligned(16))) float sE[TB][RS], sK[TB][RS], sQ[TB][RS], sF[TB][RS];
+  __shared__ __attribute__((aligned(16))) float sZ[TB][DV], sM[TB][DV];
+  __shared__ float sP[TB][NW];
+  __shared__ float sScale[DK];
+  __shared__ unsigned sFold[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = tid % G, cgi = tid / G;   // lane in its column group, column group
+  const int cb = li * DC, col0 = cgi * NC;  // my key channels and value columns
   const int bh = blockIdx.x;
   const int bb = bh / p.H, hh = bh - bb * p.H;
   const int T = p.T, H = p.H;
@@ -79,167 +139,250 @@ __global__ __launch_bounds__(DV) void recur_fwd_kernel(RecurParams p) {
   const IO* gateg = reinterpret_cast<const IO*>(p.gate);
   IO* og = reinterpret_cast<IO*>(p.o);
   const bool epi = p.gate != nullptr;
-  const float nwv = epi ? p.nw[v] : 0.f;
 
-  // state: columns col0 and col0 + 1, key channels cb .. cb + DK / 2 - 1
-  constexpr int DH = DK / 2;
-  const int col0 = v & ~1, hf = v & 1, cb = hf * DH;
-  float S[2][DH];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int c = 0; c < DH; ++c)
-      S[j][c] = p.state_in ? p.state_in[((size_t)bh * DK + cb + c) * DV + col0 + j] : 0.f;
-  // the neighbouring lane's partial sum added (DPP quad permutation 1 0 3 2)
-  auto pair_sum = [](float x) __attribute__((always_inline)) {
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
-  };
-
-  // staging layout: QPR threads cover a row of DK channels four at a time;
-  // the DV / QPR groups of them take every (DV / QPR)-th token of a block
-  constexpr int QPR = DK / 4, NG = DV / QPR, TPG = TB / NG;
-  static_assert(NG * QPR == DV && TPG * NG == TB, "staging layout");
-  const int grp = v / QPR, c4 = (v - grp * QPR) * 4;
-  const float* gsrc = decay ? p.g : reinterpret_cast<const float*>(p.v);  // any readable stand-in
-  const float* bsrc = (erase == 0 || write == 0) ? p.beta : reinterpret_cast<const float*>(p.v);
-  for (int t0 = 0; t0 < T; t0 += TB) {
-    const int nt = min(TB, T - t0);
-    // ---- key side of the block: alpha, e, k, q (zeros and alpha = 1 past T).
-    // Every load is issued first, at a token index clamped to T - 1, and
-    // masked afterwards, so that the loads of the block are in flight together.
-    {
-      f32x4 rk[TPG], rq[TPG], rg[TPG], rb[TPG];
-      float rgs[TPG], rbe[TPG], rl[TPG];
-#pragma unroll
-      for (int u = 0; u < TPG; ++u) {
-        const int tt = grp + NG * u;
-        const size_t tok = seq0 + (size_t)min(t0 + tt, T - 1) * H;
-        rk[u] = ld4x(kg + tok * DK + c4);
-        rq[u] = ld4x(qg + tok * DK + c4);
-        if (decay == 2) rg[u] = ld4x(p.g + tok * DK + c4);
-        rgs[u] = gsrc[tok];
-        if (erase == 1) rb[u] = ld4x(p.b + tok * DK + c4);
-        rbe[u] = bsrc[tok];
-        rl[u] = qmix == 2 ? p.lam[tok] : (qmix ? p.lam[hh] : 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < TPG; ++u) {
-        const int tt = grp + NG * u;
-        const bool ok = tt < nt;
-        f32x4 a, e, kk, qq;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kk[i] = ok ? rk[u][i] : 0.f;
-          qq[i] = ok ? rq[u][i] : 0.f;
-          a[i] = !ok ? 1.f : (decay == 2 ? fexp(rg[u][i]) : (decay == 1 ? fexp(rgs[u]) : 1.f));
-          if (erase == 1) e[i] = (ok ? rb[u][i] : 0.f) * kk[i];
-          else if (erase == 2) e[i] = kk[i];
-          else e[i] = rbe[u] * __builtin_fmaf(rl[u], qq[i], kk[i]);
-        }
-        *reinterpret_cast<f32x4*>(&sA[tt][c4]) = a;
-        *reinterpret_cast<f32x4*>(&sE[tt][c4]) = e;
-        *reinterpret_cast<f32x4*>(&sK[tt][c4]) = kk;
-        *reinterpret_cast<f32x4*>(&sQ[tt][c4]) = qq;
-      }
+  // my output columns after the reduce-scatter (lanes with an odd li repeat
+  // their partner's column when NC < G and do not store)
+  int ocol = 0;
+  {
+    int L = NC;
+    if constexpr (G == 8) {
+      if (L > 1) { L /= 2; ocol += (li & 4) ? L : 0; }
     }
-    // ---- value side of my column: z, the erase multiplier m and the gate
-    {
-      float rv[TB], rw[TB], rgt[TB];
+    if (L > 1) { L /= 2; ocol += (li & 2) ? L : 0; }
+    if (L > 1) { L /= 2; ocol += (li & 1) ? L : 0; }
+  }
+  const bool ostore = NC >= G || (li & 1) == 0;
+  float nwv[NO];
+#pragma unroll
+  for (int u = 0; u < NO; ++u) nwv[u] = epi ? p.nw[col0 + ocol + u] : 0.f;
+
+  // S[i][j] = state row cb + i, column col0 + j, divided by the running
+  // decay of channel cb + i (see below)
+  float S[DC][NC];
+#pragma unroll
+  for (int i = 0; i < DC; ++i)
+#pragma unroll
+    for (int j4 = 0; j4 < NC / 4; ++j4) {
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p.state_in) x = *reinterpret_cast<const f32x4*>(p.state_in + ((size_t)bh * DK + cb + i) * DV + col0 + 4 * j4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) S[i][4 * j4 + u] = x[u];
+    }
+  if (tid == 0) sFold[0] = sFold[1] = 0u;
+  __syncthreads();
+
+  // Staging: thread c owns key channel c.  The decay is applied lazily: the
+  // state is kept as Diag(s) S~ with s the product of the channel's decays
+  // since the last fold, so a token's decay costs nothing in the token loop;
+  // e and q are staged times s and k divided by s.  When s of some channel
+  // would leave [2^-40, 2^40] at a token (a strong decay, or a decay of
+  // exactly zero), that token folds: the staging writes the factor f = s for
+  // the channel, the token loop multiplies the channel's state row by it and
+  // s restarts at 1.  The call ends with one fold of every channel.
+  const int c = tid;                      // key-side staging: threads c < DK
+  const bool kside = c < DK;
+  const int ci = (c / DC) * GS + c % DC;  // channel c in a key-side row
+  const int vt = (tid + NT - DK) % NT;    // value-side staging: from thread DK on
+  float srun = 1.f;
+  // (a readable stand-in where beta is absent: its loads are never used)
+  const float* bsrc = (erase == 0 || write == 0) ? p.beta : reinterpret_cast<const float*>(p.v);
+  for (int t0 = 0, blk = 0; t0 < T; t0 += TB, ++blk) {
+    const int nt = min(TB, T - t0);
+    if (tid == 0) sFold[(blk + 1) & 1] = 0u;  // flags of the next block (last read two barriers ago)
+    if (kside) {
+      // the loads of four tokens at a time first, at token indices clamped
+      // to T - 1; each array is addressed from the block's first token with
+      // 32-bit offsets, so that the loads take the scalar-base form
+      const size_t row0 = seq0 + (size_t)t0 * H;  // token row of the block's first token
+      const IO* kb = kg + row0 * DK;
+      const IO* qb = qg + row0 * DK;
+      const float* gb = decay == 2 ? p.g + row0 * DK : p.g + row0;
+      const float* bb_ = erase == 1 ? p.b + row0 * DK : nullptr;
+      const float* beb = bsrc + row0;
+      const float* lb = qmix == 2 ? p.lam + row0 : nullptr;
+      unsigned fold = 0u;
+#pragma unroll
+      for (int h = 0; h < TB; h += 4) {
+        float kx[4], qx[4], gx[4], bx[4], bex[4], lx[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const unsigned r = (unsigned)min(h + u, nt - 1) * (unsigned)H;  // token row within the block
+          kx[u] = ldx(kb + (r * DK + c));
+          qx[u] = ldx(qb + (r * DK + c));
+          gx[u] = decay == 2 ? gb[r * DK + c] : (decay == 1 ? gb[r] : 0.f);
+          bx[u] = erase == 1 ? bb_[r * DK + c] : 0.f;
+          bex[u] = beb[r];
+          lx[u] = qmix == 2 ? lb[r] : (qmix ? p.lam[hh] : 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int tt = h + u;
+          const bool ok = tt < nt;
+          float kk = ok ? kx[u] : 0.f, qq = ok ? qx[u] : 0.f;
+          float e;
+          if (erase == 1) e = bx[u] * kk;
+          else if (erase == 2) e = kk;
+          else e = bex[u] * __builtin_fmaf(lx[u], qq, kk);
+          float f = 1.f;
+          if (decay != 0) {
+            float sp = srun * (ok ? fexp(gx[u]) : 1.f);
+            if (!(sp >= 0x1p-40f && sp <= 0x1p40f)) {
+              f = sp;
+              sp = 1.f;
+              fold |= 1u << tt;
+            }
+            srun = sp;
+            e *= sp;
+            qq *= sp;
+            kk *= __builtin_amdgcn_rcpf(sp);
+          }
+          sE[tt][ci] = e;
+          sK[tt][ci] = kk;
+          sQ[tt][ci] = qq;
+          sF[tt][ci] = f;
+        }
+      }
+      if (fold) atomicOr(&sFold[blk & 1], fold);
+    }
+    // value side: column vt, vt + NT, ... (z and the erase multiplier m)
+#pragma unroll 1
+    for (int vc = vt; vc < DV; vc += NT) {
+      const size_t row0 = seq0 + (size_t)t0 * H;
+      const IO* vb = vg + row0 * DV + vc;
+      const float* wb = erase == 2 ? p.beta + row0 * DV + vc : (write == 1 ? p.w + row0 * DV + vc : nullptr);
+      const float* beb = bsrc + row0;
+      float rv[TB], rw[TB];
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt) {
-        const size_t tok = seq0 + (size_t)min(t0 + tt, T - 1) * H;
-        rv[tt] = ldx(vg + tok * DV + v);
-        rw[tt] = erase == 2 ? p.beta[tok * DV + v] : (write == 1 ? p.w[tok * DV + v] : bsrc[tok]);
-        rgt[tt] = epi ? ldx(gateg + tok * DV + v) : 0.f;
+        const unsigned r = (unsigned)min(tt, nt - 1) * (unsigned)H;
+        rv[tt] = ldx(vb + r * DV);
+        rw[tt] = (erase == 2 || write == 1) ? wb[r * DV] : beb[r];
       }
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt) {
         const bool ok = tt < nt;
-        sM[tt][v] = (erase == 2 && ok) ? rw[tt] : 1.f;
-        sZ[tt][v] = ok ? rw[tt] * rv[tt] : 0.f;
-        sGt[tt][v] = ok ? rgt[tt] : 0.f;
+        sM[tt][vc] = (erase == 2 && ok) ? rw[tt] : 1.f;
+        sZ[tt][vc] = ok ? rw[tt] * rv[tt] : 0.f;
       }
     }
     __syncthreads();
-    float ob[TB];
+
+    // token loop: r = S_bar^T e, d = z - m (.) r, S += k d^T, o = S^T q, with
+    // the contractions over my 16 channels and then over the G lanes
+    const unsigned fb = sFold[blk & 1];
+    float ob[TB][NO];
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
-      ob[tt] = 0.f;
+#pragma unroll
+      for (int u = 0; u < NO; ++u) ob[tt][u] = 0.f;
       if (tt < nt) {
-        // forget (no decay: alpha = 1), then predict along e
-        if (decay != 0) {
+        if (fb & (1u << tt)) {
 #pragma unroll
-          for (int c = 0; c < DH; c += 4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[tt][cb + c]);
+          for (int i4 = 0; i4 < DC / 4; ++i4) {
+            const f32x4 f = *reinterpret_cast<const f32x4*>(&sF[tt][li * GS + 4 * i4]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              S[0][c + u] *= a[u];
-              S[1][c + u] *= a[u];
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int j = 0; j < NC; ++j) S[4 * i4 + u][j] *= f[u];
+          }
+        }
+        float r[NC];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) r[j] = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < DC / 4; ++i4) {
+          const f32x4 e = *reinterpret_cast<const f32x4*>(&sE[tt][li * GS + 4 * i4]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) r[j] = __builtin_fmaf(e[u], S[4 * i4 + u][j], r[j]);
+        }
+        float d[NC];
+#pragma unroll
+        for (int j4 = 0; j4 < NC / 4; ++j4) {
+          const f32x4 z = *reinterpret_cast<const f32x4*>(&sZ[tt][col0 + 4 * j4]);
+          f32x4 m = f32x4{1.f, 1.f, 1.f, 1.f};
+          if (erase == 2) m = *reinterpret_cast<const f32x4*>(&sM[tt][col0 + 4 * j4]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) d[4 * j4 + u] = z[u] - m[u] * group_sum<G>(r[4 * j4 + u]);
+        }
+        float o[NC];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) o[j] = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < DC / 4; ++i4) {
+          const f32x4 kk = *reinterpret_cast<const f32x4*>(&sK[tt][li * GS + 4 * i4]);
+          const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[tt][li * GS + 4 * i4]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+              S[4 * i4 + u][j] = __builtin_fmaf(kk[u], d[j], S[4 * i4 + u][j]);
+              o[j] = __builtin_fmaf(qq[u], S[4 * i4 + u][j], o[j]);
             }
-          }
         }
-        float r0 = 0.f, r1 = 0.f;
+        // reduce-scatter of o over the G lanes: lane li ends with columns
+        // ocol .. ocol + NO - 1
+        if constexpr (G == 8) halve<NC, kDppHalfMirror>(o, (li & 4) != 0);
+        halve<L0, kDppX2>(o, (li & 2) != 0);
+        halve<L1, kDppX1>(o, (li & 1) != 0);
 #pragma unroll
-        for (int c = 0; c < DH; c += 4) {
-          const f32x4 e = *reinterpret_cast<const f32x4*>(&sE[tt][cb + c]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            r0 = __builtin_fmaf(e[u], S[0][c + u], r0);
-            r1 = __builtin_fmaf(e[u], S[1][c + u], r1);
-          }
-        }
-        r0 = pair_sum(r0);
-        r1 = pair_sum(r1);
-        const float d0 = sZ[tt][col0] - sM[tt][col0] * r0;
-        const float d1 = sZ[tt][col0 + 1] - sM[tt][col0 + 1] * r1;
-        // write along k, then read along q
-        float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < DH; c += 4) {
-          const f32x4 kk = *reinterpret_cast<const f32x4*>(&sK[tt][cb + c]);
-          const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[tt][cb + c]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            S[0][c + u] = __builtin_fmaf(kk[u], d0, S[0][c + u]);
-            S[1][c + u] = __builtin_fmaf(kk[u], d1, S[1][c + u]);
-            o0 = __builtin_fmaf(qq[u], S[0][c + u], o0);
-            o1 = __builtin_fmaf(qq[u], S[1][c + u], o1);
-          }
-        }
-        o0 = pair_sum(o0);
-        o1 = pair_sum(o1);
-        ob[tt] = hf ? o1 : o0;  // column v
+        for (int u = 0; u < NO; ++u) ob[tt][u] = o[u];
       }
     }
     if (epi) {
       // mean of o^2 over the dv columns of each token: wave sums, then the waves'
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt) {
-        const float s = wave_sum(ob[tt] * ob[tt]);
-        if ((v & 63) == 0) sP[tt][wave] = s;
+        float s2 = 0.f;
+#pragma unroll
+        for (int u = 0; u < NO; ++u) s2 += ob[tt][u] * ob[tt][u];
+        const float s = wave_sum(ostore ? s2 : 0.f);
+        if (lane == 0) sP[tt][wave] = s;
       }
     }
-    __syncthreads();  // the block's key-side vectors (and partial sums) are read
+    __syncthreads();  // the block's staged vectors (and partial sums) are read
+    if (ostore) {
 #pragma unroll
-    for (int tt = 0; tt < TB; ++tt) {
-      if (tt < nt) {
-        const size_t tok = seq0 + (size_t)(t0 + tt) * H;
-        float y = ob[tt];
-        if (epi) {
-          float ss = 0.f;
+      for (int tt = 0; tt < TB; ++tt) {
+        if (tt < nt) {
+          const size_t tok = seq0 + (size_t)(t0 + tt) * H;
+          float inv = 1.f;
+          if (epi) {
+            float ss = 0.f;
 #pragma unroll
-          for (int w2 = 0; w2 < NW; ++w2) ss += sP[tt][w2];
-          y = y * rsqrtf(ss * (1.f / DV) + p.eps) * nwv * silu(sGt[tt][v]);
+            for (int w2 = 0; w2 < NW; ++w2) ss += sP[tt][w2];
+            inv = rsqrtf(ss * (1.f / DV) + p.eps);
+          }
+#pragma unroll
+          for (int u = 0; u < NO; ++u) {
+            const int col = col0 + ocol + u;
+            float y = ob[tt][u];
+            if (epi) y = y * inv * nwv[u] * silu(ldx(gateg + tok * DV + col));
+            og[tok * DV + col] = (IO)y;
+          }
         }
-        og[tok * DV + v] = (IO)y;
       }
     }
   }
   if (p.state_out) {
+    if (decay != 0) {
+      // the closing fold: S = Diag(s) S~
+      if (kside) sScale[c] = srun;
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < DC; ++i) {
+        const float f = sScale[cb + i];
 #pragma unroll
-      for (int c = 0; c < DH; ++c) p.state_out[((size_t)bh * DK + cb + c) * DV + col0 + j] = S[j][c];
+        for (int j = 0; j < NC; ++j) S[i][j] *= f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DC; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < NC / 4; ++j4)
+        *reinterpret_cast<f32x4*>(p.state_out + ((size_t)bh * DK + cb + i) * DV + col0 + 4 * j4) =
+            f32x4{S[i][4 * j4], S[i][4 * j4 + 1], S[i][4 * j4 + 2], S[i][4 * j4 + 3]};
   }
 }
 

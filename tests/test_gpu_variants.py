@@ -102,9 +102,13 @@ def test_recurrent_parity(name):
     assert_parity(name, o.float().cpu().numpy(), S.cpu().numpy(), o_ref, S_ref, TOL[cfg["io"]])
 
 
-def test_recurrent_streaming_is_bitwise():
-    """Two calls with the state handed over equal one call bit for bit, at a
-    split that is not a multiple of the 16-token staging block."""
+def test_recurrent_streaming_handoff():
+    """Two calls with the state handed over agree with one call, at a split
+    that is not a multiple of the 8-token staging block.  The kernel folds
+    each channel's running decay into the state at the end of a call (and
+    only when needed inside one), so a split moves roundings: the fp32 state
+    agrees to a few fp32 roundings and the bf16 output to its own rounding
+    (one bf16 step is 2^-8 of the value)."""
     cfg = config(G2, B=2, H=2, T=45, decay_shift=-4.0, state_std=0.05)
     inp = make_inputs(cfg)
     d = to_dev(inp)
@@ -120,7 +124,9 @@ def test_recurrent_streaming_is_bitwise():
     kw2["state"] = S1
     o2, S2 = gdr.recurrent_fwd(sl(d["q"], cut, 45), sl(d["k"], cut, 45), sl(d["v"], cut, 45), **kw2)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([o1, o2], dim=1), o) and torch.equal(S2, S)
+    o_split = torch.cat([o1, o2], dim=1).float().cpu().numpy()
+    assert rel_err(o_split, o.float().cpu().numpy()) <= 2.0 ** -8
+    assert rel_err(S2.cpu().numpy(), S.cpu().numpy()) <= 1e-5
 
 
 def test_recurrent_matches_the_chunk_form():
