@@ -405,294 +405,21 @@ void bwd_prod_kernel(BwdParams p) {
   if (tid % TPC == 0) ws.gC[ch * DK + tid / TPC] = sc;
 }
 
-// ---- pass B2: back to the rows, the cumulative decay and the gates -----------
-// The key channels are taken KC = 64 at a time, so that the chunk's k, e, q
-// and G columns of the pass and the whole dT and dA_qk fit in LDS together;
-// every inner-loop operand is then an LDS read (dT and dA_qk rows as
-// broadcasts).  Thread (wave w, lane c) owns channel c of the pass in 16
-// rows, so each row of a pass is one wave and its sums over the channels are
-// wave reductions.  Under a decay per key channel the weights d_ij[c] are
-// formed per term (rows w, w + 4, ...).  Under a scalar decay (or none)
-// d_ij is one number per token pair: the kernel forms D1 = dT (.) D and
-// D2 = dA_qk (.) D below the diagonal (and their transposes) once per
-// chunk, and the four sums are row products with them (rows 16 w .. + 15,
-// so that each wave's sums stop at its rows' bounds).
-template <class IO, int DK, int DV>
-__global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
-  constexpr int KC = 64, NPASS = DK / KC;
-  constexpr int NP = NTHR / KC, RPP = CH / NP;   // 4 row partitions of 16 rows
-  constexpr int VW = DV / 64;                    // waves per row of the value side
-  constexpr int TP = CH + 4;  // 16-byte rows for the b128 reads of the scalar-decay products
-  static_assert(DK % KC == 0, "key channels in passes of 64");
-  __shared__ __attribute__((aligned(16))) float sK[CH * KC], sE[CH * KC], sQ[CH * KC], sG[CH * KC];
-  __shared__ __attribute__((aligned(16))) float sdT[CH * TP], sdA[CH * TP], sD1T[CH * TP], sD2T[CH * TP];
-  __shared__ float sGC[KC], sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW], sDg[CH];
-  __shared__ float sBeta[CH], sLam[CH], sGt[CH], sDiag[CH], sRG[CH], sRX[CH];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int N = p.nchunks;
-  const size_t ch = blockIdx.x;
-  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
-  const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
+// The end of pass B2, shared by both forms of it: the value side (dZ = dR
+// gives dv and, per gate kind, dw or the write part of dbeta; each wave
+// covers 64 columns of one row per step, every load issued first) and the
+// per-token sums (the scalar-decay dg, dbeta, dlambda) from the rows' LDS
+// partial sums.
+template <class IO, int DK, int DV, int NPASS>
+__device__ __forceinline__ void key_tail(const BwdParams& p, size_t ch, int t0, size_t seq0, int tid,
+                                         const float* sBeta, float (*sRz)[DV / 64], const float* sDg,
+                                         const float (*sRb)[NPASS], const float (*sRl)[NPASS]) {
+  constexpr int VW = DV / 64;
+  const int lane = tid & 63;
   const int T = p.f.T, H = p.f.H;
-  const int t0 = n * CH;
   const int decay = p.f.decay, erase = p.f.erase, write = p.f.write, qmix = p.f.qmix;
-  const size_t seq0 = (size_t)bb * T * H + hh;
-  const IO* qg = reinterpret_cast<const IO*>(p.f.q);
-  const IO* kg = reinterpret_cast<const IO*>(p.f.k);
   const IO* vg = reinterpret_cast<const IO*>(p.f.v);
   const BwdWs& ws = p.ws;
-
-  copy_rows<CH, CH, TP>(sdT, ws.T + ch * CH * CH, tid);
-  copy_rows<CH, CH, TP>(sdA, ws.A + ch * CH * CH, tid);
-  for (int r = tid; r < CH; r += NTHR) {
-    const int t = t0 + r;
-    const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
-    sBeta[r] = (t < T && (erase == 0 || write == 0)) ? p.f.beta[tok] : 0.f;
-    sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
-    sDg[r] = 0.f;
-    sRG[r] = 0.f;
-    sRX[r] = 0.f;
-  }
-  const int c = lane;
-  const int par = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool chan = decay == 2;
-  // rows of this thread: w, w + 4, ... (per-channel decay) or 16 w .. + 15
-  auto row_of = [&](int m) { return chan ? par + NP * m : 16 * par + m; };
-
-  if (!chan) {
-    // the scalar decay's prefix sums G_t (zero past T), then
-    // D1 = dT (.) D, D2 = dA_qk (.) D strictly below the diagonal (in place;
-    // the diagonal of dA_qk kept apart) and their transposes
-    if (tid < CH) {
-      const int t = t0 + tid;
-      const float g = (decay == 1 && t < T) ? p.f.g[seq0 + (size_t)t * H] : 0.f;
-      sGt[tid] = wave_incl_scan(g);
-    }
-    __syncthreads();
-    for (int e = tid; e < CH * CH; e += NTHR) {
-      const int i = e >> 6, j = e & 63;
-      const float d = j < i ? fexp(sGt[i] - sGt[j]) : 0.f;
-      const float d1 = sdT[i * TP + j] * d, d2 = sdA[i * TP + j] * d;
-      if (i == j) sDiag[i] = sdA[i * TP + j];
-      sdT[i * TP + j] = d1;
-      sdA[i * TP + j] = d2;
-      sD1T[j * TP + i] = d1;
-      sD2T[j * TP + i] = d2;
-    }
-  }
-
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int cg = ps * KC + c;  // key channel of this thread
-    __syncthreads();             // the previous pass's columns are no longer read
-    // ---- this pass's columns of the chunk's rows (zero past T)
-    {
-      constexpr int QPR = KC / 4, NQ = CH * QPR / NTHR;
-      f32x4 rk[NQ], rq[NQ], rg[NQ], rb[NQ];
-      float rgs[NQ];
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int e = tid + NTHR * u, r = e / QPR, c4 = ps * KC + (e - r * QPR) * 4;
-        const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
-        rk[u] = ldf4(kg + tok * DK + c4);
-        rq[u] = ldf4(qg + tok * DK + c4);
-        if (decay == 2) rg[u] = ldf4(p.f.g + tok * DK + c4);
-        rgs[u] = decay == 1 ? p.f.g[tok] : 0.f;
-        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + c4);
-      }
-      __syncthreads();  // sBeta, sLam
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int e = tid + NTHR * u, r = e / QPR, cl = (e - r * QPR) * 4;
-        const bool ok = t0 + r < T;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float kv = ok ? rk[u][i] : 0.f, qv = ok ? rq[u][i] : 0.f;
-          sK[r * KC + cl + i] = kv;
-          sQ[r * KC + cl + i] = qv;
-          sE[r * KC + cl + i] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv
-                                           : sBeta[r] * __builtin_fmaf(sLam[r], qv, kv);
-          sG[r * KC + cl + i] = !ok ? 0.f : (decay == 2 ? rg[u][i] : rgs[u]);
-        }
-      }
-    }
-    __syncthreads();
-    if (chan && tid < KC) {
-      float run = 0.f;
-      for (int r = 0; r < CH; ++r) {
-        run += sG[r * KC + tid];
-        sG[r * KC + tid] = run;
-      }
-      sGC[tid] = run;
-    }
-    // the product pass's results for my rows
-    float dEb[RPP], dQg[RPP], dKt[RPP], bI[RPP];
-#pragma unroll
-    for (int m = 0; m < RPP; ++m) {
-      const size_t at = (ch * CH + row_of(m)) * DK + cg;
-      dEb[m] = ws.Eb[at];
-      dQg[m] = ws.Qg[at];
-      dKt[m] = ws.Kt[at];
-      const int t = t0 + row_of(m);
-      bI[m] = (erase == 1 && t < T) ? p.f.b[(seq0 + (size_t)t * H) * DK + cg] : 0.f;
-    }
-    __syncthreads();
-    const float GC = chan ? sGC[c] : sGt[CH - 1];
-    // scalar decay: the four sums of my 16 rows as row products with D1, D2
-    // (zero at and above the diagonal) and their transposes
-    float sP[RPP], sPq[RPP], sRm[RPP], sRq[RPP];
-    if (!chan) {
-      static_assert(RPP == 16, "16 rows per wave");
-      const int i0 = 16 * par;
-#pragma unroll
-      for (int m = 0; m < RPP; ++m) sP[m] = sPq[m] = sRm[m] = sRq[m] = 0.f;
-      for (int j0 = 0; j0 < i0 + 16; j0 += 4) {  // j < i
-        float kj[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) kj[u] = sK[(j0 + u) * KC + c];
-#pragma unroll
-        for (int m = 0; m < RPP; ++m) {
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(sdT + (i0 + m) * TP + j0);
-          const f32x4 d2 = *reinterpret_cast<const f32x4*>(sdA + (i0 + m) * TP + j0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            sP[m] = __builtin_fmaf(d1[u], kj[u], sP[m]);
-            sPq[m] = __builtin_fmaf(d2[u], kj[u], sPq[m]);
-          }
-        }
-      }
-      for (int j0 = i0; j0 < CH; j0 += 4) {  // i2 > i
-        float ej[4], qj[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ej[u] = sE[(j0 + u) * KC + c];
-          qj[u] = sQ[(j0 + u) * KC + c];
-        }
-#pragma unroll
-        for (int m = 0; m < RPP; ++m) {
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(sD1T + (i0 + m) * TP + j0);
-          const f32x4 d2 = *reinterpret_cast<const f32x4*>(sD2T + (i0 + m) * TP + j0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            sRm[m] = __builtin_fmaf(d1[u], ej[u], sRm[m]);
-            sRq[m] = __builtin_fmaf(d2[u], qj[u], sRq[m]);
-          }
-        }
-      }
-    }
-    float dGr[RPP], xkt[RPP];
-#pragma unroll
-    for (int m = 0; m < RPP; ++m) {
-      const int i = row_of(m);  // wave-uniform
-      const float gi = chan ? sG[i * KC + c] : sGt[i];
-      const float gam = fexp(gi), tl = fexp(GC - gi);
-      const float ki = sK[i * KC + c], ei = sE[i * KC + c], qi = sQ[i * KC + c];
-      // off-diagonal sums (the diagonal of A_qk has d_ii = 1 and does not
-      // depend on G: its two contributions to dG cancel exactly, so it is
-      // kept out of dG rather than added and cancelled in fp32)
-      float P = 0.f, Pq = 0.f, Rm = 0.f, Rq = 0.f;
-      if (chan) {
-        for (int j = 0; j < i; ++j) {
-          const float kd = sK[j * KC + c] * fexp(gi - sG[j * KC + c]);
-          P = __builtin_fmaf(sdT[i * TP + j], kd, P);
-          Pq = __builtin_fmaf(sdA[i * TP + j], kd, Pq);
-        }
-        for (int i2 = i + 1; i2 < CH; ++i2) {
-          const float d = fexp(sG[i2 * KC + c] - gi);
-          Rm = __builtin_fmaf(sdT[i2 * TP + i], sE[i2 * KC + c] * d, Rm);
-          Rq = __builtin_fmaf(sdA[i2 * TP + i], sQ[i2 * KC + c] * d, Rq);
-        }
-      } else {
-        P = sP[m];
-        Pq = sPq[m];
-        Rm = sRm[m];
-        Rq = sRq[m];
-      }
-      const float diag = chan ? sdA[i * TP + i] : sDiag[i];
-      const float de = __builtin_fmaf(gam, dEb[m], P);
-      float dqd = __builtin_fmaf(gam, dQg[m], __builtin_fmaf(diag, ki, Pq));
-      float dkd = tl * dKt[m] + Rm + __builtin_fmaf(diag, qi, Rq);
-      dGr[m] = ei * gam * dEb[m] + qi * gam * dQg[m] + ei * P + qi * Pq - ki * (Rm + Rq);
-      xkt[m] = ki * tl * dKt[m];  // K_tail_i dK_tail_i
-      // the erase gate
-      float rb = 0.f, rl = 0.f;
-      const int t = t0 + i;
-      const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
-      if (erase == 1) {
-        const float bi = bI[m];
-        if (t < T) p.db[tok * DK + cg] = de * ki;
-        dkd = __builtin_fmaf(bi, de, dkd);
-      } else {
-        const float bt = sBeta[i], lt = sLam[i];
-        rb = de * __builtin_fmaf(lt, qi, ki);
-        dkd = __builtin_fmaf(bt, de, dkd);
-        if (qmix) {
-          dqd = __builtin_fmaf(bt * lt, de, dqd);
-          rl = bt * de * qi;
-        }
-      }
-      if (t < T) {
-        p.dq[tok * DK + cg] = dqd;
-        p.dk[tok * DK + cg] = dkd;
-      }
-      rb = wave_total(rb);
-      rl = wave_total(rl);
-      // scalar decay: the row sums over the channels of dG and of the K_tail
-      // terms, from which the per-token dg follows after the passes
-      float rg = 0.f, rx = 0.f;
-      if (decay == 1) {
-        rg = wave_total(dGr[m]);
-        rx = wave_total(xkt[m]);
-      }
-      if (lane == 0) {
-        sRb[i][ps] = rb;
-        sRl[i][ps] = rl;
-        sRG[i] += rg;
-        sRX[i] += rx;
-      }
-    }
-    if (chan) {
-    __syncthreads();  // sG takes dG, sE the K_tail terms
-#pragma unroll
-    for (int m = 0; m < RPP; ++m) {
-      const int i = row_of(m);
-      sG[i * KC + c] = dGr[m];
-      sE[i * KC + c] = xkt[m];
-    }
-    __syncthreads();
-    // dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC
-    if (tid < KC) {
-      float pre = 0.f;
-      for (int r = 0; r < CH; ++r) {  // exclusive prefix of the K_tail terms
-        const float x = sE[r * KC + tid];
-        sE[r * KC + tid] = pre;
-        pre += x;
-      }
-      const float base = fexp(GC) * ws.gC[ch * DK + ps * KC + tid];
-      float run = 0.f;
-      for (int r = CH - 1; r >= 0; --r) {
-        run += sG[r * KC + tid];
-        const float dgv = run + sE[r * KC + tid] + base;
-        if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + ps * KC + tid] = dgv;
-      }
-    }
-    }
-  }
-  // scalar decay: dg_t = sum_{r>=t} RG_r + sum_{j<t} RX_j + gamma_C sum_c sC[c]
-  // (the per-channel form summed over the channels), by wave prefix sums
-  if (decay == 1) {
-    __syncthreads();
-    if (tid < CH) {
-      float sc = 0.f;
-      for (int c2 = tid; c2 < DK; c2 += CH) sc += ws.gC[ch * DK + c2];
-      const float base = fexp(sGt[CH - 1]) * wave_total(sc);
-      const float rg = sRG[tid], rx = sRX[tid];
-      const float ig = wave_incl_scan(rg), ix = wave_incl_scan(rx);
-      sDg[tid] = (lane_value(ig, 63) - ig + rg) + (ix - rx) + base;
-    }
-  }
-  // ---- value side: dZ = dR (every load of the thread issued first; each
-  // wave covers 64 columns of one row per step)
   {
     constexpr int NE = CH * DV / NTHR;
     const float* dz = ws.dR + ch * CH * DV;
@@ -746,6 +473,422 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
     if (qmix == 2) p.dlam[tok] = sl;
     else if (qmix == 1) ws.dlam[tok] = sl;
   }
+}
+
+// ---- pass B2: back to the rows, the cumulative decay and the gates -----------
+// Under a decay per key channel (this kernel) the weights d_ij[c] are formed
+// per term.  The key channels are taken KC = 64 at a time, so that the
+// chunk's k, e, q and G columns of the pass and the whole dT and dA_qk fit
+// in LDS together; every inner-loop operand is then an LDS read (dT and
+// dA_qk entries as broadcasts).  Thread (wave w, lane c) owns channel c of
+// the pass in rows w, w + 4, ..., so each row of a pass is one wave and its
+// sums over the channels are wave reductions.
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
+  constexpr int KC = 64, NPASS = DK / KC;
+  constexpr int NP = NTHR / KC, RPP = CH / NP;   // 4 row partitions of 16 rows
+  constexpr int VW = DV / 64;                    // waves per row of the value side
+  constexpr int TP = CH + 4;
+  static_assert(DK % KC == 0, "key channels in passes of 64");
+  __shared__ __attribute__((aligned(16))) float sK[CH * KC], sE[CH * KC], sQ[CH * KC], sG[CH * KC];
+  __shared__ __attribute__((aligned(16))) float sdT[CH * TP], sdA[CH * TP];
+  __shared__ float sGC[KC], sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW];
+  __shared__ float sBeta[CH], sLam[CH];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int N = p.nchunks;
+  const size_t ch = blockIdx.x;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
+  const int T = p.f.T, H = p.f.H;
+  const int t0 = n * CH;
+  const int erase = p.f.erase, qmix = p.f.qmix;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* qg = reinterpret_cast<const IO*>(p.f.q);
+  const IO* kg = reinterpret_cast<const IO*>(p.f.k);
+  const BwdWs& ws = p.ws;
+
+  copy_rows<CH, CH, TP>(sdT, ws.T + ch * CH * CH, tid);
+  copy_rows<CH, CH, TP>(sdA, ws.A + ch * CH * CH, tid);
+  for (int r = tid; r < CH; r += NTHR) {
+    const int t = t0 + r;
+    const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+    sBeta[r] = (t < T && (erase == 0 || p.f.write == 0)) ? p.f.beta[tok] : 0.f;
+    sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
+  }
+  const int c = lane;
+  const int par = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int cg = ps * KC + c;  // key channel of this thread
+    __syncthreads();             // the previous pass's columns are no longer read
+    // ---- this pass's columns of the chunk's rows (zero past T)
+    {
+      constexpr int QPR = KC / 4, NQ = CH * QPR / NTHR;
+      f32x4 rk[NQ], rq[NQ], rg[NQ], rb[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, c4 = ps * KC + (e - r * QPR) * 4;
+        const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+        rk[u] = ldf4(kg + tok * DK + c4);
+        rq[u] = ldf4(qg + tok * DK + c4);
+        rg[u] = ldf4(p.f.g + tok * DK + c4);
+        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + c4);
+      }
+      __syncthreads();  // sBeta, sLam
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, cl = (e - r * QPR) * 4;
+        const bool ok = t0 + r < T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float kv = ok ? rk[u][i] : 0.f, qv = ok ? rq[u][i] : 0.f;
+          sK[r * KC + cl + i] = kv;
+          sQ[r * KC + cl + i] = qv;
+          sE[r * KC + cl + i] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv
+                                           : sBeta[r] * __builtin_fmaf(sLam[r], qv, kv);
+          sG[r * KC + cl + i] = ok ? rg[u][i] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < KC) {
+      float run = 0.f;
+      for (int r = 0; r < CH; ++r) {
+        run += sG[r * KC + tid];
+        sG[r * KC + tid] = run;
+      }
+      sGC[tid] = run;
+    }
+    // the product pass's results for my rows
+    float dEb[RPP], dQg[RPP], dKt[RPP], bI[RPP];
+#pragma unroll
+    for (int m = 0; m < RPP; ++m) {
+      const int i = par + NP * m;
+      const size_t at = (ch * CH + i) * DK + cg;
+      dEb[m] = ws.Eb[at];
+      dQg[m] = ws.Qg[at];
+      dKt[m] = ws.Kt[at];
+      const int t = t0 + i;
+      bI[m] = (erase == 1 && t < T) ? p.f.b[(seq0 + (size_t)t * H) * DK + cg] : 0.f;
+    }
+    __syncthreads();
+    const float GC = sGC[c];
+    float dGr[RPP], xkt[RPP];
+#pragma unroll
+    for (int m = 0; m < RPP; ++m) {
+      const int i = par + NP * m;  // wave-uniform
+      const float gi = sG[i * KC + c];
+      const float gam = fexp(gi), tl = fexp(GC - gi);
+      const float ki = sK[i * KC + c], ei = sE[i * KC + c], qi = sQ[i * KC + c];
+      // off-diagonal sums (the diagonal of A_qk has d_ii = 1 and does not
+      // depend on G: its two contributions to dG cancel exactly, so it is
+      // kept out of dG rather than added and cancelled in fp32)
+      float P = 0.f, Pq = 0.f, Rm = 0.f, Rq = 0.f;
+      for (int j = 0; j < i; ++j) {
+        const float kd = sK[j * KC + c] * fexp(gi - sG[j * KC + c]);
+        P = __builtin_fmaf(sdT[i * TP + j], kd, P);
+        Pq = __builtin_fmaf(sdA[i * TP + j], kd, Pq);
+      }
+      for (int i2 = i + 1; i2 < CH; ++i2) {
+        const float d = fexp(sG[i2 * KC + c] - gi);
+        Rm = __builtin_fmaf(sdT[i2 * TP + i], sE[i2 * KC + c] * d, Rm);
+        Rq = __builtin_fmaf(sdA[i2 * TP + i], sQ[i2 * KC + c] * d, Rq);
+      }
+      const float diag = sdA[i * TP + i];
+      const float de = __builtin_fmaf(gam, dEb[m], P);
+      float dqd = __builtin_fmaf(gam, dQg[m], __builtin_fmaf(diag, ki, Pq));
+      float dkd = tl * dKt[m] + Rm + __builtin_fmaf(diag, qi, Rq);
+      dGr[m] = ei * gam * dEb[m] + qi * gam * dQg[m] + ei * P + qi * Pq - ki * (Rm + Rq);
+      xkt[m] = ki * tl * dKt[m];  // K_tail_i dK_tail_i
+      // the erase gate
+      float rb = 0.f, rl = 0.f;
+      const int t = t0 + i;
+      const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+      if (erase == 1) {
+        if (t < T) p.db[tok * DK + cg] = de * ki;
+        dkd = __builtin_fmaf(bI[m], de, dkd);
+      } else {
+        const float bt = sBeta[i], lt = sLam[i];
+        rb = de * __builtin_fmaf(lt, qi, ki);
+        dkd = __builtin_fmaf(bt, de, dkd);
+        if (qmix) {
+          dqd = __builtin_fmaf(bt * lt, de, dqd);
+          rl = bt * de * qi;
+        }
+      }
+      if (t < T) {
+        p.dq[tok * DK + cg] = dqd;
+        p.dk[tok * DK + cg] = dkd;
+      }
+      rb = wave_total(rb);
+      rl = wave_total(rl);
+      if (lane == 0) {
+        sRb[i][ps] = rb;
+        sRl[i][ps] = rl;
+      }
+    }
+    __syncthreads();  // sG takes dG, sE the K_tail terms
+#pragma unroll
+    for (int m = 0; m < RPP; ++m) {
+      const int i = par + NP * m;
+      sG[i * KC + c] = dGr[m];
+      sE[i * KC + c] = xkt[m];
+    }
+    __syncthreads();
+    // dg_t = sum_{r>=t} dG_r + sum_{j<t} K_tail_j dK_tail_j + gamma_C sC
+    if (tid < KC) {
+      float pre = 0.f;
+      for (int r = 0; r < CH; ++r) {  // exclusive prefix of the K_tail terms
+        const float x = sE[r * KC + tid];
+        sE[r * KC + tid] = pre;
+        pre += x;
+      }
+      const float base = fexp(GC) * ws.gC[ch * DK + ps * KC + tid];
+      float run = 0.f;
+      for (int r = CH - 1; r >= 0; --r) {
+        run += sG[r * KC + tid];
+        const float dgv = run + sE[r * KC + tid] + base;
+        if (t0 + r < T) p.dg[(seq0 + (size_t)(t0 + r) * H) * DK + ps * KC + tid] = dgv;
+      }
+    }
+  }
+  key_tail<IO, DK, DV, NPASS>(p, ch, t0, seq0, tid, sBeta, sRz, nullptr, sRb, sRl);
+}
+
+// Pass B2 under a scalar decay (or none): d_ij = exp(G_i - G_j) is one
+// number per token pair, so with D1 = dT (.) D and D2 = dA_qk (.) D (strictly
+// lower; the diagonal of dA_qk kept apart) the four sums are products of 64 x
+// 64 matrices, run on v_mfma_f32_16x16x4_f32 per pass of 64 key channels:
+//   P = D1 K,  Pq = D2 K,  Rm = D1^T E,  Rq = D2^T Q
+// Wave w owns row block w (its P, Pq over column blocks J <= w, its Rm, Rq
+// over J >= w: 160 MFMAs per wave and pass whatever w).  k-step (J, r) takes,
+// in lane group g, the token 16 J + 4 g + r, so every operand is a 16-byte
+// LDS read feeding four MFMAs: rows of D1, D2 and of their transposes, and
+// rows of K^T, E^T, Q^T (the pass's columns staged transposed).  Lane
+// (g, l) then holds rows 16 w + 4 g + r of channel 16 C + l of each column
+// block C; a row's sums over the channels end in a DPP sum over the 16
+// lanes of its group.
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_key_scalar_kernel(BwdParams p) {
+  constexpr int KC = 64, NPASS = DK / KC;
+  constexpr int VW = DV / 64;
+  constexpr int TP = CH + 4;  // 16-byte rows; 4-bank shift per row
+  static_assert(DK % KC == 0 && NTHR == 256, "key channels in passes of 64, four waves");
+  __shared__ __attribute__((aligned(16))) float sD1[CH * TP], sD2[CH * TP], sD1T[CH * TP], sD2T[CH * TP];
+  __shared__ __attribute__((aligned(16))) float sKT[KC * TP], sET[KC * TP], sQT[KC * TP];
+  __shared__ float sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW], sDg[CH];
+  __shared__ float sBeta[CH], sLam[CH], sGt[CH], sDiag[CH], sRG[CH], sRX[CH];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int N = p.nchunks;
+  const size_t ch = blockIdx.x;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
+  const int T = p.f.T, H = p.f.H;
+  const int t0 = n * CH;
+  const int decay = p.f.decay, erase = p.f.erase, qmix = p.f.qmix;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const IO* qg = reinterpret_cast<const IO*>(p.f.q);
+  const IO* kg = reinterpret_cast<const IO*>(p.f.k);
+  const BwdWs& ws = p.ws;
+
+  copy_rows<CH, CH, TP>(sD1, ws.T + ch * CH * CH, tid);
+  copy_rows<CH, CH, TP>(sD2, ws.A + ch * CH * CH, tid);
+  for (int r = tid; r < CH; r += NTHR) {
+    const int t = t0 + r;
+    const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+    sBeta[r] = (t < T && (erase == 0 || p.f.write == 0)) ? p.f.beta[tok] : 0.f;
+    sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
+    sDg[r] = 0.f;
+    sRG[r] = 0.f;
+    sRX[r] = 0.f;
+  }
+  // the scalar decay's prefix sums G_t (zero past T), then D1, D2 strictly
+  // below the diagonal (in place; the diagonal of dA_qk kept apart) and
+  // their transposes
+  if (tid < CH) {
+    const int t = t0 + tid;
+    const float gv = (decay == 1 && t < T) ? p.f.g[seq0 + (size_t)t * H] : 0.f;
+    sGt[tid] = wave_incl_scan(gv);
+  }
+  __syncthreads();
+  for (int e = tid; e < CH * CH; e += NTHR) {
+    const int i = e >> 6, j = e & 63;
+    const float d = j < i ? fexp(sGt[i] - sGt[j]) : 0.f;
+    const float d1 = sD1[i * TP + j] * d, d2 = sD2[i * TP + j] * d;
+    if (i == j) sDiag[i] = sD2[i * TP + j];
+    sD1[i * TP + j] = d1;
+    sD2[i * TP + j] = d2;
+    sD1T[j * TP + i] = d1;
+    sD2T[j * TP + i] = d2;
+  }
+  const float GC = sGt[CH - 1];  // (read after the first barrier of the pass loop)
+  // a row's sum over the 16 lanes of its group (quad permutations, then the
+  // half-row and row mirrors)
+  auto row16 = [](float x) __attribute__((always_inline)) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xf, 0xf, true));
+    return x;
+  };
+
+  for (int ps = 0; ps < NPASS; ++ps) {
+    __syncthreads();  // the previous pass's columns are no longer read
+    // ---- this pass's columns of the chunk's rows, transposed (zero past T)
+    {
+      constexpr int QPR = KC / 4, NQ = CH * QPR / NTHR;
+      f32x4 rk[NQ], rq[NQ], rb[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, c4 = ps * KC + (e - r * QPR) * 4;
+        const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+        rk[u] = ldf4(kg + tok * DK + c4);
+        rq[u] = ldf4(qg + tok * DK + c4);
+        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + c4);
+      }
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int e = tid + NTHR * u, r = e / QPR, cl = (e - r * QPR) * 4;
+        const bool ok = t0 + r < T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float kv = ok ? rk[u][i] : 0.f, qv = ok ? rq[u][i] : 0.f;
+          sKT[(cl + i) * TP + r] = kv;
+          sQT[(cl + i) * TP + r] = qv;
+          sET[(cl + i) * TP + r] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv
+                                              : sBeta[r] * __builtin_fmaf(sLam[r], qv, kv);
+        }
+      }
+    }
+    // the product pass's results and the erase gate at my (row, channel)
+    // pairs, requested before the products
+    float dEb[4][4], dQg[4][4], dKt[4][4], bI[4][4];
+#pragma unroll
+    for (int C = 0; C < 4; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * g + r, cg = ps * KC + 16 * C + l16;
+        const size_t at = (ch * CH + i) * DK + cg;
+        dEb[C][r] = ws.Eb[at];
+        dQg[C][r] = ws.Qg[at];
+        dKt[C][r] = ws.Kt[at];
+        const int t = t0 + i;
+        bI[C][r] = (erase == 1 && t < T) ? p.f.b[(seq0 + (size_t)t * H) * DK + cg] : 0.f;
+      }
+    __syncthreads();
+    // ---- the four products: row block w, column blocks C of the pass
+    f32x4 aP[4], aPq[4], aRm[4], aRq[4];
+#pragma unroll
+    for (int C = 0; C < 4; ++C) aP[C] = aPq[C] = aRm[C] = aRq[C] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J <= w) {  // P, Pq: j < i
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sD1 + (16 * w + l16) * TP + 16 * J + 4 * g);
+        const f32x4 a2 = *reinterpret_cast<const f32x4*>(sD2 + (16 * w + l16) * TP + 16 * J + 4 * g);
+#pragma unroll
+        for (int C = 0; C < 4; ++C) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(sKT + (16 * C + l16) * TP + 16 * J + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            aP[C] = mfma_f32(a1[r], b[r], aP[C]);
+            aPq[C] = mfma_f32(a2[r], b[r], aPq[C]);
+          }
+        }
+      }
+      if (J >= w) {  // Rm, Rq: i2 > i
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sD1T + (16 * w + l16) * TP + 16 * J + 4 * g);
+        const f32x4 a2 = *reinterpret_cast<const f32x4*>(sD2T + (16 * w + l16) * TP + 16 * J + 4 * g);
+#pragma unroll
+        for (int C = 0; C < 4; ++C) {
+          const f32x4 be = *reinterpret_cast<const f32x4*>(sET + (16 * C + l16) * TP + 16 * J + 4 * g);
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(sQT + (16 * C + l16) * TP + 16 * J + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            aRm[C] = mfma_f32(a1[r], be[r], aRm[C]);
+            aRq[C] = mfma_f32(a2[r], bq[r], aRq[C]);
+          }
+        }
+      }
+    }
+    // ---- rows: the gradients of q, k and e, the erase gate, the row sums
+    float gam[4], tl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float gi = sGt[16 * w + 4 * g + r];
+      gam[r] = fexp(gi);
+      tl[r] = fexp(GC - gi);
+    }
+    float sb[4] = {0.f, 0.f, 0.f, 0.f}, sl[4] = {0.f, 0.f, 0.f, 0.f};
+    float sg[4] = {0.f, 0.f, 0.f, 0.f}, sx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int C = 0; C < 4; ++C) {
+      const int c = 16 * C + l16, cg = ps * KC + c;
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(sKT + c * TP + 16 * w + 4 * g);
+      const f32x4 ev = *reinterpret_cast<const f32x4*>(sET + c * TP + 16 * w + 4 * g);
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(sQT + c * TP + 16 * w + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * g + r;
+        const float ki = kv[r], ei = ev[r], qi = qv[r];
+        const float P = aP[C][r], Pq = aPq[C][r], Rm = aRm[C][r], Rq = aRq[C][r];
+        const float diag = sDiag[i];
+        const float de = __builtin_fmaf(gam[r], dEb[C][r], P);
+        float dqd = __builtin_fmaf(gam[r], dQg[C][r], __builtin_fmaf(diag, ki, Pq));
+        float dkd = tl[r] * dKt[C][r] + Rm + __builtin_fmaf(diag, qi, Rq);
+        // (the diagonal of A_qk stays out of dG: its two terms cancel exactly)
+        sg[r] += ei * gam[r] * dEb[C][r] + qi * gam[r] * dQg[C][r] + ei * P + qi * Pq - ki * (Rm + Rq);
+        sx[r] += ki * tl[r] * dKt[C][r];  // K_tail_i dK_tail_i
+        const int t = t0 + i;
+        const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+        if (erase == 1) {
+          if (t < T) p.db[tok * DK + cg] = de * ki;
+          dkd = __builtin_fmaf(bI[C][r], de, dkd);
+        } else {
+          const float bt = sBeta[i], lt = sLam[i];
+          sb[r] += de * __builtin_fmaf(lt, qi, ki);
+          dkd = __builtin_fmaf(bt, de, dkd);
+          if (qmix) {
+            dqd = __builtin_fmaf(bt * lt, de, dqd);
+            sl[r] += bt * de * qi;
+          }
+        }
+        if (t < T) {
+          p.dq[tok * DK + cg] = dqd;
+          p.dk[tok * DK + cg] = dkd;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rb = row16(sb[r]), rl = row16(sl[r]), rg = row16(sg[r]), rx = row16(sx[r]);
+      if (l16 == 0) {
+        const int i = 16 * w + 4 * g + r;
+        sRb[i][ps] = rb;
+        sRl[i][ps] = rl;
+        sRG[i] += rg;  // (one writer per row; the passes are ordered by barriers)
+        sRX[i] += rx;
+      }
+    }
+  }
+  // dg_t = sum_{r>=t} RG_r + sum_{j<t} RX_j + gamma_C sum_c sC[c] (the
+  // per-channel form summed over the channels), by wave prefix sums
+  if (decay == 1) {
+    __syncthreads();
+    if (tid < CH) {
+      float sc = 0.f;
+      for (int c2 = tid; c2 < DK; c2 += CH) sc += ws.gC[ch * DK + c2];
+      const float base = fexp(sGt[CH - 1]) * wave_total(sc);
+      const float rg = sRG[tid], rx = sRX[tid];
+      const float ig = wave_incl_scan(rg), ix = wave_incl_scan(rx);
+      sDg[tid] = (lane_value(ig, 63) - ig + rg) + (ix - rx) + base;
+    }
+  }
+  key_tail<IO, DK, DV, NPASS>(p, ch, t0, seq0, tid, sBeta, sRz, sDg, sRb, sRl);
 }
 
 // ---- a per-head lambda: the sum of its per-token gradients ------------------
