@@ -70,6 +70,30 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
   }
 }
 
+// 4 x 4 transpose across the lanes of a quad: lane j of the quad holds row j
+// of a block in x; afterwards it holds column j.  Two exchange rounds with
+// the partners j ^ 1 and j ^ 2 (DPP quad permutations); element k is taken
+// from the partner where bit 0 (round 1) or bit 1 (round 2) of k ^ j is set.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
+  auto from = [](float v, auto ctrl) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                              0xf, 0xf, true));
+  };
+  f32x4 y;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float o = from(x[k ^ 1], IC<0xB1>{});
+    y[k] = ((k ^ j) & 1) ? o : x[k];
+  }
+  f32x4 z;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float o = from(y[k ^ 2], IC<0x4E>{});
+    z[k] = ((k ^ j) & 2) ? o : y[k];
+  }
+  return z;
+}
+
 // ---- pass A: the reverse state recurrence, on the matrix cores ----------------
 // Every product on v_mfma_f32_16x16x4_f32: one workgroup of four waves per (batch, head, 64-column slice), wave w
 // owning columns 16 w .. + 15 and dS of those columns in accumulators
@@ -132,18 +156,27 @@ void bwd_state_mfma_kernel(BwdParams p) {
     float gc;
     float o[16];  // dO rows 16 I + 4 g + r of this lane's column
   };
+  // E_bar, Q_gamma, A, A_qk are staged transposed: lane (k, j) = (lane / 4,
+  // lane % 4) of wave w loads token 4 t4 + j, channels 4 k .. + 3 of a block
+  // of 4 tokens x 64 channels (rows stay 256-byte runs), the quad transposes
+  // it, and the lane writes channel 4 k + j, tokens 4 t4 .. + 3 as one
+  // 16-byte LDS write (64 consecutive channel rows per wave: no bank
+  // conflicts).  K_tail stays row-major.
+  const int qj = lane & 3, qk = lane >> 2;
   auto load = [&](int n, Rec& R) __attribute__((always_inline)) {
     const size_t ch = (size_t)bh * N + n;
 #pragma unroll
     for (int u = 0; u < NQ_E; ++u) {
-      const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
+      const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + qj, c = 64 * (blk % (DK / 64)) + 4 * qk;
+      const size_t o = ch * CH * DK + (size_t)t * DK + c;
       R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
       R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
-      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + o);
+      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + 4 * (tid + NTHR * u));
     }
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
-      const size_t o = ch * CH * CH + 4 * (tid + NTHR * u);
+      const int t = 4 * (wave + 4 * u) + qj, c = 4 * qk;
+      const size_t o = ch * CH * CH + (size_t)t * CH + c;
       R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
       R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
     }
@@ -160,20 +193,15 @@ void bwd_state_mfma_kernel(BwdParams p) {
     for (int u = 0; u < NQ_E; ++u) {
       const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
       *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sQgT[(c + i) * SA + t] = R.qg[u][i];
-        sEbT[(c + i) * SA + t] = R.eb[u][i];
-      }
+      const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + 4 * qk + qj;
+      *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(R.qg[u], qj);
+      *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(R.eb[u], qj);
     }
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
-      const int e = 4 * (tid + NTHR * u), t = e / CH, c = e - t * CH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sAT[(c + i) * SA + t] = R.a[u][i];
-        sAqT[(c + i) * SA + t] = R.aq[u][i];
-      }
+      const int t4 = wave + 4 * u, cq = 4 * qk + qj;
+      *reinterpret_cast<f32x4*>(sAT + cq * SA + 4 * t4) = quad_transpose(R.a[u], qj);
+      *reinterpret_cast<f32x4*>(sAqT + cq * SA + 4 * t4) = quad_transpose(R.aq[u], qj);
     }
     if (tid < DK) sGC[tid] = R.gc;
   };
