@@ -70,30 +70,6 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
   }
 }
 
-// 4 x 4 transpose across the lanes of a quad: lane j of the quad holds row j
-// of a block in x; afterwards it holds column j.  Two exchange rounds with
-// the partners j ^ 1 and j ^ 2 (DPP quad permutations); element k is taken
-// from the partner where bit 0 (round 1) or bit 1 (round 2) of k ^ j is set.
-__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
-  auto from = [](float v, auto ctrl) __attribute__((always_inline)) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
-                                                              0xf, 0xf, true));
-  };
-  f32x4 y;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float o = from(x[k ^ 1], IC<0xB1>{});
-    y[k] = ((k ^ j) & 1) ? o : x[k];
-  }
-  f32x4 z;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float o = from(y[k ^ 2], IC<0x4E>{});
-    z[k] = ((k ^ j) & 2) ? o : y[k];
-  }
-  return z;
-}
-
 // ---- pass A: the reverse state recurrence, on the matrix cores ----------------
 // Every product on v_mfma_f32_16x16x4_f32: one workgroup of four waves per (batch, head, 64-column slice), wave w
 // owning columns 16 w .. + 15 and dS of those columns in accumulators

@@ -714,7 +714,11 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
       R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
       R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
-      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + o);
+      // K_tail is staged transposed: lane (k, j) = (lane / 4, lane % 4) of
+      // wave w takes token 4 t4 + j, channels 4 k .. + 3 of a block of 4
+      // tokens x 64 channels; the quad transposes it in stage()
+      const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + (lane & 3), c = 64 * (blk % (DK / 64)) + 4 * (lane >> 2);
+      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + (size_t)t * DK + c);
     }
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
@@ -739,8 +743,10 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
       *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
       *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sKtT[(c + i) * SA + t] = R.kt[u][i];
+      // channel 4 k + j of the block, tokens 4 t4 .. + 3: one 16-byte write
+      // (the wave's 64 channel rows fall in distinct banks)
+      const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + lane;
+      *reinterpret_cast<f32x4*>(sKtT + cq * SA + 4 * t4) = quad_transpose(R.kt[u], lane & 3);
     }
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
