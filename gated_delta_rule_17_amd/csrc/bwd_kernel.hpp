@@ -743,30 +743,38 @@ void bwd_key_scalar_kernel(BwdParams p) {
 
   for (int ps = 0; ps < NPASS; ++ps) {
     __syncthreads();  // the previous pass's columns are no longer read
-    // ---- this pass's columns of the chunk's rows, transposed (zero past T)
+    // ---- this pass's columns of the chunk's rows, transposed (zero past T):
+    // lane (k, j) = (lane / 4, lane % 4) of wave w takes token 4 b + j
+    // (b = w + 4 u), channels 4 k .. + 3 of the pass; the quad transposes
+    // its block, and the lane writes channel 4 k + j = lane, tokens 4 b ..
+    // + 3 as one 16-byte LDS write (64 channel rows per wave: no bank
+    // conflicts)
     {
-      constexpr int QPR = KC / 4, NQ = CH * QPR / NTHR;
+      constexpr int NQ = CH * KC / 4 / NTHR;
+      const int qj = lane & 3, cl = 4 * (lane >> 2);
       f32x4 rk[NQ], rq[NQ], rb[NQ];
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const int e = tid + NTHR * u, r = e / QPR, c4 = ps * KC + (e - r * QPR) * 4;
+        const int r = 4 * (w + 4 * u) + qj;
         const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
-        rk[u] = ldf4(kg + tok * DK + c4);
-        rq[u] = ldf4(qg + tok * DK + c4);
-        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + c4);
+        rk[u] = ldf4(kg + tok * DK + ps * KC + cl);
+        rq[u] = ldf4(qg + tok * DK + ps * KC + cl);
+        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + ps * KC + cl);
       }
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const int e = tid + NTHR * u, r = e / QPR, cl = (e - r * QPR) * 4;
+        const int b4 = w + 4 * u, r = 4 * b4 + qj;
         const bool ok = t0 + r < T;
+        f32x4 kv, qv, ev;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float kv = ok ? rk[u][i] : 0.f, qv = ok ? rq[u][i] : 0.f;
-          sKT[(cl + i) * TP + r] = kv;
-          sQT[(cl + i) * TP + r] = qv;
-          sET[(cl + i) * TP + r] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv
-                                              : sBeta[r] * __builtin_fmaf(sLam[r], qv, kv);
+          kv[i] = ok ? rk[u][i] : 0.f;
+          qv[i] = ok ? rq[u][i] : 0.f;
+          ev[i] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv[i] : sBeta[r] * __builtin_fmaf(sLam[r], qv[i], kv[i]);
         }
+        *reinterpret_cast<f32x4*>(sKT + lane * TP + 4 * b4) = quad_transpose(kv, qj);
+        *reinterpret_cast<f32x4*>(sQT + lane * TP + 4 * b4) = quad_transpose(qv, qj);
+        *reinterpret_cast<f32x4*>(sET + lane * TP + 4 * b4) = quad_transpose(ev, qj);
       }
     }
     // the product pass's results and the erase gate at my (row, channel)
