@@ -1,5 +1,7 @@
 // Instances and launch sequence of the backward (bwd_kernel.hpp): io {fp32,
 // bf16} x dk {64, 128} x dv {64, 128}.
+#include <type_traits>
+
 #include "bwd_kernel.hpp"
 #include "launch.hpp"
 #include "plain_split_kernel.hpp"
@@ -22,13 +24,23 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
   // each slice writing its entering states and W
   // (the recurrence on the matrix cores, slices of 64 columns; the backward
   // takes no per-value-channel beta)
+  // under a scalar decay (or none) with bf16 I/O the recurrence and the
+  // state pass form E_bar, Q_gamma, K_tail and gamma_C from the inputs (half
+  // the bytes of the fp32 records): the prep does not write them
+  const bool sd = p.f.decay != 2 && std::is_same<IO, bf16>::value;
   if (N > 0) {
-    hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws);
+    hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws, sd ? 0 : 1);
     ChunkParams f64 = p.f;
     f64.nslices = DV / 64;
-    hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64, p.ws);
+    if (sd)
+      hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, true>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64,
+                         p.ws);
+    else
+      hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, false>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64,
+                         p.ws);
   }
-  hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK>), dim3(BH * (DV / 64)), dim3(NTHR), 0, s, p);
+  if (sd) hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, true>), dim3(BH * (DV / 64)), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, false>), dim3(BH * (DV / 64)), dim3(NTHR), 0, s, p);
   if (N > 0) {
     hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
     // the key pass: on the matrix cores under a scalar decay (or none), per

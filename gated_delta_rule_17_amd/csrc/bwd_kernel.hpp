@@ -95,7 +95,9 @@ struct BwdAMLay {
   static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
 };
 
-template <class IO, int DK>
+// SD: a scalar decay or none; E_bar, Q_gamma, K_tail and gamma_C are formed
+// from the inputs while staging (sd_rows) rather than read from the workspace.
+template <class IO, int DK, bool SD = false>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_state_mfma_kernel(BwdParams p) {
   using L = BwdAMLay<DK>;
@@ -127,11 +129,16 @@ void bwd_state_mfma_kernel(BwdParams p) {
     for (int r = 0; r < 4; ++r)
       dS[b][r] = p.d_st ? p.d_st[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] : 0.f;
 
+  // (SD: eb, qg hold the raw k, q and bq the per-channel erase gate, in the
+  // quad layout, and sd this lane's token scalars)
   struct Rec {
-    f32x4 eb[NQ_E], qg[NQ_E], kt[NQ_E], a[NQ_A], aq[NQ_A];
+    f32x4 eb[NQ_E], qg[NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
     float gc;
+    SdLane sd;
     float o[16];  // dO rows 16 I + 4 g + r of this lane's column
   };
+  const IO* kin = reinterpret_cast<const IO*>(p.f.k);
+  const IO* qin = reinterpret_cast<const IO*>(p.f.q);
   // E_bar, Q_gamma, A, A_qk are staged transposed: lane (k, j) = (lane / 4,
   // lane % 4) of wave w loads token 4 t4 + j, channels 4 k .. + 3 of a block
   // of 4 tokens x 64 channels (rows stay 256-byte runs), the quad transposes
@@ -144,11 +151,19 @@ void bwd_state_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < NQ_E; ++u) {
       const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + qj, c = 64 * (blk % (DK / 64)) + 4 * qk;
-      const size_t o = ch * CH * DK + (size_t)t * DK + c;
-      R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
-      R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
-      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + 4 * (tid + NTHR * u));
+      if constexpr (SD) {
+        const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
+        R.eb[u] = ldf4(kin + tokq * DK + c);
+        R.qg[u] = ldf4(qin + tokq * DK + c);
+        if (p.f.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.f.b + tokq * DK + c);
+      } else {
+        const size_t o = ch * CH * DK + (size_t)t * DK + c;
+        R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
+        R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
+        R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + 4 * (tid + NTHR * u));
+      }
     }
+    if constexpr (SD) R.sd = sd_lane_load(p.f, seq0, n * CH, hh, lane);
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
       const int t = 4 * (wave + 4 * u) + qj, c = 4 * qk;
@@ -156,7 +171,7 @@ void bwd_state_mfma_kernel(BwdParams p) {
       R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
       R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
     }
-    R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
+    if constexpr (!SD) R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int t = n * CH + 16 * (k >> 2) + 4 * g + (k & 3);
@@ -164,14 +179,28 @@ void bwd_state_mfma_kernel(BwdParams p) {
       R.o[k] = t < T ? x : 0.f;
     }
   };
-  auto stage = [&](const Rec& R) __attribute__((always_inline)) {
+  auto stage = [&](const Rec& R, int t0) __attribute__((always_inline)) {
+    float G = 0.f, GC = 0.f;
+    if constexpr (SD) {
+      G = sd_scan(p.f, R.sd, t0, lane);
+      GC = lane_value(G, 63);
+    }
 #pragma unroll
     for (int u = 0; u < NQ_E; ++u) {
-      const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
-      *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
       const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + 4 * qk + qj;
-      *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(R.qg[u], qj);
-      *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(R.eb[u], qj);
+      f32x4 eb = R.eb[u], qgm = R.qg[u];
+      if constexpr (SD) {
+        // token 4 t4 + j, channels 4 k .. + 3: E_bar and Q_gamma for the
+        // transpose, K_tail as a row piece
+        const int tq = 4 * t4 + qj, cq4 = 64 * (blk % (DK / 64)) + 4 * qk;
+        sd_rows(p.f, G, R.sd, tq, t0, R.eb[u], R.qg[u], R.bq[u], eb, qgm);
+        *reinterpret_cast<f32x4*>(sKt + tq * SE + cq4) = sd_ktail(p.f, G, GC, tq, t0, R.eb[u]);
+      } else {
+        const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
+        *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
+      }
+      *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(qgm, qj);
+      *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(eb, qj);
     }
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
@@ -179,7 +208,7 @@ void bwd_state_mfma_kernel(BwdParams p) {
       *reinterpret_cast<f32x4*>(sAT + cq * SA + 4 * t4) = quad_transpose(R.a[u], qj);
       *reinterpret_cast<f32x4*>(sAqT + cq * SA + 4 * t4) = quad_transpose(R.aq[u], qj);
     }
-    if (tid < DK) sGC[tid] = R.gc;
+    if (tid < DK) sGC[tid] = SD ? fexp(GC) : R.gc;
   };
 
   Rec R;
@@ -187,7 +216,7 @@ void bwd_state_mfma_kernel(BwdParams p) {
   for (int n = N - 1; n >= 0; --n) {
     const size_t ch = (size_t)bh * N + n;
     __syncthreads();  // every read of the later chunk's LDS records is done
-    stage(R);
+    stage(R, n * CH);
     float dO[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) dO[k] = R.o[k];

@@ -1,5 +1,7 @@
 // Instances of the plain fp32 chunk kernel and of its two-pass form: io
 // {fp32, bf16} x dk {64, 128}, value slices of 16 columns.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "plain_kernel.hpp"
 #include "plain_split_kernel.hpp"
@@ -42,13 +44,20 @@ template <class IO, int DK>
 hipError_t plain_split_sequence(const ChunkParams& p, const BwdWs& ws, int dvs, int grid, int prep_grid,
                                 hipStream_t s) {
   if (dvs == 64 && p.erase == 2) return hipErrorInvalidValue;  // the substitution needs 16-column slices
-  hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws);
+  // under a scalar decay (or none) with bf16 I/O the matrix-core recurrence
+  // forms the factor rows from the inputs (half the bytes of the fp32
+  // records), so the prep does not write them; with fp32 I/O the inputs
+  // weigh as much as the records and the records are read
+  const bool sd = dvs == 64 && p.decay != 2 && std::is_same<IO, bf16>::value;
+  hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws, sd ? 0 : 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dvs == 64)
-    hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
-  else
+  if (dvs == 64) {
+    if (sd) hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false, true>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+    else hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+  } else {
     hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+  }
   return hipGetLastError();
 }
 

@@ -62,8 +62,11 @@ struct PlainPrepLay {
   static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
 };
 
+// factors = 0: the factor rows E_bar, Q_gamma, K_tail and gamma_C are not
+// written (the passes that read them form them from the inputs: a scalar
+// decay or none, see sd_rows).
 template <class IO, int DK>
-__global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs ws) {
+__global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
   using L = PlainPrepLay;
   constexpr int HP = L::HP, CHH = L::CHH, NH = DK / CHH;
   static_assert(DK % CHH == 0, "whole halves");
@@ -192,9 +195,11 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
         kt[i] = kv[i] * fexp(GC[i] - G[u][i]);
       }
       const size_t ro = (ch * CH + r) * DK + cb + c4;
-      *reinterpret_cast<f32x4*>(ws.Eb + ro) = eb;
-      *reinterpret_cast<f32x4*>(ws.Qg + ro) = qgm;
-      *reinterpret_cast<f32x4*>(ws.Kt + ro) = kt;
+      if (factors) {
+        *reinterpret_cast<f32x4*>(ws.Eb + ro) = eb;
+        *reinterpret_cast<f32x4*>(ws.Qg + ro) = qgm;
+        *reinterpret_cast<f32x4*>(ws.Kt + ro) = kt;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sK[r * HP + c4 + i] = kv[i];
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs w
         sG[r * HP + c4 + i] = G[u][i];
       }
     }
-    if (rg == 0) {
+    if (rg == 0 && factors) {
       *reinterpret_cast<f32x4*>(ws.gC + ch * DK + cb + c4) =
           f32x4{fexp(GC[0]), fexp(GC[1]), fexp(GC[2]), fexp(GC[3])};
     }
@@ -657,11 +662,60 @@ constexpr int plain_mrec_lds_bytes() {
   return PlainMrecLay<DK>::TOTAL * 4;
 }
 
+// Under a scalar decay (or none) the factor rows of a chunk are row scalings
+// of the inputs, so the passes that read them form them while staging,
+// instead of reading 96 KB per chunk (dk = 128) back from the workspace:
+//   E_bar_t = gamma_t e_t,  Q_gamma_t = gamma_t q_t,  K_tail_t = (gamma_C / gamma_t) k_t,
+//   e_t = beta_t (k_t + lam_t q_t), or b_t (.) k_t,  gamma_t = exp(G_t),
+// G the chunk's prefix sum of the log-decay (zero past T), with the prep's
+// operations (so these are the rows it would have written).  SdLane: the
+// log-decay, beta and lambda of token t0 + lane of the chunk.
+struct SdLane {
+  float g, beta, lam;
+};
+__device__ __forceinline__ SdLane sd_lane_load(const ChunkParams& p, size_t seq0, int t0, int hh, int lane) {
+  const size_t tok = seq0 + (size_t)min(t0 + lane, p.T - 1) * p.H;
+  return SdLane{p.decay == 1 ? p.g[tok] : 0.f, p.erase == 0 ? p.beta[tok] : 0.f,
+                p.qmix == 2 ? p.lam[tok] : (p.qmix ? p.lam[hh] : 0.f)};
+}
+// G_{t0 + lane} in lane lane (every lane of the wave active)
+__device__ __forceinline__ float sd_scan(const ChunkParams& p, const SdLane& s, int t0, int lane) {
+  return wave_incl_scan((p.decay == 1 && t0 + lane < p.T) ? s.g : 0.f);
+}
+// E_bar and Q_gamma of four channels of chunk token t from the raw k, q (and
+// b) of those channels (every lane active: the token's scalars come by
+// lane shuffles)
+__device__ __forceinline__ void sd_rows(const ChunkParams& p, float G, const SdLane& s, int t, int t0, f32x4 k,
+                                        f32x4 q, f32x4 b, f32x4& eb, f32x4& qg) {
+  const float Gt = __shfl(G, t), bt = __shfl(s.beta, t), lt = __shfl(s.lam, t);
+  const bool ok = t0 + t < p.T;
+  const float gam = fexp(Gt);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float kv = ok ? k[i] : 0.f, qv = ok ? q[i] : 0.f;
+    float ev = p.erase == 1 ? b[i] * kv : bt * __builtin_fmaf(lt, qv, kv);
+    if (!ok) ev = 0.f;
+    eb[i] = ev * gam;
+    qg[i] = qv * gam;
+  }
+}
+// K_tail of four channels of chunk token t
+__device__ __forceinline__ f32x4 sd_ktail(const ChunkParams& p, float G, float GC, int t, int t0, f32x4 k) {
+  const float Gt = __shfl(G, t);
+  const bool ok = t0 + t < p.T;
+  f32x4 kt;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kt[i] = (ok ? k[i] : 0.f) * fexp(GC - Gt);
+  return kt;
+}
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <class IO, int DK, bool REC = false>
+// SD: a scalar decay or none; the factor rows are formed from the inputs
+// (sd_rows) rather than read from the workspace.
+template <class IO, int DK, bool REC = false, bool SD = false>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
   using L = PlainMrecLay<DK>;
@@ -701,32 +755,47 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
     for (int r = 0; r < 4; ++r)
       S[b][r] = p.state_in ? p.state_in[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] : 0.f;
 
-  // registers of a chunk's records and of this lane's z inputs
+  // registers of a chunk's records and of this lane's z inputs (SD: eb, qg
+  // hold the raw k, q and bq the per-channel erase gate, all in the quad
+  // layout below, and sd this lane's token scalars)
   struct Rec {
-    f32x4 eb[NQ_E], qg[NQ_E], kt[NQ_E], a[NQ_A], aq[NQ_A];
+    f32x4 eb[NQ_E], qg[NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
     float gc;
+    SdLane sd;
     float v[16], gt[16];  // rows 16 I + 4 g + r of this lane's column
   };
+  const IO* kin = reinterpret_cast<const IO*>(p.k);
+  const IO* qin = reinterpret_cast<const IO*>(p.q);
   auto load = [&](int n, Rec& R) __attribute__((always_inline)) {
     const size_t ch = (size_t)bh * N + n;
 #pragma unroll
     for (int u = 0; u < NQ_E; ++u) {
-      const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
-      R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
-      R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
       // K_tail is staged transposed: lane (k, j) = (lane / 4, lane % 4) of
       // wave w takes token 4 t4 + j, channels 4 k .. + 3 of a block of 4
       // tokens x 64 channels; the quad transposes it in stage()
       const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + (lane & 3), c = 64 * (blk % (DK / 64)) + 4 * (lane >> 2);
-      R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + (size_t)t * DK + c);
+      if constexpr (SD) {
+        // (k, q, b of the same token and channels serve E_bar and Q_gamma
+        // as row pieces and K_tail through the transpose)
+        const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
+        R.eb[u] = ldf4(kin + tokq * DK + c);
+        R.qg[u] = ldf4(qin + tokq * DK + c);
+        if (p.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.b + tokq * DK + c);
+      } else {
+        const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
+        R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
+        R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
+        R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + (size_t)t * DK + c);
+      }
     }
+    if constexpr (SD) R.sd = sd_lane_load(p, seq0, n * CH, hh, lane);
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
       const size_t o = ch * CH * CH + 4 * (tid + NTHR * u);
       R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
       if constexpr (!REC) R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
     }
-    R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
+    if constexpr (!SD) R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -737,16 +806,34 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
         R.gt[k] = write == 1 ? p.w[tok * DV + col] : p.beta[tok];
       }
   };
-  auto stage = [&](const Rec& R) __attribute__((always_inline)) {
+  auto stage = [&](const Rec& R, int t0) __attribute__((always_inline)) {
+    float G = 0.f, GC = 0.f;
+    if constexpr (SD) {
+      G = sd_scan(p, R.sd, t0, lane);
+      GC = lane_value(G, 63);
+    }
 #pragma unroll
     for (int u = 0; u < NQ_E; ++u) {
-      const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
-      *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
-      *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
+      const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + lane;
+      f32x4 kt;
+      if constexpr (SD) {
+        // token 4 t4 + j, channels 4 k .. + 3 of the block: a row piece of
+        // E_bar and Q_gamma, and K_tail for the transpose
+        const int tq = 4 * t4 + (lane & 3), cq4 = 64 * (blk % (DK / 64)) + 4 * (lane >> 2);
+        f32x4 eb, qgm;
+        sd_rows(p, G, R.sd, tq, t0, R.eb[u], R.qg[u], R.bq[u], eb, qgm);
+        kt = sd_ktail(p, G, GC, tq, t0, R.eb[u]);
+        *reinterpret_cast<f32x4*>(sEb + tq * SE + cq4) = eb;
+        *reinterpret_cast<f32x4*>(sQg + tq * SE + cq4) = qgm;
+      } else {
+        const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
+        kt = R.kt[u];
+        *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
+        *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
+      }
       // channel 4 k + j of the block, tokens 4 t4 .. + 3: one 16-byte write
       // (the wave's 64 channel rows fall in distinct banks)
-      const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + lane;
-      *reinterpret_cast<f32x4*>(sKtT + cq * SA + 4 * t4) = quad_transpose(R.kt[u], lane & 3);
+      *reinterpret_cast<f32x4*>(sKtT + cq * SA + 4 * t4) = quad_transpose(kt, lane & 3);
     }
 #pragma unroll
     for (int u = 0; u < NQ_A; ++u) {
@@ -754,7 +841,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       *reinterpret_cast<f32x4*>(sA + t * SA + c) = R.a[u];
       if constexpr (!REC) *reinterpret_cast<f32x4*>(sAq + t * SA + c) = R.aq[u];
     }
-    if (tid < DK) sGC[tid] = R.gc;
+    if (tid < DK) sGC[tid] = SD ? fexp(GC) : R.gc;
   };
 
   Rec R;
@@ -763,7 +850,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
     const int t0 = n * CH;
     const size_t ch = (size_t)bh * N + n;
     __syncthreads();  // every read of the previous chunk's LDS records is done
-    stage(R);
+    stage(R, t0);
     float z[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {

@@ -36,6 +36,10 @@ CASES = {
     "kda_f32_dk128_dv64": config(F, variant="kda", B=1, H=2, T=64, dk=128, dv=64, decay_shift=-4.0),
     "gdn2_extreme": config(G2, B=1, H=2, T=100, g_const=-20.0),
     "gdn_erase_ch_f32": config(F, B=1, H=2, T=80, erase="channel", decay_shift=-3.0),
+    # bf16 under a scalar decay: the record recurrence and the state pass form
+    # the factor rows from the inputs (per-channel erase gate; lambda per token)
+    "gdn_erase_ch_bf16": config(H, B=1, H=2, T=80, erase="channel", decay_shift=-3.0),
+    "qdelta_lam_t_bf16": config(Q, B=1, H=2, T=90, lam_t=True, decay_shift=-3.0),
     "kda_write_ch_bf16": config(K, B=1, H=2, T=96, write="channel", decay_shift=-3.0),
     "gdn2_T1": config(G2, B=2, H=2, T=1, state_std=0.1),
 }

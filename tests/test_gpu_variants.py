@@ -208,6 +208,8 @@ def test_epilogue_fused(entry, io):
     ("gdn_f32_d128", config(F, B=2, H=2, T=300, d=128, decay_shift=-3.0, state_std=0.1)),
     ("kda_f32_d128_dv64", config(F, variant="kda", B=1, H=3, T=200, dk=128, dv=64, decay_shift=-4.0)),
     ("kda_bf16_lam_t", config(K, B=1, H=2, T=150, qmix=True, lam_t=True, decay_shift=-4.0)),
+    # bf16 under a scalar decay: the matrix-core recurrence forms the factor rows
+    ("qdelta_bf16_lam_t", config(Q, B=1, H=2, T=150, lam_t=True, decay_shift=-4.0)),
     ("gdn2_bf16_value_beta", config(G2, B=1, H=2, T=150, value_beta=True, decay_shift=-4.0)),
 ])
 def test_plain_two_pass_recurrences(name, cfg):
