@@ -231,20 +231,23 @@ void bwd_state_mfma_kernel(BwdParams p) {
     f32x4 dW[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+      // (the K_tail fragments of the row block requested together; the two
+      // products in two accumulators)
+      f32x4 ak[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sKt + (16 * I + l16) * SE + 16 * b + 4 * g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w = mfma_f32(a[r], dS[b][r], w);
-      }
+      for (int b = 0; b < NB; ++b) ak[b] = *reinterpret_cast<const f32x4*>(sKt + (16 * I + l16) * SE + 16 * b + 4 * g);
+      f32x4 w = {0.f, 0.f, 0.f, 0.f}, w2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int J = I; J < 4; ++J) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(sAqT + (16 * I + l16) * SA + 16 * J + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w = mfma_f32(a[r], dO[4 * J + r], w);
+        for (int r = 0; r < 4; ++r) w2 = mfma_f32(a[r], dO[4 * J + r], w2);
       }
-      dW[I] = w;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w = mfma_f32(ak[b][r], dS[b][r], w);
+      dW[I] = w + w2;
     }
     // ---- dR = A^T dW, block rows from the first (each reads dW blocks J >= I) ----
 #pragma unroll
@@ -261,21 +264,30 @@ void bwd_state_mfma_kernel(BwdParams p) {
       for (int r = 0; r < 4; ++r) ws.dR[(ch * CH + 16 * I + 4 * g + r) * DV + col] = r4[r];
     }
     // ---- dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR -----------------------
+    // (dR negated once; each block's eight fragments requested together; the
+    // two products in two accumulators, so that consecutive MFMAs do not
+    // wait on each other)
+    f32x4 ndR[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) ndR[J] = -dW[J];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + 16 * b + 4 * g);
-      f32x4 s = dS[b] * gc;
+      f32x4 aq[4], ae[4];
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        const f32x4 aq = *reinterpret_cast<const f32x4*>(sQgT + (16 * b + l16) * SA + 16 * J + 4 * g);
-        const f32x4 ae = *reinterpret_cast<const f32x4*>(sEbT + (16 * b + l16) * SA + 16 * J + 4 * g);
+        aq[J] = *reinterpret_cast<const f32x4*>(sQgT + (16 * b + l16) * SA + 16 * J + 4 * g);
+        ae[J] = *reinterpret_cast<const f32x4*>(sEbT + (16 * b + l16) * SA + 16 * J + 4 * g);
+      }
+      f32x4 sq = dS[b] * gc, se = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s = mfma_f32(aq[r], dO[4 * J + r], s);
-          s = mfma_f32(-ae[r], dW[J][r], s);
+          sq = mfma_f32(aq[J][r], dO[4 * J + r], sq);
+          se = mfma_f32(ae[J][r], ndR[J][r], se);
         }
-      }
-      dS[b] = s;
+      dS[b] = sq + se;
     }
   }
   if (p.dstate) {
