@@ -132,10 +132,11 @@ void bwd_state_mfma_kernel(BwdParams p) {
   // (SD: eb, qg hold the raw k, q and bq the per-channel erase gate, in the
   // quad layout, and sd this lane's token scalars)
   struct Rec {
-    f32x4 eb[NQ_E], qg[NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
+    typename Raw<IO>::v4 kr[SD ? NQ_E : 1], qr[SD ? NQ_E : 1];
+    f32x4 eb[SD ? 1 : NQ_E], qg[SD ? 1 : NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
     float gc;
     SdLane sd;
-    float o[16];  // dO rows 16 I + 4 g + r of this lane's column
+    IO o[16];  // dO rows 16 I + 4 g + r of this lane's column
   };
   const IO* kin = reinterpret_cast<const IO*>(p.f.k);
   const IO* qin = reinterpret_cast<const IO*>(p.f.q);
@@ -153,8 +154,8 @@ void bwd_state_mfma_kernel(BwdParams p) {
       const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + qj, c = 64 * (blk % (DK / 64)) + 4 * qk;
       if constexpr (SD) {
         const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
-        R.eb[u] = ldf4(kin + tokq * DK + c);
-        R.qg[u] = ldf4(qin + tokq * DK + c);
+        R.kr[u] = ldraw4(kin + tokq * DK + c);
+        R.qr[u] = ldraw4(qin + tokq * DK + c);
         if (p.f.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.f.b + tokq * DK + c);
       } else {
         const size_t o = ch * CH * DK + (size_t)t * DK + c;
@@ -175,8 +176,7 @@ void bwd_state_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int t = n * CH + 16 * (k >> 2) + 4 * g + (k & 3);
-      const float x = ldf(dog + (seq0 + (size_t)min(t, T - 1) * H) * DV + col);
-      R.o[k] = t < T ? x : 0.f;
+      R.o[k] = dog[(seq0 + (size_t)min(t, T - 1) * H) * DV + col];
     }
   };
   auto stage = [&](const Rec& R, int t0) __attribute__((always_inline)) {
@@ -188,16 +188,19 @@ void bwd_state_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < NQ_E; ++u) {
       const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + 4 * qk + qj;
-      f32x4 eb = R.eb[u], qgm = R.qg[u];
+      f32x4 eb, qgm;
       if constexpr (SD) {
         // token 4 t4 + j, channels 4 k .. + 3: E_bar and Q_gamma for the
         // transpose, K_tail as a row piece
         const int tq = 4 * t4 + qj, cq4 = 64 * (blk % (DK / 64)) + 4 * qk;
-        sd_rows(p.f, G, R.sd, tq, t0, R.eb[u], R.qg[u], R.bq[u], eb, qgm);
-        *reinterpret_cast<f32x4*>(sKt + tq * SE + cq4) = sd_ktail(p.f, G, GC, tq, t0, R.eb[u]);
+        const f32x4 k4 = widen(R.kr[u]);
+        sd_rows(p.f, G, R.sd, tq, t0, k4, widen(R.qr[u]), R.bq[u], eb, qgm);
+        *reinterpret_cast<f32x4*>(sKt + tq * SE + cq4) = sd_ktail(p.f, G, GC, tq, t0, k4);
       } else {
         const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
         *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
+        eb = R.eb[u];
+        qgm = R.qg[u];
       }
       *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(qgm, qj);
       *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(eb, qj);
@@ -219,7 +222,7 @@ void bwd_state_mfma_kernel(BwdParams p) {
     stage(R, n * CH);
     float dO[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) dO[k] = R.o[k];
+    for (int k = 0; k < 16; ++k) dO[k] = n * CH + 16 * (k >> 2) + 4 * g + (k & 3) < T ? (float)R.o[k] : 0.f;
     __syncthreads();
     if (n > 0) load(n - 1, R);
     // the gradient of the state leaving this chunk, for the product pass

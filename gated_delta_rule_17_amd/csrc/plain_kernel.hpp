@@ -84,6 +84,26 @@ __device__ __forceinline__ f32x4 ldf4(const bf16* p) {
   return __builtin_convertvector(*reinterpret_cast<const bf16x4*>(p), f32x4);
 }
 
+// Loads kept in the I/O type until their use: a record loaded a chunk ahead
+// and widened where it is consumed, so that no conversion right after the
+// load makes the wave wait for it there.
+template <class IO>
+struct Raw;
+template <>
+struct Raw<float> {
+  typedef f32x4 v4;
+};
+template <>
+struct Raw<bf16> {
+  typedef bf16x4 v4;
+};
+template <class IO>
+__device__ __forceinline__ typename Raw<IO>::v4 ldraw4(const IO* p) {
+  return *reinterpret_cast<const typename Raw<IO>::v4*>(p);
+}
+__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
+__device__ __forceinline__ f32x4 widen(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+
 // sum over the 16 lanes of each 16-lane group
 __device__ __forceinline__ float sum16(float s) {
   s += __shfl_xor(s, 1, 16);

@@ -673,10 +673,17 @@ constexpr int plain_mrec_lds_bytes() {
 struct SdLane {
   float g, beta, lam;
 };
+// (every load is unconditional, a scalar the gate kinds do not use read from
+// k, which is always there and holds at least four bytes per token: a value
+// chosen by a branch would make the wave wait for its load at the branch's
+// join; the flags select at use, in sd_scan and sd_rows)
 __device__ __forceinline__ SdLane sd_lane_load(const ChunkParams& p, size_t seq0, int t0, int hh, int lane) {
   const size_t tok = seq0 + (size_t)min(t0 + lane, p.T - 1) * p.H;
-  return SdLane{p.decay == 1 ? p.g[tok] : 0.f, p.erase == 0 ? p.beta[tok] : 0.f,
-                p.qmix == 2 ? p.lam[tok] : (p.qmix ? p.lam[hh] : 0.f)};
+  const float* any = reinterpret_cast<const float*>(p.k);
+  const float* gp = p.decay == 1 ? p.g : any;
+  const float* bp = p.erase == 0 ? p.beta : any;
+  const float* lp = p.qmix == 2 ? p.lam + tok : (p.qmix ? p.lam + hh : any + tok);
+  return SdLane{gp[tok], bp[tok], *lp};
 }
 // G_{t0 + lane} in lane lane (every lane of the wave active)
 __device__ __forceinline__ float sd_scan(const ChunkParams& p, const SdLane& s, int t0, int lane) {
@@ -687,7 +694,7 @@ __device__ __forceinline__ float sd_scan(const ChunkParams& p, const SdLane& s, 
 // lane shuffles)
 __device__ __forceinline__ void sd_rows(const ChunkParams& p, float G, const SdLane& s, int t, int t0, f32x4 k,
                                         f32x4 q, f32x4 b, f32x4& eb, f32x4& qg) {
-  const float Gt = __shfl(G, t), bt = __shfl(s.beta, t), lt = __shfl(s.lam, t);
+  const float Gt = __shfl(G, t), bt = __shfl(s.beta, t), lt = p.qmix ? __shfl(s.lam, t) : 0.f;
   const bool ok = t0 + t < p.T;
   const float gam = fexp(Gt);
 #pragma unroll
@@ -759,10 +766,12 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
   // hold the raw k, q and bq the per-channel erase gate, all in the quad
   // layout below, and sd this lane's token scalars)
   struct Rec {
-    f32x4 eb[NQ_E], qg[NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
+    typename Raw<IO>::v4 kr[SD ? NQ_E : 1], qr[SD ? NQ_E : 1];
+    f32x4 eb[SD ? 1 : NQ_E], qg[SD ? 1 : NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
     float gc;
     SdLane sd;
-    float v[16], gt[16];  // rows 16 I + 4 g + r of this lane's column
+    IO v[16];      // rows 16 I + 4 g + r of this lane's column
+    float gt[16];
   };
   const IO* kin = reinterpret_cast<const IO*>(p.k);
   const IO* qin = reinterpret_cast<const IO*>(p.q);
@@ -778,8 +787,8 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
         // (k, q, b of the same token and channels serve E_bar and Q_gamma
         // as row pieces and K_tail through the transpose)
         const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
-        R.eb[u] = ldf4(kin + tokq * DK + c);
-        R.qg[u] = ldf4(qin + tokq * DK + c);
+        R.kr[u] = ldraw4(kin + tokq * DK + c);
+        R.qr[u] = ldraw4(qin + tokq * DK + c);
         if (p.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.b + tokq * DK + c);
       } else {
         const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
@@ -802,8 +811,8 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       for (int r = 0; r < 4; ++r) {
         const int k = 4 * I + r;
         const size_t tok = seq0 + (size_t)min(n * CH + 16 * I + 4 * g + r, T - 1) * H;
-        R.v[k] = ldf(vg + tok * DV + col);
-        R.gt[k] = write == 1 ? p.w[tok * DV + col] : p.beta[tok];
+        R.v[k] = vg[tok * DV + col];
+        R.gt[k] = *(write == 1 ? p.w + tok * DV + col : p.beta + tok);  // (one load either way)
       }
   };
   auto stage = [&](const Rec& R, int t0) __attribute__((always_inline)) {
@@ -820,9 +829,10 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
         // token 4 t4 + j, channels 4 k .. + 3 of the block: a row piece of
         // E_bar and Q_gamma, and K_tail for the transpose
         const int tq = 4 * t4 + (lane & 3), cq4 = 64 * (blk % (DK / 64)) + 4 * (lane >> 2);
+        const f32x4 k4 = widen(R.kr[u]);
         f32x4 eb, qgm;
-        sd_rows(p, G, R.sd, tq, t0, R.eb[u], R.qg[u], R.bq[u], eb, qgm);
-        kt = sd_ktail(p, G, GC, tq, t0, R.eb[u]);
+        sd_rows(p, G, R.sd, tq, t0, k4, widen(R.qr[u]), R.bq[u], eb, qgm);
+        kt = sd_ktail(p, G, GC, tq, t0, k4);
         *reinterpret_cast<f32x4*>(sEb + tq * SE + cq4) = eb;
         *reinterpret_cast<f32x4*>(sQg + tq * SE + cq4) = qgm;
       } else {
@@ -855,7 +865,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const bool ok = t0 + 16 * (k >> 2) + 4 * g + (k & 3) < T;  // row 16 I + 4 g + r, k = 4 I + r
-      z[k] = ok ? R.gt[k] * R.v[k] : 0.f;
+      z[k] = ok ? R.gt[k] * (float)R.v[k] : 0.f;
     }
     __syncthreads();
     if (n + 1 < N) load(n + 1, R);
