@@ -48,7 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "chunked gated-delta fwd tokens/s and % bf16 MFMA peak, d=128, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
-FP32_VALU_PEAK_TFLOPS = 157.3   # 256 CU x 4 SIMD x 64 lanes x 2 flop x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3        # fp32 on the matrix cores (and the vector ALUs), dense: 256 CU x 256 flop/clk x 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_delta_rule_17_amd", "csrc")
 CALIB_BYTES = 2 << 30           # device copy that calibrates the HBM counters
@@ -76,6 +76,25 @@ def flops_per_token_head(dk, dv, C=64):
          + C * (C - 1) * dv        # U = A Z
          + 6 * C * dk * dv         # Y S, Q_gamma S, K_tail^T W
          + C * (C + 1) * dv)       # A_qk W
+    return f / C
+
+
+def bwd_flops_per_token_head(dk, dv, C=64):
+    """Algorithmic flops of the chunk backward per token and head, as the
+    passes compute it: the record pass's forward (T, A_qk, the inverse,
+    E_bar S, A R, K_tail^T W), then dW = A_qk^T dO + K_tail dS, dR = A^T dW,
+    the state gradient's Q_gamma^T dO and E_bar^T dR, the products over the
+    value channels (dT, dA_qk, dE_bar, dQ_gamma, dK_tail) and the four
+    decay-weighted sums back to the rows (D1 K, D2 K, D1^T E, D2^T Q);
+    triangular products count only their non-zero half."""
+    full = 2 * C * dk * dv             # a C x dk by dk x dv product (or any of its transposes)
+    low_v, low_k = C * (C + 1) * dv, C * (C + 1) * dk   # triangular (diagonal kept) C x C times C x n
+    slow_v, slow_k = C * (C - 1) * dv, C * (C - 1) * dk  # strictly triangular
+    f = (slow_k + low_k + C * (C - 1) * (C - 2) / 3    # T, A_qk, (I + T)^{-1}
+         + 8 * full                                     # E_bar S, K_tail^T W, K_tail dS, Q_gamma^T dO,
+                                                        # E_bar^T dR, dE_bar, dQ_gamma, dK_tail
+         + 4 * low_v + slow_v                           # A R, A_qk^T dO, A^T dW, dA_qk; dT
+         + 2 * slow_k + 2 * low_k)                      # D1 K, D1^T E; D2 K, D2^T Q
     return f / C
 
 
@@ -213,12 +232,19 @@ def bench_workload(name, op, cfg, steps, warmup, settle_ms=0.0):
         fl = flops_per_token_head(dk, dv) * B * T * H
     elif op in ("recurrent", "step"):
         fl = recurrent_flops_per_token_head(dk, dv) * B * T * H
+    elif op == "bwd":
+        fl = bwd_flops_per_token_head(dk, dv) * B * T * H
     else:
         fl = None
     if fl is not None:
+        # the peak of the arithmetic the kernels run: the backward and the
+        # fp32-I/O chunk form multiply on fp32 operands, the bf16 chunk forms on bf16
+        fp32 = op == "bwd" or (op == "chunk" and cfg["io"] == "f32")
+        peak = FP32_PEAK_TFLOPS if fp32 else MFMA_BF16_PEAK_TFLOPS
         res["algorithmic_flops"] = fl
         res["tflops"] = fl / (ms_kern * 1e-3) / 1e12
-        res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
+        res["peak_tflops"] = peak
+        res["mfma_frac"] = res["tflops"] / peak
     if op == "chunk" and T >= 64:
         res["us_per_chunk_step"] = ms_kern * 1e3 / ((T + 63) // 64)
     del copies
@@ -566,7 +592,7 @@ def main():
     for name, op, cfg in items[1:]:
         steps = max(5, args.steps // 2) if op != "bwd" else 5
         r, inp = bench_workload(name, op, cfg, steps, args.warmup, settle_ms=args.settle_ms)
-        keep = ("op", "tokens_per_s", "kernel_ms_avg", "hbm_gbs", "hbm_frac", "tflops", "mfma_frac", "plan",
+        keep = ("op", "tokens_per_s", "kernel_ms_avg", "hbm_gbs", "hbm_frac", "tflops", "peak_tflops", "mfma_frac", "plan",
                 "algorithmic_bytes", "us_per_chunk_step")
         ent = {k: r[k] for k in keep if k in r}
         tr, _ = traffic_of(name, op)

@@ -302,10 +302,11 @@ void bwd_state_mfma_kernel(BwdParams p) {
 }
 
 // ---- pass B1: products over the value channels, on the matrix cores --------
-// One workgroup of four waves per (batch, head, chunk).  The value channels
-// are taken in halves of 64: dR, dO, W [64][64] and S, dS [DK][64] of the
-// half in LDS (123 KB), the products' partial sums carried over the halves
-// in accumulators.  Wave w owns row block w (rows 16 w .. + 15) of every
+// One workgroup of four waves per (batch, head, chunk), two per CU.  The value
+// channels are taken in quarters of 32: dR, dO, W [64][32] and S, dS [DK][32]
+// of the quarter in LDS (65 KB at DK = 128), the products' partial sums
+// carried over the quarters in accumulators; while one workgroup waits for
+// its loads, the other computes.  Wave w owns row block w (rows 16 w .. + 15) of every
 // output: dT and dA_qk (blocks J <= w), dE_bar, dQ_gamma, dK_tail (all DK / 16
 // column blocks).  Every product contracts over the value channels with
 // v_mfma_f32_16x16x4_f32; k-step (b, r) takes, in lane group g, the value
@@ -313,18 +314,18 @@ void bwd_state_mfma_kernel(BwdParams p) {
 // of rows (four k-steps each).  Then sC = sum_v S (.) dS per key channel.
 template <int DK>
 struct BwdB1Lay {
-  static constexpr int VH = 64, SP = VH + 4;
+  static constexpr int VH = 32, SP = VH + 4;
   static constexpr int oR = 0, oO = oR + CH * SP, oW = oO + CH * SP, oS = oW + CH * SP, odS = oS + DK * SP;
   static constexpr int TOTAL = odS + DK * SP;
-  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+  static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
 };
 
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_prod_kernel(BwdParams p) {
   using L = BwdB1Lay<DK>;
   constexpr int VH = L::VH, SP = L::SP, NC = DK / 16;
-  static_assert(DV % VH == 0, "value channels in halves of 64");
+  static_assert(DV % VH == 0, "value channels in quarters of 32");
   __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
   float *sR = lds + L::oR, *sO = lds + L::oO, *sW = lds + L::oW, *sS = lds + L::oS, *sdS = lds + L::odS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -344,11 +345,11 @@ void bwd_prod_kernel(BwdParams p) {
   for (int J = 0; J < 4; ++J) aT[J] = aA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c) aE[c] = aQ[c] = aK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sc = 0.f;  // sum_v S (.) dS of channel tid >> 1, half of the value channels of each half
+  float sc = 0.f;  // sum_v S (.) dS of channel tid >> 1, half of the value channels of each quarter
 
   for (int vh = 0; vh < DV; vh += VH) {
-    if (vh > 0) __syncthreads();  // the previous half's reads are done
-    // ---- the half's rows to LDS (every load of the thread issued first)
+    if (vh > 0) __syncthreads();  // the previous quarter's reads are done
+    // ---- the quarter's rows to LDS (every load of the thread issued first)
     {
       constexpr int QR = CH * VH / 4 / NTHR, QS = DK * VH / 4 / NTHR;
       f32x4 xr[QR], xo[QR], xw[QR], xs[QS], xd[QS];
@@ -381,7 +382,7 @@ void bwd_prod_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    // ---- sC: channel tid >> 1 (DK = 128) or tid >> 2 (DK = 64), a run of the half
+    // ---- sC: channel tid >> 1 (DK = 128) or tid >> 2 (DK = 64), a run of the quarter
     {
       constexpr int TPC = NTHR / DK, RUN = VH / TPC;
       const int c = tid / TPC, v0 = (tid % TPC) * RUN;
@@ -393,7 +394,7 @@ void bwd_prod_kernel(BwdParams p) {
         for (int i = 0; i < 4; ++i) sc = __builtin_fmaf(a[i], b[i], sc);
       }
     }
-    // ---- the products of row block w over the half
+    // ---- the products of row block w over the quarter
 #pragma unroll
     for (int b = 0; b < VH / 16; ++b) {
       const int ko = 16 * b + 4 * g;
