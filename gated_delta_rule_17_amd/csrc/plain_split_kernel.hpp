@@ -66,7 +66,8 @@ struct PlainPrepLay {
 // written (the passes that read them form them from the inputs: a scalar
 // decay or none, see sd_rows).
 template <class IO, int DK>
-__global__ __launch_bounds__(NTHR) void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
   using L = PlainPrepLay;
   constexpr int HP = L::HP, CHH = L::CHH, NH = DK / CHH;
   static_assert(DK % CHH == 0, "whole halves");
