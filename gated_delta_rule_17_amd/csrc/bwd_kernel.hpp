@@ -469,29 +469,32 @@ __device__ __forceinline__ void key_tail(const BwdParams& p, size_t ch, int t0, 
   const int decay = p.f.decay, erase = p.f.erase, write = p.f.write, qmix = p.f.qmix;
   const IO* vg = reinterpret_cast<const IO*>(p.f.v);
   const BwdWs& ws = p.ws;
-  {
-    constexpr int NE = CH * DV / NTHR;
+  // (in groups of up to 16 elements per thread, every load of a group issued first)
+  constexpr int NE = CH * DV / NTHR, UB = NE < 16 ? NE : 16;
+  static_assert(NE % UB == 0, "whole groups");
+#pragma unroll 1
+  for (int u0 = 0; u0 < NE; u0 += UB) {
     const float* dz = ws.dR + ch * CH * DV;
-    float zr[NE], vr[NE], wr[NE];
+    float zr[UB], vr[UB], wr[UB];
 #pragma unroll
-    for (int u = 0; u < NE; ++u) {
-      const int e = tid + NTHR * u, r = e / DV, v = e - r * DV;
+    for (int uu = 0; uu < UB; ++uu) {
+      const int e = tid + NTHR * (u0 + uu), r = e / DV, v = e - r * DV;
       const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
-      zr[u] = dz[e];
-      vr[u] = ldf(vg + tok * DV + v);
-      wr[u] = write == 1 ? p.f.w[tok * DV + v] : 0.f;
+      zr[uu] = dz[e];
+      vr[uu] = ldf(vg + tok * DV + v);
+      wr[uu] = write == 1 ? p.f.w[tok * DV + v] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < NE; ++u) {
-      const int e = tid + NTHR * u, r = e / DV, v = e - r * DV;
+    for (int uu = 0; uu < UB; ++uu) {
+      const int u = u0 + uu, e = tid + NTHR * u, r = e / DV, v = e - r * DV;
       const int t = t0 + r;
       const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
-      const float z = zr[u], vv = vr[u];
+      const float z = zr[uu], vv = vr[uu];
       float zb = 0.f;
       if (t < T) {
         if (write == 1) {
           p.dw[tok * DV + v] = z * vv;
-          p.dv[tok * DV + v] = wr[u] * z;
+          p.dv[tok * DV + v] = wr[uu] * z;
         } else {
           zb = z * vv;
           p.dv[tok * DV + v] = sBeta[r] * z;
@@ -708,24 +711,27 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
 // Pass B2 under a scalar decay (or none): d_ij = exp(G_i - G_j) is one
 // number per token pair, so with D1 = dT (.) D and D2 = dA_qk (.) D (strictly
 // lower; the diagonal of dA_qk kept apart) the four sums are products of 64 x
-// 64 matrices, run on v_mfma_f32_16x16x4_f32 per pass of 64 key channels:
+// 64 matrices, run on v_mfma_f32_16x16x4_f32 per pass of 32 key channels:
 //   P = D1 K,  Pq = D2 K,  Rm = D1^T E,  Rq = D2^T Q
 // Wave w owns row block w (its P, Pq over column blocks J <= w, its Rm, Rq
-// over J >= w: 160 MFMAs per wave and pass whatever w).  k-step (J, r) takes,
-// in lane group g, the token 16 J + 4 g + r, so every operand is a 16-byte
-// LDS read feeding four MFMAs: rows of D1, D2 and of their transposes, and
-// rows of K^T, E^T, Q^T (the pass's columns staged transposed).  Lane
-// (g, l) then holds rows 16 w + 4 g + r of channel 16 C + l of each column
-// block C; a row's sums over the channels end in a DPP sum over the 16
-// lanes of its group.
+// over J >= w: the same MFMA count for every wave).  k-step (J, r) takes, in
+// lane group g, the token 16 J + 4 g + r.  The A operands of P and Pq are
+// rows of D1 and D2 (one 16-byte LDS read feeds four MFMAs), those of Rm and
+// Rq their columns (four 4-byte reads: no transposed copy is kept), the B
+// operands rows of K^T, E^T, Q^T (the pass's columns staged transposed).
+// Lane (g, l) then holds rows 16 w + 4 g + r of channel 16 C + l of each
+// column block C; a row's sums over the channels end in a DPP sum over the 16
+// lanes of its group.  65 KB of LDS and at most 256 registers per lane: two
+// workgroups share a CU, so that one computes while the other waits for its
+// loads.
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_key_scalar_kernel(BwdParams p) {
-  constexpr int KC = 64, NPASS = DK / KC;
+  constexpr int KC = 32, NPASS = DK / KC, NCB = KC / 16;
   constexpr int VW = DV / 64;
   constexpr int TP = CH + 4;  // 16-byte rows; 4-bank shift per row
-  static_assert(DK % KC == 0 && NTHR == 256, "key channels in passes of 64, four waves");
-  __shared__ __attribute__((aligned(16))) float sD1[CH * TP], sD2[CH * TP], sD1T[CH * TP], sD2T[CH * TP];
+  static_assert(DK % KC == 0 && NTHR == 256, "key channels in passes of 32, four waves");
+  __shared__ __attribute__((aligned(16))) float sD1[CH * TP], sD2[CH * TP];
   __shared__ __attribute__((aligned(16))) float sKT[KC * TP], sET[KC * TP], sQT[KC * TP];
   __shared__ float sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW], sDg[CH];
   __shared__ float sBeta[CH], sLam[CH], sGt[CH], sDiag[CH], sRG[CH], sRX[CH];
@@ -745,8 +751,15 @@ void bwd_key_scalar_kernel(BwdParams p) {
   const IO* kg = reinterpret_cast<const IO*>(p.f.k);
   const BwdWs& ws = p.ws;
 
-  copy_rows<CH, CH, TP>(sD1, ws.T + ch * CH * CH, tid);
-  copy_rows<CH, CH, TP>(sD2, ws.A + ch * CH * CH, tid);
+  // the chunk's dT and dA_qk, four 16-byte pieces of each per thread,
+  // requested first
+  constexpr int NQD = CH * CH / 4 / NTHR;
+  f32x4 xt[NQD], xa[NQD];
+#pragma unroll
+  for (int u = 0; u < NQD; ++u) {
+    xt[u] = *reinterpret_cast<const f32x4*>(ws.T + ch * CH * CH + 4 * (tid + NTHR * u));
+    xa[u] = *reinterpret_cast<const f32x4*>(ws.A + ch * CH * CH + 4 * (tid + NTHR * u));
+  }
   for (int r = tid; r < CH; r += NTHR) {
     const int t = t0 + r;
     const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
@@ -756,26 +769,31 @@ void bwd_key_scalar_kernel(BwdParams p) {
     sRG[r] = 0.f;
     sRX[r] = 0.f;
   }
-  // the scalar decay's prefix sums G_t (zero past T), then D1, D2 strictly
-  // below the diagonal (in place; the diagonal of dA_qk kept apart) and
-  // their transposes
+  // the scalar decay's prefix sums G_t (zero past T)
   if (tid < CH) {
     const int t = t0 + tid;
     const float gv = (decay == 1 && t < T) ? p.f.g[seq0 + (size_t)t * H] : 0.f;
     sGt[tid] = wave_incl_scan(gv);
   }
   __syncthreads();
-  for (int e = tid; e < CH * CH; e += NTHR) {
-    const int i = e >> 6, j = e & 63;
-    const float d = j < i ? fexp(sGt[i] - sGt[j]) : 0.f;
-    const float d1 = sD1[i * TP + j] * d, d2 = sD2[i * TP + j] * d;
-    if (i == j) sDiag[i] = sD2[i * TP + j];
-    sD1[i * TP + j] = d1;
-    sD2[i * TP + j] = d2;
-    sD1T[j * TP + i] = d1;
-    sD2T[j * TP + i] = d2;
+  // D1, D2 strictly below the diagonal, the diagonal of dA_qk kept apart
+#pragma unroll
+  for (int u = 0; u < NQD; ++u) {
+    const int e = tid + NTHR * u, i = e >> 4, j0 = (e & 15) * 4;
+    const float Gi = sGt[i];
+    f32x4 d1, d2;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = j0 + k;
+      const float d = j < i ? fexp(Gi - sGt[j]) : 0.f;
+      d1[k] = xt[u][k] * d;
+      d2[k] = xa[u][k] * d;
+      if (j == i) sDiag[i] = xa[u][k];
+    }
+    *reinterpret_cast<f32x4*>(sD1 + i * TP + j0) = d1;
+    *reinterpret_cast<f32x4*>(sD2 + i * TP + j0) = d2;
   }
-  const float GC = sGt[CH - 1];  // (read after the first barrier of the pass loop)
+  const float GC = sGt[CH - 1];
   // a row's sum over the 16 lanes of its group (quad permutations, then the
   // half-row and row mirrors)
   auto row16 = [](float x) __attribute__((always_inline)) {
@@ -787,28 +805,27 @@ void bwd_key_scalar_kernel(BwdParams p) {
   };
 
   for (int ps = 0; ps < NPASS; ++ps) {
-    __syncthreads();  // the previous pass's columns are no longer read
+    if (ps > 0) __syncthreads();  // the previous pass's columns are no longer read
     // ---- this pass's columns of the chunk's rows, transposed (zero past T):
-    // lane (k, j) = (lane / 4, lane % 4) of wave w takes token 4 b + j
-    // (b = w + 4 u), channels 4 k .. + 3 of the pass; the quad transposes
-    // its block, and the lane writes channel 4 k + j = lane, tokens 4 b ..
-    // + 3 as one 16-byte LDS write (64 channel rows per wave: no bank
-    // conflicts)
+    // lane (h, k, j) = (lane / 32, lane / 4 % 8, lane % 4) of wave w takes
+    // token 4 b + j (b = 2 (w + 4 u) + h), channels 4 k .. + 3 of the pass;
+    // the quad transposes its block, and the lane writes channel 4 k + j,
+    // tokens 4 b .. + 3 as one 16-byte LDS write
     {
       constexpr int NQ = CH * KC / 4 / NTHR;
-      const int qj = lane & 3, cl = 4 * (lane >> 2);
+      const int qj = lane & 3, cq = (lane >> 2) & 7, th = lane >> 5;
       f32x4 rk[NQ], rq[NQ], rb[NQ];
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const int r = 4 * (w + 4 * u) + qj;
+        const int r = 4 * (2 * (w + 4 * u) + th) + qj;
         const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
-        rk[u] = ldf4(kg + tok * DK + ps * KC + cl);
-        rq[u] = ldf4(qg + tok * DK + ps * KC + cl);
-        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + ps * KC + cl);
+        rk[u] = ldf4(kg + tok * DK + ps * KC + 4 * cq);
+        rq[u] = ldf4(qg + tok * DK + ps * KC + 4 * cq);
+        if (erase == 1) rb[u] = ldf4(p.f.b + tok * DK + ps * KC + 4 * cq);
       }
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const int b4 = w + 4 * u, r = 4 * b4 + qj;
+        const int b4 = 2 * (w + 4 * u) + th, r = 4 * b4 + qj;
         const bool ok = t0 + r < T;
         f32x4 kv, qv, ev;
 #pragma unroll
@@ -817,16 +834,17 @@ void bwd_key_scalar_kernel(BwdParams p) {
           qv[i] = ok ? rq[u][i] : 0.f;
           ev[i] = erase == 1 ? (ok ? rb[u][i] : 0.f) * kv[i] : sBeta[r] * __builtin_fmaf(sLam[r], qv[i], kv[i]);
         }
-        *reinterpret_cast<f32x4*>(sKT + lane * TP + 4 * b4) = quad_transpose(kv, qj);
-        *reinterpret_cast<f32x4*>(sQT + lane * TP + 4 * b4) = quad_transpose(qv, qj);
-        *reinterpret_cast<f32x4*>(sET + lane * TP + 4 * b4) = quad_transpose(ev, qj);
+        const int c = 4 * cq + qj;
+        *reinterpret_cast<f32x4*>(sKT + c * TP + 4 * b4) = quad_transpose(kv, qj);
+        *reinterpret_cast<f32x4*>(sQT + c * TP + 4 * b4) = quad_transpose(qv, qj);
+        *reinterpret_cast<f32x4*>(sET + c * TP + 4 * b4) = quad_transpose(ev, qj);
       }
     }
     // the product pass's results and the erase gate at my (row, channel)
     // pairs, requested before the products
-    float dEb[4][4], dQg[4][4], dKt[4][4], bI[4][4];
+    float dEb[NCB][4], dQg[NCB][4], dKt[NCB][4], bI[NCB][4];
 #pragma unroll
-    for (int C = 0; C < 4; ++C)
+    for (int C = 0; C < NCB; ++C)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * g + r, cg = ps * KC + 16 * C + l16;
@@ -839,16 +857,16 @@ void bwd_key_scalar_kernel(BwdParams p) {
       }
     __syncthreads();
     // ---- the four products: row block w, column blocks C of the pass
-    f32x4 aP[4], aPq[4], aRm[4], aRq[4];
+    f32x4 aP[NCB], aPq[NCB], aRm[NCB], aRq[NCB];
 #pragma unroll
-    for (int C = 0; C < 4; ++C) aP[C] = aPq[C] = aRm[C] = aRq[C] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int C = 0; C < NCB; ++C) aP[C] = aPq[C] = aRm[C] = aRq[C] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       if (J <= w) {  // P, Pq: j < i
         const f32x4 a1 = *reinterpret_cast<const f32x4*>(sD1 + (16 * w + l16) * TP + 16 * J + 4 * g);
         const f32x4 a2 = *reinterpret_cast<const f32x4*>(sD2 + (16 * w + l16) * TP + 16 * J + 4 * g);
 #pragma unroll
-        for (int C = 0; C < 4; ++C) {
+        for (int C = 0; C < NCB; ++C) {
           const f32x4 b = *reinterpret_cast<const f32x4*>(sKT + (16 * C + l16) * TP + 16 * J + 4 * g);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -857,11 +875,15 @@ void bwd_key_scalar_kernel(BwdParams p) {
           }
         }
       }
-      if (J >= w) {  // Rm, Rq: i2 > i
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sD1T + (16 * w + l16) * TP + 16 * J + 4 * g);
-        const f32x4 a2 = *reinterpret_cast<const f32x4*>(sD2T + (16 * w + l16) * TP + 16 * J + 4 * g);
+      if (J >= w) {  // Rm, Rq: i2 > i; column 16 w + l16 of D1, D2 at rows 16 J + 4 g + r
+        float a1[4], a2[4];
 #pragma unroll
-        for (int C = 0; C < 4; ++C) {
+        for (int r = 0; r < 4; ++r) {
+          a1[r] = sD1[(16 * J + 4 * g + r) * TP + 16 * w + l16];
+          a2[r] = sD2[(16 * J + 4 * g + r) * TP + 16 * w + l16];
+        }
+#pragma unroll
+        for (int C = 0; C < NCB; ++C) {
           const f32x4 be = *reinterpret_cast<const f32x4*>(sET + (16 * C + l16) * TP + 16 * J + 4 * g);
           const f32x4 bq = *reinterpret_cast<const f32x4*>(sQT + (16 * C + l16) * TP + 16 * J + 4 * g);
 #pragma unroll
@@ -883,7 +905,7 @@ void bwd_key_scalar_kernel(BwdParams p) {
     float sb[4] = {0.f, 0.f, 0.f, 0.f}, sl[4] = {0.f, 0.f, 0.f, 0.f};
     float sg[4] = {0.f, 0.f, 0.f, 0.f}, sx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int C = 0; C < 4; ++C) {
+    for (int C = 0; C < NCB; ++C) {
       const int c = 16 * C + l16, cg = ps * KC + c;
       const f32x4 kv = *reinterpret_cast<const f32x4*>(sKT + c * TP + 16 * w + 4 * g);
       const f32x4 ev = *reinterpret_cast<const f32x4*>(sET + c * TP + 16 * w + 4 * g);
