@@ -39,8 +39,8 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
       hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, false>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64,
                          p.ws);
   }
-  if (sd) hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, true>), dim3(BH * (DV / 64)), dim3(NTHR), 0, s, p);
-  else hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, false>), dim3(BH * (DV / 64)), dim3(NTHR), 0, s, p);
+  if (sd) hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, true>), dim3(BH * (DV / 64)), dim3(2 * NTHR), 0, s, p);
+  else hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, false>), dim3(BH * (DV / 64)), dim3(2 * NTHR), 0, s, p);
   if (N > 0) {
     hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
     // the key pass: on the matrix cores under a scalar decay (or none), per

@@ -71,26 +71,33 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
 }
 
 // ---- pass A: the reverse state recurrence, on the matrix cores ----------------
-// Every product on v_mfma_f32_16x16x4_f32: one workgroup of four waves per (batch, head, 64-column slice), wave w
-// owning columns 16 w .. + 15 and dS of those columns in accumulators
-// (register r of block b of lane l: dS[16 b + 4 (l / 16) + r][16 w + l % 16],
-// the forward recurrence's state layout).  k-step (b, r) takes, in lane group
-// g, the channel or token 16 b + 4 g + r, so dS, dO, dW and dR serve as B
-// operands in place and the A operands are 16-byte LDS reads:
+// One workgroup of eight waves per (batch, head, 64-column slice).  Waves 0-3
+// compute, every product on v_mfma_f32_16x16x4_f32: wave w owns columns
+// 16 w .. + 15 and dS of those columns in accumulators (register r of block b
+// of lane l: dS[16 b + 4 (l / 16) + r][16 w + l % 16], the forward
+// recurrence's state layout).  k-step (b, r) takes, in lane group g, the
+// channel or token 16 b + 4 g + r, so dS, dO, dW and dR serve as B operands in
+// place and the A operands are 16-byte LDS reads:
 //   dW = A_qk^T dO + K_tail dS        A = A_qk^T rows, K_tail rows
 //   dR = A^T dW                       A = A^T rows (upper blocks only)
 //   dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR   A = Q_gamma^T, E_bar^T rows
-// The chunk's records go to LDS once per chunk (the transposes on the way);
-// the previous chunk's are loaded into registers while this one computes.
+// Waves 4-7 stage a chunk's records in LDS (the transposes on the way; under
+// a scalar decay the factor rows formed from the inputs) in two sets, each
+// written while the computing waves read the other: set B (Q_gamma^T,
+// E_bar^T, gamma_C) of chunk n during dW and dR of chunk n, set A (K_tail,
+// A_qk^T, A^T) of chunk n - 1 during the state update of chunk n.  Each set's
+// inputs are loaded into the staging waves' registers a phase before they
+// are staged.  A computing wave and a staging wave share each SIMD, so the
+// staging arithmetic runs beside the MFMAs instead of between them.
 template <int DK>
 struct BwdAMLay {
   static constexpr int SE = DK + 4, SA = CH + 4;
-  static constexpr int oKt = 0;                  // [64][SE] K_tail rows
-  static constexpr int oQgT = oKt + CH * SE;     // [DK][SA] Q_gamma^T
-  static constexpr int oEbT = oQgT + DK * SA;    // [DK][SA] E_bar^T
-  static constexpr int oAqT = oEbT + DK * SA;    // [64][SA] A_qk^T
-  static constexpr int oAT = oAqT + CH * SA;     // [64][SA] A^T
-  static constexpr int oGC = oAT + CH * SA;      // [DK] gamma_C
+  static constexpr int oKt = 0;                  // [64][SE] K_tail rows        (set A)
+  static constexpr int oAqT = oKt + CH * SE;     // [64][SA] A_qk^T             (set A)
+  static constexpr int oAT = oAqT + CH * SA;     // [64][SA] A^T                (set A)
+  static constexpr int oQgT = oAT + CH * SA;     // [DK][SA] Q_gamma^T          (set B)
+  static constexpr int oEbT = oQgT + DK * SA;    // [DK][SA] E_bar^T            (set B)
+  static constexpr int oGC = oEbT + DK * SA;     // [DK] gamma_C                (set B)
   static constexpr int TOTAL = oGC + DK;
   static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
 };
@@ -98,7 +105,7 @@ struct BwdAMLay {
 // SD: a scalar decay or none; E_bar, Q_gamma, K_tail and gamma_C are formed
 // from the inputs while staging (sd_rows) rather than read from the workspace.
 template <class IO, int DK, bool SD = false>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_state_mfma_kernel(BwdParams p) {
   using L = BwdAMLay<DK>;
   constexpr int SE = L::SE, SA = L::SA, NB = DK / 16, DVS = 64;
@@ -117,114 +124,178 @@ void bwd_state_mfma_kernel(BwdParams p) {
   const int bh = wid / NS, slice = wid - bh * NS;
   const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
   const int T = p.f.T, H = p.f.H, DV = p.f.DV, N = p.nchunks;
-  const int col = slice * DVS + 16 * wave + l16;
   const size_t seq0 = (size_t)bb * T * H + hh;
-  const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   const BwdWs& ws = p.ws;
 
+  if (wave >= 4) {
+    // ================= staging waves =================
+    const int st = tid - NTHR, sw = wave - 4;  // thread and wave within the staging group
+    const int qj = lane & 3, qk = lane >> 2;
+    const IO* kin = reinterpret_cast<const IO*>(p.f.k);
+    const IO* qin = reinterpret_cast<const IO*>(p.f.q);
+    // set A's inputs: K_tail (SD: the raw k), A, A_qk; set B's: E_bar and
+    // Q_gamma (SD: the raw k, q and the per-channel erase gate), gamma_C.
+    // E_bar, Q_gamma, A, A_qk are staged transposed: lane (k, j) = (lane / 4,
+    // lane % 4) of staging wave w loads token 4 t4 + j, channels 4 k .. + 3
+    // of a block of 4 tokens x 64 channels (rows stay 256-byte runs), the
+    // quad transposes it, and the lane writes channel 4 k + j, tokens 4 t4 ..
+    // + 3 as one 16-byte LDS write (64 consecutive channel rows per wave: no
+    // bank conflicts).  K_tail stays row-major.
+    struct RecA {
+      typename Raw<IO>::v4 kr[SD ? NQ_E : 1];
+      f32x4 kt[SD ? 1 : NQ_E], a[NQ_A], aq[NQ_A];
+      SdLane sd;
+    };
+    struct RecB {
+      typename Raw<IO>::v4 kr[SD ? NQ_E : 1], qr[SD ? NQ_E : 1];
+      f32x4 eb[SD ? 1 : NQ_E], qg[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1];
+      float gc;
+      SdLane sd;
+    };
+    // token and first channel of piece u of a [64][DK] array in the quad layout
+    auto piece = [&](int u, int& t, int& c) __attribute__((always_inline)) {
+      const int blk = sw + 4 * u;
+      t = 4 * (blk / (DK / 64)) + qj;
+      c = 64 * (blk % (DK / 64)) + 4 * qk;
+    };
+    auto load_a = [&](int n, RecA& R) __attribute__((always_inline)) {
+      const size_t ch = (size_t)bh * N + n;
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        if constexpr (SD) {
+          int t, c;
+          piece(u, t, c);
+          R.kr[u] = ldraw4(kin + (seq0 + (size_t)min(n * CH + t, T - 1) * H) * DK + c);
+        } else {
+          R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + 4 * (st + NTHR * u));
+        }
+      }
+      if constexpr (SD) R.sd = sd_lane_load(p.f, seq0, n * CH, hh, lane);
+#pragma unroll
+      for (int u = 0; u < NQ_A; ++u) {
+        const int t = 4 * (sw + 4 * u) + qj, c = 4 * qk;
+        const size_t o = ch * CH * CH + (size_t)t * CH + c;
+        R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
+        R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
+      }
+    };
+    auto load_b = [&](int n, RecB& R) __attribute__((always_inline)) {
+      const size_t ch = (size_t)bh * N + n;
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        int t, c;
+        piece(u, t, c);
+        if constexpr (SD) {
+          const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
+          R.kr[u] = ldraw4(kin + tokq * DK + c);
+          R.qr[u] = ldraw4(qin + tokq * DK + c);
+          if (p.f.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.f.b + tokq * DK + c);
+        } else {
+          const size_t o = ch * CH * DK + (size_t)t * DK + c;
+          R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
+          R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
+        }
+      }
+      if constexpr (SD) R.sd = sd_lane_load(p.f, seq0, n * CH, hh, lane);
+      else R.gc = st < DK ? ws.gC[ch * DK + st] : 0.f;
+    };
+    auto stage_a = [&](const RecA& R, int t0) __attribute__((always_inline)) {
+      float G = 0.f, GC = 0.f;
+      if constexpr (SD) {
+        G = sd_scan(p.f, R.sd, t0, lane);
+        GC = lane_value(G, 63);
+      }
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        if constexpr (SD) {
+          int tq, cq4;
+          piece(u, tq, cq4);
+          *reinterpret_cast<f32x4*>(sKt + tq * SE + cq4) = sd_ktail(p.f, G, GC, tq, t0, widen(R.kr[u]));
+        } else {
+          const int e = 4 * (st + NTHR * u), t = e / DK, c = e - t * DK;
+          *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NQ_A; ++u) {
+        const int t4 = sw + 4 * u, cq = 4 * qk + qj;
+        *reinterpret_cast<f32x4*>(sAT + cq * SA + 4 * t4) = quad_transpose(R.a[u], qj);
+        *reinterpret_cast<f32x4*>(sAqT + cq * SA + 4 * t4) = quad_transpose(R.aq[u], qj);
+      }
+    };
+    auto stage_b = [&](const RecB& R, int t0) __attribute__((always_inline)) {
+      float G = 0.f, GC = 0.f;
+      if constexpr (SD) {
+        G = sd_scan(p.f, R.sd, t0, lane);
+        GC = lane_value(G, 63);
+      }
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        const int blk = sw + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + 4 * qk + qj;
+        f32x4 eb, qgm;
+        if constexpr (SD) {
+          int tq, cq4;
+          piece(u, tq, cq4);
+          sd_rows(p.f, G, R.sd, tq, t0, widen(R.kr[u]), widen(R.qr[u]), R.bq[u], eb, qgm);
+        } else {
+          eb = R.eb[u];
+          qgm = R.qg[u];
+        }
+        *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(qgm, qj);
+        *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(eb, qj);
+      }
+      if (st < DK) sGC[st] = SD ? fexp(GC) : R.gc;
+    };
+
+    RecA Ra;
+    RecB Rb;
+    if (N > 0) {
+      load_b(N - 1, Rb);
+      load_a(N - 1, Ra);
+      stage_a(Ra, (N - 1) * CH);
+    }
+    __syncthreads();  // set A of the last chunk is staged
+    for (int n = N - 1; n >= 0; --n) {
+      // phase 1 of chunk n (the computing waves read set A): set B of chunk n
+      if (n > 0) load_a(n - 1, Ra);
+      stage_b(Rb, n * CH);
+      __syncthreads();
+      // phase 2 of chunk n (they read set B): set A of chunk n - 1
+      if (n > 0) {
+        load_b(n - 1, Rb);
+        stage_a(Ra, (n - 1) * CH);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ================= computing waves =================
+  const int col = slice * DVS + 16 * wave + l16;
+  const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   f32x4 dS[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       dS[b][r] = p.d_st ? p.d_st[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] : 0.f;
-
-  // (SD: eb, qg hold the raw k, q and bq the per-channel erase gate, in the
-  // quad layout, and sd this lane's token scalars)
-  struct Rec {
-    typename Raw<IO>::v4 kr[SD ? NQ_E : 1], qr[SD ? NQ_E : 1];
-    f32x4 eb[SD ? 1 : NQ_E], qg[SD ? 1 : NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
-    float gc;
-    SdLane sd;
-    IO o[16];  // dO rows 16 I + 4 g + r of this lane's column
-  };
-  const IO* kin = reinterpret_cast<const IO*>(p.f.k);
-  const IO* qin = reinterpret_cast<const IO*>(p.f.q);
-  // E_bar, Q_gamma, A, A_qk are staged transposed: lane (k, j) = (lane / 4,
-  // lane % 4) of wave w loads token 4 t4 + j, channels 4 k .. + 3 of a block
-  // of 4 tokens x 64 channels (rows stay 256-byte runs), the quad transposes
-  // it, and the lane writes channel 4 k + j, tokens 4 t4 .. + 3 as one
-  // 16-byte LDS write (64 consecutive channel rows per wave: no bank
-  // conflicts).  K_tail stays row-major.
-  const int qj = lane & 3, qk = lane >> 2;
-  auto load = [&](int n, Rec& R) __attribute__((always_inline)) {
-    const size_t ch = (size_t)bh * N + n;
-#pragma unroll
-    for (int u = 0; u < NQ_E; ++u) {
-      const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + qj, c = 64 * (blk % (DK / 64)) + 4 * qk;
-      if constexpr (SD) {
-        const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
-        R.kr[u] = ldraw4(kin + tokq * DK + c);
-        R.qr[u] = ldraw4(qin + tokq * DK + c);
-        if (p.f.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.f.b + tokq * DK + c);
-      } else {
-        const size_t o = ch * CH * DK + (size_t)t * DK + c;
-        R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
-        R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
-        R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + 4 * (tid + NTHR * u));
-      }
-    }
-    if constexpr (SD) R.sd = sd_lane_load(p.f, seq0, n * CH, hh, lane);
-#pragma unroll
-    for (int u = 0; u < NQ_A; ++u) {
-      const int t = 4 * (wave + 4 * u) + qj, c = 4 * qk;
-      const size_t o = ch * CH * CH + (size_t)t * CH + c;
-      R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
-      R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
-    }
-    if constexpr (!SD) R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
+  // dO rows 16 I + 4 g + r of this lane's column, a chunk ahead
+  IO o[16];
+  auto load_o = [&](int n) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int t = n * CH + 16 * (k >> 2) + 4 * g + (k & 3);
-      R.o[k] = dog[(seq0 + (size_t)min(t, T - 1) * H) * DV + col];
+      o[k] = dog[(seq0 + (size_t)min(t, T - 1) * H) * DV + col];
     }
   };
-  auto stage = [&](const Rec& R, int t0) __attribute__((always_inline)) {
-    float G = 0.f, GC = 0.f;
-    if constexpr (SD) {
-      G = sd_scan(p.f, R.sd, t0, lane);
-      GC = lane_value(G, 63);
-    }
-#pragma unroll
-    for (int u = 0; u < NQ_E; ++u) {
-      const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + 4 * qk + qj;
-      f32x4 eb, qgm;
-      if constexpr (SD) {
-        // token 4 t4 + j, channels 4 k .. + 3: E_bar and Q_gamma for the
-        // transpose, K_tail as a row piece
-        const int tq = 4 * t4 + qj, cq4 = 64 * (blk % (DK / 64)) + 4 * qk;
-        const f32x4 k4 = widen(R.kr[u]);
-        sd_rows(p.f, G, R.sd, tq, t0, k4, widen(R.qr[u]), R.bq[u], eb, qgm);
-        *reinterpret_cast<f32x4*>(sKt + tq * SE + cq4) = sd_ktail(p.f, G, GC, tq, t0, k4);
-      } else {
-        const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
-        *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
-        eb = R.eb[u];
-        qgm = R.qg[u];
-      }
-      *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(qgm, qj);
-      *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(eb, qj);
-    }
-#pragma unroll
-    for (int u = 0; u < NQ_A; ++u) {
-      const int t4 = wave + 4 * u, cq = 4 * qk + qj;
-      *reinterpret_cast<f32x4*>(sAT + cq * SA + 4 * t4) = quad_transpose(R.a[u], qj);
-      *reinterpret_cast<f32x4*>(sAqT + cq * SA + 4 * t4) = quad_transpose(R.aq[u], qj);
-    }
-    if (tid < DK) sGC[tid] = SD ? fexp(GC) : R.gc;
-  };
-
-  Rec R;
-  if (N > 0) load(N - 1, R);
+  if (N > 0) load_o(N - 1);
+  __syncthreads();  // set A of the last chunk is staged
   for (int n = N - 1; n >= 0; --n) {
     const size_t ch = (size_t)bh * N + n;
-    __syncthreads();  // every read of the later chunk's LDS records is done
-    stage(R, n * CH);
     float dO[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) dO[k] = n * CH + 16 * (k >> 2) + 4 * g + (k & 3) < T ? (float)R.o[k] : 0.f;
-    __syncthreads();
-    if (n > 0) load(n - 1, R);
+    for (int k = 0; k < 16; ++k) dO[k] = n * CH + 16 * (k >> 2) + 4 * g + (k & 3) < T ? (float)o[k] : 0.f;
+    if (n > 0) load_o(n - 1);
     // the gradient of the state leaving this chunk, for the product pass
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -234,18 +305,18 @@ void bwd_state_mfma_kernel(BwdParams p) {
     f32x4 dW[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      // (the K_tail fragments of the row block requested together; the two
-      // products in two accumulators)
-      f32x4 ak[NB];
+      // (the fragments of the row block requested together; the two products
+      // in two accumulators)
+      f32x4 ak[NB], aa[4];
 #pragma unroll
       for (int b = 0; b < NB; ++b) ak[b] = *reinterpret_cast<const f32x4*>(sKt + (16 * I + l16) * SE + 16 * b + 4 * g);
+#pragma unroll
+      for (int J = I; J < 4; ++J) aa[J] = *reinterpret_cast<const f32x4*>(sAqT + (16 * I + l16) * SA + 16 * J + 4 * g);
       f32x4 w = {0.f, 0.f, 0.f, 0.f}, w2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = I; J < 4; ++J) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sAqT + (16 * I + l16) * SA + 16 * J + 4 * g);
+      for (int J = I; J < 4; ++J)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w2 = mfma_f32(a[r], dO[4 * J + r], w2);
-      }
+        for (int r = 0; r < 4; ++r) w2 = mfma_f32(aa[J][r], dO[4 * J + r], w2);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -255,21 +326,21 @@ void bwd_state_mfma_kernel(BwdParams p) {
     // ---- dR = A^T dW, block rows from the first (each reads dW blocks J >= I) ----
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 r4 = {0.f, 0.f, 0.f, 0.f}, aa[4];
 #pragma unroll
-      for (int J = I; J < 4; ++J) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sAT + (16 * I + l16) * SA + 16 * J + 4 * g);
+      for (int J = I; J < 4; ++J) aa[J] = *reinterpret_cast<const f32x4*>(sAT + (16 * I + l16) * SA + 16 * J + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) r4 = mfma_f32(a[r], dW[J][r], r4);
-      }
+      for (int J = I; J < 4; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r4 = mfma_f32(aa[J][r], dW[J][r], r4);
       dW[I] = r4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ws.dR[(ch * CH + 16 * I + 4 * g + r) * DV + col] = r4[r];
     }
+    __syncthreads();  // set B of this chunk is staged; set A is free
     // ---- dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR -----------------------
     // (dR negated once; each block's eight fragments requested together; the
-    // two products in two accumulators, so that consecutive MFMAs do not
-    // wait on each other)
+    // two products in two accumulators)
     f32x4 ndR[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) ndR[J] = -dW[J];
@@ -292,6 +363,7 @@ void bwd_state_mfma_kernel(BwdParams p) {
         }
       dS[b] = sq + se;
     }
+    __syncthreads();  // set A of the next chunk is staged; set B is free
   }
   if (p.dstate) {
 #pragma unroll
