@@ -33,10 +33,10 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
     ChunkParams f64 = p.f;
     f64.nslices = DV / 64;
     if (sd)
-      hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, true>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64,
+      hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, true>), dim3(BH * f64.nslices), dim3(2 * NTHR), 0, s, f64,
                          p.ws);
     else
-      hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, false>), dim3(BH * f64.nslices), dim3(NTHR), 0, s, f64,
+      hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, true, false>), dim3(BH * f64.nslices), dim3(2 * NTHR), 0, s, f64,
                          p.ws);
   }
   if (sd) hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, true>), dim3(BH * (DV / 64)), dim3(2 * NTHR), 0, s, p);

@@ -53,8 +53,8 @@ hipError_t plain_split_sequence(const ChunkParams& p, const BwdWs& ws, int dvs, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dvs == 64) {
-    if (sd) hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false, true>), dim3(grid), dim3(NTHR), 0, s, p, ws);
-    else hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
+    if (sd) hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false, true>), dim3(grid), dim3(2 * NTHR), 0, s, p, ws);
+    else hipLaunchKernelGGL((plain_mrec_kernel<IO, DK, false, false>), dim3(grid), dim3(2 * NTHR), 0, s, p, ws);
   } else {
     hipLaunchKernelGGL((plain_rec_kernel<IO, DK, 16, false>), dim3(grid), dim3(NTHR), 0, s, p, ws);
   }

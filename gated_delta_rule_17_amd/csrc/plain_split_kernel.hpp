@@ -632,9 +632,9 @@ namespace gdr {
 // ---- pass 2 on the matrix cores ---------------------------------------------
 // The same recurrence with every product on v_mfma_f32_16x16x4_f32 (fp32
 // operands, fp32 accumulation), for every gate kind but the per-value-channel
-// beta: one workgroup of four waves per (batch, head, 64-column slice), wave
-// w owning columns 16 w .. + 15 and the state S of those columns in
-// accumulators: register r of block b of lane l holds
+// beta: one workgroup of eight waves per (batch, head, 64-column slice).
+// Waves 0-3 compute: wave w owns columns 16 w .. + 15 and the state S of
+// those columns in accumulators: register r of block b of lane l holds
 // S[16 b + 4 (l / 16) + r][16 w + l % 16].
 //
 // Each product contracts over 4-wide k-steps; k-step (b, r) takes, in lane
@@ -646,8 +646,13 @@ namespace gdr {
 //   W       = A (Z - ES)                  A = A rows (token x token), lower blocks only
 //   O       = QS + Aqk W                  A = Aqk rows
 //   S      <- Diag(gamma_C) S + K_tail^T W   A = K_tail^T rows (channel x token)
-// The chunk's records go to LDS once per chunk (K_tail transposed on the
-// way); the next chunk's are loaded into registers while this one computes.
+// Waves 4-7 stage a chunk's records in LDS in two sets, each written while
+// the computing waves read the other: set B (K_tail^T, transposed on the way,
+// and gamma_C) of chunk n while they form W and O of chunk n, set A (E_bar,
+// Q_gamma, A, Aqk) of chunk n + 1 while they update the state.  Each set's
+// inputs are loaded into the staging waves' registers a phase before they
+// are staged.  A computing wave and a staging wave share each SIMD, so the
+// staging arithmetic runs beside the MFMAs instead of between them.
 template <int DK>
 struct PlainMrecLay {
   static constexpr int SE = DK + 4;  // rows of E_bar, Q_gamma (16-byte rows; 4 banks apart)
@@ -724,12 +729,12 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // SD: a scalar decay or none; the factor rows are formed from the inputs
 // (sd_rows) rather than read from the workspace.
 template <class IO, int DK, bool REC = false, bool SD = false>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
   using L = PlainMrecLay<DK>;
   constexpr int SE = L::SE, SA = L::SA, NB = DK / 16;
   constexpr int DVS = 64;
-  constexpr int NQ_E = CH * DK / 4 / NTHR;  // 16-byte pieces per thread of a [64][DK] record array
+  constexpr int NQ_E = CH * DK / 4 / NTHR;  // 16-byte pieces per staging thread of a [64][DK] record array
   constexpr int NQ_A = CH * CH / 4 / NTHR;  // of a [64][64] array
   __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
   float* sEb = lds + L::oEb;
@@ -750,126 +755,180 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
   const int bb = bh / p.H, hh = bh - bb * p.H;
   const int T = p.T, H = p.H, DV = p.DV;
   const int N = (T + CH - 1) / CH;
+  const size_t seq0 = (size_t)bb * T * H + hh;
+
+  if (wave >= 4) {
+    // ================= staging waves =================
+    const int st = tid - NTHR, sw = wave - 4;  // thread and wave within the staging group
+    const int qj = lane & 3, qk = lane >> 2;
+    const IO* kin = reinterpret_cast<const IO*>(p.k);
+    const IO* qin = reinterpret_cast<const IO*>(p.q);
+    // set A: E_bar, Q_gamma (SD: from the raw k, q and the per-channel erase
+    // gate), A, Aqk (the record mode reads neither Q_gamma nor Aqk); set B:
+    // K_tail (SD: from the raw k), gamma_C.  The pieces
+    // of the [64][DK] arrays are in the quad layout: lane (k, j) = (lane / 4,
+    // lane % 4) of staging wave w takes token 4 t4 + j, channels 4 k .. + 3 of
+    // a block of 4 tokens x 64 channels, E_bar and Q_gamma as row pieces and
+    // K_tail through the quad transpose (channel 4 k + j, tokens 4 t4 .. + 3
+    // as one 16-byte LDS write; the wave's 64 channel rows fall in distinct
+    // banks).
+    struct RecA {
+      typename Raw<IO>::v4 kr[SD ? NQ_E : 1], qr[SD ? NQ_E : 1];
+      f32x4 eb[SD ? 1 : NQ_E], qg[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[REC ? 1 : NQ_A];
+      SdLane sd;
+    };
+    struct RecB {
+      typename Raw<IO>::v4 kr[SD ? NQ_E : 1];
+      f32x4 kt[SD ? 1 : NQ_E];
+      float gc;
+      SdLane sd;
+    };
+    auto piece = [&](int u, int& t, int& c) __attribute__((always_inline)) {
+      const int blk = sw + 4 * u;
+      t = 4 * (blk / (DK / 64)) + qj;
+      c = 64 * (blk % (DK / 64)) + 4 * qk;
+    };
+    auto load_a = [&](int n, RecA& R) __attribute__((always_inline)) {
+      const size_t ch = (size_t)bh * N + n;
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        if constexpr (SD) {
+          int t, c;
+          piece(u, t, c);
+          const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
+          R.kr[u] = ldraw4(kin + tokq * DK + c);
+          R.qr[u] = ldraw4(qin + tokq * DK + c);
+          if (p.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.b + tokq * DK + c);
+        } else {
+          const size_t o = ch * CH * DK + 4 * (st + NTHR * u);
+          R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
+          if constexpr (!REC) R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
+        }
+      }
+      if constexpr (SD) R.sd = sd_lane_load(p, seq0, n * CH, hh, lane);
+#pragma unroll
+      for (int u = 0; u < NQ_A; ++u) {
+        const size_t o = ch * CH * CH + 4 * (st + NTHR * u);
+        R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
+        if constexpr (!REC) R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
+      }
+    };
+    auto load_b = [&](int n, RecB& R) __attribute__((always_inline)) {
+      const size_t ch = (size_t)bh * N + n;
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        int t, c;
+        piece(u, t, c);
+        if constexpr (SD) R.kr[u] = ldraw4(kin + (seq0 + (size_t)min(n * CH + t, T - 1) * H) * DK + c);
+        else R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + (size_t)t * DK + c);
+      }
+      if constexpr (SD) R.sd = sd_lane_load(p, seq0, n * CH, hh, lane);
+      else R.gc = st < DK ? ws.gC[ch * DK + st] : 0.f;
+    };
+    auto stage_a = [&](const RecA& R, int t0) __attribute__((always_inline)) {
+      float G = 0.f;
+      if constexpr (SD) G = sd_scan(p, R.sd, t0, lane);
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        if constexpr (SD) {
+          int tq, cq4;
+          piece(u, tq, cq4);
+          f32x4 eb, qgm;
+          sd_rows(p, G, R.sd, tq, t0, widen(R.kr[u]), widen(R.qr[u]), R.bq[u], eb, qgm);
+          *reinterpret_cast<f32x4*>(sEb + tq * SE + cq4) = eb;
+          if constexpr (!REC) *reinterpret_cast<f32x4*>(sQg + tq * SE + cq4) = qgm;
+        } else {
+          const int e = 4 * (st + NTHR * u), t = e / DK, c = e - t * DK;
+          *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
+          if constexpr (!REC) *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NQ_A; ++u) {
+        const int e = 4 * (st + NTHR * u), t = e / CH, c = e - t * CH;
+        *reinterpret_cast<f32x4*>(sA + t * SA + c) = R.a[u];
+        if constexpr (!REC) *reinterpret_cast<f32x4*>(sAq + t * SA + c) = R.aq[u];
+      }
+    };
+    auto stage_b = [&](const RecB& R, int t0) __attribute__((always_inline)) {
+      float G = 0.f, GC = 0.f;
+      if constexpr (SD) {
+        G = sd_scan(p, R.sd, t0, lane);
+        GC = lane_value(G, 63);
+      }
+#pragma unroll
+      for (int u = 0; u < NQ_E; ++u) {
+        const int blk = sw + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + lane;
+        f32x4 kt;
+        if constexpr (SD) {
+          int tq, cq4;
+          piece(u, tq, cq4);
+          kt = sd_ktail(p, G, GC, tq, t0, widen(R.kr[u]));
+        } else {
+          kt = R.kt[u];
+        }
+        *reinterpret_cast<f32x4*>(sKtT + cq * SA + 4 * t4) = quad_transpose(kt, qj);
+      }
+      if (st < DK) sGC[st] = SD ? fexp(GC) : R.gc;
+    };
+
+    RecA Ra;
+    RecB Rb;
+    if (N > 0) {
+      load_a(0, Ra);
+      load_b(0, Rb);
+      stage_a(Ra, 0);
+    }
+    __syncthreads();  // set A of the first chunk is staged
+    for (int n = 0; n < N; ++n) {
+      // phase 1 of chunk n (the computing waves read set A): set B of chunk n
+      if (n + 1 < N) load_a(n + 1, Ra);
+      stage_b(Rb, n * CH);
+      __syncthreads();
+      // phase 2 of chunk n (they read set B): set A of chunk n + 1
+      if (n + 1 < N) {
+        load_b(n + 1, Rb);
+        stage_a(Ra, (n + 1) * CH);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ================= computing waves =================
   const int write = p.write;
   const int col = slice * DVS + 16 * wave + l16;  // this lane's value column
-  const size_t seq0 = (size_t)bb * T * H + hh;
   const IO* vg = reinterpret_cast<const IO*>(p.v);
   IO* og = reinterpret_cast<IO*>(p.o);
-
   f32x4 S[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       S[b][r] = p.state_in ? p.state_in[((size_t)bh * DK + 16 * b + 4 * g + r) * DV + col] : 0.f;
-
-  // registers of a chunk's records and of this lane's z inputs (SD: eb, qg
-  // hold the raw k, q and bq the per-channel erase gate, all in the quad
-  // layout below, and sd this lane's token scalars)
-  struct Rec {
-    typename Raw<IO>::v4 kr[SD ? NQ_E : 1], qr[SD ? NQ_E : 1];
-    f32x4 eb[SD ? 1 : NQ_E], qg[SD ? 1 : NQ_E], kt[SD ? 1 : NQ_E], bq[SD ? NQ_E : 1], a[NQ_A], aq[NQ_A];
-    float gc;
-    SdLane sd;
-    IO v[16];      // rows 16 I + 4 g + r of this lane's column
-    float gt[16];
+  // this lane's z inputs, rows 16 I + 4 g + r of its column, a chunk ahead
+  IO v[16];
+  float gt[16];
+  auto load_z = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const size_t tok = seq0 + (size_t)min(n * CH + 16 * (k >> 2) + 4 * g + (k & 3), T - 1) * H;
+      v[k] = vg[tok * DV + col];
+      gt[k] = *(write == 1 ? p.w + tok * DV + col : p.beta + tok);  // (one load either way)
+    }
   };
-  const IO* kin = reinterpret_cast<const IO*>(p.k);
-  const IO* qin = reinterpret_cast<const IO*>(p.q);
-  auto load = [&](int n, Rec& R) __attribute__((always_inline)) {
-    const size_t ch = (size_t)bh * N + n;
-#pragma unroll
-    for (int u = 0; u < NQ_E; ++u) {
-      // K_tail is staged transposed: lane (k, j) = (lane / 4, lane % 4) of
-      // wave w takes token 4 t4 + j, channels 4 k .. + 3 of a block of 4
-      // tokens x 64 channels; the quad transposes it in stage()
-      const int blk = wave + 4 * u, t = 4 * (blk / (DK / 64)) + (lane & 3), c = 64 * (blk % (DK / 64)) + 4 * (lane >> 2);
-      if constexpr (SD) {
-        // (k, q, b of the same token and channels serve E_bar and Q_gamma
-        // as row pieces and K_tail through the transpose)
-        const size_t tokq = seq0 + (size_t)min(n * CH + t, T - 1) * H;
-        R.kr[u] = ldraw4(kin + tokq * DK + c);
-        R.qr[u] = ldraw4(qin + tokq * DK + c);
-        if (p.erase == 1) R.bq[u] = *reinterpret_cast<const f32x4*>(p.b + tokq * DK + c);
-      } else {
-        const size_t o = ch * CH * DK + 4 * (tid + NTHR * u);
-        R.eb[u] = *reinterpret_cast<const f32x4*>(ws.Eb + o);
-        R.qg[u] = *reinterpret_cast<const f32x4*>(ws.Qg + o);
-        R.kt[u] = *reinterpret_cast<const f32x4*>(ws.Kt + ch * CH * DK + (size_t)t * DK + c);
-      }
-    }
-    if constexpr (SD) R.sd = sd_lane_load(p, seq0, n * CH, hh, lane);
-#pragma unroll
-    for (int u = 0; u < NQ_A; ++u) {
-      const size_t o = ch * CH * CH + 4 * (tid + NTHR * u);
-      R.a[u] = *reinterpret_cast<const f32x4*>(ws.T + o);
-      if constexpr (!REC) R.aq[u] = *reinterpret_cast<const f32x4*>(ws.A + o);
-    }
-    if constexpr (!SD) R.gc = tid < DK ? ws.gC[ch * DK + tid] : 0.f;
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int k = 4 * I + r;
-        const size_t tok = seq0 + (size_t)min(n * CH + 16 * I + 4 * g + r, T - 1) * H;
-        R.v[k] = vg[tok * DV + col];
-        R.gt[k] = *(write == 1 ? p.w + tok * DV + col : p.beta + tok);  // (one load either way)
-      }
-  };
-  auto stage = [&](const Rec& R, int t0) __attribute__((always_inline)) {
-    float G = 0.f, GC = 0.f;
-    if constexpr (SD) {
-      G = sd_scan(p, R.sd, t0, lane);
-      GC = lane_value(G, 63);
-    }
-#pragma unroll
-    for (int u = 0; u < NQ_E; ++u) {
-      const int blk = wave + 4 * u, t4 = blk / (DK / 64), cq = 64 * (blk % (DK / 64)) + lane;
-      f32x4 kt;
-      if constexpr (SD) {
-        // token 4 t4 + j, channels 4 k .. + 3 of the block: a row piece of
-        // E_bar and Q_gamma, and K_tail for the transpose
-        const int tq = 4 * t4 + (lane & 3), cq4 = 64 * (blk % (DK / 64)) + 4 * (lane >> 2);
-        const f32x4 k4 = widen(R.kr[u]);
-        f32x4 eb, qgm;
-        sd_rows(p, G, R.sd, tq, t0, k4, widen(R.qr[u]), R.bq[u], eb, qgm);
-        kt = sd_ktail(p, G, GC, tq, t0, k4);
-        *reinterpret_cast<f32x4*>(sEb + tq * SE + cq4) = eb;
-        *reinterpret_cast<f32x4*>(sQg + tq * SE + cq4) = qgm;
-      } else {
-        const int e = 4 * (tid + NTHR * u), t = e / DK, c = e - t * DK;
-        kt = R.kt[u];
-        *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
-        *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
-      }
-      // channel 4 k + j of the block, tokens 4 t4 .. + 3: one 16-byte write
-      // (the wave's 64 channel rows fall in distinct banks)
-      *reinterpret_cast<f32x4*>(sKtT + cq * SA + 4 * t4) = quad_transpose(kt, lane & 3);
-    }
-#pragma unroll
-    for (int u = 0; u < NQ_A; ++u) {
-      const int e = 4 * (tid + NTHR * u), t = e / CH, c = e - t * CH;
-      *reinterpret_cast<f32x4*>(sA + t * SA + c) = R.a[u];
-      if constexpr (!REC) *reinterpret_cast<f32x4*>(sAq + t * SA + c) = R.aq[u];
-    }
-    if (tid < DK) sGC[tid] = SD ? fexp(GC) : R.gc;
-  };
-
-  Rec R;
-  if (N > 0) load(0, R);
+  if (N > 0) load_z(0);
+  __syncthreads();  // set A of the first chunk is staged
   for (int n = 0; n < N; ++n) {
     const int t0 = n * CH;
     const size_t ch = (size_t)bh * N + n;
-    __syncthreads();  // every read of the previous chunk's LDS records is done
-    stage(R, t0);
     float z[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const bool ok = t0 + 16 * (k >> 2) + 4 * g + (k & 3) < T;  // row 16 I + 4 g + r, k = 4 I + r
-      z[k] = ok ? R.gt[k] * (float)R.v[k] : 0.f;
+      z[k] = ok ? gt[k] * (float)v[k] : 0.f;
     }
-    __syncthreads();
-    if (n + 1 < N) load(n + 1, R);
+    if (n + 1 < N) load_z(n + 1);
     if constexpr (REC) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -931,6 +990,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
         }
       }
     }
+    __syncthreads();  // set B of this chunk is staged; set A is free
     // ---- S <- Diag(gamma_C) S + K_tail^T W ---------------------------------------
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -944,6 +1004,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       }
       S[b] = s;
     }
+    __syncthreads();  // set A of the next chunk is staged; set B is free
   }
   if (p.state_out) {
 #pragma unroll
