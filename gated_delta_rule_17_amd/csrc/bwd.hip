@@ -42,11 +42,15 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
   if (sd) hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, true>), dim3(BH * (DV / 64)), dim3(2 * NTHR), 0, s, p);
   else hipLaunchKernelGGL((bwd_state_mfma_kernel<IO, DK, false>), dim3(BH * (DV / 64)), dim3(2 * NTHR), 0, s, p);
   if (N > 0) {
-    hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
-    // the key pass: on the matrix cores under a scalar decay (or none), per
-    // term under a decay per key channel
-    if (p.f.decay == 2) hipLaunchKernelGGL((bwd_key_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
-    else hipLaunchKernelGGL((bwd_key_scalar_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
+    // the products over the value channels, then the key pass: per term
+    // under a decay per key channel; under a scalar decay (or none) both in
+    // one kernel, on the matrix cores
+    if (p.f.decay == 2) {
+      hipLaunchKernelGGL((bwd_prod_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
+      hipLaunchKernelGGL((bwd_key_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((bwd_prodkey_kernel<IO, DK, DV>), dim3(BH * N), dim3(NTHR), 0, s, p);
+    }
   }
   if (p.f.qmix == 1)
     hipLaunchKernelGGL(bwd_lam_reduce_kernel, dim3(p.f.H), dim3(256), 0, s, p.ws.dlam, p.dlam, p.f.B, p.f.T, p.f.H);

@@ -780,33 +780,43 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
   key_tail<IO, DK, DV, NPASS>(p, ch, t0, seq0, tid, sBeta, sRz, nullptr, sRb, sRl);
 }
 
-// Pass B2 under a scalar decay (or none): d_ij = exp(G_i - G_j) is one
-// number per token pair, so with D1 = dT (.) D and D2 = dA_qk (.) D (strictly
-// lower; the diagonal of dA_qk kept apart) the four sums are products of 64 x
-// 64 matrices, run on v_mfma_f32_16x16x4_f32 per pass of 32 key channels:
-//   P = D1 K,  Pq = D2 K,  Rm = D1^T E,  Rq = D2^T Q
-// Wave w owns row block w (its P, Pq over column blocks J <= w, its Rm, Rq
-// over J >= w: the same MFMA count for every wave).  k-step (J, r) takes, in
-// lane group g, the token 16 J + 4 g + r.  The A operands of P and Pq are
-// rows of D1 and D2 (one 16-byte LDS read feeds four MFMAs), those of Rm and
-// Rq their columns (four 4-byte reads: no transposed copy is kept), the B
-// operands rows of K^T, E^T, Q^T (the pass's columns staged transposed).
-// Lane (g, l) then holds rows 16 w + 4 g + r of channel 16 C + l of each
-// column block C; a row's sums over the channels end in a DPP sum over the 16
-// lanes of its group.  65 KB of LDS and at most 256 registers per lane: two
-// workgroups share a CU, so that one computes while the other waits for its
-// loads.
+// ---- passes B1 and B2 in one kernel, under a scalar decay (or none) ---------
+// One workgroup of four waves per (batch, head, chunk), two per CU.  Phase 1
+// is the product pass (bwd_prod_kernel's quarters of 32 value channels),
+// together with the value side (dv, dw, and the rows' sums of dZ (.) v);
+// phase 2 is the key pass under a scalar decay in passes of 32 key channels,
+// as bwd_key_scalar_kernel would run it, but dT and dA_qk go from phase 1's
+// accumulators straight to LDS as D1 = dT (.) D and D2 = dA_qk (.) D, and
+// dE_bar, dQ_gamma, dK_tail stay in the accumulators: the lane that holds
+// row 16 w + 4 g + r of column 16 c + l of dE_bar after phase 1 is the lane
+// that needs it in phase 2.  None of the five products goes to the workspace
+// and comes back (256 KB per chunk at dk = dv = 128).  Phase 2's arrays
+// overlay phase 1's.
+template <int DK>
+struct BwdPKLay {
+  static constexpr int VH = 32, SP = VH + 4;  // phase 1: a quarter's [rows][32] arrays
+  static constexpr int oR = 0, oO = oR + CH * SP, oW = oO + CH * SP, oS = oW + CH * SP, odS = oS + DK * SP;
+  static constexpr int P1 = odS + DK * SP;
+  static constexpr int KC = 32, TP = CH + 4;  // phase 2: D1, D2 and a pass's K^T, E^T, Q^T
+  static constexpr int oD1 = 0, oD2 = oD1 + CH * TP, oKT = oD2 + CH * TP, oET = oKT + KC * TP, oQT = oET + KC * TP;
+  static constexpr int P2 = oQT + KC * TP;
+  static constexpr int TOTAL = P1 > P2 ? P1 : P2;
+  static constexpr int SMALL = (2 * CH * (DK / KC) + 8 * CH + DK) * 4;  // the per-row and per-channel arrays
+  static_assert(2 * (TOTAL * 4 + SMALL) <= 160 * 1024, "two workgroups per CU");
+};
+
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_key_scalar_kernel(BwdParams p) {
-  constexpr int KC = 32, NPASS = DK / KC, NCB = KC / 16;
-  constexpr int VW = DV / 64;
-  constexpr int TP = CH + 4;  // 16-byte rows; 4-bank shift per row
-  static_assert(DK % KC == 0 && NTHR == 256, "key channels in passes of 32, four waves");
-  __shared__ __attribute__((aligned(16))) float sD1[CH * TP], sD2[CH * TP];
-  __shared__ __attribute__((aligned(16))) float sKT[KC * TP], sET[KC * TP], sQT[KC * TP];
-  __shared__ float sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH][VW], sDg[CH];
+void bwd_prodkey_kernel(BwdParams p) {
+  using L = BwdPKLay<DK>;
+  constexpr int VH = L::VH, SP = L::SP, NC = DK / 16;
+  constexpr int KC = L::KC, TP = L::TP, NPASS = DK / KC, NCB = KC / 16;
+  static_assert(DV % VH == 0 && DK % KC == 0 && NTHR == 256, "quarters of 32 value channels, passes of 32 key channels");
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  __shared__ float sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH], sDg[CH], sSC[DK];
   __shared__ float sBeta[CH], sLam[CH], sGt[CH], sDiag[CH], sRG[CH], sRX[CH];
+  float *sR = lds + L::oR, *sO = lds + L::oO, *sW = lds + L::oW, *sS = lds + L::oS, *sdS = lds + L::odS;
+  float *sD1 = lds + L::oD1, *sD2 = lds + L::oD2, *sKT = lds + L::oKT, *sET = lds + L::oET, *sQT = lds + L::oQT;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -817,25 +827,18 @@ void bwd_key_scalar_kernel(BwdParams p) {
   const int bb = bh / p.f.H, hh = bh - bb * p.f.H;
   const int T = p.f.T, H = p.f.H;
   const int t0 = n * CH;
-  const int decay = p.f.decay, erase = p.f.erase, qmix = p.f.qmix;
+  const int decay = p.f.decay, erase = p.f.erase, write = p.f.write, qmix = p.f.qmix;
   const size_t seq0 = (size_t)bb * T * H + hh;
   const IO* qg = reinterpret_cast<const IO*>(p.f.q);
   const IO* kg = reinterpret_cast<const IO*>(p.f.k);
+  const IO* vg = reinterpret_cast<const IO*>(p.f.v);
+  const IO* dog = reinterpret_cast<const IO*>(p.d_o);
   const BwdWs& ws = p.ws;
 
-  // the chunk's dT and dA_qk, four 16-byte pieces of each per thread,
-  // requested first
-  constexpr int NQD = CH * CH / 4 / NTHR;
-  f32x4 xt[NQD], xa[NQD];
-#pragma unroll
-  for (int u = 0; u < NQD; ++u) {
-    xt[u] = *reinterpret_cast<const f32x4*>(ws.T + ch * CH * CH + 4 * (tid + NTHR * u));
-    xa[u] = *reinterpret_cast<const f32x4*>(ws.A + ch * CH * CH + 4 * (tid + NTHR * u));
-  }
   for (int r = tid; r < CH; r += NTHR) {
     const int t = t0 + r;
     const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
-    sBeta[r] = (t < T && (erase == 0 || p.f.write == 0)) ? p.f.beta[tok] : 0.f;
+    sBeta[r] = (t < T && (erase == 0 || write == 0)) ? p.f.beta[tok] : 0.f;
     sLam[r] = (t < T && qmix) ? (qmix == 2 ? p.f.lam[tok] : p.f.lam[hh]) : 0.f;
     sDg[r] = 0.f;
     sRG[r] = 0.f;
@@ -847,23 +850,153 @@ void bwd_key_scalar_kernel(BwdParams p) {
     const float gv = (decay == 1 && t < T) ? p.f.g[seq0 + (size_t)t * H] : 0.f;
     sGt[tid] = wave_incl_scan(gv);
   }
-  __syncthreads();
-  // D1, D2 strictly below the diagonal, the diagonal of dA_qk kept apart
+
+  // ================= phase 1: the products over the value channels ==========
+  // Wave w owns row block w (rows 16 w .. + 15) of every output: dT and
+  // dA_qk (blocks J <= w), dE_bar, dQ_gamma, dK_tail (all DK / 16 column
+  // blocks); k-step (b, r) takes, in lane group g, the value channel
+  // 16 b + 4 g + r of the quarter, so both operands are 16-byte LDS reads of
+  // rows.  The value side takes the thread's dR pieces of the quarter (row
+  // r, channels c4 .. + 3) from its staging registers.
+  constexpr int QR = CH * VH / 4 / NTHR, QS = DK * VH / 4 / NTHR;
+  f32x4 aT[4], aA[4], aE[NC], aQ[NC], aK[NC];
 #pragma unroll
-  for (int u = 0; u < NQD; ++u) {
-    const int e = tid + NTHR * u, i = e >> 4, j0 = (e & 15) * 4;
-    const float Gi = sGt[i];
-    f32x4 d1, d2;
+  for (int J = 0; J < 4; ++J) aT[J] = aA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int j = j0 + k;
-      const float d = j < i ? fexp(Gi - sGt[j]) : 0.f;
-      d1[k] = xt[u][k] * d;
-      d2[k] = xa[u][k] * d;
-      if (j == i) sDiag[i] = xa[u][k];
+  for (int c = 0; c < NC; ++c) aE[c] = aQ[c] = aK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float sc = 0.f;          // sum_v S (.) dS of channel tid / TPC, a run of each quarter
+  float zrow[QR] = {};     // sum_v dZ (.) v of the thread's pieces (the beta write gate)
+  for (int vh = 0; vh < DV; vh += VH) {
+    if (vh > 0) __syncthreads();  // the previous quarter's reads are done
+    f32x4 xr[QR], xo[QR], xw[QR], xs[QS], xd[QS], wv[QR];
+    typename Raw<IO>::v4 vv[QR];
+#pragma unroll
+    for (int u = 0; u < QR; ++u) {
+      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+      const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+      xr[u] = *reinterpret_cast<const f32x4*>(ws.dR + (ch * CH + r) * DV + vh + c4);
+      xw[u] = *reinterpret_cast<const f32x4*>(ws.W + (ch * CH + r) * DV + vh + c4);
+      xo[u] = ldf4(dog + tok * DV + vh + c4);
+      vv[u] = ldraw4(vg + tok * DV + vh + c4);
+      if (write == 1) wv[u] = *reinterpret_cast<const f32x4*>(p.f.w + tok * DV + vh + c4);
     }
-    *reinterpret_cast<f32x4*>(sD1 + i * TP + j0) = d1;
-    *reinterpret_cast<f32x4*>(sD2 + i * TP + j0) = d2;
+#pragma unroll
+    for (int u = 0; u < QS; ++u) {
+      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+      xs[u] = *reinterpret_cast<const f32x4*>(ws.S + (ch * DK + r) * DV + vh + c4);
+      xd[u] = *reinterpret_cast<const f32x4*>(ws.dS + (ch * DK + r) * DV + vh + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < QR; ++u) {
+      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+      if (t0 + r >= T) xo[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(sR + r * SP + c4) = xr[u];
+      *reinterpret_cast<f32x4*>(sO + r * SP + c4) = xo[u];
+      *reinterpret_cast<f32x4*>(sW + r * SP + c4) = xw[u];
+    }
+#pragma unroll
+    for (int u = 0; u < QS; ++u) {
+      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+      *reinterpret_cast<f32x4*>(sS + r * SP + c4) = xs[u];
+      *reinterpret_cast<f32x4*>(sdS + r * SP + c4) = xd[u];
+    }
+    __syncthreads();  // (also: the per-row scalars are in place)
+    // ---- the value side: dZ = dR gives dv and, per write gate, dw or the
+    // rows' sums for dbeta
+#pragma unroll
+    for (int u = 0; u < QR; ++u) {
+      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+      const int t = t0 + r;
+      if (t < T) {
+        const size_t o = (seq0 + (size_t)t * H) * DV + vh + c4;
+        const f32x4 z = xr[u], v4 = widen(vv[u]);
+        if (write == 1) {
+          *reinterpret_cast<f32x4*>(p.dw + o) = z * v4;
+          *reinterpret_cast<f32x4*>(p.dv + o) = wv[u] * z;
+        } else {
+          zrow[u] += z[0] * v4[0] + z[1] * v4[1] + z[2] * v4[2] + z[3] * v4[3];
+          *reinterpret_cast<f32x4*>(p.dv + o) = sBeta[r] * z;
+        }
+      }
+    }
+    // ---- sC: channel tid / TPC, a run of the quarter
+    {
+      constexpr int TPC = NTHR / DK, RUN = VH / TPC;
+      const int c = tid / TPC, v0 = (tid % TPC) * RUN;
+#pragma unroll
+      for (int v = 0; v < RUN; v += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sS + c * SP + v0 + v);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(sdS + c * SP + v0 + v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc = __builtin_fmaf(a[i], b[i], sc);
+      }
+    }
+    // ---- the products of row block w over the quarter
+#pragma unroll
+    for (int b = 0; b < VH / 16; ++b) {
+      const int ko = 16 * b + 4 * g;
+      const f32x4 ar = *reinterpret_cast<const f32x4*>(sR + (16 * w + l16) * SP + ko);
+      const f32x4 ao = *reinterpret_cast<const f32x4*>(sO + (16 * w + l16) * SP + ko);
+      const f32x4 aw = *reinterpret_cast<const f32x4*>(sW + (16 * w + l16) * SP + ko);
+      // dT = -dR W^T, dA_qk = dO W^T: column blocks J <= w
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J > w) continue;  // wave-uniform
+        const f32x4 bw = *reinterpret_cast<const f32x4*>(sW + (16 * J + l16) * SP + ko);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          aT[J] = mfma_f32(ar[r], bw[r], aT[J]);
+          aA[J] = mfma_f32(ao[r], bw[r], aA[J]);
+        }
+      }
+      // dE_bar = -dR S^T, dQ_gamma = dO S^T, dK_tail = W dS^T
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x4 bs = *reinterpret_cast<const f32x4*>(sS + (16 * c + l16) * SP + ko);
+        const f32x4 bd = *reinterpret_cast<const f32x4*>(sdS + (16 * c + l16) * SP + ko);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          aE[c] = mfma_f32(ar[r], bs[r], aE[c]);
+          aQ[c] = mfma_f32(ao[r], bs[r], aQ[c]);
+          aK[c] = mfma_f32(aw[r], bd[r], aK[c]);
+        }
+      }
+    }
+  }
+  // the rows' sums of dZ (.) v: a row's 32 channels of a quarter lie in 8
+  // adjacent lanes
+#pragma unroll
+  for (int u = 0; u < QR; ++u) {
+    float z = zrow[u];
+    z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0xB1, 0xf, 0xf, true));
+    z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0x4E, 0xf, 0xf, true));
+    z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0x141, 0xf, 0xf, true));
+    if ((tid & 7) == 0) sRz[(tid + NTHR * u) / (VH / 4)] = z;
+  }
+  // sC: the channel's threads (adjacent lanes) combined
+  {
+    constexpr int TPC = NTHR / DK;
+    sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0xB1, 0xf, 0xf, true));
+    if constexpr (TPC == 4)
+      sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0x4E, 0xf, 0xf, true));
+    if (tid % TPC == 0) sSC[tid / TPC] = sc;
+  }
+  __syncthreads();  // phase 1's arrays are no longer read
+
+  // ================= phase 2: back to the rows =================
+  // D1, D2 strictly below the diagonal (the diagonal of dA_qk kept apart),
+  // from this wave's blocks J <= w; the blocks above are never read
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    if (J > w) continue;  // wave-uniform
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * g + r, j = 16 * J + l16;
+      const float d = j < i ? fexp(sGt[i] - sGt[j]) : 0.f;
+      sD1[i * TP + j] = -aT[J][r] * d;
+      sD2[i * TP + j] = aA[J][r] * d;
+      if (j == i) sDiag[i] = aA[J][r];
+    }
   }
   const float GC = sGt[CH - 1];
   // a row's sum over the 16 lanes of its group (quad permutations, then the
@@ -876,8 +1009,11 @@ void bwd_key_scalar_kernel(BwdParams p) {
     return x;
   };
 
+#pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
-    if (ps > 0) __syncthreads();  // the previous pass's columns are no longer read
+    // ps = 0: D1, D2 and the diagonal are in place; later: the previous
+    // pass's columns are no longer read
+    __syncthreads();
     // ---- this pass's columns of the chunk's rows, transposed (zero past T):
     // lane (h, k, j) = (lane / 32, lane / 4 % 8, lane % 4) of wave w takes
     // token 4 b + j (b = 2 (w + 4 u) + h), channels 4 k .. + 3 of the pass;
@@ -912,19 +1048,13 @@ void bwd_key_scalar_kernel(BwdParams p) {
         *reinterpret_cast<f32x4*>(sET + c * TP + 4 * b4) = quad_transpose(ev, qj);
       }
     }
-    // the product pass's results and the erase gate at my (row, channel)
-    // pairs, requested before the products
-    float dEb[NCB][4], dQg[NCB][4], dKt[NCB][4], bI[NCB][4];
+    // the erase gate at my (row, channel) pairs, requested before the products
+    float bI[NCB][4];
 #pragma unroll
     for (int C = 0; C < NCB; ++C)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * g + r, cg = ps * KC + 16 * C + l16;
-        const size_t at = (ch * CH + i) * DK + cg;
-        dEb[C][r] = ws.Eb[at];
-        dQg[C][r] = ws.Qg[at];
-        dKt[C][r] = ws.Kt[at];
-        const int t = t0 + i;
+        const int t = t0 + 16 * w + 4 * g + r, cg = ps * KC + 16 * C + l16;
         bI[C][r] = (erase == 1 && t < T) ? p.f.b[(seq0 + (size_t)t * H) * DK + cg] : 0.f;
       }
     __syncthreads();
@@ -978,7 +1108,7 @@ void bwd_key_scalar_kernel(BwdParams p) {
     float sg[4] = {0.f, 0.f, 0.f, 0.f}, sx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int C = 0; C < NCB; ++C) {
-      const int c = 16 * C + l16, cg = ps * KC + c;
+      const int c = 16 * C + l16, cg = ps * KC + c, cb = NCB * ps + C;  // cb: column block of phase 1
       const f32x4 kv = *reinterpret_cast<const f32x4*>(sKT + c * TP + 16 * w + 4 * g);
       const f32x4 ev = *reinterpret_cast<const f32x4*>(sET + c * TP + 16 * w + 4 * g);
       const f32x4 qv = *reinterpret_cast<const f32x4*>(sQT + c * TP + 16 * w + 4 * g);
@@ -986,14 +1116,15 @@ void bwd_key_scalar_kernel(BwdParams p) {
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * g + r;
         const float ki = kv[r], ei = ev[r], qi = qv[r];
+        const float dEb = -aE[cb][r], dQg = aQ[cb][r], dKt = aK[cb][r];
         const float P = aP[C][r], Pq = aPq[C][r], Rm = aRm[C][r], Rq = aRq[C][r];
         const float diag = sDiag[i];
-        const float de = __builtin_fmaf(gam[r], dEb[C][r], P);
-        float dqd = __builtin_fmaf(gam[r], dQg[C][r], __builtin_fmaf(diag, ki, Pq));
-        float dkd = tl[r] * dKt[C][r] + Rm + __builtin_fmaf(diag, qi, Rq);
+        const float de = __builtin_fmaf(gam[r], dEb, P);
+        float dqd = __builtin_fmaf(gam[r], dQg, __builtin_fmaf(diag, ki, Pq));
+        float dkd = tl[r] * dKt + Rm + __builtin_fmaf(diag, qi, Rq);
         // (the diagonal of A_qk stays out of dG: its two terms cancel exactly)
-        sg[r] += ei * gam[r] * dEb[C][r] + qi * gam[r] * dQg[C][r] + ei * P + qi * Pq - ki * (Rm + Rq);
-        sx[r] += ki * tl[r] * dKt[C][r];  // K_tail_i dK_tail_i
+        sg[r] += ei * gam[r] * dEb + qi * gam[r] * dQg + ei * P + qi * Pq - ki * (Rm + Rq);
+        sx[r] += ki * tl[r] * dKt;  // K_tail_i dK_tail_i
         const int t = t0 + i;
         const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
         if (erase == 1) {
@@ -1026,20 +1157,35 @@ void bwd_key_scalar_kernel(BwdParams p) {
       }
     }
   }
+  __syncthreads();
   // dg_t = sum_{r>=t} RG_r + sum_{j<t} RX_j + gamma_C sum_c sC[c] (the
   // per-channel form summed over the channels), by wave prefix sums
-  if (decay == 1) {
-    __syncthreads();
-    if (tid < CH) {
-      float sc = 0.f;
-      for (int c2 = tid; c2 < DK; c2 += CH) sc += ws.gC[ch * DK + c2];
-      const float base = fexp(sGt[CH - 1]) * wave_total(sc);
-      const float rg = sRG[tid], rx = sRX[tid];
-      const float ig = wave_incl_scan(rg), ix = wave_incl_scan(rx);
-      sDg[tid] = (lane_value(ig, 63) - ig + rg) + (ix - rx) + base;
-    }
+  if (decay == 1 && tid < CH) {
+    float s2 = 0.f;
+    for (int c2 = tid; c2 < DK; c2 += CH) s2 += sSC[c2];
+    const float base = fexp(GC) * wave_total(s2);
+    const float rg = sRG[tid], rx = sRX[tid];
+    const float ig = wave_incl_scan(rg), ix = wave_incl_scan(rx);
+    sDg[tid] = (lane_value(ig, 63) - ig + rg) + (ix - rx) + base;
   }
-  key_tail<IO, DK, DV, NPASS>(p, ch, t0, seq0, tid, sBeta, sRz, sDg, sRb, sRl);
+  __syncthreads();
+  // ---- per-token sums: the scalar-decay dg, dbeta, dlambda
+  for (int r = tid; r < CH; r += NTHR) {
+    const int t = t0 + r;
+    if (t >= T) continue;
+    const size_t tok = seq0 + (size_t)t * H;
+    if (decay == 1) p.dg[tok] = sDg[r];
+    float sb = 0.f, sl = 0.f;
+#pragma unroll
+    for (int q2 = 0; q2 < NPASS; ++q2) {
+      sb += sRb[r][q2];
+      sl += sRl[r][q2];
+    }
+    if (write == 0) sb += sRz[r];
+    if (erase == 0 || write == 0) p.dbeta[tok] = sb;
+    if (qmix == 2) p.dlam[tok] = sl;
+    else if (qmix == 1) ws.dlam[tok] = sl;
+  }
 }
 
 // ---- a per-head lambda: the sum of its per-token gradients ------------------
