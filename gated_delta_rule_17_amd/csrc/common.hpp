@@ -64,9 +64,9 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 __device__ __forceinline__ float wave_total(float x) { return lane_value(wave_incl_scan(x), 63); }
 
 // 4 x 4 transpose across the lanes of a quad: lane j of the quad holds row j
-// of a block in x; afterwards it holds column j.  Two exchange rounds with
-// the partners j ^ 1 and j ^ 2 (DPP quad permutations); element k is taken
-// from the partner where bit 0 (round 1) or bit 1 (round 2) of k ^ j is set.
+// of a block in x; afterwards it holds column j.  Two exchanges, with the
+// partners j ^ 1 and j ^ 2 (DPP quad permutations); element k is taken from
+// the partner where bit 0 (first exchange) or bit 1 (second) of k ^ j is set.
 __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
   auto from = [](float v, auto ctrl) __attribute__((always_inline)) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
