@@ -637,11 +637,17 @@ namespace gdr {
 // those columns in accumulators: register r of block b of lane l holds
 // S[16 b + 4 (l / 16) + r][16 w + l % 16].
 //
-// Each product contracts over 4-wide k-steps; k-step (b, r) takes, in lane
-// group g = l / 16, the channel (or token) 16 b + 4 g + r, which is where
-// that lane's accumulators hold it.  So the state, R, W and the other
-// accumulator tiles serve as B operands as they are, and the A operands are
-// 16-byte LDS reads of four consecutive channels (tokens) of one row:
+// Every product runs on bf16 matrix cores in split precision: each fp32
+// operand x is held as hi = bf16(x) and lo = bf16(x - hi), and a product
+// X Y is formed as Xhi Yhi + Xhi Ylo + Xlo Yhi (v_mfma_f32_16x16x32_bf16,
+// fp32 accumulation; the dropped Xlo Ylo and the roundings of lo leave about
+// 16 bits of each operand, against the 24 of fp32, at a sixth of the fp32
+// matrix instructions' time).  A 32-wide k-step m takes, in lane group
+// g = l / 16, the channels (or tokens) 32 m + 4 g + e and 32 m + 16 + 4 g + e
+// (e < 4): where that lane's accumulators hold them in the tiles 2m and
+// 2m + 1.  So the state, R, W and the other accumulator tiles serve as B
+// operands after the split, and the A operands are rows stored with their
+// k index in that order (kpos), one 16-byte LDS read per half and fragment:
 //   ES, QS  = E_bar S, Q_gamma S          A = E_bar, Q_gamma rows (token x channel)
 //   W       = A (Z - ES)                  A = A rows (token x token), lower blocks only
 //   O       = QS + Aqk W                  A = Aqk rows
@@ -649,23 +655,64 @@ namespace gdr {
 // Waves 4-7 stage a chunk's records in LDS in two sets, each written while
 // the computing waves read the other: set B (K_tail^T, transposed on the way,
 // and gamma_C) of chunk n while they form W and O of chunk n, set A (E_bar,
-// Q_gamma, A, Aqk) of chunk n + 1 while they update the state.  Each set's
+// Q_gamma, A, Aqk) of chunk n + 1 while they update the state; the staging
+// waves also split each record value into its two halves.  Each set's
 // inputs are loaded into the staging waves' registers a phase before they
 // are staged.  A computing wave and a staging wave share each SIMD, so the
 // staging arithmetic runs beside the MFMAs instead of between them.
 template <int DK>
 struct PlainMrecLay {
-  static constexpr int SE = DK + 4;  // rows of E_bar, Q_gamma (16-byte rows; 4 banks apart)
-  static constexpr int SA = CH + 4;  // rows of A, Aqk, K_tail^T
-  static constexpr int oEb = 0, oQg = oEb + CH * SE, oKtT = oQg + CH * SE;
-  static constexpr int oA = oKtT + DK * SA, oAq = oA + CH * SA, oGC = oAq + CH * SA;
-  static constexpr int TOTAL = oGC + DK;
-  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+  // bf16 rows (elements), hi and lo arrays of each operand; 16-row fragment
+  // reads of 16 bytes fall in distinct banks
+  static constexpr int SE = DK + 8;  // E_bar, Q_gamma: [64][SE]
+  static constexpr int SA = CH + 8;  // A, Aqk: [64][SA]; K_tail^T: [DK][SA]
+  static constexpr int szE = CH * SE, szA = CH * SA, szK = DK * SA;  // elements per half
+  static constexpr int oEb = 0, oQg = oEb + 2 * szE, oKtT = oQg + 2 * szE;  // bf16 offsets
+  static constexpr int oA = oKtT + 2 * szK, oAq = oA + 2 * szA, oEnd = oAq + 2 * szA;
+  static constexpr int oGC = oEnd * 2;  // bytes: gamma_C [DK] fp32
+  static constexpr int BYTES = oGC + DK * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert((oGC % 16) == 0 && (SE * 2) % 16 == 0 && (SA * 2) % 16 == 0, "alignment");
 };
+
+// position of channel (or token) x in a split-operand row (see above): slot
+// 8 g + e of each 32-wide k-step
+__device__ __forceinline__ constexpr int kpos(int x) {
+  return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x >> 4) & 1) + (x & 3);
+}
+__device__ __forceinline__ bf16x4 bf4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+__device__ __forceinline__ f32x4 fl4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ bf16x8 join8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// four consecutive values (k index x, a multiple of 4) of row r of a split
+// operand with row stride S: hi to arr, lo to arr + half
+template <int S>
+__device__ __forceinline__ void put_split(bf16* arr, int half, int r, int x, f32x4 v) {
+  const bf16x4 hi = bf4(v);
+  bf16* d = arr + r * S + kpos(x);
+  *reinterpret_cast<bf16x4*>(d) = hi;
+  *reinterpret_cast<bf16x4*>(d + half) = bf4(v - fl4(hi));
+}
+// B operand of k-step m from accumulator tiles t0 (k slots e < 4) and t1
+struct SplitB {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ SplitB split_b(f32x4 t0, f32x4 t1) {
+  const bf16x4 h0 = bf4(t0), h1 = bf4(t1);
+  return SplitB{join8(h0, h1), join8(bf4(t0 - fl4(h0)), bf4(t1 - fl4(h1)))};
+}
+// acc += A B in split precision, A from its two halves at a (lo at a + half)
+__device__ __forceinline__ f32x4 mma_split(const bf16* a, int half, const SplitB& b, f32x4 acc) {
+  const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + half);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.lo, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b.hi, acc, 0, 0, 0);
+}
 
 template <int DK>
 constexpr int plain_mrec_lds_bytes() {
-  return PlainMrecLay<DK>::TOTAL * 4;
+  return PlainMrecLay<DK>::BYTES;
 }
 
 // Under a scalar decay (or none) the factor rows of a chunk are row scalings
@@ -736,13 +783,14 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
   constexpr int DVS = 64;
   constexpr int NQ_E = CH * DK / 4 / NTHR;  // 16-byte pieces per staging thread of a [64][DK] record array
   constexpr int NQ_A = CH * CH / 4 / NTHR;  // of a [64][64] array
-  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
-  float* sEb = lds + L::oEb;
-  float* sQg = lds + L::oQg;
-  float* sKtT = lds + L::oKtT;
-  float* sA = lds + L::oA;
-  float* sAq = lds + L::oAq;
-  float* sGC = lds + L::oGC;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  bf16* sEb = reinterpret_cast<bf16*>(lds) + L::oEb;  // hi, then lo at + szE
+  bf16* sQg = reinterpret_cast<bf16*>(lds) + L::oQg;
+  bf16* sKtT = reinterpret_cast<bf16*>(lds) + L::oKtT;  // hi, then lo at + szK
+  bf16* sA = reinterpret_cast<bf16*>(lds) + L::oA;      // hi, then lo at + szA
+  bf16* sAq = reinterpret_cast<bf16*>(lds) + L::oAq;
+  float* sGC = reinterpret_cast<float*>(lds + L::oGC);
+  constexpr int hE = L::szE, hA = L::szA, hK = L::szK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -835,19 +883,19 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
           piece(u, tq, cq4);
           f32x4 eb, qgm;
           sd_rows(p, G, R.sd, tq, t0, widen(R.kr[u]), widen(R.qr[u]), R.bq[u], eb, qgm);
-          *reinterpret_cast<f32x4*>(sEb + tq * SE + cq4) = eb;
-          if constexpr (!REC) *reinterpret_cast<f32x4*>(sQg + tq * SE + cq4) = qgm;
+          put_split<SE>(sEb, hE, tq, cq4, eb);
+          if constexpr (!REC) put_split<SE>(sQg, hE, tq, cq4, qgm);
         } else {
           const int e = 4 * (st + NTHR * u), t = e / DK, c = e - t * DK;
-          *reinterpret_cast<f32x4*>(sEb + t * SE + c) = R.eb[u];
-          if constexpr (!REC) *reinterpret_cast<f32x4*>(sQg + t * SE + c) = R.qg[u];
+          put_split<SE>(sEb, hE, t, c, R.eb[u]);
+          if constexpr (!REC) put_split<SE>(sQg, hE, t, c, R.qg[u]);
         }
       }
 #pragma unroll
       for (int u = 0; u < NQ_A; ++u) {
         const int e = 4 * (st + NTHR * u), t = e / CH, c = e - t * CH;
-        *reinterpret_cast<f32x4*>(sA + t * SA + c) = R.a[u];
-        if constexpr (!REC) *reinterpret_cast<f32x4*>(sAq + t * SA + c) = R.aq[u];
+        put_split<SA>(sA, hA, t, c, R.a[u]);
+        if constexpr (!REC) put_split<SA>(sAq, hA, t, c, R.aq[u]);
       }
     };
     auto stage_b = [&](const RecB& R, int t0) __attribute__((always_inline)) {
@@ -867,7 +915,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
         } else {
           kt = R.kt[u];
         }
-        *reinterpret_cast<f32x4*>(sKtT + cq * SA + 4 * t4) = quad_transpose(kt, qj);
+        put_split<SA>(sKtT, hK, cq, 4 * t4, quad_transpose(kt, qj));
       }
       if (st < DK) sGC[st] = SD ? fexp(GC) : R.gc;
     };
@@ -936,37 +984,39 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
         for (int r = 0; r < 4; ++r) ws.S[(ch * DK + 16 * b + 4 * g + r) * DV + col] = S[b][r];
     }
     // ---- ES, QS -----------------------------------------------------------------
-    f32x4 W[4], QS[4];
+    constexpr int NKS = DK / 32;
+    SplitB Sb[NKS];
+#pragma unroll
+    for (int m = 0; m < NKS; ++m) Sb[m] = split_b(S[2 * m], S[2 * m + 1]);
+    f32x4 R[4], QS[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 es = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const f32x4 ae = *reinterpret_cast<const f32x4*>(sEb + (16 * I + l16) * SE + 16 * b + 4 * g);
-        const f32x4 aq = *reinterpret_cast<const f32x4*>(sQg + (16 * I + l16) * SE + 16 * b + 4 * g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          es = mfma_f32(ae[r], S[b][r], es);
-          qs = mfma_f32(aq[r], S[b][r], qs);
-        }
+      for (int m = 0; m < NKS; ++m) {
+        es = mma_split(sEb + (16 * I + l16) * SE + 32 * m + 8 * g, hE, Sb[m], es);
+        if constexpr (!REC) qs = mma_split(sQg + (16 * I + l16) * SE + 32 * m + 8 * g, hE, Sb[m], qs);
       }
       QS[I] = qs;
       // R = Z - E_bar S (rows 16 I + 4 g + r of this lane's column)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) W[I][r] = z[4 * I + r] - es[r];
+      for (int r = 0; r < 4; ++r) R[I][r] = z[4 * I + r] - es[r];
     }
-    // ---- W = A R, block rows from the last (each reads R blocks J <= I) --------
+    // ---- W = A R (row block I takes the k-steps of tokens below 32 (I / 2 + 1)) ---
+    SplitB Rb[2];
 #pragma unroll
-    for (int I = 3; I >= 0; --I) {
+    for (int q = 0; q < 2; ++q) Rb[q] = split_b(R[2 * q], R[2 * q + 1]);
+    f32x4 W[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
       f32x4 w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = 0; J <= I; ++J) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * I + l16) * SA + 16 * J + 4 * g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w = mfma_f32(a[r], W[J][r], w);
-      }
+      for (int q = 0; q <= I / 2; ++q) w = mma_split(sA + (16 * I + l16) * SA + 32 * q + 8 * g, hA, Rb[q], w);
       W[I] = w;
     }
+    SplitB Wb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) Wb[q] = split_b(W[2 * q], W[2 * q + 1]);
     if constexpr (REC) {
 #pragma unroll
       for (int I = 0; I < 4; ++I)
@@ -978,11 +1028,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       for (int I = 0; I < 4; ++I) {
         f32x4 o = QS[I];
 #pragma unroll
-        for (int J = 0; J <= I; ++J) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(sAq + (16 * I + l16) * SA + 16 * J + 4 * g);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o = mfma_f32(a[r], W[J][r], o);
-        }
+        for (int q = 0; q <= I / 2; ++q) o = mma_split(sAq + (16 * I + l16) * SA + 32 * q + 8 * g, hA, Wb[q], o);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + 16 * I + 4 * g + r;
@@ -997,11 +1043,7 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + 16 * b + 4 * g);
       f32x4 s = S[b] * gc;
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sKtT + (16 * b + l16) * SA + 16 * J + 4 * g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s = mfma_f32(a[r], W[J][r], s);
-      }
+      for (int q = 0; q < 2; ++q) s = mma_split(sKtT + (16 * b + l16) * SA + 32 * q + 8 * g, hK, Wb[q], s);
       S[b] = s;
     }
     __syncthreads();  // set A of the next chunk is staged; set B is free
