@@ -89,17 +89,24 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
 // inputs are loaded into the staging waves' registers a phase before they
 // are staged.  A computing wave and a staging wave share each SIMD, so the
 // staging arithmetic runs beside the MFMAs instead of between them.
+// Every product runs in the split precision of plain_mrec_kernel (bf16 hi
+// and lo halves of each fp32 operand, three bf16 MFMAs per product, fp32
+// accumulation), the staged rows stored with their k index in the fragments'
+// order (kpos); dS, dO, dW and dR serve as B operands once split.
 template <int DK>
 struct BwdAMLay {
-  static constexpr int SE = DK + 4, SA = CH + 4;
+  // bf16 rows (elements); hi then lo array of each operand
+  static constexpr int SE = DK + 8, SA = CH + 8;
+  static constexpr int hKt = CH * SE, hA = CH * SA, hT = DK * SA;  // elements per half
   static constexpr int oKt = 0;                  // [64][SE] K_tail rows        (set A)
-  static constexpr int oAqT = oKt + CH * SE;     // [64][SA] A_qk^T             (set A)
-  static constexpr int oAT = oAqT + CH * SA;     // [64][SA] A^T                (set A)
-  static constexpr int oQgT = oAT + CH * SA;     // [DK][SA] Q_gamma^T          (set B)
-  static constexpr int oEbT = oQgT + DK * SA;    // [DK][SA] E_bar^T            (set B)
-  static constexpr int oGC = oEbT + DK * SA;     // [DK] gamma_C                (set B)
-  static constexpr int TOTAL = oGC + DK;
-  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget exceeded");
+  static constexpr int oAqT = oKt + 2 * hKt;     // [64][SA] A_qk^T             (set A)
+  static constexpr int oAT = oAqT + 2 * hA;      // [64][SA] A^T                (set A)
+  static constexpr int oQgT = oAT + 2 * hA;      // [DK][SA] Q_gamma^T          (set B)
+  static constexpr int oEbT = oQgT + 2 * hT;     // [DK][SA] E_bar^T            (set B)
+  static constexpr int oGC = (oEbT + 2 * hT) * 2;  // bytes: [DK] gamma_C fp32   (set B)
+  static constexpr int BYTES = oGC + DK * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(oGC % 16 == 0, "alignment");
 };
 
 // SD: a scalar decay or none; E_bar, Q_gamma, K_tail and gamma_C are formed
@@ -110,9 +117,12 @@ void bwd_state_mfma_kernel(BwdParams p) {
   using L = BwdAMLay<DK>;
   constexpr int SE = L::SE, SA = L::SA, NB = DK / 16, DVS = 64;
   constexpr int NQ_E = CH * DK / 4 / NTHR, NQ_A = CH * CH / 4 / NTHR;
-  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
-  float *sKt = lds + L::oKt, *sQgT = lds + L::oQgT, *sEbT = lds + L::oEbT;
-  float *sAqT = lds + L::oAqT, *sAT = lds + L::oAT, *sGC = lds + L::oGC;
+  constexpr int hKt = L::hKt, hA = L::hA, hT = L::hT;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  bf16* lb = reinterpret_cast<bf16*>(lds);
+  bf16 *sKt = lb + L::oKt, *sQgT = lb + L::oQgT, *sEbT = lb + L::oEbT;
+  bf16 *sAqT = lb + L::oAqT, *sAT = lb + L::oAT;
+  float* sGC = reinterpret_cast<float*>(lds + L::oGC);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -210,17 +220,17 @@ void bwd_state_mfma_kernel(BwdParams p) {
         if constexpr (SD) {
           int tq, cq4;
           piece(u, tq, cq4);
-          *reinterpret_cast<f32x4*>(sKt + tq * SE + cq4) = sd_ktail(p.f, G, GC, tq, t0, widen(R.kr[u]));
+          put_split<SE>(sKt, hKt, tq, cq4, sd_ktail(p.f, G, GC, tq, t0, widen(R.kr[u])));
         } else {
           const int e = 4 * (st + NTHR * u), t = e / DK, c = e - t * DK;
-          *reinterpret_cast<f32x4*>(sKt + t * SE + c) = R.kt[u];
+          put_split<SE>(sKt, hKt, t, c, R.kt[u]);
         }
       }
 #pragma unroll
       for (int u = 0; u < NQ_A; ++u) {
         const int t4 = sw + 4 * u, cq = 4 * qk + qj;
-        *reinterpret_cast<f32x4*>(sAT + cq * SA + 4 * t4) = quad_transpose(R.a[u], qj);
-        *reinterpret_cast<f32x4*>(sAqT + cq * SA + 4 * t4) = quad_transpose(R.aq[u], qj);
+        put_split<SA>(sAT, hA, cq, 4 * t4, quad_transpose(R.a[u], qj));
+        put_split<SA>(sAqT, hA, cq, 4 * t4, quad_transpose(R.aq[u], qj));
       }
     };
     auto stage_b = [&](const RecB& R, int t0) __attribute__((always_inline)) {
@@ -241,8 +251,8 @@ void bwd_state_mfma_kernel(BwdParams p) {
           eb = R.eb[u];
           qgm = R.qg[u];
         }
-        *reinterpret_cast<f32x4*>(sQgT + cq * SA + 4 * t4) = quad_transpose(qgm, qj);
-        *reinterpret_cast<f32x4*>(sEbT + cq * SA + 4 * t4) = quad_transpose(eb, qj);
+        put_split<SA>(sQgT, hT, cq, 4 * t4, quad_transpose(qgm, qj));
+        put_split<SA>(sEbT, hT, cq, 4 * t4, quad_transpose(eb, qj));
       }
       if (st < DK) sGC[st] = SD ? fexp(GC) : R.gc;
     };
@@ -302,65 +312,56 @@ void bwd_state_mfma_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) ws.dS[(ch * DK + 16 * b + 4 * g + r) * DV + col] = dS[b][r];
     // ---- dW = A_qk^T dO + K_tail dS (A_qk^T is zero below the diagonal) ---------
+    // dO tiles (rows 16 J + 4 g + r) and dS as split B operands; row block I
+    // of an upper-triangular factor takes the k-steps of tokens from 32 (I / 2)
+    constexpr int NKS = DK / 32;
+    SplitB dOb[2], dSb[NKS];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      dOb[q] = split_b(f32x4{dO[8 * q], dO[8 * q + 1], dO[8 * q + 2], dO[8 * q + 3]},
+                       f32x4{dO[8 * q + 4], dO[8 * q + 5], dO[8 * q + 6], dO[8 * q + 7]});
+#pragma unroll
+    for (int m = 0; m < NKS; ++m) dSb[m] = split_b(dS[2 * m], dS[2 * m + 1]);
     f32x4 dW[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      // (the fragments of the row block requested together; the two products
-      // in two accumulators)
-      f32x4 ak[NB], aa[4];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) ak[b] = *reinterpret_cast<const f32x4*>(sKt + (16 * I + l16) * SE + 16 * b + 4 * g);
-#pragma unroll
-      for (int J = I; J < 4; ++J) aa[J] = *reinterpret_cast<const f32x4*>(sAqT + (16 * I + l16) * SA + 16 * J + 4 * g);
+      // (the two products in two accumulators)
       f32x4 w = {0.f, 0.f, 0.f, 0.f}, w2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = I; J < 4; ++J)
+      for (int q = I / 2; q < 2; ++q) w2 = mma_split(sAqT + (16 * I + l16) * SA + 32 * q + 8 * g, hA, dOb[q], w2);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w2 = mfma_f32(aa[J][r], dO[4 * J + r], w2);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w = mfma_f32(ak[b][r], dS[b][r], w);
+      for (int m = 0; m < NKS; ++m) w = mma_split(sKt + (16 * I + l16) * SE + 32 * m + 8 * g, hKt, dSb[m], w);
       dW[I] = w + w2;
     }
-    // ---- dR = A^T dW, block rows from the first (each reads dW blocks J >= I) ----
+    // ---- dR = A^T dW (A^T is zero below the diagonal) ------------------------------
+    SplitB dWb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dWb[q] = split_b(dW[2 * q], dW[2 * q + 1]);
+    f32x4 dR[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 r4 = {0.f, 0.f, 0.f, 0.f}, aa[4];
+      f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = I; J < 4; ++J) aa[J] = *reinterpret_cast<const f32x4*>(sAT + (16 * I + l16) * SA + 16 * J + 4 * g);
-#pragma unroll
-      for (int J = I; J < 4; ++J)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) r4 = mfma_f32(aa[J][r], dW[J][r], r4);
-      dW[I] = r4;
+      for (int q = I / 2; q < 2; ++q) r4 = mma_split(sAT + (16 * I + l16) * SA + 32 * q + 8 * g, hA, dWb[q], r4);
+      dR[I] = r4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ws.dR[(ch * CH + 16 * I + 4 * g + r) * DV + col] = r4[r];
     }
     __syncthreads();  // set B of this chunk is staged; set A is free
     // ---- dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR -----------------------
-    // (dR negated once; each block's eight fragments requested together; the
-    // two products in two accumulators)
-    f32x4 ndR[4];
+    // (dR negated once; the two products in two accumulators)
+    SplitB ndRb[2];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) ndR[J] = -dW[J];
+    for (int q = 0; q < 2; ++q) ndRb[q] = split_b(-dR[2 * q], -dR[2 * q + 1]);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + 16 * b + 4 * g);
-      f32x4 aq[4], ae[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        aq[J] = *reinterpret_cast<const f32x4*>(sQgT + (16 * b + l16) * SA + 16 * J + 4 * g);
-        ae[J] = *reinterpret_cast<const f32x4*>(sEbT + (16 * b + l16) * SA + 16 * J + 4 * g);
-      }
       f32x4 sq = dS[b] * gc, se = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = 0; J < 4; ++J)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sq = mfma_f32(aq[J][r], dO[4 * J + r], sq);
-          se = mfma_f32(ae[J][r], ndR[J][r], se);
-        }
+      for (int q = 0; q < 2; ++q) {
+        sq = mma_split(sQgT + (16 * b + l16) * SA + 32 * q + 8 * g, hT, dOb[q], sq);
+        se = mma_split(sEbT + (16 * b + l16) * SA + 32 * q + 8 * g, hT, ndRb[q], se);
+      }
       dS[b] = sq + se;
     }
     __syncthreads();  // set A of the next chunk is staged; set B is free

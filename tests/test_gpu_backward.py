@@ -1,8 +1,9 @@
 """GPU parity of the backward (gdr_chunk_bwd) against the float64 oracle's
 adjoint (``oracle.backward``, pinned by finite differences): every gradient
 of every input, element by element, max|x - ref| / max|ref| per tensor, at
-the forward's bars (1e-4 for fp32 I/O, 2e-2 for bf16 I/O; the backward's
-arithmetic is fp32 throughout, so both land far below them).  The cases
+the forward's bars (1e-4 for fp32 I/O, 2e-2 for bf16 I/O; the backward
+accumulates in fp32, its record recurrence and reverse state pass multiply
+in split precision, about 16 bits per operand, so both land far below them).  The cases
 cover each variant and gate kind, the mild-decay and alpha = 1 stress cases,
 extreme decay, ragged and single-chunk lengths, dk != dv and T = 0."""
 
