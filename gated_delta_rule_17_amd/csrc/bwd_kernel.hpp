@@ -8,7 +8,11 @@
 // pulled out of them).  Evaluated here on the regrouped forward of the plain
 // kernel (W = A R, R = Z - E_bar S), where dA = dW R^T and therefore
 //   dR = A^T dW,   dT = -tril(dR W^T, -1),   dZ = dR,   dE_bar = -dR S^T.
-// All arithmetic is fp32.  Four passes, each a kernel on the caller's stream:
+// Accumulation is fp32; the products of the record recurrence, the state
+// pass and the product pass run in split precision (each fp32 operand as
+// bf16 hi and lo halves, Xhi Yhi + Xhi Ylo + Xlo Yhi on the bf16 matrix
+// cores), the key pass on fp32 MFMAs.  Four passes, each a kernel on the
+// caller's stream:
 //
 //  0  record  the two-pass plain forward in record mode
 //             (plain_split_kernel.hpp): per chunk A = (I + T)^{-1} (in the
@@ -377,30 +381,92 @@ void bwd_state_mfma_kernel(BwdParams p) {
 // ---- pass B1: products over the value channels, on the matrix cores --------
 // One workgroup of four waves per (batch, head, chunk), two per CU.  The value
 // channels are taken in quarters of 32: dR, dO, W [64][32] and S, dS [DK][32]
-// of the quarter in LDS (65 KB at DK = 128), the products' partial sums
+// of the quarter in LDS (70 KB at DK = 128), the products' partial sums
 // carried over the quarters in accumulators; while one workgroup waits for
-// its loads, the other computes.  Wave w owns row block w (rows 16 w .. + 15) of every
-// output: dT and dA_qk (blocks J <= w), dE_bar, dQ_gamma, dK_tail (all DK / 16
-// column blocks).  Every product contracts over the value channels with
-// v_mfma_f32_16x16x4_f32; k-step (b, r) takes, in lane group g, the value
-// channel 16 b + 4 g + r of the half, so both operands are 16-byte LDS reads
-// of rows (four k-steps each).  Then sC = sum_v S (.) dS per key channel.
+// its loads, the other computes.  Wave w owns row block w (rows 16 w .. + 15)
+// of every output: dT and dA_qk (blocks J <= w), dE_bar, dQ_gamma, dK_tail
+// (all DK / 16 column blocks).  Every product contracts over the value
+// channels in the split precision of plain_mrec_kernel: each fp32 operand is
+// staged as bf16 hi and lo halves (row stride 40, the k index of every row in
+// the fragments' order, kpos), and a quarter is one k-step of
+// v_mfma_f32_16x16x32_bf16, three MFMAs per product (Xhi Yhi + Xhi Ylo +
+// Xlo Yhi) with fp32 accumulation; both operands are 16-byte LDS reads of
+// rows.  sC = sum_v S (.) dS per key channel is summed in fp32 from the
+// staging registers.
 template <int DK>
 struct BwdB1Lay {
-  static constexpr int VH = 32, SP = VH + 4;
-  static constexpr int oR = 0, oO = oR + CH * SP, oW = oO + CH * SP, oS = oW + CH * SP, odS = oS + DK * SP;
-  static constexpr int TOTAL = odS + DK * SP;
-  static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
+  static constexpr int VH = 32, SE = VH + 8;
+  // rows of the staged operands, then the elements of one half
+  static constexpr int rR = 0, rO = CH, rW = 2 * CH, rS = 3 * CH, rdS = 3 * CH + DK, NROW = 3 * CH + 2 * DK;
+  static constexpr int HALF = NROW * SE;
+  static constexpr int BYTES = 2 * HALF * 2;
+  static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
 };
+
+// One quarter's operands (the thread's pieces: row e / 8, channels
+// 4 (e % 8) .. + 3 of e = tid + NTHR u) from registers to LDS, split.
+template <int DK, int QR, int QS>
+__device__ __forceinline__ void b1_stage(bf16* sp, int tid, const f32x4 (&xr)[QR], const f32x4 (&xo)[QR],
+                                         const f32x4 (&xw)[QR], const f32x4 (&xs)[QS], const f32x4 (&xd)[QS]) {
+  using L = BwdB1Lay<DK>;
+#pragma unroll
+  for (int u = 0; u < QR; ++u) {
+    const int e = tid + NTHR * u, r = e / (L::VH / 4), c4 = (e % (L::VH / 4)) * 4;
+    put_split<L::SE>(sp, L::HALF, L::rR + r, c4, xr[u]);
+    put_split<L::SE>(sp, L::HALF, L::rO + r, c4, xo[u]);
+    put_split<L::SE>(sp, L::HALF, L::rW + r, c4, xw[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < QS; ++u) {
+    const int e = tid + NTHR * u, r = e / (L::VH / 4), c4 = (e % (L::VH / 4)) * 4;
+    put_split<L::SE>(sp, L::HALF, L::rS + r, c4, xs[u]);
+    put_split<L::SE>(sp, L::HALF, L::rdS + r, c4, xd[u]);
+  }
+}
+
+// The products of row block w over one staged quarter:
+//   dT += dR W^T, dA_qk += dO W^T (column blocks J <= w),
+//   dE_bar += dR S^T, dQ_gamma += dO S^T, dK_tail += W dS^T
+// (dT and dE_bar without their minus signs)
+template <int DK>
+__device__ __forceinline__ void b1_products(const bf16* sp, int w, int g, int l16, f32x4 (&aT)[4], f32x4 (&aA)[4],
+                                            f32x4 (&aE)[DK / 16], f32x4 (&aQ)[DK / 16], f32x4 (&aK)[DK / 16]) {
+  using L = BwdB1Lay<DK>;
+  const bf16* base = sp + l16 * L::SE + 8 * g;
+  auto frag = [&](int row0) __attribute__((always_inline)) { return lds_split(base + row0 * L::SE, L::HALF); };
+  const SplitB ar = frag(L::rR + 16 * w), ao = frag(L::rO + 16 * w), aw = frag(L::rW + 16 * w);
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    if (J > w) continue;  // wave-uniform
+    const SplitB bw = frag(L::rW + 16 * J);
+    aT[J] = mma_split(ar, bw, aT[J]);
+    aA[J] = mma_split(ao, bw, aA[J]);
+  }
+#pragma unroll
+  for (int c = 0; c < DK / 16; ++c) {
+    const SplitB bs = frag(L::rS + 16 * c), bd = frag(L::rdS + 16 * c);
+    aE[c] = mma_split(ar, bs, aE[c]);
+    aQ[c] = mma_split(ao, bs, aQ[c]);
+    aK[c] = mma_split(aw, bd, aK[c]);
+  }
+}
+
+// the sum over 8 adjacent lanes (an aligned group), in every lane of it
+__device__ __forceinline__ float sum8(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xf, 0xf, true));
+  return x;
+}
 
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_prod_kernel(BwdParams p) {
   using L = BwdB1Lay<DK>;
-  constexpr int VH = L::VH, SP = L::SP, NC = DK / 16;
+  constexpr int VH = L::VH, NC = DK / 16;
+  constexpr int QR = CH * VH / 4 / NTHR, QS = DK * VH / 4 / NTHR;
   static_assert(DV % VH == 0, "value channels in quarters of 32");
-  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
-  float *sR = lds + L::oR, *sO = lds + L::oO, *sW = lds + L::oW, *sS = lds + L::oS, *sdS = lds + L::odS;
+  __shared__ __attribute__((aligned(16))) bf16 sp[2 * L::HALF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
@@ -418,13 +484,12 @@ void bwd_prod_kernel(BwdParams p) {
   for (int J = 0; J < 4; ++J) aT[J] = aA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c) aE[c] = aQ[c] = aK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sc = 0.f;  // sum_v S (.) dS of channel tid >> 1, half of the value channels of each quarter
+  float sc[QS] = {};  // sum_v S (.) dS of the thread's pieces (key channel (tid + NTHR u) / 8)
 
   for (int vh = 0; vh < DV; vh += VH) {
     if (vh > 0) __syncthreads();  // the previous quarter's reads are done
     // ---- the quarter's rows to LDS (every load of the thread issued first)
     {
-      constexpr int QR = CH * VH / 4 / NTHR, QS = DK * VH / 4 / NTHR;
       f32x4 xr[QR], xo[QR], xw[QR], xs[QS], xd[QS];
 #pragma unroll
       for (int u = 0; u < QR; ++u) {
@@ -440,64 +505,14 @@ void bwd_prod_kernel(BwdParams p) {
         xs[u] = *reinterpret_cast<const f32x4*>(ws.S + (ch * DK + r) * DV + vh + c4);
         xd[u] = *reinterpret_cast<const f32x4*>(ws.dS + (ch * DK + r) * DV + vh + c4);
       }
+      b1_stage<DK>(sp, tid, xr, xo, xw, xs, xd);
 #pragma unroll
-      for (int u = 0; u < QR; ++u) {
-        const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
-        *reinterpret_cast<f32x4*>(sR + r * SP + c4) = xr[u];
-        *reinterpret_cast<f32x4*>(sO + r * SP + c4) = xo[u];
-        *reinterpret_cast<f32x4*>(sW + r * SP + c4) = xw[u];
-      }
+      for (int u = 0; u < QS; ++u)
 #pragma unroll
-      for (int u = 0; u < QS; ++u) {
-        const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
-        *reinterpret_cast<f32x4*>(sS + r * SP + c4) = xs[u];
-        *reinterpret_cast<f32x4*>(sdS + r * SP + c4) = xd[u];
-      }
+        for (int i = 0; i < 4; ++i) sc[u] = __builtin_fmaf(xs[u][i], xd[u][i], sc[u]);
     }
     __syncthreads();
-    // ---- sC: channel tid >> 1 (DK = 128) or tid >> 2 (DK = 64), a run of the quarter
-    {
-      constexpr int TPC = NTHR / DK, RUN = VH / TPC;
-      const int c = tid / TPC, v0 = (tid % TPC) * RUN;
-#pragma unroll
-      for (int v = 0; v < RUN; v += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sS + c * SP + v0 + v);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(sdS + c * SP + v0 + v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc = __builtin_fmaf(a[i], b[i], sc);
-      }
-    }
-    // ---- the products of row block w over the quarter
-#pragma unroll
-    for (int b = 0; b < VH / 16; ++b) {
-      const int ko = 16 * b + 4 * g;
-      const f32x4 ar = *reinterpret_cast<const f32x4*>(sR + (16 * w + l16) * SP + ko);
-      const f32x4 ao = *reinterpret_cast<const f32x4*>(sO + (16 * w + l16) * SP + ko);
-      const f32x4 aw = *reinterpret_cast<const f32x4*>(sW + (16 * w + l16) * SP + ko);
-      // dT = -dR W^T, dA_qk = dO W^T: column blocks J <= w
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        if (J > w) continue;  // wave-uniform
-        const f32x4 bw = *reinterpret_cast<const f32x4*>(sW + (16 * J + l16) * SP + ko);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          aT[J] = mfma_f32(ar[r], bw[r], aT[J]);
-          aA[J] = mfma_f32(ao[r], bw[r], aA[J]);
-        }
-      }
-      // dE_bar = -dR S^T, dQ_gamma = dO S^T, dK_tail = W dS^T
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const f32x4 bs = *reinterpret_cast<const f32x4*>(sS + (16 * c + l16) * SP + ko);
-        const f32x4 bd = *reinterpret_cast<const f32x4*>(sdS + (16 * c + l16) * SP + ko);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          aE[c] = mfma_f32(ar[r], bs[r], aE[c]);
-          aQ[c] = mfma_f32(ao[r], bs[r], aQ[c]);
-          aK[c] = mfma_f32(aw[r], bd[r], aK[c]);
-        }
-      }
-    }
+    b1_products<DK>(sp, w, g, l16, aT, aA, aE, aQ, aK);
   }
   // ---- outputs: lane holds rows 16 w + 4 g + r of column l16 of each block
 #pragma unroll
@@ -519,12 +534,12 @@ void bwd_prod_kernel(BwdParams p) {
       ws.Kt[o] = aK[c][r];
     }
   }
-  // sC: the channel's threads (adjacent lanes) combined
-  constexpr int TPC = NTHR / DK;
-  sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0xB1, 0xf, 0xf, true));
-  if constexpr (TPC == 4)
-    sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0x4E, 0xf, 0xf, true));
-  if (tid % TPC == 0) ws.gC[ch * DK + tid / TPC] = sc;
+  // sC: a key channel's pieces lie in 8 adjacent lanes
+#pragma unroll
+  for (int u = 0; u < QS; ++u) {
+    const float s = sum8(sc[u]);
+    if ((tid & 7) == 0) ws.gC[ch * DK + (tid + NTHR * u) / (VH / 4)] = s;
+  }
 }
 
 // The end of pass B2, shared by both forms of it: the value side (dZ = dR
@@ -795,9 +810,7 @@ __global__ __launch_bounds__(NTHR) void bwd_key_kernel(BwdParams p) {
 // overlay phase 1's.
 template <int DK>
 struct BwdPKLay {
-  static constexpr int VH = 32, SP = VH + 4;  // phase 1: a quarter's [rows][32] arrays
-  static constexpr int oR = 0, oO = oR + CH * SP, oW = oO + CH * SP, oS = oW + CH * SP, odS = oS + DK * SP;
-  static constexpr int P1 = odS + DK * SP;
+  static constexpr int P1 = BwdB1Lay<DK>::BYTES / 4;  // phase 1: a quarter's split rows (floats)
   static constexpr int KC = 32, TP = CH + 4;  // phase 2: D1, D2 and a pass's K^T, E^T, Q^T
   static constexpr int oD1 = 0, oD2 = oD1 + CH * TP, oKT = oD2 + CH * TP, oET = oKT + KC * TP, oQT = oET + KC * TP;
   static constexpr int P2 = oQT + KC * TP;
@@ -810,13 +823,13 @@ template <class IO, int DK, int DV>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_prodkey_kernel(BwdParams p) {
   using L = BwdPKLay<DK>;
-  constexpr int VH = L::VH, SP = L::SP, NC = DK / 16;
+  constexpr int VH = BwdB1Lay<DK>::VH, NC = DK / 16;
   constexpr int KC = L::KC, TP = L::TP, NPASS = DK / KC, NCB = KC / 16;
   static_assert(DV % VH == 0 && DK % KC == 0 && NTHR == 256, "quarters of 32 value channels, passes of 32 key channels");
   __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
   __shared__ float sRb[CH][NPASS], sRl[CH][NPASS], sRz[CH], sDg[CH], sSC[DK];
   __shared__ float sBeta[CH], sLam[CH], sGt[CH], sDiag[CH], sRG[CH], sRX[CH];
-  float *sR = lds + L::oR, *sO = lds + L::oO, *sW = lds + L::oW, *sS = lds + L::oS, *sdS = lds + L::odS;
+  bf16* sp = reinterpret_cast<bf16*>(lds);
   float *sD1 = lds + L::oD1, *sD2 = lds + L::oD2, *sKT = lds + L::oKT, *sET = lds + L::oET, *sQT = lds + L::oQT;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -853,19 +866,16 @@ void bwd_prodkey_kernel(BwdParams p) {
   }
 
   // ================= phase 1: the products over the value channels ==========
-  // Wave w owns row block w (rows 16 w .. + 15) of every output: dT and
-  // dA_qk (blocks J <= w), dE_bar, dQ_gamma, dK_tail (all DK / 16 column
-  // blocks); k-step (b, r) takes, in lane group g, the value channel
-  // 16 b + 4 g + r of the quarter, so both operands are 16-byte LDS reads of
-  // rows.  The value side takes the thread's dR pieces of the quarter (row
-  // r, channels c4 .. + 3) from its staging registers.
+  // bwd_prod_kernel's quarters (b1_stage, b1_products: split precision).
+  // The value side takes the thread's dR pieces of the quarter (row r,
+  // channels c4 .. + 3) from its staging registers.
   constexpr int QR = CH * VH / 4 / NTHR, QS = DK * VH / 4 / NTHR;
   f32x4 aT[4], aA[4], aE[NC], aQ[NC], aK[NC];
 #pragma unroll
   for (int J = 0; J < 4; ++J) aT[J] = aA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c) aE[c] = aQ[c] = aK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sc = 0.f;          // sum_v S (.) dS of channel tid / TPC, a run of each quarter
+  float sc[QS] = {};       // sum_v S (.) dS of the thread's pieces (key channel (tid + NTHR u) / 8)
   float zrow[QR] = {};     // sum_v dZ (.) v of the thread's pieces (the beta write gate)
   for (int vh = 0; vh < DV; vh += VH) {
     if (vh > 0) __syncthreads();  // the previous quarter's reads are done
@@ -889,18 +899,14 @@ void bwd_prodkey_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int u = 0; u < QR; ++u) {
-      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
+      const int r = (tid + NTHR * u) / (VH / 4);
       if (t0 + r >= T) xo[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(sR + r * SP + c4) = xr[u];
-      *reinterpret_cast<f32x4*>(sO + r * SP + c4) = xo[u];
-      *reinterpret_cast<f32x4*>(sW + r * SP + c4) = xw[u];
     }
+    b1_stage<DK>(sp, tid, xr, xo, xw, xs, xd);
 #pragma unroll
-    for (int u = 0; u < QS; ++u) {
-      const int e = tid + NTHR * u, r = e / (VH / 4), c4 = (e % (VH / 4)) * 4;
-      *reinterpret_cast<f32x4*>(sS + r * SP + c4) = xs[u];
-      *reinterpret_cast<f32x4*>(sdS + r * SP + c4) = xd[u];
-    }
+    for (int u = 0; u < QS; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[u] = __builtin_fmaf(xs[u][i], xd[u][i], sc[u]);
     __syncthreads();  // (also: the per-row scalars are in place)
     // ---- the value side: dZ = dR gives dv and, per write gate, dw or the
     // rows' sums for dbeta
@@ -920,67 +926,20 @@ void bwd_prodkey_kernel(BwdParams p) {
         }
       }
     }
-    // ---- sC: channel tid / TPC, a run of the quarter
-    {
-      constexpr int TPC = NTHR / DK, RUN = VH / TPC;
-      const int c = tid / TPC, v0 = (tid % TPC) * RUN;
-#pragma unroll
-      for (int v = 0; v < RUN; v += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sS + c * SP + v0 + v);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(sdS + c * SP + v0 + v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc = __builtin_fmaf(a[i], b[i], sc);
-      }
-    }
-    // ---- the products of row block w over the quarter
-#pragma unroll
-    for (int b = 0; b < VH / 16; ++b) {
-      const int ko = 16 * b + 4 * g;
-      const f32x4 ar = *reinterpret_cast<const f32x4*>(sR + (16 * w + l16) * SP + ko);
-      const f32x4 ao = *reinterpret_cast<const f32x4*>(sO + (16 * w + l16) * SP + ko);
-      const f32x4 aw = *reinterpret_cast<const f32x4*>(sW + (16 * w + l16) * SP + ko);
-      // dT = -dR W^T, dA_qk = dO W^T: column blocks J <= w
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        if (J > w) continue;  // wave-uniform
-        const f32x4 bw = *reinterpret_cast<const f32x4*>(sW + (16 * J + l16) * SP + ko);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          aT[J] = mfma_f32(ar[r], bw[r], aT[J]);
-          aA[J] = mfma_f32(ao[r], bw[r], aA[J]);
-        }
-      }
-      // dE_bar = -dR S^T, dQ_gamma = dO S^T, dK_tail = W dS^T
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const f32x4 bs = *reinterpret_cast<const f32x4*>(sS + (16 * c + l16) * SP + ko);
-        const f32x4 bd = *reinterpret_cast<const f32x4*>(sdS + (16 * c + l16) * SP + ko);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          aE[c] = mfma_f32(ar[r], bs[r], aE[c]);
-          aQ[c] = mfma_f32(ao[r], bs[r], aQ[c]);
-          aK[c] = mfma_f32(aw[r], bd[r], aK[c]);
-        }
-      }
-    }
+    b1_products<DK>(sp, w, g, l16, aT, aA, aE, aQ, aK);
   }
   // the rows' sums of dZ (.) v: a row's 32 channels of a quarter lie in 8
   // adjacent lanes
 #pragma unroll
   for (int u = 0; u < QR; ++u) {
-    float z = zrow[u];
-    z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0xB1, 0xf, 0xf, true));
-    z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0x4E, 0xf, 0xf, true));
-    z += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, z), 0x141, 0xf, 0xf, true));
+    const float z = sum8(zrow[u]);
     if ((tid & 7) == 0) sRz[(tid + NTHR * u) / (VH / 4)] = z;
   }
-  // sC: the channel's threads (adjacent lanes) combined
-  {
-    constexpr int TPC = NTHR / DK;
-    sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0xB1, 0xf, 0xf, true));
-    if constexpr (TPC == 4)
-      sc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sc), 0x4E, 0xf, 0xf, true));
-    if (tid % TPC == 0) sSC[tid / TPC] = sc;
+  // sC: a key channel's pieces lie in 8 adjacent lanes
+#pragma unroll
+  for (int u = 0; u < QS; ++u) {
+    const float z = sum8(sc[u]);
+    if ((tid & 7) == 0) sSC[(tid + NTHR * u) / (VH / 4)] = z;
   }
   __syncthreads();  // phase 1's arrays are no longer read
 

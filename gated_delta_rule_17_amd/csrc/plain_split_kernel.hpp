@@ -709,6 +709,16 @@ __device__ __forceinline__ f32x4 mma_split(const bf16* a, int half, const SplitB
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.lo, acc, 0, 0, 0);
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b.hi, acc, 0, 0, 0);
 }
+// a fragment of a split operand stored in LDS (hi at a, lo at a + half)
+__device__ __forceinline__ SplitB lds_split(const bf16* a, int half) {
+  return SplitB{*reinterpret_cast<const bf16x8*>(a), *reinterpret_cast<const bf16x8*>(a + half)};
+}
+// acc += A B in split precision, both operands as fragments
+__device__ __forceinline__ f32x4 mma_split(const SplitB& a, const SplitB& b, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+}
 
 template <int DK>
 constexpr int plain_mrec_lds_bytes() {
