@@ -43,15 +43,70 @@
 
 namespace gdr {
 
+// ---- split precision ------------------------------------------------------
+// Products on the bf16 matrix cores with near-fp32 operands: each fp32
+// operand x is held as hi = bf16(x) and lo = bf16(x - hi), and X Y is formed
+// as Xhi Yhi + Xhi Ylo + Xlo Yhi (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation; the dropped Xlo Ylo and the roundings of lo leave about 16
+// bits of each operand).  In a 32-wide k-step m, lane group g = l / 16 takes
+// the k indices 32 m + 4 g + e and 32 m + 16 + 4 g + e (e < 4), which is
+// where a lane's accumulators hold them in the tiles 2m and 2m + 1, so
+// accumulator tiles serve as B operands once split (split_b).  Operands in
+// LDS are rows stored with their k index in that order: kpos(x) is the
+// position of k index x in such a row.
+__device__ __forceinline__ constexpr int kpos(int x) {
+  return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x >> 4) & 1) + (x & 3);
+}
+__device__ __forceinline__ bf16x4 bf4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+__device__ __forceinline__ f32x4 fl4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ bf16x8 join8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// four consecutive values (k index x, a multiple of 4) of row r of a split
+// operand with row stride S: hi to arr, lo to arr + half
+template <int S>
+__device__ __forceinline__ void put_split(bf16* arr, int half, int r, int x, f32x4 v) {
+  const bf16x4 hi = bf4(v);
+  bf16* d = arr + r * S + kpos(x);
+  *reinterpret_cast<bf16x4*>(d) = hi;
+  *reinterpret_cast<bf16x4*>(d + half) = bf4(v - fl4(hi));
+}
+// B operand of k-step m from accumulator tiles t0 (k slots e < 4) and t1
+struct SplitB {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ SplitB split_b(f32x4 t0, f32x4 t1) {
+  const bf16x4 h0 = bf4(t0), h1 = bf4(t1);
+  return SplitB{join8(h0, h1), join8(bf4(t0 - fl4(h0)), bf4(t1 - fl4(h1)))};
+}
+// acc += A B in split precision, A from its two halves at a (lo at a + half)
+__device__ __forceinline__ f32x4 mma_split(const bf16* a, int half, const SplitB& b, f32x4 acc) {
+  const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + half);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.lo, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b.hi, acc, 0, 0, 0);
+}
+// a fragment of a split operand stored in LDS (hi at a, lo at a + half)
+__device__ __forceinline__ SplitB lds_split(const bf16* a, int half) {
+  return SplitB{*reinterpret_cast<const bf16x8*>(a), *reinterpret_cast<const bf16x8*>(a + half)};
+}
+// acc += A B in split precision, both operands as fragments
+__device__ __forceinline__ f32x4 mma_split(const SplitB& a, const SplitB& b, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+}
+
 // ---- pass 1 -----------------------------------------------------------------
-// Channels are processed in halves of 64: [64][68] arrays of k, e, q and the
-// prefix sums G of the half, 74 KB of LDS (two workgroups per CU).  Under a
-// scalar decay (or none) the Gram sums are fp32 MFMA tiles
-// (v_mfma_f32_16x16x4f32; k-step (b, r) takes, in lane group g, the channel
-// 16 b + 4 g + r, so both operands are 16-byte reads of rows): wave w owns the
-// (I, J) tile pairs w, w + 4, w + 8 of the ten on or below the diagonal.
+// Channels are processed in halves of 64, 74 KB of LDS (two workgroups per
+// CU); the next half's loads are in flight during a half's Gram sums.  Under
+// a scalar decay (or none) the Gram sums are MFMA tiles in split precision
+// (k, e, q of the half staged as bf16 hi and lo rows in kpos order, both
+// operands 16-byte reads of rows, two 32-wide k-steps per half): wave w owns
+// the (I, J) tile pairs w, w + 4, w + 8 of the ten on or below the diagonal.
 // Under a decay per key channel every term carries its own exponential and
-// the sums run on the vector ALUs, 4 x 4 (i, j) blocks per thread.
+// the sums run on the vector ALUs from [64][68] fp32 arrays of k, e, q and
+// the prefix sums G of the half, 4 x 4 (i, j) blocks per thread.
 struct PlainPrepLay {
   static constexpr int CHH = 64;       // channels per half
   static constexpr int HP = CHH + 4;   // row stride (floats): 16-byte rows
@@ -60,6 +115,11 @@ struct PlainPrepLay {
   static constexpr int oPart = oGs + CH;    // [16][64] sums of the log-decay over 4-row groups
   static constexpr int TOTAL = oPart + 16 * CHH;
   static_assert(2 * TOTAL * 4 <= 160 * 1024, "two workgroups per CU");
+  // under a scalar decay (or none): k, e, q of the half split into bf16 hi
+  // and lo halves ([64][SE] each, kpos order), over the fp32 arrays
+  static constexpr int SE = CHH + 8, HS = CH * SE;  // row stride, elements per half
+  static constexpr int oKs = 0, oXs = 2 * HS, oQs = 4 * HS;
+  static_assert(6 * HS * 2 <= oGs * 4 && (SE * 2) % 16 == 0, "split arrays below the scalars");
 };
 
 // factors = 0: the factor rows E_bar, Q_gamma, K_tail and gamma_C are not
@@ -78,6 +138,8 @@ void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
   float* sG = lds + L::oG;
   float* sGs = lds + L::oGs;
   float* sPart = lds + L::oPart;
+  bf16* sp = reinterpret_cast<bf16*>(lds);
+  constexpr int SE = L::SE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,13 +179,11 @@ void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
 #pragma unroll
   for (int t = 0; t < 3; ++t) mT[t] = mA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int half = 0; half < NH; ++half) {
-    const int cb = half * CHH;  // first channel of the half
-    if (half > 0) __syncthreads();  // the previous half's Gram reads are done
-    // ---- loads: every load of the thread first, at token indices clamped to
-    // T - 1, masked afterwards
-    f32x4 rk[4], rq[4], rgc[4], rb[4];
-    float rbeta[4], rlam[4];
+  // ---- loads of a half: every load of the thread, at token indices clamped
+  // to T - 1, masked at use
+  f32x4 rk[4], rq[4], rgc[4], rb[4];
+  float rbeta[4], rlam[4];
+  auto load_half = [&](int cb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = 4 * rg + u;
@@ -135,7 +195,14 @@ void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
       rbeta[u] = erase == 0 ? p.beta[tok] : 0.f;
       rlam[u] = qmix == 2 ? p.lam[tok] : (qmix ? p.lam[hh] : 0.f);
     }
-    __syncthreads();  // (sGs ready; sPart free)
+  };
+  load_half(0);
+
+#pragma unroll
+  for (int half = 0; half < NH; ++half) {
+    const int cb = half * CHH;  // first channel of the half
+    // (sGs ready, sPart free; after the first half: its Gram reads are done)
+    __syncthreads();
     // ---- prefix sums of the log-decay per channel: within the thread's four
     // rows, then over the 4-row groups through sPart
     float G[4][4];  // [row u][channel i]
@@ -149,12 +216,10 @@ void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
         G[u][i] = run;
       }
     }
-    if (decay == 2) {
-      *reinterpret_cast<f32x4*>(sPart + rg * CHH + c4) = f32x4{G[3][0], G[3][1], G[3][2], G[3][3]};
-    }
-    __syncthreads();
     float GC[4];
     if (decay == 2) {
+      *reinterpret_cast<f32x4*>(sPart + rg * CHH + c4) = f32x4{G[3][0], G[3][1], G[3][2], G[3][3]};
+      __syncthreads();
       f32x4 excl = {0.f, 0.f, 0.f, 0.f}, tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -201,37 +266,43 @@ void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
         *reinterpret_cast<f32x4*>(ws.Qg + ro) = qgm;
         *reinterpret_cast<f32x4*>(ws.Kt + ro) = kt;
       }
+      if (decay == 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sK[r * HP + c4 + i] = kv[i];
-        sX[r * HP + c4 + i] = ev[i];
-        sQ[r * HP + c4 + i] = qv[i];
-        sG[r * HP + c4 + i] = G[u][i];
+        for (int i = 0; i < 4; ++i) {
+          sK[r * HP + c4 + i] = kv[i];
+          sX[r * HP + c4 + i] = ev[i];
+          sQ[r * HP + c4 + i] = qv[i];
+          sG[r * HP + c4 + i] = G[u][i];
+        }
+      } else {
+        put_split<SE>(sp + L::oKs, L::HS, r, c4, kv);
+        put_split<SE>(sp + L::oXs, L::HS, r, c4, ev);
+        put_split<SE>(sp + L::oQs, L::HS, r, c4, qv);
       }
     }
     if (rg == 0 && factors) {
       *reinterpret_cast<f32x4*>(ws.gC + ch * DK + cb + c4) =
           f32x4{fexp(GC[0]), fexp(GC[1]), fexp(GC[2]), fexp(GC[3])};
     }
+    // the next half's loads, in flight during this half's Gram sums
+    if (half + 1 < NH) load_half(cb + CHH);
     __syncthreads();
     // ---- Gram sums over the half's channels ----------------------------------
     if (decay != 2) {
+      // split precision, two 32-wide k-steps per half
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int pr = wave + 4 * t;
         if (pr >= 10) continue;  // wave-uniform
         const int I = tile_I(pr), J = tile_J(pr);
 #pragma unroll
-        for (int b = 0; b < CHH / 16; ++b) {
-          const int ko = 16 * b + 4 * g;
-          const f32x4 ax = *reinterpret_cast<const f32x4*>(sX + (16 * I + l16) * HP + ko);
-          const f32x4 aq = *reinterpret_cast<const f32x4*>(sQ + (16 * I + l16) * HP + ko);
-          const f32x4 bk = *reinterpret_cast<const f32x4*>(sK + (16 * J + l16) * HP + ko);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            mT[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax[r], bk[r], mT[t], 0, 0, 0);
-            mA[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[r], bk[r], mA[t], 0, 0, 0);
-          }
+        for (int m = 0; m < CHH / 32; ++m) {
+          const bf16* base = sp + l16 * SE + 32 * m + 8 * g;
+          const SplitB bk = lds_split(base + L::oKs + 16 * J * SE, L::HS);
+          const SplitB ax = lds_split(base + L::oXs + 16 * I * SE, L::HS);
+          const SplitB aq = lds_split(base + L::oQs + 16 * I * SE, L::HS);
+          mT[t] = mma_split(ax, bk, mT[t]);
+          mA[t] = mma_split(aq, bk, mA[t]);
         }
       }
     } else if (jb <= ib) {
@@ -630,24 +701,17 @@ __global__ __launch_bounds__(NTHR) void plain_rec_kernel(ChunkParams p, BwdWs ws
 namespace gdr {
 
 // ---- pass 2 on the matrix cores ---------------------------------------------
-// The same recurrence with every product on v_mfma_f32_16x16x4_f32 (fp32
-// operands, fp32 accumulation), for every gate kind but the per-value-channel
-// beta: one workgroup of eight waves per (batch, head, 64-column slice).
+// The same recurrence on the matrix cores, for every gate kind but the
+// per-value-channel beta: one workgroup of eight waves per (batch, head,
+// 64-column slice).
 // Waves 0-3 compute: wave w owns columns 16 w .. + 15 and the state S of
 // those columns in accumulators: register r of block b of lane l holds
 // S[16 b + 4 (l / 16) + r][16 w + l % 16].
 //
-// Every product runs on bf16 matrix cores in split precision: each fp32
-// operand x is held as hi = bf16(x) and lo = bf16(x - hi), and a product
-// X Y is formed as Xhi Yhi + Xhi Ylo + Xlo Yhi (v_mfma_f32_16x16x32_bf16,
-// fp32 accumulation; the dropped Xlo Ylo and the roundings of lo leave about
-// 16 bits of each operand, against the 24 of fp32, at a sixth of the fp32
-// matrix instructions' time).  A 32-wide k-step m takes, in lane group
-// g = l / 16, the channels (or tokens) 32 m + 4 g + e and 32 m + 16 + 4 g + e
-// (e < 4): where that lane's accumulators hold them in the tiles 2m and
-// 2m + 1.  So the state, R, W and the other accumulator tiles serve as B
-// operands after the split, and the A operands are rows stored with their
-// k index in that order (kpos), one 16-byte LDS read per half and fragment:
+// Every product runs in split precision (three bf16 MFMAs, at a sixth of the
+// fp32 matrix instructions' time): the state, R, W and the other
+// accumulator tiles serve as B operands once split, and the A operands are
+// rows stored in kpos order, one 16-byte LDS read per half and fragment:
 //   ES, QS  = E_bar S, Q_gamma S          A = E_bar, Q_gamma rows (token x channel)
 //   W       = A (Z - ES)                  A = A rows (token x token), lower blocks only
 //   O       = QS + Aqk W                  A = Aqk rows
@@ -675,50 +739,6 @@ struct PlainMrecLay {
   static_assert((oGC % 16) == 0 && (SE * 2) % 16 == 0 && (SA * 2) % 16 == 0, "alignment");
 };
 
-// position of channel (or token) x in a split-operand row (see above): slot
-// 8 g + e of each 32-wide k-step
-__device__ __forceinline__ constexpr int kpos(int x) {
-  return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x >> 4) & 1) + (x & 3);
-}
-__device__ __forceinline__ bf16x4 bf4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
-__device__ __forceinline__ f32x4 fl4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
-__device__ __forceinline__ bf16x8 join8(bf16x4 a, bf16x4 b) {
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-// four consecutive values (k index x, a multiple of 4) of row r of a split
-// operand with row stride S: hi to arr, lo to arr + half
-template <int S>
-__device__ __forceinline__ void put_split(bf16* arr, int half, int r, int x, f32x4 v) {
-  const bf16x4 hi = bf4(v);
-  bf16* d = arr + r * S + kpos(x);
-  *reinterpret_cast<bf16x4*>(d) = hi;
-  *reinterpret_cast<bf16x4*>(d + half) = bf4(v - fl4(hi));
-}
-// B operand of k-step m from accumulator tiles t0 (k slots e < 4) and t1
-struct SplitB {
-  bf16x8 hi, lo;
-};
-__device__ __forceinline__ SplitB split_b(f32x4 t0, f32x4 t1) {
-  const bf16x4 h0 = bf4(t0), h1 = bf4(t1);
-  return SplitB{join8(h0, h1), join8(bf4(t0 - fl4(h0)), bf4(t1 - fl4(h1)))};
-}
-// acc += A B in split precision, A from its two halves at a (lo at a + half)
-__device__ __forceinline__ f32x4 mma_split(const bf16* a, int half, const SplitB& b, f32x4 acc) {
-  const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + half);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.hi, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.lo, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b.hi, acc, 0, 0, 0);
-}
-// a fragment of a split operand stored in LDS (hi at a, lo at a + half)
-__device__ __forceinline__ SplitB lds_split(const bf16* a, int half) {
-  return SplitB{*reinterpret_cast<const bf16x8*>(a), *reinterpret_cast<const bf16x8*>(a + half)};
-}
-// acc += A B in split precision, both operands as fragments
-__device__ __forceinline__ f32x4 mma_split(const SplitB& a, const SplitB& b, f32x4 acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
-}
 
 template <int DK>
 constexpr int plain_mrec_lds_bytes() {
