@@ -29,7 +29,10 @@ hipError_t bwd_sequence(const BwdParams& p, int BH, hipStream_t s) {
   // the bytes of the fp32 records): the prep does not write them
   const bool sd = p.f.decay != 2 && std::is_same<IO, bf16>::value;
   if (N > 0) {
-    hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws, sd ? 0 : 1);
+    if (sd && p.f.erase == 0)
+      hipLaunchKernelGGL((plain_prep_exact_kernel<DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws);
+    else
+      hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(BH * N), dim3(NTHR), 0, s, p.f, p.ws, sd ? 0 : 1);
     ChunkParams f64 = p.f;
     f64.nslices = DV / 64;
     if (sd)

@@ -49,7 +49,10 @@ hipError_t plain_split_sequence(const ChunkParams& p, const BwdWs& ws, int dvs, 
   // records), so the prep does not write them; with fp32 I/O the inputs
   // weigh as much as the records and the records are read
   const bool sd = dvs == 64 && p.decay != 2 && std::is_same<IO, bf16>::value;
-  hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws, sd ? 0 : 1);
+  if (sd && p.erase == 0)
+    hipLaunchKernelGGL((plain_prep_exact_kernel<DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws);
+  else
+    hipLaunchKernelGGL((plain_prep_kernel<IO, DK>), dim3(prep_grid), dim3(NTHR), 0, s, p, ws, sd ? 0 : 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dvs == 64) {

@@ -122,6 +122,73 @@ struct PlainPrepLay {
   static_assert(6 * HS * 2 <= oGs * 4 && (SE * 2) % 16 == 0, "split arrays below the scalars");
 };
 
+// A = (I + T)^{-1} from T (sT: dense [64][HP] fp32, zero on and above the
+// diagonal) into sAi, sP as scratch; then A to recA, the chunk's [64][64]
+// record (zero above the diagonal).  Every thread of the workgroup calls
+// it, after a barrier that follows the writes of sT.
+template <int HP>
+__device__ __forceinline__ void prep_inverse(const float* sT, float* sAi, float* sP, float* recA, int tid) {
+  // ---- A = (I + T)^{-1} ------------------------------------------------------
+  // level 0: the diagonal blocks (I + T_bb)^{-1}; thread 16 b + l solves for
+  // column l of block b (x = e_l, then x_i -= sum_{m < i} T_im x_m)
+  if (tid < CH) {
+    const int r0 = 16 * (tid >> 4), l = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i == l ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = __builtin_fmaf(sT[(r0 + i) * HP + r0 + m], x[m], s);
+      x[i] -= s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sAi[(r0 + i) * HP + r0 + l] = x[i];
+  }
+  __syncthreads();
+  // levels s = 1, 2, 3: the blocks (I, J) with I - J = s,
+  //   A_IJ = -A_II sum_{K = J}^{I - 1} T_IK A_KJ
+  // (every A_KJ on the right lies closer to the diagonal)
+  // (thread tid: element (i, j) = (tid / 16, tid % 16) of each block)
+  const int bi = tid >> 4, bj = tid & 15;
+  auto level = [&](auto slc) __attribute__((always_inline)) {
+    constexpr int sl = decltype(slc)::value;
+#pragma unroll
+    for (int J = 0; J + sl < 4; ++J) {
+      const int I = J + sl;
+      float acc = 0.f;
+#pragma unroll
+      for (int kk = 16 * J; kk < 16 * I; ++kk)
+        acc = __builtin_fmaf(sT[(16 * I + bi) * HP + kk], sAi[kk * HP + 16 * J + bj], acc);
+      sP[(16 * J + bi) * HP + bj] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int J = 0; J + sl < 4; ++J) {
+      const int I = J + sl;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        acc = __builtin_fmaf(sAi[(16 * I + bi) * HP + 16 * I + m], sP[(16 * J + m) * HP + bj], acc);
+      sAi[(16 * I + bi) * HP + 16 * J + bj] = -acc;
+    }
+    __syncthreads();
+  };
+  level(IC<1>{});
+  level(IC<2>{});
+  level(IC<3>{});
+  // A to the record in the place of T (zero above the diagonal)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + NTHR * u, i = e >> 4, j4 = (e & 15) * 4;
+    f32x4 av;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) av[b] = j4 + b <= i ? sAi[i * HP + j4 + b] : 0.f;
+    *reinterpret_cast<f32x4*>(recA + i * CH + j4) = av;
+  }
+}
+
 // factors = 0: the factor rows E_bar, Q_gamma, K_tail and gamma_C are not
 // written (the passes that read them form them from the inputs: a scalar
 // decay or none, see sd_rows).
@@ -385,65 +452,136 @@ void plain_prep_kernel(ChunkParams p, BwdWs ws, int factors) {
   }
   if (erase == 2) return;
   __syncthreads();
-  // ---- A = (I + T)^{-1} ------------------------------------------------------
-  // level 0: the diagonal blocks (I + T_bb)^{-1}; thread 16 b + l solves for
-  // column l of block b (x = e_l, then x_i -= sum_{m < i} T_im x_m)
-  if (tid < CH) {
-    const int r0 = 16 * (tid >> 4), l = tid & 15;
-    float x[16];
+  prep_inverse<HP>(sT, sAi, sP, ws.T + ch * CH * CH, tid);
+}
+
+// ---- pass 1 with bf16 inputs under a scalar decay (or none) ------------------
+// With bf16 k and q and the erase direction e = beta (k + lambda q), the Gram
+// sums split into products of the raw inputs, exact on the bf16 matrix cores
+// (fp32 accumulation), with the per-token scalars applied to the sums:
+//   T[i][j]   = beta_i ((K K^T)[i][j] + lambda_i (Q K^T)[i][j]) exp(G_i - G_j)   j <  i
+//   Aqk[i][j] = (Q K^T)[i][j] exp(G_i - G_j)                                     j <= i
+// The rows are staged once as they arrive (no halves, no conversions); the
+// inverse then takes their place.  48 KB of LDS: three workgroups per CU.
+// The factor rows are not written (the passes that read them form them from
+// the inputs).
+template <int DK>
+struct PlainPrepExactLay {
+  static constexpr int SR = DK + 8;  // bf16 row stride: 16-row fragment reads in distinct banks
+  static constexpr int HP = CH + 4;  // the inverse's fp32 arrays
+  static constexpr int oRows = 0;    // k rows, then q rows: [64][SR] bf16 each (floats: CH * SR)
+  static constexpr int oT = 0, oAi = oT + CH * HP, oP = oAi + CH * HP;  // [64][HP], [64][HP], [48][HP]
+  static constexpr int END = (oP + 48 * HP) > CH * SR ? (oP + 48 * HP) : CH * SR;
+  static constexpr int oGs = END, oBeta = oGs + CH, oLam = oBeta + CH;
+  static constexpr int TOTAL = oLam + CH;
+  static_assert(3 * TOTAL * 4 <= 160 * 1024, "three workgroups per CU");
+  static_assert((SR * 2) % 16 == 0, "16-byte rows");
+};
+
+template <int DK>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void plain_prep_exact_kernel(ChunkParams p, BwdWs ws) {
+  using L = PlainPrepExactLay<DK>;
+  constexpr int SR = L::SR, HP = L::HP;
+  __shared__ __attribute__((aligned(16))) float lds[L::TOTAL];
+  bf16* sKr = reinterpret_cast<bf16*>(lds + L::oRows);
+  bf16* sQr = sKr + CH * SR;
+  float *sT = lds + L::oT, *sAi = lds + L::oAi, *sP = lds + L::oP;
+  float *sGs = lds + L::oGs, *sBeta = lds + L::oBeta, *sLam = lds + L::oLam;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = p.T, H = p.H, N = (T + CH - 1) / CH;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int bb = bh / H, hh = bh - bb * H;
+  const int t0 = n * CH;
+  const size_t ch = blockIdx.x;  // record index (batch * H + head) * N + chunk
+  const size_t seq0 = (size_t)bb * T * H + hh;
+  const bf16* kg = reinterpret_cast<const bf16*>(p.k);
+  const bf16* qg = reinterpret_cast<const bf16*>(p.q);
+
+  // ---- rows of k and q (zero past T), every load of the thread first
+  constexpr int RPT = CH * DK / 8 / NTHR;  // 16-byte pieces per thread and array
+  bf16x8 rk[RPT], rq[RPT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = i == l ? 1.f : 0.f;
+  for (int u = 0; u < RPT; ++u) {
+    const int e = tid + NTHR * u, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+    const size_t tok = seq0 + (size_t)min(t0 + r, T - 1) * H;
+    rk[u] = *reinterpret_cast<const bf16x8*>(kg + tok * DK + c8);
+    rq[u] = *reinterpret_cast<const bf16x8*>(qg + tok * DK + c8);
+  }
+  // wave 0: prefix sums of the log-decay; wave 1: beta and lambda of the rows
+  if (wave == 0) {
+    const int t = t0 + lane;
+    const float g = (p.decay == 1 && t < T) ? p.g[seq0 + (size_t)t * H] : 0.f;
+    sGs[lane] = wave_incl_scan(g);
+  } else if (wave == 1) {
+    const int t = t0 + lane;
+    const size_t tok = seq0 + (size_t)min(t, T - 1) * H;
+    sBeta[lane] = t < T ? p.beta[tok] : 0.f;
+    sLam[lane] = p.qmix == 2 ? p.lam[tok] : (p.qmix ? p.lam[hh] : 0.f);
+  }
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) s = __builtin_fmaf(sT[(r0 + i) * HP + r0 + m], x[m], s);
-      x[i] -= s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sAi[(r0 + i) * HP + r0 + l] = x[i];
+  for (int u = 0; u < RPT; ++u) {
+    const int e = tid + NTHR * u, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+    const bool ok = t0 + r < T;
+    *reinterpret_cast<bf16x8*>(sKr + r * SR + c8) = ok ? rk[u] : bf16x8{};
+    *reinterpret_cast<bf16x8*>(sQr + r * SR + c8) = ok ? rq[u] : bf16x8{};
   }
   __syncthreads();
-  // levels s = 1, 2, 3: the blocks (I, J) with I - J = s,
-  //   A_IJ = -A_II sum_{K = J}^{I - 1} T_IK A_KJ
-  // (every A_KJ on the right lies closer to the diagonal)
-  // (thread tid: element (i, j) = (tid / 16, tid % 16) of each block)
-  const int bi = tid >> 4, bj = tid & 15;
-  auto level = [&](auto slc) __attribute__((always_inline)) {
-    constexpr int sl = decltype(slc)::value;
+  // ---- K K^T and Q K^T: tile pair pr = wave + 4 t (t < 3, pr < 10) of the
+  // ten (I >= J) in the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ..;
+  // 32-wide k-steps, both operands 16-byte reads of rows
+  const int g = lane >> 4, l16 = lane & 15;
+  auto tile_I = [](int pr) { return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3; };
+  auto tile_J = [](int pr) { return pr - (pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 3 : 6); };
+  f32x4 mK[3], mQ[3];
 #pragma unroll
-    for (int J = 0; J + sl < 4; ++J) {
-      const int I = J + sl;
-      float acc = 0.f;
+  for (int t = 0; t < 3; ++t) {
+    mK[t] = mQ[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int pr = wave + 4 * t;
+    if (pr >= 10) continue;  // wave-uniform
+    const int I = tile_I(pr), J = tile_J(pr);
 #pragma unroll
-      for (int kk = 16 * J; kk < 16 * I; ++kk)
-        acc = __builtin_fmaf(sT[(16 * I + bi) * HP + kk], sAi[kk * HP + 16 * J + bj], acc);
-      sP[(16 * J + bi) * HP + bj] = acc;
+    for (int m = 0; m < DK / 32; ++m) {
+      const int o = l16 * SR + 32 * m + 8 * g;
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(sKr + 16 * J * SR + o);
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sKr + 16 * I * SR + o);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQr + 16 * I * SR + o);
+      mK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, mK[t], 0, 0, 0);
+      mQ[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, mQ[t], 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int J = 0; J + sl < 4; ++J) {
-      const int I = J + sl;
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        acc = __builtin_fmaf(sAi[(16 * I + bi) * HP + 16 * I + m], sP[(16 * J + m) * HP + bj], acc);
-      sAi[(16 * I + bi) * HP + 16 * J + bj] = -acc;
-    }
-    __syncthreads();
-  };
-  level(IC<1>{});
-  level(IC<2>{});
-  level(IC<3>{});
-  // A to the record in the place of T (zero above the diagonal)
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + NTHR * u, i = e >> 4, j4 = (e & 15) * 4;
-    f32x4 av;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) av[b] = j4 + b <= i ? sAi[i * HP + j4 + b] : 0.f;
-    *reinterpret_cast<f32x4*>(ws.T + ch * CH * CH + i * CH + j4) = av;
   }
+  __syncthreads();  // the rows are no longer read (the inverse's arrays take their place)
+  // ---- T to LDS (dense, zeros above the mask), Aqk to the record: lane
+  // rows 16 I + 4 g + r, column 16 J + l16
+  float* recA = ws.A + ch * CH * CH;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int pr = wave + 4 * t;
+    if (pr >= 10) continue;
+    const int I = tile_I(pr), J = tile_J(pr), j = 16 * J + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * I + 4 * g + r;
+      const float d = fexp(fminf(sGs[i] - sGs[j], 0.f));
+      const float e = sBeta[i] * __builtin_fmaf(sLam[i], mQ[t][r], mK[t][r]);
+      sT[i * HP + j] = j < i ? e * d : 0.f;
+      recA[i * CH + j] = j <= i ? mQ[t][r] * d : 0.f;
+    }
+  }
+  // the six tiles above the diagonal are zero in the record (the inverse
+  // reads none of them)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int u = wave + 4 * t;
+    if (u >= 6) continue;
+    const int I = u < 3 ? 0 : u < 5 ? 1 : 2, J = u < 3 ? u + 1 : u < 5 ? u - 1 : 3, j = 16 * J + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) recA[(16 * I + 4 * g + r) * CH + j] = 0.f;
+  }
+  __syncthreads();
+  prep_inverse<HP>(sT, sAi, sP, ws.T + ch * CH * CH, tid);
 }
 
 // sum over the four lanes of each quad (DPP quad permutations), every lane
