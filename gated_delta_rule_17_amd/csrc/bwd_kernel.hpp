@@ -1124,9 +1124,16 @@ void bwd_prodkey_kernel(BwdParams p) {
     float s2 = 0.f;
     for (int c2 = tid; c2 < DK; c2 += CH) s2 += sSC[c2];
     const float base = fexp(GC) * wave_total(s2);
-    const float rg = sRG[tid], rx = sRX[tid];
-    const float ig = wave_incl_scan(rg), ix = wave_incl_scan(rx);
-    sDg[tid] = (lane_value(ig, 63) - ig + rg) + (ix - rx) + base;
+    // a true exclusive prefix and a true suffix (scan of the reversed rows):
+    // a total minus a prefix would add a row's term and take it away again,
+    // and the O(1) K_tail term of the last row (tail = 1) would leave its
+    // rounding in every other token's dg, which under a strong decay is
+    // orders of magnitude smaller
+    const float rx = sRX[tid];
+    const float ix = wave_incl_scan(rx), ixm = __shfl_up(ix, 1);
+    const float ex = lane == 0 ? 0.f : ixm;
+    const float sg = __shfl(wave_incl_scan(__shfl(sRG[tid], 63 - lane)), 63 - lane);
+    sDg[tid] = sg + ex + base;
   }
   __syncthreads();
   // ---- per-token sums: the scalar-decay dg, dbeta, dlambda

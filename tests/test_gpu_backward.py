@@ -36,6 +36,7 @@ CASES = {
     "gdn2_f32_dk64_dv128": config(F, variant="gdn2", B=1, H=2, T=70, dk=64, dv=128, decay_shift=-4.0),
     "kda_f32_dk128_dv64": config(F, variant="kda", B=1, H=2, T=64, dk=128, dv=64, decay_shift=-4.0),
     "gdn2_extreme": config(G2, B=1, H=2, T=100, g_const=-20.0),
+    "gdn_bf16_extreme": config(H, B=1, H=2, T=100, g_const=-20.0),
     "gdn_erase_ch_f32": config(F, B=1, H=2, T=80, erase="channel", decay_shift=-3.0),
     # bf16 under a scalar decay: the record recurrence and the state pass form
     # the factor rows from the inputs (per-channel erase gate; lambda per token)
