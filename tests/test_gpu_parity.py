@@ -62,6 +62,12 @@ CASES = {
     # extreme decay g = -20 per channel (s7): exercises the exact fallback Gram
     "gdn2_extreme": config(G2, B=1, H=2, T=200, g_const=-20.0),
     "kda_extreme_f32": config(F, variant="kda", B=1, H=2, T=130, g_const=-20.0),
+    # the same decay as a scalar: the pipelined kernel, the two-pass scalar
+    # form, the plain fp32 two-pass form and the fp32 MFMA kernel
+    "gdn_extreme_bf16": config(H, B=1, H=2, T=200, g_const=-20.0),
+    "qdelta_extreme_bf16": config(Q, B=1, H=2, T=200, g_const=-20.0),
+    "gdn_extreme_f32_d128": config(F, B=1, H=2, T=130, d=128, g_const=-20.0),
+    "gdn_extreme_f32": config(F, B=1, H=2, T=130, g_const=-20.0),
     # dk != dv catches transposed operands
     "gdn_dk128_dv64": config(H, B=1, H=2, T=256, dk=128, dv=64, decay_shift=-2.0),
     "kda_dk64_dv128": config(K, B=1, H=2, T=256, dk=64, dv=128, decay_shift=-3.0),
