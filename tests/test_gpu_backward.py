@@ -37,6 +37,11 @@ CASES = {
     "kda_f32_dk128_dv64": config(F, variant="kda", B=1, H=2, T=64, dk=128, dv=64, decay_shift=-4.0),
     "gdn2_extreme": config(G2, B=1, H=2, T=100, g_const=-20.0),
     "gdn_bf16_extreme": config(H, B=1, H=2, T=100, g_const=-20.0),
+    # bf16 at dk 64 (the exact prep and the product and key pass at 64 key
+    # channels) and dv 64 (one 64-column slice)
+    "gdn_bf16_d64": config(H, B=1, H=2, T=150, d=64, decay_shift=-3.0),
+    "qdelta_bf16_dk64_dv128": config(Q, B=1, H=2, T=130, dk=64, dv=128, decay_shift=-3.0),
+    "gdn_bf16_dk128_dv64": config(H, B=2, H=1, T=100, dk=128, dv=64, decay_shift=-2.0),
     "gdn_erase_ch_f32": config(F, B=1, H=2, T=80, erase="channel", decay_shift=-3.0),
     # bf16 under a scalar decay: the record recurrence and the state pass form
     # the factor rows from the inputs (per-channel erase gate; lambda per token)
