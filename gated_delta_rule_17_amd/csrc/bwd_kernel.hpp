@@ -76,12 +76,13 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
 
 // ---- pass A: the reverse state recurrence, on the matrix cores ----------------
 // One workgroup of eight waves per (batch, head, 64-column slice).  Waves 0-3
-// compute, every product on v_mfma_f32_16x16x4_f32: wave w owns columns
-// 16 w .. + 15 and dS of those columns in accumulators (register r of block b
-// of lane l: dS[16 b + 4 (l / 16) + r][16 w + l % 16], the forward
-// recurrence's state layout).  k-step (b, r) takes, in lane group g, the
-// channel or token 16 b + 4 g + r, so dS, dO, dW and dR serve as B operands in
-// place and the A operands are 16-byte LDS reads:
+// compute on the matrix cores in split precision (bf16 hi and lo halves of
+// each fp32 operand, three bf16 MFMAs per product, fp32 accumulation): wave w
+// owns columns 16 w .. + 15 and dS of those columns in accumulators (register
+// r of block b of lane l: dS[16 b + 4 (l / 16) + r][16 w + l % 16], the
+// forward recurrence's state layout).  dS, dO, dW and dR serve as B operands
+// once split, and the A operands are staged rows with their k index in the
+// fragments' order (kpos), 16-byte LDS reads per half:
 //   dW = A_qk^T dO + K_tail dS        A = A_qk^T rows, K_tail rows
 //   dR = A^T dW                       A = A^T rows (upper blocks only)
 //   dS <- Diag(gamma_C) dS + Q_gamma^T dO - E_bar^T dR   A = Q_gamma^T, E_bar^T rows
@@ -93,10 +94,6 @@ __device__ __forceinline__ void copy_rows(float* dst, const float* src, int tid)
 // inputs are loaded into the staging waves' registers a phase before they
 // are staged.  A computing wave and a staging wave share each SIMD, so the
 // staging arithmetic runs beside the MFMAs instead of between them.
-// Every product runs in the split precision of plain_mrec_kernel (bf16 hi
-// and lo halves of each fp32 operand, three bf16 MFMAs per product, fp32
-// accumulation), the staged rows stored with their k index in the fragments'
-// order (kpos); dS, dO, dW and dR serve as B operands once split.
 template <int DK>
 struct BwdAMLay {
   // bf16 rows (elements); hi then lo array of each operand

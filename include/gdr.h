@@ -170,9 +170,11 @@ typedef struct gdr_plan_info {
 /*
  * Chunkwise forward over any T >= 0 ([GDN2] key design 2, C = 64).
  * Supported: io BF16 or F32 with dk in {64, 128}; dv a multiple of 16,
- * 16..256, divisible by the slice width.  fp32 I/O runs fp32 matrix
- * arithmetic (the tighter fp32 tolerance); the per-value-channel beta and a
- * time-varying lambda run on an all-fp32 kernel with 16-column slices.  Other
+ * 16..256, divisible by the slice width.  fp32 I/O keeps fp32 accuracy (the
+ * tighter fp32 tolerance): fp32 products, or at dk 128 in the two-pass form
+ * split-precision products (each operand as two bf16 halves, fp32
+ * accumulation); the per-value-channel beta and a time-varying lambda run on
+ * the plain kernels (fp32 arithmetic or split precision).  Other
  * valid combinations return GDR_E_UNSUPPORTED.  The epilogue (out_gate)
  * needs dv in {64, 128, 256}; it runs as a second kernel over o in place,
  * because the chunk kernels split a head's value columns over workgroups.
