@@ -1145,12 +1145,6 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
       z[k] = ok ? gt[k] * (float)v[k] : 0.f;
     }
     if (n + 1 < N) load_z(n + 1);
-    if constexpr (REC) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ws.S[(ch * DK + 16 * b + 4 * g + r) * DV + col] = S[b][r];
-    }
     // ---- ES, QS -----------------------------------------------------------------
     constexpr int NKS = DK / 32;
     SplitB Sb[NKS];
@@ -1186,10 +1180,16 @@ void plain_mrec_kernel(ChunkParams p, BwdWs ws) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) Wb[q] = split_b(W[2 * q], W[2 * q + 1]);
     if constexpr (REC) {
+      // W and the entering state S to the workspace, issued after the chain's
+      // products (stored at the top of the step they delayed them)
 #pragma unroll
       for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ws.W[(ch * CH + 16 * I + 4 * g + r) * DV + col] = W[I][r];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ws.S[(ch * DK + 16 * b + 4 * g + r) * DV + col] = S[b][r];
     } else {
       // ---- O = QS + Aqk W -------------------------------------------------------
 #pragma unroll
